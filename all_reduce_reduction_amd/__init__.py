@@ -1,0 +1,269 @@
+"""Python binding of libsimar.so (argument marshalling only).
+
+Every function named ``sim_*`` here calls the C function of the same name in
+``include/simar.h`` through ctypes and raises :class:`SimError` on a
+non-zero status.  All work of the all-reduce path runs in the HIP kernels of
+the library; there is no Python or CPU fallback -- if the library is missing
+the import fails.
+
+The ``allreduce`` / ``reduce_scatter`` / ``all_gather`` helpers take lists of
+torch device tensors (PyTorch is used for device memory and streams only)
+and pass their pointers and the current HIP stream to the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+try:  # load torch's HIP runtime first so the library and torch share it
+    import torch  # noqa: F401
+except Exception:  # pragma: no cover - the host-only tests work without torch
+    torch = None
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBPATH = os.path.join(_HERE, "libsimar.so")
+
+SIM_OK = 0
+STATUS = {0: "SIM_OK", -1: "SIM_ERR_INVALID_ARG", -2: "SIM_ERR_UNSUPPORTED", -3: "SIM_ERR_ALIGN",
+          -4: "SIM_ERR_ALIAS", -5: "SIM_ERR_NOMEM", -6: "SIM_ERR_HIP", -7: "SIM_ERR_TIMEOUT",
+          -8: "SIM_ERR_VERIFY", -9: "SIM_ERR_NOT_INIT"}
+STATUS_CODE = {v: k for k, v in STATUS.items()}
+DTYPES = {"int32": 0, "fp32": 1, "fp16": 2, "bf16": 3}
+OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
+ALGOS = {"auto": 0, "ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4}
+ALGO_NAMES = {v: k for k, v in ALGOS.items()}
+ESIZE = {"int32": 4, "fp32": 4, "fp16": 2, "bf16": 2}
+XFER_KINDS = {0: "REDUCE", 1: "REDUCE_POST", 2: "COPY", 3: "GATHER_REDUCE", 4: "FANOUT", 5: "ONESHOT"}
+DEBUG = {"epoch": 0, "spin_limit": 1, "ll_wait_skew": 2, "fill_ll": 3, "log": 4, "workgroups": 5,
+         "unroll": 6}
+MAX_RANKS = 16
+LL_MAX_BYTES_PER_RANK = 1 << 20
+
+
+class SimError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBPATH):
+        raise ImportError(f"{LIBPATH} is not built; run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950) first")
+    lib = ctypes.CDLL(LIBPATH)
+    vp, sz, i, d = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_double
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "sim_init": ([i, i, sz], i),
+        "sim_finalize": ([], i),
+        "sim_allreduce": ([pp, pp, i, sz, i, i, i, vp], i),
+        "sim_reduce_scatter": ([pp, pp, i, sz, i, i, i, vp], i),
+        "sim_all_gather": ([pp, pp, i, sz, i, i, vp], i),
+        "sim_select": ([i, sz, i, i, ctypes.POINTER(i), ctypes.POINTER(d)], i),
+        "sim_last_algo": ([], i),
+        "sim_model_load": ([ctypes.c_char_p], i),
+        "sim_model_predict": ([i, i, i, d, ctypes.POINTER(d)], i),
+        "sim_model_set": ([i, d, d, d, d], i),
+        "sim_model_reset": ([], i),
+        "sim_check_error": ([vp], i),
+        "sim_schedule_info": ([i, i, ctypes.POINTER(i), ctypes.POINTER(i)], i),
+        "sim_schedule_xfers": ([i, i, i, ctypes.POINTER(i), i, ctypes.POINTER(i)], i),
+        "sim_schedule_state": ([i, i, i, ctypes.POINTER(ctypes.c_uint32)], i),
+        "sim_verify_schedule": ([i, i, ctypes.c_char_p, sz], i),
+        "sim_verify_custom": ([i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.c_char_p, sz], i),
+        "sim_debug_set": ([i, ctypes.c_uint64], i),
+        "sim_debug_get": ([i, ctypes.POINTER(ctypes.c_uint64)], i),
+        "sim_status_string": ([i], ctypes.c_char_p),
+        "sim_version": ([], i),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int, what: str) -> int:
+    if status != SIM_OK:
+        raise SimError(status, what)
+    return status
+
+
+def _ptr_array(ptrs: Sequence[int]):
+    return (ctypes.c_void_p * len(ptrs))(*[int(p) for p in ptrs])
+
+
+def _code(table, v, what):
+    if isinstance(v, str):
+        if v not in table:
+            raise ValueError(f"unknown {what} {v!r}")
+        return table[v]
+    return int(v)
+
+
+# ---- the C functions, one to one ------------------------------------------------
+def sim_init(device: int = 0, p_max: int = MAX_RANKS, max_bytes_per_rank: int = 0) -> None:
+    _check(lib.sim_init(device, p_max, max_bytes_per_rank), "sim_init")
+
+
+def sim_finalize() -> None:
+    _check(lib.sim_finalize(), "sim_finalize")
+
+
+def sim_allreduce(in_ptrs, out_ptrs, p, n, dtype, op, algo, stream=0) -> int:
+    return lib.sim_allreduce(_ptr_array(in_ptrs), _ptr_array(out_ptrs), p, n, _code(DTYPES, dtype, "dtype"),
+                             _code(OPS, op, "op"), _code(ALGOS, algo, "algo"), stream or None)
+
+
+def sim_reduce_scatter(in_ptrs, out_ptrs, p, n_out_per_rank, dtype, op, algo, stream=0) -> int:
+    return lib.sim_reduce_scatter(_ptr_array(in_ptrs), _ptr_array(out_ptrs), p, n_out_per_rank,
+                                  _code(DTYPES, dtype, "dtype"), _code(OPS, op, "op"),
+                                  _code(ALGOS, algo, "algo"), stream or None)
+
+
+def sim_all_gather(in_ptrs, out_ptrs, p, n_in_per_rank, dtype, algo, stream=0) -> int:
+    return lib.sim_all_gather(_ptr_array(in_ptrs), _ptr_array(out_ptrs), p, n_in_per_rank,
+                              _code(DTYPES, dtype, "dtype"), _code(ALGOS, algo, "algo"), stream or None)
+
+
+def sim_select(p: int, n: int, dtype, op="sum"):
+    a, us = ctypes.c_int(0), ctypes.c_double(0)
+    _check(lib.sim_select(p, n, _code(DTYPES, dtype, "dtype"), _code(OPS, op, "op"), ctypes.byref(a),
+                          ctypes.byref(us)), "sim_select")
+    return ALGO_NAMES[a.value], us.value
+
+
+def sim_last_algo() -> Optional[str]:
+    return ALGO_NAMES.get(lib.sim_last_algo())
+
+
+def sim_model_load(path: str) -> None:
+    _check(lib.sim_model_load(path.encode()), f"sim_model_load({path})")
+
+
+def sim_model_predict(algo, p: int, dtype, bytes_per_rank: float) -> float:
+    us = ctypes.c_double(0)
+    _check(lib.sim_model_predict(_code(ALGOS, algo, "algo"), p, _code(DTYPES, dtype, "dtype"),
+                                 float(bytes_per_rank), ctypes.byref(us)), "sim_model_predict")
+    return us.value
+
+
+def sim_model_set(algo, alpha_us: float, steps: float, bytes_factor: float, gbps: float) -> None:
+    _check(lib.sim_model_set(_code(ALGOS, algo, "algo"), alpha_us, steps, bytes_factor, gbps), "sim_model_set")
+
+
+def sim_model_reset() -> None:
+    _check(lib.sim_model_reset(), "sim_model_reset")
+
+
+def sim_check_error(stream=0) -> int:
+    """Returns the status (SIM_OK or SIM_ERR_TIMEOUT) without raising."""
+    return lib.sim_check_error(stream or None)
+
+
+def sim_schedule_info(algo, p: int):
+    ns, nx = ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib.sim_schedule_info(_code(ALGOS, algo, "algo"), p, ctypes.byref(ns), ctypes.byref(nx)),
+           "sim_schedule_info")
+    return ns.value, nx.value
+
+
+def sim_schedule_xfers(algo, p: int, step: int):
+    buf = (ctypes.c_int * (4 * 64))()
+    cnt = ctypes.c_int(0)
+    _check(lib.sim_schedule_xfers(_code(ALGOS, algo, "algo"), p, step, buf, 64, ctypes.byref(cnt)),
+           "sim_schedule_xfers")
+    return [tuple(buf[4 * k:4 * k + 4]) for k in range(cnt.value)]
+
+
+def sim_schedule_state(algo, p: int, after_steps: int):
+    m = (ctypes.c_uint32 * (p * p))()
+    _check(lib.sim_schedule_state(_code(ALGOS, algo, "algo"), p, after_steps, m), "sim_schedule_state")
+    return [[m[r * p + c] for c in range(p)] for r in range(p)]
+
+
+def sim_verify_schedule(algo, p: int):
+    buf = ctypes.create_string_buffer(512)
+    st = lib.sim_verify_schedule(_code(ALGOS, algo, "algo"), p, buf, 512)
+    return st, buf.value.decode()
+
+
+def sim_verify_custom(algo, p: int, steps: List[List[tuple]]):
+    counts = (ctypes.c_int * max(1, len(steps)))(*[len(s) for s in steps])
+    flat = [v for s in steps for x in s for v in x]
+    xf = (ctypes.c_int * max(1, len(flat)))(*flat)
+    buf = ctypes.create_string_buffer(512)
+    st = lib.sim_verify_custom(_code(ALGOS, algo, "algo"), p, len(steps), counts, xf, buf, 512)
+    return st, buf.value.decode()
+
+
+def sim_debug_set(key, value: int) -> None:
+    _check(lib.sim_debug_set(_code(DEBUG, key, "debug key"), int(value) & (2 ** 64 - 1)), "sim_debug_set")
+
+
+def sim_debug_get(key) -> int:
+    v = ctypes.c_uint64(0)
+    _check(lib.sim_debug_get(_code(DEBUG, key, "debug key"), ctypes.byref(v)), "sim_debug_get")
+    return v.value
+
+
+def sim_status_string(status: int) -> str:
+    return lib.sim_status_string(status).decode()
+
+
+def sim_version() -> int:
+    return lib.sim_version()
+
+
+# ---- torch tensor helpers (marshalling only) --------------------------------------
+def _dtype_name(t) -> str:
+    import torch as _t
+    m = {_t.int32: "int32", _t.float32: "fp32", _t.float16: "fp16", _t.bfloat16: "bf16"}
+    if t.dtype not in m:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream(stream) -> int:
+    import torch as _t
+    s = stream if stream is not None else _t.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptrs(ts) -> List[int]:
+    out = []
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+        out.append(t.data_ptr())
+    return out
+
+
+def allreduce(inputs: Sequence, outputs: Optional[Sequence] = None, op="sum", algo="auto", stream=None):
+    """All-reduce p same-shaped device tensors (outputs=None: in place)."""
+    outputs = list(inputs) if outputs is None else list(outputs)
+    dt = _dtype_name(inputs[0])
+    st = sim_allreduce(_ptrs(inputs), _ptrs(outputs), len(inputs), inputs[0].numel(), dt, op, algo,
+                       _stream(stream))
+    _check(st, "sim_allreduce")
+    return outputs
+
+
+def reduce_scatter(inputs: Sequence, outputs: Sequence, op="sum", algo="auto", stream=None):
+    dt = _dtype_name(inputs[0])
+    st = sim_reduce_scatter(_ptrs(inputs), _ptrs(outputs), len(inputs), outputs[0].numel(), dt, op, algo,
+                            _stream(stream))
+    _check(st, "sim_reduce_scatter")
+    return outputs
+
+
+def all_gather(inputs: Sequence, outputs: Sequence, algo="auto", stream=None):
+    dt = _dtype_name(inputs[0])
+    st = sim_all_gather(_ptrs(inputs), _ptrs(outputs), len(inputs), inputs[0].numel(), dt, algo,
+                        _stream(stream))
+    _check(st, "sim_all_gather")
+    return outputs

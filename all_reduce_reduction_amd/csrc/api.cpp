@@ -1,0 +1,837 @@
+// api.cpp -- the C ABI of libsimar.so: argument validation, the library
+// context (scratch, LL buffer, epoch, device error word), schedule-driven
+// kernel launches and the selector.
+//
+// Validation mirrors the conditions under which the MSCCL runtime refuses
+// to run a custom algorithm ("MSCCL, in depth ...", section "How the runtime
+// decides to use your algorithm": op, collective, in-place-ness, rank
+// count, divisibility, size window), except that a refusal here is an
+// explicit error status and never a silent fallback to another schedule.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "schedule.h"
+#include "select.h"
+#include "simar.h"
+
+namespace simar {
+namespace {
+
+constexpr int kVersion = 1;
+constexpr int kWgPerCu = 8;  // default workgroups per CU for bulk kernels
+
+struct Ctx {
+  bool init = false;
+  int device = 0;
+  int p_max = 0;
+  int cu_count = 256;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  unsigned long long* ll = nullptr;
+  int64_t ll_stride = 0;  // packets per rank
+  int* err = nullptr;
+  uint32_t epoch = 0;
+  unsigned long long spin_limit = 1ull << 22;
+  uint32_t wait_skew = 0;
+  int log = 0;
+  int force_wg = 0;
+  int unroll = 2;
+  int last_algo = -1;
+  int env_algo = 0;
+  int ll_occ[4][5] = {};
+  Model model = default_model();
+};
+
+Ctx g;
+
+int esize_of(int dtype) { return (dtype == SIM_FP16 || dtype == SIM_BF16) ? 2 : 4; }
+const char* algo_name(int a) {
+  static const char* n[] = {"auto", "ring", "allpairs", "oneshot", "oneshot_ll"};
+  return (a >= 0 && a < 5) ? n[a] : "?";
+}
+
+int64_t chunk_lo(int64_t n, int p, int c) { return (int64_t)(((__int128)c * n) / p); }
+
+int hip_err(hipError_t e) { return e == hipSuccess ? SIM_OK : SIM_ERR_HIP; }
+
+// ---- validation -------------------------------------------------------------
+struct Range {
+  uintptr_t lo, hi;
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_scalars(int p, int dtype, int op, bool need_op) {
+  if (!g.init) return SIM_ERR_NOT_INIT;
+  if (p < 2 || p > g.p_max) return SIM_ERR_INVALID_ARG;
+  if (dtype < SIM_INT32 || dtype > SIM_BF16) return SIM_ERR_INVALID_ARG;
+  if (need_op && (op < SIM_SUM || op > SIM_AVG)) return SIM_ERR_INVALID_ARG;
+  return SIM_OK;
+}
+
+// in-place iff out == in + inplace_off(r) for every rank (mixing is an error)
+int check_buffers(const void* const* in, void* const* out, int p, size_t in_bytes, size_t out_bytes,
+                  const std::vector<size_t>& inplace_off, bool* inplace) {
+  if (!in || !out) return SIM_ERR_INVALID_ARG;
+  int n_inplace = 0;
+  for (int r = 0; r < p; r++) {
+    if (!in[r] || !out[r]) return SIM_ERR_INVALID_ARG;
+    if (((uintptr_t)in[r] | (uintptr_t)out[r]) & 15u) return SIM_ERR_ALIGN;
+    if ((const char*)in[r] == (const char*)out[r] + inplace_off[r]) n_inplace++;
+  }
+  if (n_inplace != 0 && n_inplace != p) return SIM_ERR_INVALID_ARG;
+  *inplace = (n_inplace == p);
+  std::vector<Range> ins(p), outs(p);
+  for (int r = 0; r < p; r++) {
+    ins[r] = {(uintptr_t)in[r], (uintptr_t)in[r] + in_bytes};
+    outs[r] = {(uintptr_t)out[r], (uintptr_t)out[r] + out_bytes};
+  }
+  for (int r = 0; r < p; r++) {
+    for (int q = 0; q < p; q++) {
+      if (q != r && overlap(outs[r], outs[q])) return SIM_ERR_ALIAS;
+      if (*inplace) {
+        if (q != r && overlap(outs[r], ins[q])) return SIM_ERR_ALIAS;
+      } else if (overlap(outs[r], ins[q])) {
+        return SIM_ERR_ALIAS;
+      }
+    }
+  }
+  return SIM_OK;
+}
+
+// ---- scratch ------------------------------------------------------------------
+// Ring partial slots: [parity 0/1][rank] x (max chunk + 8) fp32/int32 values,
+// each slot rounded to 64 values so every slot starts 256-byte aligned.
+size_t slot_elems(size_t n, int p) {
+  const size_t e = (n + (size_t)p - 1) / (size_t)p + 8;
+  return (e + 63) / 64 * 64;
+}
+size_t scratch_need(size_t n, int p) { return 2 * (size_t)p * slot_elems(n, p) * 4; }
+
+int ensure_scratch(size_t bytes) {
+  if (bytes <= g.scratch_bytes) return SIM_OK;
+  if (g.scratch) {
+    if (hipDeviceSynchronize() != hipSuccess) return SIM_ERR_HIP;
+    if (hipFree(g.scratch) != hipSuccess) return SIM_ERR_HIP;
+    g.scratch = nullptr;
+    g.scratch_bytes = 0;
+  }
+  if (hipMalloc(&g.scratch, bytes) != hipSuccess) {
+    g.scratch = nullptr;
+    (void)hipGetLastError();
+    return SIM_ERR_NOMEM;
+  }
+  g.scratch_bytes = bytes;
+  return SIM_OK;
+}
+
+float inv_p_of(int p) {
+  volatile float one = 1.0f, fp = (float)p;
+  return one / fp;
+}
+
+int tiles_for(int64_t vecs_per_unit, int units, int unroll) {
+  const int64_t want = (vecs_per_unit + (int64_t)kBlock * unroll - 1) / ((int64_t)kBlock * unroll);
+  int64_t cap = g.force_wg > 0 ? std::max<int64_t>(1, g.force_wg / units)
+                               : std::max<int64_t>(1, (int64_t)g.cu_count * kWgPerCu / units);
+  if (g.force_wg > 0) return (int)cap;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, cap));
+}
+
+// ---- launch glue ----------------------------------------------------------------
+struct Call {
+  int coll, p, dtype, op, algo;
+  size_t n;            // elements per rank (AR: buffer; RS: input; AG: output)
+  const void* const* x;
+  void* const* y;
+  bool inplace;
+  hipStream_t s;
+};
+
+int run_fold(const Call& c, bool all_out, const std::vector<int64_t>& lo, const int64_t* out_shift) {
+  FoldArgs a;
+  std::memset(&a, 0, sizeof a);
+  const int V = 16 / esize_of(c.dtype);
+  int64_t maxchunk = 0;
+  for (int q = 0; q < c.p; q++) {
+    a.x[q] = c.x[q];
+    a.y[q] = c.y[q];
+    a.out_shift[q] = out_shift ? out_shift[q] : 0;
+    if (a.out_shift[q] % V == 0) a.vec_ok |= 1u << q;
+    maxchunk = std::max(maxchunk, lo[q + 1] - lo[q]);
+  }
+  for (int q = 0; q <= c.p; q++) a.lo[q] = lo[q];
+  a.p = c.p;
+  a.inv_p = inv_p_of(c.p);
+  const int unroll = (c.p == 8) ? g.unroll : 1;
+  a.tiles = tiles_for((maxchunk + V - 1) / V, c.p, unroll);
+  return hip_err(launch_fold(c.dtype, c.op, c.p, all_out, a, unroll, c.s));
+}
+
+int run_copy_step(const Call& c, const std::vector<CopyXfer>& xs) {
+  CopyArgs a;
+  std::memset(&a, 0, sizeof a);
+  const int e = esize_of(c.dtype), V = 16 / e;
+  int64_t maxlen = 0;
+  a.nx = (int)xs.size();
+  for (size_t k = 0; k < xs.size(); k++) {
+    a.x[k] = xs[k];
+    a.x[k].vec_ok = (xs[k].src_shift % V == 0) && (xs[k].dst_shift % V == 0);
+    maxlen = std::max(maxlen, xs[k].hi - xs[k].lo);
+  }
+  if (a.nx == 0) return SIM_OK;
+  a.tiles = tiles_for((maxlen + V - 1) / V, a.nx, 2);
+  return hip_err(launch_copy(e, a, c.s));
+}
+
+// Ring reduce-scatter half.  final_out_chunk: outputs are chunk-sized (RS).
+int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_chunk,
+                const std::vector<int64_t>& lo) {
+  const int p = c.p, e = esize_of(c.dtype), V = 16 / e;
+  // 32-bit all-reduce keeps partials in the receiving rank's output (a chunk
+  // it does not own yet); otherwise partials live in fp32/int32 scratch slots.
+  const bool part_in_y = (e == 4) && !final_out_chunk;
+  const size_t se = slot_elems(c.n, p);
+  if (!part_in_y && p > 2) {
+    int rc = ensure_scratch(scratch_need(c.n, p));
+    if (rc) return rc;
+  }
+  auto slot = [&](int parity, int rank) -> void* {
+    return (char*)g.scratch + ((size_t)parity * p + rank) * se * 4;
+  };
+  int64_t maxchunk = 0;
+  for (int q = 0; q < p; q++) maxchunk = std::max(maxchunk, lo[q + 1] - lo[q]);
+  for (int st = 0; st < nsteps; st++) {
+    RingArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.nx = (int)sch.steps[st].size();
+    a.p = p;
+    a.inv_p = inv_p_of(p);
+    const bool first = (st == 0), last = (st == nsteps - 1);
+    for (int k = 0; k < a.nx; k++) {
+      const Xfer& xf = sch.steps[st][k];
+      RingXfer& x = a.x[k];
+      const int64_t l = lo[xf.chunk], h = lo[xf.chunk + 1];
+      const int64_t slot_shift = l - (l % 8);
+      x.lo = l;
+      x.hi = h;
+      if (first) {
+        x.a = c.x[xf.src];
+        x.a_shift = 0;
+      } else if (part_in_y) {
+        x.a = c.y[xf.src];
+        x.a_shift = 0;
+      } else {
+        x.a = slot((st - 1) & 1, xf.src);
+        x.a_shift = slot_shift;
+      }
+      x.b = c.x[xf.dst];
+      if (last) {
+        x.d = c.y[xf.dst];
+        x.d_shift = final_out_chunk ? l : 0;
+      } else if (part_in_y) {
+        x.d = c.y[xf.dst];
+        x.d_shift = 0;
+      } else {
+        x.d = slot(st & 1, xf.dst);
+        x.d_shift = slot_shift;
+      }
+      x.vec_ok = (x.a_shift % V == 0) && (x.d_shift % V == 0);
+    }
+    a.tiles = tiles_for((maxchunk + V - 1) / V, a.nx, 2);
+    int rc = hip_err(launch_ring_reduce(c.dtype, c.op, !first, last, a, c.s));
+    if (rc) return rc;
+  }
+  return SIM_OK;
+}
+
+int run_allreduce(const Call& c) {
+  std::string diag;
+  const Schedule* sch = cached_schedule(COLL_ALLREDUCE, c.algo, c.p, &diag);
+  if (!sch) return SIM_ERR_VERIFY;
+  const int p = c.p;
+  std::vector<int64_t> lo(p + 1);
+  for (int q = 0; q <= p; q++) lo[q] = chunk_lo((int64_t)c.n, p, q);
+  switch (c.algo) {
+    case SIM_ALGO_ONESHOT:
+      return run_fold(c, true, lo, nullptr);
+    case SIM_ALGO_ALLPAIRS: {
+      int rc = run_fold(c, false, lo, nullptr);  // step 1: GATHER_REDUCE into each owner
+      if (rc) return rc;
+      std::vector<CopyXfer> xs;                  // step 2: FANOUT from each owner
+      for (const Xfer& xf : sch->steps[1]) {
+        CopyXfer x;
+        std::memset(&x, 0, sizeof x);
+        x.src = c.y[xf.src];
+        for (int r = 0; r < p; r++)
+          if (r != xf.src) x.dst[x.ndst++] = c.y[r];
+        x.lo = lo[xf.chunk];
+        x.hi = lo[xf.chunk + 1];
+        xs.push_back(x);
+      }
+      return run_copy_step(c, xs);
+    }
+    case SIM_ALGO_RING: {
+      int rc = run_ring_rs(c, *sch, p - 1, false, lo);
+      if (rc) return rc;
+      for (int st = p - 1; st < 2 * (p - 1); st++) {
+        std::vector<CopyXfer> xs;
+        for (const Xfer& xf : sch->steps[st]) {
+          CopyXfer x;
+          std::memset(&x, 0, sizeof x);
+          x.src = c.y[xf.src];
+          x.dst[x.ndst++] = c.y[xf.dst];
+          x.lo = lo[xf.chunk];
+          x.hi = lo[xf.chunk + 1];
+          xs.push_back(x);
+        }
+        rc = run_copy_step(c, xs);
+        if (rc) return rc;
+      }
+      return SIM_OK;
+    }
+    case SIM_ALGO_ONESHOT_LL: {
+      LLArgs a;
+      std::memset(&a, 0, sizeof a);
+      const int e = esize_of(c.dtype);
+      uint32_t epoch = g.epoch + 1;
+      if (epoch == 0) {  // wrapped: no packet may carry a flag the next calls use
+        int rc = hip_err(launch_fill64(g.ll, 0ull, (int64_t)g.p_max * g.ll_stride, c.s));
+        if (rc) return rc;
+        epoch = 1;
+      }
+      g.epoch = epoch;
+      for (int q = 0; q < p; q++) {
+        a.x[q] = c.x[q];
+        a.y[q] = c.y[q];
+      }
+      for (int q = 0; q <= p; q++) a.lo[q] = lo[q];
+      a.ll = g.ll;
+      a.ll_stride = g.ll_stride;
+      a.n = (int64_t)c.n;
+      a.nwords = ((int64_t)c.n * e + 3) / 4;
+      a.tile_words = kBlock;
+      a.ntiles = (a.nwords + a.tile_words - 1) / a.tile_words;
+      a.spin_limit = g.spin_limit;
+      a.err = g.err;
+      a.p = p;
+      a.epoch = epoch;
+      a.wait_epoch = epoch + g.wait_skew;
+      a.shift = a.ntiles > 1 ? 1 : 0;
+      a.inv_p = inv_p_of(p);
+      int& occ = g.ll_occ[c.dtype][c.op];
+      if (occ == 0) occ = ll_blocks_per_cu(c.dtype, c.op);
+      const int64_t resident = (int64_t)occ * g.cu_count;
+      const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(a.ntiles, resident));
+      return hip_err(launch_ll(c.dtype, c.op, a, grid, c.s));
+    }
+  }
+  return SIM_ERR_INVALID_ARG;
+}
+
+int run_reduce_scatter(const Call& c) {
+  std::string diag;
+  const Schedule* sch = cached_schedule(COLL_REDUCE_SCATTER, c.algo, c.p, &diag);
+  if (!sch) return SIM_ERR_VERIFY;
+  const int p = c.p;
+  std::vector<int64_t> lo(p + 1);
+  for (int q = 0; q <= p; q++) lo[q] = chunk_lo((int64_t)c.n, p, q);
+  if (c.algo == SIM_ALGO_ALLPAIRS) {
+    std::vector<int64_t> shift(p);
+    for (int q = 0; q < p; q++) shift[q] = lo[q];
+    return run_fold(c, false, lo, shift.data());
+  }
+  return run_ring_rs(c, *sch, p - 1, true, lo);
+}
+
+int run_all_gather(const Call& c) {
+  std::string diag;
+  const Schedule* sch = cached_schedule(COLL_ALL_GATHER, c.algo, c.p, &diag);
+  if (!sch) return SIM_ERR_VERIFY;
+  const int p = c.p;
+  const int64_t nin = (int64_t)c.n / p;
+  for (size_t st = 0; st < sch->steps.size(); st++) {
+    // merge the step's transfers that share (source rank, block) into one
+    // multi-destination copy: one load, several stores
+    std::vector<CopyXfer> xs;
+    std::vector<std::pair<int, int>> keys;
+    for (const Xfer& xf : sch->steps[st]) {
+      const int64_t l = xf.chunk * nin, h = l + nin;
+      // the source block: the rank's own input for its own block at step 0
+      // (ring) or for every block (direct); a finished output block otherwise
+      const bool from_input = (c.algo == SIM_ALGO_ALLPAIRS) || (st == 0);
+      auto key = std::make_pair(xf.src, xf.chunk);
+      size_t idx = std::find(keys.begin(), keys.end(), key) - keys.begin();
+      if (idx == keys.size()) {
+        CopyXfer x;
+        std::memset(&x, 0, sizeof x);
+        if (from_input) {
+          x.src = c.x[xf.src];
+          x.src_shift = l;
+        } else {
+          x.src = c.y[xf.src];
+          x.src_shift = 0;
+        }
+        x.lo = l;
+        x.hi = h;
+        xs.push_back(x);
+        keys.push_back(key);
+      }
+      CopyXfer& x = xs[idx];
+      auto add_dst = [&](int r) {
+        void* d = c.y[r];
+        // in place, the owner's block already holds the data
+        if (c.inplace && (const char*)d + l * esize_of(c.dtype) == (const char*)c.x[xf.src]) return;
+        x.dst[x.ndst++] = d;
+      };
+      if (xf.kind == XK_FANOUT) {
+        for (int r = 0; r < p; r++) add_dst(r);  // every rank's output, the owner's included
+      } else {
+        add_dst(xf.dst);
+      }
+    }
+    xs.erase(std::remove_if(xs.begin(), xs.end(), [](const CopyXfer& x) { return x.ndst == 0; }), xs.end());
+    int rc = run_copy_step(c, xs);
+    if (rc) return rc;
+  }
+  return SIM_OK;
+}
+
+// legal candidates for AUTO / explicit requests
+bool legal(int coll, int algo, int p, size_t n, int dtype) {
+  (void)p;
+  if (coll == COLL_ALLREDUCE) {
+    if (algo == SIM_ALGO_ONESHOT_LL) return n * (size_t)esize_of(dtype) <= SIM_LL_MAX_BYTES_PER_RANK;
+    return algo >= SIM_ALGO_RING && algo <= SIM_ALGO_ONESHOT;
+  }
+  return algo == SIM_ALGO_RING || algo == SIM_ALGO_ALLPAIRS;
+}
+
+int pick(int coll, int p, size_t n, int dtype, int* algo, double* us) {
+  int best = -1;
+  double bt = 0;
+  for (int a = SIM_ALGO_RING; a <= SIM_ALGO_ONESHOT_LL; a++) {
+    if (!legal(coll, a, p, n, dtype)) continue;
+    const double t = model_predict(g.model, coll, a, p, (double)n, esize_of(dtype));
+    if (best < 0 || t < bt) {
+      best = a;
+      bt = t;
+    }
+  }
+  if (best < 0) return SIM_ERR_UNSUPPORTED;
+  *algo = best;
+  if (us) *us = bt;
+  return SIM_OK;
+}
+
+int resolve_algo(int coll, int p, size_t n, int dtype, int* algo, double* us) {
+  if (*algo < SIM_ALGO_AUTO || *algo > SIM_ALGO_ONESHOT_LL) return SIM_ERR_INVALID_ARG;
+  if (*algo == SIM_ALGO_AUTO && coll == COLL_ALLREDUCE && g.env_algo > 0) *algo = g.env_algo;
+  if (*algo == SIM_ALGO_AUTO) return pick(coll, p, n, dtype, algo, us);
+  if (!legal(coll, *algo, p, n, dtype)) return SIM_ERR_UNSUPPORTED;
+  if (us) *us = model_predict(g.model, coll, *algo, p, (double)n, esize_of(dtype));
+  return SIM_OK;
+}
+
+void log_call(const char* what, const Call& c, double us) {
+  if (!g.log) return;
+  std::fprintf(stderr, "[simar] %s: %zu bytes/rank p %d -> algo %s steps %d predicted %.2f us\n", what,
+               c.n * (size_t)esize_of(c.dtype), c.p, algo_name(c.algo),
+               model_launches(c.coll, c.algo, c.p), us);
+}
+
+int parse_algo_env(const char* v) {
+  if (!v) return 0;
+  for (int a = 1; a < 5; a++)
+    if (!std::strcmp(v, algo_name(a))) return a;
+  return 0;
+}
+
+}  // namespace
+}  // namespace simar
+
+using namespace simar;
+
+extern "C" {
+
+int sim_version(void) { return kVersion; }
+
+const char* sim_status_string(int status) {
+  switch (status) {
+    case SIM_OK: return "ok";
+    case SIM_ERR_INVALID_ARG: return "invalid argument";
+    case SIM_ERR_UNSUPPORTED: return "unsupported by the requested algorithm";
+    case SIM_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case SIM_ERR_ALIAS: return "output overlaps an input or another output";
+    case SIM_ERR_NOMEM: return "out of device memory for library scratch";
+    case SIM_ERR_HIP: return "HIP runtime error";
+    case SIM_ERR_TIMEOUT: return "a bounded device-side wait expired";
+    case SIM_ERR_VERIFY: return "schedule failed verification";
+    case SIM_ERR_NOT_INIT: return "library not initialised";
+  }
+  return "unknown status";
+}
+
+int sim_finalize(void) {
+  if (!g.init) return SIM_OK;
+  // teardown is best effort: every allocation is released even if one call fails
+  (void)hipSetDevice(g.device);
+  (void)hipDeviceSynchronize();
+  if (g.scratch) (void)hipFree(g.scratch);
+  if (g.ll) (void)hipFree(g.ll);
+  if (g.err) (void)hipFree(g.err);
+  Model keep = g.model;
+  g = Ctx();
+  g.model = keep;
+  return SIM_OK;
+}
+
+int sim_init(int device, int p_max, size_t max_bytes_per_rank) {
+  if (p_max < 2 || p_max > SIM_MAX_RANKS) return SIM_ERR_INVALID_ARG;
+  sim_finalize();
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) {
+    (void)hipGetLastError();
+    return device < 0 ? SIM_ERR_INVALID_ARG : SIM_ERR_HIP;
+  }
+  if (hipSetDevice(device) != hipSuccess) return SIM_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return SIM_ERR_HIP;
+  g.device = device;
+  g.p_max = p_max;
+  g.cu_count = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+  if (hipMalloc(&g.err, 256) != hipSuccess) return SIM_ERR_NOMEM;
+  if (hipMemset(g.err, 0, 256) != hipSuccess) return SIM_ERR_HIP;
+  g.ll_stride = (int64_t)(2 * SIM_LL_MAX_BYTES_PER_RANK / 8);  // packets per rank
+  if (hipMalloc(&g.ll, (size_t)p_max * g.ll_stride * 8) != hipSuccess) {
+    sim_finalize();
+    return SIM_ERR_NOMEM;
+  }
+  if (launch_fill64(g.ll, 0ull, (int64_t)p_max * g.ll_stride, nullptr) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    sim_finalize();
+    return SIM_ERR_HIP;
+  }
+  g.init = true;
+  if (max_bytes_per_rank > 0) {
+    const size_t n = max_bytes_per_rank / 2;  // 16-bit elements need the most slots
+    size_t need = 0;
+    for (int p = 2; p <= p_max; p++) need = std::max(need, scratch_need(n, p));
+    int rc = ensure_scratch(need);
+    if (rc) {
+      sim_finalize();
+      return rc;
+    }
+  }
+  const char* dbg = std::getenv("SIM_DEBUG");
+  g.log = (dbg && dbg[0] == '1') ? 1 : 0;
+  g.env_algo = parse_algo_env(std::getenv("SIM_ALGO"));
+  const char* calib = std::getenv("SIM_CALIB");
+  if (calib && calib[0]) {
+    std::string err;
+    if (!model_load_json(calib, &g.model, &err) && g.log)
+      std::fprintf(stderr, "[simar] SIM_CALIB %s not loaded: %s\n", calib, err.c_str());
+  }
+  return SIM_OK;
+}
+
+int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size_t n, int dtype,
+                  int op, int algo, void* stream) {
+  int rc = check_scalars(p, dtype, op, true);
+  if (rc) return rc;
+  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_ONESHOT_LL) return SIM_ERR_INVALID_ARG;
+  if (n == 0) return SIM_OK;
+  const size_t e = (size_t)esize_of(dtype);
+  if (n > ((size_t)1 << 46) / e) return SIM_ERR_INVALID_ARG;
+  bool inplace = false;
+  rc = check_buffers(in_ptrs, out_ptrs, p, n * e, n * e, std::vector<size_t>(p, 0), &inplace);
+  if (rc) return rc;
+  double us = 0;
+  rc = resolve_algo(COLL_ALLREDUCE, p, n, dtype, &algo, &us);
+  if (rc) return rc;
+  if (hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+  Call c{COLL_ALLREDUCE, p, dtype, op, algo, n, in_ptrs, out_ptrs, inplace, (hipStream_t)stream};
+  rc = run_allreduce(c);
+  if (rc) return rc;
+  g.last_algo = algo;
+  log_call("AllReduce", c, us);
+  return SIM_OK;
+}
+
+int sim_reduce_scatter(const void* const* in_ptrs, void* const* out_ptrs, int p, size_t n_out,
+                       int dtype, int op, int algo, void* stream) {
+  int rc = check_scalars(p, dtype, op, true);
+  if (rc) return rc;
+  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_ONESHOT_LL) return SIM_ERR_INVALID_ARG;
+  if (n_out == 0) return SIM_OK;
+  const size_t e = (size_t)esize_of(dtype);
+  if (n_out > ((size_t)1 << 46) / e / (size_t)p) return SIM_ERR_INVALID_ARG;
+  if (algo == SIM_ALGO_AUTO) algo = SIM_ALGO_ALLPAIRS;
+  if (algo != SIM_ALGO_RING && algo != SIM_ALGO_ALLPAIRS) return SIM_ERR_UNSUPPORTED;
+  std::vector<size_t> off(p);
+  for (int r = 0; r < p; r++) off[r] = 0;
+  // in place: out[r] is chunk r of in[r]  (in[r] == out[r] - r*chunk)
+  bool inplace = false;
+  {
+    int n_inplace = 0;
+    if (!in_ptrs || !out_ptrs) return SIM_ERR_INVALID_ARG;
+    for (int r = 0; r < p; r++) {
+      if (!in_ptrs[r] || !out_ptrs[r]) return SIM_ERR_INVALID_ARG;
+      if ((const char*)out_ptrs[r] == (const char*)in_ptrs[r] + (size_t)r * n_out * e) n_inplace++;
+    }
+    if (n_inplace != 0 && n_inplace != p) return SIM_ERR_INVALID_ARG;
+    inplace = (n_inplace == p);
+  }
+  if (inplace) {
+    for (int r = 0; r < p; r++)
+      if (((uintptr_t)in_ptrs[r] | (uintptr_t)out_ptrs[r]) & 15u) return SIM_ERR_ALIGN;
+    // the input buffers must not overlap each other
+    for (int r = 0; r < p; r++)
+      for (int q = r + 1; q < p; q++)
+        if (overlap({(uintptr_t)in_ptrs[r], (uintptr_t)in_ptrs[r] + p * n_out * e},
+                    {(uintptr_t)in_ptrs[q], (uintptr_t)in_ptrs[q] + p * n_out * e}))
+          return SIM_ERR_ALIAS;
+  } else {
+    bool ip2 = false;
+    rc = check_buffers(in_ptrs, out_ptrs, p, (size_t)p * n_out * e, n_out * e, off, &ip2);
+    if (rc) return rc;
+    if (ip2) return SIM_ERR_ALIAS;
+  }
+  if (hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+  Call c{COLL_REDUCE_SCATTER, p, dtype, op, algo, (size_t)p * n_out, in_ptrs, out_ptrs, inplace,
+         (hipStream_t)stream};
+  rc = run_reduce_scatter(c);
+  if (rc) return rc;
+  g.last_algo = algo;
+  log_call("ReduceScatter", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e));
+  return SIM_OK;
+}
+
+int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p, size_t n_in, int dtype,
+                   int algo, void* stream) {
+  int rc = check_scalars(p, dtype, SIM_SUM, false);
+  if (rc) return rc;
+  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_ONESHOT_LL) return SIM_ERR_INVALID_ARG;
+  if (n_in == 0) return SIM_OK;
+  const size_t e = (size_t)esize_of(dtype);
+  if (n_in > ((size_t)1 << 46) / e / (size_t)p) return SIM_ERR_INVALID_ARG;
+  if (algo == SIM_ALGO_AUTO) algo = SIM_ALGO_ALLPAIRS;
+  if (algo != SIM_ALGO_RING && algo != SIM_ALGO_ALLPAIRS) return SIM_ERR_UNSUPPORTED;
+  // in place: in[r] is block r of out[r]
+  std::vector<size_t> off(p);
+  for (int r = 0; r < p; r++) off[r] = (size_t)r * n_in * e;
+  bool inplace = false;
+  if (!in_ptrs || !out_ptrs) return SIM_ERR_INVALID_ARG;
+  {
+    int n_inplace = 0;
+    for (int r = 0; r < p; r++) {
+      if (!in_ptrs[r] || !out_ptrs[r]) return SIM_ERR_INVALID_ARG;
+      if (((uintptr_t)in_ptrs[r] | (uintptr_t)out_ptrs[r]) & 15u) return SIM_ERR_ALIGN;
+      if ((const char*)in_ptrs[r] == (const char*)out_ptrs[r] + off[r]) n_inplace++;
+    }
+    if (n_inplace != 0 && n_inplace != p) return SIM_ERR_INVALID_ARG;
+    inplace = (n_inplace == p);
+  }
+  {
+    std::vector<Range> outs(p), ins(p);
+    for (int r = 0; r < p; r++) {
+      outs[r] = {(uintptr_t)out_ptrs[r], (uintptr_t)out_ptrs[r] + (size_t)p * n_in * e};
+      ins[r] = {(uintptr_t)in_ptrs[r], (uintptr_t)in_ptrs[r] + n_in * e};
+    }
+    for (int r = 0; r < p; r++)
+      for (int q = 0; q < p; q++) {
+        if (q != r && overlap(outs[r], outs[q])) return SIM_ERR_ALIAS;
+        if (inplace ? (q != r && overlap(outs[r], ins[q])) : overlap(outs[r], ins[q])) return SIM_ERR_ALIAS;
+      }
+  }
+  if (hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+  Call c{COLL_ALL_GATHER, p, dtype, SIM_SUM, algo, (size_t)p * n_in, in_ptrs, out_ptrs, inplace,
+         (hipStream_t)stream};
+  rc = run_all_gather(c);
+  if (rc) return rc;
+  g.last_algo = algo;
+  log_call("AllGather", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e));
+  return SIM_OK;
+}
+
+int sim_select(int p, size_t n, int dtype, int op, int* algo_out, double* predicted_us) {
+  if (!algo_out) return SIM_ERR_INVALID_ARG;
+  if (p < 2 || p > SIM_MAX_RANKS) return SIM_ERR_INVALID_ARG;
+  if (dtype < SIM_INT32 || dtype > SIM_BF16 || op < SIM_SUM || op > SIM_AVG) return SIM_ERR_INVALID_ARG;
+  int a = SIM_ALGO_AUTO;
+  double us = 0;
+  int rc = resolve_algo(COLL_ALLREDUCE, p, n, dtype, &a, &us);
+  if (rc) return rc;
+  *algo_out = a;
+  if (predicted_us) *predicted_us = us;
+  return SIM_OK;
+}
+
+int sim_last_algo(void) { return g.last_algo; }
+
+int sim_model_load(const char* json_path) {
+  if (!json_path) return SIM_ERR_INVALID_ARG;
+  std::string err;
+  if (!model_load_json(json_path, &g.model, &err)) {
+    if (g.log) std::fprintf(stderr, "[simar] model %s not loaded: %s\n", json_path, err.c_str());
+    return SIM_ERR_INVALID_ARG;
+  }
+  return SIM_OK;
+}
+
+int sim_model_predict(int algo, int p, int dtype, double bytes_per_rank, double* us_out) {
+  if (!us_out || algo < SIM_ALGO_RING || algo > SIM_ALGO_ONESHOT_LL || p < 2 || p > SIM_MAX_RANKS ||
+      dtype < SIM_INT32 || dtype > SIM_BF16 || !(bytes_per_rank >= 0))
+    return SIM_ERR_INVALID_ARG;
+  const int e = esize_of(dtype);
+  *us_out = model_predict(g.model, COLL_ALLREDUCE, algo, p, bytes_per_rank / e, e);
+  return SIM_OK;
+}
+
+int sim_model_set(int algo, double alpha_us, double steps, double bytes_factor, double gbps) {
+  if (algo < SIM_ALGO_RING || algo > SIM_ALGO_ONESHOT_LL || !(gbps > 0) || !(alpha_us >= 0))
+    return SIM_ERR_INVALID_ARG;
+  AlgoModel& m = g.model.a[algo];
+  m.alpha_us = alpha_us;
+  m.gbps = gbps;
+  m.steps = steps;
+  m.bytes_factor = bytes_factor;
+  g.model.source = "sim_model_set";
+  return SIM_OK;
+}
+
+int sim_model_reset(void) {
+  g.model = default_model();
+  return SIM_OK;
+}
+
+int sim_check_error(void* stream) {
+  if (!g.init) return SIM_ERR_NOT_INIT;
+  if (hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SIM_ERR_HIP;
+  int word = 0;
+  if (hipMemcpy(&word, g.err, sizeof word, hipMemcpyDeviceToHost) != hipSuccess) return SIM_ERR_HIP;
+  if (word != 0) {
+    if (hipMemset(g.err, 0, sizeof word) != hipSuccess) return SIM_ERR_HIP;
+    return word;
+  }
+  return SIM_OK;
+}
+
+int sim_schedule_info(int algo, int p, int* nsteps, int* nxfers) {
+  Schedule s;
+  if (!lower(COLL_ALLREDUCE, algo, p, &s)) return SIM_ERR_INVALID_ARG;
+  if (nsteps) *nsteps = (int)s.steps.size();
+  if (nxfers) *nxfers = s.nxfers();
+  return SIM_OK;
+}
+
+int sim_schedule_xfers(int algo, int p, int step, int* out, int max, int* count) {
+  Schedule s;
+  if (!lower(COLL_ALLREDUCE, algo, p, &s) || step < 0 || step >= (int)s.steps.size() || !count)
+    return SIM_ERR_INVALID_ARG;
+  int k = 0;
+  for (const Xfer& x : s.steps[step]) {
+    if (k >= max) break;
+    if (out) {
+      out[4 * k + 0] = x.kind;
+      out[4 * k + 1] = x.src;
+      out[4 * k + 2] = x.dst;
+      out[4 * k + 3] = x.chunk;
+    }
+    k++;
+  }
+  *count = k;
+  return SIM_OK;
+}
+
+int sim_schedule_state(int algo, int p, int after_steps, uint32_t* masks) {
+  Schedule s;
+  if (!masks || !lower(COLL_ALLREDUCE, algo, p, &s)) return SIM_ERR_INVALID_ARG;
+  std::string d;
+  return symbolic_state(s, after_steps, masks, &d) ? SIM_OK : SIM_ERR_INVALID_ARG;
+}
+
+static void put_diag(const std::string& d, char* diag, size_t len) {
+  if (!diag || len == 0) return;
+  std::snprintf(diag, len, "%s", d.c_str());
+}
+
+int sim_verify_schedule(int algo, int p, char* diag, size_t diag_len) {
+  Schedule s;
+  if (!lower(COLL_ALLREDUCE, algo, p, &s)) {
+    put_diag("no lowering for this (algo, p)", diag, diag_len);
+    return SIM_ERR_INVALID_ARG;
+  }
+  std::string d;
+  const bool ok = verify(s, &d);
+  put_diag(d, diag, diag_len);
+  return ok ? SIM_OK : SIM_ERR_VERIFY;
+}
+
+int sim_verify_custom(int algo, int p, int nsteps, const int* counts, const int* xfers, char* diag,
+                      size_t diag_len) {
+  if (p < 2 || p > SIM_MAX_RANKS || nsteps < 0 || (nsteps > 0 && (!counts || !xfers)) ||
+      algo < SIM_ALGO_RING || algo > SIM_ALGO_ONESHOT_LL)
+    return SIM_ERR_INVALID_ARG;
+  Schedule s;
+  s.algo = algo;
+  s.p = p;
+  s.coll = COLL_ALLREDUCE;
+  s.rounds = (algo == SIM_ALGO_RING) ? nsteps : 2;
+  int k = 0;
+  for (int st = 0; st < nsteps; st++) {
+    if (counts[st] < 0) return SIM_ERR_INVALID_ARG;
+    std::vector<Xfer> v;
+    for (int j = 0; j < counts[st]; j++, k++)
+      v.push_back({xfers[4 * k], xfers[4 * k + 1], xfers[4 * k + 2], xfers[4 * k + 3]});
+    s.steps.push_back(v);
+  }
+  std::string d;
+  const bool ok = verify(s, &d);
+  put_diag(d, diag, diag_len);
+  return ok ? SIM_OK : SIM_ERR_VERIFY;
+}
+
+int sim_debug_set(int key, uint64_t value) {
+  switch (key) {
+    case SIM_DEBUG_EPOCH: g.epoch = (uint32_t)value; return SIM_OK;
+    case SIM_DEBUG_SPIN_LIMIT: g.spin_limit = value; return SIM_OK;
+    case SIM_DEBUG_LL_WAIT_SKEW: g.wait_skew = (uint32_t)value; return SIM_OK;
+    case SIM_DEBUG_LOG: g.log = value ? 1 : 0; return SIM_OK;
+    case SIM_DEBUG_WORKGROUPS: g.force_wg = (int)value; return SIM_OK;
+    case SIM_DEBUG_UNROLL:
+      if (value != 1 && value != 2 && value != 4) return SIM_ERR_INVALID_ARG;
+      g.unroll = (int)value;
+      return SIM_OK;
+    case SIM_DEBUG_FILL_LL: {
+      if (!g.init) return SIM_ERR_NOT_INIT;
+      if (hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+      if (launch_fill64(g.ll, (unsigned long long)value, (int64_t)g.p_max * g.ll_stride, nullptr) != hipSuccess)
+        return SIM_ERR_HIP;
+      return hipDeviceSynchronize() == hipSuccess ? SIM_OK : SIM_ERR_HIP;
+    }
+  }
+  return SIM_ERR_INVALID_ARG;
+}
+
+int sim_debug_get(int key, uint64_t* value) {
+  if (!value) return SIM_ERR_INVALID_ARG;
+  switch (key) {
+    case SIM_DEBUG_EPOCH: *value = g.epoch; return SIM_OK;
+    case SIM_DEBUG_SPIN_LIMIT: *value = g.spin_limit; return SIM_OK;
+    case SIM_DEBUG_LL_WAIT_SKEW: *value = g.wait_skew; return SIM_OK;
+    case SIM_DEBUG_LOG: *value = (uint64_t)g.log; return SIM_OK;
+    case SIM_DEBUG_WORKGROUPS: *value = (uint64_t)g.force_wg; return SIM_OK;
+    case SIM_DEBUG_UNROLL: *value = (uint64_t)g.unroll; return SIM_OK;
+  }
+  return SIM_ERR_INVALID_ARG;
+}
+
+}  // extern "C"

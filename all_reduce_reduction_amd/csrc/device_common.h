@@ -1,0 +1,152 @@
+// device_common.h -- element types, reduction operators and 16-byte vector
+// access for the gfx950 kernels.
+//
+// Arithmetic ("Inside NCCL all-reduce", section "What all-reduce
+// promises": sum, prod, min, max, avg; avg pre-scales floating-point
+// contributions by 1/n as they are read and divides integer sums once at
+// the end):
+//   - fp16/bf16 are widened exactly to fp32 in VGPRs, accumulated in fp32
+//     and rounded once, to nearest even, when the result is written;
+//   - int32 sum/prod wrap modulo 2^32 (unsigned arithmetic);
+//   - min/max keep the accumulator unless the new operand is strictly
+//     smaller/larger: acc = (b < a) ? b : a.
+// The library is compiled with -ffp-contract=off so a multiply followed by
+// an add is never fused: each fp32 operation rounds on its own.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "simar.h"
+
+namespace simar {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Ty;
+template <> struct Ty<SIM_INT32> { typedef int32_t S; typedef int32_t A; static constexpr int E = 4; };
+template <> struct Ty<SIM_FP32>  { typedef float S;   typedef float A;   static constexpr int E = 4; };
+template <> struct Ty<SIM_FP16>  { typedef uint16_t S; typedef float A;  static constexpr int E = 2; };
+template <> struct Ty<SIM_BF16>  { typedef uint16_t S; typedef float A;  static constexpr int E = 2; };
+
+// elements per 16-byte vector of storage
+template <int DT> constexpr int epv() { return 16 / Ty<DT>::E; }
+
+// ---- 16-bit codecs ----------------------------------------------------------
+// The fp32 value is made opaque to the optimiser around each 16-bit
+// conversion.  Otherwise gfx950 instruction selection folds a final fp32
+// multiply or add together with the narrowing (or a widening together with
+// the next multiply) into one mixed-precision FMA with a +0 addend: that
+// rounds once instead of twice and turns -0 into +0, so the result would no
+// longer be "fp32 arithmetic, then one RNE narrowing".  The empty asm emits
+// no instruction.
+__device__ __forceinline__ float opaque(float f) {
+  asm("" : "+v"(f));
+  return f;
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  return opaque((float)__builtin_bit_cast(_Float16, (uint16_t)h));   // exact widening
+}
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)opaque(f));  // RNE (default mode)
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __builtin_bit_cast(float, h << 16);                 // exact widening
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)opaque(f));   // RNE
+}
+
+// storage bits -> accumulator value (widen; no avg scaling)
+template <int DT> __device__ __forceinline__ typename Ty<DT>::A widen_bits(uint32_t bits);
+template <> __device__ __forceinline__ int32_t widen_bits<SIM_INT32>(uint32_t b) { return (int32_t)b; }
+template <> __device__ __forceinline__ float widen_bits<SIM_FP32>(uint32_t b) { return __builtin_bit_cast(float, b); }
+template <> __device__ __forceinline__ float widen_bits<SIM_FP16>(uint32_t b) { return f16_bits_to_f32(b & 0xffffu); }
+template <> __device__ __forceinline__ float widen_bits<SIM_BF16>(uint32_t b) { return bf16_bits_to_f32(b & 0xffffu); }
+
+// accumulator value -> storage bits (RNE for 16-bit)
+template <int DT> __device__ __forceinline__ uint32_t narrow_bits(typename Ty<DT>::A v);
+template <> __device__ __forceinline__ uint32_t narrow_bits<SIM_INT32>(int32_t v) { return (uint32_t)v; }
+template <> __device__ __forceinline__ uint32_t narrow_bits<SIM_FP32>(float v) { return __builtin_bit_cast(uint32_t, v); }
+template <> __device__ __forceinline__ uint32_t narrow_bits<SIM_FP16>(float v) { return f32_to_f16_bits(v); }
+template <> __device__ __forceinline__ uint32_t narrow_bits<SIM_BF16>(float v) { return f32_to_bf16_bits(v); }
+
+// ---- reduction operators ------------------------------------------------------
+template <int DT, int OP> struct Op {
+  typedef typename Ty<DT>::A A;
+  // a contribution as it is read: fp avg scales by fp32(1/p)
+  static __device__ __forceinline__ A pre(A x, float inv_p) {
+    if constexpr (OP == SIM_AVG && DT != SIM_INT32) return x * inv_p;
+    else return x;
+  }
+  // acc (+) b
+  static __device__ __forceinline__ A comb(A a, A b) {
+    if constexpr (DT == SIM_INT32) {
+      if constexpr (OP == SIM_SUM || OP == SIM_AVG) return (int32_t)((uint32_t)a + (uint32_t)b);
+      else if constexpr (OP == SIM_PROD) return (int32_t)((uint32_t)a * (uint32_t)b);
+      else if constexpr (OP == SIM_MIN) return (b < a) ? b : a;
+      else return (b > a) ? b : a;
+    } else {
+      if constexpr (OP == SIM_SUM || OP == SIM_AVG) return a + b;
+      else if constexpr (OP == SIM_PROD) return a * b;
+      else if constexpr (OP == SIM_MIN) return (b < a) ? b : a;
+      else return (b > a) ? b : a;
+    }
+  }
+  // the fix-up where a chunk completes: int avg divides once (truncating)
+  static __device__ __forceinline__ A post(A v, int p) {
+    if constexpr (OP == SIM_AVG && DT == SIM_INT32) return v / p;
+    else return v;
+  }
+};
+
+// ---- 16-byte vectors -----------------------------------------------------------
+__device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
+  return __builtin_nontemporal_load((const u32x4*)((const char*)base + byte_off));
+}
+__device__ __forceinline__ void st16(void* base, int64_t byte_off, u32x4 v) {
+  __builtin_nontemporal_store(v, (u32x4*)((char*)base + byte_off));
+}
+
+// Unpack one 16-byte storage vector into EPV accumulator values.
+template <int DT>
+__device__ __forceinline__ void unpack(u32x4 v, typename Ty<DT>::A* out) {
+  if constexpr (Ty<DT>::E == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) out[k] = widen_bits<DT>(v[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      out[2 * k] = widen_bits<DT>(v[k] & 0xffffu);
+      out[2 * k + 1] = widen_bits<DT>(v[k] >> 16);
+    }
+  }
+}
+
+// Pack EPV accumulator values into one 16-byte storage vector.
+template <int DT>
+__device__ __forceinline__ u32x4 pack(const typename Ty<DT>::A* in) {
+  u32x4 v;
+  if constexpr (Ty<DT>::E == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = narrow_bits<DT>(in[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; k++) v[k] = narrow_bits<DT>(in[2 * k]) | (narrow_bits<DT>(in[2 * k + 1]) << 16);
+  }
+  return v;
+}
+
+// Scalar element access (ragged heads and tails).
+template <int DT>
+__device__ __forceinline__ typename Ty<DT>::A load_elem(const void* base, int64_t i) {
+  if constexpr (Ty<DT>::E == 4) return widen_bits<DT>(((const uint32_t*)base)[i]);
+  else return widen_bits<DT>(((const uint16_t*)base)[i]);
+}
+template <int DT>
+__device__ __forceinline__ void store_elem(void* base, int64_t i, typename Ty<DT>::A v) {
+  if constexpr (Ty<DT>::E == 4) ((uint32_t*)base)[i] = narrow_bits<DT>(v);
+  else ((uint16_t*)base)[i] = (uint16_t)narrow_bits<DT>(v);
+}
+
+}  // namespace simar

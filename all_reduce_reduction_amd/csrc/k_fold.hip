@@ -1,0 +1,168 @@
+// k_fold.hip -- the gather-fold kernel for gfx950: the fused one-shot
+// all-reduce, all-pairs step 1 and the direct reduce-scatter.
+//
+// One-shot ("MSCCL++ ...", section "The Collective Algorithm Library":
+// in 1PA every rank reads every rank's data and reduces it in one phase;
+// "concurrent multi-peer reduction" reads all peers at once instead of one
+// by one): each lane issues the 16-byte loads of all p ranks for its
+// vector back to back, folds them in VGPRs in the all-pairs order (owner of
+// the chunk first, then the other ranks ascending -- the order of the
+// scratch slots in the all-pairs program of "MSCCL, in depth ...", section
+// "Writing an algorithm in MSCCLang"), and stores the one result to every
+// rank's output from the same registers (T-CCL, section III-C1: load once,
+// store to several peers).  Each input byte is read once and each output
+// byte written once: 2 p S bytes, the floor for p ranks in one HBM.
+//
+// All-pairs step 1 / direct reduce-scatter is the same fold with only the
+// owner's output written (owner-only mode).
+//
+// Layout: grid = (tiles, p); blockIdx.y is the chunk j, so the fold order is
+// uniform over a workgroup and the operand pointers are chosen once, in
+// scalar registers.  A workgroup walks its chunk in spans of kBlock * U
+// vectors; a ragged chunk edge (a vector that would straddle two chunks, or
+// a misaligned operand) is done element by element so every element keeps
+// its own chunk's order.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace simar {
+
+template <int DT, int OP, int P, bool ALL_OUT, int U>
+__global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
+  typedef typename Ty<DT>::A A;
+  typedef Op<DT, OP> O;
+  constexpr int V = epv<DT>();
+  constexpr int E = Ty<DT>::E;
+  constexpr int MAXP = P ? P : SIM_MAX_RANKS;
+  const int p = P ? P : a.p;
+  const int j = blockIdx.y;
+  const int64_t lo = a.lo[j], hi = a.lo[j + 1];
+  const float inv_p = a.inv_p;
+
+  // operand k of the fold: rank j for k == 0, then the ranks != j ascending
+  const void* xp[MAXP];
+#pragma unroll
+  for (int k = 0; k < MAXP; k++) {
+    const int q = (k == 0) ? j : (k <= j ? k - 1 : k);
+    xp[k] = (k < p) ? a.x[q] : nullptr;
+  }
+
+  const bool vec = (a.vec_ok >> j) & 1u;
+  int64_t head = vec ? (int64_t)((V - (lo % V)) % V) : (hi - lo);
+  if (head > hi - lo) head = hi - lo;
+  const int64_t vbeg = lo + head;
+  const int64_t nvec = (hi - vbeg) / V;
+  const int64_t tail_beg = vbeg + nvec * V;
+  const int64_t nscalar = head + (hi - tail_beg);
+  const int tid = threadIdx.x;
+  const int64_t span = (int64_t)kBlock * U;
+  const int64_t stride = (int64_t)a.tiles * span;
+  const int64_t oshift = ALL_OUT ? 0 : a.out_shift[j];
+  void* const yj = a.y[j];
+
+  for (int64_t base = (int64_t)blockIdx.x * span; base < nvec; base += stride) {
+    u32x4 L[U][MAXP];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t v = base + u * kBlock + tid;
+      if (v < nvec) {
+        const int64_t off = (vbeg + v * V) * E;
+#pragma unroll
+        for (int k = 0; k < MAXP; k++)
+          if (k < p) L[u][k] = ld16(xp[k], off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t v = base + u * kBlock + tid;
+      if (v < nvec) {
+        A acc[V], t[V];
+        unpack<DT>(L[u][0], acc);
+#pragma unroll
+        for (int e = 0; e < V; e++) acc[e] = O::pre(acc[e], inv_p);
+#pragma unroll
+        for (int k = 1; k < MAXP; k++) {
+          if (k < p) {
+            unpack<DT>(L[u][k], t);
+#pragma unroll
+            for (int e = 0; e < V; e++) acc[e] = O::comb(acc[e], O::pre(t[e], inv_p));
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < V; e++) acc[e] = O::post(acc[e], p);
+        const u32x4 out = pack<DT>(acc);
+        const int64_t i0 = vbeg + v * V;
+        if constexpr (ALL_OUT) {
+#pragma unroll
+          for (int r = 0; r < MAXP; r++)
+            if (r < p) st16(a.y[r], i0 * E, out);
+        } else {
+          st16(yj, (i0 - oshift) * E, out);
+        }
+      }
+    }
+  }
+
+  // ragged edges, element by element
+  for (int64_t s = (int64_t)blockIdx.x * kBlock + tid; s < nscalar; s += (int64_t)a.tiles * kBlock) {
+    const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
+    A acc = O::pre(load_elem<DT>(xp[0], i), inv_p);
+#pragma unroll
+    for (int k = 1; k < MAXP; k++)
+      if (k < p) acc = O::comb(acc, O::pre(load_elem<DT>(xp[k], i), inv_p));
+    acc = O::post(acc, p);
+    if constexpr (ALL_OUT) {
+#pragma unroll
+      for (int r = 0; r < MAXP; r++)
+        if (r < p) store_elem<DT>(a.y[r], i, acc);
+    } else {
+      store_elem<DT>(yj, i - oshift, acc);
+    }
+  }
+}
+
+template <int DT, int OP, int P, bool ALL_OUT, int U>
+static hipError_t go(const FoldArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_fold<DT, OP, P, ALL_OUT, U>), dim3(a.tiles, a.p), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int OP>
+static hipError_t by_shape(int p, bool all_out, int unroll, const FoldArgs& a, hipStream_t s) {
+  if (p == 8) {
+    if (all_out) {
+      if (unroll >= 4) return go<DT, OP, 8, true, 4>(a, s);
+      if (unroll == 2) return go<DT, OP, 8, true, 2>(a, s);
+      return go<DT, OP, 8, true, 1>(a, s);
+    }
+    if (unroll >= 4) return go<DT, OP, 8, false, 4>(a, s);
+    if (unroll == 2) return go<DT, OP, 8, false, 2>(a, s);
+    return go<DT, OP, 8, false, 1>(a, s);
+  }
+  return all_out ? go<DT, OP, 0, true, 1>(a, s) : go<DT, OP, 0, false, 1>(a, s);
+}
+
+template <int DT>
+static hipError_t by_op(int op, int p, bool all_out, int unroll, const FoldArgs& a, hipStream_t s) {
+  switch (op) {
+    case SIM_SUM: return by_shape<DT, SIM_SUM>(p, all_out, unroll, a, s);
+    case SIM_PROD: return by_shape<DT, SIM_PROD>(p, all_out, unroll, a, s);
+    case SIM_MIN: return by_shape<DT, SIM_MIN>(p, all_out, unroll, a, s);
+    case SIM_MAX: return by_shape<DT, SIM_MAX>(p, all_out, unroll, a, s);
+    case SIM_AVG: return by_shape<DT, SIM_AVG>(p, all_out, unroll, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fold(int dtype, int op, int p, bool all_out, const FoldArgs& a, int unroll,
+                       hipStream_t s) {
+  switch (dtype) {
+    case SIM_INT32: return by_op<SIM_INT32>(op, p, all_out, unroll, a, s);
+    case SIM_FP32: return by_op<SIM_FP32>(op, p, all_out, unroll, a, s);
+    case SIM_FP16: return by_op<SIM_FP16>(op, p, all_out, unroll, a, s);
+    case SIM_BF16: return by_op<SIM_BF16>(op, p, all_out, unroll, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace simar

@@ -1,0 +1,211 @@
+// k_step.hip -- per-step kernels of the multi-launch schedules (gfx950).
+//
+// k_ring_reduce runs one reduce-scatter step of the ring: for each of the
+// step's transfers (one per rank, blockIdx.y), the arriving running value of
+// the chunk is combined with the receiving rank's own element and written
+// on -- the fused receive-reduce-send primitive of NCCL's runRing
+// ("Inside NCCL all-reduce", section "The ring, exactly as the kernel runs
+// it").  On the last step of the half the chunk completes: the post-op (the
+// int avg divide, the one RNE narrowing of 16-bit types) is applied and the
+// result goes to the owner's output.  Partials are accumulator-typed: for
+// 32-bit types they live in the receiving rank's output buffer (the slot of
+// a chunk that rank does not own yet); for fp16/bf16 they stay fp32, in
+// library scratch, so each element is rounded to 16 bits exactly once.
+//
+// k_copy moves finished chunks: the ring's all-gather forwards, the
+// all-pairs fan-out (one 16-byte load, up to p-1 stores from the same
+// registers) and the standalone all-gather.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace simar {
+
+// accumulator-typed partials: V values at element index i0 (vector aligned)
+template <int DT>
+__device__ __forceinline__ void load_part(const void* base, int64_t idx, typename Ty<DT>::A* out) {
+  constexpr int V = epv<DT>();
+#pragma unroll
+  for (int h = 0; h < V / 4; h++) {
+    const u32x4 w = ld16(base, (idx + 4 * h) * 4);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      // copy the lane out first: a bit cast applied directly to a vector
+      // subscript reads element 0 with this compiler
+      const uint32_t bits = w[k];
+      out[4 * h + k] = __builtin_bit_cast(typename Ty<DT>::A, bits);
+    }
+  }
+}
+template <int DT>
+__device__ __forceinline__ void store_part(void* base, int64_t idx, const typename Ty<DT>::A* in) {
+  constexpr int V = epv<DT>();
+#pragma unroll
+  for (int h = 0; h < V / 4; h++) {
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; k++) w[k] = __builtin_bit_cast(uint32_t, in[4 * h + k]);
+    st16(base, (idx + 4 * h) * 4, w);
+  }
+}
+
+template <int DT, int OP, bool A_PART, bool D_FINAL, int U>
+__global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
+  typedef typename Ty<DT>::A A;
+  typedef Op<DT, OP> O;
+  constexpr int V = epv<DT>();
+  constexpr int E = Ty<DT>::E;
+  const RingXfer x = args.x[blockIdx.y];
+  const float inv_p = args.inv_p;
+  const int p = args.p;
+  const int64_t lo = x.lo, hi = x.hi;
+  int64_t head = x.vec_ok ? (int64_t)((V - (lo % V)) % V) : (hi - lo);
+  if (head > hi - lo) head = hi - lo;
+  const int64_t vbeg = lo + head;
+  const int64_t nvec = (hi - vbeg) / V;
+  const int64_t tail_beg = vbeg + nvec * V;
+  const int64_t nscalar = head + (hi - tail_beg);
+  const int tid = threadIdx.x;
+  const int64_t span = (int64_t)kBlock * U;
+  const int64_t stride = (int64_t)args.tiles * span;
+
+  for (int64_t base = (int64_t)blockIdx.x * span; base < nvec; base += stride) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t v = base + u * kBlock + tid;
+      if (v < nvec) {
+        const int64_t i0 = vbeg + v * V;
+        A in[V], own[V];
+        if constexpr (A_PART) {
+          load_part<DT>(x.a, i0 - x.a_shift, in);
+        } else {
+          unpack<DT>(ld16(x.a, i0 * E), in);
+#pragma unroll
+          for (int e = 0; e < V; e++) in[e] = O::pre(in[e], inv_p);
+        }
+        unpack<DT>(ld16(x.b, i0 * E), own);
+#pragma unroll
+        for (int e = 0; e < V; e++) in[e] = O::comb(in[e], O::pre(own[e], inv_p));
+        if constexpr (D_FINAL) {
+#pragma unroll
+          for (int e = 0; e < V; e++) in[e] = O::post(in[e], p);
+          st16(x.d, (i0 - x.d_shift) * E, pack<DT>(in));
+        } else {
+          store_part<DT>(x.d, i0 - x.d_shift, in);
+        }
+      }
+    }
+  }
+
+  for (int64_t s = (int64_t)blockIdx.x * kBlock + tid; s < nscalar; s += (int64_t)args.tiles * kBlock) {
+    const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
+    A in;
+    if constexpr (A_PART) in = ((const A*)x.a)[i - x.a_shift];
+    else in = O::pre(load_elem<DT>(x.a, i), inv_p);
+    A v = O::comb(in, O::pre(load_elem<DT>(x.b, i), inv_p));
+    if constexpr (D_FINAL) store_elem<DT>(x.d, i - x.d_shift, O::post(v, p));
+    else ((A*)x.d)[i - x.d_shift] = v;
+  }
+}
+
+template <int E, int U>
+__global__ void __launch_bounds__(kBlock) k_copy(CopyArgs args) {
+  constexpr int V = 16 / E;
+  const CopyXfer& x = args.x[blockIdx.y];
+  const int64_t lo = x.lo, hi = x.hi;
+  const int nd = x.ndst;
+  int64_t head = x.vec_ok ? (int64_t)((V - (lo % V)) % V) : (hi - lo);
+  if (head > hi - lo) head = hi - lo;
+  const int64_t vbeg = lo + head;
+  const int64_t nvec = (hi - vbeg) / V;
+  const int64_t tail_beg = vbeg + nvec * V;
+  const int64_t nscalar = head + (hi - tail_beg);
+  const int tid = threadIdx.x;
+  const int64_t span = (int64_t)kBlock * U;
+  const int64_t stride = (int64_t)args.tiles * span;
+
+  for (int64_t base = (int64_t)blockIdx.x * span; base < nvec; base += stride) {
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t v = base + u * kBlock + tid;
+      if (v < nvec) w[u] = ld16(x.src, (vbeg + v * V - x.src_shift) * E);
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t v = base + u * kBlock + tid;
+      if (v < nvec) {
+        const int64_t off = (vbeg + v * V - x.dst_shift) * E;
+        for (int d = 0; d < nd; d++) st16(x.dst[d], off, w[u]);
+      }
+    }
+  }
+  for (int64_t s = (int64_t)blockIdx.x * kBlock + tid; s < nscalar; s += (int64_t)args.tiles * kBlock) {
+    const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
+    if constexpr (E == 4) {
+      const uint32_t w = ((const uint32_t*)x.src)[i - x.src_shift];
+      for (int d = 0; d < nd; d++) ((uint32_t*)x.dst[d])[i - x.dst_shift] = w;
+    } else {
+      const uint16_t w = ((const uint16_t*)x.src)[i - x.src_shift];
+      for (int d = 0; d < nd; d++) ((uint16_t*)x.dst[d])[i - x.dst_shift] = w;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) k_fill64(unsigned long long* p, unsigned long long v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock) p[i] = v;
+}
+
+// ---- launchers ----------------------------------------------------------------
+template <int DT, int OP>
+static hipError_t ring_go(bool a_part, bool d_final, const RingArgs& a, hipStream_t s) {
+  const dim3 grid(a.tiles, a.nx), block(kBlock);
+  if (a_part) {
+    if (d_final) hipLaunchKernelGGL((k_ring_reduce<DT, OP, true, true, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_ring_reduce<DT, OP, true, false, 2>), grid, block, 0, s, a);
+  } else {
+    if (d_final) hipLaunchKernelGGL((k_ring_reduce<DT, OP, false, true, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_ring_reduce<DT, OP, false, false, 2>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t ring_by_op(int op, bool ap, bool df, const RingArgs& a, hipStream_t s) {
+  switch (op) {
+    case SIM_SUM: return ring_go<DT, SIM_SUM>(ap, df, a, s);
+    case SIM_PROD: return ring_go<DT, SIM_PROD>(ap, df, a, s);
+    case SIM_MIN: return ring_go<DT, SIM_MIN>(ap, df, a, s);
+    case SIM_MAX: return ring_go<DT, SIM_MAX>(ap, df, a, s);
+    case SIM_AVG: return ring_go<DT, SIM_AVG>(ap, df, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, const RingArgs& a,
+                              hipStream_t s) {
+  switch (dtype) {
+    case SIM_INT32: return ring_by_op<SIM_INT32>(op, a_partial, d_final, a, s);
+    case SIM_FP32: return ring_by_op<SIM_FP32>(op, a_partial, d_final, a, s);
+    case SIM_FP16: return ring_by_op<SIM_FP16>(op, a_partial, d_final, a, s);
+    case SIM_BF16: return ring_by_op<SIM_BF16>(op, a_partial, d_final, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy(int esize, const CopyArgs& a, hipStream_t s) {
+  const dim3 grid(a.tiles, a.nx), block(kBlock);
+  if (esize == 4) hipLaunchKernelGGL((k_copy<4, 2>), grid, block, 0, s, a);
+  else if (esize == 2) hipLaunchKernelGGL((k_copy<2, 2>), grid, block, 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_fill64(unsigned long long* p, unsigned long long v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + kBlock - 1) / kBlock;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill64, dim3((unsigned)blocks), dim3(kBlock), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace simar

@@ -1,0 +1,107 @@
+// kernels.h -- kernel argument blocks and host-side launchers shared by the
+// C-ABI layer (api.cpp) and the gfx950 kernels (k_*.hip).
+//
+// Every argument block is passed by value as the kernel's argument segment
+// (at most 4 KiB).  Element indices are absolute within a rank's buffer;
+// an operand with a `shift` is addressed at [i - shift] (chunk-sized outputs
+// and scratch slots).  `vec_ok` says the 16-byte vector body is aligned for
+// every operand of that transfer; otherwise the transfer runs element by
+// element (only for ragged sizes).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "simar.h"
+
+namespace simar {
+
+constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts of 64)
+
+// Gather-fold of whole chunks: the fused one-shot (every rank's output
+// written from the same registers) or all-pairs step 1 / direct
+// reduce-scatter (only the owner's output written).
+struct FoldArgs {
+  const void* x[SIM_MAX_RANKS];
+  void* y[SIM_MAX_RANKS];
+  int64_t lo[SIM_MAX_RANKS + 1];     // chunk bounds
+  int64_t out_shift[SIM_MAX_RANKS];  // owner-only mode: y[j] index = i - out_shift[j]
+  uint32_t vec_ok;                   // bit j: chunk j may use the vector body
+  int p;
+  int tiles;                         // workgroups per chunk (gridDim.x)
+  float inv_p;                       // fp32(1/p) for fp avg
+};
+
+// One ring reduce-scatter step: p transfers, each over one chunk.
+struct RingXfer {
+  const void* a;    // running value from the predecessor: an input (first step) or a partial
+  int64_t a_shift;
+  const void* b;    // the receiving rank's own input, absolute index
+  void* d;          // partial (not last step) or output (last step)
+  int64_t d_shift;
+  int64_t lo, hi;
+  int vec_ok;
+  int pad_;
+};
+struct RingArgs {
+  RingXfer x[SIM_MAX_RANKS];
+  int nx;
+  int p;
+  int tiles;
+  float inv_p;
+};
+
+// Bit copies: ring all-gather forwards, all-pairs fan-out, all-gather.
+struct CopyXfer {
+  const void* src;
+  int64_t src_shift;
+  void* dst[SIM_MAX_RANKS];
+  int64_t dst_shift;
+  int64_t lo, hi;
+  int ndst;
+  int vec_ok;
+};
+struct CopyArgs {
+  CopyXfer x[SIM_MAX_RANKS];
+  int nx;
+  int tiles;
+};
+
+// LL packet one-shot: producers write 8-byte {data, flag} packets, the
+// consumers poll them and fold.
+struct LLArgs {
+  const void* x[SIM_MAX_RANKS];
+  void* y[SIM_MAX_RANKS];
+  unsigned long long* ll;   // packets: rank q's word k at ll[q * ll_stride + k]
+  int64_t ll_stride;
+  int64_t n;                // elements per rank
+  int64_t nwords;           // 32-bit data words per rank
+  int64_t lo[SIM_MAX_RANKS + 1];
+  int64_t tile_words;       // words per tile (one workgroup's share)
+  int64_t ntiles;
+  unsigned long long spin_limit;
+  int* err;                 // device error word
+  int p;
+  unsigned int epoch;       // flag the producers write
+  unsigned int wait_epoch;  // flag the consumers accept (== epoch unless a test skews it)
+  int shift;                // consumers take tile (t + shift) mod ntiles
+  float inv_p;
+};
+
+static_assert(sizeof(FoldArgs) <= 4096, "kernel argument segment too large");
+static_assert(sizeof(RingArgs) <= 4096, "kernel argument segment too large");
+static_assert(sizeof(CopyArgs) <= 4096, "kernel argument segment too large");
+static_assert(sizeof(LLArgs) <= 4096, "kernel argument segment too large");
+
+// Launchers: select the (dtype, op, ...) instantiation and enqueue.
+hipError_t launch_fold(int dtype, int op, int p, bool all_out, const FoldArgs& a, int unroll,
+                       hipStream_t s);
+hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, const RingArgs& a,
+                              hipStream_t s);
+hipError_t launch_copy(int esize, const CopyArgs& a, hipStream_t s);
+hipError_t launch_ll(int dtype, int op, const LLArgs& a, int grid, hipStream_t s);
+hipError_t launch_fill64(unsigned long long* p, unsigned long long v, int64_t n, hipStream_t s);
+// Workgroups of the LL kernel (dtype, op) that fit on one CU at once.
+int ll_blocks_per_cu(int dtype, int op);
+
+}  // namespace simar

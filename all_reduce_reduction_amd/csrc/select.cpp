@@ -1,0 +1,272 @@
+// select.cpp -- alpha-beta model and its calibration file.
+//
+// The model is the one the pages price schedules with: time = latency x
+// number of synchronised steps + bytes / bandwidth ("MSCCL, in depth ...",
+// section "Why generic collectives leave time on the table"; "Inside NCCL
+// all-reduce", section "How NCCL picks: a cost model, not a threshold":
+// one line of cost per candidate, argmin per call, no stored threshold).
+// On one GPU a "step" is a kernel launch and the bytes are the schedule's
+// HBM traffic over all simulated ranks, so alpha and B are fitted to this
+// GPU by the calibration sweep and stored as JSON.
+#include "select.h"
+
+#include <cctype>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <vector>
+
+#include "schedule.h"
+#include "simar.h"
+
+namespace simar {
+
+Model default_model() {
+  Model m;
+  for (int a = 0; a < kNumAlgos; a++) {
+    m.a[a].alpha_us = 4.0;
+    m.a[a].gbps = 4500.0;
+  }
+  m.a[SIM_ALGO_ONESHOT_LL].gbps = 1500.0;
+  return m;
+}
+
+int model_launches(int coll, int algo, int p) {
+  switch (algo) {
+    case SIM_ALGO_RING: return coll == COLL_ALLREDUCE ? 2 * (p - 1) : p - 1;
+    case SIM_ALGO_ALLPAIRS: return coll == COLL_ALLREDUCE ? 2 : 1;
+    case SIM_ALGO_ONESHOT: return 1;
+    case SIM_ALGO_ONESHOT_LL: return 1;
+  }
+  return 0;
+}
+
+double model_traffic(int coll, int algo, int p, double n, int esize) {
+  const double e = esize, S = n * e;
+  if (coll == COLL_ALLREDUCE) {
+    switch (algo) {
+      case SIM_ALGO_ONESHOT: return 2.0 * p * S;          // p inputs read, p outputs written
+      case SIM_ALGO_ALLPAIRS: return (2.0 * p + 1.0) * S;  // step 1: pS + S; step 2: S + (p-1)S
+      case SIM_ALGO_ONESHOT_LL: return 6.0 * p * S;        // pack 3pS, consume 3pS
+      case SIM_ALGO_RING: {
+        // reduce-scatter: first step in,in->part; middle part,in->part;
+        // last part,in->out; partials are 4-byte accumulators.  Each step
+        // touches n elements in total (p transfers of n/p).
+        double rs;
+        if (p == 2) rs = n * (e + e + e);
+        else rs = n * (e + e + 4) + (p - 3) * n * (4 + e + 4) + n * (4 + e + e);
+        const double ag = (p - 1) * n * (e + e);
+        return rs + ag;
+      }
+    }
+  } else if (coll == COLL_REDUCE_SCATTER) {
+    switch (algo) {
+      case SIM_ALGO_ALLPAIRS: return (p + 1.0) * S;       // all inputs read, p chunk outputs
+      case SIM_ALGO_RING:
+        if (p == 2) return n * (e + e + e);
+        return n * (e + e + 4) + (p - 3) * n * (4 + e + 4) + n * (4 + e + e);
+    }
+  } else if (coll == COLL_ALL_GATHER) {
+    switch (algo) {
+      case SIM_ALGO_ALLPAIRS: return (p + 1.0) * S;       // S/p read per block, S written per rank
+      case SIM_ALGO_RING: return (2.0 * p - 1.0) * S;     // step 0 reads once, writes twice
+    }
+  }
+  return 0.0;
+}
+
+double model_predict(const Model& m, int coll, int algo, int p, double n, int esize) {
+  if (algo <= 0 || algo >= kNumAlgos) return 1e30;
+  const AlgoModel& am = m.a[algo];
+  const double steps = am.steps >= 0 ? am.steps : (double)model_launches(coll, algo, p);
+  const double bytes = am.bytes_factor >= 0 ? am.bytes_factor * n * esize
+                                            : model_traffic(coll, algo, p, n, esize);
+  return am.alpha_us * steps + bytes / (am.gbps * 1e3);  // GB/s -> bytes per us
+}
+
+// ---------------------------------------------------------------------------
+// A small JSON reader for the calibration file: objects, arrays, strings,
+// numbers, true/false/null.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct JVal {
+  enum Kind { NUL, BOOL, NUM, STR, ARR, OBJ } kind = NUL;
+  double num = 0;
+  std::string str;
+  std::vector<JVal> arr;
+  std::map<std::string, JVal> obj;
+};
+
+struct Parser {
+  const char* s;
+  const char* end;
+  std::string err;
+  void ws() {
+    while (s < end && std::isspace((unsigned char)*s)) s++;
+  }
+  bool lit(const char* w) {
+    size_t k = std::strlen(w);
+    if ((size_t)(end - s) >= k && std::strncmp(s, w, k) == 0) {
+      s += k;
+      return true;
+    }
+    return false;
+  }
+  bool str(std::string* out) {
+    if (s >= end || *s != '"') return fail("expected a string");
+    s++;
+    while (s < end && *s != '"') {
+      if (*s == '\\') {
+        s++;
+        if (s >= end) return fail("bad escape");
+        char c = *s;
+        out->push_back(c == 'n' ? '\n' : c == 't' ? '\t' : c);
+      } else {
+        out->push_back(*s);
+      }
+      s++;
+    }
+    if (s >= end) return fail("unterminated string");
+    s++;
+    return true;
+  }
+  bool fail(const char* m) {
+    if (err.empty()) err = m;
+    return false;
+  }
+  bool value(JVal* v, int depth) {
+    if (depth > 32) return fail("nesting too deep");
+    ws();
+    if (s >= end) return fail("unexpected end");
+    if (*s == '{') {
+      v->kind = JVal::OBJ;
+      s++;
+      ws();
+      if (s < end && *s == '}') {
+        s++;
+        return true;
+      }
+      for (;;) {
+        ws();
+        std::string k;
+        if (!str(&k)) return false;
+        ws();
+        if (s >= end || *s != ':') return fail("expected ':'");
+        s++;
+        if (!value(&v->obj[k], depth + 1)) return false;
+        ws();
+        if (s < end && *s == ',') {
+          s++;
+          continue;
+        }
+        if (s < end && *s == '}') {
+          s++;
+          return true;
+        }
+        return fail("expected ',' or '}'");
+      }
+    }
+    if (*s == '[') {
+      v->kind = JVal::ARR;
+      s++;
+      ws();
+      if (s < end && *s == ']') {
+        s++;
+        return true;
+      }
+      for (;;) {
+        v->arr.emplace_back();
+        if (!value(&v->arr.back(), depth + 1)) return false;
+        ws();
+        if (s < end && *s == ',') {
+          s++;
+          continue;
+        }
+        if (s < end && *s == ']') {
+          s++;
+          return true;
+        }
+        return fail("expected ',' or ']'");
+      }
+    }
+    if (*s == '"') {
+      v->kind = JVal::STR;
+      return str(&v->str);
+    }
+    if (lit("true")) {
+      v->kind = JVal::BOOL;
+      v->num = 1;
+      return true;
+    }
+    if (lit("false")) {
+      v->kind = JVal::BOOL;
+      return true;
+    }
+    if (lit("null")) return true;
+    char* e2 = nullptr;
+    std::string tmp(s, (size_t)std::min<ptrdiff_t>(end - s, 64));
+    double d = std::strtod(tmp.c_str(), &e2);
+    if (e2 == tmp.c_str()) return fail("bad value");
+    s += (e2 - tmp.c_str());
+    v->kind = JVal::NUM;
+    v->num = d;
+    return true;
+  }
+};
+
+const char* kAlgoNames[kNumAlgos] = {"auto", "ring", "allpairs", "oneshot", "oneshot_ll"};
+
+}  // namespace
+
+bool model_load_json(const char* path, Model* m, std::string* err) {
+  FILE* f = std::fopen(path, "rb");
+  if (!f) {
+    if (err) *err = "cannot open file";
+    return false;
+  }
+  std::string text;
+  char buf[4096];
+  size_t k;
+  while ((k = std::fread(buf, 1, sizeof buf, f)) > 0) text.append(buf, k);
+  std::fclose(f);
+  Parser ps{text.data(), text.data() + text.size(), ""};
+  JVal root;
+  if (!ps.value(&root, 0) || root.kind != JVal::OBJ) {
+    if (err) *err = ps.err.empty() ? "top level is not an object" : ps.err;
+    return false;
+  }
+  auto it = root.obj.find("algos");
+  if (it == root.obj.end() || it->second.kind != JVal::OBJ) {
+    if (err) *err = "missing object 'algos'";
+    return false;
+  }
+  Model out = *m;
+  for (int a = 1; a < kNumAlgos; a++) {
+    auto ai = it->second.obj.find(kAlgoNames[a]);
+    if (ai == it->second.obj.end()) continue;
+    const JVal& o = ai->second;
+    if (o.kind != JVal::OBJ) {
+      if (err) *err = "algo entry is not an object";
+      return false;
+    }
+    auto al = o.obj.find("alpha_us");
+    auto bw = o.obj.find("gbps");
+    if (al == o.obj.end() || bw == o.obj.end() || al->second.kind != JVal::NUM ||
+        bw->second.kind != JVal::NUM || !(bw->second.num > 0) || !(al->second.num >= 0)) {
+      if (err) *err = "algo entry needs numeric alpha_us >= 0 and gbps > 0";
+      return false;
+    }
+    out.a[a].alpha_us = al->second.num;
+    out.a[a].gbps = bw->second.num;
+    out.a[a].steps = -1;
+    out.a[a].bytes_factor = -1;
+  }
+  out.source = path;
+  *m = out;
+  return true;
+}
+
+}  // namespace simar

@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the simulated all-reduce on one MI355X.
+
+Workload (one "step" = one all-reduce call through the C-ABI, selector
+included): p = 8 simulated ranks, bf16 in/out with fp32 accumulation,
+8192 hidden x 4096 tokens = 33,554,432 elements = 64 MiB per rank, values
+N(0,1) * 0.02 from the seeded generator -- a tensor-parallel activation
+all-reduce.  Inputs are resident in HBM before the timed region starts.
+
+Printed JSON line:
+  value          NCCL-style bus bandwidth 2(p-1)/p * S / t  (GB/s)
+  roofline       the dominant kernel's algorithmic bytes per launch over its
+                 average launch time (HIP events on the launch stream), vs
+                 MI355X's 8 TB/s HBM peak; `traffic` = rocprofv3 FETCH_SIZE +
+                 WRITE_SIZE per launch when a matching counter summary is
+                 committed under profiles/, else null
+  per_algo       the same workload forced to each legal schedule
+  latency_8KiB   per-call microseconds at 8 KiB per rank (p = 8, fp16):
+                 plain one-shot vs the LL packet path vs the selector's pick
+  cpu_baseline   the CPU oracle on the same host arrays (all host threads)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "all-reduce busBW & HBM GB/s vs peak, p=8 bf16 64 MiB; 8 KiB latency (us)"
+P = 8
+HIDDEN, TOKENS = 8192, 4096
+N = HIDDEN * TOKENS          # elements per rank
+ESIZE = 2
+S = N * ESIZE                # bytes per rank
+LAT_N = 4096                 # 8 KiB of fp16 per rank
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--algo", default="auto", help="auto|ring|allpairs|oneshot")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip per-algo and latency figures")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="only the timed steps of the headline workload (for rocprofv3 runs)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(algo: str) -> float:
+    """HBM bytes of one call over all ranks (the schedules' traffic laws)."""
+    if algo == "oneshot":
+        return 2.0 * P * S
+    if algo == "allpairs":
+        return (2.0 * P + 1.0) * S
+    if algo == "ring":  # bf16 with fp32 partials
+        n, e = N, ESIZE
+        rs = n * (e + e + 4) + (P - 3) * n * (4 + e + 4) + n * (4 + e + e)
+        return rs + (P - 1) * n * (e + e)
+    raise ValueError(algo)
+
+
+def time_calls(fn, steps: int, warmup: int) -> float:
+    """Seconds per call: HIP events on torch's current stream, which is the
+    stream every call here launches on."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3 / steps
+
+
+def load_traffic(kernel: str):
+    """rocprofv3 counter summary for `kernel` (committed under profiles/)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    ent = d.get("kernels", {}).get(kernel)
+    if not ent or ent.get("source_hash") != d.get("source_hash_now"):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: the p simulated ranks all live in one GPU's HBM "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import all_reduce_reduction_amd as sim
+    import synthdata
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    sim.sim_init(0, P, S)
+    stream = int(torch.cuda.current_stream().cuda_stream)
+
+    xs = synthdata.workload_inputs(3, P, N, "bf16")
+    din = [torch.from_numpy(x.view(np.int16)).to(dev) for x in xs]
+    dout = [torch.empty(N, dtype=torch.int16, device=dev) for _ in range(P)]
+    ip = [t.data_ptr() for t in din]
+    op_ = [t.data_ptr() for t in dout]
+
+    def step(algo=args.algo):
+        st = sim.sim_allreduce(ip, op_, P, N, "bf16", "sum", algo, stream)
+        if st:
+            raise sim.SimError(st, "sim_allreduce")
+
+    t = time_calls(step, args.steps, args.warmup)
+    assert sim.sim_check_error(stream) == 0
+    ran = sim.sim_last_algo()
+    if args.profile_only:
+        print(json.dumps({"algo": ran, "us_per_step": t * 1e6}), flush=True)
+        return
+    busbw = 2 * (P - 1) / P * S / t / 1e9
+    kernel = {"oneshot": "k_fold (one-shot, all outputs)", "allpairs": "k_fold + k_copy",
+              "ring": "k_ring_reduce + k_copy"}[ran]
+    achieved = algorithmic_bytes(ran) / t / 1e9
+    traffic = load_traffic(ran)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": kernel,
+                "algorithmic_bytes_per_launch": algorithmic_bytes(ran)}
+
+    extras = {}
+    if not args.no_extras:
+        per_algo = {}
+        for a in ("oneshot", "allpairs", "ring"):
+            ta = time_calls(lambda a=a: step(a), max(10, args.steps // 4), 5)
+            per_algo[a] = {"us": round(ta * 1e6, 2), "busbw_GBps": round(2 * (P - 1) / P * S / ta / 1e9, 1),
+                           "hbm_algorithmic_GBps": round(algorithmic_bytes(a) / ta / 1e9, 1)}
+        extras["per_algo"] = per_algo
+        # small-message latency: 8 KiB per rank, fp16
+        lx = synthdata.workload_inputs(4, P, LAT_N, "fp16")
+        lin = [torch.from_numpy(x.view(np.int16)).to(dev) for x in lx]
+        lout = [torch.empty(LAT_N, dtype=torch.int16, device=dev) for _ in range(P)]
+        lip, lop = [t_.data_ptr() for t_ in lin], [t_.data_ptr() for t_ in lout]
+        lat = {}
+        for a in ("oneshot", "oneshot_ll", "allpairs", "ring", "auto"):
+            def call(a=a):
+                st = sim.sim_allreduce(lip, lop, P, LAT_N, "fp16", "sum", a, stream)
+                if st:
+                    raise sim.SimError(st, "sim_allreduce")
+            lat[a] = round(time_calls(call, 2000, 200) * 1e6, 2)
+            if a == "auto":
+                lat["auto_pick"] = sim.sim_last_algo()
+        assert sim.sim_check_error(stream) == 0
+        extras["latency_8KiB_us"] = lat
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.get()
+        runs = []
+        t_end = time.perf_counter() + 10.0
+        while len(runs) < 3 or (time.perf_counter() < t_end and len(runs) < 20):
+            t0 = time.perf_counter()
+            orc.allreduce(xs, "bf16", "sum", ran)
+            runs.append(time.perf_counter() - t0)
+        tc = float(np.median(runs))
+        cpu = {"value": round(2 * (P - 1) / P * S / tc / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
+               "kind": "oracle",
+               "sample": f"the full workload (8 ranks x 64 MiB bf16, schedule '{ran}'), median of {len(runs)} runs",
+               "seconds_per_call": round(tc, 3)}
+
+    out = {
+        "metric": METRIC, "value": round(busbw, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "all-reduce sum, p=8 simulated ranks, bf16 (fp32 accumulate), 8192 hidden x 4096 "
+                               "tokens = 64 MiB per rank, N(0,1)*0.02", "p": P, "n_per_rank": N,
+                   "bytes_per_rank": S, "algo": ran, "parallelism": "1 GPU (p simulated ranks in one HBM)"},
+        "roofline": roofline, "cpu_baseline": cpu, **extras,
+    }
+    print(json.dumps(out), flush=True)
+    sim.sim_finalize()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,217 @@
+/*
+ * simar.h -- C ABI of libsimar.so: a simulated all-reduce on one MI355X.
+ *
+ * p simulated ranks each hold a same-shaped buffer in the one HBM.  The
+ * library combines them element-wise and leaves every rank's output buffer
+ * holding the identical result, executing the chunked schedules the pages
+ * describe with hand-written HIP kernels for gfx950:
+ *   - the contract (sum, prod, min, max, avg; identical result on every
+ *     rank): "Inside NCCL all-reduce" (rakshithvasudev.github.io), section
+ *     "What all-reduce promises";
+ *   - ring = reduce-scatter then all-gather, 2(p-1) steps: same page,
+ *     section "The ring, exactly as the kernel runs it";
+ *   - all-pairs (2 steps), one-shot (the two fused in one phase) and the LL
+ *     packet protocol: "MSCCL++: Rethinking GPU Communication Abstractions
+ *     for AI Inference", sections "The Collective Algorithm Library" (1PA,
+ *     2PA, 2PR) and 4.2 (LL protocol); "MSCCL, in depth ...", section
+ *     "Writing an algorithm in MSCCLang" (the all-pairs program);
+ *   - the alpha-beta selector: "MSCCL, in depth ...", section "Why generic
+ *     collectives leave time on the table"; "Inside NCCL all-reduce",
+ *     section "How NCCL picks: a cost model, not a threshold".
+ *
+ * Conventions shared by every entry point:
+ *   - Every function returns an int status: SIM_OK (0) or a negative
+ *     SIM_ERR_* code.  Argument errors are detected synchronously and
+ *     NOTHING is enqueued when an error is returned; there is no silent
+ *     fallback to another schedule (the failure mode "MSCCL, in depth ...",
+ *     section "How the runtime decides to use your algorithm", warns of).
+ *   - Collectives are asynchronous and stream-ordered: they enqueue kernels
+ *     on `stream` (a hipStream_t, or NULL for the null stream) and return.
+ *     Device buffers are owned by the caller and must stay valid until the
+ *     stream work completes.  `in_ptrs` / `out_ptrs` are caller-owned host
+ *     arrays of p device pointers; the library copies them into kernel
+ *     arguments and keeps no reference after returning.
+ *   - Device pointers must be 16-byte aligned (SIM_ERR_ALIGN otherwise).
+ *   - In-place means in_ptrs[r] == out_ptrs[r] for every rank; mixing
+ *     in-place and out-of-place ranks is SIM_ERR_INVALID_ARG.  Any other
+ *     overlap between an output and an input or another output is
+ *     SIM_ERR_ALIAS.
+ *   - n == 0 is a no-op that returns SIM_OK after the scalar arguments
+ *     (p, dtype, op, algo) are checked.
+ *   - Chunk c of an n-element buffer is [floor(c*n/p), floor((c+1)*n/p)).
+ *   - One host thread per process drives the library (no internal locking).
+ *
+ * Results: int32 and fp32 results are bit-exact functions of the schedule:
+ * ring chunk c folds ranks c+1, c+2, ..., c+p (mod p) left to right;
+ * all-pairs, one-shot and LL fold the owner c first and then the other
+ * ranks in ascending order.  fp16/bf16 are widened exactly to fp32,
+ * accumulated in fp32 (ring partials are kept in fp32) and rounded once,
+ * to nearest even, at the final write.  fp avg multiplies each operand by
+ * fp32(1/p) as it is read; int32 avg divides the wrapped int32 sum by p
+ * once (truncating).  int32 sum/prod wrap modulo 2^32.
+ */
+#ifndef SIMAR_H
+#define SIMAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+enum {
+  SIM_OK = 0,
+  SIM_ERR_INVALID_ARG = -1,  /* bad p, NULL pointer, unknown code, mixed in-place */
+  SIM_ERR_UNSUPPORTED = -2,  /* legal call, but this algo cannot serve it (e.g. LL above its buffer) */
+  SIM_ERR_ALIGN = -3,        /* a device pointer is not 16-byte aligned */
+  SIM_ERR_ALIAS = -4,        /* an output overlaps an input or another output */
+  SIM_ERR_NOMEM = -5,        /* library scratch could not be allocated */
+  SIM_ERR_HIP = -6,          /* a HIP runtime call or kernel launch failed */
+  SIM_ERR_TIMEOUT = -7,      /* a bounded device-side wait expired (reported by sim_check_error) */
+  SIM_ERR_VERIFY = -8,       /* a schedule failed the symbolic verifier */
+  SIM_ERR_NOT_INIT = -9      /* sim_init has not been called */
+};
+
+/* ---- element types, reduction ops, schedules -------------------------- */
+enum { SIM_INT32 = 0, SIM_FP32 = 1, SIM_FP16 = 2, SIM_BF16 = 3 };
+enum { SIM_SUM = 0, SIM_PROD = 1, SIM_MIN = 2, SIM_MAX = 3, SIM_AVG = 4 };
+enum {
+  SIM_ALGO_AUTO = 0,        /* alpha-beta argmin over the legal schedules */
+  SIM_ALGO_RING = 1,        /* 2(p-1) steps, one launch per step */
+  SIM_ALGO_ALLPAIRS = 2,    /* 2 steps: owner gather-reduce, then fan-out */
+  SIM_ALGO_ONESHOT = 3,     /* the 2 all-pairs steps fused in one launch */
+  SIM_ALGO_ONESHOT_LL = 4   /* one-shot through 8-byte data+flag packets */
+};
+
+#define SIM_MAX_RANKS 16
+/* LL packets carry 4 data bytes in 8: the LL buffer holds 2x the payload.
+ * LL is legal for messages of at most this many bytes per rank. */
+#define SIM_LL_MAX_BYTES_PER_RANK ((size_t)1 << 20)
+
+/* ---- lifetime ---------------------------------------------------------- */
+
+/* Initialise the library on HIP device `device` for up to p_max ranks
+ * (2..SIM_MAX_RANKS).  Allocates the device error word, the LL packet
+ * buffer (p_max * 2 * SIM_LL_MAX_BYTES_PER_RANK bytes) and, when
+ * max_bytes_per_rank > 0, the ring/reduce-scatter partial scratch for
+ * messages up to that size (otherwise scratch grows on first need).
+ * Calling it again re-initialises (finalize + init).  Errors:
+ * SIM_ERR_INVALID_ARG, SIM_ERR_HIP, SIM_ERR_NOMEM. */
+int sim_init(int device, int p_max, size_t max_bytes_per_rank);
+
+/* Free everything sim_init allocated (synchronises the device first). */
+int sim_finalize(void);
+
+/* ---- collectives -------------------------------------------------------- */
+
+/* All-reduce: out_ptrs[r][i] = X[0][i] (+) ... (+) X[p-1][i] for every rank
+ * r, each buffer holding n elements of `dtype`, combined with `op` in the
+ * fold order of `algo` (see the header comment).  algo SIM_ALGO_AUTO picks
+ * the schedule with sim_select().  Ring on fp16/bf16 keeps fp32 partials in
+ * library scratch (8 * (ceil(n/p) + 8) * p bytes).  Errors: every code
+ * above except SIM_ERR_TIMEOUT/SIM_ERR_VERIFY (asynchronous device errors
+ * come back through sim_check_error). */
+int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size_t n,
+                  int dtype, int op, int algo, void* stream);
+
+/* Reduce-scatter ("Inside NCCL all-reduce", "What all-reduce promises":
+ * every rank ends owning the finished reduction of one slice): inputs hold
+ * p * n_out_per_rank elements; out_ptrs[r] (n_out_per_rank elements)
+ * receives the reduction of chunk r.  algo: SIM_ALGO_RING (the ring's
+ * reduce-scatter half, p-1 steps, partials in library scratch) or
+ * SIM_ALGO_ALLPAIRS (direct: each owner gathers and folds its chunk, one
+ * step); SIM_ALGO_AUTO picks ALLPAIRS.  Fold orders as for sim_allreduce. */
+int sim_reduce_scatter(const void* const* in_ptrs, void* const* out_ptrs, int p,
+                       size_t n_out_per_rank, int dtype, int op, int algo, void* stream);
+
+/* All-gather: out_ptrs[r][q*n_in_per_rank + i] = in_ptrs[q][i] for all r,
+ * q (a bit copy).  algo: SIM_ALGO_RING (own block placed, then p-1
+ * forwarding steps) or SIM_ALGO_ALLPAIRS (direct fan-out, one step);
+ * SIM_ALGO_AUTO picks ALLPAIRS.  In-place is in_ptrs[r] == out_ptrs[r] +
+ * r*n_in_per_rank*esize for every r. */
+int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p,
+                   size_t n_in_per_rank, int dtype, int algo, void* stream);
+
+/* ---- selection and the cost model ------------------------------------- */
+
+/* The schedule SIM_ALGO_AUTO would run for this call, with its predicted
+ * time in microseconds: argmin over legal algos of
+ *   T_a = alpha_a * launches_a(p) + traffic_a(p, n, dtype) / B_a
+ * ("time = latency + bytes / bandwidth"), traffic_a being the schedule's
+ * algorithmic HBM bytes over all simulated ranks. */
+int sim_select(int p, size_t n, int dtype, int op, int* algo_out, double* predicted_us);
+
+/* The algo the most recent successful collective actually ran. */
+int sim_last_algo(void);
+
+/* Load per-algo alpha (us per launch) and B (GB/s) from a JSON file
+ * written by the calibration sweep.  Errors: SIM_ERR_INVALID_ARG. */
+int sim_model_load(const char* json_path);
+
+/* Predicted time of `algo` for `bytes_per_rank` bytes per rank. */
+int sim_model_predict(int algo, int p, int dtype, double bytes_per_rank, double* us_out);
+
+/* Override one algo's model: alpha_us and gbps always; `steps` (latency
+ * units) and `bytes_factor` (bytes moved per byte of message) replace the
+ * built-in laws when >= 0 -- e.g. the multi-GPU form 2(p-1) alpha +
+ * 2(p-1)/p n / B.  Pass negative values to keep the built-in laws. */
+int sim_model_set(int algo, double alpha_us, double steps, double bytes_factor, double gbps);
+
+/* Restore the built-in default model. */
+int sim_model_reset(void);
+
+/* ---- device errors ------------------------------------------------------ */
+
+/* Synchronise `stream`, then return and clear the device error word:
+ * SIM_OK, or SIM_ERR_TIMEOUT if a bounded wait expired since the last
+ * check (that call's outputs are undefined). */
+int sim_check_error(void* stream);
+
+/* ---- schedules and the verifier (host only; no device needed) --------- */
+
+/* Step and transfer counts of the lowered schedule of (algo, p). */
+int sim_schedule_info(int algo, int p, int* nsteps, int* nxfers);
+
+/* The transfers of one step: 4 ints each {kind, src rank, dst rank,
+ * chunk}, kind 0 REDUCE, 1 REDUCE_POST, 2 COPY, 3 GATHER_REDUCE,
+ * 4 FANOUT, 5 ONESHOT.  `*count` gets the number written (at most max). */
+int sim_schedule_xfers(int algo, int p, int step, int* out, int max, int* count);
+
+/* Symbolic state after `after_steps` steps: masks[r*p + c] = bit mask of
+ * the ranks whose contribution rank r's slot for chunk c holds. */
+int sim_schedule_state(int algo, int p, int after_steps, uint32_t* masks);
+
+/* Check() -- run the schedule symbolically and prove that every output
+ * chunk holds each rank's contribution exactly once, in the documented
+ * fold order, with no read/write hazard inside a step and the closed-form
+ * step count.  Returns SIM_OK or SIM_ERR_VERIFY with a message in diag. */
+int sim_verify_schedule(int algo, int p, char* diag, size_t diag_len);
+
+/* Same check on a caller-supplied schedule (nsteps steps; step s has
+ * counts[s] transfers laid out as in sim_schedule_xfers, concatenated in
+ * xfers).  `algo` names the fold order the result must follow. */
+int sim_verify_custom(int algo, int p, int nsteps, const int* counts, const int* xfers,
+                      char* diag, size_t diag_len);
+
+/* ---- test hooks --------------------------------------------------------- */
+enum {
+  SIM_DEBUG_EPOCH = 0,         /* set the LL epoch counter (next call uses value+1) */
+  SIM_DEBUG_SPIN_LIMIT = 1,    /* polls before a bounded wait gives up */
+  SIM_DEBUG_LL_WAIT_SKEW = 2,  /* consumers wait for epoch+value (0 = normal) */
+  SIM_DEBUG_FILL_LL = 3,       /* fill the LL buffer with this 64-bit packet (synchronous) */
+  SIM_DEBUG_LOG = 4,           /* 1: log one line per call to stderr (also SIM_DEBUG=1) */
+  SIM_DEBUG_WORKGROUPS = 5,    /* force the workgroup count of bulk kernels (0 = heuristic) */
+  SIM_DEBUG_UNROLL = 6         /* vectors in flight per lane in the p = 8 fold kernel: 1, 2 or 4 */
+};
+int sim_debug_set(int key, uint64_t value);
+int sim_debug_get(int key, uint64_t* value);
+
+const char* sim_status_string(int status);
+int sim_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SIMAR_H */

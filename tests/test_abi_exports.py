@@ -1,0 +1,49 @@
+"""The C-ABI library loads and exports every function include/simar.h
+declares (host only: no compute calls)."""
+import os
+import re
+import subprocess
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "simar.h")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(sim_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for must in ("sim_init", "sim_finalize", "sim_allreduce", "sim_reduce_scatter", "sim_all_gather",
+                 "sim_select", "sim_check_error", "sim_verify_schedule", "sim_model_load"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    import all_reduce_reduction_amd as sim
+    out = subprocess.run(["nm", "-D", "--defined-only", sim.LIBPATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(sim_\w+)", out))
+    missing = [n for n in declared() if n not in exported]
+    assert not missing, missing
+    for n in declared():
+        assert hasattr(sim.lib, n)
+    assert sim.sim_version() >= 1
+
+
+def test_status_strings_and_not_initialised():
+    import all_reduce_reduction_amd as sim
+    assert sim.sim_status_string(0) == "ok"
+    assert "aligned" in sim.sim_status_string(-3)
+    # collectives before sim_init are refused synchronously
+    st = sim.sim_allreduce([0, 0], [0, 0], 2, 4, "int32", "sum", "oneshot")
+    assert st == -9
+    assert sim.sim_check_error() == -9
+
+
+def test_binding_has_same_names_as_header():
+    import all_reduce_reduction_amd as sim
+    for n in declared():
+        assert callable(getattr(sim, n)), n

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle,
+element by element, on seeded inputs (small and ragged sizes spanning
+several workgroup tiles).  int32/fp32 bit-exact; fp16/bf16 within the
+2^-8 relative bar (and, as both sides round once from the same fp32
+schedule-order value, bit-exact too)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = ["ring", "allpairs", "oneshot", "oneshot_ll"]
+ESIZE = {"int32": 4, "fp32": 4, "fp16": 2, "bf16": 2}
+DTYPES = ["int32", "fp32", "fp16", "bf16"]
+OPS = ["sum", "prod", "min", "max", "avg"]
+# (p, n): tiny, ragged, n < p, several tiles (256 lanes x 2 vectors x 8 bf16 = 4096 elements per tile)
+SHAPES = [(2, 1), (2, 4), (3, 7), (8, 3), (4, 4096), (5, 4099), (8, 8 * 4096 * 3 + 13), (16, 16 * 1024 + 1),
+          (8, 65536), (7, 12345)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    import all_reduce_reduction_amd as sim
+    sim.sim_init(0, 16, 0)
+    yield sim
+
+
+def inputs(p, n, dtype, seed, orc):
+    rng = np.random.default_rng([seed, p, n])
+    if dtype == "int32":
+        return [rng.integers(-1000, 1000, n, endpoint=True, dtype=np.int32) for _ in range(p)]
+    x32 = [rng.standard_normal(n).astype(np.float32) for _ in range(p)]
+    if dtype == "fp32":
+        return x32
+    if dtype == "fp16":
+        return [x.astype(np.float16).view(np.uint16) for x in x32]
+    return [orc.f32_to_bf16(x) for x in x32]
+
+
+def prod_inputs(p, n, dtype, seed, orc):
+    """prod over 16 ranks of N(0,1) would under/overflow 16-bit; use [0.5, 2]."""
+    rng = np.random.default_rng([seed, p, n, 7])
+    if dtype == "int32":
+        return [rng.integers(-3, 4, n, dtype=np.int32) for _ in range(p)]
+    x32 = [rng.uniform(0.5, 2.0, n).astype(np.float32) for _ in range(p)]
+    if dtype == "fp32":
+        return x32
+    if dtype == "fp16":
+        return [x.astype(np.float16).view(np.uint16) for x in x32]
+    return [orc.f32_to_bf16(x) for x in x32]
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_allreduce_matches_oracle(orc, dtype, op, algo):
+    from tests.gpu_util import assert_parity, run_allreduce
+    for p, n in SHAPES:
+        xs = (prod_inputs if op == "prod" else inputs)(p, n, dtype, 1, orc)
+        want, steps = orc.allreduce(xs, dtype, op, algo)
+        for inplace in (False, True):
+            got = run_allreduce([x.copy() for x in xs], dtype, op, algo, inplace=inplace)
+            for r in range(p):
+                assert_parity(got[r], want[r], dtype, f"{algo} {dtype} {op} p={p} n={n} inplace={inplace} rank {r}")
+
+
+def test_worked_example_every_algo(orc):
+    import json, os
+    from tests.gpu_util import run_allreduce
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
+    xs = [np.array(v, dtype=np.int32) for v in g["inputs"]]
+    for algo in ALGOS:
+        for inplace in (False, True):
+            got = run_allreduce([x.copy() for x in xs], "int32", "sum", algo, inplace=inplace)
+            assert [y.tolist() for y in got] == g["outputs"], (algo, inplace)
+
+
+def test_oneshot_allpairs_ll_bit_identical(orc):
+    """The three share one fold order, so their fp results agree bit for bit,
+    while the ring's order gives different bits somewhere."""
+    from tests.gpu_util import bits, run_allreduce
+    xs = inputs(8, 8 * 5000, "fp32", 3, orc)
+    outs = {a: run_allreduce(xs, "fp32", "sum", a) for a in ALGOS}
+    for a in ("allpairs", "oneshot_ll"):
+        for r in range(8):
+            assert (bits(outs[a][r]) == bits(outs["oneshot"][r])).all(), a
+    assert (bits(outs["ring"][0]) != bits(outs["oneshot"][0])).any()
+
+
+def test_edge_values(orc):
+    """Signed zeros, subnormals, infinities and values near 16-bit limits."""
+    from tests.gpu_util import assert_parity, run_allreduce
+    specials = np.array([0.0, -0.0, 1e-40, -1e-40, 1.4e-45, 3.0e38, -3.0e38, np.inf, -np.inf,
+                         65504.0, 65520.0, 6.0e-8, 2.0 ** -24, 1.0, -1.0, 0.5], dtype=np.float32)
+    rng = np.random.default_rng(5)
+    for p in (2, 3, 8):
+        n = 8 * 40 + 3
+        x32 = [specials[rng.integers(0, len(specials), n)] for _ in range(p)]
+        for dtype in ("fp32", "fp16", "bf16"):
+            if dtype == "fp32":
+                xs = x32
+            elif dtype == "fp16":
+                with np.errstate(over="ignore"):
+                    xs = [x.astype(np.float16).view(np.uint16) for x in x32]
+            else:
+                xs = [orc.f32_to_bf16(x) for x in x32]
+            for op in ("min", "max"):
+                for algo in ALGOS:
+                    want, _ = orc.allreduce(xs, dtype, op, algo)
+                    got = run_allreduce(xs, dtype, op, algo)
+                    for r in range(p):
+                        assert_parity(got[r], want[r], dtype, f"{dtype} {op} {algo} p={p}")
+        # sums of finite values without overflow: signed zeros and subnormals
+        finite = np.array([0.0, -0.0, 1e-40, -1e-40, 1.4e-45, 1.0, -1.0, 2.0 ** -126, 2.0 ** -20, -3.0],
+                          dtype=np.float32)
+        x32 = [finite[rng.integers(0, len(finite), n)] for _ in range(p)]
+        for dtype in ("fp32", "fp16", "bf16"):
+            xs = (x32 if dtype == "fp32" else [x.astype(np.float16).view(np.uint16) for x in x32]
+                  if dtype == "fp16" else [orc.f32_to_bf16(x) for x in x32])
+            for op in ("sum", "prod", "avg"):
+                for algo in ALGOS:
+                    want, _ = orc.allreduce(xs, dtype, op, algo)
+                    got = run_allreduce(xs, dtype, op, algo)
+                    for r in range(p):
+                        assert_parity(got[r], want[r], dtype, f"finite {dtype} {op} {algo} p={p}")
+
+
+def test_16bit_ties_round_to_even(orc):
+    """Products of 16-bit values often land exactly half-way between two
+    16-bit numbers in fp32; the result must be the fp32 value rounded once,
+    ties to even (not a fused multiply-narrow)."""
+    from tests.gpu_util import assert_parity, run_allreduce
+    rng = np.random.default_rng(12)
+    for dtype in ("fp16", "bf16"):
+        for p in (2, 3, 8):
+            n = 4096 * 3 + 5
+            vals = np.array([1.0 + k / 64 for k in range(64)], dtype=np.float32)
+            x32 = [vals[rng.integers(0, 64, n)] * np.where(rng.random(n) < 0.5, -1, 1).astype(np.float32)
+                   for _ in range(p)]
+            xs = [x.astype(np.float16).view(np.uint16) for x in x32] if dtype == "fp16" else [orc.f32_to_bf16(x) for x in x32]
+            for op in ("prod", "sum", "avg"):
+                for algo in ALGOS:
+                    want, _ = orc.allreduce(xs, dtype, op, algo)
+                    got = run_allreduce(xs, dtype, op, algo)
+                    for r in range(p):
+                        assert_parity(got[r], want[r], dtype, f"ties {dtype} {op} {algo} p={p}")
+
+
+def test_int32_wraps(orc):
+    from tests.gpu_util import assert_parity, run_allreduce
+    rng = np.random.default_rng(9)
+    xs = [rng.integers(-2 ** 31, 2 ** 31 - 1, 3001, endpoint=True, dtype=np.int32) for _ in range(8)]
+    for op in OPS:
+        for algo in ALGOS:
+            want, _ = orc.allreduce(xs, "int32", op, algo)
+            got = run_allreduce(xs, "int32", op, algo)
+            for r in range(8):
+                assert_parity(got[r], want[r], "int32", f"{op} {algo}")
+
+
+@pytest.mark.parametrize("algo", ["ring", "allpairs"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_reduce_scatter_matches_oracle(orc, dtype, algo):
+    import all_reduce_reduction_amd as sim
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
+    for p, n_out in ((2, 1), (3, 5), (8, 1000), (8, 4096), (5, 999), (16, 257)):
+        for op in OPS:
+            xs = (prod_inputs if op == "prod" else inputs)(p, p * n_out, dtype, 2, orc)
+            want, steps = orc.reduce_scatter(xs, dtype, op, algo)
+            din = to_device(xs, dtype)
+            dout = empty_like_poisoned(n_out, dtype, p)
+            assert sim.sim_reduce_scatter(ptrs(din), ptrs(dout), p, n_out, dtype, op, algo, stream()) == 0
+            assert sim.sim_check_error(stream()) == 0
+            got = to_host(dout, dtype)
+            for r in range(p):
+                assert_parity(got[r], want[r], dtype, f"RS {algo} {dtype} {op} p={p} n_out={n_out} r={r}")
+            # in place: out[r] is chunk r of in[r] (16-byte aligned only when
+            # the chunk size is a multiple of 16 bytes)
+            din = to_device(xs, dtype)
+            outs = [d[r * n_out:(r + 1) * n_out] for r, d in enumerate(din)]
+            st = sim.sim_reduce_scatter(ptrs(din), ptrs(outs), p, n_out, dtype, op, algo, stream())
+            if (n_out * ESIZE[dtype]) % 16:
+                assert st == sim.STATUS_CODE["SIM_ERR_ALIGN"]
+                continue
+            assert st == 0
+            got = to_host(outs, dtype)
+            for r in range(p):
+                assert_parity(got[r], want[r], dtype, f"RS in-place {algo} {dtype} {op} p={p} r={r}")
+
+
+@pytest.mark.parametrize("algo", ["ring", "allpairs"])
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_all_gather_matches_oracle(orc, dtype, algo):
+    import torch
+    import all_reduce_reduction_amd as sim
+    from tests.gpu_util import TORCH_STORAGE, assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
+    for p, n_in in ((2, 1), (3, 5), (8, 1000), (8, 4096), (5, 999), (16, 257)):
+        xs = inputs(p, n_in, dtype, 3, orc)
+        want, steps = orc.all_gather(xs, dtype, algo)
+        din = to_device(xs, dtype)
+        dout = empty_like_poisoned(p * n_in, dtype, p)
+        assert sim.sim_all_gather(ptrs(din), ptrs(dout), p, n_in, dtype, algo, stream()) == 0
+        got = to_host(dout, dtype)
+        for r in range(p):
+            assert_parity(got[r], want[r], dtype, f"AG {algo} {dtype} p={p} n_in={n_in} r={r}")
+        # in place: in[r] is block r of out[r]
+        outs = empty_like_poisoned(p * n_in, dtype, p)
+        for r in range(p):
+            outs[r][r * n_in:(r + 1) * n_in].copy_(din[r])
+        ins = [o[r * n_in:(r + 1) * n_in] for r, o in enumerate(outs)]
+        st = sim.sim_all_gather(ptrs(ins), ptrs(outs), p, n_in, dtype, algo, stream())
+        if (n_in * ESIZE[dtype]) % 16:
+            assert st == sim.STATUS_CODE["SIM_ERR_ALIGN"]
+            continue
+        assert st == 0
+        got = to_host(outs, dtype)
+        for r in range(p):
+            assert_parity(got[r], want[r], dtype, f"AG in-place {algo} {dtype} p={p} r={r}")

@@ -1,0 +1,94 @@
+"""The alpha-beta selector of the library (host only), against the
+written-out model in oracle/model.py and the printed worked example."""
+import json
+import os
+
+import pytest
+
+import all_reduce_reduction_amd as sim
+from oracle import model
+
+G = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "alpha_beta_example.json")))
+
+
+@pytest.fixture
+def example_model():
+    p = G["p"]
+    k = 2 * (p - 1) / p
+    # all-pairs with LL (half the link rate), ring with LL128 (120/128)
+    sim.sim_model_set("allpairs", G["alpha_us"], 2, k, G["link_GBps"] * model.LL_EFFICIENCY)
+    sim.sim_model_set("ring", G["alpha_us"], 2 * (p - 1), k, G["link_GBps"] * model.LL128_EFFICIENCY)
+    yield
+    sim.sim_model_reset()
+
+
+@pytest.mark.parametrize("nbytes", [1024, 65536, 1 << 20, 4 << 20, 64 << 20, 1 << 30])
+def test_predictions_match_the_written_out_model(example_model, nbytes):
+    ta, tr = model.worked_example(nbytes)
+    # sim_model_predict takes bytes per rank; fp32 elements
+    assert sim.sim_model_predict("allpairs", 8, "fp32", nbytes) == pytest.approx(ta * 1e6, rel=1e-12)
+    assert sim.sim_model_predict("ring", 8, "fp32", nbytes) == pytest.approx(tr * 1e6, rel=1e-12)
+
+
+def test_printed_ratios(example_model):
+    r64k = sim.sim_model_predict("ring", 8, "fp32", 65536) / sim.sim_model_predict("allpairs", 8, "fp32", 65536)
+    assert round(r64k, 2) == G["printed"]["allpairs_speedup_at_64KB"]
+    r64m = sim.sim_model_predict("allpairs", 8, "fp32", 64 << 20) / sim.sim_model_predict("ring", 8, "fp32", 64 << 20)
+    assert round(r64m, 1) == G["printed"]["ring_speedup_at_64MB_about"]
+
+
+def test_argmin_switches_at_the_crossover(example_model):
+    # make one-shot and LL unattractive so the choice is ring vs all-pairs
+    sim.sim_model_set("oneshot", 1e9, -1, -1, 1.0)
+    sim.sim_model_set("oneshot_ll", 1e9, -1, -1, 1.0)
+    x = model.crossover_bytes()
+    below = int(x * 0.98) // 4 * 4
+    above = int(x * 1.02) // 4 * 4
+    assert sim.sim_select(8, below // 4, "fp32")[0] == "allpairs"
+    assert sim.sim_select(8, above // 4, "fp32")[0] == "ring"
+    algo, us = sim.sim_select(8, (64 << 20) // 4, "fp32")
+    assert algo == "ring" and us == pytest.approx(model.worked_example(64 << 20)[1] * 1e6)
+
+
+def test_ll_is_never_picked_above_its_buffer():
+    sim.sim_model_reset()
+    sim.sim_model_set("oneshot_ll", 0.0, -1, -1, 1e9)   # LL would win everything
+    try:
+        assert sim.sim_select(8, 4096, "fp16")[0] == "oneshot_ll"
+        assert sim.sim_select(8, (1 << 20) // 2, "fp16")[0] == "oneshot_ll"
+        assert sim.sim_select(8, (1 << 20) // 2 + 1, "fp16")[0] != "oneshot_ll"
+    finally:
+        sim.sim_model_reset()
+
+
+def test_builtin_traffic_laws():
+    sim.sim_model_reset()
+    for algo in ("ring", "allpairs", "oneshot", "oneshot_ll"):
+        sim.sim_model_set(algo, 0.0, -1, -1, 1e-3)   # 1 MB/s: time in us == bytes
+    S = 1 << 20
+    n = S // 2
+    assert sim.sim_model_predict("oneshot", 8, "bf16", S) == pytest.approx(2 * 8 * S)
+    assert sim.sim_model_predict("allpairs", 8, "bf16", S) == pytest.approx(17 * S)
+    assert sim.sim_model_predict("oneshot_ll", 8, "bf16", S) == pytest.approx(48 * S)
+    # ring, 16-bit with fp32 partials: 94 bytes per element at p = 8
+    assert sim.sim_model_predict("ring", 8, "bf16", S) == pytest.approx(94 * n)
+    # ring, 32-bit: 5 (p-1) S
+    assert sim.sim_model_predict("ring", 8, "fp32", S) == pytest.approx(35 * S)
+    sim.sim_model_reset()
+
+
+def test_model_json_roundtrip(tmp_path):
+    f = tmp_path / "m.json"
+    f.write_text(json.dumps({"device": "x", "algos": {"oneshot": {"alpha_us": 1.5, "gbps": 1000.0},
+                                                       "ring": {"alpha_us": 2.0, "gbps": 2000.0}}}))
+    sim.sim_model_load(str(f))
+    try:
+        assert sim.sim_model_predict("oneshot", 2, "fp32", 1000) == pytest.approx(1.5 + 4000 / 1e6)
+        bad = tmp_path / "bad.json"
+        bad.write_text('{"algos": {"ring": {"alpha_us": "x"}}}')
+        with pytest.raises(sim.SimError):
+            sim.sim_model_load(str(bad))
+        with pytest.raises(sim.SimError):
+            sim.sim_model_load(str(tmp_path / "missing.json"))
+    finally:
+        sim.sim_model_reset()
