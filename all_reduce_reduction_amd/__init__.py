@@ -22,7 +22,9 @@ except Exception:  # pragma: no cover - the host-only tests work without torch
     torch = None
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIBPATH = os.path.join(_HERE, "libsimar.so")
+# SIMAR_LIB selects another build of the same library (e.g. a variant
+# compiled with different cache-policy flags); the default is the in-tree one.
+LIBPATH = os.environ.get("SIMAR_LIB") or os.path.join(_HERE, "libsimar.so")
 
 SIM_OK = 0
 STATUS = {0: "SIM_OK", -1: "SIM_ERR_INVALID_ARG", -2: "SIM_ERR_UNSUPPORTED", -3: "SIM_ERR_ALIGN",

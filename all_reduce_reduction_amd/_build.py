@@ -14,6 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "simar")
 LIB = os.path.join(HERE, "libsimar.so")
+# extra compiler flags (space separated), e.g. "-DSIMAR_STORE_NT=0" for a variant build
+EXTRA = os.environ.get("SIMAR_EXTRA_FLAGS", "").split()
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -32,7 +34,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the gfx950 feature name; that note is harmless
     noise = "is not a recognized feature for this target"
@@ -44,22 +46,29 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 0) -> str:
-    """Compile every source and link libsimar.so; always rebuilds."""
+def build(jobs: int = 0, out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source and link libsimar.so (or `out`); always rebuilds."""
+    global BUILD
+    BUILD = build_dir
     if not shutil.which(HIPCC) and not os.path.exists(HIPCC):
         raise RuntimeError(f"hipcc not found at {HIPCC}")
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, sources()))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build())
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("--build-dir", default=BUILD)
+    a = ap.parse_args()
+    print(build(out=a.out, build_dir=a.build_dir))

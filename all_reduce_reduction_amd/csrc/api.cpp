@@ -25,7 +25,7 @@ namespace simar {
 namespace {
 
 constexpr int kVersion = 1;
-constexpr int kWgPerCu = 8;  // default workgroups per CU for bulk kernels
+constexpr int64_t kMaxTiles = 1 << 20;  // cap on workgroups per transfer
 
 struct Ctx {
   bool init = false;
@@ -42,7 +42,7 @@ struct Ctx {
   uint32_t wait_skew = 0;
   int log = 0;
   int force_wg = 0;
-  int unroll = 2;
+  int unroll = 1;
   int last_algo = -1;
   int env_algo = 0;
   int ll_occ[4][5] = {};
@@ -136,12 +136,14 @@ float inv_p_of(int p) {
   return one / fp;
 }
 
+// Workgroups per transfer (gridDim.x).  Measured on MI355X: streaming
+// kernels run fastest with one short-lived workgroup per kBlock * unroll
+// vectors (many waves in flight, no grid-stride loop), so the default covers
+// the transfer exactly; SIM_DEBUG_WORKGROUPS forces a total instead.
 int tiles_for(int64_t vecs_per_unit, int units, int unroll) {
+  if (g.force_wg > 0) return (int)std::max<int64_t>(1, g.force_wg / units);
   const int64_t want = (vecs_per_unit + (int64_t)kBlock * unroll - 1) / ((int64_t)kBlock * unroll);
-  int64_t cap = g.force_wg > 0 ? std::max<int64_t>(1, g.force_wg / units)
-                               : std::max<int64_t>(1, (int64_t)g.cu_count * kWgPerCu / units);
-  if (g.force_wg > 0) return (int)cap;
-  return (int)std::max<int64_t>(1, std::min<int64_t>(want, cap));
+  return (int)std::max<int64_t>(1, std::min<int64_t>(want, kMaxTiles));
 }
 
 // ---- launch glue ----------------------------------------------------------------
@@ -186,8 +188,8 @@ int run_copy_step(const Call& c, const std::vector<CopyXfer>& xs) {
     maxlen = std::max(maxlen, xs[k].hi - xs[k].lo);
   }
   if (a.nx == 0) return SIM_OK;
-  a.tiles = tiles_for((maxlen + V - 1) / V, a.nx, 2);
-  return hip_err(launch_copy(e, a, c.s));
+  a.tiles = tiles_for((maxlen + V - 1) / V, a.nx, g.unroll);
+  return hip_err(launch_copy(e, a, g.unroll, c.s));
 }
 
 // Ring reduce-scatter half.  final_out_chunk: outputs are chunk-sized (RS).
@@ -244,8 +246,8 @@ int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_c
       }
       x.vec_ok = (x.a_shift % V == 0) && (x.d_shift % V == 0);
     }
-    a.tiles = tiles_for((maxchunk + V - 1) / V, a.nx, 2);
-    int rc = hip_err(launch_ring_reduce(c.dtype, c.op, !first, last, a, c.s));
+    a.tiles = tiles_for((maxchunk + V - 1) / V, a.nx, g.unroll);
+    int rc = hip_err(launch_ring_reduce(c.dtype, c.op, !first, last, a, g.unroll, c.s));
     if (rc) return rc;
   }
   return SIM_OK;
@@ -807,7 +809,7 @@ int sim_debug_set(int key, uint64_t value) {
     case SIM_DEBUG_LOG: g.log = value ? 1 : 0; return SIM_OK;
     case SIM_DEBUG_WORKGROUPS: g.force_wg = (int)value; return SIM_OK;
     case SIM_DEBUG_UNROLL:
-      if (value != 1 && value != 2 && value != 4) return SIM_ERR_INVALID_ARG;
+      if (value != 1 && value != 2) return SIM_ERR_INVALID_ARG;
       g.unroll = (int)value;
       return SIM_OK;
     case SIM_DEBUG_FILL_LL: {

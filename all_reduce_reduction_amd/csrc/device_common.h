@@ -101,11 +101,29 @@ template <int DT, int OP> struct Op {
 };
 
 // ---- 16-byte vectors -----------------------------------------------------------
+// Bulk data is touched once per call, so loads and stores are streaming
+// (nontemporal) by default: they should not evict other data from L2/MALL.
+#ifndef SIMAR_LOAD_NT
+#define SIMAR_LOAD_NT 1
+#endif
+#ifndef SIMAR_STORE_NT
+#define SIMAR_STORE_NT 1
+#endif
 __device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
-  return __builtin_nontemporal_load((const u32x4*)((const char*)base + byte_off));
+  const u32x4* p = (const u32x4*)((const char*)base + byte_off);
+#if SIMAR_LOAD_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
 }
 __device__ __forceinline__ void st16(void* base, int64_t byte_off, u32x4 v) {
-  __builtin_nontemporal_store(v, (u32x4*)((char*)base + byte_off));
+  u32x4* p = (u32x4*)((char*)base + byte_off);
+#if SIMAR_STORE_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
 }
 
 // Unpack one 16-byte storage vector into EPV accumulator values.

@@ -130,14 +130,8 @@ static hipError_t go(const FoldArgs& a, hipStream_t s) {
 template <int DT, int OP>
 static hipError_t by_shape(int p, bool all_out, int unroll, const FoldArgs& a, hipStream_t s) {
   if (p == 8) {
-    if (all_out) {
-      if (unroll >= 4) return go<DT, OP, 8, true, 4>(a, s);
-      if (unroll == 2) return go<DT, OP, 8, true, 2>(a, s);
-      return go<DT, OP, 8, true, 1>(a, s);
-    }
-    if (unroll >= 4) return go<DT, OP, 8, false, 4>(a, s);
-    if (unroll == 2) return go<DT, OP, 8, false, 2>(a, s);
-    return go<DT, OP, 8, false, 1>(a, s);
+    if (all_out) return unroll == 2 ? go<DT, OP, 8, true, 2>(a, s) : go<DT, OP, 8, true, 1>(a, s);
+    return unroll == 2 ? go<DT, OP, 8, false, 2>(a, s) : go<DT, OP, 8, false, 1>(a, s);
   }
   return all_out ? go<DT, OP, 0, true, 1>(a, s) : go<DT, OP, 0, false, 1>(a, s);
 }

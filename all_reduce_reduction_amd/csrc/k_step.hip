@@ -156,47 +156,58 @@ __global__ void __launch_bounds__(kBlock) k_fill64(unsigned long long* p, unsign
 }
 
 // ---- launchers ----------------------------------------------------------------
-template <int DT, int OP>
+template <int DT, int OP, int U>
 static hipError_t ring_go(bool a_part, bool d_final, const RingArgs& a, hipStream_t s) {
   const dim3 grid(a.tiles, a.nx), block(kBlock);
   if (a_part) {
-    if (d_final) hipLaunchKernelGGL((k_ring_reduce<DT, OP, true, true, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_ring_reduce<DT, OP, true, false, 2>), grid, block, 0, s, a);
+    if (d_final) hipLaunchKernelGGL((k_ring_reduce<DT, OP, true, true, U>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_ring_reduce<DT, OP, true, false, U>), grid, block, 0, s, a);
   } else {
-    if (d_final) hipLaunchKernelGGL((k_ring_reduce<DT, OP, false, true, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_ring_reduce<DT, OP, false, false, 2>), grid, block, 0, s, a);
+    if (d_final) hipLaunchKernelGGL((k_ring_reduce<DT, OP, false, true, U>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_ring_reduce<DT, OP, false, false, U>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
+template <int DT, int OP>
+static hipError_t ring_by_unroll(int unroll, bool ap, bool df, const RingArgs& a, hipStream_t s) {
+  return unroll == 2 ? ring_go<DT, OP, 2>(ap, df, a, s) : ring_go<DT, OP, 1>(ap, df, a, s);
+}
+
 template <int DT>
-static hipError_t ring_by_op(int op, bool ap, bool df, const RingArgs& a, hipStream_t s) {
+static hipError_t ring_by_op(int op, int unroll, bool ap, bool df, const RingArgs& a, hipStream_t s) {
   switch (op) {
-    case SIM_SUM: return ring_go<DT, SIM_SUM>(ap, df, a, s);
-    case SIM_PROD: return ring_go<DT, SIM_PROD>(ap, df, a, s);
-    case SIM_MIN: return ring_go<DT, SIM_MIN>(ap, df, a, s);
-    case SIM_MAX: return ring_go<DT, SIM_MAX>(ap, df, a, s);
-    case SIM_AVG: return ring_go<DT, SIM_AVG>(ap, df, a, s);
+    case SIM_SUM: return ring_by_unroll<DT, SIM_SUM>(unroll, ap, df, a, s);
+    case SIM_PROD: return ring_by_unroll<DT, SIM_PROD>(unroll, ap, df, a, s);
+    case SIM_MIN: return ring_by_unroll<DT, SIM_MIN>(unroll, ap, df, a, s);
+    case SIM_MAX: return ring_by_unroll<DT, SIM_MAX>(unroll, ap, df, a, s);
+    case SIM_AVG: return ring_by_unroll<DT, SIM_AVG>(unroll, ap, df, a, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, const RingArgs& a,
-                              hipStream_t s) {
+                              int unroll, hipStream_t s) {
   switch (dtype) {
-    case SIM_INT32: return ring_by_op<SIM_INT32>(op, a_partial, d_final, a, s);
-    case SIM_FP32: return ring_by_op<SIM_FP32>(op, a_partial, d_final, a, s);
-    case SIM_FP16: return ring_by_op<SIM_FP16>(op, a_partial, d_final, a, s);
-    case SIM_BF16: return ring_by_op<SIM_BF16>(op, a_partial, d_final, a, s);
+    case SIM_INT32: return ring_by_op<SIM_INT32>(op, unroll, a_partial, d_final, a, s);
+    case SIM_FP32: return ring_by_op<SIM_FP32>(op, unroll, a_partial, d_final, a, s);
+    case SIM_FP16: return ring_by_op<SIM_FP16>(op, unroll, a_partial, d_final, a, s);
+    case SIM_BF16: return ring_by_op<SIM_BF16>(op, unroll, a_partial, d_final, a, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_copy(int esize, const CopyArgs& a, hipStream_t s) {
+hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s) {
   const dim3 grid(a.tiles, a.nx), block(kBlock);
-  if (esize == 4) hipLaunchKernelGGL((k_copy<4, 2>), grid, block, 0, s, a);
-  else if (esize == 2) hipLaunchKernelGGL((k_copy<2, 2>), grid, block, 0, s, a);
-  else return hipErrorInvalidValue;
+  if (esize == 4) {
+    if (unroll == 2) hipLaunchKernelGGL((k_copy<4, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_copy<4, 1>), grid, block, 0, s, a);
+  } else if (esize == 2) {
+    if (unroll == 2) hipLaunchKernelGGL((k_copy<2, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_copy<2, 1>), grid, block, 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

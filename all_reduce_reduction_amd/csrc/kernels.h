@@ -97,8 +97,8 @@ static_assert(sizeof(LLArgs) <= 4096, "kernel argument segment too large");
 hipError_t launch_fold(int dtype, int op, int p, bool all_out, const FoldArgs& a, int unroll,
                        hipStream_t s);
 hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, const RingArgs& a,
-                              hipStream_t s);
-hipError_t launch_copy(int esize, const CopyArgs& a, hipStream_t s);
+                              int unroll, hipStream_t s);
+hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s);
 hipError_t launch_ll(int dtype, int op, const LLArgs& a, int grid, hipStream_t s);
 hipError_t launch_fill64(unsigned long long* p, unsigned long long v, int64_t n, hipStream_t s);
 // Workgroups of the LL kernel (dtype, op) that fit on one CU at once.

@@ -203,7 +203,7 @@ enum {
   SIM_DEBUG_FILL_LL = 3,       /* fill the LL buffer with this 64-bit packet (synchronous) */
   SIM_DEBUG_LOG = 4,           /* 1: log one line per call to stderr (also SIM_DEBUG=1) */
   SIM_DEBUG_WORKGROUPS = 5,    /* force the workgroup count of bulk kernels (0 = heuristic) */
-  SIM_DEBUG_UNROLL = 6         /* vectors in flight per lane in the p = 8 fold kernel: 1, 2 or 4 */
+  SIM_DEBUG_UNROLL = 6         /* 16-byte vectors per lane per pass in bulk kernels: 1 or 2 */
 };
 int sim_debug_set(int key, uint64_t value);
 int sim_debug_get(int key, uint64_t* value);

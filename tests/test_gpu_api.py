@@ -1,0 +1,183 @@
+"""The boundary on the GPU: argument errors are refused synchronously with
+nothing enqueued, n == 0 is a no-op, the LL packet path survives stale
+flags, epoch wraparound and repeated calls, and a bounded wait that cannot
+be satisfied (forced from the host) reports SIM_ERR_TIMEOUT instead of
+hanging."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+OK, INVALID, UNSUPPORTED, ALIGN, ALIAS, TIMEOUT = 0, -1, -2, -3, -4, -7
+
+
+@pytest.fixture(autouse=True)
+def lib():
+    import all_reduce_reduction_amd as sim
+    sim.sim_init(0, 8, 0)
+    yield sim
+    sim.sim_debug_set("ll_wait_skew", 0)
+    sim.sim_debug_set("spin_limit", 1 << 22)
+
+
+def _bufs(p, n, dtype="fp32"):
+    import torch
+    from tests.gpu_util import empty_like_poisoned
+    ins = [torch.randn(n, device="cuda:0") for _ in range(p)]
+    outs = empty_like_poisoned(n, dtype, p)
+    return ins, outs
+
+
+def _untouched(outs):
+    import torch
+    torch.cuda.synchronize()
+    return all(bool(torch.isnan(o).all()) for o in outs)
+
+
+def test_argument_errors_enqueue_nothing(lib):
+    import torch
+    from tests.gpu_util import ptrs, stream
+    sim = lib
+    ins, outs = _bufs(4, 1024)
+    I, O, s = ptrs(ins), ptrs(outs), stream()
+    cases = {
+        "p=1": (sim.sim_allreduce(I[:1], O[:1], 1, 1024, "fp32", "sum", "oneshot", s), INVALID),
+        "p>p_max": (sim.sim_allreduce(I * 3, O * 3, 12, 1024, "fp32", "sum", "oneshot", s), INVALID),
+        "bad dtype": (sim.sim_allreduce(I, O, 4, 1024, 7, "sum", "oneshot", s), INVALID),
+        "bad op": (sim.sim_allreduce(I, O, 4, 1024, "fp32", 9, "oneshot", s), INVALID),
+        "bad algo": (sim.sim_allreduce(I, O, 4, 1024, "fp32", "sum", 11, s), INVALID),
+        "null ptr": (sim.sim_allreduce(I[:3] + [0], O, 4, 1024, "fp32", "sum", "oneshot", s), INVALID),
+        "misaligned": (sim.sim_allreduce([I[0] + 4] + I[1:], O, 4, 1000, "fp32", "sum", "oneshot", s), ALIGN),
+        "outputs overlap": (sim.sim_allreduce(I, [O[0], O[0] + 2048] + O[2:], 4, 1024, "fp32", "sum", "ring", s), ALIAS),
+        "output overlaps input": (sim.sim_allreduce(I, [I[1]] + O[1:], 4, 1024, "fp32", "sum", "ring", s), ALIAS),
+        "mixed in-place": (sim.sim_allreduce(I, [I[0]] + O[1:], 4, 1024, "fp32", "sum", "ring", s), INVALID),
+        "rs oneshot": (sim.sim_reduce_scatter(I, O, 4, 256, "fp32", "sum", "oneshot", s), UNSUPPORTED),
+        "ag ll": (sim.sim_all_gather(I, O, 4, 256, "fp32", "oneshot_ll", s), UNSUPPORTED),
+    }
+    for name, (got, want) in cases.items():
+        assert got == want, (name, got, want)
+    assert _untouched(outs), "an erroring call wrote to an output"
+
+
+def test_ll_above_its_buffer_is_refused(lib):
+    import torch
+    from tests.gpu_util import ptrs, stream
+    sim = lib
+    n = sim.LL_MAX_BYTES_PER_RANK // 4 + 4
+    ins, outs = _bufs(8, n)
+    assert sim.sim_allreduce(ptrs(ins), ptrs(outs), 8, n, "fp32", "sum", "oneshot_ll", stream()) == UNSUPPORTED
+    assert _untouched(outs)
+    # the selector never picks it there
+    assert sim.sim_select(8, n, "fp32")[0] != "oneshot_ll"
+
+
+def test_zero_elements_is_a_noop(lib):
+    from tests.gpu_util import ptrs, stream
+    sim = lib
+    ins, outs = _bufs(4, 16)
+    for algo in ("ring", "allpairs", "oneshot", "oneshot_ll", "auto"):
+        assert sim.sim_allreduce(ptrs(ins), ptrs(outs), 4, 0, "fp32", "sum", algo, stream()) == OK
+    assert sim.sim_reduce_scatter(ptrs(ins), ptrs(outs), 4, 0, "fp32", "sum", "ring", stream()) == OK
+    assert sim.sim_all_gather(ptrs(ins), ptrs(outs), 4, 0, "fp32", "ring", stream()) == OK
+    assert _untouched(outs)
+
+
+def test_init_argument_errors(lib):
+    sim = lib
+    assert sim.lib.sim_init(0, 1, 0) == INVALID
+    assert sim.lib.sim_init(0, 17, 0) == INVALID
+    assert sim.lib.sim_init(-1, 8, 0) == INVALID
+    sim.sim_init(0, 8, 1 << 20)     # and a good one works again
+    assert sim.sim_check_error() == OK
+
+
+def _ll_case(orc, p=8, n=4096 * 3 + 1, seed=0):
+    import synthdata
+    xs = synthdata.normal(40 + seed, p, n, "fp16")
+    want, _ = orc.allreduce(xs, "fp16", "sum", "oneshot_ll")
+    return xs, want
+
+
+def test_ll_ignores_stale_flags(lib, orc):
+    from tests.gpu_util import run_allreduce
+    sim = lib
+    xs, want = _ll_case(orc)
+    run_allreduce(xs, "fp16", "sum", "oneshot_ll")
+    cur = sim.sim_debug_get("epoch")
+    # every packet now carries the previous call's flag with garbage data
+    sim.sim_debug_set("fill_ll", (cur << 32) | 0xDEADBEEF)
+    got = run_allreduce(xs, "fp16", "sum", "oneshot_ll")
+    for r in range(8):
+        assert (got[r] == want[r]).all()
+    # and an unrelated flag value
+    sim.sim_debug_set("fill_ll", (0x13572468 << 32) | 0x0BADF00D)
+    got = run_allreduce(xs, "fp16", "sum", "oneshot_ll")
+    for r in range(8):
+        assert (got[r] == want[r]).all()
+
+
+def test_ll_epoch_wraparound(lib, orc):
+    from tests.gpu_util import run_allreduce
+    sim = lib
+    xs, want = _ll_case(orc, seed=1)
+    sim.sim_debug_set("epoch", 0xFFFFFFFD)
+    seen = []
+    for _ in range(4):
+        got = run_allreduce(xs, "fp16", "sum", "oneshot_ll")
+        seen.append(sim.sim_debug_get("epoch"))
+        for r in range(8):
+            assert (got[r] == want[r]).all()
+    assert seen == [0xFFFFFFFE, 0xFFFFFFFF, 1, 2]
+
+
+def test_ll_repeated_calls_without_sync(lib, orc):
+    import torch
+    from tests.gpu_util import empty_like_poisoned, ptrs, stream, to_device, to_host
+    sim = lib
+    xs, want = _ll_case(orc, seed=2)
+    din = to_device(xs, "fp16")
+    outs = [empty_like_poisoned(xs[0].size, "fp16", 8) for _ in range(3)]
+    for k in range(30):  # back to back, alternating output sets and schedules
+        algo = "oneshot_ll" if k % 3 else "oneshot"
+        assert sim.sim_allreduce(ptrs(din), ptrs(outs[k % 3]), 8, xs[0].size, "fp16", "sum", algo, stream()) == OK
+    assert sim.sim_check_error(stream()) == OK
+    for o in outs:
+        got = to_host(o, "fp16")
+        for r in range(8):
+            assert (got[r] == want[r]).all()
+
+
+def test_forced_timeout_reports_and_recovers(lib, orc):
+    """Consumers are told to wait for a flag no producer writes; every poll
+    gives up after a tiny spin limit, the kernel exits, and the error word
+    says SIM_ERR_TIMEOUT.  The next call is correct again."""
+    from tests.gpu_util import ptrs, run_allreduce, stream, to_device, empty_like_poisoned
+    sim = lib
+    xs, want = _ll_case(orc, n=2048, seed=3)
+    sim.sim_debug_set("spin_limit", 64)
+    sim.sim_debug_set("ll_wait_skew", 1)
+    din = to_device(xs, "fp16")
+    dout = empty_like_poisoned(xs[0].size, "fp16", 8)
+    assert sim.sim_allreduce(ptrs(din), ptrs(dout), 8, xs[0].size, "fp16", "sum", "oneshot_ll", stream()) == OK
+    assert sim.sim_check_error(stream()) == TIMEOUT
+    assert sim.sim_check_error(stream()) == OK          # the word was cleared
+    sim.sim_debug_set("ll_wait_skew", 0)
+    sim.sim_debug_set("spin_limit", 1 << 22)
+    got = run_allreduce(xs, "fp16", "sum", "oneshot_ll")
+    for r in range(8):
+        assert (got[r] == want[r]).all()
+
+
+def test_auto_reports_what_ran_and_logs(lib, capfd):
+    from tests.gpu_util import ptrs, stream
+    sim = lib
+    ins, outs = _bufs(8, 8192)
+    sim.sim_debug_set("log", 1)
+    try:
+        assert sim.sim_allreduce(ptrs(ins), ptrs(outs), 8, 8192, "fp32", "sum", "auto", stream()) == OK
+    finally:
+        sim.sim_debug_set("log", 0)
+    pick, _ = sim.sim_select(8, 8192, "fp32")
+    assert sim.sim_last_algo() == pick
+    err = capfd.readouterr().err
+    assert "AllReduce" in err and f"algo {pick}" in err
