@@ -107,9 +107,17 @@ def _code(table, v, what):
     return int(v)
 
 
+# The model fitted by calibrate.py on MI355X; sim_init loads it unless the
+# SIM_CALIB environment variable names another file (which the C library
+# then loads itself).
+CALIBRATION = os.path.join(_HERE, "calib", "mi355x.json")
+
+
 # ---- the C functions, one to one ------------------------------------------------
 def sim_init(device: int = 0, p_max: int = MAX_RANKS, max_bytes_per_rank: int = 0) -> None:
     _check(lib.sim_init(device, p_max, max_bytes_per_rank), "sim_init")
+    if not os.environ.get("SIM_CALIB") and os.path.exists(CALIBRATION):
+        sim_model_load(CALIBRATION)
 
 
 def sim_finalize() -> None:

@@ -16,12 +16,18 @@
 // All-pairs step 1 / direct reduce-scatter is the same fold with only the
 // owner's output written (owner-only mode).
 //
-// Layout: grid = (tiles, p); blockIdx.y is the chunk j, so the fold order is
-// uniform over a workgroup and the operand pointers are chosen once, in
-// scalar registers.  A workgroup walks its chunk in spans of kBlock * U
-// vectors; a ragged chunk edge (a vector that would straddle two chunks, or
-// a misaligned operand) is done element by element so every element keeps
-// its own chunk's order.
+// Layout: a 1-D grid of tiles * p workgroups; workgroup b folds chunk
+// j = b mod p, tile b / p.  The chunk is uniform over a workgroup, so the
+// fold order is too and the operand pointers are chosen once, in scalar
+// registers.  Neighbouring workgroups -- the ones in flight together --
+// work on different chunks: at any moment the 2p streams of the chunk being
+// folded are spread over p regions of every buffer instead of one, which
+// measured ~13% faster on MI355X than running the chunks one after another
+// (the same offset in p buffers tends to land on the same HBM channels).
+// A workgroup walks its chunk in spans of kBlock * U vectors; a ragged
+// chunk edge (a vector that would straddle two chunks, or a misaligned
+// operand) is done element by element so every element keeps its own
+// chunk's order.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -35,7 +41,8 @@ __global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
   constexpr int E = Ty<DT>::E;
   constexpr int MAXP = P ? P : SIM_MAX_RANKS;
   const int p = P ? P : a.p;
-  const int j = blockIdx.y;
+  const int j = (int)(blockIdx.x % (unsigned)p);
+  const int64_t tile = blockIdx.x / (unsigned)p;
   const int64_t lo = a.lo[j], hi = a.lo[j + 1];
   const float inv_p = a.inv_p;
 
@@ -60,7 +67,7 @@ __global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
   const int64_t oshift = ALL_OUT ? 0 : a.out_shift[j];
   void* const yj = a.y[j];
 
-  for (int64_t base = (int64_t)blockIdx.x * span; base < nvec; base += stride) {
+  for (int64_t base = tile * span; base < nvec; base += stride) {
     u32x4 L[U][MAXP];
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -104,7 +111,7 @@ __global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
   }
 
   // ragged edges, element by element
-  for (int64_t s = (int64_t)blockIdx.x * kBlock + tid; s < nscalar; s += (int64_t)a.tiles * kBlock) {
+  for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)a.tiles * kBlock) {
     const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
     A acc = O::pre(load_elem<DT>(xp[0], i), inv_p);
 #pragma unroll
@@ -123,7 +130,8 @@ __global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
 
 template <int DT, int OP, int P, bool ALL_OUT, int U>
 static hipError_t go(const FoldArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_fold<DT, OP, P, ALL_OUT, U>), dim3(a.tiles, a.p), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL((k_fold<DT, OP, P, ALL_OUT, U>), dim3((unsigned)a.tiles * (unsigned)a.p), dim3(kBlock), 0, s,
+                     a);
   return hipGetLastError();
 }
 

@@ -1,7 +1,7 @@
 // k_step.hip -- per-step kernels of the multi-launch schedules (gfx950).
 //
 // k_ring_reduce runs one reduce-scatter step of the ring: for each of the
-// step's transfers (one per rank, blockIdx.y), the arriving running value of
+// step's transfers (one per rank), the arriving running value of
 // the chunk is combined with the receiving rank's own element and written
 // on -- the fused receive-reduce-send primitive of NCCL's runRing
 // ("Inside NCCL all-reduce", section "The ring, exactly as the kernel runs
@@ -54,7 +54,11 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
   typedef Op<DT, OP> O;
   constexpr int V = epv<DT>();
   constexpr int E = Ty<DT>::E;
-  const RingXfer x = args.x[blockIdx.y];
+  // 1-D grid, transfers interleaved: workgroup b runs tile b / nx of
+  // transfer b mod nx, so the transfers in flight together cover every chunk
+  const unsigned xi = blockIdx.x % (unsigned)args.nx;
+  const int64_t tile = blockIdx.x / (unsigned)args.nx;
+  const RingXfer x = args.x[xi];
   const float inv_p = args.inv_p;
   const int p = args.p;
   const int64_t lo = x.lo, hi = x.hi;
@@ -68,7 +72,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
   const int64_t span = (int64_t)kBlock * U;
   const int64_t stride = (int64_t)args.tiles * span;
 
-  for (int64_t base = (int64_t)blockIdx.x * span; base < nvec; base += stride) {
+  for (int64_t base = tile * span; base < nvec; base += stride) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int64_t v = base + u * kBlock + tid;
@@ -96,7 +100,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
     }
   }
 
-  for (int64_t s = (int64_t)blockIdx.x * kBlock + tid; s < nscalar; s += (int64_t)args.tiles * kBlock) {
+  for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)args.tiles * kBlock) {
     const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
     A in;
     if constexpr (A_PART) in = ((const A*)x.a)[i - x.a_shift];
@@ -110,7 +114,9 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
 template <int E, int U>
 __global__ void __launch_bounds__(kBlock) k_copy(CopyArgs args) {
   constexpr int V = 16 / E;
-  const CopyXfer& x = args.x[blockIdx.y];
+  const unsigned xi = blockIdx.x % (unsigned)args.nx;  // transfers interleaved, as above
+  const int64_t tile = blockIdx.x / (unsigned)args.nx;
+  const CopyXfer& x = args.x[xi];
   const int64_t lo = x.lo, hi = x.hi;
   const int nd = x.ndst;
   int64_t head = x.vec_ok ? (int64_t)((V - (lo % V)) % V) : (hi - lo);
@@ -123,7 +129,7 @@ __global__ void __launch_bounds__(kBlock) k_copy(CopyArgs args) {
   const int64_t span = (int64_t)kBlock * U;
   const int64_t stride = (int64_t)args.tiles * span;
 
-  for (int64_t base = (int64_t)blockIdx.x * span; base < nvec; base += stride) {
+  for (int64_t base = tile * span; base < nvec; base += stride) {
     u32x4 w[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
@@ -139,7 +145,7 @@ __global__ void __launch_bounds__(kBlock) k_copy(CopyArgs args) {
       }
     }
   }
-  for (int64_t s = (int64_t)blockIdx.x * kBlock + tid; s < nscalar; s += (int64_t)args.tiles * kBlock) {
+  for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)args.tiles * kBlock) {
     const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
     if constexpr (E == 4) {
       const uint32_t w = ((const uint32_t*)x.src)[i - x.src_shift];
@@ -158,7 +164,7 @@ __global__ void __launch_bounds__(kBlock) k_fill64(unsigned long long* p, unsign
 // ---- launchers ----------------------------------------------------------------
 template <int DT, int OP, int U>
 static hipError_t ring_go(bool a_part, bool d_final, const RingArgs& a, hipStream_t s) {
-  const dim3 grid(a.tiles, a.nx), block(kBlock);
+  const dim3 grid((unsigned)a.tiles * (unsigned)a.nx), block(kBlock);
   if (a_part) {
     if (d_final) hipLaunchKernelGGL((k_ring_reduce<DT, OP, true, true, U>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_ring_reduce<DT, OP, true, false, U>), grid, block, 0, s, a);
@@ -198,7 +204,7 @@ hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, c
 }
 
 hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s) {
-  const dim3 grid(a.tiles, a.nx), block(kBlock);
+  const dim3 grid((unsigned)a.tiles * (unsigned)a.nx), block(kBlock);
   if (esize == 4) {
     if (unroll == 2) hipLaunchKernelGGL((k_copy<4, 2>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_copy<4, 1>), grid, block, 0, s, a);

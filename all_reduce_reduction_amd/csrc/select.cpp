@@ -23,13 +23,16 @@
 
 namespace simar {
 
+// Built-in defaults: the fit of the calibration sweep on MI355X (p = 8,
+// bf16, 1.5 KiB .. 192 MiB per rank), rounded.  A calibration file loaded
+// with sim_model_load() or SIM_CALIB replaces them.
 Model default_model() {
   Model m;
-  for (int a = 0; a < kNumAlgos; a++) {
-    m.a[a].alpha_us = 4.0;
-    m.a[a].gbps = 4500.0;
-  }
-  m.a[SIM_ALGO_ONESHOT_LL].gbps = 1500.0;
+  m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING] = {4.0, 6550.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ALLPAIRS] = {4.7, 7000.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT] = {5.1, 6600.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT_LL] = {9.4, 6750.0, -1.0, -1.0};
   return m;
 }
 

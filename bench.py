@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip per-algo and latency figures")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed steps of the headline workload (for rocprofv3 runs)")
+    ap.add_argument("--profile-copy", action="store_true",
+                    help="only a plain 512 MiB -> 512 MiB device copy (the counter scale reference)")
     return ap.parse_args()
 
 
@@ -83,19 +85,32 @@ def time_calls(fn, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / 1e3 / steps
 
 
-def load_traffic(kernel: str):
-    """rocprofv3 counter summary for `kernel` (committed under profiles/)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["all_reduce_reduction_amd/csrc/k_fold.hip", "all_reduce_reduction_amd/csrc/k_step.hip",
+                  "all_reduce_reduction_amd/csrc/device_common.h", "all_reduce_reduction_amd/csrc/kernels.h"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(algo: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic_bf16_p8_64MiB.json")
     if not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
     except Exception:
         return None
-    ent = d.get("kernels", {}).get(kernel)
-    if not ent or ent.get("source_hash") != d.get("source_hash_now"):
+    if d.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return ent.get("bytes_per_launch")
+    ent = d.get("algos", {}).get(algo)
+    return None if not ent else ent.get("hbm_bytes_per_launch_scaled")
 
 
 def main():
@@ -114,6 +129,26 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.profile_copy:
+        # Counter scale references of known size: (1) the library's own copy
+        # kernel (k_copy, same 16-byte streaming loads/stores as k_fold) as the
+        # all-gather step of a p = 2 fp32 ring all-reduce of 256 MiB per rank:
+        # each k_copy launch reads 256 MiB and writes 256 MiB; (2) torch's
+        # device-to-device copy of 512 MiB.
+        sim.sim_init(0, 2, 0)
+        n2 = (256 << 20) // 4
+        bufs = [torch.empty(n2, dtype=torch.float32, device=dev).fill_(1.0) for _ in range(4)]
+        ptr = [b.data_ptr() for b in bufs]
+        s2 = int(torch.cuda.current_stream().cuda_stream)
+        t1 = time_calls(lambda: sim.sim_allreduce(ptr[:2], ptr[2:], 2, n2, "fp32", "sum", "ring", s2),
+                        args.steps, args.warmup)
+        src = torch.empty(S * P // 2 // 4, dtype=torch.int32, device=dev).fill_(7)
+        dst = torch.empty_like(src)
+        t2 = time_calls(lambda: dst.copy_(src), args.steps, args.warmup)
+        print(json.dumps({"k_copy_bytes_read": 2 * n2 * 4 // 2 * 1, "k_copy_bytes_written": n2 * 4,
+                          "us_per_ring_call": t1 * 1e6, "torch_copy_bytes": src.numel() * 4,
+                          "us_per_torch_copy": t2 * 1e6}), flush=True)
+        return
     sim.sim_init(0, P, S)
     stream = int(torch.cuda.current_stream().cuda_stream)
 

@@ -92,3 +92,16 @@ def test_model_json_roundtrip(tmp_path):
             sim.sim_model_load(str(tmp_path / "missing.json"))
     finally:
         sim.sim_model_reset()
+
+
+def test_packaged_calibration_loads_and_picks_oneshot():
+    """The MI355X fit: on one HBM the fused one-shot moves the fewest bytes in
+    one launch, so it is the model's pick at every evaluation size."""
+    sim.sim_model_load(sim.CALIBRATION)
+    try:
+        for dtype, n in [("bf16", 8192 * t) for t in (1, 16, 256, 4096)] + [("fp16", (1 << k) // 2) for k in range(10, 21)]:
+            assert sim.sim_select(8, n, dtype)[0] == "oneshot"
+        rep = json.load(open(os.path.join(os.path.dirname(sim.CALIBRATION), "selector_check_mi355x.json")))
+        assert rep["strict_matches"] == rep["cases"]
+    finally:
+        sim.sim_model_reset()
