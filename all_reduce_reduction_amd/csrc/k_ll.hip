@@ -20,9 +20,10 @@
 //            (owner first, then ascending) and writes every rank's output.
 // Every workgroup produces before it consumes and all workgroups are
 // co-resident (the host caps the grid at the occupancy limit), so every
-// poll is answered; each poll is still bounded by spin_limit, and on expiry
-// the lane records SIM_ERR_TIMEOUT in the device error word, skips its
-// writes and the kernel exits normally.
+// poll is answered.  A lane issues its p polls together and re-polls only
+// the packets still missing, at most spin_limit rounds; on expiry it
+// records SIM_ERR_TIMEOUT in the device error word, skips its writes and
+// the kernel exits normally.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -57,30 +58,37 @@ __global__ void __launch_bounds__(kBlock) k_ll(LLArgs a) {
     const int64_t tile = (t + a.shift) % a.ntiles;
     const int64_t kend = min(nwords, (tile + 1) * a.tile_words);
     for (int64_t k = tile * a.tile_words + threadIdx.x; k < kend; k += kBlock) {
-      uint32_t d[SIM_MAX_RANKS];
-      bool ok = true;
+      // issue the p polls back to back (one memory round trip when every
+      // packet is already there), then re-poll only the packets still missing
+      unsigned long long pk[SIM_MAX_RANKS];
 #pragma unroll
-      for (int q = 0; q < SIM_MAX_RANKS; q++) {
-        d[q] = 0;
-        if (q < p && ok) {
-          const unsigned long long* src = a.ll + q * a.ll_stride + k;
-          unsigned long long pk = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          unsigned long long spins = 0;
-          while ((unsigned)(pk >> 32) != a.wait_epoch) {
-            if (++spins > a.spin_limit) {
-              ok = false;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            pk = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          d[q] = (uint32_t)pk;
+      for (int q = 0; q < SIM_MAX_RANKS; q++)
+        if (q < p)
+          pk[q] = __hip_atomic_load(a.ll + q * a.ll_stride + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bool ok = true;
+      for (unsigned long long round = 0;; round++) {
+        bool all = true;
+#pragma unroll
+        for (int q = 0; q < SIM_MAX_RANKS; q++)
+          if (q < p && (unsigned)(pk[q] >> 32) != a.wait_epoch) all = false;
+        if (all) break;
+        if (round >= a.spin_limit) {
+          ok = false;
+          break;
         }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int q = 0; q < SIM_MAX_RANKS; q++)
+          if (q < p && (unsigned)(pk[q] >> 32) != a.wait_epoch)
+            pk[q] = __hip_atomic_load(a.ll + q * a.ll_stride + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (!ok) {
         __hip_atomic_store(a.err, (int)SIM_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         continue;
       }
+      uint32_t d[SIM_MAX_RANKS];
+#pragma unroll
+      for (int q = 0; q < SIM_MAX_RANKS; q++) d[q] = (q < p) ? (uint32_t)pk[q] : 0u;
       uint32_t outw = 0;
 #pragma unroll
       for (int e = 0; e < EPW; e++) {
