@@ -33,12 +33,12 @@ STATUS = {0: "SIM_OK", -1: "SIM_ERR_INVALID_ARG", -2: "SIM_ERR_UNSUPPORTED", -3:
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 DTYPES = {"int32": 0, "fp32": 1, "fp16": 2, "bf16": 3}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
-ALGOS = {"auto": 0, "ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4}
+ALGOS = {"auto": 0, "ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4, "ring_fifo": 5}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 ESIZE = {"int32": 4, "fp32": 4, "fp16": 2, "bf16": 2}
 XFER_KINDS = {0: "REDUCE", 1: "REDUCE_POST", 2: "COPY", 3: "GATHER_REDUCE", 4: "FANOUT", 5: "ONESHOT"}
 DEBUG = {"epoch": 0, "spin_limit": 1, "ll_wait_skew": 2, "fill_ll": 3, "log": 4, "workgroups": 5,
-         "unroll": 6}
+         "unroll": 6, "fifo_channels": 7, "fifo_slots": 8, "fifo_withhold": 9}
 MAX_RANKS = 16
 LL_MAX_BYTES_PER_RANK = 1 << 20
 
@@ -127,6 +127,18 @@ def sim_finalize() -> None:
 def sim_allreduce(in_ptrs, out_ptrs, p, n, dtype, op, algo, stream=0) -> int:
     return lib.sim_allreduce(_ptr_array(in_ptrs), _ptr_array(out_ptrs), p, n, _code(DTYPES, dtype, "dtype"),
                              _code(OPS, op, "op"), _code(ALGOS, algo, "algo"), stream or None)
+
+
+def prepare_allreduce(in_ptrs, out_ptrs, p, n, dtype, op, algo, stream=0):
+    """The same call as sim_allreduce with its arguments marshalled once:
+    returns a function of no arguments that calls the C entry point and
+    returns its status (for loops that repeat one call, where Python-side
+    marshalling would otherwise dominate a few-microsecond call)."""
+    f = lib.sim_allreduce
+    ia, oa = _ptr_array(in_ptrs), _ptr_array(out_ptrs)
+    args = (ia, oa, p, n, _code(DTYPES, dtype, "dtype"), _code(OPS, op, "op"), _code(ALGOS, algo, "algo"),
+            stream or None)
+    return lambda: f(*args)
 
 
 def sim_reduce_scatter(in_ptrs, out_ptrs, p, n_out_per_rank, dtype, op, algo, stream=0) -> int:

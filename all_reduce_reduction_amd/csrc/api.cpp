@@ -26,6 +26,10 @@ namespace {
 
 constexpr int kVersion = 1;
 constexpr int64_t kMaxTiles = 1 << 20;  // cap on workgroups per transfer
+// single-launch ring: FIFO geometry
+constexpr int kFifoMaxChannels = 64;      // channels per rank
+constexpr int kFifoMaxSlots = 8;          // slots per FIFO
+constexpr int kFifoSlotElems = kBlock * 16;  // 4096 elements (16 KiB of 32-bit words) per slot
 
 struct Ctx {
   bool init = false;
@@ -38,7 +42,7 @@ struct Ctx {
   int64_t ll_stride = 0;  // packets per rank
   int* err = nullptr;
   uint32_t epoch = 0;
-  unsigned long long spin_limit = 1ull << 22;
+  unsigned long long spin_limit = 1ull << 20;
   uint32_t wait_skew = 0;
   int log = 0;
   int force_wg = 0;
@@ -46,6 +50,13 @@ struct Ctx {
   int last_algo = -1;
   int env_algo = 0;
   int ll_occ[4][5] = {};
+  uint32_t* fifo = nullptr;
+  unsigned long long* fifo_sem = nullptr;
+  uint32_t fifo_epoch = 0;
+  int fifo_channels = 0;  // 0: heuristic
+  int fifo_slots = 4;
+  int fifo_withhold = 0;  // test hook: rank 0's workgroups leave at once
+  int fifo_occ[4][5] = {};
   Model model = default_model();
 };
 
@@ -53,13 +64,22 @@ Ctx g;
 
 int esize_of(int dtype) { return (dtype == SIM_FP16 || dtype == SIM_BF16) ? 2 : 4; }
 const char* algo_name(int a) {
-  static const char* n[] = {"auto", "ring", "allpairs", "oneshot", "oneshot_ll"};
-  return (a >= 0 && a < 5) ? n[a] : "?";
+  static const char* n[] = {"auto", "ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"};
+  return (a >= 0 && a < 6) ? n[a] : "?";
 }
 
 int64_t chunk_lo(int64_t n, int p, int c) { return (int64_t)(((__int128)c * n) / p); }
 
 int hip_err(hipError_t e) { return e == hipSuccess ? SIM_OK : SIM_ERR_HIP; }
+
+// Make the library's device current on the calling thread (only switches
+// when another device is current: a per-call switch costs launch latency).
+int use_device() {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return SIM_ERR_HIP;
+  if (cur != g.device && hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+  return SIM_OK;
+}
 
 // ---- validation -------------------------------------------------------------
 struct Range {
@@ -253,6 +273,49 @@ int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_c
   return SIM_OK;
 }
 
+// The whole ring in one launch (k_ring_fifo): p * C persistent workgroups,
+// all co-resident, exchanging partials through bounded FIFOs.
+int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
+  const int p = c.p;
+  RingFifoArgs a;
+  std::memset(&a, 0, sizeof a);
+  int64_t maxchunk = 0;
+  for (int q = 0; q < p; q++) {
+    a.x[q] = c.x[q];
+    a.y[q] = c.y[q];
+    maxchunk = std::max(maxchunk, lo[q + 1] - lo[q]);
+  }
+  for (int q = 0; q <= p; q++) a.lo[q] = lo[q];
+  int& occ = g.fifo_occ[c.dtype][c.op];
+  if (occ == 0) occ = ring_fifo_blocks_per_cu(c.dtype, c.op);
+  const int64_t resident = (int64_t)occ * g.cu_count;  // every workgroup must be resident at once
+  int64_t C = g.fifo_channels > 0 ? g.fifo_channels
+                                  : std::max<int64_t>(1, (maxchunk + kFifoSlotElems - 1) / kFifoSlotElems);
+  C = std::min<int64_t>(C, kFifoMaxChannels);
+  C = std::min<int64_t>(C, std::max<int64_t>(1, resident / p));
+  const int64_t slice = (maxchunk + C - 1) / C;
+  uint32_t epoch = g.fifo_epoch + 1;
+  if (epoch == 0) {  // wrapped: clear every counter so no stale value can compare high
+    int rc = hip_err(launch_fill64(g.fifo_sem, 0ull, (int64_t)g.p_max * kFifoMaxChannels * 2, c.s));
+    if (rc) return rc;
+    epoch = 1;
+  }
+  g.fifo_epoch = epoch;
+  a.fifo = g.fifo;
+  a.sem = g.fifo_sem;
+  a.err = g.err;
+  a.spin_limit = g.spin_limit;
+  a.p = p;
+  a.C = (int)C;
+  a.NS = g.fifo_slots;
+  a.nsub = (int)std::max<int64_t>(1, (slice + kFifoSlotElems - 1) / kFifoSlotElems);
+  a.slot_elems = kFifoSlotElems;
+  a.epoch = epoch;
+  a.inv_p = inv_p_of(p);
+  a.withhold = g.fifo_withhold;
+  return hip_err(launch_ring_fifo(c.dtype, c.op, a, c.s));
+}
+
 int run_allreduce(const Call& c) {
   std::string diag;
   const Schedule* sch = cached_schedule(COLL_ALLREDUCE, c.algo, c.p, &diag);
@@ -298,6 +361,8 @@ int run_allreduce(const Call& c) {
       }
       return SIM_OK;
     }
+    case SIM_ALGO_RING_FIFO:
+      return run_ring_fifo(c, lo);
     case SIM_ALGO_ONESHOT_LL: {
       LLArgs a;
       std::memset(&a, 0, sizeof a);
@@ -410,7 +475,7 @@ bool legal(int coll, int algo, int p, size_t n, int dtype) {
   (void)p;
   if (coll == COLL_ALLREDUCE) {
     if (algo == SIM_ALGO_ONESHOT_LL) return n * (size_t)esize_of(dtype) <= SIM_LL_MAX_BYTES_PER_RANK;
-    return algo >= SIM_ALGO_RING && algo <= SIM_ALGO_ONESHOT;
+    return algo >= SIM_ALGO_RING && algo <= SIM_ALGO_RING_FIFO;
   }
   return algo == SIM_ALGO_RING || algo == SIM_ALGO_ALLPAIRS;
 }
@@ -418,7 +483,7 @@ bool legal(int coll, int algo, int p, size_t n, int dtype) {
 int pick(int coll, int p, size_t n, int dtype, int* algo, double* us) {
   int best = -1;
   double bt = 0;
-  for (int a = SIM_ALGO_RING; a <= SIM_ALGO_ONESHOT_LL; a++) {
+  for (int a = SIM_ALGO_RING; a <= SIM_ALGO_RING_FIFO; a++) {
     if (!legal(coll, a, p, n, dtype)) continue;
     const double t = model_predict(g.model, coll, a, p, (double)n, esize_of(dtype));
     if (best < 0 || t < bt) {
@@ -433,7 +498,7 @@ int pick(int coll, int p, size_t n, int dtype, int* algo, double* us) {
 }
 
 int resolve_algo(int coll, int p, size_t n, int dtype, int* algo, double* us) {
-  if (*algo < SIM_ALGO_AUTO || *algo > SIM_ALGO_ONESHOT_LL) return SIM_ERR_INVALID_ARG;
+  if (*algo < SIM_ALGO_AUTO || *algo > SIM_ALGO_RING_FIFO) return SIM_ERR_INVALID_ARG;
   if (*algo == SIM_ALGO_AUTO && coll == COLL_ALLREDUCE && g.env_algo > 0) *algo = g.env_algo;
   if (*algo == SIM_ALGO_AUTO) return pick(coll, p, n, dtype, algo, us);
   if (!legal(coll, *algo, p, n, dtype)) return SIM_ERR_UNSUPPORTED;
@@ -450,7 +515,7 @@ void log_call(const char* what, const Call& c, double us) {
 
 int parse_algo_env(const char* v) {
   if (!v) return 0;
-  for (int a = 1; a < 5; a++)
+  for (int a = 1; a <= SIM_ALGO_RING_FIFO; a++)
     if (!std::strcmp(v, algo_name(a))) return a;
   return 0;
 }
@@ -487,6 +552,8 @@ int sim_finalize(void) {
   (void)hipDeviceSynchronize();
   if (g.scratch) (void)hipFree(g.scratch);
   if (g.ll) (void)hipFree(g.ll);
+  if (g.fifo) (void)hipFree(g.fifo);
+  if (g.fifo_sem) (void)hipFree(g.fifo_sem);
   if (g.err) (void)hipFree(g.err);
   Model keep = g.model;
   g = Ctx();
@@ -520,6 +587,16 @@ int sim_init(int device, int p_max, size_t max_bytes_per_rank) {
     sim_finalize();
     return SIM_ERR_HIP;
   }
+  const size_t fifo_bytes = (size_t)p_max * kFifoMaxChannels * kFifoMaxSlots * kFifoSlotElems * 4;
+  const int64_t nsem = (int64_t)p_max * kFifoMaxChannels * 2;
+  if (hipMalloc(&g.fifo, fifo_bytes) != hipSuccess || hipMalloc(&g.fifo_sem, (size_t)nsem * 8) != hipSuccess) {
+    sim_finalize();
+    return SIM_ERR_NOMEM;
+  }
+  if (launch_fill64(g.fifo_sem, 0ull, nsem, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    sim_finalize();
+    return SIM_ERR_HIP;
+  }
   g.init = true;
   if (max_bytes_per_rank > 0) {
     const size_t n = max_bytes_per_rank / 2;  // 16-bit elements need the most slots
@@ -547,7 +624,7 @@ int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size
                   int op, int algo, void* stream) {
   int rc = check_scalars(p, dtype, op, true);
   if (rc) return rc;
-  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_ONESHOT_LL) return SIM_ERR_INVALID_ARG;
+  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_RING_FIFO) return SIM_ERR_INVALID_ARG;
   if (n == 0) return SIM_OK;
   const size_t e = (size_t)esize_of(dtype);
   if (n > ((size_t)1 << 46) / e) return SIM_ERR_INVALID_ARG;
@@ -557,7 +634,7 @@ int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size
   double us = 0;
   rc = resolve_algo(COLL_ALLREDUCE, p, n, dtype, &algo, &us);
   if (rc) return rc;
-  if (hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+  if (use_device() != SIM_OK) return SIM_ERR_HIP;
   Call c{COLL_ALLREDUCE, p, dtype, op, algo, n, in_ptrs, out_ptrs, inplace, (hipStream_t)stream};
   rc = run_allreduce(c);
   if (rc) return rc;
@@ -570,7 +647,7 @@ int sim_reduce_scatter(const void* const* in_ptrs, void* const* out_ptrs, int p,
                        int dtype, int op, int algo, void* stream) {
   int rc = check_scalars(p, dtype, op, true);
   if (rc) return rc;
-  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_ONESHOT_LL) return SIM_ERR_INVALID_ARG;
+  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_RING_FIFO) return SIM_ERR_INVALID_ARG;
   if (n_out == 0) return SIM_OK;
   const size_t e = (size_t)esize_of(dtype);
   if (n_out > ((size_t)1 << 46) / e / (size_t)p) return SIM_ERR_INVALID_ARG;
@@ -605,7 +682,7 @@ int sim_reduce_scatter(const void* const* in_ptrs, void* const* out_ptrs, int p,
     if (rc) return rc;
     if (ip2) return SIM_ERR_ALIAS;
   }
-  if (hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+  if (use_device() != SIM_OK) return SIM_ERR_HIP;
   Call c{COLL_REDUCE_SCATTER, p, dtype, op, algo, (size_t)p * n_out, in_ptrs, out_ptrs, inplace,
          (hipStream_t)stream};
   rc = run_reduce_scatter(c);
@@ -619,7 +696,7 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p, siz
                    int algo, void* stream) {
   int rc = check_scalars(p, dtype, SIM_SUM, false);
   if (rc) return rc;
-  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_ONESHOT_LL) return SIM_ERR_INVALID_ARG;
+  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_RING_FIFO) return SIM_ERR_INVALID_ARG;
   if (n_in == 0) return SIM_OK;
   const size_t e = (size_t)esize_of(dtype);
   if (n_in > ((size_t)1 << 46) / e / (size_t)p) return SIM_ERR_INVALID_ARG;
@@ -652,7 +729,7 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p, siz
         if (inplace ? (q != r && overlap(outs[r], ins[q])) : overlap(outs[r], ins[q])) return SIM_ERR_ALIAS;
       }
   }
-  if (hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+  if (use_device() != SIM_OK) return SIM_ERR_HIP;
   Call c{COLL_ALL_GATHER, p, dtype, SIM_SUM, algo, (size_t)p * n_in, in_ptrs, out_ptrs, inplace,
          (hipStream_t)stream};
   rc = run_all_gather(c);
@@ -688,7 +765,7 @@ int sim_model_load(const char* json_path) {
 }
 
 int sim_model_predict(int algo, int p, int dtype, double bytes_per_rank, double* us_out) {
-  if (!us_out || algo < SIM_ALGO_RING || algo > SIM_ALGO_ONESHOT_LL || p < 2 || p > SIM_MAX_RANKS ||
+  if (!us_out || algo < SIM_ALGO_RING || algo > SIM_ALGO_RING_FIFO || p < 2 || p > SIM_MAX_RANKS ||
       dtype < SIM_INT32 || dtype > SIM_BF16 || !(bytes_per_rank >= 0))
     return SIM_ERR_INVALID_ARG;
   const int e = esize_of(dtype);
@@ -697,7 +774,7 @@ int sim_model_predict(int algo, int p, int dtype, double bytes_per_rank, double*
 }
 
 int sim_model_set(int algo, double alpha_us, double steps, double bytes_factor, double gbps) {
-  if (algo < SIM_ALGO_RING || algo > SIM_ALGO_ONESHOT_LL || !(gbps > 0) || !(alpha_us >= 0))
+  if (algo < SIM_ALGO_RING || algo > SIM_ALGO_RING_FIFO || !(gbps > 0) || !(alpha_us >= 0))
     return SIM_ERR_INVALID_ARG;
   AlgoModel& m = g.model.a[algo];
   m.alpha_us = alpha_us;
@@ -715,7 +792,7 @@ int sim_model_reset(void) {
 
 int sim_check_error(void* stream) {
   if (!g.init) return SIM_ERR_NOT_INIT;
-  if (hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+  if (use_device() != SIM_OK) return SIM_ERR_HIP;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return SIM_ERR_HIP;
   int word = 0;
   if (hipMemcpy(&word, g.err, sizeof word, hipMemcpyDeviceToHost) != hipSuccess) return SIM_ERR_HIP;
@@ -780,7 +857,7 @@ int sim_verify_schedule(int algo, int p, char* diag, size_t diag_len) {
 int sim_verify_custom(int algo, int p, int nsteps, const int* counts, const int* xfers, char* diag,
                       size_t diag_len) {
   if (p < 2 || p > SIM_MAX_RANKS || nsteps < 0 || (nsteps > 0 && (!counts || !xfers)) ||
-      algo < SIM_ALGO_RING || algo > SIM_ALGO_ONESHOT_LL)
+      algo < SIM_ALGO_RING || algo > SIM_ALGO_RING_FIFO)
     return SIM_ERR_INVALID_ARG;
   Schedule s;
   s.algo = algo;
@@ -812,9 +889,20 @@ int sim_debug_set(int key, uint64_t value) {
       if (value != 1 && value != 2) return SIM_ERR_INVALID_ARG;
       g.unroll = (int)value;
       return SIM_OK;
+    case SIM_DEBUG_FIFO_CHANNELS:
+      if (value > (uint64_t)kFifoMaxChannels) return SIM_ERR_INVALID_ARG;
+      g.fifo_channels = (int)value;
+      return SIM_OK;
+    case SIM_DEBUG_FIFO_WITHHOLD: g.fifo_withhold = value ? 1 : 0; return SIM_OK;
+    case SIM_DEBUG_FIFO_SLOTS:
+      // two slots are the minimum: with one, every rank waits for its
+      // successor to consume before sending and the ring deadlocks
+      if (value < 2 || value > (uint64_t)kFifoMaxSlots) return SIM_ERR_INVALID_ARG;
+      g.fifo_slots = (int)value;
+      return SIM_OK;
     case SIM_DEBUG_FILL_LL: {
       if (!g.init) return SIM_ERR_NOT_INIT;
-      if (hipSetDevice(g.device) != hipSuccess) return SIM_ERR_HIP;
+      if (use_device() != SIM_OK) return SIM_ERR_HIP;
       if (launch_fill64(g.ll, (unsigned long long)value, (int64_t)g.p_max * g.ll_stride, nullptr) != hipSuccess)
         return SIM_ERR_HIP;
       return hipDeviceSynchronize() == hipSuccess ? SIM_OK : SIM_ERR_HIP;
@@ -832,6 +920,9 @@ int sim_debug_get(int key, uint64_t* value) {
     case SIM_DEBUG_LOG: *value = (uint64_t)g.log; return SIM_OK;
     case SIM_DEBUG_WORKGROUPS: *value = (uint64_t)g.force_wg; return SIM_OK;
     case SIM_DEBUG_UNROLL: *value = (uint64_t)g.unroll; return SIM_OK;
+    case SIM_DEBUG_FIFO_CHANNELS: *value = (uint64_t)g.fifo_channels; return SIM_OK;
+    case SIM_DEBUG_FIFO_WITHHOLD: *value = (uint64_t)g.fifo_withhold; return SIM_OK;
+    case SIM_DEBUG_FIFO_SLOTS: *value = (uint64_t)g.fifo_slots; return SIM_OK;
   }
   return SIM_ERR_INVALID_ARG;
 }

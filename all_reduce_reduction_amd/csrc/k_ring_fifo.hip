@@ -1,0 +1,301 @@
+// k_ring_fifo.hip -- the whole ring all-reduce in ONE launch (gfx950).
+//
+// NCCL's runRing ("Inside NCCL all-reduce", section "The ring, exactly as
+// the kernel runs it") executed by persistent workgroups: workgroup
+// (rank r, channel ch) runs rank r's primitive sequence
+//     send, (p-2) x recvReduceSend, recvReduceCopySend(post-op),
+//     (p-2) x recvCopySend, recv
+// over its channel's slice of every chunk ("Channels: the ring is plural":
+// each channel owns a slice of the buffer and its own FIFOs).  Data move
+// between neighbouring ranks through bounded FIFOs of NS slots (the 8-slot
+// FIFO per peer of the same page, section "Why a 100 GB all-reduce doesn't
+// OOM"), so a partial sum never round-trips a full-size HBM buffer: the
+// FIFOs are small and stay in L2/MALL, and HBM sees the p inputs read once
+// and the p outputs written once.
+//
+// Synchronisation is the MemoryChannel put / signal / wait of "MSCCL++ ...",
+// section 4 (signal after the data, wait blocks, a monotonic expected value
+// so a stale signal never satisfies a wait):
+//   - posted[r][ch]   written by rank r-1 after it fills a slot of rank r's FIFO
+//   - consumed[r][ch] written by rank r after it has read a slot
+// Both hold (epoch << 32 | count) with a per-call epoch, so values left by
+// an earlier call compare lower than anything this call waits for.  A
+// sender may run at most NS slots ahead of its receiver (backpressure).
+// Memory ordering: the slot's data stores, an agent-scope release fence in
+// every wave, a workgroup barrier, then one agent-scope RELEASE store of the
+// counter; the waiter polls with relaxed agent-scope loads, passes a
+// barrier, and every lane then performs an agent-scope ACQUIRE load before
+// reading the slot (the other XCDs' L2s are not coherent with this one for
+// plain accesses).
+// Every wait is bounded by spin_limit polls; on expiry the workgroup writes
+// SIM_ERR_TIMEOUT to the error word and leaves, so a missing partner (e.g.
+// workgroups that could not be co-resident) ends in an error, never a hang.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace simar {
+
+namespace {
+
+__device__ __forceinline__ unsigned long long tag(unsigned epoch, unsigned long long count) {
+  return ((unsigned long long)epoch << 32) | count;
+}
+
+// thread 0 polls *p until it reaches `want` (or the spin limit); the whole
+// workgroup learns the outcome through *flag_lds.  Returns false on
+// timeout.  Each call site owns its flag word: a lane reads the flag after
+// this barrier and before the end-of-step barrier, and the flag is only
+// rewritten (by the same call site) after that end-of-step barrier.
+__device__ __forceinline__ bool wait_geq(unsigned long long* p, unsigned long long want,
+                                         unsigned long long spin_limit, int* flag_lds) {
+  if (threadIdx.x == 0) {
+    unsigned long long v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned long long spins = 0;
+    bool ok = true;
+    while (v < want) {
+      if (++spins > spin_limit) {
+        ok = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *flag_lds = ok ? 1 : 0;
+  }
+  __syncthreads();
+  return *flag_lds != 0;
+}
+
+}  // namespace
+
+template <int DT, int OP>
+__global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
+  typedef typename Ty<DT>::A A;
+  typedef Op<DT, OP> O;
+  constexpr int E = Ty<DT>::E;
+  constexpr int V = epv<DT>();  // elements per 16-byte storage vector
+  __shared__ int ok_recv, ok_send;
+
+  const int p = a.p;
+  const int r = (int)(blockIdx.x % (unsigned)p);
+  const int ch = (int)(blockIdx.x / (unsigned)p);
+  const int nxt = (r + 1 == p) ? 0 : r + 1;
+  const int tid = threadIdx.x;
+  const unsigned epoch = a.epoch;
+  const float inv_p = a.inv_p;
+  const int64_t slot_words = a.slot_elems;  // one 32-bit word per element
+
+  // my receive FIFO and counters, and my successor's
+  uint32_t* my_fifo = a.fifo + ((int64_t)r * a.C + ch) * a.NS * slot_words;
+  uint32_t* nx_fifo = a.fifo + ((int64_t)nxt * a.C + ch) * a.NS * slot_words;
+  unsigned long long* my_posted = a.sem + ((int64_t)r * a.C + ch) * 2;
+  unsigned long long* my_consumed = my_posted + 1;
+  unsigned long long* nx_posted = a.sem + ((int64_t)nxt * a.C + ch) * 2;
+  unsigned long long* nx_consumed = nx_posted + 1;
+
+  const void* xr = a.x[r];
+  void* yr = a.y[r];
+  unsigned long long sent = 0, recvd = 0;
+  if (a.withhold && r == 0) return;  // test hook: a partner that never shows up
+
+  for (int k = 0; k < a.nsub; k++) {
+    for (int step = 0; step < 2 * p - 1; step++) {
+      // step 0: send; 1..p-2: recvReduceSend; p-1: recvReduceCopySend;
+      // p..2p-3: recvCopySend; 2p-2: recv
+      const bool do_recv = step > 0;
+      const bool do_send = step < 2 * p - 2;
+      const bool reduce = step < p;            // reduce-scatter half (incl. the finishing step)
+      const bool finish = (step == p - 1);     // the chunk completes here: post-op + output
+      // chunk handled at this step
+      int c;
+      if (step < p) c = r - 1 - step;          // send0: r-1; recvReduceSend j: r-1-j; finishing: r
+      else c = r - (step - p + 1);             // recvCopySend j: r-j; recv: r-(p-1)
+      c = ((c % p) + p) % p;
+      const int64_t clo = a.lo[c], chi = a.lo[c + 1];
+      const int64_t clen = chi - clo;
+      const int64_t s_lo = clo + clen * ch / a.C, s_hi = clo + clen * (ch + 1) / a.C;
+      const int64_t e0 = s_lo + (int64_t)k * a.slot_elems;
+      const int64_t e1 = min(s_hi, e0 + (int64_t)a.slot_elems);
+      const int64_t len = e1 > e0 ? e1 - e0 : 0;
+
+      // ---- wait for the incoming slot ----
+      if (do_recv) {
+        if (!wait_geq(my_posted, tag(epoch, recvd + 1), a.spin_limit, &ok_recv)) goto timeout;
+        (void)__hip_atomic_load(my_posted, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // ---- wait for room in the successor's FIFO ----
+      if (do_send && sent + 1 > (unsigned long long)a.NS) {
+        if (!wait_geq(nx_consumed, tag(epoch, sent + 1 - a.NS), a.spin_limit, &ok_send)) goto timeout;
+      }
+      {
+        const uint32_t* in_slot = my_fifo + (int64_t)(recvd % a.NS) * slot_words;
+        uint32_t* out_slot = nx_fifo + (int64_t)(sent % a.NS) * slot_words;
+        const bool vec = ((e0 % V) == 0);
+        for (int64_t off = (int64_t)tid * V; off < len; off += (int64_t)kBlock * V) {
+          const int64_t i0 = e0 + off;
+          A v[V];
+          uint32_t w[V];
+          const int cnt = (int)min((int64_t)V, len - off);
+          if (vec && cnt == V) {
+            if (reduce) {
+              A own[V];
+              unpack<DT>(ld16(xr, i0 * E), own);
+              if (step == 0) {
+#pragma unroll
+                for (int e = 0; e < V; e++) v[e] = O::pre(own[e], inv_p);
+              } else {
+#pragma unroll
+                for (int h = 0; h < V / 4; h++) {
+                  const u32x4 q = *(const u32x4*)(in_slot + off + 4 * h);
+#pragma unroll
+                  for (int e = 0; e < 4; e++) {
+                    const uint32_t bits = q[e];
+                    v[4 * h + e] = __builtin_bit_cast(A, bits);
+                  }
+                }
+#pragma unroll
+                for (int e = 0; e < V; e++) v[e] = O::comb(v[e], O::pre(own[e], inv_p));
+              }
+              if (finish) {
+#pragma unroll
+                for (int e = 0; e < V; e++) v[e] = O::post(v[e], p);
+                const u32x4 packed = pack<DT>(v);
+                st16(yr, i0 * E, packed);
+#pragma unroll
+                for (int e = 0; e < V; e++) w[e] = narrow_bits<DT>(v[e]);
+              } else {
+#pragma unroll
+                for (int e = 0; e < V; e++) w[e] = __builtin_bit_cast(uint32_t, v[e]);
+              }
+            } else {  // gather: finished storage bits arrive; keep and forward them
+#pragma unroll
+              for (int h = 0; h < V / 4; h++) {
+                const u32x4 q = *(const u32x4*)(in_slot + off + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; e++) w[4 * h + e] = q[e];
+              }
+              u32x4 out;
+              if constexpr (E == 4) {
+#pragma unroll
+                for (int e = 0; e < 4; e++) out[e] = w[e];
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; e++) out[e] = (w[2 * e] & 0xffffu) | (w[2 * e + 1] << 16);
+              }
+              st16(yr, i0 * E, out);
+            }
+            if (do_send) {
+#pragma unroll
+              for (int h = 0; h < V / 4; h++) {
+                u32x4 q;
+#pragma unroll
+                for (int e = 0; e < 4; e++) q[e] = w[4 * h + e];
+                *(u32x4*)(out_slot + off + 4 * h) = q;
+              }
+            }
+          } else {  // ragged: element by element
+            for (int e = 0; e < cnt; e++) {
+              const int64_t i = i0 + e;
+              uint32_t word;
+              if (reduce) {
+                A val;
+                const A own = O::pre(load_elem<DT>(xr, i), inv_p);
+                if (step == 0) {
+                  val = own;
+                } else {
+                  const uint32_t bits = in_slot[off + e];
+                  val = O::comb(__builtin_bit_cast(A, bits), own);
+                }
+                if (finish) {
+                  val = O::post(val, p);
+                  store_elem<DT>(yr, i, val);
+                  word = narrow_bits<DT>(val);
+                } else {
+                  word = __builtin_bit_cast(uint32_t, val);
+                }
+              } else {
+                word = in_slot[off + e];
+                if constexpr (E == 4) ((uint32_t*)yr)[i] = word;
+                else ((uint16_t*)yr)[i] = (uint16_t)word;
+              }
+              if (do_send) out_slot[off + e] = word;
+            }
+          }
+        }
+      }
+      // Every wave makes its own slot stores visible at agent scope before
+      // the barrier: a workgroup barrier alone does not wait for the other
+      // waves' stores, so thread 0's release would not cover them (seen as
+      // stale words in other waves' lanes at 64 channels x 8 slots).
+      if (do_send) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();  // every lane's slot reads and writes are complete
+      if (tid == 0) {
+        if (do_send)
+          __hip_atomic_store(nx_posted, tag(epoch, sent + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (do_recv)
+          __hip_atomic_store(my_consumed, tag(epoch, recvd + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (do_send) sent++;
+      if (do_recv) recvd++;
+    }
+  }
+  return;
+
+timeout:
+  if (tid == 0) __hip_atomic_store(a.err, (int)SIM_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int DT>
+static hipError_t fifo_by_op(int op, const RingFifoArgs& a, hipStream_t s) {
+  const dim3 g((unsigned)(a.p * a.C)), b(kBlock);
+  switch (op) {
+    case SIM_SUM: hipLaunchKernelGGL((k_ring_fifo<DT, SIM_SUM>), g, b, 0, s, a); break;
+    case SIM_PROD: hipLaunchKernelGGL((k_ring_fifo<DT, SIM_PROD>), g, b, 0, s, a); break;
+    case SIM_MIN: hipLaunchKernelGGL((k_ring_fifo<DT, SIM_MIN>), g, b, 0, s, a); break;
+    case SIM_MAX: hipLaunchKernelGGL((k_ring_fifo<DT, SIM_MAX>), g, b, 0, s, a); break;
+    case SIM_AVG: hipLaunchKernelGGL((k_ring_fifo<DT, SIM_AVG>), g, b, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_fifo(int dtype, int op, const RingFifoArgs& a, hipStream_t s) {
+  switch (dtype) {
+    case SIM_INT32: return fifo_by_op<SIM_INT32>(op, a, s);
+    case SIM_FP32: return fifo_by_op<SIM_FP32>(op, a, s);
+    case SIM_FP16: return fifo_by_op<SIM_FP16>(op, a, s);
+    case SIM_BF16: return fifo_by_op<SIM_BF16>(op, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int OP>
+static int occ1() {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)k_ring_fifo<DT, OP>, kBlock, 0) !=
+      hipSuccess)
+    return 1;
+  return nb > 0 ? nb : 1;
+}
+
+template <int DT>
+static int occ_op(int op) {
+  switch (op) {
+    case SIM_SUM: return occ1<DT, SIM_SUM>();
+    case SIM_PROD: return occ1<DT, SIM_PROD>();
+    case SIM_MIN: return occ1<DT, SIM_MIN>();
+    case SIM_MAX: return occ1<DT, SIM_MAX>();
+    default: return occ1<DT, SIM_AVG>();
+  }
+}
+
+int ring_fifo_blocks_per_cu(int dtype, int op) {
+  switch (dtype) {
+    case SIM_INT32: return occ_op<SIM_INT32>(op);
+    case SIM_FP32: return occ_op<SIM_FP32>(op);
+    case SIM_FP16: return occ_op<SIM_FP16>(op);
+    default: return occ_op<SIM_BF16>(op);
+  }
+}
+
+}  // namespace simar

@@ -88,7 +88,28 @@ struct LLArgs {
   float inv_p;
 };
 
+// Single-launch ring: p * C persistent workgroups, bounded FIFOs between
+// neighbouring ranks, epoch-tagged monotonic semaphores.
+struct RingFifoArgs {
+  const void* x[SIM_MAX_RANKS];
+  void* y[SIM_MAX_RANKS];
+  int64_t lo[SIM_MAX_RANKS + 1];
+  uint32_t* fifo;              // [p][C][NS][slot_elems] 32-bit words
+  unsigned long long* sem;     // [p][C][2]: posted, consumed
+  int* err;
+  unsigned long long spin_limit;
+  int p;
+  int C;                       // channels per rank
+  int NS;                      // slots per FIFO
+  int nsub;                    // slots per channel slice of a chunk
+  int slot_elems;              // multiple of kBlock * 8
+  unsigned int epoch;
+  float inv_p;
+  int withhold;                // test hook: rank 0 leaves at once, its partners' waits expire
+};
+
 static_assert(sizeof(FoldArgs) <= 4096, "kernel argument segment too large");
+static_assert(sizeof(RingFifoArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(CopyArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(LLArgs) <= 4096, "kernel argument segment too large");
@@ -103,5 +124,7 @@ hipError_t launch_ll(int dtype, int op, const LLArgs& a, int grid, hipStream_t s
 hipError_t launch_fill64(unsigned long long* p, unsigned long long v, int64_t n, hipStream_t s);
 // Workgroups of the LL kernel (dtype, op) that fit on one CU at once.
 int ll_blocks_per_cu(int dtype, int op);
+hipError_t launch_ring_fifo(int dtype, int op, const RingFifoArgs& a, hipStream_t s);
+int ring_fifo_blocks_per_cu(int dtype, int op);
 
 }  // namespace simar

@@ -39,7 +39,8 @@ bool lower(int coll, int algo, int p, Schedule* out) {
   s.algo = algo;
   s.p = p;
   s.coll = coll;
-  const bool ring = (algo == SIM_ALGO_RING);
+  // the single-launch ring executes the same schedule as the ring
+  const bool ring = (algo == SIM_ALGO_RING || algo == SIM_ALGO_RING_FIFO);
   const bool allpairs = (algo == SIM_ALGO_ALLPAIRS);
   const bool fused = (algo == SIM_ALGO_ONESHOT || algo == SIM_ALGO_ONESHOT_LL);
   if (coll == COLL_ALLREDUCE) {
@@ -116,7 +117,7 @@ bool lower(int coll, int algo, int p, Schedule* out) {
 
 std::vector<int> expected_order(int algo, int p, int c) {
   std::vector<int> o;
-  if (algo == SIM_ALGO_RING) {
+  if (algo == SIM_ALGO_RING || algo == SIM_ALGO_RING_FIFO) {
     for (int k = 1; k <= p; k++) o.push_back(mod(c + k, p));
   } else {
     o.push_back(c);
@@ -324,7 +325,7 @@ bool apply_step(const Schedule& s, int st, Sym* y, std::vector<char>* post, std:
 }
 
 int closed_form_rounds(int coll, int algo, int p) {
-  const bool ring = algo == SIM_ALGO_RING;
+  const bool ring = algo == SIM_ALGO_RING || algo == SIM_ALGO_RING_FIFO;
   if (coll == COLL_ALLREDUCE) return ring ? 2 * (p - 1) : 2;
   return ring ? p - 1 : 1;
 }
@@ -394,7 +395,7 @@ bool verify(const Schedule& s, std::string* diag) {
     if (diag) *diag = fmt("schedule claims %d rounds, closed form is %d", s.rounds, want);
     return false;
   }
-  if (s.algo == SIM_ALGO_RING && (int)s.steps.size() != want) {
+  if ((s.algo == SIM_ALGO_RING || s.algo == SIM_ALGO_RING_FIFO) && (int)s.steps.size() != want) {
     if (diag) *diag = fmt("ring has %d steps, closed form is %d", (int)s.steps.size(), want);
     return false;
   }

@@ -33,6 +33,7 @@ Model default_model() {
   m.a[SIM_ALGO_ALLPAIRS] = {4.7, 7000.0, -1.0, -1.0};
   m.a[SIM_ALGO_ONESHOT] = {5.1, 6600.0, -1.0, -1.0};
   m.a[SIM_ALGO_ONESHOT_LL] = {9.4, 6750.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING_FIFO] = {30.0, 4000.0, -1.0, -1.0};  // until calibrated
   return m;
 }
 
@@ -42,6 +43,7 @@ int model_launches(int coll, int algo, int p) {
     case SIM_ALGO_ALLPAIRS: return coll == COLL_ALLREDUCE ? 2 : 1;
     case SIM_ALGO_ONESHOT: return 1;
     case SIM_ALGO_ONESHOT_LL: return 1;
+    case SIM_ALGO_RING_FIFO: return 1;
   }
   return 0;
 }
@@ -53,6 +55,7 @@ double model_traffic(int coll, int algo, int p, double n, int esize) {
       case SIM_ALGO_ONESHOT: return 2.0 * p * S;          // p inputs read, p outputs written
       case SIM_ALGO_ALLPAIRS: return (2.0 * p + 1.0) * S;  // step 1: pS + S; step 2: S + (p-1)S
       case SIM_ALGO_ONESHOT_LL: return 6.0 * p * S;        // pack 3pS, consume 3pS
+      case SIM_ALGO_RING_FIFO: return 2.0 * p * S;         // HBM: inputs once, outputs once (FIFOs stay cached)
       case SIM_ALGO_RING: {
         // reduce-scatter: first step in,in->part; middle part,in->part;
         // last part,in->out; partials are 4-byte accumulators.  Each step
@@ -220,7 +223,7 @@ struct Parser {
   }
 };
 
-const char* kAlgoNames[kNumAlgos] = {"auto", "ring", "allpairs", "oneshot", "oneshot_ll"};
+const char* kAlgoNames[kNumAlgos] = {"auto", "ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"};
 
 }  // namespace
 

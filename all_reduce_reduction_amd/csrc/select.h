@@ -6,7 +6,7 @@
 
 namespace simar {
 
-constexpr int kNumAlgos = 5;  // indices are the SIM_ALGO_* codes (0 = AUTO unused)
+constexpr int kNumAlgos = 6;  // indices are the SIM_ALGO_* codes (0 = AUTO unused)
 
 struct AlgoModel {
   double alpha_us = 4.0;       // fixed cost per launch (sync step)

@@ -193,10 +193,9 @@ def main():
         lip, lop = [t_.data_ptr() for t_ in lin], [t_.data_ptr() for t_ in lout]
         lat = {}
         for a in ("oneshot", "oneshot_ll", "allpairs", "ring", "auto"):
-            def call(a=a):
-                st = sim.sim_allreduce(lip, lop, P, LAT_N, "fp16", "sum", a, stream)
-                if st:
-                    raise sim.SimError(st, "sim_allreduce")
+            call = sim.prepare_allreduce(lip, lop, P, LAT_N, "fp16", "sum", a, stream)
+            if call() != 0:
+                raise sim.SimError(call(), f"sim_allreduce({a})")
             lat[a] = round(time_calls(call, 2000, 200) * 1e6, 2)
             if a == "auto":
                 lat["auto_pick"] = sim.sim_last_algo()

@@ -40,9 +40,12 @@
  *     (p, dtype, op, algo) are checked.
  *   - Chunk c of an n-element buffer is [floor(c*n/p), floor((c+1)*n/p)).
  *   - One host thread per process drives the library (no internal locking).
+ *     Calls make the library's device (the one given to sim_init) current
+ *     on the calling thread when another one is.
  *
  * Results: int32 and fp32 results are bit-exact functions of the schedule:
- * ring chunk c folds ranks c+1, c+2, ..., c+p (mod p) left to right;
+ * ring chunk c (both ring executions) folds ranks c+1, c+2, ..., c+p
+ * (mod p) left to right;
  * all-pairs, one-shot and LL fold the owner c first and then the other
  * ranks in ascending order.  fp16/bf16 are widened exactly to fp32,
  * accumulated in fp32 (ring partials are kept in fp32) and rounded once,
@@ -82,7 +85,9 @@ enum {
   SIM_ALGO_RING = 1,        /* 2(p-1) steps, one launch per step */
   SIM_ALGO_ALLPAIRS = 2,    /* 2 steps: owner gather-reduce, then fan-out */
   SIM_ALGO_ONESHOT = 3,     /* the 2 all-pairs steps fused in one launch */
-  SIM_ALGO_ONESHOT_LL = 4   /* one-shot through 8-byte data+flag packets */
+  SIM_ALGO_ONESHOT_LL = 4,  /* one-shot through 8-byte data+flag packets */
+  SIM_ALGO_RING_FIFO = 5    /* the ring in ONE launch: persistent workgroups, bounded
+                               FIFOs between neighbours, in-kernel signal/wait */
 };
 
 #define SIM_MAX_RANKS 16
@@ -94,7 +99,8 @@ enum {
 
 /* Initialise the library on HIP device `device` for up to p_max ranks
  * (2..SIM_MAX_RANKS).  Allocates the device error word, the LL packet
- * buffer (p_max * 2 * SIM_LL_MAX_BYTES_PER_RANK bytes) and, when
+ * buffer (p_max * 2 * SIM_LL_MAX_BYTES_PER_RANK bytes), the single-launch
+ * ring's FIFOs and semaphores (p_max * 64 channels * 8 slots * 16 KiB) and, when
  * max_bytes_per_rank > 0, the ring/reduce-scatter partial scratch for
  * messages up to that size (otherwise scratch grows on first need).
  * Calling it again re-initialises (finalize + init).  Errors:
@@ -203,7 +209,10 @@ enum {
   SIM_DEBUG_FILL_LL = 3,       /* fill the LL buffer with this 64-bit packet (synchronous) */
   SIM_DEBUG_LOG = 4,           /* 1: log one line per call to stderr (also SIM_DEBUG=1) */
   SIM_DEBUG_WORKGROUPS = 5,    /* force the workgroup count of bulk kernels (0 = heuristic) */
-  SIM_DEBUG_UNROLL = 6         /* 16-byte vectors per lane per pass in bulk kernels: 1 or 2 */
+  SIM_DEBUG_UNROLL = 6,        /* 16-byte vectors per lane per pass in bulk kernels: 1 or 2 */
+  SIM_DEBUG_FIFO_CHANNELS = 7, /* single-launch ring: channels per rank (0 = heuristic) */
+  SIM_DEBUG_FIFO_SLOTS = 8,    /* single-launch ring: slots per FIFO, 2..8 (default 4) */
+  SIM_DEBUG_FIFO_WITHHOLD = 9  /* 1: rank 0's ring workgroups leave at once (forces a bounded-wait expiry) */
 };
 int sim_debug_set(int key, uint64_t value);
 int sim_debug_get(int key, uint64_t* value);

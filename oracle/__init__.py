@@ -35,7 +35,7 @@ LIBPATH = os.path.join(_HERE, "liboracle.so")
 
 DTYPES = {"int32": 0, "fp32": 1, "fp16": 2, "bf16": 3}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
-ALGOS = {"ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4}
+ALGOS = {"ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4, "ring_fifo": 5}
 STORAGE = {"int32": np.int32, "fp32": np.float32, "fp16": np.uint16, "bf16": np.uint16}
 
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",

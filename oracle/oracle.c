@@ -52,7 +52,7 @@
 /* ---- codes (kept numerically equal to the library's public enums) ---- */
 enum { OR_INT32 = 0, OR_FP32 = 1, OR_FP16 = 2, OR_BF16 = 3 };
 enum { OR_SUM = 0, OR_PROD = 1, OR_MIN = 2, OR_MAX = 3, OR_AVG = 4 };
-enum { OR_RING = 1, OR_ALLPAIRS = 2, OR_ONESHOT = 3, OR_ONESHOT_LL = 4 };
+enum { OR_RING = 1, OR_ALLPAIRS = 2, OR_ONESHOT = 3, OR_ONESHOT_LL = 4, OR_RING_FIFO = 5 };
 #define OR_EBADARG (-1)
 
 /* ------------------------------------------------------------------ */
@@ -321,7 +321,8 @@ int oracle_allreduce(const void* const* X, void* const* Y, int p, int64_t n,
                      int dtype, int op, int algo) {
   if (check_args(p, n, dtype, op)) return OR_EBADARG;
   ctx_t c = make_ctx(p, dtype, op);
-  if (algo == OR_RING) {
+  /* the single-launch ring runs the ring's schedule: same steps, same order */
+  if (algo == OR_RING || algo == OR_RING_FIFO) {
     int s1 = ring_reduce_scatter(&c, X, Y, n, 0);
     if (s1 < 0) return s1;
     return s1 + ring_all_gather_inplace(&c, Y, n);
@@ -397,7 +398,8 @@ int oracle_all_gather(const void* const* X, void* const* Y, int p, int64_t n_in,
 int oracle_allreduce_at(const void* const* X, int p, int64_t n, int dtype, int op,
                         int algo, const int64_t* idx, int64_t m, void* out) {
   if (check_args(p, n, dtype, op)) return OR_EBADARG;
-  if (algo != OR_RING && algo != OR_ALLPAIRS && algo != OR_ONESHOT && algo != OR_ONESHOT_LL)
+  if (algo != OR_RING && algo != OR_ALLPAIRS && algo != OR_ONESHOT && algo != OR_ONESHOT_LL &&
+      algo != OR_RING_FIFO)
     return OR_EBADARG;
   ctx_t c = make_ctx(p, dtype, op);
   for (int64_t k = 0; k < m; k++) if (idx[k] < 0 || idx[k] >= n) return OR_EBADARG;
@@ -406,7 +408,7 @@ int oracle_allreduce_at(const void* const* X, int p, int64_t n, int dtype, int o
     const int64_t i = idx[k];
     const int ch = (int)chunk_of(n, p, i);
     acc_t v;
-    if (algo == OR_RING) {
+    if (algo == OR_RING || algo == OR_RING_FIFO) {
       v = pre(&c, X[(ch + 1) % p], i);
       for (int s = 0; s <= p - 2; s++) {
         const int r = (ch + 1 + s) % p;     /* sender of chunk ch at step s */

@@ -15,7 +15,7 @@ from fractions import Fraction
 import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll")
+ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo")
 
 
 def _golden(name):
@@ -31,7 +31,7 @@ def chunk_bounds(n, p):
 def documented_order(algo, p, c):
     """Fold order of chunk c: ring starts at rank c+1 and walks the ring;
     all-pairs (and one-shot, LL) starts at the owner c, then ascending."""
-    if algo == "ring":
+    if algo in ("ring", "ring_fifo"):
         return [(c + 1 + k) % p for k in range(p)]
     return [c] + [q for q in range(p) if q != c]
 
@@ -61,6 +61,7 @@ def check_step_counts(orc):
     for p in range(2, 17):
         xs = [np.full(3 * p + 1, q, dtype=np.int32) for q in range(p)]
         assert orc.allreduce(xs, "int32", "sum", "ring")[1] == 2 * (p - 1), p
+        assert orc.allreduce(xs, "int32", "sum", "ring_fifo")[1] == 2 * (p - 1), p
         for algo in ("allpairs", "oneshot", "oneshot_ll"):
             assert orc.allreduce(xs, "int32", "sum", algo)[1] == 2, (p, algo)
 

@@ -17,7 +17,8 @@ def lib():
     sim.sim_init(0, 8, 0)
     yield sim
     sim.sim_debug_set("ll_wait_skew", 0)
-    sim.sim_debug_set("spin_limit", 1 << 22)
+    sim.sim_debug_set("fifo_withhold", 0)
+    sim.sim_debug_set("spin_limit", 1 << 20)
 
 
 def _bufs(p, n, dtype="fp32"):
@@ -53,6 +54,7 @@ def test_argument_errors_enqueue_nothing(lib):
         "mixed in-place": (sim.sim_allreduce(I, [I[0]] + O[1:], 4, 1024, "fp32", "sum", "ring", s), INVALID),
         "rs oneshot": (sim.sim_reduce_scatter(I, O, 4, 256, "fp32", "sum", "oneshot", s), UNSUPPORTED),
         "ag ll": (sim.sim_all_gather(I, O, 4, 256, "fp32", "oneshot_ll", s), UNSUPPORTED),
+        "rs ring_fifo": (sim.sim_reduce_scatter(I, O, 4, 256, "fp32", "sum", "ring_fifo", s), UNSUPPORTED),
     }
     for name, (got, want) in cases.items():
         assert got == want, (name, got, want)
@@ -162,7 +164,7 @@ def test_forced_timeout_reports_and_recovers(lib, orc):
     assert sim.sim_check_error(stream()) == TIMEOUT
     assert sim.sim_check_error(stream()) == OK          # the word was cleared
     sim.sim_debug_set("ll_wait_skew", 0)
-    sim.sim_debug_set("spin_limit", 1 << 22)
+    sim.sim_debug_set("spin_limit", 1 << 20)
     got = run_allreduce(xs, "fp16", "sum", "oneshot_ll")
     for r in range(8):
         assert (got[r] == want[r]).all()
@@ -181,3 +183,71 @@ def test_auto_reports_what_ran_and_logs(lib, capfd):
     assert sim.sim_last_algo() == pick
     err = capfd.readouterr().err
     assert "AllReduce" in err and f"algo {pick}" in err
+
+
+def test_single_launch_ring_missing_partner_times_out(lib, orc):
+    """Rank 0's workgroups leave at once (a host-set test flag): its partners'
+    bounded waits expire, the kernel ends, the error word says
+    SIM_ERR_TIMEOUT.  The next call (flag cleared) is correct."""
+    from tests.gpu_util import ptrs, run_allreduce, stream, to_device, empty_like_poisoned
+    import synthdata
+    sim = lib
+    xs = synthdata.normal(47, 8, 8 * 4096 + 3, "bf16")
+    want, _ = orc.allreduce(xs, "bf16", "sum", "ring_fifo")
+    sim.sim_debug_set("spin_limit", 64)
+    sim.sim_debug_set("fifo_withhold", 1)
+    din = to_device(xs, "bf16")
+    dout = empty_like_poisoned(xs[0].size, "bf16", 8)
+    assert sim.sim_allreduce(ptrs(din), ptrs(dout), 8, xs[0].size, "bf16", "sum", "ring_fifo", stream()) == OK
+    assert sim.sim_check_error(stream()) == TIMEOUT
+    sim.sim_debug_set("fifo_withhold", 0)
+    sim.sim_debug_set("spin_limit", 1 << 20)
+    got = run_allreduce(xs, "bf16", "sum", "ring_fifo")
+    for r in range(8):
+        assert (got[r] == want[r]).all()
+
+
+def test_single_launch_ring_shapes(lib, orc):
+    """Channel counts and FIFO depths (2 slots is the minimum: with one the
+    ring would deadlock, and the library refuses it)."""
+    import synthdata
+    from tests.gpu_util import assert_parity, run_allreduce
+    sim = lib
+    assert sim.lib.sim_debug_set(sim.DEBUG["fifo_slots"], 1) == INVALID
+    xs = synthdata.normal(48, 8, 8 * 4096 * 5 + 77, "fp32")
+    want, _ = orc.allreduce(xs, "fp32", "sum", "ring_fifo")
+    try:
+        for ch in (1, 3, 16, 64):
+            for ns in (2, 4, 8):
+                sim.sim_debug_set("fifo_channels", ch)
+                sim.sim_debug_set("fifo_slots", ns)
+                for rep in range(3 if ch == 64 else 1):
+                    got = run_allreduce(xs, "fp32", "sum", "ring_fifo")
+                    for r in range(8):
+                        assert_parity(got[r], want[r], "fp32", f"channels {ch} slots {ns} rep {rep} r{r}")
+    finally:
+        sim.sim_debug_set("fifo_channels", 0)
+        sim.sim_debug_set("fifo_slots", 4)
+
+
+def test_single_launch_ring_repeated_large(lib, orc):
+    """Many back-to-back calls on a large ragged buffer (several slots per
+    channel, every FIFO wrapping many times), each checked in full."""
+    import synthdata
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
+    sim = lib
+    n = 8 * 4096 * 40 + 1237
+    xs = synthdata.normal(49, 8, n, "bf16")
+    want, _ = orc.allreduce(xs, "bf16", "sum", "ring_fifo")
+    din = to_device(xs, "bf16")
+    outs = [empty_like_poisoned(n, "bf16", 8) for _ in range(4)]
+    for ns in (2, 8):
+        sim.sim_debug_set("fifo_slots", ns)
+        for k in range(40):
+            assert sim.sim_allreduce(ptrs(din), ptrs(outs[k % 4]), 8, n, "bf16", "sum", "ring_fifo", stream()) == OK
+        assert sim.sim_check_error(stream()) == OK
+        for o in outs:
+            got = to_host(o, "bf16")
+            for r in range(8):
+                assert_parity(got[r], want[r], "bf16", f"slots {ns} r{r}")
+    sim.sim_debug_set("fifo_slots", 4)

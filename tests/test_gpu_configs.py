@@ -55,11 +55,11 @@ def test_workload2_fp32_32MiB(orc):
     n = 8_388_608
     xs = synthdata.workload_inputs(2, 8, n, "fp32")
     outs = {}
-    for algo in ("ring", "allpairs", "oneshot"):
+    for algo in ("ring", "allpairs", "oneshot", "ring_fifo"):
         print(f"workload 2: {algo}", flush=True)
         got = _run(xs, "fp32", "sum", algo)
         want, steps = orc.allreduce(xs, "fp32", "sum", algo)
-        assert steps == (14 if algo == "ring" else 2)
+        assert steps == (14 if algo in ("ring", "ring_fifo") else 2)
         for r in range(8):
             assert_parity(got[r], want[r], "fp32", f"w2 {algo} r{r}")
         outs[algo] = got[0]
@@ -74,7 +74,7 @@ def test_workload3_bf16_tp(orc, tokens):
     from tests.gpu_util import assert_parity
     n = 8192 * tokens
     xs = synthdata.workload_inputs(3, 8, n, "bf16")
-    algos = ["ring", "allpairs", "oneshot", "auto"]
+    algos = ["ring", "allpairs", "oneshot", "ring_fifo", "auto"]
     if n * 2 <= sim.LL_MAX_BYTES_PER_RANK:
         algos.append("oneshot_ll")
     for algo in algos:
@@ -122,7 +122,7 @@ def test_workload5_allreduce_256MiB(orc, dtype, ops):
     idx = _sample_idx(n, p, rng)
     tidx = torch.from_numpy(idx).to(din[0].device)
     for op in ops:
-        for algo in ("auto", "ring"):
+        for algo in ("auto", "ring", "ring_fifo"):
             print(f"workload 5: {dtype} {op} {algo}", flush=True)
             st = sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, algo, stream())
             assert st == 0

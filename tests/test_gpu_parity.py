@@ -8,7 +8,7 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = ["ring", "allpairs", "oneshot", "oneshot_ll"]
+ALGOS = ["ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"]
 ESIZE = {"int32": 4, "fp32": 4, "fp16": 2, "bf16": 2}
 DTYPES = ["int32", "fp32", "fp16", "bf16"]
 OPS = ["sum", "prod", "min", "max", "avg"]
@@ -83,6 +83,8 @@ def test_oneshot_allpairs_ll_bit_identical(orc):
     for a in ("allpairs", "oneshot_ll"):
         for r in range(8):
             assert (bits(outs[a][r]) == bits(outs["oneshot"][r])).all(), a
+    for r in range(8):  # the two executions of the ring agree bit for bit
+        assert (bits(outs["ring_fifo"][r]) == bits(outs["ring"][r])).all()
     assert (bits(outs["ring"][0]) != bits(outs["oneshot"][0])).any()
 
 

@@ -38,9 +38,9 @@ def test_printed_ratios(example_model):
 
 
 def test_argmin_switches_at_the_crossover(example_model):
-    # make one-shot and LL unattractive so the choice is ring vs all-pairs
-    sim.sim_model_set("oneshot", 1e9, -1, -1, 1.0)
-    sim.sim_model_set("oneshot_ll", 1e9, -1, -1, 1.0)
+    # make the other schedules unattractive so the choice is ring vs all-pairs
+    for other in ("oneshot", "oneshot_ll", "ring_fifo"):
+        sim.sim_model_set(other, 1e9, -1, -1, 1.0)
     x = model.crossover_bytes()
     below = int(x * 0.98) // 4 * 4
     above = int(x * 1.02) // 4 * 4
@@ -63,7 +63,7 @@ def test_ll_is_never_picked_above_its_buffer():
 
 def test_builtin_traffic_laws():
     sim.sim_model_reset()
-    for algo in ("ring", "allpairs", "oneshot", "oneshot_ll"):
+    for algo in ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"):
         sim.sim_model_set(algo, 0.0, -1, -1, 1e-3)   # 1 MB/s: time in us == bytes
     S = 1 << 20
     n = S // 2
@@ -74,6 +74,8 @@ def test_builtin_traffic_laws():
     assert sim.sim_model_predict("ring", 8, "bf16", S) == pytest.approx(94 * n)
     # ring, 32-bit: 5 (p-1) S
     assert sim.sim_model_predict("ring", 8, "fp32", S) == pytest.approx(35 * S)
+    # the single-launch ring: inputs read once, outputs written once
+    assert sim.sim_model_predict("ring_fifo", 8, "bf16", S) == pytest.approx(16 * S)
     sim.sim_model_reset()
 
 
