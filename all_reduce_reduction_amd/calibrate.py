@@ -27,7 +27,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_OUT = os.path.join(HERE, "calib", "mi355x.json")
-ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll")
+ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo")
 P = 8
 
 
@@ -75,10 +75,10 @@ class Bench:
         nbytes = n * sim.ESIZE[dtype]
         steps = max(5, min(2000, int(2e5 / max(1.0, nbytes / 4e3))))
 
-        def call():
-            st = sim.sim_allreduce(self.ip, self.op, P, n, dtype, "sum", algo, self.stream)
-            if st:
-                raise sim.SimError(st, f"sim_allreduce({algo})")
+        call = sim.prepare_allreduce(self.ip, self.op, P, n, dtype, "sum", algo, self.stream)
+        st = call()
+        if st:
+            raise sim.SimError(st, f"sim_allreduce({algo})")
         us, spread = self.time(call, steps, max(2, steps // 10))
         if sim.sim_check_error(self.stream) != 0:
             raise RuntimeError("device error during calibration")

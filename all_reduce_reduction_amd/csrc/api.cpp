@@ -27,9 +27,8 @@ namespace {
 constexpr int kVersion = 1;
 constexpr int64_t kMaxTiles = 1 << 20;  // cap on workgroups per transfer
 // single-launch ring: FIFO geometry
-constexpr int kFifoMaxChannels = 64;      // channels per rank
+constexpr int kFifoMaxChannels = 128;     // channels per rank
 constexpr int kFifoMaxSlots = 8;          // slots per FIFO
-constexpr int kFifoSlotElems = kBlock * 16;  // 4096 elements (16 KiB of 32-bit words) per slot
 
 struct Ctx {
   bool init = false;
@@ -51,6 +50,7 @@ struct Ctx {
   int env_algo = 0;
   int ll_occ[4][5] = {};
   uint32_t* fifo = nullptr;
+  size_t fifo_bytes = 0;
   unsigned long long* fifo_sem = nullptr;
   uint32_t fifo_epoch = 0;
   int fifo_channels = 0;  // 0: heuristic
@@ -277,6 +277,8 @@ int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_c
 // all co-resident, exchanging partials through bounded FIFOs.
 int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
   const int p = c.p;
+  const int V = 16 / esize_of(c.dtype);
+  const int slot = kBlock * kFifoVecsPerLane * V;
   RingFifoArgs a;
   std::memset(&a, 0, sizeof a);
   int64_t maxchunk = 0;
@@ -289,11 +291,34 @@ int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
   int& occ = g.fifo_occ[c.dtype][c.op];
   if (occ == 0) occ = ring_fifo_blocks_per_cu(c.dtype, c.op);
   const int64_t resident = (int64_t)occ * g.cu_count;  // every workgroup must be resident at once
-  int64_t C = g.fifo_channels > 0 ? g.fifo_channels
-                                  : std::max<int64_t>(1, (maxchunk + kFifoSlotElems - 1) / kFifoSlotElems);
+  int64_t C = g.fifo_channels > 0 ? g.fifo_channels : std::max<int64_t>(1, (maxchunk + slot - 1) / slot);
   C = std::min<int64_t>(C, kFifoMaxChannels);
   C = std::min<int64_t>(C, std::max<int64_t>(1, resident / p));
-  const int64_t slice = (maxchunk + C - 1) / C;
+  // slots per channel slice: the longest slice over all chunks (same formula as the kernel)
+  int64_t maxslice = 0;
+  for (int q = 0; q < p; q++) {
+    const int64_t clen = lo[q + 1] - lo[q];
+    for (int64_t ch = 0; ch < C; ch++) {
+      const int64_t s_lo = (clen * ch / C) / V * V;
+      const int64_t s_hi = (ch + 1 == C) ? clen : (clen * (ch + 1) / C) / V * V;
+      maxslice = std::max(maxslice, s_hi - s_lo);
+    }
+  }
+  const int NS = g.fifo_slots;
+  const size_t need = (size_t)p * C * NS * slot * 4;
+  if (need > g.fifo_bytes) {  // grow (synchronises the device once)
+    if (g.fifo) {
+      if (hipDeviceSynchronize() != hipSuccess || hipFree(g.fifo) != hipSuccess) return SIM_ERR_HIP;
+      g.fifo = nullptr;
+      g.fifo_bytes = 0;
+    }
+    if (hipMalloc(&g.fifo, need) != hipSuccess) {
+      g.fifo = nullptr;
+      (void)hipGetLastError();
+      return SIM_ERR_NOMEM;
+    }
+    g.fifo_bytes = need;
+  }
   uint32_t epoch = g.fifo_epoch + 1;
   if (epoch == 0) {  // wrapped: clear every counter so no stale value can compare high
     int rc = hip_err(launch_fill64(g.fifo_sem, 0ull, (int64_t)g.p_max * kFifoMaxChannels * 2, c.s));
@@ -307,9 +332,9 @@ int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
   a.spin_limit = g.spin_limit;
   a.p = p;
   a.C = (int)C;
-  a.NS = g.fifo_slots;
-  a.nsub = (int)std::max<int64_t>(1, (slice + kFifoSlotElems - 1) / kFifoSlotElems);
-  a.slot_elems = kFifoSlotElems;
+  a.NS = NS;
+  a.nsub = (int)std::max<int64_t>(1, (maxslice + slot - 1) / slot);
+  a.slot_elems = slot;
   a.epoch = epoch;
   a.inv_p = inv_p_of(p);
   a.withhold = g.fifo_withhold;
@@ -587,9 +612,8 @@ int sim_init(int device, int p_max, size_t max_bytes_per_rank) {
     sim_finalize();
     return SIM_ERR_HIP;
   }
-  const size_t fifo_bytes = (size_t)p_max * kFifoMaxChannels * kFifoMaxSlots * kFifoSlotElems * 4;
   const int64_t nsem = (int64_t)p_max * kFifoMaxChannels * 2;
-  if (hipMalloc(&g.fifo, fifo_bytes) != hipSuccess || hipMalloc(&g.fifo_sem, (size_t)nsem * 8) != hipSuccess) {
+  if (hipMalloc(&g.fifo_sem, (size_t)nsem * 8) != hipSuccess) {
     sim_finalize();
     return SIM_ERR_NOMEM;
   }

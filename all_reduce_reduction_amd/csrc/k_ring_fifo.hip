@@ -21,12 +21,17 @@
 // Both hold (epoch << 32 | count) with a per-call epoch, so values left by
 // an earlier call compare lower than anything this call waits for.  A
 // sender may run at most NS slots ahead of its receiver (backpressure).
-// Memory ordering: the slot's data stores, an agent-scope release fence in
-// every wave, a workgroup barrier, then one agent-scope RELEASE store of the
-// counter; the waiter polls with relaxed agent-scope loads, passes a
-// barrier, and every lane then performs an agent-scope ACQUIRE load before
-// reading the slot (the other XCDs' L2s are not coherent with this one for
-// plain accesses).
+// Memory ordering.  Each XCD has its own L2, not coherent with the others
+// for plain accesses.  FIFO words are therefore only ever read and written
+// with device-scope (sc1) buffer instructions, which are coherent across
+// XCDs without flushing or invalidating any L2.  A producer wave issues its
+// slot stores, waits for them to complete (s_waitcnt vmcnt(0)), the
+// workgroup meets at a barrier, and only then does one lane store the
+// counter (a relaxed agent-scope atomic, also sc1).  The consumer's lane 0
+// polls the counter with agent-scope loads; the workgroup meets at a
+// barrier; only then are the slot's words loaded.  (A release/acquire pair
+// on the counter would add an L2 write-back and invalidate per step, which
+// measured ~10 us per step.)
 // Every wait is bounded by spin_limit polls; on expiry the workgroup writes
 // SIM_ERR_TIMEOUT to the error word and leaves, so a missing partner (e.g.
 // workgroups that could not be co-resident) ends in an error, never a hang.
@@ -40,6 +45,15 @@ namespace {
 __device__ __forceinline__ unsigned long long tag(unsigned epoch, unsigned long long count) {
   return ((unsigned long long)epoch << 32) | count;
 }
+
+// Device-scope (sc1) accesses to FIFO words through a buffer resource
+// covering one FIFO (offsets are bytes; out-of-range offsets are dropped by
+// the hardware bounds check of the resource).
+constexpr int kSC1 = 16;  // cache-policy bit: coherent at device scope
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t fifo_rsrc(uint32_t* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // thread 0 polls *p until it reaches `want` (or the spin limit); the whole
 // workgroup learns the outcome through *flag_lds.  Returns false on
@@ -74,6 +88,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
   typedef Op<DT, OP> O;
   constexpr int E = Ty<DT>::E;
   constexpr int V = epv<DT>();  // elements per 16-byte storage vector
+  constexpr int U = kFifoVecsPerLane;  // a slot is exactly kBlock * U vectors
   __shared__ int ok_recv, ok_send;
 
   const int p = a.p;
@@ -88,6 +103,8 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
   // my receive FIFO and counters, and my successor's
   uint32_t* my_fifo = a.fifo + ((int64_t)r * a.C + ch) * a.NS * slot_words;
   uint32_t* nx_fifo = a.fifo + ((int64_t)nxt * a.C + ch) * a.NS * slot_words;
+  const __amdgpu_buffer_rsrc_t in_rs = fifo_rsrc(my_fifo, a.NS * slot_words * 4);
+  const __amdgpu_buffer_rsrc_t out_rs = fifo_rsrc(nx_fifo, a.NS * slot_words * 4);
   unsigned long long* my_posted = a.sem + ((int64_t)r * a.C + ch) * 2;
   unsigned long long* my_consumed = my_posted + 1;
   unsigned long long* nx_posted = a.sem + ((int64_t)nxt * a.C + ch) * 2;
@@ -113,7 +130,9 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
       c = ((c % p) + p) % p;
       const int64_t clo = a.lo[c], chi = a.lo[c + 1];
       const int64_t clen = chi - clo;
-      const int64_t s_lo = clo + clen * ch / a.C, s_hi = clo + clen * (ch + 1) / a.C;
+      // channel slice of the chunk, its inner boundaries on whole vectors
+      const int64_t s_lo = clo + (clen * ch / a.C) / V * V;
+      const int64_t s_hi = (ch + 1 == a.C) ? chi : clo + (clen * (ch + 1) / a.C) / V * V;
       const int64_t e0 = s_lo + (int64_t)k * a.slot_elems;
       const int64_t e1 = min(s_hi, e0 + (int64_t)a.slot_elems);
       const int64_t len = e1 > e0 ? e1 - e0 : 0;
@@ -121,35 +140,52 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
       // ---- wait for the incoming slot ----
       if (do_recv) {
         if (!wait_geq(my_posted, tag(epoch, recvd + 1), a.spin_limit, &ok_recv)) goto timeout;
-        (void)__hip_atomic_load(my_posted, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
       }
       // ---- wait for room in the successor's FIFO ----
       if (do_send && sent + 1 > (unsigned long long)a.NS) {
         if (!wait_geq(nx_consumed, tag(epoch, sent + 1 - a.NS), a.spin_limit, &ok_send)) goto timeout;
       }
       {
-        const uint32_t* in_slot = my_fifo + (int64_t)(recvd % a.NS) * slot_words;
-        uint32_t* out_slot = nx_fifo + (int64_t)(sent % a.NS) * slot_words;
+        const int in_base = (int)((recvd % a.NS) * slot_words * 4);   // byte offsets in the FIFOs
+        const int out_base = (int)((sent % a.NS) * slot_words * 4);
         const bool vec = ((e0 % V) == 0);
-        for (int64_t off = (int64_t)tid * V; off < len; off += (int64_t)kBlock * V) {
+        // phase 1: issue every load of this step (U vectors per lane)
+        u32x4 xin[U];
+        u32x4 fin[U][V / 4];
+        bool full[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+          const int64_t off = ((int64_t)u * kBlock + tid) * V;
+          full[u] = vec && off + V <= len;
+          if (full[u]) {
+            if (reduce) xin[u] = ld16(xr, (e0 + off) * E);
+            if (do_recv) {
+#pragma unroll
+              for (int h = 0; h < V / 4; h++)
+                fin[u][h] = __builtin_amdgcn_raw_buffer_load_b128(in_rs, in_base + (int)(off + 4 * h) * 4, 0, kSC1);
+            }
+          }
+        }
+        // phase 2: fold, write the output and the outgoing slot
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+          const int64_t off = ((int64_t)u * kBlock + tid) * V;
           const int64_t i0 = e0 + off;
-          A v[V];
-          uint32_t w[V];
-          const int cnt = (int)min((int64_t)V, len - off);
-          if (vec && cnt == V) {
+          if (full[u]) {
+            A v[V];
+            uint32_t w[V];
             if (reduce) {
               A own[V];
-              unpack<DT>(ld16(xr, i0 * E), own);
+              unpack<DT>(xin[u], own);
               if (step == 0) {
 #pragma unroll
                 for (int e = 0; e < V; e++) v[e] = O::pre(own[e], inv_p);
               } else {
 #pragma unroll
                 for (int h = 0; h < V / 4; h++) {
-                  const u32x4 q = *(const u32x4*)(in_slot + off + 4 * h);
 #pragma unroll
                   for (int e = 0; e < 4; e++) {
-                    const uint32_t bits = q[e];
+                    const uint32_t bits = fin[u][h][e];
                     v[4 * h + e] = __builtin_bit_cast(A, bits);
                   }
                 }
@@ -159,8 +195,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
               if (finish) {
 #pragma unroll
                 for (int e = 0; e < V; e++) v[e] = O::post(v[e], p);
-                const u32x4 packed = pack<DT>(v);
-                st16(yr, i0 * E, packed);
+                st16(yr, i0 * E, pack<DT>(v));
 #pragma unroll
                 for (int e = 0; e < V; e++) w[e] = narrow_bits<DT>(v[e]);
               } else {
@@ -170,9 +205,11 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
             } else {  // gather: finished storage bits arrive; keep and forward them
 #pragma unroll
               for (int h = 0; h < V / 4; h++) {
-                const u32x4 q = *(const u32x4*)(in_slot + off + 4 * h);
 #pragma unroll
-                for (int e = 0; e < 4; e++) w[4 * h + e] = q[e];
+                for (int e = 0; e < 4; e++) {
+                  const uint32_t bits = fin[u][h][e];
+                  w[4 * h + e] = bits;
+                }
               }
               u32x4 out;
               if constexpr (E == 4) {
@@ -190,10 +227,11 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
                 u32x4 q;
 #pragma unroll
                 for (int e = 0; e < 4; e++) q[e] = w[4 * h + e];
-                *(u32x4*)(out_slot + off + 4 * h) = q;
+                __builtin_amdgcn_raw_buffer_store_b128(q, out_rs, out_base + (int)(off + 4 * h) * 4, 0, kSC1);
               }
             }
-          } else {  // ragged: element by element
+          } else if (off < len) {  // ragged: element by element
+            const int cnt = (int)min((int64_t)V, len - off);
             for (int e = 0; e < cnt; e++) {
               const int64_t i = i0 + e;
               uint32_t word;
@@ -203,7 +241,8 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
                 if (step == 0) {
                   val = own;
                 } else {
-                  const uint32_t bits = in_slot[off + e];
+                  const uint32_t bits =
+                      __builtin_amdgcn_raw_buffer_load_b32(in_rs, in_base + (int)(off + e) * 4, 0, kSC1);
                   val = O::comb(__builtin_bit_cast(A, bits), own);
                 }
                 if (finish) {
@@ -214,26 +253,27 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
                   word = __builtin_bit_cast(uint32_t, val);
                 }
               } else {
-                word = in_slot[off + e];
+                word = __builtin_amdgcn_raw_buffer_load_b32(in_rs, in_base + (int)(off + e) * 4, 0, kSC1);
                 if constexpr (E == 4) ((uint32_t*)yr)[i] = word;
                 else ((uint16_t*)yr)[i] = (uint16_t)word;
               }
-              if (do_send) out_slot[off + e] = word;
+              if (do_send)
+                __builtin_amdgcn_raw_buffer_store_b32(word, out_rs, out_base + (int)(off + e) * 4, 0, kSC1);
             }
           }
         }
       }
-      // Every wave makes its own slot stores visible at agent scope before
-      // the barrier: a workgroup barrier alone does not wait for the other
-      // waves' stores, so thread 0's release would not cover them (seen as
-      // stale words in other waves' lanes at 64 channels x 8 slots).
-      if (do_send) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();  // every lane's slot reads and writes are complete
+      // Every wave waits for its own slot stores (and loads) to complete
+      // before the barrier: a workgroup barrier alone does not wait for the
+      // other waves' memory operations, so lane 0's signal could otherwise
+      // overtake them.
+      wait_stores();
+      __syncthreads();
       if (tid == 0) {
         if (do_send)
-          __hip_atomic_store(nx_posted, tag(epoch, sent + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(nx_posted, tag(epoch, sent + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (do_recv)
-          __hip_atomic_store(my_consumed, tag(epoch, recvd + 1), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(my_consumed, tag(epoch, recvd + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       if (do_send) sent++;
       if (do_recv) recvd++;

@@ -89,7 +89,11 @@ struct LLArgs {
 };
 
 // Single-launch ring: p * C persistent workgroups, bounded FIFOs between
-// neighbouring ranks, epoch-tagged monotonic semaphores.
+// neighbouring ranks, epoch-tagged monotonic semaphores.  A FIFO slot holds
+// kBlock * kFifoVecsPerLane 16-byte vectors' worth of elements (one 32-bit
+// word per element): 8192 elements for 16-bit types, 4096 for 32-bit.
+constexpr int kFifoVecsPerLane = 4;
+constexpr int kFifoMaxSlotElems = kBlock * kFifoVecsPerLane * 8;
 struct RingFifoArgs {
   const void* x[SIM_MAX_RANKS];
   void* y[SIM_MAX_RANKS];
@@ -102,7 +106,7 @@ struct RingFifoArgs {
   int C;                       // channels per rank
   int NS;                      // slots per FIFO
   int nsub;                    // slots per channel slice of a chunk
-  int slot_elems;              // multiple of kBlock * 8
+  int slot_elems;              // kBlock * kFifoVecsPerLane * (16 / element bytes)
   unsigned int epoch;
   float inv_p;
   int withhold;                // test hook: rank 0 leaves at once, its partners' waits expire

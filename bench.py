@@ -65,6 +65,8 @@ def algorithmic_bytes(algo: str) -> float:
         n, e = N, ESIZE
         rs = n * (e + e + 4) + (P - 3) * n * (4 + e + 4) + n * (4 + e + e)
         return rs + (P - 1) * n * (e + e)
+    if algo == "ring_fifo":  # HBM-side: inputs once, outputs once (FIFO words counted apart)
+        return 2.0 * P * S
     raise ValueError(algo)
 
 
@@ -171,7 +173,7 @@ def main():
         return
     busbw = 2 * (P - 1) / P * S / t / 1e9
     kernel = {"oneshot": "k_fold (one-shot, all outputs)", "allpairs": "k_fold + k_copy",
-              "ring": "k_ring_reduce + k_copy"}[ran]
+              "ring": "k_ring_reduce + k_copy", "ring_fifo": "k_ring_fifo"}[ran]
     achieved = algorithmic_bytes(ran) / t / 1e9
     traffic = load_traffic(ran)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -181,7 +183,7 @@ def main():
     extras = {}
     if not args.no_extras:
         per_algo = {}
-        for a in ("oneshot", "allpairs", "ring"):
+        for a in ("oneshot", "allpairs", "ring", "ring_fifo"):
             ta = time_calls(lambda a=a: step(a), max(10, args.steps // 4), 5)
             per_algo[a] = {"us": round(ta * 1e6, 2), "busbw_GBps": round(2 * (P - 1) / P * S / ta / 1e9, 1),
                            "hbm_algorithmic_GBps": round(algorithmic_bytes(a) / ta / 1e9, 1)}
@@ -192,7 +194,7 @@ def main():
         lout = [torch.empty(LAT_N, dtype=torch.int16, device=dev) for _ in range(P)]
         lip, lop = [t_.data_ptr() for t_ in lin], [t_.data_ptr() for t_ in lout]
         lat = {}
-        for a in ("oneshot", "oneshot_ll", "allpairs", "ring", "auto"):
+        for a in ("oneshot", "oneshot_ll", "allpairs", "ring", "ring_fifo", "auto"):
             call = sim.prepare_allreduce(lip, lop, P, LAT_N, "fp16", "sum", a, stream)
             if call() != 0:
                 raise sim.SimError(call(), f"sim_allreduce({a})")

@@ -100,7 +100,8 @@ enum {
 /* Initialise the library on HIP device `device` for up to p_max ranks
  * (2..SIM_MAX_RANKS).  Allocates the device error word, the LL packet
  * buffer (p_max * 2 * SIM_LL_MAX_BYTES_PER_RANK bytes), the single-launch
- * ring's FIFOs and semaphores (p_max * 64 channels * 8 slots * 16 KiB) and, when
+ * ring's semaphores (its FIFOs, p * channels * slots * 32 KiB at most,
+ * are allocated on first use and grown when needed) and, when
  * max_bytes_per_rank > 0, the ring/reduce-scatter partial scratch for
  * messages up to that size (otherwise scratch grows on first need).
  * Calling it again re-initialises (finalize + init).  Errors:
@@ -210,7 +211,7 @@ enum {
   SIM_DEBUG_LOG = 4,           /* 1: log one line per call to stderr (also SIM_DEBUG=1) */
   SIM_DEBUG_WORKGROUPS = 5,    /* force the workgroup count of bulk kernels (0 = heuristic) */
   SIM_DEBUG_UNROLL = 6,        /* 16-byte vectors per lane per pass in bulk kernels: 1 or 2 */
-  SIM_DEBUG_FIFO_CHANNELS = 7, /* single-launch ring: channels per rank (0 = heuristic) */
+  SIM_DEBUG_FIFO_CHANNELS = 7, /* single-launch ring: channels per rank, <= 128 (0 = heuristic) */
   SIM_DEBUG_FIFO_SLOTS = 8,    /* single-launch ring: slots per FIFO, 2..8 (default 4) */
   SIM_DEBUG_FIFO_WITHHOLD = 9  /* 1: rank 0's ring workgroups leave at once (forces a bounded-wait expiry) */
 };
