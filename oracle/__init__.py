@@ -15,7 +15,10 @@ What it computes follows the pages (see the header of ``oracle.c``):
   * the all-pairs schedule -- "MSCCL, in depth ...", section "Writing an
     algorithm in MSCCLang"; one-shot/LL share its fold order ("MSCCL++:
     Rethinking GPU Communication Abstractions for AI Inference", section
-    "The Collective Algorithm Library", 1PA/2PA).
+    "The Collective Algorithm Library", 1PA/2PA);
+  * the double binary tree -- "Inside NCCL all-reduce", section "The double
+    binary tree"; 2PH -- the MSCCL++ page, same section, item 4; the k-ary
+    recursive exchange -- the NVSHMEM analysis, Fig. 7.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against printed
 values, closed forms, brute force and library routines.
@@ -35,7 +38,9 @@ LIBPATH = os.path.join(_HERE, "liboracle.so")
 
 DTYPES = {"int32": 0, "fp32": 1, "fp16": 2, "bf16": 3}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
-ALGOS = {"ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4, "ring_fifo": 5}
+ALGOS = {"ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4, "ring_fifo": 5,
+         "tree": 6, "rexch": 7, "hier": 8, "hier_large": 9}
+TOPO_ALGOS = ("tree", "rexch", "hier", "hier_large")
 STORAGE = {"int32": np.int32, "fp32": np.float32, "fp16": np.uint16, "bf16": np.uint16}
 
 CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
@@ -63,7 +68,15 @@ class Oracle:
         lib.oracle_all_gather.argtypes = [pp, pp, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int]
         lib.oracle_allreduce_at.argtypes = [pp, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_void_p, i64, ctypes.c_void_p]
-        for name in ("allreduce", "definition", "reduce_scatter", "all_gather", "allreduce_at"):
+        lib.oracle_allreduce_topo.argtypes = [pp, pp, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.oracle_allreduce_at_topo.argtypes = [pp, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_void_p, i64, ctypes.c_void_p]
+        lib.oracle_tree_parent.argtypes = [ctypes.c_int] * 4
+        lib.oracle_tree_parent.restype = ctypes.c_int
+        for name in ("allreduce", "definition", "reduce_scatter", "all_gather", "allreduce_at",
+                     "allreduce_topo", "allreduce_at_topo"):
             getattr(lib, "oracle_" + name).restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_chunk_lo.argtypes = [i64, ctypes.c_int, ctypes.c_int]
@@ -89,12 +102,15 @@ class Oracle:
 
     # -- collectives ---------------------------------------------------
     def allreduce(self, xs: Sequence[np.ndarray], dtype: str, op: str, algo: str,
-                  inplace: bool = False) -> Tuple[List[np.ndarray], int]:
-        """Run the algorithm's schedule; returns (p outputs, steps)."""
+                  inplace: bool = False, ranks_per_node: int = 1, radix: int = 2
+                  ) -> Tuple[List[np.ndarray], int]:
+        """Run the algorithm's schedule; returns (p outputs, steps or rounds).
+        ranks_per_node and radix are the topology of the tree, recursive
+        exchange and 2PH schedules (ignored by the others)."""
         n = self._check_inputs(xs, dtype)
         ys = list(xs) if inplace else [np.empty_like(x) for x in xs]
-        steps = self.lib.oracle_allreduce(self._ptrs(xs), self._ptrs(ys), len(xs), n,
-                                          DTYPES[dtype], OPS[op], ALGOS[algo])
+        steps = self.lib.oracle_allreduce_topo(self._ptrs(xs), self._ptrs(ys), len(xs), n,
+                                               DTYPES[dtype], OPS[op], ALGOS[algo], ranks_per_node, radix)
         if steps < 0:
             raise ValueError("oracle_allreduce rejected its arguments")
         return ys, steps
@@ -129,13 +145,14 @@ class Oracle:
         return ys, steps
 
     def allreduce_at(self, xs: Sequence[np.ndarray], dtype: str, op: str, algo: str,
-                     idx: np.ndarray) -> np.ndarray:
+                     idx: np.ndarray, ranks_per_node: int = 1, radix: int = 2) -> np.ndarray:
         """The result at the given element indices (identical on every rank)."""
         n = self._check_inputs(xs, dtype)
         idx = np.ascontiguousarray(idx, dtype=np.int64)
         out = np.empty(idx.size, dtype=STORAGE[dtype])
-        rc = self.lib.oracle_allreduce_at(self._ptrs(xs), len(xs), n, DTYPES[dtype], OPS[op], ALGOS[algo],
-                                          idx.ctypes.data, idx.size, out.ctypes.data)
+        rc = self.lib.oracle_allreduce_at_topo(self._ptrs(xs), len(xs), n, DTYPES[dtype], OPS[op],
+                                               ALGOS[algo], ranks_per_node, radix,
+                                               idx.ctypes.data, idx.size, out.ctypes.data)
         if rc < 0:
             raise ValueError("oracle_allreduce_at rejected its arguments")
         return out
@@ -164,6 +181,13 @@ class Oracle:
         y = np.empty(h.shape, dtype=np.float32)
         self.lib.oracle_f16_to_f32_array(h.ctypes.data, y.ctypes.data, h.size)
         return y
+
+    def tree_parent(self, tree: int, p: int, ranks_per_node: int, rank: int) -> int:
+        """Parent of `rank` in tree 0 or 1 of the double binary tree (-1: root)."""
+        v = self.lib.oracle_tree_parent(tree, p, ranks_per_node, rank)
+        if v < -1:
+            raise ValueError("oracle_tree_parent rejected its arguments")
+        return v
 
     def num_threads(self) -> int:
         return self.lib.oracle_num_threads()

@@ -17,7 +17,13 @@
  *           (a different reduction order is not bitwise equal).
  *  [MSCCLPP] "MSCCL++: Rethinking GPU Communication Abstractions for AI
  *           Inference": section "The Collective Algorithm Library" (1PA, 2PA,
- *           2PR).
+ *           2PR, and 2PH: local reduce-scatter, cross-node all-pairs, local
+ *           all-gather; small- and large-message forms).
+ *  [NCCL]   also section "The double binary tree" (the bit-trick tree, its
+ *           14-rank drawing, the mirror/shift second tree, chains inside a
+ *           node) and section "How NCCL picks" (the tree's latency count).
+ *  [NVSHMEM] "Demystifying NVSHMEM" analysis, Fig. 7 (k-ary recursive
+ *           exchange as the P2P all-reduce).
  *
  * Arithmetic.  Accumulation is fp32 for every floating type (the parity bar
  * fixes fp32 accumulation and bit-exact fp32 results in schedule order), and
@@ -41,6 +47,23 @@
  *  - 16-bit outputs: partials stay fp32 between ring hops; one RNE narrowing
  *    at the final write.
  *  - min/max: acc = (b < a) ? b : a  /  (b > a) ? b : a, a = accumulator.
+ *  - double binary tree: chunk t (t = 0, 1) of the buffer cut in two runs on
+ *    tree t; a rank adds its children's subtree totals to its own value in
+ *    ascending child order; the root's total is post-processed and is every
+ *    rank's result.  Tree two = tree one's mirror (node x plays n-1-x) for
+ *    an even node count, tree one shifted by +1 node for an odd one (the
+ *    pages say "shifted by one rank" without a direction: the +1 is a
+ *    reading, and parity is unpinned for that direction alone).  With
+ *    G ranks per node, node k is rank kG and ranks kG+1..kG+G-1 hang below
+ *    it as a chain.
+ *  - recursive exchange: p must be k^m; round j (j = 0 first) folds the k
+ *    ranks that differ only in base-k digit j, in ascending rank order.
+ *  - 2PH: nodes are G consecutive ranks.  Small form: G chunks; chunk i is
+ *    folded inside node K by rank (K, i) -- own element, then the node's
+ *    others ascending -- and the node partials are folded in ascending node
+ *    order.  Large form: p chunks; chunk c is owned by rank c = (K, i);
+ *    node partials as above at position i; the owner's node partial first,
+ *    then the other nodes' ascending.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -52,7 +75,9 @@
 /* ---- codes (kept numerically equal to the library's public enums) ---- */
 enum { OR_INT32 = 0, OR_FP32 = 1, OR_FP16 = 2, OR_BF16 = 3 };
 enum { OR_SUM = 0, OR_PROD = 1, OR_MIN = 2, OR_MAX = 3, OR_AVG = 4 };
-enum { OR_RING = 1, OR_ALLPAIRS = 2, OR_ONESHOT = 3, OR_ONESHOT_LL = 4, OR_RING_FIFO = 5 };
+enum { OR_RING = 1, OR_ALLPAIRS = 2, OR_ONESHOT = 3, OR_ONESHOT_LL = 4, OR_RING_FIFO = 5,
+       OR_TREE = 6, OR_REXCH = 7, OR_HIER = 8, OR_HIER_LARGE = 9 };
+#define OR_MAXP 128
 #define OR_EBADARG (-1)
 
 /* ------------------------------------------------------------------ */
@@ -211,7 +236,7 @@ static int64_t chunk_of(int64_t n, int p, int64_t i) {
 }
 
 static int check_args(int p, int64_t n, int dtype, int op) {
-  if (p < 2 || p > 64 || n < 0) return OR_EBADARG;
+  if (p < 2 || p > OR_MAXP || n < 0) return OR_EBADARG;
   if (dtype < OR_INT32 || dtype > OR_BF16) return OR_EBADARG;
   if (op < OR_SUM || op > OR_AVG) return OR_EBADARG;
   return 0;
@@ -314,13 +339,187 @@ static int allpairs(const ctx_t* c, const void* const* X, void* const* Y, int64_
 }
 
 /* ------------------------------------------------------------------ */
+/* Topology schedules: each rank's result is computed element by element */
+/* straight from the algorithm's definition.                             */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  int algo, G, k;              /* ranks per node, radix */
+  int nchunks;
+  int parent[2][OR_MAXP];      /* rank trees (double binary tree) */
+} topo_t;
+
+/* NCCL's tree over n nodes, by its parent rule only ([NCCL] "The double
+ * binary tree"): the lowest set bit b of x is cleared and the next bit up is
+ * set; if that leaves the node range, b is only cleared.  Node 0 is the
+ * root.  Children are found by inverting this relation. */
+static int bittree_parent(int n, int x) {
+  if (x == 0) return -1;
+  int b = 1;
+  while (!(x & b)) b <<= 1;
+  int up = (x & ~b) | (b << 1);
+  if (up >= n) up = x & ~b;
+  return up;
+}
+
+/* Node parent in tree t: t = 1 relabels tree one's nodes, x -> n-1-x when
+ * n is even, x -> x+1 (mod n) when n is odd. */
+static int node_parent(int t, int n, int x) {
+  if (t == 0) return bittree_parent(n, x);
+  if (n % 2 == 0) {
+    int q = bittree_parent(n, n - 1 - x);
+    return q < 0 ? -1 : n - 1 - q;
+  }
+  int q = bittree_parent(n, (x + n - 1) % n);
+  return q < 0 ? -1 : (q + 1) % n;
+}
+
+static int topo_init(topo_t* T, int algo, int p, int G, int k) {
+  memset(T, 0, sizeof *T);
+  T->algo = algo; T->G = G; T->k = k;
+  if (algo == OR_TREE || algo == OR_HIER || algo == OR_HIER_LARGE)
+    if (G < 1 || p % G != 0) return OR_EBADARG;
+  if (algo == OR_TREE) {
+    const int nn = p / G;
+    for (int t = 0; t < 2; t++)
+      for (int r = 0; r < p; r++) {
+        if (r % G != 0) { T->parent[t][r] = r - 1; continue; }   /* chain inside the node */
+        int up = node_parent(t, nn, r / G);
+        T->parent[t][r] = up < 0 ? -1 : up * G;
+      }
+    T->nchunks = 2;
+  } else if (algo == OR_REXCH) {
+    if (k < 2) return OR_EBADARG;
+    int v = 1;
+    while (v < p) v *= k;
+    if (v != p) return OR_EBADARG;
+    T->nchunks = 1;
+  } else if (algo == OR_HIER) {
+    T->nchunks = G;
+  } else if (algo == OR_HIER_LARGE) {
+    T->nchunks = p;
+  } else {
+    return OR_EBADARG;
+  }
+  return 0;
+}
+
+/* Subtree total of rank r in tree t: own value, then each child's subtree
+ * total, children in ascending rank order. */
+static acc_t subtree(const ctx_t* c, const topo_t* T, const void* const* X, int t, int r, int64_t i) {
+  acc_t v = pre(c, X[r], i);
+  for (int q = 0; q < c->p; q++)
+    if (q != r && T->parent[t][q] == r) v = combine(c, v, subtree(c, T, X, t, q, i));
+  return v;
+}
+
+/* Node K's partial of element i at local position pos: rank (K, pos) first,
+ * then the node's other ranks ascending. */
+static acc_t node_partial(const ctx_t* c, int G, const void* const* X, int K, int pos, int64_t i) {
+  acc_t v = pre(c, X[K * G + pos], i);
+  for (int j = 0; j < G; j++)
+    if (j != pos) v = combine(c, v, pre(c, X[K * G + j], i));
+  return v;
+}
+
+/* The value rank r ends with at element i (before post-processing). */
+static acc_t topo_value(const ctx_t* c, const topo_t* T, const void* const* X, int64_t n, int r, int64_t i) {
+  const int p = c->p;
+  const int ch = (int)chunk_of(n, T->nchunks, i);
+  switch (T->algo) {
+    case OR_TREE: {
+      int root = 0;
+      while (T->parent[ch][root] >= 0) root = T->parent[ch][root];   /* walk up from rank 0 */
+      return subtree(c, T, X, ch, root, i);
+    }
+    case OR_REXCH: {
+      acc_t v[OR_MAXP], w[OR_MAXP];
+      for (int q = 0; q < p; q++) v[q] = pre(c, X[q], i);
+      for (int stride = 1; stride < p; stride *= T->k) {
+        for (int q = 0; q < p; q++) {
+          const int digit = (q / stride) % T->k;
+          const int first = q - digit * stride;      /* the group's lowest rank */
+          acc_t a = v[first];
+          for (int m = 1; m < T->k; m++) a = combine(c, a, v[first + m * stride]);
+          w[q] = a;
+        }
+        memcpy(v, w, sizeof(acc_t) * (size_t)p);
+      }
+      return v[r];
+    }
+    case OR_HIER: {
+      acc_t a = node_partial(c, T->G, X, 0, ch, i);
+      for (int K = 1; K < p / T->G; K++) a = combine(c, a, node_partial(c, T->G, X, K, ch, i));
+      return a;
+    }
+    default: {   /* OR_HIER_LARGE: chunk ch is owned by rank ch */
+      const int K0 = ch / T->G, pos = ch % T->G;
+      acc_t a = node_partial(c, T->G, X, K0, pos, i);
+      for (int K = 0; K < p / T->G; K++)
+        if (K != K0) a = combine(c, a, node_partial(c, T->G, X, K, pos, i));
+      return a;
+    }
+  }
+}
+
+/* Communication rounds: tree, 2 x the root's height (up, then down);
+ * recursive exchange, log_k p; 2PH, one per phase that has work. */
+static int topo_rounds(const topo_t* T, int p) {
+  if (T->algo == OR_TREE) {
+    int h = 0;
+    for (int r = 0; r < p; r++) {       /* deepest rank in tree one */
+      int d = 0;
+      for (int q = r; T->parent[0][q] >= 0; q = T->parent[0][q]) d++;
+      if (d > h) h = d;
+    }
+    return 2 * h;
+  }
+  if (T->algo == OR_REXCH) {
+    int m = 0;
+    for (int v = 1; v < p; v *= T->k) m++;
+    return m;
+  }
+  const int local = T->G > 1, cross = p / T->G > 1;
+  return (T->algo == OR_HIER) ? 2 * local + cross : 2 * local + 2 * cross;
+}
+
+static int topo_allreduce(const ctx_t* c, const void* const* X, void* const* Y, int64_t n,
+                          int algo, int G, int k) {
+  const int p = c->p;
+  topo_t T;
+  if (topo_init(&T, algo, p, G, k)) return OR_EBADARG;
+  const int e = esize(c->dtype);
+  /* results go to a separate buffer first so that in-place calls read
+   * untouched inputs */
+  char* out = (char*)malloc((size_t)(n > 0 ? n : 1) * (size_t)e * (size_t)p);
+  if (!out) return OR_EBADARG;
+  #pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; i++)
+    for (int r = 0; r < p; r++)
+      post_store(c, topo_value(c, &T, X, n, r, i), out + (size_t)r * (size_t)n * (size_t)e, i);
+  for (int r = 0; r < p; r++) memcpy(Y[r], out + (size_t)r * (size_t)n * (size_t)e, (size_t)n * (size_t)e);
+  free(out);
+  return topo_rounds(&T, p);
+}
+
+/* Parent of rank r in tree t (0 or 1) of the double binary tree over p
+ * ranks with G ranks per node; -1 for the root, -2 for bad arguments. */
+int oracle_tree_parent(int t, int p, int G, int r) {
+  topo_t T;
+  if (p < 1 || p > OR_MAXP || t < 0 || t > 1 || r < 0 || r >= p) return -2;
+  if (topo_init(&T, OR_TREE, p, G, 2)) return -2;
+  return T.parent[t][r];
+}
+
+/* ------------------------------------------------------------------ */
 /* Public entry points.  X, Y: arrays of p host pointers.  In-place      */
 /* (X[r] == Y[r]) is allowed.  Return: steps executed, or -1.            */
 /* ------------------------------------------------------------------ */
-int oracle_allreduce(const void* const* X, void* const* Y, int p, int64_t n,
-                     int dtype, int op, int algo) {
+int oracle_allreduce_topo(const void* const* X, void* const* Y, int p, int64_t n,
+                          int dtype, int op, int algo, int ranks_per_node, int radix) {
   if (check_args(p, n, dtype, op)) return OR_EBADARG;
   ctx_t c = make_ctx(p, dtype, op);
+  if (algo >= OR_TREE && algo <= OR_HIER_LARGE)
+    return topo_allreduce(&c, X, Y, n, algo, ranks_per_node, radix);
   /* the single-launch ring runs the ring's schedule: same steps, same order */
   if (algo == OR_RING || algo == OR_RING_FIFO) {
     int s1 = ring_reduce_scatter(&c, X, Y, n, 0);
@@ -330,6 +529,13 @@ int oracle_allreduce(const void* const* X, void* const* Y, int p, int64_t n,
   if (algo == OR_ALLPAIRS || algo == OR_ONESHOT || algo == OR_ONESHOT_LL)
     return allpairs(&c, X, Y, n);
   return OR_EBADARG;
+}
+
+/* The schedules that take no topology (ring, all-pairs, one-shot, LL);
+ * the topology ones with one rank per node and radix 2. */
+int oracle_allreduce(const void* const* X, void* const* Y, int p, int64_t n,
+                     int dtype, int op, int algo) {
+  return oracle_allreduce_topo(X, Y, p, n, dtype, op, algo, 1, 2);
 }
 
 /* The plain definition Y[r][i] = X[0][i] (+) X[1][i] (+) ... (+) X[p-1][i]
@@ -395,14 +601,20 @@ int oracle_all_gather(const void* const* X, void* const* Y, int p, int64_t n_in,
  * (ch+1+s) mod p to its successor, which folds its own element in; the
  * all-gather half only copies.  All-pairs/one-shot/LL: owner first, then the
  * other ranks ascending.  out is dtype-typed, m elements. */
-int oracle_allreduce_at(const void* const* X, int p, int64_t n, int dtype, int op,
-                        int algo, const int64_t* idx, int64_t m, void* out) {
+int oracle_allreduce_at_topo(const void* const* X, int p, int64_t n, int dtype, int op,
+                             int algo, int ranks_per_node, int radix,
+                             const int64_t* idx, int64_t m, void* out) {
   if (check_args(p, n, dtype, op)) return OR_EBADARG;
-  if (algo != OR_RING && algo != OR_ALLPAIRS && algo != OR_ONESHOT && algo != OR_ONESHOT_LL &&
-      algo != OR_RING_FIFO)
-    return OR_EBADARG;
+  if (algo < OR_RING || algo > OR_HIER_LARGE) return OR_EBADARG;
   ctx_t c = make_ctx(p, dtype, op);
   for (int64_t k = 0; k < m; k++) if (idx[k] < 0 || idx[k] >= n) return OR_EBADARG;
+  if (algo >= OR_TREE) {   /* rank 0's value: every rank ends with the same */
+    topo_t T;
+    if (topo_init(&T, algo, p, ranks_per_node, radix)) return OR_EBADARG;
+    #pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < m; k++) post_store(&c, topo_value(&c, &T, X, n, 0, idx[k]), out, k);
+    return 0;
+  }
   #pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < m; k++) {
     const int64_t i = idx[k];
@@ -421,6 +633,11 @@ int oracle_allreduce_at(const void* const* X, int p, int64_t n, int dtype, int o
     post_store(&c, v, out, k);
   }
   return 0;
+}
+
+int oracle_allreduce_at(const void* const* X, int p, int64_t n, int dtype, int op,
+                        int algo, const int64_t* idx, int64_t m, void* out) {
+  return oracle_allreduce_at_topo(X, p, n, dtype, op, algo, 1, 2, idx, m, out);
 }
 
 int oracle_num_threads(void) {

@@ -16,6 +16,7 @@ import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo")
+TOPO_ALGOS = ("tree", "rexch", "hier", "hier_large")
 
 
 def _golden(name):
@@ -322,9 +323,318 @@ def check_sampled(orc):
                 assert got.tobytes() == ys[0][idx].tobytes(), (p, n, algo, op)
 
 
+# --------------------------------------------------------------------------
+# Double binary tree, recursive exchange, 2PH.
+# --------------------------------------------------------------------------
+def _tree_from_golden():
+    g = _golden("tree14.json")
+    parent = [-1] * g["n"]
+    for child, par in g["edges"]:
+        parent[child] = par
+    return g["n"], parent
+
+
+def _children(parent):
+    ch = {r: [] for r in range(len(parent))}
+    for r, q in enumerate(parent):
+        if q >= 0:
+            ch[q].append(r)
+    return {r: sorted(v) for r, v in ch.items()}
+
+
+def _tree_ok(parent):
+    """A spanning tree: one root, every rank reaches it without a cycle."""
+    n = len(parent)
+    roots = [r for r in range(n) if parent[r] == -1]
+    assert len(roots) == 1, roots
+    for r in range(n):
+        seen, q = set(), r
+        while q != -1:
+            assert q not in seen and 0 <= q < n, (r, q)
+            seen.add(q)
+            q = parent[q]
+    return roots[0]
+
+
+def _f32_tree_total(vals, parent):
+    """Own value first, then each child's subtree total, children ascending."""
+    ch = _children(parent)
+    root = _tree_ok(parent)
+
+    def total(r):
+        acc = np.float32(vals[r])
+        for c in ch[r]:
+            acc = np.float32(acc + total(c))
+        return acc
+    return total(root)
+
+
+def _oracle_tree(orc, t, p, G):
+    return [orc.tree_parent(t, p, G, r) for r in range(p)]
+
+
+def check_tree_drawing(orc):
+    """Tree one over 14 ranks is the tree the page draws, edge for edge."""
+    n, parent = _tree_from_golden()
+    assert _oracle_tree(orc, 0, n, 1) == parent
+
+
+def check_dtree_listing(orc):
+    """The 12-rank figure: interior/leaf split of both trees, tree two as
+    the mirror image of tree one, and tree one's interior ranks in level
+    order (levels top down, ascending inside a level)."""
+    g = _golden("dtree12.json")
+    n, k = g["n"], g["interior"]
+    for t, listing in ((0, g["tree_one"]), (1, g["tree_two"])):
+        ch = _children(_oracle_tree(orc, t, n, 1))
+        interior = {r for r in range(n) if ch[r]}
+        assert interior == set(listing[:k]), (t, interior)
+        assert {r for r in range(n) if not ch[r]} == set(listing[k:]), t
+    # the figure's own mirror relation: interior lists correspond rank for rank
+    assert g["tree_two"][:k] == [n - 1 - r for r in g["tree_one"][:k]]
+    parent = _oracle_tree(orc, 0, n, 1)
+    ch = _children(parent)
+    level, order = [_tree_ok(parent)], []
+    while level:
+        order += [r for r in level if ch[r]]
+        level = sorted(c for r in level for c in ch[r])
+    assert order == g["tree_one"][:k], order
+
+
+def check_tree_shapes(orc):
+    """For every node count: both trees span all ranks, binary, tree one's
+    leaves are the odd ranks, height ceil(log2 n); with an even count every
+    rank is interior in exactly one tree, with an odd count exactly one
+    rank is interior in both."""
+    for n in range(2, 65):
+        both = None
+        for t in (0, 1):
+            parent = _oracle_tree(orc, t, n, 1)
+            _tree_ok(parent)
+            ch = _children(parent)
+            assert max(len(v) for v in ch.values()) <= 2, (n, t)
+            if t == 0:
+                assert {r for r in range(n) if not ch[r]} == {r for r in range(1, n, 2)}, n
+                depth = 0
+                for r in range(n):
+                    d, q = 0, r
+                    while parent[q] != -1:
+                        q, d = parent[q], d + 1
+                    depth = max(depth, d)
+                assert depth == (n - 1).bit_length(), (n, depth)
+            inner = {r for r in range(n) if ch[r]}
+            both = inner if both is None else both & inner
+            if t == 1:
+                union = both | inner
+        interior_in_both = both
+        if n % 2 == 0:
+            assert not interior_in_both, (n, interior_in_both)
+        else:
+            assert len(interior_in_both) == 1, (n, interior_in_both)
+
+
+def check_tree_chains(orc):
+    """G ranks per node: rank kG+i (i > 0) hangs below kG+i-1; rank kG sits
+    at node k's place in the node tree."""
+    for p, G in ((8, 2), (12, 3), (16, 4), (12, 12), (6, 1)):
+        for t in (0, 1):
+            parent = _oracle_tree(orc, t, p, G)
+            node = _oracle_tree(orc, t, p // G, 1) if p // G > 1 else [-1]
+            for r in range(p):
+                if r % G:
+                    assert parent[r] == r - 1, (p, G, t, r)
+                else:
+                    want = node[r // G]
+                    assert parent[r] == (-1 if want == -1 else want * G), (p, G, t, r)
+
+
+def check_tree_rounds(orc):
+    """The page's tree latency count 2((ranks per node - 1) + log2(nodes))
+    hops, and its two printed cases: 16 nodes -> 8, 128 nodes -> 14."""
+    for nodes, want in ((16, 8), (128, 14)):
+        xs = [np.zeros(1, dtype=np.int32) for _ in range(nodes)]
+        assert orc.allreduce(xs, "int32", "sum", "tree")[1] == want, nodes
+    for p in range(2, 17):
+        for G in range(1, p + 1):
+            nodes = p // G
+            if p % G or nodes & (nodes - 1):
+                continue
+            xs = [np.zeros(3, dtype=np.int32) for _ in range(p)]
+            rounds = orc.allreduce(xs, "int32", "sum", "tree", ranks_per_node=G)[1]
+            assert rounds == 2 * ((G - 1) + nodes.bit_length() - 1), (p, G, rounds)
+
+
+def check_tree_association(orc):
+    """fp32 sums: each half of the buffer is the tree total (own value, then
+    children ascending) on its tree -- for 14 ranks the page's drawing and
+    its mirror; elsewhere the oracle's trees, whose shapes the checks above
+    pin."""
+    rng = np.random.default_rng(61)
+    n14, drawn = _tree_from_golden()
+    mirror = [-1 if drawn[n14 - 1 - r] == -1 else n14 - 1 - drawn[n14 - 1 - r] for r in range(n14)]
+    cases = [(n14, 1, drawn, mirror)]
+    for p, G in ((5, 1), (8, 1), (9, 1), (16, 1), (8, 2), (12, 3), (6, 6)):
+        cases.append((p, G, _oracle_tree(orc, 0, p, G), _oracle_tree(orc, 1, p, G)))
+    for p, G, t0, t1 in cases:
+        n = 41
+        xs = [rng.standard_normal(n).astype(np.float32) for _ in range(p)]
+        ys, _ = orc.allreduce(xs, "fp32", "sum", "tree", ranks_per_node=G)
+        for i in range(n):
+            parent = t0 if i < n // 2 else t1
+            want = _f32_tree_total([x[i] for x in xs], parent)
+            for y in ys:
+                assert y[i] == want, (p, G, i)
+
+
+def check_tree_chain_closed_form(orc):
+    """One node (G = p): the tree is the chain 0 <- 1 <- ... <- p-1, so the
+    result is x0 + (x1 + (... + x_{p-1})), a right fold; 2(p-1) rounds."""
+    rng = np.random.default_rng(62)
+    for p in (2, 3, 5, 8):
+        xs = [rng.standard_normal(23).astype(np.float32) for _ in range(p)]
+        ys, rounds = orc.allreduce(xs, "fp32", "sum", "tree", ranks_per_node=p)
+        assert rounds == 2 * (p - 1)
+        acc = xs[p - 1].copy()
+        for q in range(p - 2, -1, -1):
+            acc = (xs[q] + acc).astype(np.float32)
+        for y in ys:
+            assert y.tobytes() == acc.tobytes(), p
+
+
+def _kary_closed_form(xs, k):
+    """Consecutive blocks of k values folded left to right, repeated: the
+    k-ary tree reduction over the rank order."""
+    cur = [x.astype(np.float32) for x in xs]
+    while len(cur) > 1:
+        nxt = []
+        for b in range(0, len(cur), k):
+            acc = cur[b]
+            for t in range(1, k):
+                acc = (acc + cur[b + t]).astype(np.float32)
+            nxt.append(acc)
+        cur = nxt
+    return cur[0]
+
+
+def check_rexch(orc):
+    """Recursive exchange: log_k p rounds; fp32 sums equal the k-ary tree
+    reduction over consecutive rank blocks (digit 0 first); one round
+    (p = k) is the plain left fold of the definition; p must be k^m."""
+    rng = np.random.default_rng(63)
+    for p, k in ((2, 2), (4, 2), (8, 2), (16, 2), (16, 4), (9, 3), (8, 8), (16, 16), (27, 3)):
+        xs = [rng.standard_normal(37).astype(np.float32) for _ in range(p)]
+        ys, rounds = orc.allreduce(xs, "fp32", "sum", "rexch", radix=k)
+        m, v = 0, 1
+        while v < p:
+            v, m = v * k, m + 1
+        assert rounds == m, (p, k, rounds)
+        want = _kary_closed_form(xs, k)
+        for y in ys:
+            assert y.tobytes() == want.tobytes(), (p, k)
+        if p == k:
+            assert ys[0].tobytes() == orc.definition(xs, "fp32", "sum").tobytes()
+    for p, k in ((6, 2), (8, 3), (12, 4)):
+        xs = [np.zeros(4, dtype=np.int32) for _ in range(p)]
+        try:
+            orc.allreduce(xs, "int32", "sum", "rexch", radix=k)
+        except ValueError:
+            continue
+        raise AssertionError(("accepted a rank count that is not a power of the radix", p, k))
+
+
+def _hier_closed_form(xs, G, large):
+    p = len(xs)
+    nodes = p // G
+    n = xs[0].size
+    nch = p if large else G
+    out = np.empty(n, dtype=np.float32)
+
+    def partial(K, pos, i):
+        acc = np.float32(xs[K * G + pos][i])
+        for j in range(G):
+            if j != pos:
+                acc = np.float32(acc + xs[K * G + j][i])
+        return acc
+    for c, (lo, hi) in enumerate(chunk_bounds(n, nch)):
+        for i in range(lo, hi):
+            if large:
+                K0, pos = divmod(c, G)
+                order = [K0] + [K for K in range(nodes) if K != K0]
+            else:
+                pos, order = c, list(range(nodes))
+            acc = partial(order[0], pos, i)
+            for K in order[1:]:
+                acc = np.float32(acc + partial(K, pos, i))
+            out[i] = acc
+    return out
+
+
+def check_hier(orc):
+    """2PH: one rank per node, small form = the plain definition (all-pairs
+    across nodes, ascending), large form = the 2PA all-pairs; one node = the
+    2PA all-pairs (the local reduce-scatter + all-gather); in between, the
+    node partials of the page's description; round counts per phase."""
+    rng = np.random.default_rng(64)
+    for p in (2, 4, 6, 8):
+        xs = [rng.standard_normal(29).astype(np.float32) for _ in range(p)]
+        ap = orc.allreduce(xs, "fp32", "sum", "allpairs")[0][0]
+        df = orc.definition(xs, "fp32", "sum")
+        ys, r = orc.allreduce(xs, "fp32", "sum", "hier", ranks_per_node=1)
+        assert r == 1 and all(y.tobytes() == df.tobytes() for y in ys), p
+        ys, r = orc.allreduce(xs, "fp32", "sum", "hier_large", ranks_per_node=1)
+        assert r == 2 and all(y.tobytes() == ap.tobytes() for y in ys), p
+        for algo in ("hier", "hier_large"):
+            ys, r = orc.allreduce(xs, "fp32", "sum", algo, ranks_per_node=p)
+            assert r == 2 and all(y.tobytes() == ap.tobytes() for y in ys), (p, algo)
+    for p, G in ((4, 2), (8, 2), (8, 4), (12, 3), (16, 4)):
+        xs = [rng.standard_normal(3 * p + 5).astype(np.float32) for _ in range(p)]
+        for algo, large, rounds in (("hier", False, 3), ("hier_large", True, 4)):
+            ys, r = orc.allreduce(xs, "fp32", "sum", algo, ranks_per_node=G)
+            assert r == rounds, (p, G, algo, r)
+            want = _hier_closed_form(xs, G, large)
+            for y in ys:
+                assert y.tobytes() == want.tobytes(), (p, G, algo)
+
+
+def check_topology_exact(orc):
+    """Exactly-once and the exact integer ops (Python integers) for every
+    topology schedule and several topologies, all ranks identical, in and
+    out of place; the sampled entry point agrees."""
+    rng = np.random.default_rng(65)
+    for algo, p, topo in (("tree", 8, dict(ranks_per_node=1)), ("tree", 12, dict(ranks_per_node=3)),
+                          ("tree", 7, dict(ranks_per_node=1)), ("rexch", 8, dict(radix=2)),
+                          ("rexch", 9, dict(radix=3)), ("hier", 8, dict(ranks_per_node=2)),
+                          ("hier", 12, dict(ranks_per_node=4)), ("hier_large", 8, dict(ranks_per_node=4)),
+                          ("hier_large", 6, dict(ranks_per_node=3))):
+        n = 5 * p + 3
+        xs = [np.full(n, 1 << q, dtype=np.int32) for q in range(p)]
+        for y in orc.allreduce(xs, "int32", "sum", algo, **topo)[0]:
+            assert (y == (1 << p) - 1).all(), (algo, p, topo)
+        xs = [rng.integers(-(2 ** 31), 2 ** 31 - 1, n, endpoint=True, dtype=np.int32) for _ in range(p)]
+        cols = [[int(x[i]) for x in xs] for i in range(n)]
+        want = {"sum": [_wrap32(sum(c)) for c in cols], "min": [min(c) for c in cols],
+                "max": [max(c) for c in cols],
+                "prod": [_wrap32(int(np.prod([Fraction(v) for v in c]))) for c in cols]}
+        for op, w in want.items():
+            ys, _ = orc.allreduce(xs, "int32", op, algo, **topo)
+            for y in ys:
+                assert y.tolist() == w, (algo, p, topo, op)
+            ys2, _ = orc.allreduce([x.copy() for x in xs], "int32", op, algo, inplace=True, **topo)
+            assert all(y.tolist() == w for y in ys2), (algo, p, topo, op, "inplace")
+        x32 = [rng.standard_normal(n).astype(np.float32) for _ in range(p)]
+        idx = rng.integers(0, n, 30).astype(np.int64)
+        for op in ("sum", "avg", "prod"):
+            ys, _ = orc.allreduce(x32, "fp32", op, algo, **topo)
+            for y in ys[1:]:
+                assert y.tobytes() == ys[0].tobytes(), (algo, op)
+            assert orc.allreduce_at(x32, "fp32", op, algo, idx, **topo).tobytes() == ys[0][idx].tobytes()
+
+
 ALL_CHECKS = [
     check_worked_example, check_step_counts, check_exactly_once, check_int_brute_force,
     check_fold_order_probes, check_identical_ranks, check_order_independent_fp,
     check_minmax_library, check_p2_sum, check_avg, check_16bit_single_rounding,
     check_error_bound_16bit, check_rs_ag, check_sampled,
+    check_tree_drawing, check_dtree_listing, check_tree_shapes, check_tree_chains, check_tree_rounds,
+    check_tree_association, check_tree_chain_closed_form, check_rexch, check_hier, check_topology_exact,
 ]

@@ -45,6 +45,28 @@ MUTANTS = {
     "f16_decode_subnormal_scale": ("float v = (float)m * u2f(0x33800000u);", "float v = (float)m * u2f(0x34000000u);"),
     "f16_exponent_bias": ("int e16 = (int)exp - 127 + 15;", "int e16 = (int)exp - 127 + 16;"),
     "sampled_ring_start": ("v = pre(&c, X[(ch + 1) % p], i);", "v = pre(&c, X[ch], i);"),
+    "tree_children_descending": ("for (int q = 0; q < c->p; q++)\n    if (q != r && T->parent[t][q] == r)",
+                                 "for (int q = c->p - 1; q >= 0; q--)\n    if (q != r && T->parent[t][q] == r)"),
+    "tree_children_before_own": ("acc_t v = pre(c, X[r], i);\n  for (int q = 0; q < c->p; q++)\n    if (q != r && T->parent[t][q] == r) v = combine(c, v, subtree(c, T, X, t, q, i));\n  return v;",
+                                 "acc_t v = pre(c, X[r], i);\n  int first = 1; acc_t w = v;\n  for (int q = 0; q < c->p; q++)\n    if (q != r && T->parent[t][q] == r) { w = first ? subtree(c, T, X, t, q, i) : combine(c, w, subtree(c, T, X, t, q, i)); first = 0; }\n  return first ? v : combine(c, w, v);"),
+    "tree_no_range_fallback": ("if (up >= n) up = x & ~b;", "if (up >= n) up = 0;"),
+    "tree_mirror_as_shift": ("if (n % 2 == 0) {\n    int q = bittree_parent(n, n - 1 - x);",
+                             "if (n % 2 == 2) {\n    int q = bittree_parent(n, n - 1 - x);"),
+    "tree_chain_reversed": ("if (r % G != 0) { T->parent[t][r] = r - 1; continue; }",
+                            "if (r % G != G - 1) { T->parent[t][r] = r + 1; continue; }"),
+    "tree_one_tree_only": ("return subtree(c, T, X, ch, root, i);", "return subtree(c, T, X, 0, 0, i);"),
+    "rexch_high_digit_first": ("for (int stride = 1; stride < p; stride *= T->k) {",
+                               "for (int stride = p / T->k; stride >= 1; stride /= T->k) {"),
+    "rexch_group_descending": ("acc_t a = v[first];\n          for (int m = 1; m < T->k; m++) a = combine(c, a, v[first + m * stride]);",
+                               "acc_t a = v[first + (T->k - 1) * stride];\n          for (int m = T->k - 2; m >= 0; m--) a = combine(c, a, v[first + m * stride]);"),
+    "hier_nodes_descending": ("acc_t a = node_partial(c, T->G, X, 0, ch, i);\n      for (int K = 1; K < p / T->G; K++)",
+                              "acc_t a = node_partial(c, T->G, X, p / T->G - 1, ch, i);\n      for (int K = p / T->G - 2; K >= 0; K--)"),
+    "hier_node_partial_from_node_start": ("acc_t v = pre(c, X[K * G + pos], i);\n  for (int j = 0; j < G; j++)\n    if (j != pos)",
+                                          "acc_t v = pre(c, X[K * G], i);\n  for (int j = 0; j < G; j++)\n    if (j != 0)"),
+    "hier_large_owner_not_first": ("acc_t a = node_partial(c, T->G, X, K0, pos, i);\n      for (int K = 0; K < p / T->G; K++)\n        if (K != K0)",
+                                   "acc_t a = node_partial(c, T->G, X, 0, pos, i);\n      for (int K = 0; K < p / T->G; K++)\n        if (K != 0)"),
+    "hier_rounds_no_local_ag": ("return (T->algo == OR_HIER) ? 2 * local + cross : 2 * local + 2 * cross;",
+                                "return (T->algo == OR_HIER) ? local + cross : 2 * local + 2 * cross;"),
     "rs_direct_offset": ("allpairs_fold_chunk(&c, X, Y[j], n, j, chunk_lo(n, p, j));",
                          "allpairs_fold_chunk(&c, X, Y[j], n, (j + 1) % p, chunk_lo(n, p, (j + 1) % p));"),
 }
