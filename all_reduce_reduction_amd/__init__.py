@@ -33,10 +33,14 @@ STATUS = {0: "SIM_OK", -1: "SIM_ERR_INVALID_ARG", -2: "SIM_ERR_UNSUPPORTED", -3:
 STATUS_CODE = {v: k for k, v in STATUS.items()}
 DTYPES = {"int32": 0, "fp32": 1, "fp16": 2, "bf16": 3}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
-ALGOS = {"auto": 0, "ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4, "ring_fifo": 5}
+ALGOS = {"auto": 0, "ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4, "ring_fifo": 5,
+         "tree": 6, "rexch": 7, "hier": 8, "hier_large": 9}
+TOPOLOGY_ALGOS = ("tree", "rexch", "hier", "hier_large")
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 ESIZE = {"int32": 4, "fp32": 4, "fp16": 2, "bf16": 2}
-XFER_KINDS = {0: "REDUCE", 1: "REDUCE_POST", 2: "COPY", 3: "GATHER_REDUCE", 4: "FANOUT", 5: "ONESHOT"}
+XFER_KINDS = {0: "REDUCE", 1: "REDUCE_POST", 2: "COPY", 3: "GATHER_REDUCE", 4: "FANOUT", 5: "ONESHOT",
+              6: "GATHER", 7: "GATHER_POST", 8: "EXCH", 9: "EXCH_POST", 10: "MCAST"}
+CONFIG = {"ranks_per_node": 0, "radix": 1}
 DEBUG = {"epoch": 0, "spin_limit": 1, "ll_wait_skew": 2, "fill_ll": 3, "log": 4, "workgroups": 5,
          "unroll": 6, "fifo_channels": 7, "fifo_slots": 8, "fifo_withhold": 9}
 MAX_RANKS = 16
@@ -69,11 +73,14 @@ def _load() -> ctypes.CDLL:
         "sim_model_set": ([i, d, d, d, d], i),
         "sim_model_reset": ([], i),
         "sim_check_error": ([vp], i),
-        "sim_schedule_info": ([i, i, ctypes.POINTER(i), ctypes.POINTER(i)], i),
+        "sim_config_set": ([i, i], i),
+        "sim_config_get": ([i, ctypes.POINTER(i)], i),
+        "sim_tree_info": ([i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)], i),
+        "sim_schedule_info": ([i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)], i),
         "sim_schedule_xfers": ([i, i, i, ctypes.POINTER(i), i, ctypes.POINTER(i)], i),
         "sim_schedule_state": ([i, i, i, ctypes.POINTER(ctypes.c_uint32)], i),
         "sim_verify_schedule": ([i, i, ctypes.c_char_p, sz], i),
-        "sim_verify_custom": ([i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.c_char_p, sz], i),
+        "sim_verify_custom": ([i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.c_char_p, sz], i),
         "sim_debug_set": ([i, ctypes.c_uint64], i),
         "sim_debug_get": ([i, ctypes.POINTER(ctypes.c_uint64)], i),
         "sim_status_string": ([i], ctypes.c_char_p),
@@ -187,39 +194,69 @@ def sim_check_error(stream=0) -> int:
     return lib.sim_check_error(stream or None)
 
 
+def sim_config_set(key, value: int) -> None:
+    _check(lib.sim_config_set(_code(CONFIG, key, "config key"), int(value)), "sim_config_set")
+
+
+def sim_config_get(key) -> int:
+    v = ctypes.c_int(0)
+    _check(lib.sim_config_get(_code(CONFIG, key, "config key"), ctypes.byref(v)), "sim_config_get")
+    return v.value
+
+
+def sim_tree_info(tree: int, p: int, ranks_per_node: int, rank: int):
+    """(parent, [children ascending]) of `rank` in tree 0 or 1."""
+    par, nch = ctypes.c_int(0), ctypes.c_int(0)
+    ch = (ctypes.c_int * 3)()
+    _check(lib.sim_tree_info(tree, p, ranks_per_node, rank, ctypes.byref(par), ch, ctypes.byref(nch)),
+           "sim_tree_info")
+    return par.value, list(ch[:nch.value])
+
+
 def sim_schedule_info(algo, p: int):
-    ns, nx = ctypes.c_int(0), ctypes.c_int(0)
-    _check(lib.sim_schedule_info(_code(ALGOS, algo, "algo"), p, ctypes.byref(ns), ctypes.byref(nx)),
-           "sim_schedule_info")
-    return ns.value, nx.value
+    """(steps, transfers, chunks) of the lowered all-reduce schedule."""
+    ns, nx, nc = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    _check(lib.sim_schedule_info(_code(ALGOS, algo, "algo"), p, ctypes.byref(ns), ctypes.byref(nx),
+                                 ctypes.byref(nc)), "sim_schedule_info")
+    return ns.value, nx.value, nc.value
 
 
 def sim_schedule_xfers(algo, p: int, step: int):
-    buf = (ctypes.c_int * (4 * 64))()
+    """The step's transfers as (kind, src, dst, chunk, rank set) tuples."""
+    cap = 512
+    buf = (ctypes.c_int * (5 * cap))()
     cnt = ctypes.c_int(0)
-    _check(lib.sim_schedule_xfers(_code(ALGOS, algo, "algo"), p, step, buf, 64, ctypes.byref(cnt)),
+    _check(lib.sim_schedule_xfers(_code(ALGOS, algo, "algo"), p, step, buf, cap, ctypes.byref(cnt)),
            "sim_schedule_xfers")
-    return [tuple(buf[4 * k:4 * k + 4]) for k in range(cnt.value)]
+    return [tuple(buf[5 * k:5 * k + 5]) for k in range(cnt.value)]
 
 
 def sim_schedule_state(algo, p: int, after_steps: int):
-    m = (ctypes.c_uint32 * (p * p))()
+    """masks[r][c] after `after_steps` steps."""
+    nch = sim_schedule_info(algo, p)[2]
+    m = (ctypes.c_uint32 * (p * nch))()
     _check(lib.sim_schedule_state(_code(ALGOS, algo, "algo"), p, after_steps, m), "sim_schedule_state")
-    return [[m[r * p + c] for c in range(p)] for r in range(p)]
+    return [[m[r * nch + c] for c in range(nch)] for r in range(p)]
 
 
 def sim_verify_schedule(algo, p: int):
-    buf = ctypes.create_string_buffer(512)
-    st = lib.sim_verify_schedule(_code(ALGOS, algo, "algo"), p, buf, 512)
+    buf = ctypes.create_string_buffer(1024)
+    st = lib.sim_verify_schedule(_code(ALGOS, algo, "algo"), p, buf, 1024)
     return st, buf.value.decode()
 
 
-def sim_verify_custom(algo, p: int, steps: List[List[tuple]]):
+def sim_verify_custom(algo, p: int, steps: List[List[tuple]], nchunks: Optional[int] = None,
+                      rounds: Optional[int] = None):
+    """Check a caller-made all-reduce schedule.  Transfers are 5-tuples
+    (kind, src, dst, chunk, rank set); 4-tuples get an empty rank set.
+    nchunks defaults to p, rounds to the number of steps."""
+    steps = [[tuple(x) + (0,) * (5 - len(x)) for x in s] for s in steps]
     counts = (ctypes.c_int * max(1, len(steps)))(*[len(s) for s in steps])
     flat = [v for s in steps for x in s for v in x]
     xf = (ctypes.c_int * max(1, len(flat)))(*flat)
-    buf = ctypes.create_string_buffer(512)
-    st = lib.sim_verify_custom(_code(ALGOS, algo, "algo"), p, len(steps), counts, xf, buf, 512)
+    buf = ctypes.create_string_buffer(1024)
+    st = lib.sim_verify_custom(_code(ALGOS, algo, "algo"), p, p if nchunks is None else nchunks,
+                               len(steps) if rounds is None else rounds, len(steps), counts, xf, buf, 1024)
     return st, buf.value.decode()
 
 

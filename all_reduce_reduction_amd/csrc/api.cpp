@@ -64,9 +64,16 @@ Ctx g;
 
 int esize_of(int dtype) { return (dtype == SIM_FP16 || dtype == SIM_BF16) ? 2 : 4; }
 const char* algo_name(int a) {
-  static const char* n[] = {"auto", "ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"};
-  return (a >= 0 && a < 6) ? n[a] : "?";
+  static const char* n[] = {"auto",      "ring", "allpairs", "oneshot", "oneshot_ll",
+                            "ring_fifo", "tree", "rexch",    "hier",    "hier_large"};
+  return (a >= 0 && a < SIM_NUM_ALGOS) ? n[a] : "?";
 }
+constexpr int kLastAlgo = SIM_NUM_ALGOS - 1;
+bool is_topology_algo(int a) { return a >= SIM_ALGO_TREE && a <= SIM_ALGO_HIER_LARGE; }
+
+// The simulated topology of the tree / recursive-exchange / 2PH schedules:
+// process-wide, kept across sim_init.
+Topology g_topo;
 
 int64_t chunk_lo(int64_t n, int p, int c) { return (int64_t)(((__int128)c * n) / p); }
 
@@ -341,10 +348,129 @@ int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
   return hip_err(launch_ring_fifo(c.dtype, c.op, a, c.s));
 }
 
+// Tree, recursive exchange and 2PH: every lowered step runs as fold
+// launches (GATHER / EXCH transfers, the members of an exchange group
+// sharing one transfer) and copy launches (MCAST).  Within a step no
+// transfer touches a slot another one writes (the verifier proves it), so
+// the step's transfers may run in any order and in one launch.  A rank's
+// value of a chunk lives in its input until a fold replaces it with a
+// partial, and in its output once finished.  Partials are accumulator-typed:
+// 32-bit types keep them in the rank's own output buffer (the slot is only
+// read by later steps, never by one that still needs the input there);
+// fp16/bf16 keep fp32 partials in library scratch.
+int run_sched(const Call& c, const Schedule& sch) {
+  const int p = c.p, e = esize_of(c.dtype), V = 16 / e;
+  const int nch = sch.nchunks;
+  std::vector<int64_t> lo(nch + 1);
+  for (int q = 0; q <= nch; q++) lo[q] = chunk_lo((int64_t)c.n, nch, q);
+  void* part[SIM_MAX_RANKS] = {};
+  if (e == 4) {
+    for (int r = 0; r < p; r++) part[r] = c.y[r];
+  } else {
+    const size_t stride = (c.n + 63) / 64 * 64;  // fp32 elements per rank, 256-byte aligned slots
+    int rc = ensure_scratch((size_t)p * stride * 4);
+    if (rc) return rc;
+    for (int r = 0; r < p; r++) part[r] = (char*)g.scratch + (size_t)r * stride * 4;
+  }
+  enum { IN = 0, PART = 1, OUT = 2 };
+  std::vector<uint8_t> loc((size_t)p * nch, IN);
+  auto where = [&](int r, int ch) -> uint8_t& { return loc[(size_t)r * nch + ch]; };
+  for (const auto& step : sch.steps) {
+    std::vector<SchedXfer> folds;
+    std::vector<std::pair<int, uint32_t>> group_key;  // (chunk, set) of exchange folds; -1 chunk otherwise
+    std::vector<CopyXfer> copies;
+    std::vector<std::pair<int, uint8_t>> moves;  // (slot index, new location), applied after the step
+    for (const Xfer& xf : step) {
+      const bool gather = (xf.kind == XK_GATHER || xf.kind == XK_GATHER_POST);
+      const bool exch = (xf.kind == XK_EXCH || xf.kind == XK_EXCH_POST);
+      if (gather || exch) {
+        const bool fin = (xf.kind == XK_GATHER_POST || xf.kind == XK_EXCH_POST);
+        moves.push_back({xf.dst * nch + xf.chunk, fin ? (uint8_t)OUT : (uint8_t)PART});
+        if (exch) {
+          bool merged = false;
+          for (size_t k = 0; k < folds.size(); k++)
+            if (group_key[k] == std::make_pair(xf.chunk, xf.mask)) {
+              folds[k].dmask |= 1u << xf.dst;
+              merged = true;
+            }
+          if (merged) continue;
+        }
+        SchedXfer f;
+        std::memset(&f, 0, sizeof f);
+        f.lo = lo[xf.chunk];
+        f.hi = lo[xf.chunk + 1];
+        f.dmask = 1u << xf.dst;
+        f.final_ = fin ? 1 : 0;
+        auto add = [&](int q) {
+          const uint8_t w = where(q, xf.chunk);
+          if (w == OUT) return false;  // finished values are never folded again
+          f.order |= (uint64_t)q << (4 * f.nsrc);
+          if (w == PART) f.from_part |= 1u << f.nsrc;
+          f.nsrc++;
+          return true;
+        };
+        if (gather && !add(xf.dst)) return SIM_ERR_VERIFY;
+        for (int q = 0; q < p; q++)
+          if ((xf.mask >> q) & 1u)
+            if (!add(q)) return SIM_ERR_VERIFY;
+        folds.push_back(f);
+        group_key.push_back(exch ? std::make_pair(xf.chunk, xf.mask) : std::make_pair(-1, 0u));
+      } else if (xf.kind == XK_MCAST) {
+        if (where(xf.src, xf.chunk) != OUT) return SIM_ERR_VERIFY;
+        CopyXfer x;
+        std::memset(&x, 0, sizeof x);
+        x.src = c.y[xf.src];
+        for (int q = 0; q < p; q++)
+          if ((xf.mask >> q) & 1u) {
+            x.dst[x.ndst++] = c.y[q];
+            moves.push_back({q * nch + xf.chunk, (uint8_t)OUT});
+          }
+        x.lo = lo[xf.chunk];
+        x.hi = lo[xf.chunk + 1];
+        if (x.hi > x.lo) copies.push_back(x);
+      } else {
+        return SIM_ERR_VERIFY;  // not a kind this executor runs
+      }
+    }
+    // launch the folds, at most kSchedMaxXfers per launch (empty chunks skipped)
+    folds.erase(std::remove_if(folds.begin(), folds.end(), [](const SchedXfer& f) { return f.hi <= f.lo; }),
+                folds.end());
+    for (size_t b = 0; b < folds.size(); b += kSchedMaxXfers) {
+      SchedArgs a;
+      std::memset(&a, 0, sizeof a);
+      for (int r = 0; r < p; r++) {
+        a.x[r] = c.x[r];
+        a.y[r] = c.y[r];
+        a.part[r] = part[r];
+      }
+      a.p = p;
+      a.inv_p = inv_p_of(p);
+      a.nx = (int)std::min<size_t>(kSchedMaxXfers, folds.size() - b);
+      int64_t maxlen = 0;
+      for (int k = 0; k < a.nx; k++) {
+        a.xf[k] = folds[b + k];
+        maxlen = std::max(maxlen, a.xf[k].hi - a.xf[k].lo);
+      }
+      a.tiles = tiles_for((maxlen + V - 1) / V, a.nx, 1);
+      int rc = hip_err(launch_sched_fold(c.dtype, c.op, a, c.s));
+      if (rc) return rc;
+    }
+    for (size_t b = 0; b < copies.size(); b += SIM_MAX_RANKS) {
+      std::vector<CopyXfer> part_of(copies.begin() + b,
+                                    copies.begin() + std::min(copies.size(), b + SIM_MAX_RANKS));
+      int rc = run_copy_step(c, part_of);
+      if (rc) return rc;
+    }
+    for (auto& m : moves) loc[(size_t)m.first] = m.second;
+  }
+  return SIM_OK;
+}
+
 int run_allreduce(const Call& c) {
   std::string diag;
-  const Schedule* sch = cached_schedule(COLL_ALLREDUCE, c.algo, c.p, &diag);
+  const Schedule* sch = cached_schedule(COLL_ALLREDUCE, c.algo, c.p, g_topo, &diag);
   if (!sch) return SIM_ERR_VERIFY;
+  if (is_topology_algo(c.algo)) return run_sched(c, *sch);
   const int p = c.p;
   std::vector<int64_t> lo(p + 1);
   for (int q = 0; q <= p; q++) lo[q] = chunk_lo((int64_t)c.n, p, q);
@@ -429,7 +555,7 @@ int run_allreduce(const Call& c) {
 
 int run_reduce_scatter(const Call& c) {
   std::string diag;
-  const Schedule* sch = cached_schedule(COLL_REDUCE_SCATTER, c.algo, c.p, &diag);
+  const Schedule* sch = cached_schedule(COLL_REDUCE_SCATTER, c.algo, c.p, g_topo, &diag);
   if (!sch) return SIM_ERR_VERIFY;
   const int p = c.p;
   std::vector<int64_t> lo(p + 1);
@@ -444,7 +570,7 @@ int run_reduce_scatter(const Call& c) {
 
 int run_all_gather(const Call& c) {
   std::string diag;
-  const Schedule* sch = cached_schedule(COLL_ALL_GATHER, c.algo, c.p, &diag);
+  const Schedule* sch = cached_schedule(COLL_ALL_GATHER, c.algo, c.p, g_topo, &diag);
   if (!sch) return SIM_ERR_VERIFY;
   const int p = c.p;
   const int64_t nin = (int64_t)c.n / p;
@@ -497,10 +623,10 @@ int run_all_gather(const Call& c) {
 
 // legal candidates for AUTO / explicit requests
 bool legal(int coll, int algo, int p, size_t n, int dtype) {
-  (void)p;
   if (coll == COLL_ALLREDUCE) {
     if (algo == SIM_ALGO_ONESHOT_LL) return n * (size_t)esize_of(dtype) <= SIM_LL_MAX_BYTES_PER_RANK;
-    return algo >= SIM_ALGO_RING && algo <= SIM_ALGO_RING_FIFO;
+    if (is_topology_algo(algo)) return cached_schedule(coll, algo, p, g_topo, nullptr) != nullptr;
+    return algo >= SIM_ALGO_RING && algo <= kLastAlgo;
   }
   return algo == SIM_ALGO_RING || algo == SIM_ALGO_ALLPAIRS;
 }
@@ -508,9 +634,11 @@ bool legal(int coll, int algo, int p, size_t n, int dtype) {
 int pick(int coll, int p, size_t n, int dtype, int* algo, double* us) {
   int best = -1;
   double bt = 0;
+  // AUTO weighs the single-node schedules; the tree, recursive-exchange and
+  // 2PH schedules model multi-node topologies and run when asked for by name
   for (int a = SIM_ALGO_RING; a <= SIM_ALGO_RING_FIFO; a++) {
     if (!legal(coll, a, p, n, dtype)) continue;
-    const double t = model_predict(g.model, coll, a, p, (double)n, esize_of(dtype));
+    const double t = model_predict(g.model, coll, a, p, (double)n, esize_of(dtype), g_topo);
     if (best < 0 || t < bt) {
       best = a;
       bt = t;
@@ -523,11 +651,11 @@ int pick(int coll, int p, size_t n, int dtype, int* algo, double* us) {
 }
 
 int resolve_algo(int coll, int p, size_t n, int dtype, int* algo, double* us) {
-  if (*algo < SIM_ALGO_AUTO || *algo > SIM_ALGO_RING_FIFO) return SIM_ERR_INVALID_ARG;
+  if (*algo < SIM_ALGO_AUTO || *algo > kLastAlgo) return SIM_ERR_INVALID_ARG;
   if (*algo == SIM_ALGO_AUTO && coll == COLL_ALLREDUCE && g.env_algo > 0) *algo = g.env_algo;
   if (*algo == SIM_ALGO_AUTO) return pick(coll, p, n, dtype, algo, us);
   if (!legal(coll, *algo, p, n, dtype)) return SIM_ERR_UNSUPPORTED;
-  if (us) *us = model_predict(g.model, coll, *algo, p, (double)n, esize_of(dtype));
+  if (us) *us = model_predict(g.model, coll, *algo, p, (double)n, esize_of(dtype), g_topo);
   return SIM_OK;
 }
 
@@ -535,12 +663,12 @@ void log_call(const char* what, const Call& c, double us) {
   if (!g.log) return;
   std::fprintf(stderr, "[simar] %s: %zu bytes/rank p %d -> algo %s steps %d predicted %.2f us\n", what,
                c.n * (size_t)esize_of(c.dtype), c.p, algo_name(c.algo),
-               model_launches(c.coll, c.algo, c.p), us);
+               model_launches(c.coll, c.algo, c.p, g_topo), us);
 }
 
 int parse_algo_env(const char* v) {
   if (!v) return 0;
-  for (int a = 1; a <= SIM_ALGO_RING_FIFO; a++)
+  for (int a = 1; a <= kLastAlgo; a++)
     if (!std::strcmp(v, algo_name(a))) return a;
   return 0;
 }
@@ -648,7 +776,7 @@ int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size
                   int op, int algo, void* stream) {
   int rc = check_scalars(p, dtype, op, true);
   if (rc) return rc;
-  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_RING_FIFO) return SIM_ERR_INVALID_ARG;
+  if (algo < SIM_ALGO_AUTO || algo > kLastAlgo) return SIM_ERR_INVALID_ARG;
   if (n == 0) return SIM_OK;
   const size_t e = (size_t)esize_of(dtype);
   if (n > ((size_t)1 << 46) / e) return SIM_ERR_INVALID_ARG;
@@ -671,7 +799,7 @@ int sim_reduce_scatter(const void* const* in_ptrs, void* const* out_ptrs, int p,
                        int dtype, int op, int algo, void* stream) {
   int rc = check_scalars(p, dtype, op, true);
   if (rc) return rc;
-  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_RING_FIFO) return SIM_ERR_INVALID_ARG;
+  if (algo < SIM_ALGO_AUTO || algo > kLastAlgo) return SIM_ERR_INVALID_ARG;
   if (n_out == 0) return SIM_OK;
   const size_t e = (size_t)esize_of(dtype);
   if (n_out > ((size_t)1 << 46) / e / (size_t)p) return SIM_ERR_INVALID_ARG;
@@ -712,7 +840,7 @@ int sim_reduce_scatter(const void* const* in_ptrs, void* const* out_ptrs, int p,
   rc = run_reduce_scatter(c);
   if (rc) return rc;
   g.last_algo = algo;
-  log_call("ReduceScatter", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e));
+  log_call("ReduceScatter", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e, g_topo));
   return SIM_OK;
 }
 
@@ -720,7 +848,7 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p, siz
                    int algo, void* stream) {
   int rc = check_scalars(p, dtype, SIM_SUM, false);
   if (rc) return rc;
-  if (algo < SIM_ALGO_AUTO || algo > SIM_ALGO_RING_FIFO) return SIM_ERR_INVALID_ARG;
+  if (algo < SIM_ALGO_AUTO || algo > kLastAlgo) return SIM_ERR_INVALID_ARG;
   if (n_in == 0) return SIM_OK;
   const size_t e = (size_t)esize_of(dtype);
   if (n_in > ((size_t)1 << 46) / e / (size_t)p) return SIM_ERR_INVALID_ARG;
@@ -759,7 +887,7 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p, siz
   rc = run_all_gather(c);
   if (rc) return rc;
   g.last_algo = algo;
-  log_call("AllGather", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e));
+  log_call("AllGather", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e, g_topo));
   return SIM_OK;
 }
 
@@ -789,16 +917,18 @@ int sim_model_load(const char* json_path) {
 }
 
 int sim_model_predict(int algo, int p, int dtype, double bytes_per_rank, double* us_out) {
-  if (!us_out || algo < SIM_ALGO_RING || algo > SIM_ALGO_RING_FIFO || p < 2 || p > SIM_MAX_RANKS ||
+  if (!us_out || algo < SIM_ALGO_RING || algo > kLastAlgo || p < 2 || p > SIM_MAX_RANKS ||
       dtype < SIM_INT32 || dtype > SIM_BF16 || !(bytes_per_rank >= 0))
     return SIM_ERR_INVALID_ARG;
+  if (is_topology_algo(algo) && !cached_schedule(COLL_ALLREDUCE, algo, p, g_topo, nullptr))
+    return SIM_ERR_UNSUPPORTED;
   const int e = esize_of(dtype);
-  *us_out = model_predict(g.model, COLL_ALLREDUCE, algo, p, bytes_per_rank / e, e);
+  *us_out = model_predict(g.model, COLL_ALLREDUCE, algo, p, bytes_per_rank / e, e, g_topo);
   return SIM_OK;
 }
 
 int sim_model_set(int algo, double alpha_us, double steps, double bytes_factor, double gbps) {
-  if (algo < SIM_ALGO_RING || algo > SIM_ALGO_RING_FIFO || !(gbps > 0) || !(alpha_us >= 0))
+  if (algo < SIM_ALGO_RING || algo > kLastAlgo || !(gbps > 0) || !(alpha_us >= 0))
     return SIM_ERR_INVALID_ARG;
   AlgoModel& m = g.model.a[algo];
   m.alpha_us = alpha_us;
@@ -827,26 +957,69 @@ int sim_check_error(void* stream) {
   return SIM_OK;
 }
 
-int sim_schedule_info(int algo, int p, int* nsteps, int* nxfers) {
+int sim_config_set(int key, int value) {
+  switch (key) {
+    case SIM_CONFIG_RANKS_PER_NODE:
+      if (value < 1 || value > SIM_MAX_RANKS) return SIM_ERR_INVALID_ARG;
+      g_topo.ranks_per_node = value;
+      return SIM_OK;
+    case SIM_CONFIG_RADIX:
+      if (value < 2 || value > SIM_MAX_RANKS) return SIM_ERR_INVALID_ARG;
+      g_topo.radix = value;
+      return SIM_OK;
+  }
+  return SIM_ERR_INVALID_ARG;
+}
+
+int sim_config_get(int key, int* value) {
+  if (!value) return SIM_ERR_INVALID_ARG;
+  switch (key) {
+    case SIM_CONFIG_RANKS_PER_NODE: *value = g_topo.ranks_per_node; return SIM_OK;
+    case SIM_CONFIG_RADIX: *value = g_topo.radix; return SIM_OK;
+  }
+  return SIM_ERR_INVALID_ARG;
+}
+
+int sim_tree_info(int tree, int p, int ranks_per_node, int rank, int* parent, int* children, int* nchildren) {
+  if (tree < 0 || tree > 1 || p < 2 || p > SIM_MAX_RANKS || ranks_per_node < 1 || p % ranks_per_node != 0 ||
+      rank < 0 || rank >= p || !parent || !children || !nchildren)
+    return SIM_ERR_INVALID_ARG;
+  *parent = rank_tree_parent(tree, p, ranks_per_node, rank);
+  *nchildren = rank_tree_children(tree, p, ranks_per_node, rank, children);
+  return SIM_OK;
+}
+
+// lowered (not cached) schedule of the current topology; SIM_ERR_UNSUPPORTED
+// when (algo, p, topology) has none
+static int lower_current(int algo, int p, Schedule* s) {
+  if (p < 2 || p > SIM_MAX_RANKS || algo < SIM_ALGO_RING || algo > kLastAlgo) return SIM_ERR_INVALID_ARG;
+  return lower(COLL_ALLREDUCE, algo, p, g_topo, s) ? SIM_OK : SIM_ERR_UNSUPPORTED;
+}
+
+int sim_schedule_info(int algo, int p, int* nsteps, int* nxfers, int* nchunks) {
   Schedule s;
-  if (!lower(COLL_ALLREDUCE, algo, p, &s)) return SIM_ERR_INVALID_ARG;
+  int rc = lower_current(algo, p, &s);
+  if (rc) return rc;
   if (nsteps) *nsteps = (int)s.steps.size();
   if (nxfers) *nxfers = s.nxfers();
+  if (nchunks) *nchunks = s.nchunks;
   return SIM_OK;
 }
 
 int sim_schedule_xfers(int algo, int p, int step, int* out, int max, int* count) {
   Schedule s;
-  if (!lower(COLL_ALLREDUCE, algo, p, &s) || step < 0 || step >= (int)s.steps.size() || !count)
-    return SIM_ERR_INVALID_ARG;
+  int rc = lower_current(algo, p, &s);
+  if (rc) return rc;
+  if (step < 0 || step >= (int)s.steps.size() || !count) return SIM_ERR_INVALID_ARG;
   int k = 0;
   for (const Xfer& x : s.steps[step]) {
     if (k >= max) break;
     if (out) {
-      out[4 * k + 0] = x.kind;
-      out[4 * k + 1] = x.src;
-      out[4 * k + 2] = x.dst;
-      out[4 * k + 3] = x.chunk;
+      out[5 * k + 0] = x.kind;
+      out[5 * k + 1] = x.src;
+      out[5 * k + 2] = x.dst;
+      out[5 * k + 3] = x.chunk;
+      out[5 * k + 4] = (int)x.mask;
     }
     k++;
   }
@@ -856,7 +1029,9 @@ int sim_schedule_xfers(int algo, int p, int step, int* out, int max, int* count)
 
 int sim_schedule_state(int algo, int p, int after_steps, uint32_t* masks) {
   Schedule s;
-  if (!masks || !lower(COLL_ALLREDUCE, algo, p, &s)) return SIM_ERR_INVALID_ARG;
+  if (!masks) return SIM_ERR_INVALID_ARG;
+  int rc = lower_current(algo, p, &s);
+  if (rc) return rc;
   std::string d;
   return symbolic_state(s, after_steps, masks, &d) ? SIM_OK : SIM_ERR_INVALID_ARG;
 }
@@ -868,9 +1043,10 @@ static void put_diag(const std::string& d, char* diag, size_t len) {
 
 int sim_verify_schedule(int algo, int p, char* diag, size_t diag_len) {
   Schedule s;
-  if (!lower(COLL_ALLREDUCE, algo, p, &s)) {
-    put_diag("no lowering for this (algo, p)", diag, diag_len);
-    return SIM_ERR_INVALID_ARG;
+  int rc = lower_current(algo, p, &s);
+  if (rc) {
+    put_diag("no lowering for this (algo, p, topology)", diag, diag_len);
+    return rc;
   }
   std::string d;
   const bool ok = verify(s, &d);
@@ -878,22 +1054,33 @@ int sim_verify_schedule(int algo, int p, char* diag, size_t diag_len) {
   return ok ? SIM_OK : SIM_ERR_VERIFY;
 }
 
-int sim_verify_custom(int algo, int p, int nsteps, const int* counts, const int* xfers, char* diag,
-                      size_t diag_len) {
+int sim_verify_custom(int algo, int p, int nchunks, int rounds, int nsteps, const int* counts,
+                      const int* xfers, char* diag, size_t diag_len) {
   if (p < 2 || p > SIM_MAX_RANKS || nsteps < 0 || (nsteps > 0 && (!counts || !xfers)) ||
-      algo < SIM_ALGO_RING || algo > SIM_ALGO_RING_FIFO)
+      algo < SIM_ALGO_RING || algo > kLastAlgo || nchunks < 1 || nchunks > p)
     return SIM_ERR_INVALID_ARG;
   Schedule s;
   s.algo = algo;
   s.p = p;
   s.coll = COLL_ALLREDUCE;
-  s.rounds = (algo == SIM_ALGO_RING) ? nsteps : 2;
+  s.nchunks = nchunks;
+  s.rounds = rounds;
+  if (is_topology_algo(algo)) {
+    if (algo == SIM_ALGO_REXCH) s.topo.radix = g_topo.radix;
+    else s.topo.ranks_per_node = g_topo.ranks_per_node;
+  }
   int k = 0;
   for (int st = 0; st < nsteps; st++) {
     if (counts[st] < 0) return SIM_ERR_INVALID_ARG;
     std::vector<Xfer> v;
-    for (int j = 0; j < counts[st]; j++, k++)
-      v.push_back({xfers[4 * k], xfers[4 * k + 1], xfers[4 * k + 2], xfers[4 * k + 3]});
+    for (int j = 0; j < counts[st]; j++, k++) {
+      const int* w = xfers + 5 * (size_t)k;
+      if (w[0] < 0 || w[0] >= kNumXferKinds) {
+        put_diag("unknown transfer kind", diag, diag_len);
+        return SIM_ERR_VERIFY;
+      }
+      v.push_back({w[0], w[1], w[2], w[3], (uint32_t)w[4]});
+    }
     s.steps.push_back(v);
   }
   std::string d;

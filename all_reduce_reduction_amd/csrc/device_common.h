@@ -155,6 +155,34 @@ __device__ __forceinline__ u32x4 pack(const typename Ty<DT>::A* in) {
   return v;
 }
 
+// accumulator-typed partials: V values at element index i0 (vector aligned)
+template <int DT>
+__device__ __forceinline__ void load_part(const void* base, int64_t idx, typename Ty<DT>::A* out) {
+  constexpr int V = epv<DT>();
+#pragma unroll
+  for (int h = 0; h < V / 4; h++) {
+    const u32x4 w = ld16(base, (idx + 4 * h) * 4);
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      // copy the lane out first: a bit cast applied directly to a vector
+      // subscript reads element 0 with this compiler
+      const uint32_t bits = w[k];
+      out[4 * h + k] = __builtin_bit_cast(typename Ty<DT>::A, bits);
+    }
+  }
+}
+template <int DT>
+__device__ __forceinline__ void store_part(void* base, int64_t idx, const typename Ty<DT>::A* in) {
+  constexpr int V = epv<DT>();
+#pragma unroll
+  for (int h = 0; h < V / 4; h++) {
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; k++) w[k] = __builtin_bit_cast(uint32_t, in[4 * h + k]);
+    st16(base, (idx + 4 * h) * 4, w);
+  }
+}
+
 // Scalar element access (ragged heads and tails).
 template <int DT>
 __device__ __forceinline__ typename Ty<DT>::A load_elem(const void* base, int64_t i) {

@@ -112,7 +112,33 @@ struct RingFifoArgs {
   int withhold;                // test hook: rank 0 leaves at once, its partners' waits expire
 };
 
+// One step of the tree, recursive-exchange and 2PH schedules: a set of
+// folds, each over one chunk.  A fold's operands are ranks' current values
+// in fold order -- an input (widened, avg-scaled as it is read) or an
+// accumulator-typed partial -- and its result goes to every rank in
+// `dmask`: post-processed and narrowed into the outputs, or as a partial.
+constexpr int kSchedMaxXfers = 32;
+struct SchedXfer {
+  int64_t lo, hi;      // element range (a chunk)
+  uint64_t order;      // operand ranks in fold order, 4 bits each
+  uint32_t from_part;  // bit k: operand k is a partial
+  uint32_t dmask;      // ranks that receive the result
+  int nsrc;            // operands, 1..SIM_MAX_RANKS
+  int final_;          // 1: post-processed output; 0: partial
+};
+struct SchedArgs {
+  const void* x[SIM_MAX_RANKS];
+  void* y[SIM_MAX_RANKS];
+  void* part[SIM_MAX_RANKS];  // accumulator-typed partials, absolute element index, 16-byte aligned
+  SchedXfer xf[kSchedMaxXfers];
+  int nx;
+  int p;
+  int tiles;                  // workgroups per fold (gridDim.x = tiles * nx)
+  float inv_p;
+};
+
 static_assert(sizeof(FoldArgs) <= 4096, "kernel argument segment too large");
+static_assert(sizeof(SchedArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingFifoArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(CopyArgs) <= 4096, "kernel argument segment too large");
@@ -129,6 +155,7 @@ hipError_t launch_fill64(unsigned long long* p, unsigned long long v, int64_t n,
 // Workgroups of the LL kernel (dtype, op) that fit on one CU at once.
 int ll_blocks_per_cu(int dtype, int op);
 hipError_t launch_ring_fifo(int dtype, int op, const RingFifoArgs& a, hipStream_t s);
+hipError_t launch_sched_fold(int dtype, int op, const SchedArgs& a, hipStream_t s);
 int ring_fifo_blocks_per_cu(int dtype, int op);
 
 }  // namespace simar

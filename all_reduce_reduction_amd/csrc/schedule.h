@@ -26,6 +26,20 @@ enum Coll { COLL_ALLREDUCE = 0, COLL_REDUCE_SCATTER = 1, COLL_ALL_GATHER = 2 };
 //   FANOUT        owner `src` sends its finished `chunk` to every other
 //                 rank (all-pairs step 2)
 //   ONESHOT       GATHER_REDUCE + FANOUT of `chunk` fused in one transfer
+// Tree, recursive-exchange and hierarchical steps carry a rank set `mask`
+// (bit q = rank q); sets are always folded in ascending rank order:
+//   GATHER        dst's running value for `chunk` folds in the values of
+//                 the ranks in `mask`, ascending (a tree parent taking its
+//                 children's subtotals; a node-local reduce-scatter owner
+//                 taking its node's elements); values as before the step
+//   GATHER_POST   the same, completing the value (post-processed output)
+//   EXCH          dst's value becomes the fold of the values of the ranks
+//                 in `mask` (which contains dst), ascending, all as they
+//                 were before the step: every member of one group ends
+//                 with the same value (recursive exchange, cross-node
+//                 all-pairs); _POST completes the value
+//   MCAST         src's value for `chunk` is copied to every rank in
+//                 `mask` (tree broadcast, node-local all-gather)
 enum XferKind {
   XK_REDUCE = 0,
   XK_REDUCE_POST = 1,
@@ -33,21 +47,35 @@ enum XferKind {
   XK_GATHER_REDUCE = 3,
   XK_FANOUT = 4,
   XK_ONESHOT = 5,
+  XK_GATHER = 6,
+  XK_GATHER_POST = 7,
+  XK_EXCH = 8,
+  XK_EXCH_POST = 9,
+  XK_MCAST = 10,
 };
+constexpr int kNumXferKinds = 11;
 
 struct Xfer {
   int kind;
-  int src;    // -1: every rank (GATHER_REDUCE, ONESHOT)
-  int dst;    // -1: every other rank (FANOUT) / every rank (ONESHOT)
+  int src;    // -1: every rank (GATHER_REDUCE, ONESHOT) / unused (GATHER, EXCH)
+  int dst;    // -1: every other rank (FANOUT) / every rank (ONESHOT) / unused (MCAST)
   int chunk;
+  uint32_t mask = 0;  // rank set of GATHER, EXCH, MCAST
+};
+
+struct Topology {
+  int ranks_per_node = 1;  // G: consecutive ranks kG .. kG+G-1 form node k
+  int radix = 2;           // k of the k-ary recursive exchange
 };
 
 struct Schedule {
   int algo = 0;
   int p = 0;
   int coll = COLL_ALLREDUCE;
-  int rounds = 0;  // communication rounds: every rank sends once per round
-  std::vector<std::vector<Xfer>> steps;  // one entry per lowered step (launch)
+  int nchunks = 0;  // the buffer is cut into nchunks chunks, floor(c*n/nchunks)
+  Topology topo;
+  int rounds = 0;   // communication rounds (closed form of the algorithm)
+  std::vector<std::vector<Xfer>> steps;  // one entry per lowered step
   int nxfers() const {
     int n = 0;
     for (auto& s : steps) n += (int)s.size();
@@ -55,20 +83,43 @@ struct Schedule {
   }
 };
 
-// Lowering.  Returns false for an unknown (coll, algo) pair or p < 2.
-bool lower(int coll, int algo, int p, Schedule* out);
+// NCCL's binary tree over n nodes ("Inside NCCL all-reduce", section "The
+// double binary tree"): a node's lowest set bit b fixes its height; its
+// parent clears b and sets the next bit up, or only clears b when that
+// leaves the node range; its children are the node minus and plus b/2,
+// the plus side halving again until it falls inside the range.  Node 0 is
+// the root and its one child is the largest power of two below n.
+// which = 0: that tree; which = 1: the second tree of the double tree --
+// node x plays node n-1-x of the first tree (mirror) for even n, node x-1
+// (shifted by one) for odd n.  Parent -1 for the root; children ascending.
+int tree_parent(int which, int n, int x);
+int tree_children(int which, int n, int x, int out[2]);
 
-// The fold order chunk c must follow under `algo`.
-std::vector<int> expected_order(int algo, int p, int c);
+// The tree actually run over p ranks with G ranks per node: node k's first
+// rank kG takes the node's place in the tree over the p/G nodes; the other
+// ranks of the node hang below it as a chain (kG+i is the parent of
+// kG+i+1).  Children (at most three) are returned ascending.
+int rank_tree_parent(int which, int p, int G, int r);
+int rank_tree_children(int which, int p, int G, int r, int out[3]);
 
-// Check(): symbolic run with contributor masks and fold-order traces.
+// Lowering.  Returns false for an unknown (coll, algo) pair, p < 2, or a
+// topology the algo cannot use (G must divide p; the recursive exchange
+// needs p to be a power of the radix).
+bool lower(int coll, int algo, int p, const Topology& t, Schedule* out);
+
+// The fold chunk c must end with, as an expression over rank numbers:
+// "(a+b)" combines a then b.  Derived from each algorithm's definition,
+// independently of its lowering.
+std::string expected_expr(const Schedule& s, int c);
+
+// Check(): symbolic run with contributor masks and fold expressions.
 // Returns true when the schedule is proven; otherwise false with a message.
 bool verify(const Schedule& s, std::string* diag);
 
-// Contributor masks after `after_steps` steps, masks[r*p + c].
+// Contributor masks after `after_steps` steps, masks[r*nchunks + c].
 bool symbolic_state(const Schedule& s, int after_steps, uint32_t* masks, std::string* diag);
 
-// Cached, verified schedules (lowered and checked once per (coll, algo, p)).
-const Schedule* cached_schedule(int coll, int algo, int p, std::string* diag);
+// Cached, verified schedules (lowered and checked once per key).
+const Schedule* cached_schedule(int coll, int algo, int p, const Topology& t, std::string* diag);
 
 }  // namespace simar

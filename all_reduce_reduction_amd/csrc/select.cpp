@@ -16,6 +16,7 @@
 #include <cstring>
 #include <map>
 #include <memory>
+#include <utility>
 #include <vector>
 
 #include "schedule.h"
@@ -34,10 +35,16 @@ Model default_model() {
   m.a[SIM_ALGO_ONESHOT] = {5.1, 6600.0, -1.0, -1.0};
   m.a[SIM_ALGO_ONESHOT_LL] = {9.4, 6750.0, -1.0, -1.0};
   m.a[SIM_ALGO_RING_FIFO] = {30.0, 4000.0, -1.0, -1.0};  // until calibrated
+  m.a[SIM_ALGO_TREE] = {4.5, 6000.0, -1.0, -1.0};
+  m.a[SIM_ALGO_REXCH] = {4.5, 6000.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER] = {4.5, 6000.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER_LARGE] = {4.5, 6000.0, -1.0, -1.0};
   return m;
 }
 
-int model_launches(int coll, int algo, int p) {
+static bool is_topology_algo(int algo) { return algo >= SIM_ALGO_TREE && algo <= SIM_ALGO_HIER_LARGE; }
+
+int model_launches(int coll, int algo, int p, const Topology& t) {
   switch (algo) {
     case SIM_ALGO_RING: return coll == COLL_ALLREDUCE ? 2 * (p - 1) : p - 1;
     case SIM_ALGO_ALLPAIRS: return coll == COLL_ALLREDUCE ? 2 : 1;
@@ -45,11 +52,60 @@ int model_launches(int coll, int algo, int p) {
     case SIM_ALGO_ONESHOT_LL: return 1;
     case SIM_ALGO_RING_FIFO: return 1;
   }
+  if (is_topology_algo(algo) && coll == COLL_ALLREDUCE) {
+    const Schedule* s = cached_schedule(coll, algo, p, t, nullptr);
+    return s ? (int)s->steps.size() : -1;  // one launch per step
+  }
   return 0;
 }
 
-double model_traffic(int coll, int algo, int p, double n, int esize) {
+double schedule_traffic(const Schedule& s, double n, int esize) {
+  const double e = esize;
+  const int p = s.p;
+  std::vector<char> part((size_t)p * s.nchunks, 0);  // value held as a 4-byte partial
+  double bytes = 0;
+  for (const auto& step : s.steps) {
+    std::vector<char> next = part;
+    std::vector<std::pair<int, uint32_t>> groups;  // (chunk, set) of the step's exchanges
+    for (const Xfer& x : step) {
+      const double len = n / s.nchunks;
+      auto operand = [&](int q) { return len * (part[(size_t)q * s.nchunks + x.chunk] ? 4.0 : e); };
+      const bool post = (x.kind == XK_GATHER_POST || x.kind == XK_EXCH_POST);
+      const double out = len * (post ? e : 4.0);
+      if (x.kind == XK_GATHER || x.kind == XK_GATHER_POST) {
+        bytes += operand(x.dst) + out;
+        for (int q = 0; q < p; q++)
+          if (x.mask & (1u << q)) bytes += operand(q);
+        next[(size_t)x.dst * s.nchunks + x.chunk] = !post;
+      } else if (x.kind == XK_EXCH || x.kind == XK_EXCH_POST) {
+        const std::pair<int, uint32_t> key(x.chunk, x.mask);
+        bool seen = false;
+        for (auto& k : groups) seen = seen || (k == key);
+        if (!seen) {
+          groups.push_back(key);
+          for (int q = 0; q < p; q++)
+            if (x.mask & (1u << q)) bytes += operand(q);
+        }
+        bytes += out;
+        next[(size_t)x.dst * s.nchunks + x.chunk] = !post;
+      } else if (x.kind == XK_MCAST) {
+        int k = 0;
+        for (int q = 0; q < p; q++)
+          if (x.mask & (1u << q)) k++;
+        bytes += len * e * (1 + k);
+      }
+    }
+    part = next;
+  }
+  return bytes;
+}
+
+double model_traffic(int coll, int algo, int p, double n, int esize, const Topology& t) {
   const double e = esize, S = n * e;
+  if (is_topology_algo(algo)) {
+    const Schedule* s = (coll == COLL_ALLREDUCE) ? cached_schedule(coll, algo, p, t, nullptr) : nullptr;
+    return s ? schedule_traffic(*s, n, esize) : 0.0;
+  }
   if (coll == COLL_ALLREDUCE) {
     switch (algo) {
       case SIM_ALGO_ONESHOT: return 2.0 * p * S;          // p inputs read, p outputs written
@@ -83,12 +139,14 @@ double model_traffic(int coll, int algo, int p, double n, int esize) {
   return 0.0;
 }
 
-double model_predict(const Model& m, int coll, int algo, int p, double n, int esize) {
+double model_predict(const Model& m, int coll, int algo, int p, double n, int esize, const Topology& t) {
   if (algo <= 0 || algo >= kNumAlgos) return 1e30;
   const AlgoModel& am = m.a[algo];
-  const double steps = am.steps >= 0 ? am.steps : (double)model_launches(coll, algo, p);
+  const int launches = model_launches(coll, algo, p, t);
+  if (launches < 0) return 1e30;  // no schedule for this topology
+  const double steps = am.steps >= 0 ? am.steps : (double)launches;
   const double bytes = am.bytes_factor >= 0 ? am.bytes_factor * n * esize
-                                            : model_traffic(coll, algo, p, n, esize);
+                                            : model_traffic(coll, algo, p, n, esize, t);
   return am.alpha_us * steps + bytes / (am.gbps * 1e3);  // GB/s -> bytes per us
 }
 
@@ -223,7 +281,8 @@ struct Parser {
   }
 };
 
-const char* kAlgoNames[kNumAlgos] = {"auto", "ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"};
+const char* kAlgoNames[kNumAlgos] = {"auto",       "ring", "allpairs", "oneshot", "oneshot_ll",
+                                     "ring_fifo", "tree", "rexch",    "hier",    "hier_large"};
 
 }  // namespace
 

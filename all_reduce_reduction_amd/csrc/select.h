@@ -4,9 +4,11 @@
 #include <cstddef>
 #include <string>
 
+#include "schedule.h"
+
 namespace simar {
 
-constexpr int kNumAlgos = 6;  // indices are the SIM_ALGO_* codes (0 = AUTO unused)
+constexpr int kNumAlgos = 10;  // indices are the SIM_ALGO_* codes (0 = AUTO unused)
 
 struct AlgoModel {
   double alpha_us = 4.0;       // fixed cost per launch (sync step)
@@ -22,16 +24,27 @@ struct Model {
 
 Model default_model();
 
-// Launches (latency units) of a schedule; `coll` is a simar::Coll.
-int model_launches(int coll, int algo, int p);
+// Launches (latency units) of a schedule; `coll` is a simar::Coll.  The
+// tree, recursive exchange and 2PH schedules depend on the topology (-1
+// when it does not fit p).
+int model_launches(int coll, int algo, int p, const Topology& t = Topology());
 
 // Algorithmic HBM bytes of one call, summed over all simulated ranks.
 // n = elements per rank of the all-reduce input (reduce-scatter: the full
 // input; all-gather: the full output), esize = bytes per element.
-double model_traffic(int coll, int algo, int p, double n, int esize);
+double model_traffic(int coll, int algo, int p, double n, int esize, const Topology& t = Topology());
+
+// The same for a lowered tree / recursive-exchange / 2PH schedule as the
+// step executor runs it: each fold reads its operands once (inputs at
+// storage width, partials as 4-byte accumulators) and writes every
+// receiving rank once (finished values at storage width, partials at 4
+// bytes); the members of an exchange group share one fold; a broadcast
+// reads once and writes each receiver.
+double schedule_traffic(const Schedule& s, double n, int esize);
 
 // T = alpha * launches + traffic / B, in microseconds.
-double model_predict(const Model& m, int coll, int algo, int p, double n, int esize);
+double model_predict(const Model& m, int coll, int algo, int p, double n, int esize,
+                     const Topology& t = Topology());
 
 // Parse a calibration file; returns false (and leaves *m alone) on error.
 bool model_load_json(const char* path, Model* m, std::string* err);

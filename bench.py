@@ -14,7 +14,8 @@ Printed JSON line:
                  MI355X's 8 TB/s HBM peak; `traffic` = rocprofv3 FETCH_SIZE +
                  WRITE_SIZE per launch when a matching counter summary is
                  committed under profiles/, else null
-  per_algo       the same workload forced to each legal schedule
+  per_algo       the same workload forced to each legal schedule (the tree,
+                 recursive-exchange and 2PH ones at a stated topology)
   latency_8KiB   per-call microseconds at 8 KiB per rank (p = 8, fp16):
                  plain one-shot vs the LL packet path vs the selector's pick
   cpu_baseline   the CPU oracle on the same host arrays (all host threads)
@@ -68,6 +69,43 @@ def algorithmic_bytes(algo: str) -> float:
     if algo == "ring_fifo":  # HBM-side: inputs once, outputs once (FIFO words counted apart)
         return 2.0 * P * S
     raise ValueError(algo)
+
+
+# The tree, recursive-exchange and 2PH schedules, each at the topology it is
+# timed with: (name, algo, ranks per node, radix).
+TOPOLOGY_RUNS = [("tree", "tree", 1, 2), ("rexch_k2", "rexch", 1, 2), ("hier_G4", "hier", 4, 2),
+                 ("hier_large_G4", "hier_large", 4, 2)]
+
+
+def schedule_bytes(sim, algo: str, n: int, esize: int) -> float:
+    """Algorithmic HBM bytes of one call of a lowered tree / exchange / 2PH
+    schedule as the step executor runs it: a fold reads each operand once
+    (inputs at storage width, partials as 4-byte fp32) and writes each
+    receiver once (finished values at storage width, partials at 4 bytes);
+    an exchange group shares one fold; a broadcast reads once and writes
+    each receiver."""
+    nsteps, _, nch = sim.sim_schedule_info(algo, P)
+    part = set()
+    total = 0.0
+    for st in range(nsteps):
+        groups, nxt = set(), set(part)
+        for kind, src, dst, chunk, mask in sim.sim_schedule_xfers(algo, P, st):
+            ln = n / nch
+            members = [q for q in range(P) if (mask >> q) & 1]
+            width = lambda q: 4 if (q, chunk) in part else esize  # noqa: E731
+            if kind in (6, 7, 8, 9):
+                post = kind in (7, 9)
+                if kind in (6, 7):
+                    total += ln * (width(dst) + sum(width(q) for q in members))
+                elif (chunk, mask) not in groups:
+                    groups.add((chunk, mask))
+                    total += ln * sum(width(q) for q in members)
+                total += ln * (esize if post else 4)
+                (nxt.discard if post else nxt.add)((dst, chunk))
+            elif kind == 10:
+                total += ln * esize * (1 + len(members))
+        part = nxt
+    return total
 
 
 def time_calls(fn, steps: int, warmup: int) -> float:
@@ -187,6 +225,15 @@ def main():
             ta = time_calls(lambda a=a: step(a), max(10, args.steps // 4), 5)
             per_algo[a] = {"us": round(ta * 1e6, 2), "busbw_GBps": round(2 * (P - 1) / P * S / ta / 1e9, 1),
                            "hbm_algorithmic_GBps": round(algorithmic_bytes(a) / ta / 1e9, 1)}
+        for name, a, G, k in TOPOLOGY_RUNS:
+            sim.sim_config_set("ranks_per_node", G)
+            sim.sim_config_set("radix", k)
+            ta = time_calls(lambda a=a: step(a), max(10, args.steps // 4), 5)
+            per_algo[name] = {"us": round(ta * 1e6, 2), "busbw_GBps": round(2 * (P - 1) / P * S / ta / 1e9, 1),
+                              "hbm_algorithmic_GBps": round(schedule_bytes(sim, a, N, ESIZE) / ta / 1e9, 1),
+                              "steps": sim.sim_schedule_info(a, P)[0]}
+        sim.sim_config_set("ranks_per_node", 1)
+        sim.sim_config_set("radix", 2)
         extras["per_algo"] = per_algo
         # small-message latency: 8 KiB per rank, fp16
         lx = synthdata.workload_inputs(4, P, LAT_N, "fp16")
@@ -201,6 +248,15 @@ def main():
             lat[a] = round(time_calls(call, 2000, 200) * 1e6, 2)
             if a == "auto":
                 lat["auto_pick"] = sim.sim_last_algo()
+        for name, a, G, k in TOPOLOGY_RUNS:
+            sim.sim_config_set("ranks_per_node", G)
+            sim.sim_config_set("radix", k)
+            call = sim.prepare_allreduce(lip, lop, P, LAT_N, "fp16", "sum", a, stream)
+            if call() != 0:
+                raise sim.SimError(call(), f"sim_allreduce({a})")
+            lat[name] = round(time_calls(call, 2000, 200) * 1e6, 2)
+        sim.sim_config_set("ranks_per_node", 1)
+        sim.sim_config_set("radix", 2)
         assert sim.sim_check_error(stream) == 0
         extras["latency_8KiB_us"] = lat
 

@@ -47,7 +47,13 @@
  * ring chunk c (both ring executions) folds ranks c+1, c+2, ..., c+p
  * (mod p) left to right;
  * all-pairs, one-shot and LL fold the owner c first and then the other
- * ranks in ascending order.  fp16/bf16 are widened exactly to fp32,
+ * ranks in ascending order; the tree folds each rank's own value and then
+ * its children's subtree totals in ascending rank order; the recursive
+ * exchange folds each group in ascending rank order, lowest base-k digit
+ * first; 2PH folds a node's ranks starting with the rank that holds the
+ * chunk, then the node partials (small form: nodes ascending; large form:
+ * the owner's node first, then the others ascending).  Every rank's output
+ * is the same bits.  fp16/bf16 are widened exactly to fp32,
  * accumulated in fp32 (ring partials are kept in fp32) and rounded once,
  * to nearest even, at the final write.  fp avg multiplies each operand by
  * fp32(1/p) as it is read; int32 avg divides the wrapped int32 sum by p
@@ -81,14 +87,23 @@ enum {
 enum { SIM_INT32 = 0, SIM_FP32 = 1, SIM_FP16 = 2, SIM_BF16 = 3 };
 enum { SIM_SUM = 0, SIM_PROD = 1, SIM_MIN = 2, SIM_MAX = 3, SIM_AVG = 4 };
 enum {
-  SIM_ALGO_AUTO = 0,        /* alpha-beta argmin over the legal schedules */
+  SIM_ALGO_AUTO = 0,        /* alpha-beta argmin over the legal schedules 1..5 (the
+                               topology schedules 6..9 run only when named) */
   SIM_ALGO_RING = 1,        /* 2(p-1) steps, one launch per step */
   SIM_ALGO_ALLPAIRS = 2,    /* 2 steps: owner gather-reduce, then fan-out */
   SIM_ALGO_ONESHOT = 3,     /* the 2 all-pairs steps fused in one launch */
   SIM_ALGO_ONESHOT_LL = 4,  /* one-shot through 8-byte data+flag packets */
-  SIM_ALGO_RING_FIFO = 5    /* the ring in ONE launch: persistent workgroups, bounded
+  SIM_ALGO_RING_FIFO = 5,   /* the ring in ONE launch: persistent workgroups, bounded
                                FIFOs between neighbours, in-kernel signal/wait */
+  SIM_ALGO_TREE = 6,        /* double binary tree: each half of the buffer reduced up
+                               and broadcast down one of two complementary trees */
+  SIM_ALGO_REXCH = 7,       /* k-ary recursive exchange: log_k(p) rounds */
+  SIM_ALGO_HIER = 8,        /* 2PH, small-message form: node-local reduce-scatter into
+                               G chunks, all-pairs across nodes, node-local all-gather */
+  SIM_ALGO_HIER_LARGE = 9   /* 2PH, large-message form: p chunks; node-local and
+                               cross-node reduce-scatter, then the two all-gathers */
 };
+#define SIM_NUM_ALGOS 10
 
 #define SIM_MAX_RANKS 16
 /* LL packets carry 4 data bytes in 8: the LL buffer holds 2x the payload.
@@ -176,31 +191,77 @@ int sim_model_reset(void);
  * check (that call's outputs are undefined). */
 int sim_check_error(void* stream);
 
+/* ---- topology (host only; no device needed) ------------------------- */
+
+/* The simulated topology that SIM_ALGO_TREE, SIM_ALGO_REXCH, SIM_ALGO_HIER
+ * and SIM_ALGO_HIER_LARGE follow ("Inside NCCL all-reduce", section "The
+ * double binary tree": trees link nodes, a node's ranks form a chain;
+ * "MSCCL++ ...", section "The Collective Algorithm Library", 2PH: local
+ * collectives inside a node; "Demystifying NVSHMEM", Fig. 7: k-ary
+ * recursive exchange).  Process-wide settings, kept across sim_init.
+ *   SIM_CONFIG_RANKS_PER_NODE  G: ranks kG .. kG+G-1 form node k.  1..16,
+ *                              default 1.  Collectives with a G that does
+ *                              not divide p are SIM_ERR_UNSUPPORTED for the
+ *                              algos that use it.
+ *   SIM_CONFIG_RADIX           k of the recursive exchange, 2..16, default
+ *                              2; it needs p to be a power of k
+ *                              (SIM_ERR_UNSUPPORTED otherwise).
+ * Out-of-range values are SIM_ERR_INVALID_ARG and change nothing. */
+enum { SIM_CONFIG_RANKS_PER_NODE = 0, SIM_CONFIG_RADIX = 1 };
+int sim_config_set(int key, int value);
+int sim_config_get(int key, int* value);
+
+/* The rank tree SIM_ALGO_TREE runs for p ranks, G ranks per node.
+ * tree 0: NCCL's bit-trick binary tree over the p/G nodes (node k's lowest
+ * set bit fixes its height; its parent clears that bit and sets the next
+ * one up, or only clears it at the edge of the range; its children are k
+ * minus and plus half that bit); tree 1: its mirror image (node x plays
+ * node p/G-1-x) for an even node count, the tree shifted by one node for an
+ * odd one.  Node k's place is taken by rank kG; ranks kG+1 .. kG+G-1 hang
+ * below it as a chain.  *parent gets -1 for the root; children[0..2] get
+ * up to three children in ascending order, *nchildren their count. */
+int sim_tree_info(int tree, int p, int ranks_per_node, int rank, int* parent, int* children,
+                  int* nchildren);
+
 /* ---- schedules and the verifier (host only; no device needed) --------- */
 
-/* Step and transfer counts of the lowered schedule of (algo, p). */
-int sim_schedule_info(int algo, int p, int* nsteps, int* nxfers);
+/* The all-reduce schedules below use the current topology settings.
+ * Step and transfer counts of the lowered schedule of (algo, p), and the
+ * number of chunks it cuts the buffer into (chunk c of nchunks is
+ * [floor(c*n/nchunks), floor((c+1)*n/nchunks))).  SIM_ERR_UNSUPPORTED when
+ * (algo, p, topology) has no schedule. */
+int sim_schedule_info(int algo, int p, int* nsteps, int* nxfers, int* nchunks);
 
-/* The transfers of one step: 4 ints each {kind, src rank, dst rank,
- * chunk}, kind 0 REDUCE, 1 REDUCE_POST, 2 COPY, 3 GATHER_REDUCE,
- * 4 FANOUT, 5 ONESHOT.  `*count` gets the number written (at most max). */
+/* The transfers of one step: 5 ints each {kind, src rank, dst rank, chunk,
+ * rank set}, kind 0 REDUCE, 1 REDUCE_POST, 2 COPY, 3 GATHER_REDUCE,
+ * 4 FANOUT, 5 ONESHOT, 6 GATHER, 7 GATHER_POST, 8 EXCH, 9 EXCH_POST,
+ * 10 MCAST; the rank set (bit q = rank q) is used by kinds 6..10:
+ *   GATHER(_POST) dst folds into its own value the set's values, ascending;
+ *   EXCH(_POST)   dst's value becomes the fold of the set's values
+ *                 (the set contains dst), ascending, as before the step;
+ *   MCAST         src's finished value is copied to every rank in the set.
+ * _POST kinds complete the value.  `*count` gets the number written (at
+ * most max). */
 int sim_schedule_xfers(int algo, int p, int step, int* out, int max, int* count);
 
-/* Symbolic state after `after_steps` steps: masks[r*p + c] = bit mask of
- * the ranks whose contribution rank r's slot for chunk c holds. */
+/* Symbolic state after `after_steps` steps: masks[r*nchunks + c] = bit
+ * mask of the ranks whose contribution rank r's slot for chunk c holds. */
 int sim_schedule_state(int algo, int p, int after_steps, uint32_t* masks);
 
 /* Check() -- run the schedule symbolically and prove that every output
  * chunk holds each rank's contribution exactly once, in the documented
- * fold order, with no read/write hazard inside a step and the closed-form
- * step count.  Returns SIM_OK or SIM_ERR_VERIFY with a message in diag. */
+ * fold order, with no read/write hazard inside a step (members of one
+ * exchange group excepted) and the closed-form round count.  Returns
+ * SIM_OK or SIM_ERR_VERIFY with a message in diag. */
 int sim_verify_schedule(int algo, int p, char* diag, size_t diag_len);
 
-/* Same check on a caller-supplied schedule (nsteps steps; step s has
- * counts[s] transfers laid out as in sim_schedule_xfers, concatenated in
- * xfers).  `algo` names the fold order the result must follow. */
-int sim_verify_custom(int algo, int p, int nsteps, const int* counts, const int* xfers,
-                      char* diag, size_t diag_len);
+/* Same check on a caller-supplied all-reduce schedule over nchunks chunks
+ * (nsteps steps; step s has counts[s] transfers laid out as in
+ * sim_schedule_xfers, concatenated in xfers).  `algo` names the fold order
+ * (and, for the topology algos, the current topology) the result must
+ * follow; `rounds` is the round count the schedule claims. */
+int sim_verify_custom(int algo, int p, int nchunks, int rounds, int nsteps, const int* counts,
+                      const int* xfers, char* diag, size_t diag_len);
 
 /* ---- test hooks --------------------------------------------------------- */
 enum {

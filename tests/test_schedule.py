@@ -26,8 +26,8 @@ def test_ring_reproduces_the_3gpu_table():
 
 @pytest.mark.parametrize("p", range(2, 17))
 def test_step_counts(p):
-    assert sim.sim_schedule_info("ring", p) == (2 * (p - 1), 2 * (p - 1) * p)
-    assert sim.sim_schedule_info("allpairs", p) == (2, 2 * p)
+    assert sim.sim_schedule_info("ring", p) == (2 * (p - 1), 2 * (p - 1) * p, p)
+    assert sim.sim_schedule_info("allpairs", p) == (2, 2 * p, p)
     assert sim.sim_schedule_info("oneshot", p)[0] == 1
 
 
@@ -41,7 +41,7 @@ def test_ring_primitive_counts_per_rank(p):
     for st in range(2 * (p - 1)):
         xs = sim.sim_schedule_xfers("ring", p, st)
         assert len(xs) == p and sorted(x[1] for x in xs) == list(range(p))  # every rank sends once
-        for kind, src, dst, chunk in xs:
+        for kind, src, dst, chunk, _ in xs:
             assert dst == (src + 1) % p
             if kind == REDUCE:
                 recv_reduce[dst] += 1
@@ -60,12 +60,12 @@ def test_bytes_sent_per_rank_is_optimal(p):
     # each rank sends 2(p-1)/p of its buffer (counted in chunks of S/p)
     sent = {r: 0 for r in range(p)}
     for st in range(2 * (p - 1)):
-        for kind, src, dst, chunk in sim.sim_schedule_xfers("ring", p, st):
+        for kind, src, dst, chunk, _ in sim.sim_schedule_xfers("ring", p, st):
             sent[src] += 1
     assert all(v == 2 * (p - 1) for v in sent.values())
     sent = {r: 0 for r in range(p)}
     for st in range(2):
-        for kind, src, dst, chunk in sim.sim_schedule_xfers("allpairs", p, st):
+        for kind, src, dst, chunk, _ in sim.sim_schedule_xfers("allpairs", p, st):
             if kind == GATHER_REDUCE:
                 for q in range(p):
                     if q != dst:
@@ -88,6 +88,9 @@ def _ring(p):
 
 def test_verifier_accepts_the_unmodified_copy():
     assert sim.sim_verify_custom("ring", 4, _ring(4))[0] == 0
+    # a schedule that claims another round count than the closed form
+    st, diag = sim.sim_verify_custom("ring", 4, _ring(4), rounds=5)
+    assert st == -8 and "closed form" in diag
 
 
 @pytest.mark.parametrize("p", [3, 4, 8])
@@ -96,13 +99,13 @@ def test_verifier_rejects_mutations(p):
     muts = {}
     m = [list(s) for s in base]; del m[1][2]; muts["dropped transfer"] = m
     m = [list(s) for s in base]; m[0].append(m[0][0]); muts["duplicated reduce"] = m
-    m = [list(s) for s in base]; k, a, b, c = m[0][1]; m[0][1] = (k, a, b, (c + 1) % p); muts["swapped chunk"] = m
+    m = [list(s) for s in base]; k, a, b, c, w = m[0][1]; m[0][1] = (k, a, b, (c + 1) % p, w); muts["swapped chunk"] = m
     m = [list(s) for s in base]; m[1], m[0] = m[0], m[1]; muts["steps reordered"] = m
     m = [list(s) for s in base]; del m[-1]; muts["missing step"] = m
-    m = [list(s) for s in base]; m[p - 2] = [(REDUCE, a, b, c) for (_, a, b, c) in m[p - 2]]; muts["no post-op"] = m
-    m = [list(s) for s in base]; k, a, b, c = m[p - 1][0]; m[p - 1][0] = (k, a, (b + 1) % p, c); muts["wrong copy target"] = m
+    m = [list(s) for s in base]; m[p - 2] = [(REDUCE, a, b, c, w) for (_, a, b, c, w) in m[p - 2]]; muts["no post-op"] = m
+    m = [list(s) for s in base]; k, a, b, c, w = m[p - 1][0]; m[p - 1][0] = (k, a, (b + 1) % p, c, w); muts["wrong copy target"] = m
     for name, steps in muts.items():
-        st, diag = sim.sim_verify_custom("ring", p, steps)
+        st, diag = sim.sim_verify_custom("ring", p, steps, rounds=2 * (p - 1))
         assert st == -8, (name, diag)
         assert diag, name
 
@@ -110,7 +113,7 @@ def test_verifier_rejects_mutations(p):
 def test_verifier_rejects_an_intra_step_hazard():
     # two reduces in one step: the second reads the slot the first writes
     steps = [[(REDUCE, 0, 1, 0), (REDUCE, 1, 2, 0)]]
-    st, diag = sim.sim_verify_custom("ring", 3, steps)
+    st, diag = sim.sim_verify_custom("ring", 3, steps, rounds=4)
     assert st == -8 and "read by one transfer and written by another" in diag
 
 
@@ -118,5 +121,5 @@ def test_verifier_checks_fold_order():
     # the all-pairs schedule is correct as an all-pairs but not in ring order
     ap = [sim.sim_schedule_xfers("allpairs", 4, s) for s in range(2)]
     assert sim.sim_verify_custom("allpairs", 4, ap)[0] == 0
-    st, diag = sim.sim_verify_custom("ring", 4, ap)
-    assert st == -8
+    st, diag = sim.sim_verify_custom("ring", 4, ap, rounds=6)
+    assert st == -8 and "another order" in diag
