@@ -10,7 +10,7 @@ message sizes that sits BETWEEN the evaluation sizes (powers of two times
 squares with relative weights (so microsecond and millisecond points count
 alike), and writes the JSON file sim_model_load() reads.
 
---check then times every legal schedule at the evaluation sizes (8192 x
+The fit is a two-regime estimate (see fit()).  --check then times every legal schedule at the evaluation sizes (8192 x
 {1, 16, 256, 4096} tokens bf16, and 1 KiB .. 1 MiB fp16) and compares the
 selector's pick with the measured fastest: a strict match, and a tolerant
 match when the pick is within max(3%, the measured spread) of the best.
@@ -28,7 +28,16 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_OUT = os.path.join(HERE, "calib", "mi355x.json")
 ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo")
+# The topology schedules are fitted too (sim_model_predict prices them),
+# each at the topology stated here; AUTO does not weigh them.
+TOPOLOGY = {"tree": (1, 2), "rexch": (1, 2), "hier": (4, 2), "hier_large": (4, 2)}  # (ranks per node, radix)
 P = 8
+
+
+def set_topology(sim, algo):
+    g, k = TOPOLOGY.get(algo, (1, 2))
+    sim.sim_config_set("ranks_per_node", g)
+    sim.sim_config_set("radix", k)
 
 
 def _timer():
@@ -86,15 +95,31 @@ class Bench:
 
 
 def fit(points, algo):
-    """Weighted least squares of t = alpha * L + bytes * inv_b over the
-    points [(launches, bytes, t_us)], weights 1/t (relative error)."""
+    """Fit t = alpha * L + bytes / B over the points [(launches, bytes, t_us)].
+
+    A start from weighted least squares (weights 1/t, i.e. relative error),
+    then each parameter re-estimated from the regime it governs: B from the
+    points where the bytes term is at least 80% of the predicted time
+    (total bytes over total time left after the launches), alpha from the
+    points where the launch term is at least 80% (median of the time left
+    after the bytes, per launch).  A joint line across the bend between the
+    latency-flat small sizes and the bandwidth-bound large ones otherwise
+    under-estimates B and mis-ranks schedules at large sizes."""
     import numpy as np
     A = np.array([[L / t, b / t] for (L, b, t) in points])
     y = np.ones(len(points))
     sol, *_ = np.linalg.lstsq(A, y, rcond=None)
-    alpha, inv_b = float(sol[0]), float(sol[1])
-    alpha = max(alpha, 0.0)
-    inv_b = max(inv_b, 1e-9)
+    alpha = max(float(sol[0]), 0.0)
+    inv_b = max(float(sol[1]), 1e-9)
+    for _ in range(3):
+        pred = [(alpha * L, b * inv_b) for (L, b, t) in points]
+        bw = [(L, b, t) for (L, b, t), (pa, pb) in zip(points, pred) if pb >= 0.8 * (pa + pb)]
+        lat = [(L, b, t) for (L, b, t), (pa, pb) in zip(points, pred) if pa >= 0.8 * (pa + pb)]
+        if bw:
+            left = sum(max(t - alpha * L, 1e-3) for (L, b, t) in bw)
+            inv_b = left / sum(b for (L, b, t) in bw)
+        if lat:
+            alpha = max(0.0, float(np.median([(t - b * inv_b) / L for (L, b, t) in lat])))
     return alpha, 1.0 / inv_b / 1e3  # bytes/us -> GB/s
 
 
@@ -104,7 +129,8 @@ def calibrate(out_path: str):
     sizes = [int(1.5 * (1 << k)) // 16 * 16 for k in range(10, 28)]   # 1.5 KiB .. 192 MiB
     b = Bench(max(sizes))
     raw = {}
-    for algo in ALGOS:
+    for algo in ALGOS + tuple(TOPOLOGY):
+        set_topology(sim, algo)
         pts = []
         for nbytes in sizes:
             if not b.legal(algo, nbytes):
@@ -123,10 +149,12 @@ def calibrate(out_path: str):
         raw[algo + "_fit_points"] = len(pts)
         alpha, gbps = fit(pts, algo)
         raw.setdefault("fit", {})[algo] = {"alpha_us": alpha, "gbps": gbps}
+    set_topology(sim, "ring")
     sim.sim_model_reset()
     model = {"device": "MI355X (gfx950)", "p": P, "dtype": "bf16",
              "grid": "1.5 x 2^k bytes per rank, k = 10..27",
-             "algos": raw["fit"], "measurements": {a: raw[a] for a in ALGOS if a in raw}}
+             "topology": {a: {"ranks_per_node": g, "radix": k} for a, (g, k) in TOPOLOGY.items()},
+             "algos": raw["fit"], "measurements": {a: raw[a] for a in ALGOS + tuple(TOPOLOGY) if a in raw}}
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
         json.dump(model, f, indent=1)

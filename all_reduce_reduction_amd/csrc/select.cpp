@@ -25,20 +25,21 @@
 namespace simar {
 
 // Built-in defaults: the fit of the calibration sweep on MI355X (p = 8,
-// bf16, 1.5 KiB .. 192 MiB per rank), rounded.  A calibration file loaded
-// with sim_model_load() or SIM_CALIB replaces them.
+// bf16, 1.5 KiB .. 192 MiB per rank; the topology schedules at the
+// topologies the calibration file states), rounded.  A calibration file
+// loaded with sim_model_load() or SIM_CALIB replaces them.
 Model default_model() {
   Model m;
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING] = {4.0, 6550.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ALLPAIRS] = {4.7, 7000.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT] = {5.1, 6600.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT_LL] = {9.4, 6750.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING_FIFO] = {30.0, 4000.0, -1.0, -1.0};  // until calibrated
-  m.a[SIM_ALGO_TREE] = {4.5, 6000.0, -1.0, -1.0};
-  m.a[SIM_ALGO_REXCH] = {4.5, 6000.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER] = {4.5, 6000.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER_LARGE] = {4.5, 6000.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING] = {4.4, 5900.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ALLPAIRS] = {4.7, 5650.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT] = {4.3, 5750.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT_LL] = {7.9, 7050.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING_FIFO] = {32.0, 790.0, -1.0, -1.0};
+  m.a[SIM_ALGO_TREE] = {4.6, 6000.0, -1.0, -1.0};
+  m.a[SIM_ALGO_REXCH] = {4.3, 5250.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER] = {4.9, 5950.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER_LARGE] = {5.2, 5900.0, -1.0, -1.0};
   return m;
 }
 

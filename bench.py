@@ -209,6 +209,8 @@ def main():
     if args.profile_only:
         print(json.dumps({"algo": ran, "us_per_step": t * 1e6}), flush=True)
         return
+    # the same step repeated in 5 further batches (spread of the timed figure)
+    reps = [time_calls(step, max(10, args.steps // 5), 2) for _ in range(5)]
     busbw = 2 * (P - 1) / P * S / t / 1e9
     kernel = {"oneshot": "k_fold (one-shot, all outputs)", "allpairs": "k_fold + k_copy",
               "ring": "k_ring_reduce + k_copy", "ring_fifo": "k_ring_fifo"}[ran]
@@ -275,6 +277,22 @@ def main():
                "kind": "oracle",
                "sample": f"the full workload (8 ranks x 64 MiB bf16, schedule '{ran}'), median of {len(runs)} runs",
                "seconds_per_call": round(tc, 3)}
+        # one thread, on the first 1/16 of every rank's buffer (the oracle's cost per element does not
+        # depend on n): a rate scaled to the same unit
+        threads = orc.num_threads()
+        orc.set_num_threads(1)
+        sub = [x[: N // 16].copy() for x in xs]
+        runs1 = []
+        t_end = time.perf_counter() + 10.0
+        while len(runs1) < 3 or (time.perf_counter() < t_end and len(runs1) < 10):
+            t0 = time.perf_counter()
+            orc.allreduce(sub, "bf16", "sum", ran)
+            runs1.append(time.perf_counter() - t0)
+        orc.set_num_threads(threads)
+        t1 = float(np.median(runs1)) * 16
+        cpu["single_thread"] = {"value": round(2 * (P - 1) / P * S / t1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                "sample": f"first 1/16 of each rank's buffer, median of {len(runs1)} runs, "
+                                          "scaled to the full buffer"}
 
     out = {
         "metric": METRIC, "value": round(busbw, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -283,7 +301,10 @@ def main():
         "config": {"workload": "all-reduce sum, p=8 simulated ranks, bf16 (fp32 accumulate), 8192 hidden x 4096 "
                                "tokens = 64 MiB per rank, N(0,1)*0.02", "p": P, "n_per_rank": N,
                    "bytes_per_rank": S, "algo": ran, "parallelism": "1 GPU (p simulated ranks in one HBM)"},
-        "roofline": roofline, "cpu_baseline": cpu, **extras,
+        "roofline": roofline, "cpu_baseline": cpu,
+        "repeat_batches_us": {"values": [round(v * 1e6, 2) for v in reps],
+                              "median": round(float(np.median(reps)) * 1e6, 2)},
+        **extras,
     }
     print(json.dumps(out), flush=True)
     sim.sim_finalize()

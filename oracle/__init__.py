@@ -79,6 +79,8 @@ class Oracle:
                      "allreduce_topo", "allreduce_at_topo"):
             getattr(lib, "oracle_" + name).restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = ctypes.c_int
         lib.oracle_chunk_lo.argtypes = [i64, ctypes.c_int, ctypes.c_int]
         lib.oracle_chunk_lo.restype = i64
         for name in ("bf16", "f16"):
@@ -191,6 +193,10 @@ class Oracle:
 
     def num_threads(self) -> int:
         return self.lib.oracle_num_threads()
+
+    def set_num_threads(self, n: int) -> int:
+        """Threads for later calls (timing only); returns the count in effect."""
+        return self.lib.oracle_set_num_threads(n)
 
     def chunk_lo(self, n: int, p: int, c: int) -> int:
         return self.lib.oracle_chunk_lo(n, p, c)

@@ -648,4 +648,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the element loops of later calls (timing only; results do
+ * not depend on it).  Returns the count now in effect. */
+int oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
 int64_t oracle_chunk_lo(int64_t n, int p, int c) { return chunk_lo(n, p, c); }
