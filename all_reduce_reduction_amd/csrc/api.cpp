@@ -56,6 +56,8 @@ struct Ctx {
   int fifo_channels = 0;  // 0: heuristic
   int fifo_slots = 4;
   int fifo_withhold = 0;  // test hook: rank 0's workgroups leave at once
+  int fifo_vecs = kFifoVecsPerLane;  // 16-byte vectors per lane per slot: 1, 2 or 4
+
   int fifo_occ[4][5] = {};
   Model model = default_model();
 };
@@ -285,7 +287,7 @@ int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_c
 int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
   const int p = c.p;
   const int V = 16 / esize_of(c.dtype);
-  const int slot = kBlock * kFifoVecsPerLane * V;
+  const int slot = kBlock * g.fifo_vecs * V;
   RingFifoArgs a;
   std::memset(&a, 0, sizeof a);
   int64_t maxchunk = 0;
@@ -301,6 +303,10 @@ int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
   int64_t C = g.fifo_channels > 0 ? g.fifo_channels : std::max<int64_t>(1, (maxchunk + slot - 1) / slot);
   C = std::min<int64_t>(C, kFifoMaxChannels);
   C = std::min<int64_t>(C, std::max<int64_t>(1, resident / p));
+  // rank-major grid padded to whole rounds of the 8 XCDs (when the padded
+  // grid still fits at once): the ranks of a channel run on one XCD
+  int64_t Cg = (C + 7) / 8 * 8;
+  if ((int64_t)p * Cg > resident) Cg = C;
   // slots per channel slice: the longest slice over all chunks (same formula as the kernel)
   int64_t maxslice = 0;
   for (int q = 0; q < p; q++) {
@@ -339,6 +345,7 @@ int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
   a.spin_limit = g.spin_limit;
   a.p = p;
   a.C = (int)C;
+  a.Cg = (int)Cg;
   a.NS = NS;
   a.nsub = (int)std::max<int64_t>(1, (maxslice + slot - 1) / slot);
   a.slot_elems = slot;
@@ -1105,6 +1112,11 @@ int sim_debug_set(int key, uint64_t value) {
       g.fifo_channels = (int)value;
       return SIM_OK;
     case SIM_DEBUG_FIFO_WITHHOLD: g.fifo_withhold = value ? 1 : 0; return SIM_OK;
+    case SIM_DEBUG_FIFO_VECS:
+      if (value != 1 && value != 2 && value != (uint64_t)kFifoVecsPerLane) return SIM_ERR_INVALID_ARG;
+      g.fifo_vecs = (int)value;
+      return SIM_OK;
+
     case SIM_DEBUG_FIFO_SLOTS:
       // two slots are the minimum: with one, every rank waits for its
       // successor to consume before sending and the ring deadlocks
@@ -1133,6 +1145,7 @@ int sim_debug_get(int key, uint64_t* value) {
     case SIM_DEBUG_UNROLL: *value = (uint64_t)g.unroll; return SIM_OK;
     case SIM_DEBUG_FIFO_CHANNELS: *value = (uint64_t)g.fifo_channels; return SIM_OK;
     case SIM_DEBUG_FIFO_WITHHOLD: *value = (uint64_t)g.fifo_withhold; return SIM_OK;
+    case SIM_DEBUG_FIFO_VECS: *value = (uint64_t)g.fifo_vecs; return SIM_OK;
     case SIM_DEBUG_FIFO_SLOTS: *value = (uint64_t)g.fifo_slots; return SIM_OK;
   }
   return SIM_ERR_INVALID_ARG;

@@ -88,10 +88,11 @@ struct LLArgs {
   float inv_p;
 };
 
-// Single-launch ring: p * C persistent workgroups, bounded FIFOs between
-// neighbouring ranks, epoch-tagged monotonic semaphores.  A FIFO slot holds
-// kBlock * kFifoVecsPerLane 16-byte vectors' worth of elements (one 32-bit
-// word per element): 8192 elements for 16-bit types, 4096 for 32-bit.
+// Single-launch ring: p * C persistent workgroups (grid p * Cg, rank-major),
+// bounded FIFOs between neighbouring ranks, epoch-tagged monotonic
+// semaphores.  A FIFO slot holds kBlock * U 16-byte vectors' worth of
+// elements (one 32-bit word per element), U = 1, 2 or kFifoVecsPerLane:
+// up to 8192 elements for 16-bit types, 4096 for 32-bit.
 constexpr int kFifoVecsPerLane = 4;
 constexpr int kFifoMaxSlotElems = kBlock * kFifoVecsPerLane * 8;
 struct RingFifoArgs {
@@ -104,6 +105,7 @@ struct RingFifoArgs {
   unsigned long long spin_limit;
   int p;
   int C;                       // channels per rank
+  int Cg;                      // channels in the grid: C rounded up to a multiple of 8 (rank-major grid)
   int NS;                      // slots per FIFO
   int nsub;                    // slots per channel slice of a chunk
   int slot_elems;              // kBlock * kFifoVecsPerLane * (16 / element bytes)

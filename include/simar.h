@@ -274,7 +274,8 @@ enum {
   SIM_DEBUG_UNROLL = 6,        /* 16-byte vectors per lane per pass in bulk kernels: 1 or 2 */
   SIM_DEBUG_FIFO_CHANNELS = 7, /* single-launch ring: channels per rank, <= 128 (0 = heuristic) */
   SIM_DEBUG_FIFO_SLOTS = 8,    /* single-launch ring: slots per FIFO, 2..8 (default 4) */
-  SIM_DEBUG_FIFO_WITHHOLD = 9  /* 1: rank 0's ring workgroups leave at once (forces a bounded-wait expiry) */
+  SIM_DEBUG_FIFO_WITHHOLD = 9, /* 1: rank 0's ring workgroups leave at once (forces a bounded-wait expiry) */
+  SIM_DEBUG_FIFO_VECS = 10     /* single-launch ring: 16-byte vectors per lane per slot, 1, 2 or 4 (default 4) */
 };
 int sim_debug_set(int key, uint64_t value);
 int sim_debug_get(int key, uint64_t* value);

@@ -217,17 +217,21 @@ def test_single_launch_ring_shapes(lib, orc):
     xs = synthdata.normal(48, 8, 8 * 4096 * 5 + 77, "fp32")
     want, _ = orc.allreduce(xs, "fp32", "sum", "ring_fifo")
     try:
-        for ch in (1, 3, 16, 64):
-            for ns in (2, 4, 8):
-                sim.sim_debug_set("fifo_channels", ch)
-                sim.sim_debug_set("fifo_slots", ns)
-                for rep in range(3 if ch == 64 else 1):
-                    got = run_allreduce(xs, "fp32", "sum", "ring_fifo")
-                    for r in range(8):
-                        assert_parity(got[r], want[r], "fp32", f"channels {ch} slots {ns} rep {rep} r{r}")
+        for vecs in (4, 2, 1):
+            sim.sim_debug_set("fifo_vecs", vecs)
+            for ch in (1, 3, 16, 64):
+                for ns in (2, 4, 8):
+                    sim.sim_debug_set("fifo_channels", ch)
+                    sim.sim_debug_set("fifo_slots", ns)
+                    for rep in range(3 if ch == 64 else 1):
+                        print(f"ring_fifo vecs {vecs} channels {ch} slots {ns} rep {rep}", flush=True)
+                        got = run_allreduce(xs, "fp32", "sum", "ring_fifo")
+                        for r in range(8):
+                            assert_parity(got[r], want[r], "fp32", f"vecs {vecs} channels {ch} slots {ns} rep {rep} r{r}")
     finally:
         sim.sim_debug_set("fifo_channels", 0)
         sim.sim_debug_set("fifo_slots", 4)
+        sim.sim_debug_set("fifo_vecs", 4)
 
 
 def test_single_launch_ring_repeated_large(lib, orc):
@@ -241,13 +245,15 @@ def test_single_launch_ring_repeated_large(lib, orc):
     want, _ = orc.allreduce(xs, "bf16", "sum", "ring_fifo")
     din = to_device(xs, "bf16")
     outs = [empty_like_poisoned(n, "bf16", 8) for _ in range(4)]
-    for ns in (2, 8):
+    for ns, vecs in ((2, 4), (8, 4), (4, 1)):
         sim.sim_debug_set("fifo_slots", ns)
+        sim.sim_debug_set("fifo_vecs", vecs)
         for k in range(40):
             assert sim.sim_allreduce(ptrs(din), ptrs(outs[k % 4]), 8, n, "bf16", "sum", "ring_fifo", stream()) == OK
         assert sim.sim_check_error(stream()) == OK
         for o in outs:
             got = to_host(o, "bf16")
             for r in range(8):
-                assert_parity(got[r], want[r], "bf16", f"slots {ns} r{r}")
+                assert_parity(got[r], want[r], "bf16", f"slots {ns} vecs {vecs} r{r}")
     sim.sim_debug_set("fifo_slots", 4)
+    sim.sim_debug_set("fifo_vecs", 4)
