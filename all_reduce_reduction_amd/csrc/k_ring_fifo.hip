@@ -6,12 +6,14 @@
 //     send, (p-2) x recvReduceSend, recvReduceCopySend(post-op),
 //     (p-2) x recvCopySend, recv
 // over its channel's slice of every chunk ("Channels: the ring is plural":
-// each channel owns a slice of the buffer and its own FIFOs).  Data move
-// between neighbouring ranks through bounded FIFOs of NS slots (the 8-slot
-// FIFO per peer of the same page, section "Why a 100 GB all-reduce doesn't
-// OOM"), so a partial sum never round-trips a full-size HBM buffer: the
-// FIFOs are small and stay in L2/MALL, and HBM sees the p inputs read once
-// and the p outputs written once.
+// each channel owns a slice of the buffer and its own FIFOs).  Partial sums
+// of the reduce-scatter half move between neighbouring ranks through
+// bounded FIFOs of NS slots (the 8-slot FIFO per peer of the same page,
+// section "Why a 100 GB all-reduce doesn't OOM"), so a partial never
+// round-trips a full-size buffer.  In the all-gather half a finished slice
+// is final where it lands, so the successor reads it straight from this
+// rank's output buffer (NCCL's direct read of a peer's buffer) at storage
+// width instead of through a FIFO.
 //
 // Synchronisation is the MemoryChannel put / signal / wait of "MSCCL++ ...",
 // section 4 (signal after the data, wait blocks, a monotonic expected value
@@ -20,7 +22,8 @@
 //   - consumed[r][ch] written by rank r after it has read a slot
 // Both hold (epoch << 32 | count) with a per-call epoch, so values left by
 // an earlier call compare lower than anything this call waits for.  A
-// sender may run at most NS slots ahead of its receiver (backpressure).
+// sender may run at most NS FIFO slots ahead of its receiver (backpressure);
+// output slices are written once per call and need none.
 // Placement.  The grid is rank-major, workgroup b = r * Cg + ch with Cg the
 // channel count rounded up to a multiple of 8 (padding workgroups leave at
 // once).  Under the round-robin dispatch of workgroups to the 8 XCDs this
@@ -31,7 +34,8 @@
 // for plain accesses, and a CU's own cache is coherent only for its own
 // waves.  FIFO words are therefore only ever read and written with
 // device-scope (sc1) buffer instructions, coherent across CUs and XCDs
-// without flushing or invalidating any cache.  (Keeping a channel's FIFO
+// without flushing or invalidating any cache; so are the output slices a
+// successor will read.  (Keeping a channel's FIFO
 // words in its XCD's L2 with workgroup-scope accesses and a CU-cache
 // invalidate was tried: it returned stale words -- outside thread-group
 // split mode that scope does not reach another CU.)  A producer wave issues
@@ -62,6 +66,10 @@ __device__ __forceinline__ unsigned long long tag(unsigned epoch, unsigned long 
 constexpr int kSC1 = 16;  // cache-policy bit: coherent at device scope
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t fifo_rsrc(uint32_t* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+// a buffer resource over `bytes` bytes of an output buffer from byte `at`
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* base, int64_t at, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((char*)base + at, (short)0, (int)bytes, 0x00020000);
 }
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -106,6 +114,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
   const int ch = (int)(blockIdx.x % (unsigned)a.Cg);
   if (ch >= a.C) return;  // grid padding: the channel count rounded up to whole XCD rounds
   const int nxt = (r + 1 == p) ? 0 : r + 1;
+  const int prv = (r == 0) ? p - 1 : r - 1;
   const int tid = threadIdx.x;
   const unsigned epoch = a.epoch;
   const float inv_p = a.inv_p;
@@ -135,6 +144,9 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
       const bool do_send = step < 2 * p - 2;
       const bool reduce = step < p;            // reduce-scatter half (incl. the finishing step)
       const bool finish = (step == p - 1);     // the chunk completes here: post-op + output
+      const bool part_in = do_recv && reduce;  // a partial arrives through the FIFO
+      const bool part_out = step < p - 1;      // a partial leaves through the FIFO
+      const bool peer_out = do_send && !part_out;  // the output slice is what the successor reads next
       // chunk handled at this step
       int c;
       if (step < p) c = r - 1 - step;          // send0: r-1; recvReduceSend j: r-1-j; finishing: r
@@ -148,18 +160,27 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
       const int64_t e0 = s_lo + (int64_t)k * a.slot_elems;
       const int64_t e1 = min(s_hi, e0 + (int64_t)a.slot_elems);
       const int64_t len = e1 > e0 ? e1 - e0 : 0;
+      // FIFO slots are used by the reduce-scatter sends only: use u of this
+      // channel goes to slot u mod NS
+      const unsigned long long use_out = (unsigned long long)k * (p - 1) + step;
+      const unsigned long long use_in = (unsigned long long)k * (p - 1) + (step - 1);
 
-      // ---- wait for the incoming slot ----
+      // ---- wait for the incoming slot / the predecessor's finished slice ----
       if (do_recv) {
         if (!wait_geq(my_posted, tag(epoch, recvd + 1), a.spin_limit, &ok_recv)) goto timeout;
       }
-      // ---- wait for room in the successor's FIFO ----
-      if (do_send && sent + 1 > (unsigned long long)a.NS) {
-        if (!wait_geq(nx_consumed, tag(epoch, sent + 1 - a.NS), a.spin_limit, &ok_send)) goto timeout;
+      // ---- wait until the successor has drained the slot about to be refilled ----
+      if (part_out && use_out >= (unsigned long long)a.NS) {
+        const unsigned long long u = use_out - a.NS;  // the earlier use of the same slot
+        const unsigned long long drained = (u / (p - 1)) * (2 * p - 2) + (u % (p - 1)) + 1;
+        if (!wait_geq(nx_consumed, tag(epoch, drained), a.spin_limit, &ok_send)) goto timeout;
       }
-      {
-        const int in_base = (int)((recvd % a.NS) * slot_words * 4);   // byte offsets in the FIFOs
-        const int out_base = (int)((sent % a.NS) * slot_words * 4);
+      if (len > 0) {
+        const int in_base = (int)((use_in % a.NS) * slot_words * 4);   // byte offsets in the FIFOs
+        const int out_base = (int)((use_out % a.NS) * slot_words * 4);
+        // this slice of my output and of the predecessor's (device-scope access)
+        const __amdgpu_buffer_rsrc_t my_y = out_rsrc(yr, e0 * E, len * E);
+        const __amdgpu_buffer_rsrc_t pv_y = out_rsrc(a.y[prv], e0 * E, len * E);
         const bool vec = ((e0 % V) == 0);
         // phase 1: issue every load of this step (U vectors per lane)
         u32x4 xin[U];
@@ -171,22 +192,23 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
           full[u] = vec && off + V <= len;
           if (full[u]) {
             if (reduce) xin[u] = ld16(xr, (e0 + off) * E);
-            if (do_recv) {
+            if (part_in) {
 #pragma unroll
               for (int h = 0; h < V / 4; h++)
                 fin[u][h] = __builtin_amdgcn_raw_buffer_load_b128(in_rs, in_base + (int)(off + 4 * h) * 4, 0, kSC1);
+            } else if (do_recv) {  // gather: the predecessor's finished storage vector
+              fin[u][0] = __builtin_amdgcn_raw_buffer_load_b128(pv_y, (int)(off * E), 0, kSC1);
             }
           }
         }
-        // phase 2: fold, write the output and the outgoing slot
+        // phase 2: fold, write the output and the outgoing partial
 #pragma unroll
         for (int u = 0; u < U; u++) {
           const int64_t off = ((int64_t)u * kBlock + tid) * V;
           const int64_t i0 = e0 + off;
           if (full[u]) {
-            A v[V];
-            uint32_t w[V];
             if (reduce) {
+              A v[V];
               A own[V];
               unpack<DT>(xin[u], own);
               if (step == 0) {
@@ -207,46 +229,25 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
               if (finish) {
 #pragma unroll
                 for (int e = 0; e < V; e++) v[e] = O::post(v[e], p);
-                st16(yr, i0 * E, pack<DT>(v));
-#pragma unroll
-                for (int e = 0; e < V; e++) w[e] = narrow_bits<DT>(v[e]);
+                __builtin_amdgcn_raw_buffer_store_b128(pack<DT>(v), my_y, (int)(off * E), 0, kSC1);
               } else {
 #pragma unroll
-                for (int e = 0; e < V; e++) w[e] = __builtin_bit_cast(uint32_t, v[e]);
-              }
-            } else {  // gather: finished storage bits arrive; keep and forward them
+                for (int h = 0; h < V / 4; h++) {
+                  u32x4 q;
 #pragma unroll
-              for (int h = 0; h < V / 4; h++) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                  const uint32_t bits = fin[u][h][e];
-                  w[4 * h + e] = bits;
+                  for (int e = 0; e < 4; e++) q[e] = __builtin_bit_cast(uint32_t, v[4 * h + e]);
+                  __builtin_amdgcn_raw_buffer_store_b128(q, out_rs, out_base + (int)(off + 4 * h) * 4, 0, kSC1);
                 }
               }
-              u32x4 out;
-              if constexpr (E == 4) {
-#pragma unroll
-                for (int e = 0; e < 4; e++) out[e] = w[e];
-              } else {
-#pragma unroll
-                for (int e = 0; e < 4; e++) out[e] = (w[2 * e] & 0xffffu) | (w[2 * e + 1] << 16);
-              }
-              st16(yr, i0 * E, out);
-            }
-            if (do_send) {
-#pragma unroll
-              for (int h = 0; h < V / 4; h++) {
-                u32x4 q;
-#pragma unroll
-                for (int e = 0; e < 4; e++) q[e] = w[4 * h + e];
-                __builtin_amdgcn_raw_buffer_store_b128(q, out_rs, out_base + (int)(off + 4 * h) * 4, 0, kSC1);
-              }
+            } else {  // gather: keep the finished vector and pass it on through my output
+              if (peer_out) __builtin_amdgcn_raw_buffer_store_b128(fin[u][0], my_y, (int)(off * E), 0, kSC1);
+              else st16(yr, i0 * E, fin[u][0]);
             }
           } else if (off < len) {  // ragged: element by element
             const int cnt = (int)min((int64_t)V, len - off);
             for (int e = 0; e < cnt; e++) {
               const int64_t i = i0 + e;
-              uint32_t word;
+              const int yoff = (int)((off + e) * E);
               if (reduce) {
                 A val;
                 const A own = O::pre(load_elem<DT>(xr, i), inv_p);
@@ -259,25 +260,31 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
                 }
                 if (finish) {
                   val = O::post(val, p);
-                  store_elem<DT>(yr, i, val);
-                  word = narrow_bits<DT>(val);
+                  if constexpr (E == 4) __builtin_amdgcn_raw_buffer_store_b32(narrow_bits<DT>(val), my_y, yoff, 0, kSC1);
+                  else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)narrow_bits<DT>(val), my_y, yoff, 0, kSC1);
                 } else {
-                  word = __builtin_bit_cast(uint32_t, val);
+                  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), out_rs,
+                                                        out_base + (int)(off + e) * 4, 0, kSC1);
                 }
               } else {
-                word = __builtin_amdgcn_raw_buffer_load_b32(in_rs, in_base + (int)(off + e) * 4, 0, kSC1);
-                if constexpr (E == 4) ((uint32_t*)yr)[i] = word;
-                else ((uint16_t*)yr)[i] = (uint16_t)word;
+                uint32_t word;
+                if constexpr (E == 4) word = __builtin_amdgcn_raw_buffer_load_b32(pv_y, yoff, 0, kSC1);
+                else word = __builtin_amdgcn_raw_buffer_load_b16(pv_y, yoff, 0, kSC1);
+                if (peer_out) {
+                  if constexpr (E == 4) __builtin_amdgcn_raw_buffer_store_b32(word, my_y, yoff, 0, kSC1);
+                  else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)word, my_y, yoff, 0, kSC1);
+                } else {
+                  if constexpr (E == 4) ((uint32_t*)yr)[i] = word;
+                  else ((uint16_t*)yr)[i] = (uint16_t)word;
+                }
               }
-              if (do_send)
-                __builtin_amdgcn_raw_buffer_store_b32(word, out_rs, out_base + (int)(off + e) * 4, 0, kSC1);
             }
           }
         }
       }
-      // Every wave waits for its own slot stores (and loads) to complete
-      // before the barrier: a workgroup barrier alone does not wait for the
-      // other waves' memory operations, so lane 0's signal could otherwise
+      // Every wave waits for its own stores (and loads) to complete before
+      // the barrier: a workgroup barrier alone does not wait for the other
+      // waves' memory operations, so lane 0's signal could otherwise
       // overtake them.
       wait_stores();
       __syncthreads();

@@ -112,7 +112,8 @@ double model_traffic(int coll, int algo, int p, double n, int esize, const Topol
       case SIM_ALGO_ONESHOT: return 2.0 * p * S;          // p inputs read, p outputs written
       case SIM_ALGO_ALLPAIRS: return (2.0 * p + 1.0) * S;  // step 1: pS + S; step 2: S + (p-1)S
       case SIM_ALGO_ONESHOT_LL: return 6.0 * p * S;        // pack 3pS, consume 3pS
-      case SIM_ALGO_RING_FIFO: return 2.0 * p * S;         // HBM: inputs once, outputs once (FIFOs stay cached)
+      case SIM_ALGO_RING_FIFO:  // inputs and outputs once; fp32 partials through FIFOs; peer reads
+        return 2.0 * p * S + (p - 1) * n * 8.0 + (p - 1) * n * e;
       case SIM_ALGO_RING: {
         // reduce-scatter: first step in,in->part; middle part,in->part;
         // last part,in->out; partials are 4-byte accumulators.  Each step

@@ -66,8 +66,8 @@ def algorithmic_bytes(algo: str) -> float:
         n, e = N, ESIZE
         rs = n * (e + e + 4) + (P - 3) * n * (4 + e + 4) + n * (4 + e + e)
         return rs + (P - 1) * n * (e + e)
-    if algo == "ring_fifo":  # HBM-side: inputs once, outputs once (FIFO words counted apart)
-        return 2.0 * P * S
+    if algo == "ring_fifo":  # inputs and outputs once; fp32 partials through FIFOs; peer reads
+        return 2.0 * P * S + (P - 1) * N * 8.0 + (P - 1) * N * ESIZE
     raise ValueError(algo)
 
 

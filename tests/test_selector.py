@@ -74,8 +74,11 @@ def test_builtin_traffic_laws():
     assert sim.sim_model_predict("ring", 8, "bf16", S) == pytest.approx(94 * n)
     # ring, 32-bit: 5 (p-1) S
     assert sim.sim_model_predict("ring", 8, "fp32", S) == pytest.approx(35 * S)
-    # the single-launch ring: inputs read once, outputs written once
-    assert sim.sim_model_predict("ring_fifo", 8, "bf16", S) == pytest.approx(16 * S)
+    # the single-launch ring: inputs read and outputs written once (2pS), fp32
+    # partials through the FIFOs (written and read, (p-1) n 8 bytes), finished
+    # slices read from the predecessor's output ((p-1) n e bytes): 51 S at p = 8
+    assert sim.sim_model_predict("ring_fifo", 8, "bf16", S) == pytest.approx(16 * S + 7 * n * 8 + 7 * n * 2)
+    assert sim.sim_model_predict("ring_fifo", 8, "fp32", S) == pytest.approx(16 * S + 7 * (S // 4) * 12)
     sim.sim_model_reset()
 
 
