@@ -64,6 +64,17 @@ __device__ __forceinline__ unsigned long long tag(unsigned epoch, unsigned long 
 // covering one FIFO (offsets are bytes; out-of-range offsets are dropped by
 // the hardware bounds check of the resource).
 constexpr int kSC1 = 16;  // cache-policy bit: coherent at device scope
+// cache policy of the device-scope loads and stores (the build may add the
+// nontemporal bit, 2, to either)
+#ifndef SIMAR_FIFO_LOAD_AUX
+#define SIMAR_FIFO_LOAD_AUX 16
+#endif
+#ifndef SIMAR_FIFO_STORE_AUX
+#define SIMAR_FIFO_STORE_AUX 16
+#endif
+constexpr int kLd = SIMAR_FIFO_LOAD_AUX;
+constexpr int kSt = SIMAR_FIFO_STORE_AUX;
+static_assert((kLd & kSC1) && (kSt & kSC1), "FIFO and peer accesses must stay device-scope");
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t fifo_rsrc(uint32_t* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
 }
@@ -195,9 +206,9 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
             if (part_in) {
 #pragma unroll
               for (int h = 0; h < V / 4; h++)
-                fin[u][h] = __builtin_amdgcn_raw_buffer_load_b128(in_rs, in_base + (int)(off + 4 * h) * 4, 0, kSC1);
+                fin[u][h] = __builtin_amdgcn_raw_buffer_load_b128(in_rs, in_base + (int)(off + 4 * h) * 4, 0, kLd);
             } else if (do_recv) {  // gather: the predecessor's finished storage vector
-              fin[u][0] = __builtin_amdgcn_raw_buffer_load_b128(pv_y, (int)(off * E), 0, kSC1);
+              fin[u][0] = __builtin_amdgcn_raw_buffer_load_b128(pv_y, (int)(off * E), 0, kLd);
             }
           }
         }
@@ -229,18 +240,18 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
               if (finish) {
 #pragma unroll
                 for (int e = 0; e < V; e++) v[e] = O::post(v[e], p);
-                __builtin_amdgcn_raw_buffer_store_b128(pack<DT>(v), my_y, (int)(off * E), 0, kSC1);
+                __builtin_amdgcn_raw_buffer_store_b128(pack<DT>(v), my_y, (int)(off * E), 0, kSt);
               } else {
 #pragma unroll
                 for (int h = 0; h < V / 4; h++) {
                   u32x4 q;
 #pragma unroll
                   for (int e = 0; e < 4; e++) q[e] = __builtin_bit_cast(uint32_t, v[4 * h + e]);
-                  __builtin_amdgcn_raw_buffer_store_b128(q, out_rs, out_base + (int)(off + 4 * h) * 4, 0, kSC1);
+                  __builtin_amdgcn_raw_buffer_store_b128(q, out_rs, out_base + (int)(off + 4 * h) * 4, 0, kSt);
                 }
               }
             } else {  // gather: keep the finished vector and pass it on through my output
-              if (peer_out) __builtin_amdgcn_raw_buffer_store_b128(fin[u][0], my_y, (int)(off * E), 0, kSC1);
+              if (peer_out) __builtin_amdgcn_raw_buffer_store_b128(fin[u][0], my_y, (int)(off * E), 0, kSt);
               else st16(yr, i0 * E, fin[u][0]);
             }
           } else if (off < len) {  // ragged: element by element
@@ -255,24 +266,24 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
                   val = own;
                 } else {
                   const uint32_t bits =
-                      __builtin_amdgcn_raw_buffer_load_b32(in_rs, in_base + (int)(off + e) * 4, 0, kSC1);
+                      __builtin_amdgcn_raw_buffer_load_b32(in_rs, in_base + (int)(off + e) * 4, 0, kLd);
                   val = O::comb(__builtin_bit_cast(A, bits), own);
                 }
                 if (finish) {
                   val = O::post(val, p);
-                  if constexpr (E == 4) __builtin_amdgcn_raw_buffer_store_b32(narrow_bits<DT>(val), my_y, yoff, 0, kSC1);
-                  else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)narrow_bits<DT>(val), my_y, yoff, 0, kSC1);
+                  if constexpr (E == 4) __builtin_amdgcn_raw_buffer_store_b32(narrow_bits<DT>(val), my_y, yoff, 0, kSt);
+                  else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)narrow_bits<DT>(val), my_y, yoff, 0, kSt);
                 } else {
                   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), out_rs,
-                                                        out_base + (int)(off + e) * 4, 0, kSC1);
+                                                        out_base + (int)(off + e) * 4, 0, kSt);
                 }
               } else {
                 uint32_t word;
-                if constexpr (E == 4) word = __builtin_amdgcn_raw_buffer_load_b32(pv_y, yoff, 0, kSC1);
-                else word = __builtin_amdgcn_raw_buffer_load_b16(pv_y, yoff, 0, kSC1);
+                if constexpr (E == 4) word = __builtin_amdgcn_raw_buffer_load_b32(pv_y, yoff, 0, kLd);
+                else word = __builtin_amdgcn_raw_buffer_load_b16(pv_y, yoff, 0, kLd);
                 if (peer_out) {
-                  if constexpr (E == 4) __builtin_amdgcn_raw_buffer_store_b32(word, my_y, yoff, 0, kSC1);
-                  else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)word, my_y, yoff, 0, kSC1);
+                  if constexpr (E == 4) __builtin_amdgcn_raw_buffer_store_b32(word, my_y, yoff, 0, kSt);
+                  else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)word, my_y, yoff, 0, kSt);
                 } else {
                   if constexpr (E == 4) ((uint32_t*)yr)[i] = word;
                   else ((uint16_t*)yr)[i] = (uint16_t)word;
