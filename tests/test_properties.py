@@ -1,0 +1,308 @@
+"""Property tests (hypothesis, CPU only).
+
+- Oracle invariants over p, n, dtype, op and schedule (topology schedules
+  included): every rank holds the same bits; exact ops equal the plain
+  definition; on inputs whose every partial sum is exact, all schedules
+  agree with the exact sum.
+- The symbolic verifier against an independent interpreter: random
+  mutations of lowered schedules are run through a small Python model of
+  the transfer semantics written from the header's description; the
+  library's verdict must match the model's (a schedule is correct iff
+  every output slot ends with the unmutated schedule's proven fold, with no
+  step hazard and no finished value folded again).
+- The selector picks the argmin of its own predictions over the legal
+  single-node schedules.
+"""
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import all_reduce_reduction_amd as sim
+
+SINGLE = ["ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"]
+
+
+def _topologies(p):
+    out = [("tree", 1, 2), ("hier", 1, 2), ("hier_large", 1, 2)]
+    for g in range(2, p + 1):
+        if p % g == 0:
+            out += [("tree", g, 2), ("hier", g, 2), ("hier_large", g, 2)]
+    for k in range(2, p + 1):
+        v = 1
+        while v < p:
+            v *= k
+        if v == p:
+            out.append(("rexch", 1, k))
+    return out
+
+
+@st.composite
+def oracle_case(draw):
+    p = draw(st.integers(2, 8))
+    n = draw(st.integers(0, 200))
+    dtype = draw(st.sampled_from(["int32", "fp32", "fp16", "bf16"]))
+    op = draw(st.sampled_from(["sum", "prod", "min", "max", "avg"]))
+    choices = [(a, 1, 2) for a in SINGLE] + _topologies(p)
+    algo, g, k = draw(st.sampled_from(choices))
+    seed = draw(st.integers(0, 2 ** 31))
+    return p, n, dtype, op, algo, g, k, seed
+
+
+def _inputs(p, n, dtype, op, seed, orc):
+    rng = np.random.default_rng(seed)
+    if dtype == "int32":
+        return [rng.integers(-(2 ** 31), 2 ** 31 - 1, n, endpoint=True, dtype=np.int32) for _ in range(p)]
+    x = [(rng.uniform(0.5, 2.0, n) if op == "prod" else rng.standard_normal(n)).astype(np.float32)
+         for _ in range(p)]
+    if dtype == "fp32":
+        return x
+    if dtype == "fp16":
+        return [v.astype(np.float16).view(np.uint16) for v in x]
+    return [orc.f32_to_bf16(v) for v in x]
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(oracle_case())
+def test_oracle_invariants(orc, case):
+    p, n, dtype, op, algo, g, k, seed = case
+    xs = _inputs(p, n, dtype, op, seed, orc)
+    ys, _ = orc.allreduce(xs, dtype, op, algo, ranks_per_node=g, radix=k)
+    for y in ys[1:]:
+        assert y.tobytes() == ys[0].tobytes(), (algo, g, k)
+    if dtype == "int32" or op in ("min", "max"):
+        assert ys[0].tobytes() == orc.definition(xs, dtype, op).tobytes(), (algo, op)
+    if n:
+        idx = np.arange(n, dtype=np.int64)
+        assert orc.allreduce_at(xs, dtype, op, algo, idx, ranks_per_node=g, radix=k).tobytes() == ys[0].tobytes()
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.function_scoped_fixture])
+@given(st.integers(2, 8), st.integers(1, 120), st.integers(0, 2 ** 31))
+def test_exact_inputs_agree_across_schedules(orc, p, n, seed):
+    rng = np.random.default_rng(seed)
+    xs = [(rng.integers(-2048, 2048, n) / np.float32(16)).astype(np.float32) for _ in range(p)]
+    exact = [sum(Fraction(float(x[i])) for x in xs) for i in range(n)]
+    for algo, g, k in [(a, 1, 2) for a in SINGLE] + _topologies(p):
+        ys, _ = orc.allreduce(xs, "fp32", "sum", algo, ranks_per_node=g, radix=k)
+        assert [Fraction(float(v)) for v in ys[0]] == exact, (algo, g, k)
+
+
+# ---------------------------------------------------------------------------
+# The verifier against an independent model of the transfer semantics.
+# ---------------------------------------------------------------------------
+REDUCE, REDUCE_POST, COPY, GATHER_REDUCE, FANOUT, ONESHOT, GATHER, GATHER_POST, EXCH, EXCH_POST, MCAST = range(11)
+
+
+class Bad(Exception):
+    pass
+
+
+def _members(mask, p):
+    return [q for q in range(p) if (mask >> q) & 1]
+
+
+def _rw(x, p):
+    kind, src, dst, c, mask = x
+    rd, wr = [], []
+    if kind in (REDUCE, REDUCE_POST):
+        rd, wr = [(src, c), (dst, c)], [(dst, c)]
+    elif kind == COPY:
+        rd, wr = [(src, c)], ([] if src == dst else [(dst, c)])
+    elif kind == GATHER_REDUCE:
+        rd, wr = [(q, c) for q in range(p)], [(dst, c)]
+    elif kind == FANOUT:
+        rd, wr = [(src, c)], [(r, c) for r in range(p) if r != src]
+    elif kind == ONESHOT:
+        rd = wr = [(q, c) for q in range(p)]
+    elif kind in (GATHER, GATHER_POST):
+        rd, wr = [(dst, c)] + [(q, c) for q in _members(mask, p)], [(dst, c)]
+    elif kind in (EXCH, EXCH_POST):
+        rd, wr = [(q, c) for q in _members(mask, p)], [(dst, c)]
+    elif kind == MCAST:
+        rd, wr = [(src, c)], [(q, c) for q in _members(mask, p)]
+    return rd, wr
+
+
+def _valid(x, p, nch):
+    kind, src, dst, c, mask = x
+    ok = lambda r: 0 <= r < p  # noqa: E731
+    if not 0 <= c < nch or mask >> p:
+        return False
+    if kind in (REDUCE, REDUCE_POST):
+        return ok(src) and ok(dst) and src != dst
+    if kind == COPY:
+        return ok(src) and ok(dst)
+    if kind == GATHER_REDUCE:
+        return ok(dst)
+    if kind == FANOUT:
+        return ok(src)
+    if kind == ONESHOT:
+        return True
+    if kind in (GATHER, GATHER_POST):
+        return ok(dst) and mask != 0 and not (mask >> dst) & 1
+    if kind in (EXCH, EXCH_POST):
+        return ok(dst) and bool((mask >> dst) & 1)
+    if kind == MCAST:
+        return ok(src) and mask != 0 and not (mask >> src) & 1
+    return False
+
+
+def _fold(vals):
+    """Values are (expr, mask, finished); fold left, refusing overlaps and
+    finished operands."""
+    e, m, f = vals[0]
+    if f:
+        raise Bad("finished operand")
+    for e2, m2, f2 in vals[1:]:
+        if f2 or m & m2:
+            raise Bad("finished or duplicate")
+        e, m = f"({e}+{e2})", m | m2
+    return e, m, False
+
+
+def _interpret(steps, p, nch):
+    """Final slot values, or raise Bad."""
+    slot = {(r, c): (str(r), 1 << r, False) for r in range(p) for c in range(nch)}
+    for xs in steps:
+        writer = {}
+        for i, x in enumerate(xs):
+            if not _valid(x, p, nch):
+                raise Bad("invalid")
+            for w in _rw(x, p)[1]:
+                if w in writer:
+                    raise Bad("double write")
+                writer[w] = i
+        for i, x in enumerate(xs):
+            for r in _rw(x, p)[0]:
+                j = writer.get(r, i)
+                if j != i:
+                    y = xs[j]
+                    same_group = x[0] in (EXCH, EXCH_POST) and x[0] == y[0] and x[3] == y[3] and x[4] == y[4]
+                    if not same_group:
+                        raise Bad("hazard")
+        before = dict(slot)
+        for kind, src, dst, c, mask in xs:
+            B = lambda q: before[(q, c)]  # noqa: E731
+            if kind in (REDUCE, REDUCE_POST):
+                e, m, _ = _fold([B(src), B(dst)])
+                slot[(dst, c)] = (e, m, kind == REDUCE_POST)
+            elif kind == COPY:
+                slot[(dst, c)] = B(src)
+            elif kind in (GATHER_REDUCE, ONESHOT):
+                e, m, _ = _fold([B(c)] + [B(q) for q in range(p) if q != c])
+                for r in ([dst] if kind == GATHER_REDUCE else range(p)):
+                    slot[(r, c)] = (e, m, True)
+            elif kind == FANOUT:
+                for r in range(p):
+                    if r != src:
+                        slot[(r, c)] = B(src)
+            elif kind in (GATHER, GATHER_POST, EXCH, EXCH_POST):
+                ops = ([B(dst)] if kind in (GATHER, GATHER_POST) else []) + [B(q) for q in _members(mask, p)]
+                e, m, _ = _fold(ops)
+                slot[(dst, c)] = (e, m, kind in (GATHER_POST, EXCH_POST))
+            elif kind == MCAST:
+                if not B(src)[2]:
+                    raise Bad("unfinished broadcast")
+                for q in _members(mask, p):
+                    slot[(q, c)] = B(src)
+    return slot
+
+
+ALGO_SETUPS = [("ring", 1, 2), ("allpairs", 1, 2), ("oneshot", 1, 2), ("tree", 1, 2), ("tree", 2, 2),
+               ("rexch", 1, 2), ("hier", 2, 2), ("hier_large", 4, 2)]
+
+
+@st.composite
+def mutated_schedule(draw):
+    algo, g, k = draw(st.sampled_from(ALGO_SETUPS))
+    p = draw(st.sampled_from([4, 8]))
+    return algo, g, k, p, draw(st.integers(0, 2 ** 31)), draw(st.integers(1, 3))
+
+
+def _mutate(steps, p, nch, rng, count):
+    steps = [list(s) for s in steps]
+    for _ in range(count):
+        what = rng.randrange(6)
+        s = rng.randrange(len(steps))
+        if what == 0 and steps[s]:                       # drop a transfer
+            del steps[s][rng.randrange(len(steps[s]))]
+        elif what == 1 and len(steps) > 1:               # swap two steps
+            t = rng.randrange(len(steps))
+            steps[s], steps[t] = steps[t], steps[s]
+        elif what == 2 and steps[s]:                     # change a field
+            i = rng.randrange(len(steps[s]))
+            x = list(steps[s][i])
+            f = rng.choice([1, 2, 3, 4])
+            if f == 3:
+                x[3] = rng.randrange(nch)
+            elif f == 4:
+                x[4] ^= 1 << rng.randrange(p)
+            else:
+                x[f] = rng.randrange(p) if x[f] >= 0 else x[f]
+            steps[s][i] = tuple(x)
+        elif what == 3 and steps[s]:                     # duplicate a transfer into another step
+            t = rng.randrange(len(steps))
+            steps[t].append(steps[s][rng.randrange(len(steps[s]))])
+        elif what == 4 and steps[s]:                     # flip post-processing
+            i = rng.randrange(len(steps[s]))
+            x = list(steps[s][i])
+            flip = {REDUCE: REDUCE_POST, REDUCE_POST: REDUCE, GATHER: GATHER_POST, GATHER_POST: GATHER,
+                    EXCH: EXCH_POST, EXCH_POST: EXCH}
+            x[0] = flip.get(x[0], x[0])
+            steps[s][i] = tuple(x)
+        elif what == 5 and len(steps) > 1:               # merge two steps
+            t = rng.randrange(len(steps))
+            if t != s:
+                steps[s] += steps[t]
+                del steps[t]
+    return steps
+
+
+@settings(max_examples=300, deadline=None)
+@given(mutated_schedule())
+def test_verifier_agrees_with_independent_model(case):
+    algo, g, k, p, seed, count = case
+    sim.sim_config_set("ranks_per_node", g)
+    sim.sim_config_set("radix", k)
+    try:
+        nsteps, _, nch = sim.sim_schedule_info(algo, p)
+        base = [sim.sim_schedule_xfers(algo, p, s) for s in range(nsteps)]
+        want = _interpret(base, p, nch)  # the unmutated, proven schedule's final slots
+        full = (1 << p) - 1
+        assert all(m == full and f for (_, m, f) in want.values())
+        steps = _mutate(base, p, nch, random.Random(seed), count)
+        try:
+            got = _interpret(steps, p, nch)
+            model_ok = got == want
+        except Bad:
+            model_ok = False
+        rounds = len(steps) if algo not in ("oneshot", "allpairs") else 2
+        if len(steps) != nsteps and algo not in ("oneshot", "allpairs"):
+            model_ok = False  # one step per round: the closed-form count is part of the contract
+        st_, diag = sim.sim_verify_custom(algo, p, steps, nchunks=nch, rounds=rounds)
+        assert (st_ == 0) == model_ok, (algo, p, g, k, seed, count, diag)
+    finally:
+        sim.sim_config_set("ranks_per_node", 1)
+        sim.sim_config_set("radix", 2)
+
+
+# ---------------------------------------------------------------------------
+@settings(max_examples=100, deadline=None)
+@given(st.integers(2, 16), st.integers(1, 1 << 28), st.sampled_from(["int32", "fp32", "fp16", "bf16"]))
+def test_selector_picks_its_own_argmin(p, nbytes, dtype):
+    esize = sim.ESIZE[dtype]
+    n = max(1, nbytes // esize)
+    pick, pred = sim.sim_select(p, n, dtype)
+    best = None
+    for a in SINGLE:
+        if a == "oneshot_ll" and n * esize > sim.LL_MAX_BYTES_PER_RANK:
+            continue
+        t = sim.sim_model_predict(a, p, dtype, n * esize)
+        if best is None or t < best[1]:
+            best = (a, t)
+    assert pred == pytest.approx(best[1])
+    assert sim.sim_model_predict(pick, p, dtype, n * esize) == pytest.approx(best[1])
