@@ -237,6 +237,22 @@ def main():
         sim.sim_config_set("ranks_per_node", 1)
         sim.sim_config_set("radix", 2)
         extras["per_algo"] = per_algo
+        # reduce-scatter then all-gather vs the all-reduce of the same schedule
+        # (the ring all-reduce is exactly these two halves back to back)
+        n_out = N // P
+        rs_out = [torch.empty(n_out, dtype=torch.int16, device=dev) for _ in range(P)]
+        rs_p = [t_.data_ptr() for t_ in rs_out]
+        rs_ag = {}
+        for a in ("ring", "allpairs"):
+            def rs_then_ag(a=a):
+                if sim.sim_reduce_scatter(ip, rs_p, P, n_out, "bf16", "sum", a, stream):
+                    raise sim.SimError(-1, "sim_reduce_scatter")
+                if sim.sim_all_gather(rs_p, op_, P, n_out, "bf16", a, stream):
+                    raise sim.SimError(-1, "sim_all_gather")
+            tr = time_calls(rs_then_ag, max(10, args.steps // 4), 5)
+            rs_ag[a] = {"rs_plus_ag_us": round(tr * 1e6, 2), "allreduce_us": per_algo[a]["us"],
+                        "ratio": round(tr * 1e6 / per_algo[a]["us"], 3)}
+        extras["rs_then_ag_vs_allreduce"] = rs_ag
         # small-message latency: 8 KiB per rank, fp16
         lx = synthdata.workload_inputs(4, P, LAT_N, "fp16")
         lin = [torch.from_numpy(x.view(np.int16)).to(dev) for x in lx]
