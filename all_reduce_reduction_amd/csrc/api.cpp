@@ -57,6 +57,9 @@ struct Ctx {
   int fifo_slots = 4;
   int fifo_withhold = 0;  // test hook: rank 0's workgroups leave at once
   int fifo_vecs = kFifoVecsPerLane;  // 16-byte vectors per lane per slot: 1, 2 or 4
+  bool capturing = false;  // the current call's stream is being captured into a graph
+  bool captured = false;   // some call has been captured since sim_init
+  std::vector<void*> retired;  // outgrown scratch a captured graph may still use
 
   int fifo_occ[4][5] = {};
   Model model = default_model();
@@ -143,11 +146,21 @@ size_t slot_elems(size_t n, int p) {
 }
 size_t scratch_need(size_t n, int p) { return 2 * (size_t)p * slot_elems(n, p) * 4; }
 
+// Grow the partial scratch.  Under stream capture it cannot grow (that would
+// allocate, and the captured graph would keep the new address); once any
+// call has been captured, an outgrown buffer is retired instead of freed,
+// since a graph may still replay kernels that use it (all are freed by
+// sim_finalize).
 int ensure_scratch(size_t bytes) {
   if (bytes <= g.scratch_bytes) return SIM_OK;
+  if (g.capturing) return SIM_ERR_UNSUPPORTED;
   if (g.scratch) {
-    if (hipDeviceSynchronize() != hipSuccess) return SIM_ERR_HIP;
-    if (hipFree(g.scratch) != hipSuccess) return SIM_ERR_HIP;
+    if (g.captured) {
+      g.retired.push_back(g.scratch);
+    } else {
+      if (hipDeviceSynchronize() != hipSuccess) return SIM_ERR_HIP;
+      if (hipFree(g.scratch) != hipSuccess) return SIM_ERR_HIP;
+    }
     g.scratch = nullptr;
     g.scratch_bytes = 0;
   }
@@ -630,6 +643,9 @@ int run_all_gather(const Call& c) {
 
 // legal candidates for AUTO / explicit requests
 bool legal(int coll, int algo, int p, size_t n, int dtype) {
+  // LL and the single-launch ring carry a per-call epoch in their kernel
+  // arguments: a replayed graph would repeat it and accept stale flags
+  if (g.capturing && (algo == SIM_ALGO_ONESHOT_LL || algo == SIM_ALGO_RING_FIFO)) return false;
   if (coll == COLL_ALLREDUCE) {
     if (algo == SIM_ALGO_ONESHOT_LL) return n * (size_t)esize_of(dtype) <= SIM_LL_MAX_BYTES_PER_RANK;
     if (is_topology_algo(algo)) return cached_schedule(coll, algo, p, g_topo, nullptr) != nullptr;
@@ -663,6 +679,18 @@ int resolve_algo(int coll, int p, size_t n, int dtype, int* algo, double* us) {
   if (*algo == SIM_ALGO_AUTO) return pick(coll, p, n, dtype, algo, us);
   if (!legal(coll, *algo, p, n, dtype)) return SIM_ERR_UNSUPPORTED;
   if (us) *us = model_predict(g.model, coll, *algo, p, (double)n, esize_of(dtype), g_topo);
+  return SIM_OK;
+}
+
+// Is `s` being captured into a graph?  Sets g.capturing for the current call.
+int begin_call(void* stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing((hipStream_t)stream, &st) != hipSuccess) {
+    (void)hipGetLastError();
+    return SIM_ERR_HIP;
+  }
+  g.capturing = (st != hipStreamCaptureStatusNone);
+  if (g.capturing) g.captured = true;
   return SIM_OK;
 }
 
@@ -711,6 +739,7 @@ int sim_finalize(void) {
   (void)hipSetDevice(g.device);
   (void)hipDeviceSynchronize();
   if (g.scratch) (void)hipFree(g.scratch);
+  for (void* r : g.retired) (void)hipFree(r);
   if (g.ll) (void)hipFree(g.ll);
   if (g.fifo) (void)hipFree(g.fifo);
   if (g.fifo_sem) (void)hipFree(g.fifo_sem);
@@ -791,9 +820,11 @@ int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size
   rc = check_buffers(in_ptrs, out_ptrs, p, n * e, n * e, std::vector<size_t>(p, 0), &inplace);
   if (rc) return rc;
   double us = 0;
+  if (use_device() != SIM_OK) return SIM_ERR_HIP;
+  rc = begin_call(stream);
+  if (rc) return rc;
   rc = resolve_algo(COLL_ALLREDUCE, p, n, dtype, &algo, &us);
   if (rc) return rc;
-  if (use_device() != SIM_OK) return SIM_ERR_HIP;
   Call c{COLL_ALLREDUCE, p, dtype, op, algo, n, in_ptrs, out_ptrs, inplace, (hipStream_t)stream};
   rc = run_allreduce(c);
   if (rc) return rc;
@@ -842,6 +873,8 @@ int sim_reduce_scatter(const void* const* in_ptrs, void* const* out_ptrs, int p,
     if (ip2) return SIM_ERR_ALIAS;
   }
   if (use_device() != SIM_OK) return SIM_ERR_HIP;
+  rc = begin_call(stream);
+  if (rc) return rc;
   Call c{COLL_REDUCE_SCATTER, p, dtype, op, algo, (size_t)p * n_out, in_ptrs, out_ptrs, inplace,
          (hipStream_t)stream};
   rc = run_reduce_scatter(c);
@@ -889,6 +922,8 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p, siz
       }
   }
   if (use_device() != SIM_OK) return SIM_ERR_HIP;
+  rc = begin_call(stream);
+  if (rc) return rc;
   Call c{COLL_ALL_GATHER, p, dtype, SIM_SUM, algo, (size_t)p * n_in, in_ptrs, out_ptrs, inplace,
          (hipStream_t)stream};
   rc = run_all_gather(c);
@@ -904,6 +939,7 @@ int sim_select(int p, size_t n, int dtype, int op, int* algo_out, double* predic
   if (dtype < SIM_INT32 || dtype > SIM_BF16 || op < SIM_SUM || op > SIM_AVG) return SIM_ERR_INVALID_ARG;
   int a = SIM_ALGO_AUTO;
   double us = 0;
+  g.capturing = false;  // the pick of an ordinary (not captured) call
   int rc = resolve_algo(COLL_ALLREDUCE, p, n, dtype, &a, &us);
   if (rc) return rc;
   *algo_out = a;

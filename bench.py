@@ -18,6 +18,8 @@ Printed JSON line:
                  recursive-exchange and 2PH ones at a stated topology)
   latency_8KiB   per-call microseconds at 8 KiB per rank (p = 8, fp16):
                  plain one-shot vs the LL packet path vs the selector's pick
+                 (and, as latency_8KiB_graph_us, calls replayed from a
+                 captured HIP graph)
   cpu_baseline   the CPU oracle on the same host arrays (all host threads)
 """
 from __future__ import annotations
@@ -277,6 +279,24 @@ def main():
         sim.sim_config_set("radix", 2)
         assert sim.sim_check_error(stream) == 0
         extras["latency_8KiB_us"] = lat
+        # the same calls replayed from a captured graph (20 calls per graph):
+        # no host work per call; multi-launch schedules keep their launches
+        glat = {}
+        for a in ("oneshot", "allpairs", "ring", "tree"):
+            graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(graph, stream=side):
+                    cs = int(torch.cuda.current_stream().cuda_stream)
+                    for _ in range(20):
+                        if sim.sim_allreduce(lip, lop, P, LAT_N, "fp16", "sum", a, cs):
+                            raise sim.SimError(-1, f"captured sim_allreduce({a})")
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            glat[a] = round(time_calls(graph.replay, 100, 10) * 1e6 / 20, 2)
+            del graph
+        extras["latency_8KiB_graph_us"] = glat
 
     cpu = None
     if not args.no_cpu_baseline:

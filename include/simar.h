@@ -42,6 +42,16 @@
  *   - One host thread per process drives the library (no internal locking).
  *     Calls make the library's device (the one given to sim_init) current
  *     on the calling thread when another one is.
+ *   - Graph capture: a collective enqueued on a stream that is being
+ *     captured (hipStreamBeginCapture, torch.cuda.graph) is recorded like
+ *     any other kernel launch and may be replayed.  SIM_ALGO_ONESHOT_LL and
+ *     SIM_ALGO_RING_FIFO carry a per-call epoch in their kernel arguments,
+ *     which a replay would repeat: under capture they are
+ *     SIM_ERR_UNSUPPORTED and AUTO skips them.  Library scratch cannot grow
+ *     during capture (SIM_ERR_UNSUPPORTED): size it with sim_init's
+ *     max_bytes_per_rank or make one uncaptured call of the same shape
+ *     first.  Once a call has been captured, outgrown scratch is kept until
+ *     sim_finalize, so recorded graphs stay valid until then (not after).
  *
  * Results: int32 and fp32 results are bit-exact functions of the schedule:
  * ring chunk c (both ring executions) folds ranks c+1, c+2, ..., c+p
