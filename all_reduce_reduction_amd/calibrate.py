@@ -10,7 +10,9 @@ message sizes that sits BETWEEN the evaluation sizes (powers of two times
 squares with relative weights (so microsecond and millisecond points count
 alike), and writes the JSON file sim_model_load() reads.
 
-The fit is a two-regime estimate (see fit()).  --check then times every legal schedule at the evaluation sizes (8192 x
+The fit is a two-regime estimate (see fit()).  A launch-configuration sweep
+(sweep_workgroups) then stores the best total workgroups per size for the
+bulk schedules.  --check then times every legal schedule at the evaluation sizes (8192 x
 {1, 16, 256, 4096} tokens bf16, and 1 KiB .. 1 MiB fp16) and compares the
 selector's pick with the measured fastest: a strict match, and a tolerant
 match when the pick is within max(3%, the measured spread) of the best.
@@ -123,6 +125,42 @@ def fit(points, algo):
     return alpha, 1.0 / inv_b / 1e3  # bytes/us -> GB/s
 
 
+# Launch-configuration sweep (after T-CCL's offline ranking of CTA
+# configurations per collective and size, section III-C3): the bulk
+# schedules at each grid size with a range of total workgroups; 0 is the
+# library's default (one workgroup per kBlock vectors, covering the
+# transfer).  The best total per size goes into the calibration file; a
+# total within 1% of the default's time keeps the default.
+WG_ALGOS = ("oneshot", "allpairs", "ring")
+WG_TOTALS = (0, 256, 512, 1024, 2048, 4096, 8192, 16384)
+
+
+def sweep_workgroups(sim, b, sizes):
+    table = {}
+    raw = {}
+    for algo in WG_ALGOS:
+        rows = []
+        for nbytes in sizes:
+            if nbytes < (96 << 10):
+                continue
+            n = nbytes // 2
+            times = {}
+            for total in WG_TOTALS:
+                sim.sim_debug_set("workgroups", total)
+                times[total] = b.measure(algo, "bf16", n)[0]
+            sim.sim_debug_set("workgroups", 0)
+            best = min(times, key=times.get)
+            if times[best] >= times[0] * 0.99:
+                best = 0
+            rows.append([nbytes, best])
+            raw.setdefault(algo, []).append({"bytes_per_rank": nbytes,
+                                             "us": {str(k): round(v, 3) for k, v in times.items()}})
+            print(f"workgroups {algo:9s} {nbytes:>10d} B/rank best {best:6d} "
+                  + " ".join(f"{k}={v:.1f}" for k, v in times.items()), flush=True)
+        table[algo] = rows
+    return table, raw
+
+
 def calibrate(out_path: str):
     import all_reduce_reduction_amd as sim
     sim.sim_init(0, P, 0)
@@ -151,10 +189,13 @@ def calibrate(out_path: str):
         raw.setdefault("fit", {})[algo] = {"alpha_us": alpha, "gbps": gbps}
     set_topology(sim, "ring")
     sim.sim_model_reset()
+    wg_table, wg_raw = sweep_workgroups(sim, b, sizes)
     model = {"device": "MI355X (gfx950)", "p": P, "dtype": "bf16",
              "grid": "1.5 x 2^k bytes per rank, k = 10..27",
              "topology": {a: {"ranks_per_node": g, "radix": k} for a, (g, k) in TOPOLOGY.items()},
-             "algos": raw["fit"], "measurements": {a: raw[a] for a in ALGOS + tuple(TOPOLOGY) if a in raw}}
+             "algos": raw["fit"], "workgroups": wg_table,
+             "measurements": {a: raw[a] for a in ALGOS + tuple(TOPOLOGY) if a in raw},
+             "workgroup_measurements": wg_raw}
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
         json.dump(model, f, indent=1)

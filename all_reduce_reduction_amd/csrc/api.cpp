@@ -79,6 +79,8 @@ bool is_topology_algo(int a) { return a >= SIM_ALGO_TREE && a <= SIM_ALGO_HIER_L
 // The simulated topology of the tree / recursive-exchange / 2PH schedules:
 // process-wide, kept across sim_init.
 Topology g_topo;
+// Workgroup budget of one launch (0: none); process-wide like the topology.
+int g_max_wg = 0;
 
 int64_t chunk_lo(int64_t n, int p, int c) { return (int64_t)(((__int128)c * n) / p); }
 
@@ -178,16 +180,6 @@ float inv_p_of(int p) {
   return one / fp;
 }
 
-// Workgroups per transfer (gridDim.x).  Measured on MI355X: streaming
-// kernels run fastest with one short-lived workgroup per kBlock * unroll
-// vectors (many waves in flight, no grid-stride loop), so the default covers
-// the transfer exactly; SIM_DEBUG_WORKGROUPS forces a total instead.
-int tiles_for(int64_t vecs_per_unit, int units, int unroll) {
-  if (g.force_wg > 0) return (int)std::max<int64_t>(1, g.force_wg / units);
-  const int64_t want = (vecs_per_unit + (int64_t)kBlock * unroll - 1) / ((int64_t)kBlock * unroll);
-  return (int)std::max<int64_t>(1, std::min<int64_t>(want, kMaxTiles));
-}
-
 // ---- launch glue ----------------------------------------------------------------
 struct Call {
   int coll, p, dtype, op, algo;
@@ -197,6 +189,28 @@ struct Call {
   bool inplace;
   hipStream_t s;
 };
+
+// Workgroups per transfer (gridDim.x) of a bulk kernel; every bulk kernel
+// walks its transfer with a grid-stride loop, so any count >= 1 is correct.
+// Measured on MI355X: streaming kernels run fastest with one short-lived
+// workgroup per kBlock * unroll vectors (many waves in flight), so the
+// default covers the transfer exactly.  The calibration's launch table, when
+// it has an entry for this algo, replaces that with the measured best total
+// for the nearest message size; SIM_CONFIG_MAX_WORKGROUPS caps the total
+// (T-CCL's restricted mode: communication given a fixed slice of the GPU);
+// SIM_DEBUG_WORKGROUPS forces a total.
+int tiles_for(const Call& c, int64_t vecs_per_unit, int units, int unroll) {
+  int64_t t;
+  if (g.force_wg > 0) {
+    t = g.force_wg / units;
+  } else {
+    t = (vecs_per_unit + (int64_t)kBlock * unroll - 1) / ((int64_t)kBlock * unroll);
+    const int total = model_workgroups(g.model, c.algo, (double)c.n * esize_of(c.dtype));
+    if (total > 0) t = std::min<int64_t>(t, std::max(1, total / units));
+  }
+  if (g_max_wg > 0) t = std::min<int64_t>(t, g_max_wg / units);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(t, kMaxTiles));
+}
 
 int run_fold(const Call& c, bool all_out, const std::vector<int64_t>& lo, const int64_t* out_shift) {
   FoldArgs a;
@@ -214,7 +228,7 @@ int run_fold(const Call& c, bool all_out, const std::vector<int64_t>& lo, const 
   a.p = c.p;
   a.inv_p = inv_p_of(c.p);
   const int unroll = (c.p == 8) ? g.unroll : 1;
-  a.tiles = tiles_for((maxchunk + V - 1) / V, c.p, unroll);
+  a.tiles = tiles_for(c, (maxchunk + V - 1) / V, c.p, unroll);
   return hip_err(launch_fold(c.dtype, c.op, c.p, all_out, a, unroll, c.s));
 }
 
@@ -230,7 +244,7 @@ int run_copy_step(const Call& c, const std::vector<CopyXfer>& xs) {
     maxlen = std::max(maxlen, xs[k].hi - xs[k].lo);
   }
   if (a.nx == 0) return SIM_OK;
-  a.tiles = tiles_for((maxlen + V - 1) / V, a.nx, g.unroll);
+  a.tiles = tiles_for(c, (maxlen + V - 1) / V, a.nx, g.unroll);
   return hip_err(launch_copy(e, a, g.unroll, c.s));
 }
 
@@ -288,7 +302,7 @@ int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_c
       }
       x.vec_ok = (x.a_shift % V == 0) && (x.d_shift % V == 0);
     }
-    a.tiles = tiles_for((maxchunk + V - 1) / V, a.nx, g.unroll);
+    a.tiles = tiles_for(c, (maxchunk + V - 1) / V, a.nx, g.unroll);
     int rc = hip_err(launch_ring_reduce(c.dtype, c.op, !first, last, a, g.unroll, c.s));
     if (rc) return rc;
   }
@@ -316,10 +330,11 @@ int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
   int64_t C = g.fifo_channels > 0 ? g.fifo_channels : std::max<int64_t>(1, (maxchunk + slot - 1) / slot);
   C = std::min<int64_t>(C, kFifoMaxChannels);
   C = std::min<int64_t>(C, std::max<int64_t>(1, resident / p));
+  if (g_max_wg > 0) C = std::min<int64_t>(C, std::max(1, g_max_wg / p));  // at least one per rank
   // rank-major grid padded to whole rounds of the 8 XCDs (when the padded
   // grid still fits at once): the ranks of a channel run on one XCD
   int64_t Cg = (C + 7) / 8 * 8;
-  if ((int64_t)p * Cg > resident) Cg = C;
+  if ((int64_t)p * Cg > resident || g_max_wg > 0) Cg = C;  // no padding under a budget
   // slots per channel slice: the longest slice over all chunks (same formula as the kernel)
   int64_t maxslice = 0;
   for (int q = 0; q < p; q++) {
@@ -471,7 +486,7 @@ int run_sched(const Call& c, const Schedule& sch) {
         a.xf[k] = folds[b + k];
         maxlen = std::max(maxlen, a.xf[k].hi - a.xf[k].lo);
       }
-      a.tiles = tiles_for((maxlen + V - 1) / V, a.nx, 1);
+      a.tiles = tiles_for(c, (maxlen + V - 1) / V, a.nx, 1);
       int rc = hip_err(launch_sched_fold(c.dtype, c.op, a, c.s));
       if (rc) return rc;
     }
@@ -566,7 +581,9 @@ int run_allreduce(const Call& c) {
       int& occ = g.ll_occ[c.dtype][c.op];
       if (occ == 0) occ = ll_blocks_per_cu(c.dtype, c.op);
       const int64_t resident = (int64_t)occ * g.cu_count;
-      const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(a.ntiles, resident));
+      int64_t cap = resident;
+      if (g_max_wg > 0) cap = std::min<int64_t>(cap, g_max_wg);
+      const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(a.ntiles, cap));
       return hip_err(launch_ll(c.dtype, c.op, a, grid, c.s));
     }
   }
@@ -1010,6 +1027,10 @@ int sim_config_set(int key, int value) {
       if (value < 2 || value > SIM_MAX_RANKS) return SIM_ERR_INVALID_ARG;
       g_topo.radix = value;
       return SIM_OK;
+    case SIM_CONFIG_MAX_WORKGROUPS:
+      if (value < 0) return SIM_ERR_INVALID_ARG;
+      g_max_wg = value;
+      return SIM_OK;
   }
   return SIM_ERR_INVALID_ARG;
 }
@@ -1019,6 +1040,7 @@ int sim_config_get(int key, int* value) {
   switch (key) {
     case SIM_CONFIG_RANKS_PER_NODE: *value = g_topo.ranks_per_node; return SIM_OK;
     case SIM_CONFIG_RADIX: *value = g_topo.radix; return SIM_OK;
+    case SIM_CONFIG_MAX_WORKGROUPS: *value = g_max_wg; return SIM_OK;
   }
   return SIM_ERR_INVALID_ARG;
 }

@@ -74,7 +74,7 @@ constexpr int kSC1 = 16;  // cache-policy bit: coherent at device scope
 #endif
 constexpr int kLd = SIMAR_FIFO_LOAD_AUX;
 constexpr int kSt = SIMAR_FIFO_STORE_AUX;
-static_assert((kLd & kSC1) && (kSt & kSC1), "FIFO and peer accesses must stay device-scope");
+static_assert((kLd & kSC1) != 0 && (kSt & kSC1) != 0, "FIFO and peer accesses must stay device-scope");
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t fifo_rsrc(uint32_t* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
 }

@@ -11,9 +11,11 @@
 #include "select.h"
 
 #include <cctype>
+#include <cmath>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <memory>
 #include <utility>
@@ -31,15 +33,15 @@ namespace simar {
 Model default_model() {
   Model m;
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING] = {4.4, 5900.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ALLPAIRS] = {4.7, 5650.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT] = {4.3, 5750.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT_LL] = {7.9, 7050.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING_FIFO] = {32.0, 790.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING] = {4.2, 5850.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ALLPAIRS] = {4.6, 5600.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT] = {4.4, 5650.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT_LL] = {8.0, 7400.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING_FIFO] = {28.5, 4400.0, -1.0, -1.0};
   m.a[SIM_ALGO_TREE] = {4.6, 6000.0, -1.0, -1.0};
   m.a[SIM_ALGO_REXCH] = {4.3, 5250.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER] = {4.9, 5950.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER_LARGE] = {5.2, 5900.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER] = {4.9, 5850.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER_LARGE] = {5.0, 5850.0, -1.0, -1.0};
   return m;
 }
 
@@ -139,6 +141,22 @@ double model_traffic(int coll, int algo, int p, double n, int esize, const Topol
     }
   }
   return 0.0;
+}
+
+int model_workgroups(const Model& m, int algo, double bytes_per_rank) {
+  if (algo <= 0 || algo >= kNumAlgos || m.wg[algo].empty() || !(bytes_per_rank > 0)) return 0;
+  int best = 0;
+  double bd = 0;
+  bool found = false;
+  for (const auto& e : m.wg[algo]) {  // a total of 0 means: cover the transfer
+    const double d = std::fabs(std::log2(e.first) - std::log2(bytes_per_rank));
+    if (!found || d < bd) {
+      best = e.second;
+      bd = d;
+      found = true;
+    }
+  }
+  return best;
 }
 
 double model_predict(const Model& m, int coll, int algo, int p, double n, int esize, const Topology& t) {
@@ -330,6 +348,34 @@ bool model_load_json(const char* path, Model* m, std::string* err) {
     out.a[a].gbps = bw->second.num;
     out.a[a].steps = -1;
     out.a[a].bytes_factor = -1;
+  }
+  // optional launch-configuration table: "workgroups": {algo: [[bytes, total], ...]}
+  auto wt = root.obj.find("workgroups");
+  if (wt != root.obj.end()) {
+    if (wt->second.kind != JVal::OBJ) {
+      if (err) *err = "'workgroups' is not an object";
+      return false;
+    }
+    for (int a = 1; a < kNumAlgos; a++) {
+      auto ai = wt->second.obj.find(kAlgoNames[a]);
+      if (ai == wt->second.obj.end()) continue;
+      if (ai->second.kind != JVal::ARR) {
+        if (err) *err = "workgroup entry is not an array";
+        return false;
+      }
+      std::vector<std::pair<double, int>> v;
+      for (const JVal& e : ai->second.arr) {
+        if (e.kind != JVal::ARR || e.arr.size() != 2 || e.arr[0].kind != JVal::NUM ||
+            e.arr[1].kind != JVal::NUM || !(e.arr[0].num > 0) || e.arr[1].num < 0 ||
+            e.arr[1].num > (double)(1 << 24)) {
+          if (err) *err = "workgroup entries are [bytes > 0, total in 0..2^24]";
+          return false;
+        }
+        v.push_back({e.arr[0].num, (int)e.arr[1].num});
+      }
+      std::sort(v.begin(), v.end());
+      out.wg[a] = v;
+    }
   }
   out.source = path;
   *m = out;

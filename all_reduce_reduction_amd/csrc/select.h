@@ -3,6 +3,8 @@
 
 #include <cstddef>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "schedule.h"
 
@@ -19,8 +21,16 @@ struct AlgoModel {
 
 struct Model {
   AlgoModel a[kNumAlgos];
+  // Measured launch configurations (after T-CCL's ranked CTA-config table):
+  // per algo, (bytes per rank, total workgroups) pairs from the calibration
+  // sweep, ascending in bytes; empty = cover every transfer exactly.
+  std::vector<std::pair<double, int>> wg[kNumAlgos];
   std::string source = "built-in defaults";
 };
+
+// Total workgroups the table holds for (algo, bytes per rank): the entry of
+// the nearest size on a log scale; 0 when the table has none.
+int model_workgroups(const Model& m, int algo, double bytes_per_rank);
 
 Model default_model();
 

@@ -255,6 +255,14 @@ def main():
             rs_ag[a] = {"rs_plus_ag_us": round(tr * 1e6, 2), "allreduce_us": per_algo[a]["us"],
                         "ratio": round(tr * 1e6 / per_algo[a]["us"], 3)}
         extras["rs_then_ag_vs_allreduce"] = rs_ag
+        # T-CCL's restricted mode: the one-shot with a workgroup budget
+        budget = {}
+        for b in (32, 128, 512, 2048, 0):
+            sim.sim_config_set("max_workgroups", b)
+            tb = time_calls(lambda: step("oneshot"), max(10, args.steps // 4), 5)
+            budget[str(b) if b else "none"] = round(2 * (P - 1) / P * S / tb / 1e9, 1)
+        sim.sim_config_set("max_workgroups", 0)
+        extras["oneshot_busbw_by_workgroup_budget"] = budget
         # small-message latency: 8 KiB per rank, fp16
         lx = synthdata.workload_inputs(4, P, LAT_N, "fp16")
         lin = [torch.from_numpy(x.view(np.int16)).to(dev) for x in lx]

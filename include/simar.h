@@ -179,7 +179,12 @@ int sim_select(int p, size_t n, int dtype, int op, int* algo_out, double* predic
 int sim_last_algo(void);
 
 /* Load per-algo alpha (us per launch) and B (GB/s) from a JSON file
- * written by the calibration sweep.  Errors: SIM_ERR_INVALID_ARG. */
+ * written by the calibration sweep, and its optional launch table
+ * ("workgroups": {algo: [[bytes per rank, total workgroups], ...]}, after
+ * T-CCL's ranked launch-configuration table, section III-C3): bulk kernels
+ * of that algo then launch the measured best total of the nearest size
+ * (log scale), never more than covers the transfer.  Errors:
+ * SIM_ERR_INVALID_ARG (the current model is kept). */
 int sim_model_load(const char* json_path);
 
 /* Predicted time of `algo` for `bytes_per_rank` bytes per rank. */
@@ -216,8 +221,15 @@ int sim_check_error(void* stream);
  *   SIM_CONFIG_RADIX           k of the recursive exchange, 2..16, default
  *                              2; it needs p to be a power of k
  *                              (SIM_ERR_UNSUPPORTED otherwise).
+ *   SIM_CONFIG_MAX_WORKGROUPS  workgroup budget of every launch (T-CCL's
+ *                              restricted mode, "T-CCL ...", sections III-C3
+ *                              and IV-B: communication limited to a fixed
+ *                              number of thread blocks so the rest of the GPU
+ *                              stays free for compute).  0 (default) = no cap;
+ *                              the single-launch ring still uses at least one
+ *                              workgroup per rank.  Results do not depend on it.
  * Out-of-range values are SIM_ERR_INVALID_ARG and change nothing. */
-enum { SIM_CONFIG_RANKS_PER_NODE = 0, SIM_CONFIG_RADIX = 1 };
+enum { SIM_CONFIG_RANKS_PER_NODE = 0, SIM_CONFIG_RADIX = 1, SIM_CONFIG_MAX_WORKGROUPS = 2 };
 int sim_config_set(int key, int value);
 int sim_config_get(int key, int* value);
 

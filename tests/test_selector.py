@@ -110,3 +110,39 @@ def test_packaged_calibration_loads_and_picks_oneshot():
         assert rep["strict_matches"] == rep["cases"]
     finally:
         sim.sim_model_reset()
+
+
+def test_launch_table_json(tmp_path):
+    """The calibration's launch table ("workgroups") loads with the model;
+    malformed tables are refused and leave the model as it was."""
+    good = tmp_path / "wg.json"
+    good.write_text(json.dumps({"algos": {"oneshot": {"alpha_us": 3.0, "gbps": 5000.0}},
+                                "workgroups": {"oneshot": [[1048576, 0], [67108864, 4096]],
+                                               "ring": [[4096, 64]]}}))
+    try:
+        sim.sim_model_load(str(good))
+        assert sim.sim_model_predict("oneshot", 8, "bf16", 1 << 20) == pytest.approx(
+            3.0 + 16 * (1 << 20) / 5000.0e3)
+        for table in ('{"oneshot": [[0, 10]]}', '{"oneshot": [[4096, -1]]}', '{"oneshot": [4096, 16]}',
+                      '{"oneshot": {"4096": 16}}', '[1, 2]'):
+            bad = tmp_path / "bad.json"
+            bad.write_text('{"algos": {"oneshot": {"alpha_us": 9.0, "gbps": 1.0}}, "workgroups": %s}' % table)
+            with pytest.raises(sim.SimError):
+                sim.sim_model_load(str(bad))
+            # the refused file changed nothing
+            assert sim.sim_model_predict("oneshot", 8, "bf16", 1 << 20) == pytest.approx(
+                3.0 + 16 * (1 << 20) / 5000.0e3)
+    finally:
+        sim.sim_model_reset()
+
+
+def test_workgroup_budget_config():
+    assert sim.sim_config_get("max_workgroups") == 0
+    try:
+        sim.sim_config_set("max_workgroups", 64)
+        assert sim.sim_config_get("max_workgroups") == 64
+        with pytest.raises(sim.SimError):
+            sim.sim_config_set("max_workgroups", -1)
+        assert sim.sim_config_get("max_workgroups") == 64
+    finally:
+        sim.sim_config_set("max_workgroups", 0)
