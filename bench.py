@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-extras", action="store_true", help="skip per-algo and latency figures")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed steps of the headline workload (for rocprofv3 runs)")
+    ap.add_argument("--profile-large", action="store_true",
+                    help="only the 256 MiB-per-rank fp32 avg one-shot (workload 5's 4 GiB working set)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="only a plain 512 MiB -> 512 MiB device copy (the counter scale reference)")
     return ap.parse_args()
@@ -155,6 +157,28 @@ def load_traffic(algo: str):
     return None if not ent else ent.get("hbm_bytes_per_launch_scaled")
 
 
+N5 = 67_108_864  # workload 5: 256 MiB of fp32 per rank
+
+
+def large_workload(sim, synthdata, torch, np, dev, stream, steps, warmup) -> float:
+    """Microseconds per one-shot fp32 avg all-reduce at 256 MiB per rank
+    (inputs 2 GiB + outputs 2 GiB: far past the 256 MB Infinity Cache)."""
+    xs5 = synthdata.workload_inputs(5, P, N5, "fp32")
+    d5 = [torch.from_numpy(x).to(dev) for x in xs5]
+    del xs5
+    o5 = [torch.empty(N5, dtype=torch.float32, device=dev) for _ in range(P)]
+    i5, p5 = [t.data_ptr() for t in d5], [t.data_ptr() for t in o5]
+
+    def call():
+        if sim.sim_allreduce(i5, p5, P, N5, "fp32", "avg", "oneshot", stream):
+            raise sim.SimError(-1, "sim_allreduce (workload 5)")
+    t5 = time_calls(call, steps, warmup)
+    assert sim.sim_check_error(stream) == 0
+    del d5, o5
+    torch.cuda.empty_cache()
+    return t5 * 1e6
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -193,6 +217,10 @@ def main():
         return
     sim.sim_init(0, P, S)
     stream = int(torch.cuda.current_stream().cuda_stream)
+    if args.profile_large:
+        us5 = large_workload(sim, synthdata, torch, np, dev, stream, args.steps, args.warmup)
+        print(json.dumps({"workload": "fp32 avg, p=8, 256 MiB per rank", "us_per_step": us5}), flush=True)
+        return
 
     xs = synthdata.workload_inputs(3, P, N, "bf16")
     din = [torch.from_numpy(x.view(np.int16)).to(dev) for x in xs]
@@ -263,6 +291,11 @@ def main():
             budget[str(b) if b else "none"] = round(2 * (P - 1) / P * S / tb / 1e9, 1)
         sim.sim_config_set("max_workgroups", 0)
         extras["oneshot_busbw_by_workgroup_budget"] = budget
+        us5 = large_workload(sim, synthdata, torch, np, dev, stream, max(10, args.steps // 10), 3)
+        extras["workload5_fp32_avg_256MiB_oneshot"] = {
+            "us": round(us5, 2), "busbw_GBps": round(2 * (P - 1) / P * N5 * 4 / us5 / 1e3, 1),
+            "hbm_algorithmic_GBps": round(2 * P * N5 * 4 / us5 / 1e3, 1),
+            "frac_of_peak": round(2 * P * N5 * 4 / us5 / 1e3 / HBM_PEAK_GBPS, 4)}
         # small-message latency: 8 KiB per rank, fp16
         lx = synthdata.workload_inputs(4, P, LAT_N, "fp16")
         lin = [torch.from_numpy(x.view(np.int16)).to(dev) for x in lx]
