@@ -290,10 +290,13 @@ struct Parser {
       return true;
     }
     if (lit("null")) return true;
+    // JSON numbers only: strtod alone would also take inf, nan and hex forms
+    if (*s != '-' && !(*s >= '0' && *s <= '9')) return fail("bad value");
     char* e2 = nullptr;
     std::string tmp(s, (size_t)std::min<ptrdiff_t>(end - s, 64));
     double d = std::strtod(tmp.c_str(), &e2);
-    if (e2 == tmp.c_str()) return fail("bad value");
+    if (e2 == tmp.c_str() || !std::isfinite(d) || tmp.find_first_of("xX") < (size_t)(e2 - tmp.c_str()))
+      return fail("bad number");
     s += (e2 - tmp.c_str());
     v->kind = JVal::NUM;
     v->num = d;
@@ -321,6 +324,11 @@ bool model_load_json(const char* path, Model* m, std::string* err) {
   JVal root;
   if (!ps.value(&root, 0) || root.kind != JVal::OBJ) {
     if (err) *err = ps.err.empty() ? "top level is not an object" : ps.err;
+    return false;
+  }
+  ps.ws();
+  if (ps.s != ps.end) {
+    if (err) *err = "trailing content after the top-level object";
     return false;
   }
   auto it = root.obj.find("algos");

@@ -95,6 +95,15 @@ def test_model_json_roundtrip(tmp_path):
             sim.sim_model_load(str(bad))
         with pytest.raises(sim.SimError):
             sim.sim_model_load(str(tmp_path / "missing.json"))
+        good = '{"algos": {"ring": {"alpha_us": 2.0, "gbps": %s}}}'
+        for text in (good % "Infinity", good % "inf", good % "nan", good % "-1e999", good % "0x10",
+                     good % "1e999", good % "2000" + " x", good % "2000" + "{}"):
+            bad.write_text(text)
+            with pytest.raises(sim.SimError):
+                sim.sim_model_load(str(bad))
+        bad.write_text(good % "2.5e3" + "\n")
+        sim.sim_model_load(str(bad))
+        assert sim.sim_model_predict("ring", 2, "fp32", 1000) > 0
     finally:
         sim.sim_model_reset()
 
