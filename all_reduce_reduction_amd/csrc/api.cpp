@@ -14,6 +14,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "kernels.h"
@@ -29,6 +30,35 @@ constexpr int64_t kMaxTiles = 1 << 20;  // cap on workgroups per transfer
 // single-launch ring: FIFO geometry
 constexpr int kFifoMaxChannels = 128;     // channels per rank
 constexpr int kFifoMaxSlots = 8;          // slots per FIFO
+// pointer table: distinct rank pointer sets kept in device memory
+constexpr int kPtrSets = 512;
+
+// A call's rank pointers as a hash key (p, then x[0..p), y[0..p)).
+struct PtrKey {
+  int p = 0;
+  uintptr_t w[2 * SIM_MAX_RANKS] = {};
+  bool operator==(const PtrKey& o) const {
+    if (p != o.p) return false;
+    for (int i = 0; i < 2 * p; i++)
+      if (w[i] != o.w[i]) return false;
+    return true;
+  }
+};
+struct PtrKeyHash {
+  size_t operator()(const PtrKey& k) const {
+    uint64_t h = 0x9e3779b97f4a7c15ull ^ (uint64_t)k.p;
+    for (int i = 0; i < 2 * k.p; i++) {
+      h ^= (uint64_t)k.w[i] + 0x9e3779b97f4a7c15ull + (h << 6) + (h >> 2);
+    }
+    return (size_t)h;
+  }
+};
+// A table slot: written by an async copy, complete once `done` has fired
+// (`ready` caches that).
+struct PtrSlot {
+  hipEvent_t done = nullptr;
+  bool ready = false;
+};
 
 struct Ctx {
   bool init = false;
@@ -60,6 +90,15 @@ struct Ctx {
   bool capturing = false;  // the current call's stream is being captured into a graph
   bool captured = false;   // some call has been captured since sim_init
   std::vector<void*> retired;  // outgrown scratch a captured graph may still use
+  // pointer table (one-shot calls outside graph capture): slot i of `ptab`
+  // holds a pointer set, copied from slot i of the pinned `ptab_host`; slots
+  // are never rewritten or evicted, so no launch can see a slot change
+  PtrSet* ptab = nullptr;
+  PtrSet* ptab_host = nullptr;
+  int ptab_used = 0;
+  int ptab_on = 1;
+  std::unordered_map<PtrKey, int, PtrKeyHash> ptab_index;
+  std::vector<PtrSlot> ptab_slots;
 
   int fifo_occ[4][5] = {};
   Model model = default_model();
@@ -212,6 +251,56 @@ int tiles_for(const Call& c, int64_t vecs_per_unit, int units, int unroll) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(t, kMaxTiles));
 }
 
+// The device copy of the call's rank pointers, or nullptr when this call
+// must carry them in its kernel arguments: under graph capture (a replay
+// pays no launch cost, and a captured kernel keeps no reference into the
+// table), when the table is full or off, or while the set's copy may still
+// be in flight.  A new set is copied on the call's stream, so the launch
+// that follows it is ordered after the copy; any later call uses the entry
+// only once the copy's event has completed (a later call may come on
+// another stream, or on a new stream that reuses the handle).
+const PtrSet* ptr_set_for(const Call& c) {
+  if (!g.ptab_on || !g.ptab || g.capturing || c.p > SIM_MAX_RANKS) return nullptr;
+  PtrKey k;
+  k.p = c.p;
+  for (int q = 0; q < c.p; q++) {
+    k.w[q] = (uintptr_t)c.x[q];
+    k.w[c.p + q] = (uintptr_t)c.y[q];
+  }
+  auto it = g.ptab_index.find(k);
+  if (it != g.ptab_index.end()) {
+    PtrSlot& sl = g.ptab_slots[it->second];
+    if (!sl.ready) {
+      if (hipEventQuery(sl.done) == hipSuccess) sl.ready = true;
+      else (void)hipGetLastError();  // not yet complete: clear the query's status
+    }
+    return sl.ready ? g.ptab + it->second : nullptr;
+  }
+  if (g.ptab_used >= kPtrSets) return nullptr;
+  // the slot is taken even if a call below fails: its staging entry may be
+  // in use by a copy and is never written again
+  const int i = g.ptab_used++;
+  PtrSet& h = g.ptab_host[i];
+  std::memset(&h, 0, sizeof h);
+  for (int q = 0; q < c.p; q++) {
+    h.x[q] = c.x[q];
+    h.y[q] = c.y[q];
+  }
+  PtrSlot& sl = g.ptab_slots[i];
+  if (hipEventCreateWithFlags(&sl.done, hipEventDisableTiming) != hipSuccess) {
+    sl.done = nullptr;
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (hipMemcpyAsync(g.ptab + i, &h, sizeof h, hipMemcpyHostToDevice, c.s) != hipSuccess ||
+      hipEventRecord(sl.done, c.s) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g.ptab_index.emplace(k, i);
+  return g.ptab + i;
+}
+
 int run_fold(const Call& c, bool all_out, const std::vector<int64_t>& lo, const int64_t* out_shift) {
   FoldArgs a;
   std::memset(&a, 0, sizeof a);
@@ -229,6 +318,18 @@ int run_fold(const Call& c, bool all_out, const std::vector<int64_t>& lo, const 
   a.inv_p = inv_p_of(c.p);
   const int unroll = (c.p == 8) ? g.unroll : 1;
   a.tiles = tiles_for(c, (maxchunk + V - 1) / V, c.p, unroll);
+  if (all_out) {
+    if (const PtrSet* set = ptr_set_for(c)) {  // the same launch from a 32-byte argument block
+      FoldTabArgs t;
+      std::memset(&t, 0, sizeof t);
+      t.set = set;
+      t.n = (int64_t)c.n;
+      t.p = c.p;
+      t.tiles = a.tiles;
+      t.inv_p = a.inv_p;
+      return hip_err(launch_fold_tab(c.dtype, c.op, c.p, t, unroll, c.s));
+    }
+  }
   return hip_err(launch_fold(c.dtype, c.op, c.p, all_out, a, unroll, c.s));
 }
 
@@ -751,7 +852,8 @@ const char* sim_status_string(int status) {
 }
 
 int sim_finalize(void) {
-  if (!g.init) return SIM_OK;
+  // (also releases what a failed sim_init had allocated before it gave up)
+  if (!g.init && !g.err && !g.ll && !g.fifo_sem && !g.scratch && !g.ptab && !g.ptab_host) return SIM_OK;
   // teardown is best effort: every allocation is released even if one call fails
   (void)hipSetDevice(g.device);
   (void)hipDeviceSynchronize();
@@ -761,6 +863,11 @@ int sim_finalize(void) {
   if (g.fifo) (void)hipFree(g.fifo);
   if (g.fifo_sem) (void)hipFree(g.fifo_sem);
   if (g.err) (void)hipFree(g.err);
+  for (PtrSlot& sl : g.ptab_slots)
+    if (sl.done) (void)hipEventDestroy(sl.done);
+  if (g.ptab) (void)hipFree(g.ptab);
+  if (g.ptab_host) (void)hipHostFree(g.ptab_host);
+  (void)hipGetLastError();
   Model keep = g.model;
   g = Ctx();
   g.model = keep;
@@ -802,6 +909,16 @@ int sim_init(int device, int p_max, size_t max_bytes_per_rank) {
     sim_finalize();
     return SIM_ERR_HIP;
   }
+  // the pointer table only makes launches cheaper: without it every call
+  // carries its pointers in its kernel arguments
+  if (hipMalloc(&g.ptab, sizeof(PtrSet) * kPtrSets) != hipSuccess ||
+      hipHostMalloc(&g.ptab_host, sizeof(PtrSet) * kPtrSets, hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    if (g.ptab) (void)hipFree(g.ptab);
+    g.ptab = nullptr;
+    g.ptab_host = nullptr;
+  }
+  g.ptab_slots.assign(kPtrSets, PtrSlot());
   g.init = true;
   if (max_bytes_per_rank > 0) {
     const size_t n = max_bytes_per_rank / 2;  // 16-bit elements need the most slots
@@ -1170,6 +1287,7 @@ int sim_debug_set(int key, uint64_t value) {
       g.fifo_channels = (int)value;
       return SIM_OK;
     case SIM_DEBUG_FIFO_WITHHOLD: g.fifo_withhold = value ? 1 : 0; return SIM_OK;
+    case SIM_DEBUG_PTR_TABLE: g.ptab_on = value ? 1 : 0; return SIM_OK;
     case SIM_DEBUG_FIFO_VECS:
       if (value != 1 && value != 2 && value != (uint64_t)kFifoVecsPerLane) return SIM_ERR_INVALID_ARG;
       g.fifo_vecs = (int)value;
@@ -1205,6 +1323,8 @@ int sim_debug_get(int key, uint64_t* value) {
     case SIM_DEBUG_FIFO_WITHHOLD: *value = (uint64_t)g.fifo_withhold; return SIM_OK;
     case SIM_DEBUG_FIFO_VECS: *value = (uint64_t)g.fifo_vecs; return SIM_OK;
     case SIM_DEBUG_FIFO_SLOTS: *value = (uint64_t)g.fifo_slots; return SIM_OK;
+    case SIM_DEBUG_PTR_TABLE: *value = (uint64_t)g.ptab_on; return SIM_OK;
+    case SIM_DEBUG_PTR_SETS: *value = (uint64_t)g.ptab_index.size(); return SIM_OK;
   }
   return SIM_ERR_INVALID_ARG;
 }

@@ -28,13 +28,36 @@
 // chunk edge (a vector that would straddle two chunks, or a misaligned
 // operand) is done element by element so every element keeps its own
 // chunk's order.
+//
+// The one-shot also runs from a small argument block whose rank pointers
+// sit in device memory (FoldTabArgs); both argument forms are read through
+// the accessors below, and every pointer is loaded once, before the first
+// store.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
 namespace simar {
 
-template <int DT, int OP, int P, bool ALL_OUT, int U>
-__global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
+namespace {
+// rank pointers, chunk bounds, vector eligibility and output shift of chunk j
+__device__ __forceinline__ const void* x_of(const FoldArgs& a, int q) { return a.x[q]; }
+__device__ __forceinline__ void* y_of(const FoldArgs& a, int r) { return a.y[r]; }
+__device__ __forceinline__ int64_t lo_of(const FoldArgs& a, int j, int) { return a.lo[j]; }
+__device__ __forceinline__ bool vec_of(const FoldArgs& a, int j) { return (a.vec_ok >> j) & 1u; }
+__device__ __forceinline__ int64_t shift_of(const FoldArgs& a, int j) { return a.out_shift[j]; }
+
+__device__ __forceinline__ const void* x_of(const FoldTabArgs& a, int q) { return a.set->x[q]; }
+__device__ __forceinline__ void* y_of(const FoldTabArgs& a, int r) { return a.set->y[r]; }
+// floor(j n / p): n < 2^46 and j <= 16, so j n cannot overflow
+__device__ __forceinline__ int64_t lo_of(const FoldTabArgs& a, int j, int p) { return (int64_t)j * a.n / p; }
+__device__ __forceinline__ bool vec_of(const FoldTabArgs&, int) { return true; }  // every pointer is 16-byte aligned
+__device__ __forceinline__ int64_t shift_of(const FoldTabArgs&, int) { return 0; }
+}  // namespace
+
+template <int DT, int OP, int P, bool ALL_OUT, int U, class Args>
+__global__ void __launch_bounds__(kBlock) k_fold(Args a) {
   typedef typename Ty<DT>::A A;
   typedef Op<DT, OP> O;
   constexpr int V = epv<DT>();
@@ -43,7 +66,7 @@ __global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
   const int p = P ? P : a.p;
   const int j = (int)(blockIdx.x % (unsigned)p);
   const int64_t tile = blockIdx.x / (unsigned)p;
-  const int64_t lo = a.lo[j], hi = a.lo[j + 1];
+  const int64_t lo = lo_of(a, j, p), hi = lo_of(a, j + 1, p);
   const float inv_p = a.inv_p;
 
   // operand k of the fold: rank j for k == 0, then the ranks != j ascending
@@ -51,10 +74,14 @@ __global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
 #pragma unroll
   for (int k = 0; k < MAXP; k++) {
     const int q = (k == 0) ? j : (k <= j ? k - 1 : k);
-    xp[k] = (k < p) ? a.x[q] : nullptr;
+    xp[k] = (k < p) ? x_of(a, q) : nullptr;
   }
+  // outputs: every rank's (one-shot) or the owner's
+  void* yp[ALL_OUT ? MAXP : 1];
+#pragma unroll
+  for (int r = 0; r < (ALL_OUT ? MAXP : 1); r++) yp[r] = (r < p) ? y_of(a, ALL_OUT ? r : j) : nullptr;
 
-  const bool vec = (a.vec_ok >> j) & 1u;
+  const bool vec = vec_of(a, j);
   int64_t head = vec ? (int64_t)((V - (lo % V)) % V) : (hi - lo);
   if (head > hi - lo) head = hi - lo;
   const int64_t vbeg = lo + head;
@@ -64,8 +91,8 @@ __global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
   const int tid = threadIdx.x;
   const int64_t span = (int64_t)kBlock * U;
   const int64_t stride = (int64_t)a.tiles * span;
-  const int64_t oshift = ALL_OUT ? 0 : a.out_shift[j];
-  void* const yj = a.y[j];
+  const int64_t oshift = ALL_OUT ? 0 : shift_of(a, j);
+  void* const yj = yp[0];
 
   for (int64_t base = tile * span; base < nvec; base += stride) {
     u32x4 L[U][MAXP];
@@ -102,7 +129,7 @@ __global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
         if constexpr (ALL_OUT) {
 #pragma unroll
           for (int r = 0; r < MAXP; r++)
-            if (r < p) st16(a.y[r], i0 * E, out);
+            if (r < p) st16(yp[r], i0 * E, out);
         } else {
           st16(yj, (i0 - oshift) * E, out);
         }
@@ -121,31 +148,36 @@ __global__ void __launch_bounds__(kBlock) k_fold(FoldArgs a) {
     if constexpr (ALL_OUT) {
 #pragma unroll
       for (int r = 0; r < MAXP; r++)
-        if (r < p) store_elem<DT>(a.y[r], i, acc);
+        if (r < p) store_elem<DT>(yp[r], i, acc);
     } else {
       store_elem<DT>(yj, i - oshift, acc);
     }
   }
 }
 
-template <int DT, int OP, int P, bool ALL_OUT, int U>
-static hipError_t go(const FoldArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_fold<DT, OP, P, ALL_OUT, U>), dim3((unsigned)a.tiles * (unsigned)a.p), dim3(kBlock), 0, s,
-                     a);
+template <int DT, int OP, int P, bool ALL_OUT, int U, class Args>
+static hipError_t go(const Args& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_fold<DT, OP, P, ALL_OUT, U, Args>), dim3((unsigned)a.tiles * (unsigned)a.p), dim3(kBlock),
+                     0, s, a);
   return hipGetLastError();
 }
 
-template <int DT, int OP>
-static hipError_t by_shape(int p, bool all_out, int unroll, const FoldArgs& a, hipStream_t s) {
-  if (p == 8) {
-    if (all_out) return unroll == 2 ? go<DT, OP, 8, true, 2>(a, s) : go<DT, OP, 8, true, 1>(a, s);
-    return unroll == 2 ? go<DT, OP, 8, false, 2>(a, s) : go<DT, OP, 8, false, 1>(a, s);
+template <int DT, int OP, class Args>
+static hipError_t by_shape(int p, bool all_out, int unroll, const Args& a, hipStream_t s) {
+  if constexpr (std::is_same<Args, FoldTabArgs>::value) {  // the one-shot only
+    if (p == 8) return unroll == 2 ? go<DT, OP, 8, true, 2>(a, s) : go<DT, OP, 8, true, 1>(a, s);
+    return go<DT, OP, 0, true, 1>(a, s);
+  } else {
+    if (p == 8) {
+      if (all_out) return unroll == 2 ? go<DT, OP, 8, true, 2>(a, s) : go<DT, OP, 8, true, 1>(a, s);
+      return unroll == 2 ? go<DT, OP, 8, false, 2>(a, s) : go<DT, OP, 8, false, 1>(a, s);
+    }
+    return all_out ? go<DT, OP, 0, true, 1>(a, s) : go<DT, OP, 0, false, 1>(a, s);
   }
-  return all_out ? go<DT, OP, 0, true, 1>(a, s) : go<DT, OP, 0, false, 1>(a, s);
 }
 
-template <int DT>
-static hipError_t by_op(int op, int p, bool all_out, int unroll, const FoldArgs& a, hipStream_t s) {
+template <int DT, class Args>
+static hipError_t by_op(int op, int p, bool all_out, int unroll, const Args& a, hipStream_t s) {
   switch (op) {
     case SIM_SUM: return by_shape<DT, SIM_SUM>(p, all_out, unroll, a, s);
     case SIM_PROD: return by_shape<DT, SIM_PROD>(p, all_out, unroll, a, s);
@@ -156,8 +188,8 @@ static hipError_t by_op(int op, int p, bool all_out, int unroll, const FoldArgs&
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fold(int dtype, int op, int p, bool all_out, const FoldArgs& a, int unroll,
-                       hipStream_t s) {
+template <class Args>
+static hipError_t by_dtype(int dtype, int op, int p, bool all_out, const Args& a, int unroll, hipStream_t s) {
   switch (dtype) {
     case SIM_INT32: return by_op<SIM_INT32>(op, p, all_out, unroll, a, s);
     case SIM_FP32: return by_op<SIM_FP32>(op, p, all_out, unroll, a, s);
@@ -165,6 +197,15 @@ hipError_t launch_fold(int dtype, int op, int p, bool all_out, const FoldArgs& a
     case SIM_BF16: return by_op<SIM_BF16>(op, p, all_out, unroll, a, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fold(int dtype, int op, int p, bool all_out, const FoldArgs& a, int unroll,
+                       hipStream_t s) {
+  return by_dtype(dtype, op, p, all_out, a, unroll, s);
+}
+
+hipError_t launch_fold_tab(int dtype, int op, int p, const FoldTabArgs& a, int unroll, hipStream_t s) {
+  return by_dtype(dtype, op, p, true, a, unroll, s);
 }
 
 }  // namespace simar

@@ -32,6 +32,24 @@ struct FoldArgs {
   float inv_p;                       // fp32(1/p) for fp avg
 };
 
+// The fused one-shot with its rank pointers in device memory: one entry of
+// the library's pointer table, written (in stream order) before the first
+// launch that uses it.  The argument block then fits the HIP runtime's
+// small-argument launch path (<= 64 bytes), which measured ~1 us cheaper
+// per launch on MI355X than argument blocks of 128 bytes or more.  Chunk j
+// is [floor(j n / p), floor((j+1) n / p)), computed in the kernel.
+struct PtrSet {
+  const void* x[SIM_MAX_RANKS];
+  void* y[SIM_MAX_RANKS];
+};
+struct FoldTabArgs {
+  const PtrSet* set;  // device memory
+  int64_t n;          // elements per rank (< 2^46)
+  int p;
+  int tiles;          // workgroups per chunk
+  float inv_p;        // fp32(1/p) for fp avg
+};
+
 // One ring reduce-scatter step: p transfers, each over one chunk.
 struct RingXfer {
   const void* a;    // running value from the predecessor: an input (first step) or a partial
@@ -140,6 +158,7 @@ struct SchedArgs {
 };
 
 static_assert(sizeof(FoldArgs) <= 4096, "kernel argument segment too large");
+static_assert(sizeof(FoldTabArgs) <= 64, "must fit the small-argument launch path");
 static_assert(sizeof(SchedArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingFifoArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingArgs) <= 4096, "kernel argument segment too large");
@@ -149,6 +168,7 @@ static_assert(sizeof(LLArgs) <= 4096, "kernel argument segment too large");
 // Launchers: select the (dtype, op, ...) instantiation and enqueue.
 hipError_t launch_fold(int dtype, int op, int p, bool all_out, const FoldArgs& a, int unroll,
                        hipStream_t s);
+hipError_t launch_fold_tab(int dtype, int op, int p, const FoldTabArgs& a, int unroll, hipStream_t s);
 hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, const RingArgs& a,
                               int unroll, hipStream_t s);
 hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s);

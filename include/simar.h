@@ -52,6 +52,16 @@
  *     max_bytes_per_rank or make one uncaptured call of the same shape
  *     first.  Once a call has been captured, outgrown scratch is kept until
  *     sim_finalize, so recorded graphs stay valid until then (not after).
+ *   - Pointer table: the first 512 distinct (p, in_ptrs, out_ptrs) sets of
+ *     SIM_ALGO_ONESHOT calls made outside graph capture are copied once
+ *     (asynchronously, on the call's stream) into a device-memory table
+ *     that the library owns until sim_finalize; later calls with the same
+ *     set launch with a 32-byte argument block instead of the full pointer
+ *     list, which is cheaper to enqueue.  Entries hold addresses only (no
+ *     ownership) and are never rewritten or evicted; other sets, captured
+ *     calls, and calls made while a set's copy has not completed yet carry
+ *     their pointers in the kernel arguments.  Results are the same either
+ *     way.
  *
  * Results: int32 and fp32 results are bit-exact functions of the schedule:
  * ring chunk c (both ring executions) folds ranks c+1, c+2, ..., c+p
@@ -297,7 +307,9 @@ enum {
   SIM_DEBUG_FIFO_CHANNELS = 7, /* single-launch ring: channels per rank, <= 128 (0 = heuristic) */
   SIM_DEBUG_FIFO_SLOTS = 8,    /* single-launch ring: slots per FIFO, 2..8 (default 4) */
   SIM_DEBUG_FIFO_WITHHOLD = 9, /* 1: rank 0's ring workgroups leave at once (forces a bounded-wait expiry) */
-  SIM_DEBUG_FIFO_VECS = 10     /* single-launch ring: 16-byte vectors per lane per slot, 1, 2 or 4 (default 4) */
+  SIM_DEBUG_FIFO_VECS = 10,    /* single-launch ring: 16-byte vectors per lane per slot, 1, 2 or 4 (default 4) */
+  SIM_DEBUG_PTR_TABLE = 11,    /* 0: one-shot calls never use the pointer table (default 1) */
+  SIM_DEBUG_PTR_SETS = 12      /* get only: pointer sets the table holds */
 };
 int sim_debug_set(int key, uint64_t value);
 int sim_debug_get(int key, uint64_t* value);

@@ -1,0 +1,178 @@
+"""The one-shot's small-argument launch: rank pointer sets kept in a
+device-memory table.  A call whose set is in the table and a call that
+carries its pointers in the kernel arguments must give the same bits, and
+both must match the oracle; new inputs behind the same pointers must be
+read afresh; sets beyond the table's capacity, calls on another stream and
+captured calls fall back to the argument path."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+TABLE_CAPACITY = 512
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    import all_reduce_reduction_amd as sim
+    sim.sim_init(0, 16, 0)
+    yield sim
+    sim.sim_debug_set("ptr_table", 1)
+    sim.sim_init(0, 8, 0)
+
+
+def _inputs(dtype, p, n, seed):
+    import synthdata
+    if dtype == "int32":
+        return synthdata.int_uniform(seed, p, n, -1000, 1000)
+    return synthdata.normal(seed, p, n, dtype)
+
+
+def _sets(sim):
+    return sim.sim_debug_get("ptr_sets")
+
+
+@pytest.mark.parametrize("p,n", [(8, 8 * 4096 * 3 + 77), (8, 4096), (2, 5), (3, 1000), (16, 16 * 1024 + 9)])
+@pytest.mark.parametrize("dtype,op", [("bf16", "sum"), ("fp16", "avg"), ("fp32", "prod"), ("int32", "max"),
+                                      ("int32", "avg")])
+def test_table_and_argument_paths_agree_with_the_oracle(orc, lib, p, n, dtype, op):
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
+    sim = lib
+    sim.sim_init(0, 16, 0)  # empty table: the allocator may hand out addresses an earlier case used
+    xs = _inputs(dtype, p, n, 90 + p)
+    want, _ = orc.allreduce(xs, dtype, op, "oneshot")
+    din = to_device(xs, dtype)
+    results = {}
+    dout = None
+    for mode in ("args", "table_first", "table_again"):
+        sim.sim_debug_set("ptr_table", 0 if mode == "args" else 1)
+        if mode == "table_again":  # the same pointers, outputs poisoned again
+            fresh = empty_like_poisoned(n, dtype, p)
+            for t, f in zip(dout, fresh):
+                t.copy_(f)
+        else:
+            dout = empty_like_poisoned(n, dtype, p)
+        before = _sets(sim)
+        assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, "oneshot", stream()) == 0
+        got = to_host(dout, dtype)
+        if mode == "args":
+            assert _sets(sim) == before
+        elif mode == "table_first":
+            assert _sets(sim) == before + 1     # a new set is copied into the table
+        else:
+            assert _sets(sim) == before         # and found there the next time
+        for r in range(p):
+            assert_parity(got[r], want[r], dtype, f"{mode} {dtype} {op} p={p} n={n} r{r}")
+        results[mode] = got
+    for r in range(p):
+        assert (results["args"][r] == results["table_again"][r]).all()
+
+
+@pytest.mark.parametrize("unroll", [1, 2])
+def test_table_path_vectors_per_lane(orc, lib, unroll):
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
+    sim = lib
+    p, n, dtype = 8, 8 * 8192 * 5 + 13, "bf16"
+    xs = _inputs(dtype, p, n, 30 + unroll)
+    want, _ = orc.allreduce(xs, dtype, "sum", "oneshot")
+    din = to_device(xs, dtype)
+    dout = empty_like_poisoned(n, dtype, p)
+    sim.sim_debug_set("unroll", unroll)
+    try:
+        for rep in range(2):  # the second call finds its set in the table
+            assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, "sum", "oneshot", stream()) == 0
+            got = to_host(dout, dtype)
+            for r in range(p):
+                assert_parity(got[r], want[r], dtype, f"unroll {unroll} rep {rep} r{r}")
+            for t, f in zip(dout, empty_like_poisoned(n, dtype, p)):
+                t.copy_(f)
+    finally:
+        sim.sim_debug_set("unroll", 1)
+
+
+def test_same_pointers_new_contents(orc, lib):
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
+    sim = lib
+    p, n, dtype = 8, 8 * 1024 + 3, "bf16"
+    din = to_device(_inputs(dtype, p, n, 1), dtype)
+    dout = empty_like_poisoned(n, dtype, p)
+    for rep in range(4):
+        xs = _inputs(dtype, p, n, 100 + rep)
+        for t, x in zip(din, to_device(xs, dtype)):
+            t.copy_(x)
+        assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, "sum", "oneshot", stream()) == 0
+        got = to_host(dout, dtype)
+        want, _ = orc.allreduce(xs, dtype, "sum", "oneshot")
+        for r in range(p):
+            assert_parity(got[r], want[r], dtype, f"rep {rep} r{r}")
+
+
+def test_capacity_and_other_stream(orc, lib):
+    """More distinct sets than the table holds: the later ones carry their
+    pointers in the arguments; every result is right.  Then a set first
+    seen on one stream is used at once from another."""
+    import torch
+    from tests.gpu_util import ptrs, stream, to_device
+    sim = lib
+    sim.sim_init(0, 16, 0)  # empty table
+    assert _sets(sim) == 0
+    p, n = 2, 32  # 128 bytes of fp32 per rank
+    xs = _inputs("fp32", p, n, 7)
+    want, _ = orc.allreduce(xs, "fp32", "sum", "oneshot")
+    din = to_device(xs, "fp32")
+    count = TABLE_CAPACITY + 40
+    arena = torch.full((count * p * n,), float("nan"), dtype=torch.float32, device="cuda:0")
+    for k in range(count):
+        outs = [arena[(k * p + r) * n:(k * p + r + 1) * n] for r in range(p)]
+        assert sim.sim_allreduce(ptrs(din), ptrs(outs), p, n, "fp32", "sum", "oneshot", stream()) == 0
+    assert _sets(sim) == TABLE_CAPACITY
+    got = arena.view(count, p, n).cpu().numpy()
+    for r in range(p):
+        assert (got[:, r, :].view(np.uint32) == want[r].view(np.uint32)[None, :]).all(), r
+    # a new set first seen on a side stream, used again at once (no
+    # synchronisation) on the current stream, whose call must not read the
+    # table entry before the side stream's copy of it has completed
+    side = torch.cuda.Stream()
+    sim.sim_init(0, 16, 0)
+    keep = []  # every trial's outputs stay allocated, so each trial's pointer set is new
+    for trial in range(3):
+        outs = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda:0") for _ in range(p)]
+        keep.append(outs)
+        torch.cuda.synchronize()
+        assert sim.sim_allreduce(ptrs(din), ptrs(outs), p, n, "fp32", "sum", "oneshot", int(side.cuda_stream)) == 0
+        assert sim.sim_allreduce(ptrs(din), ptrs(outs), p, n, "fp32", "sum", "oneshot", stream()) == 0
+        torch.cuda.synchronize()
+        for r in range(p):
+            assert (outs[r].cpu().numpy().view(np.uint32) == want[r].view(np.uint32)).all(), (trial, r)
+        assert _sets(sim) == trial + 1
+
+
+def test_captured_calls_do_not_use_the_table(orc, lib):
+    import torch
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, to_device, to_host
+    sim = lib
+    sim.sim_init(0, 16, 0)
+    p, n, dtype = 8, 8 * 2048 + 5, "fp16"
+    xs = _inputs(dtype, p, n, 11)
+    din = to_device(xs, dtype)
+    dout = empty_like_poisoned(n, dtype, p)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            s = int(torch.cuda.current_stream().cuda_stream)
+            assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, "sum", "oneshot", s) == 0
+    torch.cuda.current_stream().wait_stream(side)
+    assert _sets(sim) == 0
+    for rep in range(3):
+        for t in dout:
+            t.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = to_host(dout, dtype)
+        want, _ = orc.allreduce(xs, dtype, "sum", "oneshot")
+        for r in range(p):
+            assert_parity(got[r], want[r], dtype, f"replay {rep} r{r}")
+    del graph
