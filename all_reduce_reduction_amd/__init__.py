@@ -142,10 +142,13 @@ def prepare_allreduce(in_ptrs, out_ptrs, p, n, dtype, op, algo, stream=0):
     returns a function of no arguments that calls the C entry point and
     returns its status (for loops that repeat one call, where Python-side
     marshalling would otherwise dominate a few-microsecond call)."""
-    f = lib.sim_allreduce
-    ia, oa = _ptr_array(in_ptrs), _ptr_array(out_ptrs)
-    args = (ia, oa, p, n, _code(DTYPES, dtype, "dtype"), _code(OPS, op, "op"), _code(ALGOS, algo, "algo"),
-            stream or None)
+    # a bare function pointer (no argtypes) called with ready-made ctypes
+    # objects: no per-call argument conversion (~0.8 us less per call)
+    f = lib["sim_allreduce"]
+    f.restype = ctypes.c_int
+    args = (_ptr_array(in_ptrs), _ptr_array(out_ptrs), ctypes.c_int(p), ctypes.c_size_t(n),
+            ctypes.c_int(_code(DTYPES, dtype, "dtype")), ctypes.c_int(_code(OPS, op, "op")),
+            ctypes.c_int(_code(ALGOS, algo, "algo")), ctypes.c_void_p(stream or None))
     return lambda: f(*args)
 
 

@@ -40,6 +40,7 @@ def test_status_strings_and_not_initialised():
     # collectives before sim_init are refused synchronously
     st = sim.sim_allreduce([0, 0], [0, 0], 2, 4, "int32", "sum", "oneshot")
     assert st == -9
+    assert sim.prepare_allreduce([0, 0], [0, 0], 2, 4, "int32", "sum", "oneshot")() == -9
     assert sim.sim_check_error() == -9
 
 

@@ -176,3 +176,23 @@ def test_captured_calls_do_not_use_the_table(orc, lib):
         for r in range(p):
             assert_parity(got[r], want[r], dtype, f"replay {rep} r{r}")
     del graph
+
+
+def test_prepared_call_matches_the_oracle(orc, lib):
+    """The binding's prepared call (arguments marshalled once) repeated
+    with new inputs behind the same pointers."""
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
+    sim = lib
+    p, n, dtype = 8, 4096 + 3, "fp16"
+    din = to_device(_inputs(dtype, p, n, 2), dtype)
+    dout = empty_like_poisoned(n, dtype, p)
+    call = sim.prepare_allreduce(ptrs(din), ptrs(dout), p, n, dtype, "sum", "auto", stream())
+    for rep in range(3):
+        xs = _inputs(dtype, p, n, 200 + rep)
+        for t, x in zip(din, to_device(xs, dtype)):
+            t.copy_(x)
+        assert call() == 0
+        got = to_host(dout, dtype)
+        want, _ = orc.allreduce(xs, dtype, "sum", sim.sim_last_algo())
+        for r in range(p):
+            assert_parity(got[r], want[r], dtype, f"prepared rep {rep} r{r}")
