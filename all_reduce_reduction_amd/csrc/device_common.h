@@ -109,8 +109,14 @@ template <int DT, int OP> struct Op {
 #ifndef SIMAR_STORE_NT
 #define SIMAR_STORE_NT 1
 #endif
+// Every buffer is device-visible global memory: the accesses are typed as
+// such (global_load/store, with a scalar base where the address allows it)
+// rather than generic flat accesses -- pointers read from memory, such as the
+// pointer table's, would otherwise stay generic.
+typedef __attribute__((address_space(1))) const u32x4 gconst_u32x4;
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
 __device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
-  const u32x4* p = (const u32x4*)((const char*)base + byte_off);
+  gconst_u32x4* p = (gconst_u32x4*)((const char*)base + byte_off);
 #if SIMAR_LOAD_NT
   return __builtin_nontemporal_load(p);
 #else
@@ -118,12 +124,30 @@ __device__ __forceinline__ u32x4 ld16(const void* base, int64_t byte_off) {
 #endif
 }
 __device__ __forceinline__ void st16(void* base, int64_t byte_off, u32x4 v) {
-  u32x4* p = (u32x4*)((char*)base + byte_off);
+  g_u32x4* p = (g_u32x4*)((char*)base + byte_off);
 #if SIMAR_STORE_NT
   __builtin_nontemporal_store(v, p);
 #else
   *p = v;
 #endif
+}
+
+// The same access split into a workgroup-uniform byte offset and a 32-bit
+// per-lane offset: base + uoff is computed in scalar registers and the lane
+// offset rides in one VGPR shared by every operand (the global_load/store
+// form with a scalar base), instead of a 64-bit address pair per operand.
+__device__ __forceinline__ u32x4 ld16u(const void* base, int64_t uoff, uint32_t lane_off) {
+  return ld16((const char*)base + uoff, (int64_t)lane_off);
+}
+__device__ __forceinline__ void st16u(void* base, int64_t uoff, uint32_t lane_off, u32x4 v) {
+  st16((char*)base + uoff, (int64_t)lane_off, v);
+}
+// Hide a per-lane offset's derivation from the optimiser for one loop
+// iteration, so it is not folded into loop-invariant 64-bit pointers (one
+// VGPR pair per operand would cut the waves a SIMD can hold).
+__device__ __forceinline__ uint32_t lane_offset(uint32_t off) {
+  asm volatile("" : "+v"(off));
+  return off;
 }
 
 // Unpack one 16-byte storage vector into EPV accumulator values.

@@ -94,22 +94,26 @@ __global__ void __launch_bounds__(kBlock) k_fold(Args a) {
   const int64_t oshift = ALL_OUT ? 0 : shift_of(a, j);
   void* const yj = yp[0];
 
-  for (int64_t base = tile * span; base < nvec; base += stride) {
+  // One span: U vectors per lane, each folded from p operands and stored to
+  // the output(s).  GUARD: the span may run past nvec (the last one only).
+  auto span_body = [&](int64_t base, auto guard) {
+    constexpr bool GUARD = decltype(guard)::value;
+    // this span's first byte in every buffer (uniform) and the lane's 16-byte
+    // slot within it (one 32-bit VGPR for all 2p accesses)
+    const int64_t sbyte = (vbeg + base * V) * E;
+    const uint32_t lane = lane_offset((uint32_t)tid * 16u);
     u32x4 L[U][MAXP];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const int64_t v = base + u * kBlock + tid;
-      if (v < nvec) {
-        const int64_t off = (vbeg + v * V) * E;
+      if (!GUARD || base + u * kBlock + tid < nvec) {
 #pragma unroll
         for (int k = 0; k < MAXP; k++)
-          if (k < p) L[u][k] = ld16(xp[k], off);
+          if (k < p) L[u][k] = ld16u(xp[k], sbyte + (int64_t)u * kBlock * 16, lane);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const int64_t v = base + u * kBlock + tid;
-      if (v < nvec) {
+      if (!GUARD || base + u * kBlock + tid < nvec) {
         A acc[V], t[V];
         unpack<DT>(L[u][0], acc);
 #pragma unroll
@@ -125,17 +129,25 @@ __global__ void __launch_bounds__(kBlock) k_fold(Args a) {
 #pragma unroll
         for (int e = 0; e < V; e++) acc[e] = O::post(acc[e], p);
         const u32x4 out = pack<DT>(acc);
-        const int64_t i0 = vbeg + v * V;
+        const int64_t ub = sbyte + (int64_t)u * kBlock * 16;
         if constexpr (ALL_OUT) {
 #pragma unroll
           for (int r = 0; r < MAXP; r++)
-            if (r < p) st16(yp[r], i0 * E, out);
+            if (r < p) st16u(yp[r], ub, lane, out);
         } else {
-          st16(yj, (i0 - oshift) * E, out);
+          st16u(yj, ub - oshift * E, lane, out);
         }
       }
     }
-  }
+  };
+  // Whole spans run unguarded: a span's loads, fold and stores are then one
+  // straight-line block, and the compiler's wait counting needs no
+  // conservative wait (for stores still in flight) before the next span's
+  // loads, which an exec-masked load block followed by a separately masked
+  // fold block had forced.  The one partial span, if any, is guarded.
+  int64_t base = tile * span;
+  for (; base + span <= nvec; base += stride) span_body(base, std::false_type());
+  if (base < nvec) span_body(base, std::true_type());
 
   // ragged edges, element by element
   for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)a.tiles * kBlock) {

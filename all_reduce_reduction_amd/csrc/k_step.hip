@@ -15,6 +15,8 @@
 // k_copy moves finished chunks: the ring's all-gather forwards, the
 // all-pairs fan-out (one 16-byte load, up to p-1 stores from the same
 // registers) and the standalone all-gather.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -44,11 +46,13 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
   const int64_t span = (int64_t)kBlock * U;
   const int64_t stride = (int64_t)args.tiles * span;
 
-  for (int64_t base = tile * span; base < nvec; base += stride) {
+  // one span of U vectors per lane; GUARD: the span may run past nvec
+  auto span_body = [&](int64_t base, auto guard) {
+    constexpr bool GUARD = decltype(guard)::value;
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int64_t v = base + u * kBlock + tid;
-      if (v < nvec) {
+      if (!GUARD || v < nvec) {
         const int64_t i0 = vbeg + v * V;
         A in[V], own[V];
         if constexpr (A_PART) {
@@ -70,7 +74,12 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
         }
       }
     }
-  }
+  };
+  // whole spans unguarded (one straight-line block per span), then the
+  // partial span, if any
+  int64_t base = tile * span;
+  for (; base + span <= nvec; base += stride) span_body(base, std::false_type());
+  if (base < nvec) span_body(base, std::true_type());
 
   for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)args.tiles * kBlock) {
     const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
@@ -83,7 +92,11 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
   }
 }
 
-template <int E, int U>
+// ONE: every transfer of the launch has a single destination (the ring's
+// all-gather steps).  Measured on MI355X: loading all 16 destination
+// pointers up front costs such short-lived workgroups ~20% on a ring
+// all-gather step, while it saves the fan-out ~4%.
+template <int E, int U, bool ONE>
 __global__ void __launch_bounds__(kBlock) k_copy(CopyArgs args) {
   constexpr int V = 16 / E;
   const unsigned xi = blockIdx.x % (unsigned)args.nx;  // transfers interleaved, as above
@@ -101,30 +114,51 @@ __global__ void __launch_bounds__(kBlock) k_copy(CopyArgs args) {
   const int64_t span = (int64_t)kBlock * U;
   const int64_t stride = (int64_t)args.tiles * span;
 
-  for (int64_t base = tile * span; base < nvec; base += stride) {
+  // destination pointers in scalar registers, loaded once (a loop over a
+  // run-time count would re-load each one from the argument segment and
+  // wait for it before every store)
+  constexpr int ND = ONE ? 1 : SIM_MAX_RANKS;
+  void* dp[ND];
+#pragma unroll
+  for (int d = 0; d < ND; d++) dp[d] = (d < nd) ? x.dst[d] : nullptr;
+  const void* const src = x.src;
+  const int64_t src_off = x.src_shift * E, dst_off = x.dst_shift * E;
+  // one span of U vectors per lane; GUARD: the span may run past nvec
+  auto span_body = [&](int64_t base, auto guard) {
+    constexpr bool GUARD = decltype(guard)::value;
+    const int64_t sb = (vbeg + base * V) * E;  // the span's first byte (uniform)
+    const uint32_t lane = lane_offset((uint32_t)tid * 16u);
     u32x4 w[U];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int64_t v = base + u * kBlock + tid;
-      if (v < nvec) w[u] = ld16(x.src, (vbeg + v * V - x.src_shift) * E);
-    }
+    for (int u = 0; u < U; u++)
+      if (!GUARD || base + u * kBlock + tid < nvec)
+        w[u] = ld16u(src, sb - src_off + (int64_t)u * kBlock * 16, lane);
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int64_t v = base + u * kBlock + tid;
-      if (v < nvec) {
-        const int64_t off = (vbeg + v * V - x.dst_shift) * E;
-        for (int d = 0; d < nd; d++) st16(x.dst[d], off, w[u]);
+    for (int u = 0; u < U; u++)
+      if (!GUARD || base + u * kBlock + tid < nvec) {
+        const int64_t ub = sb - dst_off + (int64_t)u * kBlock * 16;
+#pragma unroll
+        for (int d = 0; d < ND; d++)
+          if (d < nd) st16u(dp[d], ub, lane, w[u]);
       }
-    }
-  }
+  };
+  // whole spans unguarded (one straight-line block per span), then the
+  // partial span, if any
+  int64_t base = tile * span;
+  for (; base + span <= nvec; base += stride) span_body(base, std::false_type());
+  if (base < nvec) span_body(base, std::true_type());
   for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)args.tiles * kBlock) {
     const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
     if constexpr (E == 4) {
       const uint32_t w = ((const uint32_t*)x.src)[i - x.src_shift];
-      for (int d = 0; d < nd; d++) ((uint32_t*)x.dst[d])[i - x.dst_shift] = w;
+#pragma unroll
+      for (int d = 0; d < ND; d++)
+        if (d < nd) ((uint32_t*)dp[d])[i - x.dst_shift] = w;
     } else {
       const uint16_t w = ((const uint16_t*)x.src)[i - x.src_shift];
-      for (int d = 0; d < nd; d++) ((uint16_t*)x.dst[d])[i - x.dst_shift] = w;
+#pragma unroll
+      for (int d = 0; d < ND; d++)
+        if (d < nd) ((uint16_t*)dp[d])[i - x.dst_shift] = w;
     }
   }
 }
@@ -175,18 +209,25 @@ hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, c
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s) {
+template <bool ONE>
+static hipError_t copy_go(int esize, const CopyArgs& a, int unroll, hipStream_t s) {
   const dim3 grid((unsigned)a.tiles * (unsigned)a.nx), block(kBlock);
   if (esize == 4) {
-    if (unroll == 2) hipLaunchKernelGGL((k_copy<4, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_copy<4, 1>), grid, block, 0, s, a);
+    if (unroll == 2) hipLaunchKernelGGL((k_copy<4, 2, ONE>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_copy<4, 1, ONE>), grid, block, 0, s, a);
   } else if (esize == 2) {
-    if (unroll == 2) hipLaunchKernelGGL((k_copy<2, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_copy<2, 1>), grid, block, 0, s, a);
+    if (unroll == 2) hipLaunchKernelGGL((k_copy<2, 2, ONE>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_copy<2, 1, ONE>), grid, block, 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s) {
+  bool one = true;  // every transfer has a single destination (ring all-gather steps)
+  for (int k = 0; k < a.nx; k++) one = one && a.x[k].ndst <= 1;
+  return one ? copy_go<true>(esize, a, unroll, s) : copy_go<false>(esize, a, unroll, s);
 }
 
 hipError_t launch_fill64(unsigned long long* p, unsigned long long v, int64_t n, hipStream_t s) {
