@@ -11,8 +11,8 @@ squares with relative weights (so microsecond and millisecond points count
 alike), and writes the JSON file sim_model_load() reads.
 
 The fit is a two-regime estimate (see fit()).  A launch-configuration sweep
-(sweep_workgroups) then stores the best total workgroups per size for the
-bulk schedules.  --check then times every legal schedule at the evaluation sizes (8192 x
+(sweep_workgroups) then stores the best (total workgroups, 16-byte vectors
+per lane) per size for the bulk schedules.  --check then times every legal schedule at the evaluation sizes (8192 x
 {1, 16, 256, 4096} tokens bf16, and 1 KiB .. 1 MiB fp16) and compares the
 selector's pick with the measured fastest: a strict match, and a tolerant
 match when the pick is within max(3%, the measured spread) of the best.
@@ -127,12 +127,14 @@ def fit(points, algo):
 
 # Launch-configuration sweep (after T-CCL's offline ranking of CTA
 # configurations per collective and size, section III-C3): the bulk
-# schedules at each grid size with a range of total workgroups; 0 is the
-# library's default (one workgroup per kBlock vectors, covering the
-# transfer).  The best total per size goes into the calibration file; a
-# total within 1% of the default's time keeps the default.
+# schedules at each grid size with a range of total workgroups and one or
+# two 16-byte vectors per lane; (0, 1) is the library's default (one vector
+# per lane, one workgroup per kBlock vectors, covering the transfer).  The
+# best pair per size goes into the calibration file; a pair within 1% of the
+# default's time keeps the default.
 WG_ALGOS = ("oneshot", "allpairs", "ring")
 WG_TOTALS = (0, 256, 512, 1024, 2048, 4096, 8192, 16384)
+WG_UNROLLS = (1, 2)  # 16-byte vectors per lane per pass
 
 
 def sweep_workgroups(sim, b, sizes):
@@ -145,18 +147,21 @@ def sweep_workgroups(sim, b, sizes):
                 continue
             n = nbytes // 2
             times = {}
-            for total in WG_TOTALS:
-                sim.sim_debug_set("workgroups", total)
-                times[total] = b.measure(algo, "bf16", n)[0]
+            for unroll in WG_UNROLLS:
+                sim.sim_debug_set("unroll", unroll)
+                for total in WG_TOTALS:
+                    sim.sim_debug_set("workgroups", total)
+                    times[(total, unroll)] = b.measure(algo, "bf16", n)[0]
             sim.sim_debug_set("workgroups", 0)
+            sim.sim_debug_set("unroll", 0)
             best = min(times, key=times.get)
-            if times[best] >= times[0] * 0.99:
-                best = 0
-            rows.append([nbytes, best])
+            if times[best] >= times[(0, 1)] * 0.99:  # keep the default unless it gains >= 1%
+                best = (0, 1)
+            rows.append([nbytes, best[0], best[1]])
             raw.setdefault(algo, []).append({"bytes_per_rank": nbytes,
-                                             "us": {str(k): round(v, 3) for k, v in times.items()}})
-            print(f"workgroups {algo:9s} {nbytes:>10d} B/rank best {best:6d} "
-                  + " ".join(f"{k}={v:.1f}" for k, v in times.items()), flush=True)
+                                             "us": {f"{t}x{u}": round(v, 3) for (t, u), v in times.items()}})
+            print(f"workgroups {algo:9s} {nbytes:>10d} B/rank best {best[0]:6d} x{best[1]} "
+                  + " ".join(f"{t}x{u}={v:.1f}" for (t, u), v in times.items()), flush=True)
         table[algo] = rows
     return table, raw
 

@@ -75,7 +75,7 @@ struct Ctx {
   uint32_t wait_skew = 0;
   int log = 0;
   int force_wg = 0;
-  int unroll = 1;
+  int unroll = 0;  // forced vectors per lane (debug hook); 0: the launch table's, else 1
   int last_algo = -1;
   int env_algo = 0;
   int ll_occ[4][5] = {};
@@ -238,6 +238,14 @@ struct Call {
 // for the nearest message size; SIM_CONFIG_MAX_WORKGROUPS caps the total
 // (T-CCL's restricted mode: communication given a fixed slice of the GPU);
 // SIM_DEBUG_WORKGROUPS forces a total.
+// 16-byte vectors per lane per pass of a bulk kernel: forced by the debug
+// hook, else the calibration's launch table entry for this call, else 1.
+int unroll_for(const Call& c) {
+  if (g.unroll > 0) return g.unroll;
+  const int u = model_launch(g.model, c.algo, (double)c.n * esize_of(c.dtype)).unroll;
+  return u > 0 ? u : 1;
+}
+
 int tiles_for(const Call& c, int64_t vecs_per_unit, int units, int unroll) {
   int64_t t;
   if (g.force_wg > 0) {
@@ -316,7 +324,7 @@ int run_fold(const Call& c, bool all_out, const std::vector<int64_t>& lo, const 
   for (int q = 0; q <= c.p; q++) a.lo[q] = lo[q];
   a.p = c.p;
   a.inv_p = inv_p_of(c.p);
-  const int unroll = (c.p == 8) ? g.unroll : 1;
+  const int unroll = (c.p == 8) ? unroll_for(c) : 1;  // the p = 8 kernels have a 2-vector form
   a.tiles = tiles_for(c, (maxchunk + V - 1) / V, c.p, unroll);
   if (all_out) {
     if (const PtrSet* set = ptr_set_for(c)) {  // the same launch from a 32-byte argument block
@@ -345,8 +353,9 @@ int run_copy_step(const Call& c, const std::vector<CopyXfer>& xs) {
     maxlen = std::max(maxlen, xs[k].hi - xs[k].lo);
   }
   if (a.nx == 0) return SIM_OK;
-  a.tiles = tiles_for(c, (maxlen + V - 1) / V, a.nx, g.unroll);
-  return hip_err(launch_copy(e, a, g.unroll, c.s));
+  const int unroll = unroll_for(c);
+  a.tiles = tiles_for(c, (maxlen + V - 1) / V, a.nx, unroll);
+  return hip_err(launch_copy(e, a, unroll, c.s));
 }
 
 // Ring reduce-scatter half.  final_out_chunk: outputs are chunk-sized (RS).
@@ -403,8 +412,9 @@ int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_c
       }
       x.vec_ok = (x.a_shift % V == 0) && (x.d_shift % V == 0);
     }
-    a.tiles = tiles_for(c, (maxchunk + V - 1) / V, a.nx, g.unroll);
-    int rc = hip_err(launch_ring_reduce(c.dtype, c.op, !first, last, a, g.unroll, c.s));
+    const int unroll = unroll_for(c);
+    a.tiles = tiles_for(c, (maxchunk + V - 1) / V, a.nx, unroll);
+    int rc = hip_err(launch_ring_reduce(c.dtype, c.op, !first, last, a, unroll, c.s));
     if (rc) return rc;
   }
   return SIM_OK;
@@ -1279,7 +1289,7 @@ int sim_debug_set(int key, uint64_t value) {
     case SIM_DEBUG_LOG: g.log = value ? 1 : 0; return SIM_OK;
     case SIM_DEBUG_WORKGROUPS: g.force_wg = (int)value; return SIM_OK;
     case SIM_DEBUG_UNROLL:
-      if (value != 1 && value != 2) return SIM_ERR_INVALID_ARG;
+      if (value > 2) return SIM_ERR_INVALID_ARG;
       g.unroll = (int)value;
       return SIM_OK;
     case SIM_DEBUG_FIFO_CHANNELS:

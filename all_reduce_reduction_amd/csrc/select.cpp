@@ -143,20 +143,25 @@ double model_traffic(int coll, int algo, int p, double n, int esize, const Topol
   return 0.0;
 }
 
-int model_workgroups(const Model& m, int algo, double bytes_per_rank) {
-  if (algo <= 0 || algo >= kNumAlgos || m.wg[algo].empty() || !(bytes_per_rank > 0)) return 0;
-  int best = 0;
+LaunchEntry model_launch(const Model& m, int algo, double bytes_per_rank) {
+  LaunchEntry best;
+  if (algo <= 0 || algo >= kNumAlgos || m.wg[algo].empty() || !(bytes_per_rank > 0)) return best;
+  const double lb = std::log2(bytes_per_rank);
   double bd = 0;
   bool found = false;
-  for (const auto& e : m.wg[algo]) {  // a total of 0 means: cover the transfer
-    const double d = std::fabs(std::log2(e.first) - std::log2(bytes_per_rank));
+  for (const auto& e : m.wg[algo]) {
+    const double d = std::fabs(e.lb - lb);
     if (!found || d < bd) {
-      best = e.second;
+      best = e;
       bd = d;
       found = true;
     }
   }
   return best;
+}
+
+int model_workgroups(const Model& m, int algo, double bytes_per_rank) {
+  return model_launch(m, algo, bytes_per_rank).total;
 }
 
 double model_predict(const Model& m, int coll, int algo, int p, double n, int esize, const Topology& t) {
@@ -371,15 +376,23 @@ bool model_load_json(const char* path, Model* m, std::string* err) {
         if (err) *err = "workgroup entry is not an array";
         return false;
       }
-      std::vector<std::pair<double, int>> v;
+      std::vector<LaunchEntry> v;
       for (const JVal& e : ai->second.arr) {
-        if (e.kind != JVal::ARR || e.arr.size() != 2 || e.arr[0].kind != JVal::NUM ||
-            e.arr[1].kind != JVal::NUM || !(e.arr[0].num > 0) || e.arr[1].num < 0 ||
-            e.arr[1].num > (double)(1 << 24)) {
-          if (err) *err = "workgroup entries are [bytes > 0, total in 0..2^24]";
+        const bool shape = e.kind == JVal::ARR && (e.arr.size() == 2 || e.arr.size() == 3);
+        bool ok = shape && e.arr[0].kind == JVal::NUM && e.arr[1].kind == JVal::NUM && e.arr[0].num > 0 &&
+                  e.arr[1].num >= 0 && e.arr[1].num <= (double)(1 << 24);
+        if (ok && e.arr.size() == 3)
+          ok = e.arr[2].kind == JVal::NUM && (e.arr[2].num == 1 || e.arr[2].num == 2);
+        if (!ok) {
+          if (err) *err = "workgroup entries are [bytes > 0, total in 0..2^24(, vectors per lane 1 or 2)]";
           return false;
         }
-        v.push_back({e.arr[0].num, (int)e.arr[1].num});
+        LaunchEntry le;
+        le.bytes = e.arr[0].num;
+        le.total = (int)e.arr[1].num;
+        le.unroll = e.arr.size() == 3 ? (int)e.arr[2].num : 0;
+        le.lb = std::log2(le.bytes);
+        v.push_back(le);
       }
       std::sort(v.begin(), v.end());
       out.wg[a] = v;

@@ -19,17 +19,29 @@ struct AlgoModel {
   double bytes_factor = -1.0;  // override of the traffic law (bytes per message byte) when >= 0
 };
 
+// One measured launch configuration.
+struct LaunchEntry {
+  double bytes = 0;  // bytes per rank it was measured at
+  int total = 0;     // total workgroups (0: cover every transfer exactly)
+  int unroll = 0;    // 16-byte vectors per lane per pass, 1 or 2 (0: the default, 1)
+  double lb = 0;     // log2(bytes), kept for the nearest-size lookup
+  bool operator<(const LaunchEntry& o) const { return bytes < o.bytes; }
+};
+
 struct Model {
   AlgoModel a[kNumAlgos];
   // Measured launch configurations (after T-CCL's ranked CTA-config table):
-  // per algo, (bytes per rank, total workgroups) pairs from the calibration
-  // sweep, ascending in bytes; empty = cover every transfer exactly.
-  std::vector<std::pair<double, int>> wg[kNumAlgos];
+  // per algo, entries from the calibration sweep, ascending in bytes; empty
+  // = cover every transfer exactly with one vector per lane.
+  std::vector<LaunchEntry> wg[kNumAlgos];
   std::string source = "built-in defaults";
 };
 
-// Total workgroups the table holds for (algo, bytes per rank): the entry of
-// the nearest size on a log scale; 0 when the table has none.
+// The table's entry for (algo, bytes per rank): the one of the nearest size
+// on a log scale; a default entry (total 0, unroll 0) when the table has
+// none.
+LaunchEntry model_launch(const Model& m, int algo, double bytes_per_rank);
+// Its total workgroups (0: cover the transfer).
 int model_workgroups(const Model& m, int algo, double bytes_per_rank);
 
 Model default_model();

@@ -190,10 +190,11 @@ int sim_last_algo(void);
 
 /* Load per-algo alpha (us per launch) and B (GB/s) from a JSON file
  * written by the calibration sweep, and its optional launch table
- * ("workgroups": {algo: [[bytes per rank, total workgroups], ...]}, after
- * T-CCL's ranked launch-configuration table, section III-C3): bulk kernels
- * of that algo then launch the measured best total of the nearest size
- * (log scale), never more than covers the transfer.  Errors:
+ * ("workgroups": {algo: [[bytes per rank, total workgroups(, vectors per
+ * lane)], ...]}, after T-CCL's ranked launch-configuration table, section
+ * III-C3): bulk kernels of that algo then launch the measured best total of
+ * the nearest size (log scale), never more than covers the transfer, with
+ * the entry's 16-byte vectors per lane (1 or 2; 1 when absent).  Errors:
  * SIM_ERR_INVALID_ARG (the current model is kept). */
 int sim_model_load(const char* json_path);
 
@@ -303,7 +304,8 @@ enum {
   SIM_DEBUG_FILL_LL = 3,       /* fill the LL buffer with this 64-bit packet (synchronous) */
   SIM_DEBUG_LOG = 4,           /* 1: log one line per call to stderr (also SIM_DEBUG=1) */
   SIM_DEBUG_WORKGROUPS = 5,    /* force the workgroup count of bulk kernels (0 = heuristic) */
-  SIM_DEBUG_UNROLL = 6,        /* 16-byte vectors per lane per pass in bulk kernels: 1 or 2 */
+  SIM_DEBUG_UNROLL = 6,        /* 16-byte vectors per lane per pass in bulk kernels: 1 or 2
+                                  (0, the default: the launch table's entry, else 1) */
   SIM_DEBUG_FIFO_CHANNELS = 7, /* single-launch ring: channels per rank, <= 128 (0 = heuristic) */
   SIM_DEBUG_FIFO_SLOTS = 8,    /* single-launch ring: slots per FIFO, 2..8 (default 4) */
   SIM_DEBUG_FIFO_WITHHOLD = 9, /* 1: rank 0's ring workgroups leave at once (forces a bounded-wait expiry) */

@@ -87,7 +87,7 @@ def test_table_path_vectors_per_lane(orc, lib, unroll):
             for t, f in zip(dout, empty_like_poisoned(n, dtype, p)):
                 t.copy_(f)
     finally:
-        sim.sim_debug_set("unroll", 1)
+        sim.sim_debug_set("unroll", 0)
 
 
 def test_same_pointers_new_contents(orc, lib):

@@ -23,6 +23,7 @@ def lib():
     sim.sim_config_set("max_workgroups", 0)
     sim.sim_config_set("ranks_per_node", 1)
     sim.sim_debug_set("workgroups", 0)
+    sim.sim_debug_set("unroll", 0)
     sim.sim_model_load(sim.CALIBRATION)
 
 
@@ -91,12 +92,14 @@ def test_forced_workgroups(orc, lib, total):
         lib.sim_debug_set("workgroups", 0)
 
 
-def test_launch_table(orc, lib, tmp_path):
+@pytest.mark.parametrize("unroll", [None, 1, 2])
+def test_launch_table(orc, lib, tmp_path, unroll):
     f = tmp_path / "table.json"
-    table = {a: [[1024, 16], [1 << 20, 40], [64 << 20, 0]] for a, _ in ALGOS}
+    extra = [] if unroll is None else [unroll]
+    table = {a: [[1024, 16] + extra, [1 << 20, 40] + extra, [64 << 20, 0] + extra] for a, _ in ALGOS}
     f.write_text(json.dumps({"algos": {}, "workgroups": table}))
     lib.sim_model_load(str(f))
     try:
-        _check_all(orc, lib, "table")
+        _check_all(orc, lib, f"table unroll {unroll}")
     finally:
         lib.sim_model_load(lib.CALIBRATION)

@@ -126,14 +126,16 @@ def test_launch_table_json(tmp_path):
     malformed tables are refused and leave the model as it was."""
     good = tmp_path / "wg.json"
     good.write_text(json.dumps({"algos": {"oneshot": {"alpha_us": 3.0, "gbps": 5000.0}},
-                                "workgroups": {"oneshot": [[1048576, 0], [67108864, 4096]],
-                                               "ring": [[4096, 64]]}}))
+                                "workgroups": {"oneshot": [[1048576, 0], [67108864, 4096, 2]],
+                                               "ring": [[4096, 64, 1]]}}))
     try:
         sim.sim_model_load(str(good))
         assert sim.sim_model_predict("oneshot", 8, "bf16", 1 << 20) == pytest.approx(
             3.0 + 16 * (1 << 20) / 5000.0e3)
         for table in ('{"oneshot": [[0, 10]]}', '{"oneshot": [[4096, -1]]}', '{"oneshot": [4096, 16]}',
-                      '{"oneshot": {"4096": 16}}', '[1, 2]'):
+                      '{"oneshot": {"4096": 16}}', '[1, 2]', '{"oneshot": [[4096, 16, 3]]}',
+                      '{"oneshot": [[4096, 16, 0]]}', '{"oneshot": [[4096, 16, "2"]]}',
+                      '{"oneshot": [[4096, 16, 2, 1]]}'):
             bad = tmp_path / "bad.json"
             bad.write_text('{"algos": {"oneshot": {"alpha_us": 9.0, "gbps": 1.0}}, "workgroups": %s}' % table)
             with pytest.raises(sim.SimError):
@@ -143,6 +145,15 @@ def test_launch_table_json(tmp_path):
                 3.0 + 16 * (1 << 20) / 5000.0e3)
     finally:
         sim.sim_model_reset()
+
+
+def test_unroll_debug_hook_range():
+    assert sim.sim_debug_get("unroll") == 0  # default: the launch table decides
+    for v in (1, 2, 0):
+        sim.sim_debug_set("unroll", v)
+        assert sim.sim_debug_get("unroll") == v
+    with pytest.raises(sim.SimError):
+        sim.sim_debug_set("unroll", 3)
 
 
 def test_workgroup_budget_config():
