@@ -84,6 +84,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* base, int64_t a
 }
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Byte offset in a FIFO slot of fp32 partial e (0 <= e < V) of vector u of
+// lane t.  The slot holds 16-byte words ordered [u][e / 4][t], so each
+// 16-byte store or load instruction of a wave covers one contiguous
+// 1 KiB run.  (Laid out element by element, a lane's V = 8 partials of a
+// 16-bit vector span 32 bytes and each instruction would cover every other
+// 16 bytes: half lines, which the device-scope stores wrote through to
+// memory as separate partial writes -- twice the FIFO bytes in the write
+// counters.)  The producer and the consumer of a slot run the same (u, t, e)
+// over the same elements, so the layout is private to this kernel.
+template <int V>
+__device__ __forceinline__ int fifo_off(int u, int t, int e) {
+  return ((u * (V / 4) + e / 4) * kBlock + t) * 16 + (e % 4) * 4;
+}
+
 // thread 0 polls *p until it reaches `want` (or the spin limit); the whole
 // workgroup learns the outcome through *flag_lds.  Returns false on
 // timeout.  Each call site owns its flag word: a lane reads the flag after
@@ -206,7 +220,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
             if (part_in) {
 #pragma unroll
               for (int h = 0; h < V / 4; h++)
-                fin[u][h] = __builtin_amdgcn_raw_buffer_load_b128(in_rs, in_base + (int)(off + 4 * h) * 4, 0, kLd);
+                fin[u][h] = __builtin_amdgcn_raw_buffer_load_b128(in_rs, in_base + fifo_off<V>(u, tid, 4 * h), 0, kLd);
             } else if (do_recv) {  // gather: the predecessor's finished storage vector
               fin[u][0] = __builtin_amdgcn_raw_buffer_load_b128(pv_y, (int)(off * E), 0, kLd);
             }
@@ -247,7 +261,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
                   u32x4 q;
 #pragma unroll
                   for (int e = 0; e < 4; e++) q[e] = __builtin_bit_cast(uint32_t, v[4 * h + e]);
-                  __builtin_amdgcn_raw_buffer_store_b128(q, out_rs, out_base + (int)(off + 4 * h) * 4, 0, kSt);
+                  __builtin_amdgcn_raw_buffer_store_b128(q, out_rs, out_base + fifo_off<V>(u, tid, 4 * h), 0, kSt);
                 }
               }
             } else {  // gather: keep the finished vector and pass it on through my output
@@ -266,7 +280,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
                   val = own;
                 } else {
                   const uint32_t bits =
-                      __builtin_amdgcn_raw_buffer_load_b32(in_rs, in_base + (int)(off + e) * 4, 0, kLd);
+                      __builtin_amdgcn_raw_buffer_load_b32(in_rs, in_base + fifo_off<V>(u, tid, e), 0, kLd);
                   val = O::comb(__builtin_bit_cast(A, bits), own);
                 }
                 if (finish) {
@@ -275,7 +289,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_fifo(RingFifoArgs a) {
                   else __builtin_amdgcn_raw_buffer_store_b16((unsigned short)narrow_bits<DT>(val), my_y, yoff, 0, kSt);
                 } else {
                   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), out_rs,
-                                                        out_base + (int)(off + e) * 4, 0, kSt);
+                                                        out_base + fifo_off<V>(u, tid, e), 0, kSt);
                 }
               } else {
                 uint32_t word;
