@@ -33,15 +33,15 @@ namespace simar {
 Model default_model() {
   Model m;
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING] = {4.2, 5850.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ALLPAIRS] = {4.6, 5600.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT] = {4.4, 5650.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT_LL] = {8.0, 7400.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING_FIFO] = {28.5, 4400.0, -1.0, -1.0};
-  m.a[SIM_ALGO_TREE] = {4.6, 6000.0, -1.0, -1.0};
-  m.a[SIM_ALGO_REXCH] = {4.3, 5250.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER] = {4.9, 5850.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER_LARGE] = {5.0, 5850.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING] = {4.2, 5900.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ALLPAIRS] = {4.3, 5700.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT] = {3.6, 5700.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT_LL] = {8.0, 7050.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING_FIFO] = {29.9, 6500.0, -1.0, -1.0};
+  m.a[SIM_ALGO_TREE] = {4.2, 5950.0, -1.0, -1.0};
+  m.a[SIM_ALGO_REXCH] = {4.4, 5250.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER] = {4.5, 6000.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER_LARGE] = {4.7, 5850.0, -1.0, -1.0};
   return m;
 }
 
