@@ -34,7 +34,7 @@ STATUS_CODE = {v: k for k, v in STATUS.items()}
 DTYPES = {"int32": 0, "fp32": 1, "fp16": 2, "bf16": 3}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
 ALGOS = {"auto": 0, "ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4, "ring_fifo": 5,
-         "tree": 6, "rexch": 7, "hier": 8, "hier_large": 9}
+         "tree": 6, "rexch": 7, "hier": 8, "hier_large": 9, "allpairs_persistent": 10}
 TOPOLOGY_ALGOS = ("tree", "rexch", "hier", "hier_large")
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 ESIZE = {"int32": 4, "fp32": 4, "fp16": 2, "bf16": 2}

@@ -29,7 +29,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_OUT = os.path.join(HERE, "calib", "mi355x.json")
-ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo")
+ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo", "allpairs_persistent")
 # The topology schedules are fitted too (sim_model_predict prices them),
 # each at the topology stated here; AUTO does not weigh them.
 TOPOLOGY = {"tree": (1, 2), "rexch": (1, 2), "hier": (4, 2), "hier_large": (4, 2)}  # (ranks per node, radix)

@@ -101,6 +101,7 @@ struct Ctx {
   std::vector<PtrSlot> ptab_slots;
 
   int fifo_occ[4][5] = {};
+  int ap_occ[4][5][2] = {};  // persistent all-pairs: [dtype][op][p == 8]
   Model model = default_model();
 };
 
@@ -108,8 +109,8 @@ Ctx g;
 
 int esize_of(int dtype) { return (dtype == SIM_FP16 || dtype == SIM_BF16) ? 2 : 4; }
 const char* algo_name(int a) {
-  static const char* n[] = {"auto",      "ring", "allpairs", "oneshot", "oneshot_ll",
-                            "ring_fifo", "tree", "rexch",    "hier",    "hier_large"};
+  static const char* n[] = {"auto",  "ring", "allpairs", "oneshot",    "oneshot_ll",         "ring_fifo",
+                            "tree",  "rexch", "hier",    "hier_large", "allpairs_persistent"};
   return (a >= 0 && a < SIM_NUM_ALGOS) ? n[a] : "?";
 }
 constexpr int kLastAlgo = SIM_NUM_ALGOS - 1;
@@ -420,6 +421,69 @@ int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_c
   return SIM_OK;
 }
 
+// The epoch of a call of a persistent kernel (the single-launch ring and
+// all-pairs share the semaphore array and this one monotonic count, so a
+// counter value left by any earlier call compares lower than anything the
+// new call waits for).  On wrap every counter is cleared first.
+int next_sem_epoch(const Call& c, uint32_t* epoch) {
+  uint32_t e = g.fifo_epoch + 1;
+  if (e == 0) {
+    int rc = hip_err(launch_fill64(g.fifo_sem, 0ull, (int64_t)g.p_max * kFifoMaxChannels * 2, c.s));
+    if (rc) return rc;
+    e = 1;
+  }
+  g.fifo_epoch = e;
+  *epoch = e;
+  return SIM_OK;
+}
+
+// The two all-pairs steps in one launch (k_allpairs_persistent): p * C
+// persistent workgroups, all co-resident; channel c of every rank handles
+// the same slice of each chunk.
+int run_allpairs_persistent(const Call& c, const std::vector<int64_t>& lo) {
+  const int p = c.p;
+  const int V = 16 / esize_of(c.dtype);
+  AllPairsPArgs a;
+  std::memset(&a, 0, sizeof a);
+  int64_t maxchunk = 0;
+  for (int q = 0; q < p; q++) {
+    a.x[q] = c.x[q];
+    a.y[q] = c.y[q];
+    maxchunk = std::max(maxchunk, lo[q + 1] - lo[q]);
+  }
+  for (int q = 0; q <= p; q++) a.lo[q] = lo[q];
+  int& occ = g.ap_occ[c.dtype][c.op][p == 8 ? 1 : 0];
+  if (occ == 0) occ = allpairs_persistent_blocks_per_cu(c.dtype, c.op, p);
+  const int64_t resident = (int64_t)occ * g.cu_count;  // every workgroup must be resident at once
+  // one pass (kAllPairsPVecsPerLane vectors per lane) per slice, but at
+  // least 8 channels while a slice still holds a vector per lane: small
+  // messages want the parallelism (measured on MI355X: 256 KiB per rank
+  // 9.3 -> 8.2 us; one vector per lane everywhere cost 4 MiB 12%)
+  const int64_t lane_elems = (int64_t)kBlock * V;
+  const int64_t span = lane_elems * kAllPairsPVecsPerLane;
+  int64_t C = std::max((maxchunk + span - 1) / span, std::min<int64_t>(8, (maxchunk + lane_elems - 1) / lane_elems));
+  if (g.fifo_channels > 0) C = g.fifo_channels;
+  C = std::max<int64_t>(C, 1);
+  C = std::min<int64_t>(C, kFifoMaxChannels);
+  C = std::min<int64_t>(C, std::max<int64_t>(1, resident / p));
+  if (g_max_wg > 0) C = std::min<int64_t>(C, std::max(1, g_max_wg / p));  // at least one per rank
+  int64_t Cg = (C + 7) / 8 * 8;  // rank-major grid padded to whole rounds of the 8 XCDs
+  if ((int64_t)p * Cg > resident || g_max_wg > 0) Cg = C;
+  uint32_t epoch = 0;
+  int rc = next_sem_epoch(c, &epoch);
+  if (rc) return rc;
+  a.sem = g.fifo_sem;
+  a.err = g.err;
+  a.spin_limit = g.spin_limit;
+  a.p = p;
+  a.C = (int)C;
+  a.Cg = (int)Cg;
+  a.epoch = epoch;
+  a.inv_p = inv_p_of(p);
+  a.withhold = g.fifo_withhold;
+  return hip_err(launch_allpairs_persistent(c.dtype, c.op, a, c.s));
+}
+
 // The whole ring in one launch (k_ring_fifo): p * C persistent workgroups,
 // all co-resident, exchanging partials through bounded FIFOs.
 int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
@@ -471,13 +535,9 @@ int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
     }
     g.fifo_bytes = need;
   }
-  uint32_t epoch = g.fifo_epoch + 1;
-  if (epoch == 0) {  // wrapped: clear every counter so no stale value can compare high
-    int rc = hip_err(launch_fill64(g.fifo_sem, 0ull, (int64_t)g.p_max * kFifoMaxChannels * 2, c.s));
-    if (rc) return rc;
-    epoch = 1;
-  }
-  g.fifo_epoch = epoch;
+  uint32_t epoch = 0;
+  int rc = next_sem_epoch(c, &epoch);
+  if (rc) return rc;
   a.fifo = g.fifo;
   a.sem = g.fifo_sem;
   a.err = g.err;
@@ -660,6 +720,8 @@ int run_allreduce(const Call& c) {
     }
     case SIM_ALGO_RING_FIFO:
       return run_ring_fifo(c, lo);
+    case SIM_ALGO_ALLPAIRS_PERSISTENT:
+      return run_allpairs_persistent(c, lo);
     case SIM_ALGO_ONESHOT_LL: {
       LLArgs a;
       std::memset(&a, 0, sizeof a);
@@ -771,9 +833,12 @@ int run_all_gather(const Call& c) {
 
 // legal candidates for AUTO / explicit requests
 bool legal(int coll, int algo, int p, size_t n, int dtype) {
-  // LL and the single-launch ring carry a per-call epoch in their kernel
-  // arguments: a replayed graph would repeat it and accept stale flags
-  if (g.capturing && (algo == SIM_ALGO_ONESHOT_LL || algo == SIM_ALGO_RING_FIFO)) return false;
+  // LL and the single-launch ring and all-pairs carry a per-call epoch in
+  // their kernel arguments: a replayed graph would repeat it and accept
+  // stale flags
+  if (g.capturing && (algo == SIM_ALGO_ONESHOT_LL || algo == SIM_ALGO_RING_FIFO ||
+                      algo == SIM_ALGO_ALLPAIRS_PERSISTENT))
+    return false;
   if (coll == COLL_ALLREDUCE) {
     if (algo == SIM_ALGO_ONESHOT_LL) return n * (size_t)esize_of(dtype) <= SIM_LL_MAX_BYTES_PER_RANK;
     if (is_topology_algo(algo)) return cached_schedule(coll, algo, p, g_topo, nullptr) != nullptr;
@@ -787,7 +852,9 @@ int pick(int coll, int p, size_t n, int dtype, int* algo, double* us) {
   double bt = 0;
   // AUTO weighs the single-node schedules; the tree, recursive-exchange and
   // 2PH schedules model multi-node topologies and run when asked for by name
-  for (int a = SIM_ALGO_RING; a <= SIM_ALGO_RING_FIFO; a++) {
+  static const int kCandidates[] = {SIM_ALGO_RING,   SIM_ALGO_ALLPAIRS,  SIM_ALGO_ONESHOT,
+                                    SIM_ALGO_ONESHOT_LL, SIM_ALGO_RING_FIFO, SIM_ALGO_ALLPAIRS_PERSISTENT};
+  for (int a : kCandidates) {
     if (!legal(coll, a, p, n, dtype)) continue;
     const double t = model_predict(g.model, coll, a, p, (double)n, esize_of(dtype), g_topo);
     if (best < 0 || t < bt) {

@@ -49,40 +49,12 @@
 // Every wait is bounded by spin_limit polls; on expiry the workgroup writes
 // SIM_ERR_TIMEOUT to the error word and leaves, so a missing partner (e.g.
 // workgroups that could not be co-resident) ends in an error, never a hang.
-#include "device_common.h"
+#include "device_sync.h"
 #include "kernels.h"
 
 namespace simar {
 
 namespace {
-
-__device__ __forceinline__ unsigned long long tag(unsigned epoch, unsigned long long count) {
-  return ((unsigned long long)epoch << 32) | count;
-}
-
-// Device-scope (sc1) accesses to FIFO words through a buffer resource
-// covering one FIFO (offsets are bytes; out-of-range offsets are dropped by
-// the hardware bounds check of the resource).
-constexpr int kSC1 = 16;  // cache-policy bit: coherent at device scope
-// cache policy of the device-scope loads and stores (the build may add the
-// nontemporal bit, 2, to either)
-#ifndef SIMAR_FIFO_LOAD_AUX
-#define SIMAR_FIFO_LOAD_AUX 16
-#endif
-#ifndef SIMAR_FIFO_STORE_AUX
-#define SIMAR_FIFO_STORE_AUX 16
-#endif
-constexpr int kLd = SIMAR_FIFO_LOAD_AUX;
-constexpr int kSt = SIMAR_FIFO_STORE_AUX;
-static_assert((kLd & kSC1) != 0 && (kSt & kSC1) != 0, "FIFO and peer accesses must stay device-scope");
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t fifo_rsrc(uint32_t* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
-}
-// a buffer resource over `bytes` bytes of an output buffer from byte `at`
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* base, int64_t at, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((char*)base + at, (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Byte offset in a FIFO slot of fp32 partial e (0 <= e < V) of vector u of
 // lane t.  The slot holds 16-byte words ordered [u][e / 4][t], so each
@@ -96,31 +68,6 @@ __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)
 template <int V>
 __device__ __forceinline__ int fifo_off(int u, int t, int e) {
   return ((u * (V / 4) + e / 4) * kBlock + t) * 16 + (e % 4) * 4;
-}
-
-// thread 0 polls *p until it reaches `want` (or the spin limit); the whole
-// workgroup learns the outcome through *flag_lds.  Returns false on
-// timeout.  Each call site owns its flag word: a lane reads the flag after
-// this barrier and before the end-of-step barrier, and the flag is only
-// rewritten (by the same call site) after that end-of-step barrier.
-__device__ __forceinline__ bool wait_geq(unsigned long long* p, unsigned long long want,
-                                         unsigned long long spin_limit, int* flag_lds) {
-  if (threadIdx.x == 0) {
-    unsigned long long v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned long long spins = 0;
-    bool ok = true;
-    while (v < want) {
-      if (++spins > spin_limit) {
-        ok = false;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-      v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    *flag_lds = ok ? 1 : 0;
-  }
-  __syncthreads();
-  return *flag_lds != 0;
 }
 
 }  // namespace

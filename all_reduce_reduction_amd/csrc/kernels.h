@@ -132,6 +132,27 @@ struct RingFifoArgs {
   int withhold;                // test hook: rank 0 leaves at once, its partners' waits expire
 };
 
+// The all-pairs schedule in ONE launch: p * C persistent workgroups.
+// Workgroup (rank r, channel c) folds its slice of chunk r from every
+// rank's input into Y[r] (owner first, then ascending) and signals; then,
+// for every other owner j, it waits for (j, c)'s signal and copies that
+// slice of Y[j] into Y[r].
+struct AllPairsPArgs {
+  const void* x[SIM_MAX_RANKS];
+  void* y[SIM_MAX_RANKS];
+  int64_t lo[SIM_MAX_RANKS + 1];
+  unsigned long long* sem;     // ready counter of (r, c) = word (r * C + c) * 2 (the ring's semaphore array)
+  int* err;
+  unsigned long long spin_limit;
+  int p;
+  int C;                       // channels per rank
+  int Cg;                      // channels in the grid (C rounded up to a multiple of 8: rank-major grid)
+  unsigned int epoch;
+  float inv_p;
+  int withhold;                // test hook: rank 0 leaves at once, its partners' waits expire
+};
+constexpr int kAllPairsPVecsPerLane = 2;  // 16-byte vectors per lane per pass
+
 // One step of the tree, recursive-exchange and 2PH schedules: a set of
 // folds, each over one chunk.  A fold's operands are ranks' current values
 // in fold order -- an input (widened, avg-scaled as it is read) or an
@@ -161,6 +182,7 @@ static_assert(sizeof(FoldArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(FoldTabArgs) <= 64, "must fit the small-argument launch path");
 static_assert(sizeof(SchedArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingFifoArgs) <= 4096, "kernel argument segment too large");
+static_assert(sizeof(AllPairsPArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(CopyArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(LLArgs) <= 4096, "kernel argument segment too large");
@@ -179,5 +201,7 @@ int ll_blocks_per_cu(int dtype, int op);
 hipError_t launch_ring_fifo(int dtype, int op, const RingFifoArgs& a, hipStream_t s);
 hipError_t launch_sched_fold(int dtype, int op, const SchedArgs& a, hipStream_t s);
 int ring_fifo_blocks_per_cu(int dtype, int op);
+hipError_t launch_allpairs_persistent(int dtype, int op, const AllPairsPArgs& a, hipStream_t s);
+int allpairs_persistent_blocks_per_cu(int dtype, int op, int p);
 
 }  // namespace simar

@@ -309,7 +309,8 @@ bool lower(int coll, int algo, int p, const Topology& topo, Schedule* out) {
   const int G = s.topo.ranks_per_node;
   // the single-launch ring executes the same schedule as the ring
   const bool ring = (algo == SIM_ALGO_RING || algo == SIM_ALGO_RING_FIFO);
-  const bool allpairs = (algo == SIM_ALGO_ALLPAIRS);
+  // the single-launch all-pairs executes the same two steps as the all-pairs
+  const bool allpairs = (algo == SIM_ALGO_ALLPAIRS || algo == SIM_ALGO_ALLPAIRS_PERSISTENT);
   const bool fused = (algo == SIM_ALGO_ONESHOT || algo == SIM_ALGO_ONESHOT_LL);
   if (coll == COLL_ALLREDUCE) {
     if (ring) {
@@ -345,7 +346,7 @@ bool lower(int coll, int algo, int p, const Topology& topo, Schedule* out) {
     if (ring) {
       ring_rs_steps(p, &s);
       s.rounds = p - 1;
-    } else if (allpairs) {
+    } else if (algo == SIM_ALGO_ALLPAIRS) {
       std::vector<Xfer> a;
       for (int j = 0; j < p; j++) a.push_back({XK_GATHER_REDUCE, -1, j, j});
       s.steps.push_back(a);
@@ -364,7 +365,7 @@ bool lower(int coll, int algo, int p, const Topology& topo, Schedule* out) {
         s.steps.push_back(v);
       }
       s.rounds = p - 1;
-    } else if (allpairs) {
+    } else if (algo == SIM_ALGO_ALLPAIRS) {
       std::vector<Xfer> a;
       for (int j = 0; j < p; j++) a.push_back({XK_FANOUT, j, -1, j});
       s.steps.push_back(a);
@@ -419,6 +420,7 @@ std::string expected_expr(const Schedule& s, int c) {
       for (int k = 1; k <= p; k++) xs.push_back(rank_str(mod(c + k, p)));
       return fold_exprs(xs);
     case SIM_ALGO_ALLPAIRS:
+    case SIM_ALGO_ALLPAIRS_PERSISTENT:
     case SIM_ALGO_ONESHOT:
     case SIM_ALGO_ONESHOT_LL:  // owner first, then the others ascending
       xs.push_back(rank_str(c));
@@ -752,6 +754,7 @@ int closed_form_rounds(const Schedule& s) {
     case SIM_ALGO_RING_FIFO:
       return s.coll == COLL_ALLREDUCE ? 2 * (p - 1) : p - 1;
     case SIM_ALGO_ALLPAIRS:
+    case SIM_ALGO_ALLPAIRS_PERSISTENT:
     case SIM_ALGO_ONESHOT:
     case SIM_ALGO_ONESHOT_LL:
       return s.coll == COLL_ALLREDUCE ? 2 : 1;
@@ -841,7 +844,7 @@ bool verify(const Schedule& s, std::string* diag) {
     return false;
   }
   const bool one_step_per_round = !(s.algo == SIM_ALGO_ONESHOT || s.algo == SIM_ALGO_ONESHOT_LL ||
-                                    s.algo == SIM_ALGO_ALLPAIRS);
+                                    s.algo == SIM_ALGO_ALLPAIRS || s.algo == SIM_ALGO_ALLPAIRS_PERSISTENT);
   if (one_step_per_round && (int)s.steps.size() != want) {
     if (diag) *diag = fmt("schedule has %d steps, closed form is %d", (int)s.steps.size(), want);
     return false;

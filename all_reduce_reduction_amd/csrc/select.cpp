@@ -42,6 +42,7 @@ Model default_model() {
   m.a[SIM_ALGO_REXCH] = {4.4, 5250.0, -1.0, -1.0};
   m.a[SIM_ALGO_HIER] = {4.5, 6000.0, -1.0, -1.0};
   m.a[SIM_ALGO_HIER_LARGE] = {4.7, 5850.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {5.0, 5500.0, -1.0, -1.0};
   return m;
 }
 
@@ -53,6 +54,7 @@ int model_launches(int coll, int algo, int p, const Topology& t) {
     case SIM_ALGO_ALLPAIRS: return coll == COLL_ALLREDUCE ? 2 : 1;
     case SIM_ALGO_ONESHOT: return 1;
     case SIM_ALGO_ONESHOT_LL: return 1;
+    case SIM_ALGO_ALLPAIRS_PERSISTENT: return coll == COLL_ALLREDUCE ? 1 : -1;
     case SIM_ALGO_RING_FIFO: return 1;
   }
   if (is_topology_algo(algo) && coll == COLL_ALLREDUCE) {
@@ -114,6 +116,8 @@ double model_traffic(int coll, int algo, int p, double n, int esize, const Topol
       case SIM_ALGO_ONESHOT: return 2.0 * p * S;          // p inputs read, p outputs written
       case SIM_ALGO_ALLPAIRS: return (2.0 * p + 1.0) * S;  // step 1: pS + S; step 2: S + (p-1)S
       case SIM_ALGO_ONESHOT_LL: return 6.0 * p * S;        // pack 3pS, consume 3pS
+      case SIM_ALGO_ALLPAIRS_PERSISTENT:  // step 1: pS + S; step 2: every rank pulls (p-1) chunks: 2(p-1)S
+        return (3.0 * p - 1.0) * S;
       case SIM_ALGO_RING_FIFO:  // inputs and outputs once; fp32 partials through FIFOs; peer reads
         return 2.0 * p * S + (p - 1) * n * 8.0 + (p - 1) * n * e;
       case SIM_ALGO_RING: {
@@ -309,8 +313,8 @@ struct Parser {
   }
 };
 
-const char* kAlgoNames[kNumAlgos] = {"auto",       "ring", "allpairs", "oneshot", "oneshot_ll",
-                                     "ring_fifo", "tree", "rexch",    "hier",    "hier_large"};
+const char* kAlgoNames[kNumAlgos] = {"auto",      "ring",  "allpairs", "oneshot",    "oneshot_ll",         "ring_fifo",
+                                     "tree",      "rexch", "hier",     "hier_large", "allpairs_persistent"};
 
 }  // namespace
 

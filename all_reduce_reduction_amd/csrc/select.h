@@ -10,7 +10,7 @@
 
 namespace simar {
 
-constexpr int kNumAlgos = 10;  // indices are the SIM_ALGO_* codes (0 = AUTO unused)
+constexpr int kNumAlgos = 11;  // indices are the SIM_ALGO_* codes (0 = AUTO unused)
 
 struct AlgoModel {
   double alpha_us = 4.0;       // fixed cost per launch (sync step)

@@ -72,6 +72,8 @@ def algorithmic_bytes(algo: str) -> float:
         return rs + (P - 1) * n * (e + e)
     if algo == "ring_fifo":  # inputs and outputs once; fp32 partials through FIFOs; peer reads
         return 2.0 * P * S + (P - 1) * N * 8.0 + (P - 1) * N * ESIZE
+    if algo == "allpairs_persistent":  # step 1 pS + S; step 2 each rank pulls p-1 chunks: 2(p-1)S
+        return (3.0 * P - 1.0) * S
     raise ValueError(algo)
 
 
@@ -243,7 +245,8 @@ def main():
     reps = [time_calls(step, max(10, args.steps // 5), 2) for _ in range(5)]
     busbw = 2 * (P - 1) / P * S / t / 1e9
     kernel = {"oneshot": "k_fold (one-shot, all outputs)", "allpairs": "k_fold + k_copy",
-              "ring": "k_ring_reduce + k_copy", "ring_fifo": "k_ring_fifo"}[ran]
+              "ring": "k_ring_reduce + k_copy", "ring_fifo": "k_ring_fifo",
+              "allpairs_persistent": "k_allpairs_persistent"}[ran]
     achieved = algorithmic_bytes(ran) / t / 1e9
     traffic = load_traffic(ran)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -253,7 +256,7 @@ def main():
     extras = {}
     if not args.no_extras:
         per_algo = {}
-        for a in ("oneshot", "allpairs", "ring", "ring_fifo"):
+        for a in ("oneshot", "allpairs", "ring", "ring_fifo", "allpairs_persistent"):
             ta = time_calls(lambda a=a: step(a), max(10, args.steps // 4), 5)
             per_algo[a] = {"us": round(ta * 1e6, 2), "busbw_GBps": round(2 * (P - 1) / P * S / ta / 1e9, 1),
                            "hbm_algorithmic_GBps": round(algorithmic_bytes(a) / ta / 1e9, 1)}
@@ -302,7 +305,7 @@ def main():
         lout = [torch.empty(LAT_N, dtype=torch.int16, device=dev) for _ in range(P)]
         lip, lop = [t_.data_ptr() for t_ in lin], [t_.data_ptr() for t_ in lout]
         lat = {}
-        for a in ("oneshot", "oneshot_ll", "allpairs", "ring", "ring_fifo", "auto"):
+        for a in ("oneshot", "oneshot_ll", "allpairs", "ring", "ring_fifo", "allpairs_persistent", "auto"):
             call = sim.prepare_allreduce(lip, lop, P, LAT_N, "fp16", "sum", a, stream)
             if call() != 0:
                 raise sim.SimError(call(), f"sim_allreduce({a})")

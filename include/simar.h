@@ -44,8 +44,9 @@
  *     on the calling thread when another one is.
  *   - Graph capture: a collective enqueued on a stream that is being
  *     captured (hipStreamBeginCapture, torch.cuda.graph) is recorded like
- *     any other kernel launch and may be replayed.  SIM_ALGO_ONESHOT_LL and
- *     SIM_ALGO_RING_FIFO carry a per-call epoch in their kernel arguments,
+ *     any other kernel launch and may be replayed.  SIM_ALGO_ONESHOT_LL,
+ *     SIM_ALGO_RING_FIFO and SIM_ALGO_ALLPAIRS_PERSISTENT carry a per-call
+ *     epoch in their kernel arguments,
  *     which a replay would repeat: under capture they are
  *     SIM_ERR_UNSUPPORTED and AUTO skips them.  Library scratch cannot grow
  *     during capture (SIM_ERR_UNSUPPORTED): size it with sim_init's
@@ -107,8 +108,8 @@ enum {
 enum { SIM_INT32 = 0, SIM_FP32 = 1, SIM_FP16 = 2, SIM_BF16 = 3 };
 enum { SIM_SUM = 0, SIM_PROD = 1, SIM_MIN = 2, SIM_MAX = 3, SIM_AVG = 4 };
 enum {
-  SIM_ALGO_AUTO = 0,        /* alpha-beta argmin over the legal schedules 1..5 (the
-                               topology schedules 6..9 run only when named) */
+  SIM_ALGO_AUTO = 0,        /* alpha-beta argmin over the legal schedules 1..5 and 10
+                               (the topology schedules 6..9 run only when named) */
   SIM_ALGO_RING = 1,        /* 2(p-1) steps, one launch per step */
   SIM_ALGO_ALLPAIRS = 2,    /* 2 steps: owner gather-reduce, then fan-out */
   SIM_ALGO_ONESHOT = 3,     /* the 2 all-pairs steps fused in one launch */
@@ -120,10 +121,13 @@ enum {
   SIM_ALGO_REXCH = 7,       /* k-ary recursive exchange: log_k(p) rounds */
   SIM_ALGO_HIER = 8,        /* 2PH, small-message form: node-local reduce-scatter into
                                G chunks, all-pairs across nodes, node-local all-gather */
-  SIM_ALGO_HIER_LARGE = 9   /* 2PH, large-message form: p chunks; node-local and
+  SIM_ALGO_HIER_LARGE = 9,  /* 2PH, large-message form: p chunks; node-local and
                                cross-node reduce-scatter, then the two all-gathers */
+  SIM_ALGO_ALLPAIRS_PERSISTENT = 10  /* the 2 all-pairs steps in ONE launch: persistent
+                               workgroups, each owner signals its finished chunk and
+                               the other ranks wait and pull it (in-kernel signal/wait) */
 };
-#define SIM_NUM_ALGOS 10
+#define SIM_NUM_ALGOS 11
 
 #define SIM_MAX_RANKS 16
 /* LL packets carry 4 data bytes in 8: the LL buffer holds 2x the payload.

@@ -39,7 +39,7 @@ LIBPATH = os.path.join(_HERE, "liboracle.so")
 DTYPES = {"int32": 0, "fp32": 1, "fp16": 2, "bf16": 3}
 OPS = {"sum": 0, "prod": 1, "min": 2, "max": 3, "avg": 4}
 ALGOS = {"ring": 1, "allpairs": 2, "oneshot": 3, "oneshot_ll": 4, "ring_fifo": 5,
-         "tree": 6, "rexch": 7, "hier": 8, "hier_large": 9}
+         "tree": 6, "rexch": 7, "hier": 8, "hier_large": 9, "allpairs_persistent": 10}
 TOPO_ALGOS = ("tree", "rexch", "hier", "hier_large")
 STORAGE = {"int32": np.int32, "fp32": np.float32, "fp16": np.uint16, "bf16": np.uint16}
 

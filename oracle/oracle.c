@@ -76,7 +76,7 @@
 enum { OR_INT32 = 0, OR_FP32 = 1, OR_FP16 = 2, OR_BF16 = 3 };
 enum { OR_SUM = 0, OR_PROD = 1, OR_MIN = 2, OR_MAX = 3, OR_AVG = 4 };
 enum { OR_RING = 1, OR_ALLPAIRS = 2, OR_ONESHOT = 3, OR_ONESHOT_LL = 4, OR_RING_FIFO = 5,
-       OR_TREE = 6, OR_REXCH = 7, OR_HIER = 8, OR_HIER_LARGE = 9 };
+       OR_TREE = 6, OR_REXCH = 7, OR_HIER = 8, OR_HIER_LARGE = 9, OR_ALLPAIRS_PERSISTENT = 10 };
 #define OR_MAXP 128
 #define OR_EBADARG (-1)
 
@@ -526,7 +526,8 @@ int oracle_allreduce_topo(const void* const* X, void* const* Y, int p, int64_t n
     if (s1 < 0) return s1;
     return s1 + ring_all_gather_inplace(&c, Y, n);
   }
-  if (algo == OR_ALLPAIRS || algo == OR_ONESHOT || algo == OR_ONESHOT_LL)
+  /* the single-launch all-pairs runs the all-pairs' two steps: same order */
+  if (algo == OR_ALLPAIRS || algo == OR_ONESHOT || algo == OR_ONESHOT_LL || algo == OR_ALLPAIRS_PERSISTENT)
     return allpairs(&c, X, Y, n);
   return OR_EBADARG;
 }
@@ -605,10 +606,10 @@ int oracle_allreduce_at_topo(const void* const* X, int p, int64_t n, int dtype, 
                              int algo, int ranks_per_node, int radix,
                              const int64_t* idx, int64_t m, void* out) {
   if (check_args(p, n, dtype, op)) return OR_EBADARG;
-  if (algo < OR_RING || algo > OR_HIER_LARGE) return OR_EBADARG;
+  if (algo < OR_RING || algo > OR_ALLPAIRS_PERSISTENT) return OR_EBADARG;
   ctx_t c = make_ctx(p, dtype, op);
   for (int64_t k = 0; k < m; k++) if (idx[k] < 0 || idx[k] >= n) return OR_EBADARG;
-  if (algo >= OR_TREE) {   /* rank 0's value: every rank ends with the same */
+  if (algo >= OR_TREE && algo <= OR_HIER_LARGE) {   /* rank 0's value: every rank ends with the same */
     topo_t T;
     if (topo_init(&T, algo, p, ranks_per_node, radix)) return OR_EBADARG;
     #pragma omp parallel for schedule(static)

@@ -15,7 +15,7 @@ from fractions import Fraction
 import numpy as np
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo")
+ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo", "allpairs_persistent")
 TOPO_ALGOS = ("tree", "rexch", "hier", "hier_large")
 
 
@@ -63,7 +63,7 @@ def check_step_counts(orc):
         xs = [np.full(3 * p + 1, q, dtype=np.int32) for q in range(p)]
         assert orc.allreduce(xs, "int32", "sum", "ring")[1] == 2 * (p - 1), p
         assert orc.allreduce(xs, "int32", "sum", "ring_fifo")[1] == 2 * (p - 1), p
-        for algo in ("allpairs", "oneshot", "oneshot_ll"):
+        for algo in ("allpairs", "oneshot", "oneshot_ll", "allpairs_persistent"):
             assert orc.allreduce(xs, "int32", "sum", algo)[1] == 2, (p, algo)
 
 

@@ -55,6 +55,7 @@ def test_argument_errors_enqueue_nothing(lib):
         "rs oneshot": (sim.sim_reduce_scatter(I, O, 4, 256, "fp32", "sum", "oneshot", s), UNSUPPORTED),
         "ag ll": (sim.sim_all_gather(I, O, 4, 256, "fp32", "oneshot_ll", s), UNSUPPORTED),
         "rs ring_fifo": (sim.sim_reduce_scatter(I, O, 4, 256, "fp32", "sum", "ring_fifo", s), UNSUPPORTED),
+        "ag allpairs_persistent": (sim.sim_all_gather(I, O, 4, 256, "fp32", "allpairs_persistent", s), UNSUPPORTED),
     }
     for name, (got, want) in cases.items():
         assert got == want, (name, got, want)
@@ -257,3 +258,61 @@ def test_single_launch_ring_repeated_large(lib, orc):
                 assert_parity(got[r], want[r], "bf16", f"slots {ns} vecs {vecs} r{r}")
     sim.sim_debug_set("fifo_slots", 4)
     sim.sim_debug_set("fifo_vecs", 4)
+
+
+def test_single_launch_allpairs_missing_partner_times_out(lib, orc):
+    """The single-launch all-pairs with rank 0's workgroups leaving at once:
+    the other ranks' waits for rank 0's chunk expire, the kernel ends and
+    the error word says SIM_ERR_TIMEOUT; the next call is correct."""
+    import synthdata
+    from tests.gpu_util import empty_like_poisoned, ptrs, run_allreduce, stream, to_device
+    sim = lib
+    xs = synthdata.normal(50, 8, 8 * 4096 + 5, "bf16")
+    want, _ = orc.allreduce(xs, "bf16", "sum", "allpairs_persistent")
+    sim.sim_debug_set("spin_limit", 64)
+    sim.sim_debug_set("fifo_withhold", 1)
+    din = to_device(xs, "bf16")
+    dout = empty_like_poisoned(xs[0].size, "bf16", 8)
+    assert sim.sim_allreduce(ptrs(din), ptrs(dout), 8, xs[0].size, "bf16", "sum", "allpairs_persistent", stream()) == OK
+    assert sim.sim_check_error(stream()) == TIMEOUT
+    sim.sim_debug_set("fifo_withhold", 0)
+    sim.sim_debug_set("spin_limit", 1 << 20)
+    got = run_allreduce(xs, "bf16", "sum", "allpairs_persistent")
+    for r in range(8):
+        assert (got[r] == want[r]).all()
+
+
+def test_single_launch_allpairs_channels_and_shared_epoch(lib, orc):
+    """Channel counts from one to many (one slice per rank up to many
+    passes per slice), ragged sizes, in place, and calls alternating with
+    the single-launch ring, which shares the semaphore words and the epoch
+    count: a counter left by one schedule must never satisfy the other's
+    wait."""
+    import synthdata
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, run_allreduce, stream, to_device, to_host
+    sim = lib
+    n = 8 * 4096 * 7 + 333
+    xs = synthdata.normal(51, 8, n, "fp16")
+    want, _ = orc.allreduce(xs, "fp16", "sum", "allpairs_persistent")
+    want_ring, _ = orc.allreduce(xs, "fp16", "sum", "ring_fifo")
+    try:
+        for ch in (1, 3, 16, 128):
+            sim.sim_debug_set("fifo_channels", ch)
+            for inplace in (False, True):
+                print(f"allpairs_persistent channels {ch} inplace {inplace}", flush=True)
+                got = run_allreduce([x.copy() for x in xs], "fp16", "sum", "allpairs_persistent", inplace=inplace)
+                for r in range(8):
+                    assert_parity(got[r], want[r], "fp16", f"channels {ch} inplace {inplace} r{r}")
+        sim.sim_debug_set("fifo_channels", 0)
+        din = to_device(xs, "fp16")
+        outs = {a: empty_like_poisoned(n, "fp16", 8) for a in ("allpairs_persistent", "ring_fifo")}
+        for k in range(20):
+            a = "allpairs_persistent" if k % 2 == 0 else "ring_fifo"
+            assert sim.sim_allreduce(ptrs(din), ptrs(outs[a]), 8, n, "fp16", "sum", a, stream()) == OK
+        assert sim.sim_check_error(stream()) == OK
+        for a, w in (("allpairs_persistent", want), ("ring_fifo", want_ring)):
+            got = to_host(outs[a], "fp16")
+            for r in range(8):
+                assert_parity(got[r], w[r], "fp16", f"alternating {a} r{r}")
+    finally:
+        sim.sim_debug_set("fifo_channels", 0)

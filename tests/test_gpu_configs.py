@@ -55,7 +55,7 @@ def test_workload2_fp32_32MiB(orc):
     n = 8_388_608
     xs = synthdata.workload_inputs(2, 8, n, "fp32")
     outs = {}
-    for algo in ("ring", "allpairs", "oneshot", "ring_fifo"):
+    for algo in ("ring", "allpairs", "oneshot", "ring_fifo", "allpairs_persistent"):
         print(f"workload 2: {algo}", flush=True)
         got = _run(xs, "fp32", "sum", algo)
         want, steps = orc.allreduce(xs, "fp32", "sum", algo)
@@ -65,6 +65,7 @@ def test_workload2_fp32_32MiB(orc):
         outs[algo] = got[0]
     # one-shot and all-pairs share their order; the ring's differs
     assert (outs["oneshot"].view(np.uint32) == outs["allpairs"].view(np.uint32)).all()
+    assert (outs["allpairs_persistent"].view(np.uint32) == outs["allpairs"].view(np.uint32)).all()
     assert (outs["ring"].view(np.uint32) != outs["oneshot"].view(np.uint32)).any()
 
 
@@ -74,7 +75,7 @@ def test_workload3_bf16_tp(orc, tokens):
     from tests.gpu_util import assert_parity
     n = 8192 * tokens
     xs = synthdata.workload_inputs(3, 8, n, "bf16")
-    algos = ["ring", "allpairs", "oneshot", "ring_fifo", "auto"]
+    algos = ["ring", "allpairs", "oneshot", "ring_fifo", "allpairs_persistent", "auto"]
     if n * 2 <= sim.LL_MAX_BYTES_PER_RANK:
         algos.append("oneshot_ll")
     for algo in algos:
@@ -122,7 +123,7 @@ def test_workload5_allreduce_256MiB(orc, dtype, ops):
     idx = _sample_idx(n, p, rng)
     tidx = torch.from_numpy(idx).to(din[0].device)
     for op in ops:
-        for algo in ("auto", "ring", "ring_fifo"):
+        for algo in ("auto", "ring", "ring_fifo", "allpairs_persistent"):
             print(f"workload 5: {dtype} {op} {algo}", flush=True)
             st = sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, algo, stream())
             assert st == 0

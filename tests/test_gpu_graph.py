@@ -80,13 +80,13 @@ def test_epoch_schedules_are_refused_under_capture(orc, lib):
     xs = _fresh(p, n, "fp16", 62, orc)
     din = to_device(xs, "fp16")
     dout = empty_like_poisoned(n, "fp16", p)
-    for algo in ("oneshot_ll", "ring_fifo"):
+    for algo in ("oneshot_ll", "ring_fifo", "allpairs_persistent"):
         graph, st = _capture(sim, din, dout, p, n, "fp16", algo)
         assert st == -2, (algo, st)
         del graph
     # AUTO under capture picks a capturable schedule and the replay is right
     graph, st = _capture(sim, din, dout, p, n, "fp16", "auto")
-    assert st == 0 and sim.sim_last_algo() not in ("oneshot_ll", "ring_fifo")
+    assert st == 0 and sim.sim_last_algo() not in ("oneshot_ll", "ring_fifo", "allpairs_persistent")
     graph.replay()
     torch.cuda.synchronize()
     want, _ = orc.allreduce(xs, "fp16", "sum", sim.sim_last_algo())

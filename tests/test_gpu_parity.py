@@ -8,7 +8,7 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = ["ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"]
+ALGOS = ["ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo", "allpairs_persistent"]
 ESIZE = {"int32": 4, "fp32": 4, "fp16": 2, "bf16": 2}
 DTYPES = ["int32", "fp32", "fp16", "bf16"]
 OPS = ["sum", "prod", "min", "max", "avg"]
@@ -75,12 +75,12 @@ def test_worked_example_every_algo(orc):
 
 
 def test_oneshot_allpairs_ll_bit_identical(orc):
-    """The three share one fold order, so their fp results agree bit for bit,
+    """The four share one fold order, so their fp results agree bit for bit,
     while the ring's order gives different bits somewhere."""
     from tests.gpu_util import bits, run_allreduce
     xs = inputs(8, 8 * 5000, "fp32", 3, orc)
     outs = {a: run_allreduce(xs, "fp32", "sum", a) for a in ALGOS}
-    for a in ("allpairs", "oneshot_ll"):
+    for a in ("allpairs", "oneshot_ll", "allpairs_persistent"):
         for r in range(8):
             assert (bits(outs[a][r]) == bits(outs["oneshot"][r])).all(), a
     for r in range(8):  # the two executions of the ring agree bit for bit

@@ -11,7 +11,8 @@ import pytest
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = [("oneshot", 1), ("allpairs", 1), ("ring", 1), ("ring_fifo", 1), ("oneshot_ll", 1), ("tree", 2),
+ALGOS = [("oneshot", 1), ("allpairs", 1), ("ring", 1), ("ring_fifo", 1), ("allpairs_persistent", 1),
+         ("oneshot_ll", 1), ("tree", 2),
          ("rexch", 1), ("hier", 4), ("hier_large", 2)]
 
 

@@ -23,7 +23,7 @@ from hypothesis import strategies as st
 
 import all_reduce_reduction_amd as sim
 
-SINGLE = ["ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"]
+SINGLE = ["ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo", "allpairs_persistent"]
 
 
 def _topologies(p):

@@ -75,7 +75,7 @@ def test_bytes_sent_per_rank_is_optimal(p):
     assert all(v == 2 * (p - 1) for v in sent.values())
 
 
-@pytest.mark.parametrize("algo", ["ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"])
+@pytest.mark.parametrize("algo", ["ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo", "allpairs_persistent"])
 @pytest.mark.parametrize("p", range(2, 17))
 def test_verifier_proves_every_lowering(algo, p):
     st, diag = sim.sim_verify_schedule(algo, p)

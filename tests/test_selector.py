@@ -39,7 +39,7 @@ def test_printed_ratios(example_model):
 
 def test_argmin_switches_at_the_crossover(example_model):
     # make the other schedules unattractive so the choice is ring vs all-pairs
-    for other in ("oneshot", "oneshot_ll", "ring_fifo"):
+    for other in ("oneshot", "oneshot_ll", "ring_fifo", "allpairs_persistent"):
         sim.sim_model_set(other, 1e9, -1, -1, 1.0)
     x = model.crossover_bytes()
     below = int(x * 0.98) // 4 * 4
@@ -63,7 +63,7 @@ def test_ll_is_never_picked_above_its_buffer():
 
 def test_builtin_traffic_laws():
     sim.sim_model_reset()
-    for algo in ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo"):
+    for algo in ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo", "allpairs_persistent"):
         sim.sim_model_set(algo, 0.0, -1, -1, 1e-3)   # 1 MB/s: time in us == bytes
     S = 1 << 20
     n = S // 2
@@ -79,6 +79,9 @@ def test_builtin_traffic_laws():
     # slices read from the predecessor's output ((p-1) n e bytes): 51 S at p = 8
     assert sim.sim_model_predict("ring_fifo", 8, "bf16", S) == pytest.approx(16 * S + 7 * n * 8 + 7 * n * 2)
     assert sim.sim_model_predict("ring_fifo", 8, "fp32", S) == pytest.approx(16 * S + 7 * (S // 4) * 12)
+    # the single-launch all-pairs: step 1 reads pS and writes S; step 2 every
+    # rank reads the p-1 other finished chunks and writes them: 23 S at p = 8
+    assert sim.sim_model_predict("allpairs_persistent", 8, "bf16", S) == pytest.approx(23 * S)
     sim.sim_model_reset()
 
 
