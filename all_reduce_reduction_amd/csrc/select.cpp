@@ -42,7 +42,7 @@ Model default_model() {
   m.a[SIM_ALGO_REXCH] = {4.4, 5250.0, -1.0, -1.0};
   m.a[SIM_ALGO_HIER] = {4.5, 6000.0, -1.0, -1.0};
   m.a[SIM_ALGO_HIER_LARGE] = {4.7, 5850.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {5.0, 5500.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {6.6, 6600.0, -1.0, -1.0};
   return m;
 }
 
