@@ -53,6 +53,14 @@
  *     max_bytes_per_rank or make one uncaptured call of the same shape
  *     first.  Once a call has been captured, outgrown scratch is kept until
  *     sim_finalize, so recorded graphs stay valid until then (not after).
+ *   - Shared library buffers: the partial scratch (16-bit ring, tree,
+ *     recursive exchange and 2PH all-reduces; the ring reduce-scatter), the
+ *     LL packet buffer, and the FIFOs and counters of the single-launch
+ *     ring and all-pairs belong to the library, one set per process.  Calls
+ *     that use one of them must not run at the same time on different
+ *     streams (calls on one stream are ordered); one-shot, all-pairs, the
+ *     32-bit ring all-reduce, the ring all-gather and the all-pairs
+ *     reduce-scatter / all-gather use none and may overlap freely.
  *   - Pointer table: the first 512 distinct (p, in_ptrs, out_ptrs) sets of
  *     SIM_ALGO_ONESHOT calls made outside graph capture are copied once
  *     (asynchronously, on the call's stream) into a device-memory table
