@@ -235,7 +235,7 @@ def check(model_path: str):
                      "strict": s_ok, "tolerant": t_ok})
         print(f"check {dtype} {nbytes:>9d} B/rank pick {pick:10s} best {best:10s} "
               + " ".join(f"{a}={v:.1f}" for a, v in meas.items()), flush=True)
-    report = {"model": model_path, "cases": len(cases), "strict_matches": strict, "tolerant_matches": tolerant,
+    report = {"model": os.path.basename(model_path), "cases": len(cases), "strict_matches": strict, "tolerant_matches": tolerant,
               "rows": rows}
     print(json.dumps({"selector_check": {k: report[k] for k in ("cases", "strict_matches", "tolerant_matches")}}),
           flush=True)

@@ -33,7 +33,7 @@
  * OpenMP parallelises only over elements inside one chunk transfer; each
  * element's own sequence of operations is untouched by it.
  *
- * Readings of points the pages leave open (each listed in the design doc):
+ * Readings of points the pages leave open:
  *  - chunk c = elements [floor(c*n/p), floor((c+1)*n/p)).
  *  - ring: at reduce-scatter step s rank r sends chunk (r-1-s) mod p to rank
  *    r+1, which folds its own contribution in (accumulator first); at
