@@ -310,7 +310,12 @@ const PtrSet* ptr_set_for(const Call& c) {
   return g.ptab + i;
 }
 
-int run_fold(const Call& c, bool all_out, const std::vector<int64_t>& lo, const int64_t* out_shift) {
+// set: the call's entry in the pointer table, or nullptr.  With an entry the
+// launch carries a 32-byte argument block; that form computes the standard
+// chunk bounds itself and writes outputs unshifted, so it serves the
+// one-shot and all-pairs step 1 of an all-reduce (not the reduce-scatter).
+int run_fold(const Call& c, bool all_out, const std::vector<int64_t>& lo, const int64_t* out_shift,
+             const PtrSet* set) {
   FoldArgs a;
   std::memset(&a, 0, sizeof a);
   const int V = 16 / esize_of(c.dtype);
@@ -327,17 +332,15 @@ int run_fold(const Call& c, bool all_out, const std::vector<int64_t>& lo, const 
   a.inv_p = inv_p_of(c.p);
   const int unroll = (c.p == 8) ? unroll_for(c) : 1;  // the p = 8 kernels have a 2-vector form
   a.tiles = tiles_for(c, (maxchunk + V - 1) / V, c.p, unroll);
-  if (all_out) {
-    if (const PtrSet* set = ptr_set_for(c)) {  // the same launch from a 32-byte argument block
-      FoldTabArgs t;
-      std::memset(&t, 0, sizeof t);
-      t.set = set;
-      t.n = (int64_t)c.n;
-      t.p = c.p;
-      t.tiles = a.tiles;
-      t.inv_p = a.inv_p;
-      return hip_err(launch_fold_tab(c.dtype, c.op, c.p, t, unroll, c.s));
-    }
+  if (set && out_shift == nullptr) {
+    FoldTabArgs t;
+    std::memset(&t, 0, sizeof t);
+    t.set = set;
+    t.n = (int64_t)c.n;
+    t.p = c.p;
+    t.tiles = a.tiles;
+    t.inv_p = a.inv_p;
+    return hip_err(launch_fold_tab(c.dtype, c.op, c.p, all_out, t, unroll, c.s));
   }
   return hip_err(launch_fold(c.dtype, c.op, c.p, all_out, a, unroll, c.s));
 }
@@ -682,10 +685,24 @@ int run_allreduce(const Call& c) {
   for (int q = 0; q <= p; q++) lo[q] = chunk_lo((int64_t)c.n, p, q);
   switch (c.algo) {
     case SIM_ALGO_ONESHOT:
-      return run_fold(c, true, lo, nullptr);
+      return run_fold(c, true, lo, nullptr, ptr_set_for(c));
     case SIM_ALGO_ALLPAIRS: {
-      int rc = run_fold(c, false, lo, nullptr);  // step 1: GATHER_REDUCE into each owner
+      const PtrSet* set = ptr_set_for(c);
+      int rc = run_fold(c, false, lo, nullptr, set);  // step 1: GATHER_REDUCE into each owner
       if (rc) return rc;
+      if (set) {  // step 2 (FANOUT) from the same table entry
+        const int V = 16 / esize_of(c.dtype);
+        int64_t maxchunk = 0;
+        for (int q = 0; q < p; q++) maxchunk = std::max(maxchunk, lo[q + 1] - lo[q]);
+        const int unroll = unroll_for(c);
+        FanoutTabArgs f;
+        std::memset(&f, 0, sizeof f);
+        f.set = set;
+        f.n = (int64_t)c.n;
+        f.p = p;
+        f.tiles = tiles_for(c, (maxchunk + V - 1) / V, p, unroll);
+        return hip_err(launch_fanout_tab(esize_of(c.dtype), f, unroll, c.s));
+      }
       std::vector<CopyXfer> xs;                  // step 2: FANOUT from each owner
       for (const Xfer& xf : sch->steps[1]) {
         CopyXfer x;
@@ -773,7 +790,7 @@ int run_reduce_scatter(const Call& c) {
   if (c.algo == SIM_ALGO_ALLPAIRS) {
     std::vector<int64_t> shift(p);
     for (int q = 0; q < p; q++) shift[q] = lo[q];
-    return run_fold(c, false, lo, shift.data());
+    return run_fold(c, false, lo, shift.data(), nullptr);
   }
   return run_ring_rs(c, *sch, p - 1, true, lo);
 }

@@ -29,8 +29,10 @@
 // operand) is done element by element so every element keeps its own
 // chunk's order.
 //
-// The one-shot also runs from a small argument block whose rank pointers
-// sit in device memory (FoldTabArgs); both argument forms are read through
+// The one-shot and all-pairs step 1 also run from a small argument block
+// whose rank pointers sit in device memory (FoldTabArgs; it computes the
+// standard chunk bounds and writes outputs unshifted, so the direct
+// reduce-scatter keeps the full form); both argument forms are read through
 // the accessors below, and every pointer is loaded once, before the first
 // store.
 #include <type_traits>
@@ -176,16 +178,11 @@ static hipError_t go(const Args& a, hipStream_t s) {
 
 template <int DT, int OP, class Args>
 static hipError_t by_shape(int p, bool all_out, int unroll, const Args& a, hipStream_t s) {
-  if constexpr (std::is_same<Args, FoldTabArgs>::value) {  // the one-shot only
-    if (p == 8) return unroll == 2 ? go<DT, OP, 8, true, 2>(a, s) : go<DT, OP, 8, true, 1>(a, s);
-    return go<DT, OP, 0, true, 1>(a, s);
-  } else {
-    if (p == 8) {
-      if (all_out) return unroll == 2 ? go<DT, OP, 8, true, 2>(a, s) : go<DT, OP, 8, true, 1>(a, s);
-      return unroll == 2 ? go<DT, OP, 8, false, 2>(a, s) : go<DT, OP, 8, false, 1>(a, s);
-    }
-    return all_out ? go<DT, OP, 0, true, 1>(a, s) : go<DT, OP, 0, false, 1>(a, s);
+  if (p == 8) {
+    if (all_out) return unroll == 2 ? go<DT, OP, 8, true, 2>(a, s) : go<DT, OP, 8, true, 1>(a, s);
+    return unroll == 2 ? go<DT, OP, 8, false, 2>(a, s) : go<DT, OP, 8, false, 1>(a, s);
   }
+  return all_out ? go<DT, OP, 0, true, 1>(a, s) : go<DT, OP, 0, false, 1>(a, s);
 }
 
 template <int DT, class Args>
@@ -216,8 +213,8 @@ hipError_t launch_fold(int dtype, int op, int p, bool all_out, const FoldArgs& a
   return by_dtype(dtype, op, p, all_out, a, unroll, s);
 }
 
-hipError_t launch_fold_tab(int dtype, int op, int p, const FoldTabArgs& a, int unroll, hipStream_t s) {
-  return by_dtype(dtype, op, p, true, a, unroll, s);
+hipError_t launch_fold_tab(int dtype, int op, int p, bool all_out, const FoldTabArgs& a, int unroll, hipStream_t s) {
+  return by_dtype(dtype, op, p, all_out, a, unroll, s);
 }
 
 }  // namespace simar

@@ -92,19 +92,17 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
   }
 }
 
-// ONE: every transfer of the launch has a single destination (the ring's
-// all-gather steps).  Measured on MI355X: loading all 16 destination
-// pointers up front costs such short-lived workgroups ~20% on a ring
-// all-gather step, while it saves the fan-out ~4%.
-template <int E, int U, bool ONE>
-__global__ void __launch_bounds__(kBlock) k_copy(CopyArgs args) {
+// One transfer's share for workgroup `tile` of `tiles`: elements [lo, hi)
+// of src (read at [i - src_shift]) to the nd destinations in dp (written at
+// [i - dst_shift]).  The destination pointers sit in scalar registers,
+// loaded once by the caller (a loop over a run-time count would re-load each
+// one and wait for it before every store).
+template <int E, int U, int ND>
+__device__ __forceinline__ void copy_tiles(const void* const src, void* const (&dp)[ND], const int nd, const int64_t lo,
+                                           const int64_t hi, const bool vec_ok, const int64_t src_shift,
+                                           const int64_t dst_shift, const int64_t tile, const int tiles) {
   constexpr int V = 16 / E;
-  const unsigned xi = blockIdx.x % (unsigned)args.nx;  // transfers interleaved, as above
-  const int64_t tile = blockIdx.x / (unsigned)args.nx;
-  const CopyXfer& x = args.x[xi];
-  const int64_t lo = x.lo, hi = x.hi;
-  const int nd = x.ndst;
-  int64_t head = x.vec_ok ? (int64_t)((V - (lo % V)) % V) : (hi - lo);
+  int64_t head = vec_ok ? (int64_t)((V - (lo % V)) % V) : (hi - lo);
   if (head > hi - lo) head = hi - lo;
   const int64_t vbeg = lo + head;
   const int64_t nvec = (hi - vbeg) / V;
@@ -112,17 +110,8 @@ __global__ void __launch_bounds__(kBlock) k_copy(CopyArgs args) {
   const int64_t nscalar = head + (hi - tail_beg);
   const int tid = threadIdx.x;
   const int64_t span = (int64_t)kBlock * U;
-  const int64_t stride = (int64_t)args.tiles * span;
-
-  // destination pointers in scalar registers, loaded once (a loop over a
-  // run-time count would re-load each one from the argument segment and
-  // wait for it before every store)
-  constexpr int ND = ONE ? 1 : SIM_MAX_RANKS;
-  void* dp[ND];
-#pragma unroll
-  for (int d = 0; d < ND; d++) dp[d] = (d < nd) ? x.dst[d] : nullptr;
-  const void* const src = x.src;
-  const int64_t src_off = x.src_shift * E, dst_off = x.dst_shift * E;
+  const int64_t stride = (int64_t)tiles * span;
+  const int64_t src_off = src_shift * E, dst_off = dst_shift * E;
   // one span of U vectors per lane; GUARD: the span may run past nvec
   auto span_body = [&](int64_t base, auto guard) {
     constexpr bool GUARD = decltype(guard)::value;
@@ -147,20 +136,53 @@ __global__ void __launch_bounds__(kBlock) k_copy(CopyArgs args) {
   int64_t base = tile * span;
   for (; base + span <= nvec; base += stride) span_body(base, std::false_type());
   if (base < nvec) span_body(base, std::true_type());
-  for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)args.tiles * kBlock) {
+  for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)tiles * kBlock) {
     const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
     if constexpr (E == 4) {
-      const uint32_t w = ((const uint32_t*)x.src)[i - x.src_shift];
+      const uint32_t w = ((const uint32_t*)src)[i - src_shift];
 #pragma unroll
       for (int d = 0; d < ND; d++)
-        if (d < nd) ((uint32_t*)dp[d])[i - x.dst_shift] = w;
+        if (d < nd) ((uint32_t*)dp[d])[i - dst_shift] = w;
     } else {
-      const uint16_t w = ((const uint16_t*)x.src)[i - x.src_shift];
+      const uint16_t w = ((const uint16_t*)src)[i - src_shift];
 #pragma unroll
       for (int d = 0; d < ND; d++)
-        if (d < nd) ((uint16_t*)dp[d])[i - x.dst_shift] = w;
+        if (d < nd) ((uint16_t*)dp[d])[i - dst_shift] = w;
     }
   }
+}
+
+// ONE: every transfer of the launch has a single destination (the ring's
+// all-gather steps).  Measured on MI355X: loading all 16 destination
+// pointers up front costs such short-lived workgroups ~20% on a ring
+// all-gather step, while it saves the fan-out ~4%.
+template <int E, int U, bool ONE>
+__global__ void __launch_bounds__(kBlock) k_copy(CopyArgs args) {
+  const unsigned xi = blockIdx.x % (unsigned)args.nx;  // transfers interleaved, as above
+  const int64_t tile = blockIdx.x / (unsigned)args.nx;
+  const CopyXfer& x = args.x[xi];
+  const int nd = x.ndst;
+  constexpr int ND = ONE ? 1 : SIM_MAX_RANKS;
+  void* dp[ND];
+#pragma unroll
+  for (int d = 0; d < ND; d++) dp[d] = (d < nd) ? x.dst[d] : nullptr;
+  copy_tiles<E, U, ND>(x.src, dp, nd, x.lo, x.hi, x.vec_ok != 0, x.src_shift, x.dst_shift, tile, args.tiles);
+}
+
+// The all-pairs fan-out with its pointers in the library's pointer table:
+// workgroup b copies tile b / p of chunk j = b mod p from the owner's
+// output to every other rank's output (chunk j = [floor(j n / p),
+// floor((j+1) n / p)), every pointer 16-byte aligned).
+template <int E, int U>
+__global__ void __launch_bounds__(kBlock) k_fanout_tab(FanoutTabArgs a) {
+  const int p = a.p;
+  const int j = (int)(blockIdx.x % (unsigned)p);
+  const int64_t tile = blockIdx.x / (unsigned)p;
+  void* dp[SIM_MAX_RANKS];
+#pragma unroll
+  for (int d = 0; d < SIM_MAX_RANKS; d++) dp[d] = (d < p - 1) ? a.set->y[d < j ? d : d + 1] : nullptr;
+  const int64_t lo = (int64_t)j * a.n / p, hi = (int64_t)(j + 1) * a.n / p;
+  copy_tiles<E, U, SIM_MAX_RANKS>(a.set->y[j], dp, p - 1, lo, hi, true, 0, 0, tile, a.tiles);
 }
 
 __global__ void __launch_bounds__(kBlock) k_fill64(unsigned long long* p, unsigned long long v, int64_t n) {
@@ -228,6 +250,20 @@ hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s) 
   bool one = true;  // every transfer has a single destination (ring all-gather steps)
   for (int k = 0; k < a.nx; k++) one = one && a.x[k].ndst <= 1;
   return one ? copy_go<true>(esize, a, unroll, s) : copy_go<false>(esize, a, unroll, s);
+}
+
+hipError_t launch_fanout_tab(int esize, const FanoutTabArgs& a, int unroll, hipStream_t s) {
+  const dim3 grid((unsigned)a.tiles * (unsigned)a.p), block(kBlock);
+  if (esize == 4) {
+    if (unroll == 2) hipLaunchKernelGGL((k_fanout_tab<4, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_fanout_tab<4, 1>), grid, block, 0, s, a);
+  } else if (esize == 2) {
+    if (unroll == 2) hipLaunchKernelGGL((k_fanout_tab<2, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_fanout_tab<2, 1>), grid, block, 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_fill64(unsigned long long* p, unsigned long long v, int64_t n, hipStream_t s) {

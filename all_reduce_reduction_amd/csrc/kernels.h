@@ -32,7 +32,7 @@ struct FoldArgs {
   float inv_p;                       // fp32(1/p) for fp avg
 };
 
-// The fused one-shot with its rank pointers in device memory: one entry of
+// The fused one-shot (and all-pairs step 1) with its rank pointers in device memory: one entry of
 // the library's pointer table, written (in stream order) before the first
 // launch that uses it.  The argument block then fits the HIP runtime's
 // small-argument launch path (<= 64 bytes), which measured ~1 us cheaper
@@ -48,6 +48,14 @@ struct FoldTabArgs {
   int p;
   int tiles;          // workgroups per chunk
   float inv_p;        // fp32(1/p) for fp avg
+};
+// The all-pairs fan-out (step 2) from the same table entry: chunk j of the
+// owner's output y[j] to every other rank's output.
+struct FanoutTabArgs {
+  const PtrSet* set;
+  int64_t n;
+  int p;
+  int tiles;
 };
 
 // One ring reduce-scatter step: p transfers, each over one chunk.
@@ -180,6 +188,7 @@ struct SchedArgs {
 
 static_assert(sizeof(FoldArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(FoldTabArgs) <= 64, "must fit the small-argument launch path");
+static_assert(sizeof(FanoutTabArgs) <= 64, "must fit the small-argument launch path");
 static_assert(sizeof(SchedArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingFifoArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(AllPairsPArgs) <= 4096, "kernel argument segment too large");
@@ -190,7 +199,9 @@ static_assert(sizeof(LLArgs) <= 4096, "kernel argument segment too large");
 // Launchers: select the (dtype, op, ...) instantiation and enqueue.
 hipError_t launch_fold(int dtype, int op, int p, bool all_out, const FoldArgs& a, int unroll,
                        hipStream_t s);
-hipError_t launch_fold_tab(int dtype, int op, int p, const FoldTabArgs& a, int unroll, hipStream_t s);
+// all_out: the one-shot (every output); otherwise all-pairs step 1 (the owner's output only)
+hipError_t launch_fold_tab(int dtype, int op, int p, bool all_out, const FoldTabArgs& a, int unroll, hipStream_t s);
+hipError_t launch_fanout_tab(int esize, const FanoutTabArgs& a, int unroll, hipStream_t s);
 hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, const RingArgs& a,
                               int unroll, hipStream_t s);
 hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s);

@@ -1,5 +1,5 @@
-"""The one-shot's small-argument launch: rank pointer sets kept in a
-device-memory table.  A call whose set is in the table and a call that
+"""The small-argument launches of the one-shot and both all-pairs steps:
+rank pointer sets kept in a device-memory table.  A call whose set is in the table and a call that
 carries its pointers in the kernel arguments must give the same bits, and
 both must match the oracle; new inputs behind the same pointers must be
 read afresh; sets beyond the table's capacity, calls on another stream and
@@ -32,15 +32,16 @@ def _sets(sim):
     return sim.sim_debug_get("ptr_sets")
 
 
+@pytest.mark.parametrize("algo", ["oneshot", "allpairs"])
 @pytest.mark.parametrize("p,n", [(8, 8 * 4096 * 3 + 77), (8, 4096), (2, 5), (3, 1000), (16, 16 * 1024 + 9)])
 @pytest.mark.parametrize("dtype,op", [("bf16", "sum"), ("fp16", "avg"), ("fp32", "prod"), ("int32", "max"),
                                       ("int32", "avg")])
-def test_table_and_argument_paths_agree_with_the_oracle(orc, lib, p, n, dtype, op):
+def test_table_and_argument_paths_agree_with_the_oracle(orc, lib, algo, p, n, dtype, op):
     from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
     sim = lib
     sim.sim_init(0, 16, 0)  # empty table: the allocator may hand out addresses an earlier case used
     xs = _inputs(dtype, p, n, 90 + p)
-    want, _ = orc.allreduce(xs, dtype, op, "oneshot")
+    want, _ = orc.allreduce(xs, dtype, op, algo)
     din = to_device(xs, dtype)
     results = {}
     dout = None
@@ -53,7 +54,7 @@ def test_table_and_argument_paths_agree_with_the_oracle(orc, lib, p, n, dtype, o
         else:
             dout = empty_like_poisoned(n, dtype, p)
         before = _sets(sim)
-        assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, "oneshot", stream()) == 0
+        assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, algo, stream()) == 0
         got = to_host(dout, dtype)
         if mode == "args":
             assert _sets(sim) == before
@@ -62,28 +63,29 @@ def test_table_and_argument_paths_agree_with_the_oracle(orc, lib, p, n, dtype, o
         else:
             assert _sets(sim) == before         # and found there the next time
         for r in range(p):
-            assert_parity(got[r], want[r], dtype, f"{mode} {dtype} {op} p={p} n={n} r{r}")
+            assert_parity(got[r], want[r], dtype, f"{algo} {mode} {dtype} {op} p={p} n={n} r{r}")
         results[mode] = got
     for r in range(p):
         assert (results["args"][r] == results["table_again"][r]).all()
 
 
+@pytest.mark.parametrize("algo", ["oneshot", "allpairs"])
 @pytest.mark.parametrize("unroll", [1, 2])
-def test_table_path_vectors_per_lane(orc, lib, unroll):
+def test_table_path_vectors_per_lane(orc, lib, algo, unroll):
     from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
     sim = lib
     p, n, dtype = 8, 8 * 8192 * 5 + 13, "bf16"
     xs = _inputs(dtype, p, n, 30 + unroll)
-    want, _ = orc.allreduce(xs, dtype, "sum", "oneshot")
+    want, _ = orc.allreduce(xs, dtype, "sum", algo)
     din = to_device(xs, dtype)
     dout = empty_like_poisoned(n, dtype, p)
     sim.sim_debug_set("unroll", unroll)
     try:
         for rep in range(2):  # the second call finds its set in the table
-            assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, "sum", "oneshot", stream()) == 0
+            assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, "sum", algo, stream()) == 0
             got = to_host(dout, dtype)
             for r in range(p):
-                assert_parity(got[r], want[r], dtype, f"unroll {unroll} rep {rep} r{r}")
+                assert_parity(got[r], want[r], dtype, f"{algo} unroll {unroll} rep {rep} r{r}")
             for t, f in zip(dout, empty_like_poisoned(n, dtype, p)):
                 t.copy_(f)
     finally:
@@ -196,3 +198,24 @@ def test_prepared_call_matches_the_oracle(orc, lib):
         want, _ = orc.allreduce(xs, dtype, "sum", sim.sim_last_algo())
         for r in range(p):
             assert_parity(got[r], want[r], dtype, f"prepared rep {rep} r{r}")
+
+
+@pytest.mark.parametrize("algo", ["oneshot", "allpairs"])
+def test_table_path_in_place(orc, lib, algo):
+    """In place (out_ptrs == in_ptrs): the first call inserts the set, the
+    second finds it; fresh inputs are copied in before each call."""
+    from tests.gpu_util import assert_parity, stream, to_device, to_host, ptrs
+    sim = lib
+    sim.sim_init(0, 16, 0)
+    p, n, dtype = 8, 8 * 4096 * 2 + 21, "fp32"
+    buf = to_device(_inputs(dtype, p, n, 300), dtype)
+    for rep in range(2):
+        xs = _inputs(dtype, p, n, 301 + rep)
+        for t, x in zip(buf, to_device(xs, dtype)):
+            t.copy_(x)
+        assert sim.sim_allreduce(ptrs(buf), ptrs(buf), p, n, dtype, "sum", algo, stream()) == 0
+        got = to_host(buf, dtype)
+        want, _ = orc.allreduce(xs, dtype, "sum", algo)
+        for r in range(p):
+            assert_parity(got[r], want[r], dtype, f"{algo} in place rep {rep} r{r}")
+    assert _sets(sim) == 1
