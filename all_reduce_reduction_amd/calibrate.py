@@ -172,6 +172,14 @@ def calibrate(out_path: str):
     sizes = [int(1.5 * (1 << k)) // 16 * 16 for k in range(10, 28)]   # 1.5 KiB .. 192 MiB
     b = Bench(max(sizes))
     raw = {}
+    # warm-up: the first schedule measured otherwise ran its smallest sizes
+    # while host and GPU clocks were still ramping (a run measured the ring
+    # at 59.7 us for 1.5 and 3 KiB per rank and 39.1 us from 6 KiB on)
+    for algo in ALGOS:
+        set_topology(sim, algo)
+        for nbytes in sizes[:6]:
+            if b.legal(algo, nbytes):
+                b.measure(algo, "bf16", nbytes // 2)
     for algo in ALGOS + tuple(TOPOLOGY):
         set_topology(sim, algo)
         pts = []
