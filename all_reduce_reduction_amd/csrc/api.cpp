@@ -424,6 +424,43 @@ int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_c
   return SIM_OK;
 }
 
+// The all-reduce ring from the pointer table: each of the 2(p-1) steps
+// launches with a 48-byte argument block and derives its transfers from the
+// step number, exactly as the ring's lowering lists them (the schedule
+// verifier proves that list); partials as in run_ring_rs.
+int run_ring_tab(const Call& c, const PtrSet* set, const std::vector<int64_t>& lo) {
+  const int p = c.p, e = esize_of(c.dtype), V = 16 / e;
+  const bool part_in_y = (e == 4);
+  const size_t se = slot_elems(c.n, p);
+  if (!part_in_y && p > 2) {
+    int rc = ensure_scratch(scratch_need(c.n, p));
+    if (rc) return rc;
+  }
+  int64_t maxchunk = 0;
+  for (int q = 0; q < p; q++) maxchunk = std::max(maxchunk, lo[q + 1] - lo[q]);
+  const int unroll = unroll_for(c);
+  RingTabArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.set = set;
+  a.scratch = (part_in_y || p == 2) ? nullptr : g.scratch;
+  a.n = (int64_t)c.n;
+  a.slot_elems = (int64_t)se;
+  a.p = p;
+  a.tiles = tiles_for(c, (maxchunk + V - 1) / V, p, unroll);
+  a.inv_p = inv_p_of(p);
+  for (int st = 0; st < p - 1; st++) {  // reduce-scatter
+    a.step = st;
+    int rc = hip_err(launch_ring_reduce_tab(c.dtype, c.op, st > 0, st == p - 2, a, unroll, c.s));
+    if (rc) return rc;
+  }
+  for (int st = 0; st < p - 1; st++) {  // all-gather
+    a.step = st;
+    int rc = hip_err(launch_ring_copy_tab(e, a, unroll, c.s));
+    if (rc) return rc;
+  }
+  return SIM_OK;
+}
+
 // The epoch of a call of a persistent kernel (the single-launch ring and
 // all-pairs share the semaphore array and this one monotonic count, so a
 // counter value left by any earlier call compares lower than anything the
@@ -717,6 +754,7 @@ int run_allreduce(const Call& c) {
       return run_copy_step(c, xs);
     }
     case SIM_ALGO_RING: {
+      if (const PtrSet* set = ptr_set_for(c)) return run_ring_tab(c, set, lo);
       int rc = run_ring_rs(c, *sch, p - 1, false, lo);
       if (rc) return rc;
       for (int st = p - 1; st < 2 * (p - 1); st++) {

@@ -22,19 +22,14 @@
 
 namespace simar {
 
+// One reduce-scatter transfer's share for workgroup `tile` of `tiles`.
 template <int DT, int OP, bool A_PART, bool D_FINAL, int U>
-__global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
+__device__ __forceinline__ void ring_reduce_xfer(const RingXfer& x, const int64_t tile, const int tiles, const int p,
+                                                 const float inv_p) {
   typedef typename Ty<DT>::A A;
   typedef Op<DT, OP> O;
   constexpr int V = epv<DT>();
   constexpr int E = Ty<DT>::E;
-  // 1-D grid, transfers interleaved: workgroup b runs tile b / nx of
-  // transfer b mod nx, so the transfers in flight together cover every chunk
-  const unsigned xi = blockIdx.x % (unsigned)args.nx;
-  const int64_t tile = blockIdx.x / (unsigned)args.nx;
-  const RingXfer x = args.x[xi];
-  const float inv_p = args.inv_p;
-  const int p = args.p;
   const int64_t lo = x.lo, hi = x.hi;
   int64_t head = x.vec_ok ? (int64_t)((V - (lo % V)) % V) : (hi - lo);
   if (head > hi - lo) head = hi - lo;
@@ -44,7 +39,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
   const int64_t nscalar = head + (hi - tail_beg);
   const int tid = threadIdx.x;
   const int64_t span = (int64_t)kBlock * U;
-  const int64_t stride = (int64_t)args.tiles * span;
+  const int64_t stride = (int64_t)tiles * span;
 
   // one span of U vectors per lane; GUARD: the span may run past nvec
   auto span_body = [&](int64_t base, auto guard) {
@@ -81,7 +76,7 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
   for (; base + span <= nvec; base += stride) span_body(base, std::false_type());
   if (base < nvec) span_body(base, std::true_type());
 
-  for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)args.tiles * kBlock) {
+  for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)tiles * kBlock) {
     const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
     A in;
     if constexpr (A_PART) in = ((const A*)x.a)[i - x.a_shift];
@@ -90,6 +85,60 @@ __global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
     if constexpr (D_FINAL) store_elem<DT>(x.d, i - x.d_shift, O::post(v, p));
     else ((A*)x.d)[i - x.d_shift] = v;
   }
+}
+
+template <int DT, int OP, bool A_PART, bool D_FINAL, int U>
+__global__ void __launch_bounds__(kBlock) k_ring_reduce(RingArgs args) {
+  // 1-D grid, transfers interleaved: workgroup b runs tile b / nx of
+  // transfer b mod nx, so the transfers in flight together cover every chunk
+  const unsigned xi = blockIdx.x % (unsigned)args.nx;
+  const int64_t tile = blockIdx.x / (unsigned)args.nx;
+  const RingXfer x = args.x[xi];
+  ring_reduce_xfer<DT, OP, A_PART, D_FINAL, U>(x, tile, args.tiles, args.p, args.inv_p);
+}
+
+// The same step of an all-reduce ring from the library's pointer table: the
+// transfers follow from the step, as the ring's lowering defines them --
+// at reduce-scatter step s rank r sends chunk (r - 1 - s) mod p to rank
+// r + 1, which folds its own input in; fp16/bf16 partials alternate between
+// two scratch slot sets by step parity (32-bit partials stay in the
+// receiving rank's output).
+template <int DT, int OP, bool A_PART, bool D_FINAL, int U>
+__global__ void __launch_bounds__(kBlock) k_ring_reduce_tab(RingTabArgs a) {
+  const int p = a.p;
+  const int r = (int)(blockIdx.x % (unsigned)p);
+  const int64_t tile = blockIdx.x / (unsigned)p;
+  const int s = a.step;
+  const int c = ((r - 1 - s) % p + p) % p;
+  const int d = (r + 1 == p) ? 0 : r + 1;
+  RingXfer x;
+  x.lo = (int64_t)c * a.n / p;
+  x.hi = (int64_t)(c + 1) * a.n / p;
+  const int64_t slot_shift = x.lo - (x.lo % 8);
+  auto slot = [&](int parity, int rank) -> void* {
+    return (char*)a.scratch + ((int64_t)parity * p + rank) * a.slot_elems * 4;
+  };
+  if (!A_PART) {
+    x.a = a.set->x[r];
+    x.a_shift = 0;
+  } else if (a.scratch) {
+    x.a = slot((s - 1) & 1, r);
+    x.a_shift = slot_shift;
+  } else {
+    x.a = a.set->y[r];
+    x.a_shift = 0;
+  }
+  x.b = a.set->x[d];
+  if (D_FINAL || !a.scratch) {
+    x.d = a.set->y[d];
+    x.d_shift = 0;
+  } else {
+    x.d = slot(s & 1, d);
+    x.d_shift = slot_shift;
+  }
+  x.vec_ok = 1;  // every shift is a multiple of 8 elements and every pointer 16-byte aligned
+  x.pad_ = 0;
+  ring_reduce_xfer<DT, OP, A_PART, D_FINAL, U>(x, tile, a.tiles, p, a.inv_p);
 }
 
 // One transfer's share for workgroup `tile` of `tiles`: elements [lo, hi)
@@ -185,6 +234,19 @@ __global__ void __launch_bounds__(kBlock) k_fanout_tab(FanoutTabArgs a) {
   copy_tiles<E, U, SIM_MAX_RANKS>(a.set->y[j], dp, p - 1, lo, hi, true, 0, 0, tile, a.tiles);
 }
 
+// A ring all-gather step from the pointer table: at step s rank r forwards
+// its finished chunk (r - s) mod p to rank r + 1.
+template <int E, int U>
+__global__ void __launch_bounds__(kBlock) k_ring_copy_tab(RingTabArgs a) {
+  const int p = a.p;
+  const int r = (int)(blockIdx.x % (unsigned)p);
+  const int64_t tile = blockIdx.x / (unsigned)p;
+  const int c = ((r - a.step) % p + p) % p;
+  void* dp[1] = {a.set->y[(r + 1 == p) ? 0 : r + 1]};
+  const int64_t lo = (int64_t)c * a.n / p, hi = (int64_t)(c + 1) * a.n / p;
+  copy_tiles<E, U, 1>(a.set->y[r], dp, 1, lo, hi, true, 0, 0, tile, a.tiles);
+}
+
 __global__ void __launch_bounds__(kBlock) k_fill64(unsigned long long* p, unsigned long long v, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += (int64_t)gridDim.x * kBlock) p[i] = v;
 }
@@ -203,13 +265,26 @@ static hipError_t ring_go(bool a_part, bool d_final, const RingArgs& a, hipStrea
   return hipGetLastError();
 }
 
-template <int DT, int OP>
-static hipError_t ring_by_unroll(int unroll, bool ap, bool df, const RingArgs& a, hipStream_t s) {
+template <int DT, int OP, int U>
+static hipError_t ring_go(bool a_part, bool d_final, const RingTabArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.tiles * (unsigned)a.p), block(kBlock);
+  if (a_part) {
+    if (d_final) hipLaunchKernelGGL((k_ring_reduce_tab<DT, OP, true, true, U>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_ring_reduce_tab<DT, OP, true, false, U>), grid, block, 0, s, a);
+  } else {
+    if (d_final) hipLaunchKernelGGL((k_ring_reduce_tab<DT, OP, false, true, U>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_ring_reduce_tab<DT, OP, false, false, U>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DT, int OP, class Args>
+static hipError_t ring_by_unroll(int unroll, bool ap, bool df, const Args& a, hipStream_t s) {
   return unroll == 2 ? ring_go<DT, OP, 2>(ap, df, a, s) : ring_go<DT, OP, 1>(ap, df, a, s);
 }
 
-template <int DT>
-static hipError_t ring_by_op(int op, int unroll, bool ap, bool df, const RingArgs& a, hipStream_t s) {
+template <int DT, class Args>
+static hipError_t ring_by_op(int op, int unroll, bool ap, bool df, const Args& a, hipStream_t s) {
   switch (op) {
     case SIM_SUM: return ring_by_unroll<DT, SIM_SUM>(unroll, ap, df, a, s);
     case SIM_PROD: return ring_by_unroll<DT, SIM_PROD>(unroll, ap, df, a, s);
@@ -240,6 +315,31 @@ static hipError_t copy_go(int esize, const CopyArgs& a, int unroll, hipStream_t 
   } else if (esize == 2) {
     if (unroll == 2) hipLaunchKernelGGL((k_copy<2, 2, ONE>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((k_copy<2, 1, ONE>), grid, block, 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_reduce_tab(int dtype, int op, bool a_partial, bool d_final, const RingTabArgs& a,
+                                  int unroll, hipStream_t s) {
+  switch (dtype) {
+    case SIM_INT32: return ring_by_op<SIM_INT32>(op, unroll, a_partial, d_final, a, s);
+    case SIM_FP32: return ring_by_op<SIM_FP32>(op, unroll, a_partial, d_final, a, s);
+    case SIM_FP16: return ring_by_op<SIM_FP16>(op, unroll, a_partial, d_final, a, s);
+    case SIM_BF16: return ring_by_op<SIM_BF16>(op, unroll, a_partial, d_final, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_ring_copy_tab(int esize, const RingTabArgs& a, int unroll, hipStream_t s) {
+  const dim3 grid((unsigned)a.tiles * (unsigned)a.p), block(kBlock);
+  if (esize == 4) {
+    if (unroll == 2) hipLaunchKernelGGL((k_ring_copy_tab<4, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_ring_copy_tab<4, 1>), grid, block, 0, s, a);
+  } else if (esize == 2) {
+    if (unroll == 2) hipLaunchKernelGGL((k_ring_copy_tab<2, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_ring_copy_tab<2, 1>), grid, block, 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

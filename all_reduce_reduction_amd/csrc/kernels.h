@@ -57,6 +57,20 @@ struct FanoutTabArgs {
   int p;
   int tiles;
 };
+// One step of the all-reduce ring from the same table entry: the step's
+// transfers follow from the step number (reduce-scatter step s: rank r
+// sends chunk (r - 1 - s) mod p to r + 1; all-gather step s: rank r
+// forwards chunk (r - s) mod p).
+struct RingTabArgs {
+  const PtrSet* set;
+  void* scratch;       // fp16/bf16 partial slots [2][p][slot_elems] fp32; nullptr: partials in the outputs
+  int64_t n;
+  int64_t slot_elems;
+  int p;
+  int step;
+  int tiles;
+  float inv_p;
+};
 
 // One ring reduce-scatter step: p transfers, each over one chunk.
 struct RingXfer {
@@ -189,6 +203,7 @@ struct SchedArgs {
 static_assert(sizeof(FoldArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(FoldTabArgs) <= 64, "must fit the small-argument launch path");
 static_assert(sizeof(FanoutTabArgs) <= 64, "must fit the small-argument launch path");
+static_assert(sizeof(RingTabArgs) <= 64, "must fit the small-argument launch path");
 static_assert(sizeof(SchedArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingFifoArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(AllPairsPArgs) <= 4096, "kernel argument segment too large");
@@ -202,6 +217,9 @@ hipError_t launch_fold(int dtype, int op, int p, bool all_out, const FoldArgs& a
 // all_out: the one-shot (every output); otherwise all-pairs step 1 (the owner's output only)
 hipError_t launch_fold_tab(int dtype, int op, int p, bool all_out, const FoldTabArgs& a, int unroll, hipStream_t s);
 hipError_t launch_fanout_tab(int esize, const FanoutTabArgs& a, int unroll, hipStream_t s);
+hipError_t launch_ring_reduce_tab(int dtype, int op, bool a_partial, bool d_final, const RingTabArgs& a,
+                                  int unroll, hipStream_t s);
+hipError_t launch_ring_copy_tab(int esize, const RingTabArgs& a, int unroll, hipStream_t s);
 hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, const RingArgs& a,
                               int unroll, hipStream_t s);
 hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s);

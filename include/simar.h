@@ -62,12 +62,12 @@
  *     32-bit ring all-reduce, the ring all-gather and the all-pairs
  *     reduce-scatter / all-gather use none and may overlap freely.
  *   - Pointer table: the first 512 distinct (p, in_ptrs, out_ptrs) sets of
- *     SIM_ALGO_ONESHOT and SIM_ALGO_ALLPAIRS all-reduce calls made outside
- *     graph capture are copied once
- *     (asynchronously, on the call's stream) into a device-memory table
+ *     SIM_ALGO_ONESHOT, SIM_ALGO_ALLPAIRS and SIM_ALGO_RING all-reduce calls
+ *     made outside graph capture are copied once (asynchronously, on the
+ *     call's stream) into a device-memory table
  *     that the library owns until sim_finalize; later calls with the same
- *     set launch with 32-byte argument blocks instead of the full pointer
- *     lists, which are cheaper to enqueue.  Entries hold addresses only (no
+ *     set launch with argument blocks of at most 64 bytes instead of the
+ *     full pointer lists, which are cheaper to enqueue.  Entries hold addresses only (no
  *     ownership) and are never rewritten or evicted; other sets, captured
  *     calls, and calls made while a set's copy has not completed yet carry
  *     their pointers in the kernel arguments.  Results are the same either
@@ -323,7 +323,7 @@ enum {
   SIM_DEBUG_FIFO_SLOTS = 8,    /* single-launch ring: slots per FIFO, 2..8 (default 4) */
   SIM_DEBUG_FIFO_WITHHOLD = 9, /* 1: rank 0's ring workgroups leave at once (forces a bounded-wait expiry) */
   SIM_DEBUG_FIFO_VECS = 10,    /* single-launch ring: 16-byte vectors per lane per slot, 1, 2 or 4 (default 4) */
-  SIM_DEBUG_PTR_TABLE = 11,    /* 0: one-shot / all-pairs calls never use the pointer table (default 1) */
+  SIM_DEBUG_PTR_TABLE = 11,    /* 0: all-reduce calls never use the pointer table (default 1) */
   SIM_DEBUG_PTR_SETS = 12      /* get only: pointer sets the table holds */
 };
 int sim_debug_set(int key, uint64_t value);

@@ -1,4 +1,5 @@
-"""The small-argument launches of the one-shot and both all-pairs steps:
+"""The small-argument launches of the one-shot, both all-pairs steps and
+the ring's steps:
 rank pointer sets kept in a device-memory table.  A call whose set is in the table and a call that
 carries its pointers in the kernel arguments must give the same bits, and
 both must match the oracle; new inputs behind the same pointers must be
@@ -32,7 +33,7 @@ def _sets(sim):
     return sim.sim_debug_get("ptr_sets")
 
 
-@pytest.mark.parametrize("algo", ["oneshot", "allpairs"])
+@pytest.mark.parametrize("algo", ["oneshot", "allpairs", "ring"])
 @pytest.mark.parametrize("p,n", [(8, 8 * 4096 * 3 + 77), (8, 4096), (2, 5), (3, 1000), (16, 16 * 1024 + 9)])
 @pytest.mark.parametrize("dtype,op", [("bf16", "sum"), ("fp16", "avg"), ("fp32", "prod"), ("int32", "max"),
                                       ("int32", "avg")])
@@ -69,7 +70,7 @@ def test_table_and_argument_paths_agree_with_the_oracle(orc, lib, algo, p, n, dt
         assert (results["args"][r] == results["table_again"][r]).all()
 
 
-@pytest.mark.parametrize("algo", ["oneshot", "allpairs"])
+@pytest.mark.parametrize("algo", ["oneshot", "allpairs", "ring"])
 @pytest.mark.parametrize("unroll", [1, 2])
 def test_table_path_vectors_per_lane(orc, lib, algo, unroll):
     from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
@@ -200,14 +201,15 @@ def test_prepared_call_matches_the_oracle(orc, lib):
             assert_parity(got[r], want[r], dtype, f"prepared rep {rep} r{r}")
 
 
-@pytest.mark.parametrize("algo", ["oneshot", "allpairs"])
-def test_table_path_in_place(orc, lib, algo):
+@pytest.mark.parametrize("algo", ["oneshot", "allpairs", "ring"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_table_path_in_place(orc, lib, algo, dtype):
     """In place (out_ptrs == in_ptrs): the first call inserts the set, the
     second finds it; fresh inputs are copied in before each call."""
     from tests.gpu_util import assert_parity, stream, to_device, to_host, ptrs
     sim = lib
     sim.sim_init(0, 16, 0)
-    p, n, dtype = 8, 8 * 4096 * 2 + 21, "fp32"
+    p, n = 8, 8 * 4096 * 2 + 21
     buf = to_device(_inputs(dtype, p, n, 300), dtype)
     for rep in range(2):
         xs = _inputs(dtype, p, n, 301 + rep)
