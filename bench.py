@@ -199,9 +199,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.profile_copy:
         # Counter scale references of known size: (1) the library's own copy
-        # kernel (k_copy, same 16-byte streaming loads/stores as k_fold) as the
-        # all-gather step of a p = 2 fp32 ring all-reduce of 256 MiB per rank:
-        # each k_copy launch reads 256 MiB and writes 256 MiB; (2) torch's
+        # kernel (the ring all-gather step, same 16-byte streaming loads/stores
+        # as k_fold) in a p = 2 fp32 ring all-reduce of 256 MiB per rank: each
+        # such launch reads 256 MiB and writes 256 MiB; (2) torch's
         # device-to-device copy of 512 MiB.
         sim.sim_init(0, 2, 0)
         n2 = (256 << 20) // 4
