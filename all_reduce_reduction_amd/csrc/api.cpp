@@ -23,6 +23,9 @@
 #include "simar.h"
 
 namespace simar {
+
+int g_launch_device = 0;
+
 namespace {
 
 constexpr int kVersion = 1;
@@ -151,17 +154,17 @@ int check_scalars(int p, int dtype, int op, bool need_op) {
 
 // in-place iff out == in + inplace_off(r) for every rank (mixing is an error)
 int check_buffers(const void* const* in, void* const* out, int p, size_t in_bytes, size_t out_bytes,
-                  const std::vector<size_t>& inplace_off, bool* inplace) {
+                  const size_t* inplace_off, bool* inplace) {
   if (!in || !out) return SIM_ERR_INVALID_ARG;
   int n_inplace = 0;
   for (int r = 0; r < p; r++) {
     if (!in[r] || !out[r]) return SIM_ERR_INVALID_ARG;
     if (((uintptr_t)in[r] | (uintptr_t)out[r]) & 15u) return SIM_ERR_ALIGN;
-    if ((const char*)in[r] == (const char*)out[r] + inplace_off[r]) n_inplace++;
+    if ((const char*)in[r] == (const char*)out[r] + (inplace_off ? inplace_off[r] : 0)) n_inplace++;
   }
   if (n_inplace != 0 && n_inplace != p) return SIM_ERR_INVALID_ARG;
   *inplace = (n_inplace == p);
-  std::vector<Range> ins(p), outs(p);
+  Range ins[SIM_MAX_RANKS], outs[SIM_MAX_RANKS];  // p <= SIM_MAX_RANKS (check_scalars)
   for (int r = 0; r < p; r++) {
     ins[r] = {(uintptr_t)in[r], (uintptr_t)in[r] + in_bytes};
     outs[r] = {(uintptr_t)out[r], (uintptr_t)out[r] + out_bytes};
@@ -314,7 +317,7 @@ const PtrSet* ptr_set_for(const Call& c) {
 // launch carries a 32-byte argument block; that form computes the standard
 // chunk bounds itself and writes outputs unshifted, so it serves the
 // one-shot and all-pairs step 1 of an all-reduce (not the reduce-scatter).
-int run_fold(const Call& c, bool all_out, const std::vector<int64_t>& lo, const int64_t* out_shift,
+int run_fold(const Call& c, bool all_out, const int64_t* lo, const int64_t* out_shift,
              const PtrSet* set) {
   FoldArgs a;
   std::memset(&a, 0, sizeof a);
@@ -364,7 +367,7 @@ int run_copy_step(const Call& c, const std::vector<CopyXfer>& xs) {
 
 // Ring reduce-scatter half.  final_out_chunk: outputs are chunk-sized (RS).
 int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_chunk,
-                const std::vector<int64_t>& lo) {
+                const int64_t* lo) {
   const int p = c.p, e = esize_of(c.dtype), V = 16 / e;
   // 32-bit all-reduce keeps partials in the receiving rank's output (a chunk
   // it does not own yet); otherwise partials live in fp32/int32 scratch slots.
@@ -428,7 +431,7 @@ int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_c
 // launches with a 48-byte argument block and derives its transfers from the
 // step number, exactly as the ring's lowering lists them (the schedule
 // verifier proves that list); partials as in run_ring_rs.
-int run_ring_tab(const Call& c, const PtrSet* set, const std::vector<int64_t>& lo) {
+int run_ring_tab(const Call& c, const PtrSet* set, const int64_t* lo) {
   const int p = c.p, e = esize_of(c.dtype), V = 16 / e;
   const bool part_in_y = (e == 4);
   const size_t se = slot_elems(c.n, p);
@@ -480,7 +483,7 @@ int next_sem_epoch(const Call& c, uint32_t* epoch) {
 // The two all-pairs steps in one launch (k_allpairs_persistent): p * C
 // persistent workgroups, all co-resident; channel c of every rank handles
 // the same slice of each chunk.
-int run_allpairs_persistent(const Call& c, const std::vector<int64_t>& lo) {
+int run_allpairs_persistent(const Call& c, const int64_t* lo) {
   const int p = c.p;
   const int V = 16 / esize_of(c.dtype);
   AllPairsPArgs a;
@@ -526,7 +529,7 @@ int run_allpairs_persistent(const Call& c, const std::vector<int64_t>& lo) {
 
 // The whole ring in one launch (k_ring_fifo): p * C persistent workgroups,
 // all co-resident, exchanging partials through bounded FIFOs.
-int run_ring_fifo(const Call& c, const std::vector<int64_t>& lo) {
+int run_ring_fifo(const Call& c, const int64_t* lo) {
   const int p = c.p;
   const int V = 16 / esize_of(c.dtype);
   const int slot = kBlock * g.fifo_vecs * V;
@@ -718,7 +721,7 @@ int run_allreduce(const Call& c) {
   if (!sch) return SIM_ERR_VERIFY;
   if (is_topology_algo(c.algo)) return run_sched(c, *sch);
   const int p = c.p;
-  std::vector<int64_t> lo(p + 1);
+  int64_t lo[SIM_MAX_RANKS + 1];
   for (int q = 0; q <= p; q++) lo[q] = chunk_lo((int64_t)c.n, p, q);
   switch (c.algo) {
     case SIM_ALGO_ONESHOT:
@@ -828,9 +831,9 @@ int run_reduce_scatter(const Call& c) {
   if (c.algo == SIM_ALGO_ALLPAIRS) {
     std::vector<int64_t> shift(p);
     for (int q = 0; q < p; q++) shift[q] = lo[q];
-    return run_fold(c, false, lo, shift.data(), nullptr);
+    return run_fold(c, false, lo.data(), shift.data(), nullptr);
   }
-  return run_ring_rs(c, *sch, p - 1, true, lo);
+  return run_ring_rs(c, *sch, p - 1, true, lo.data());
 }
 
 int run_all_gather(const Call& c) {
@@ -1018,6 +1021,7 @@ int sim_init(int device, int p_max, size_t max_bytes_per_rank) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, device) != hipSuccess) return SIM_ERR_HIP;
   g.device = device;
+  g_launch_device = device;
   g.p_max = p_max;
   g.cu_count = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   if (hipMalloc(&g.err, 256) != hipSuccess) return SIM_ERR_NOMEM;
@@ -1083,7 +1087,7 @@ int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size
   const size_t e = (size_t)esize_of(dtype);
   if (n > ((size_t)1 << 46) / e) return SIM_ERR_INVALID_ARG;
   bool inplace = false;
-  rc = check_buffers(in_ptrs, out_ptrs, p, n * e, n * e, std::vector<size_t>(p, 0), &inplace);
+  rc = check_buffers(in_ptrs, out_ptrs, p, n * e, n * e, nullptr, &inplace);
   if (rc) return rc;
   double us = 0;
   if (use_device() != SIM_OK) return SIM_ERR_HIP;
@@ -1134,7 +1138,7 @@ int sim_reduce_scatter(const void* const* in_ptrs, void* const* out_ptrs, int p,
           return SIM_ERR_ALIAS;
   } else {
     bool ip2 = false;
-    rc = check_buffers(in_ptrs, out_ptrs, p, (size_t)p * n_out * e, n_out * e, off, &ip2);
+    rc = check_buffers(in_ptrs, out_ptrs, p, (size_t)p * n_out * e, n_out * e, off.data(), &ip2);
     if (rc) return rc;
     if (ip2) return SIM_ERR_ALIAS;
   }

@@ -34,6 +34,7 @@
 // share an XCD as in the single-launch ring.
 #include "device_sync.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace simar {
 
@@ -190,9 +191,8 @@ timeout:
 template <int DT, int OP>
 static hipError_t ap_go(const AllPairsPArgs& a, hipStream_t s) {
   const dim3 g((unsigned)(a.p * a.Cg)), b(kBlock);
-  if (a.p == 8) hipLaunchKernelGGL((k_allpairs_persistent<DT, OP, 8>), g, b, 0, s, a);
-  else hipLaunchKernelGGL((k_allpairs_persistent<DT, OP, 0>), g, b, 0, s, a);
-  return hipGetLastError();
+  if (a.p == 8) return launch<k_allpairs_persistent<DT, OP, 8>>(g, b, s, a);
+  return launch<k_allpairs_persistent<DT, OP, 0>>(g, b, s, a);
 }
 
 template <int DT>

@@ -39,6 +39,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace simar {
 
@@ -171,9 +172,7 @@ __global__ void __launch_bounds__(kBlock) k_fold(Args a) {
 
 template <int DT, int OP, int P, bool ALL_OUT, int U, class Args>
 static hipError_t go(const Args& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_fold<DT, OP, P, ALL_OUT, U, Args>), dim3((unsigned)a.tiles * (unsigned)a.p), dim3(kBlock),
-                     0, s, a);
-  return hipGetLastError();
+  return launch<k_fold<DT, OP, P, ALL_OUT, U, Args>>(dim3((unsigned)a.tiles * (unsigned)a.p), dim3(kBlock), s, a);
 }
 
 template <int DT, int OP, class Args>

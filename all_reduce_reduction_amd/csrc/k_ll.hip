@@ -26,6 +26,7 @@
 // the kernel exits normally.
 #include "device_common.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace simar {
 
@@ -121,14 +122,13 @@ template <int DT>
 static hipError_t ll_by_op(int op, const LLArgs& a, int grid, hipStream_t s) {
   const dim3 g(grid), b(kBlock);
   switch (op) {
-    case SIM_SUM: hipLaunchKernelGGL((k_ll<DT, SIM_SUM>), g, b, 0, s, a); break;
-    case SIM_PROD: hipLaunchKernelGGL((k_ll<DT, SIM_PROD>), g, b, 0, s, a); break;
-    case SIM_MIN: hipLaunchKernelGGL((k_ll<DT, SIM_MIN>), g, b, 0, s, a); break;
-    case SIM_MAX: hipLaunchKernelGGL((k_ll<DT, SIM_MAX>), g, b, 0, s, a); break;
-    case SIM_AVG: hipLaunchKernelGGL((k_ll<DT, SIM_AVG>), g, b, 0, s, a); break;
+    case SIM_SUM: return launch<k_ll<DT, SIM_SUM>>(g, b, s, a);
+    case SIM_PROD: return launch<k_ll<DT, SIM_PROD>>(g, b, s, a);
+    case SIM_MIN: return launch<k_ll<DT, SIM_MIN>>(g, b, s, a);
+    case SIM_MAX: return launch<k_ll<DT, SIM_MAX>>(g, b, s, a);
+    case SIM_AVG: return launch<k_ll<DT, SIM_AVG>>(g, b, s, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_ll(int dtype, int op, const LLArgs& a, int grid, hipStream_t s) {

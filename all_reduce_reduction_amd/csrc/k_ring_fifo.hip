@@ -51,6 +51,7 @@
 // workgroups that could not be co-resident) ends in an error, never a hang.
 #include "device_sync.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace simar {
 
@@ -280,14 +281,13 @@ template <int DT>
 static hipError_t fifo_by_op(int op, const RingFifoArgs& a, hipStream_t s) {
   const dim3 g((unsigned)(a.p * a.Cg)), b(kBlock);
   switch (op) {
-    case SIM_SUM: hipLaunchKernelGGL((k_ring_fifo<DT, SIM_SUM>), g, b, 0, s, a); break;
-    case SIM_PROD: hipLaunchKernelGGL((k_ring_fifo<DT, SIM_PROD>), g, b, 0, s, a); break;
-    case SIM_MIN: hipLaunchKernelGGL((k_ring_fifo<DT, SIM_MIN>), g, b, 0, s, a); break;
-    case SIM_MAX: hipLaunchKernelGGL((k_ring_fifo<DT, SIM_MAX>), g, b, 0, s, a); break;
-    case SIM_AVG: hipLaunchKernelGGL((k_ring_fifo<DT, SIM_AVG>), g, b, 0, s, a); break;
+    case SIM_SUM: return launch<k_ring_fifo<DT, SIM_SUM>>(g, b, s, a);
+    case SIM_PROD: return launch<k_ring_fifo<DT, SIM_PROD>>(g, b, s, a);
+    case SIM_MIN: return launch<k_ring_fifo<DT, SIM_MIN>>(g, b, s, a);
+    case SIM_MAX: return launch<k_ring_fifo<DT, SIM_MAX>>(g, b, s, a);
+    case SIM_AVG: return launch<k_ring_fifo<DT, SIM_AVG>>(g, b, s, a);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_ring_fifo(int dtype, int op, const RingFifoArgs& a, hipStream_t s) {

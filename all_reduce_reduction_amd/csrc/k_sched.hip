@@ -25,6 +25,7 @@
 // lives in scalar registers.  Ragged chunk edges run element by element.
 #include "device_common.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace simar {
 
@@ -114,8 +115,7 @@ __global__ void __launch_bounds__(kBlock) k_sched_fold(SchedArgs a) {
 
 template <int DT, int OP>
 static hipError_t go(const SchedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_sched_fold<DT, OP>), dim3((unsigned)a.tiles * (unsigned)a.nx), dim3(kBlock), 0, s, a);
-  return hipGetLastError();
+  return launch<k_sched_fold<DT, OP>>(dim3((unsigned)a.tiles * (unsigned)a.nx), dim3(kBlock), s, a);
 }
 
 template <int DT>

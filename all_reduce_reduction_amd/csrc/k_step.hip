@@ -19,6 +19,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "launch.h"
 
 namespace simar {
 
@@ -256,26 +257,22 @@ template <int DT, int OP, int U>
 static hipError_t ring_go(bool a_part, bool d_final, const RingArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.tiles * (unsigned)a.nx), block(kBlock);
   if (a_part) {
-    if (d_final) hipLaunchKernelGGL((k_ring_reduce<DT, OP, true, true, U>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_ring_reduce<DT, OP, true, false, U>), grid, block, 0, s, a);
-  } else {
-    if (d_final) hipLaunchKernelGGL((k_ring_reduce<DT, OP, false, true, U>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_ring_reduce<DT, OP, false, false, U>), grid, block, 0, s, a);
+    if (d_final) return launch<k_ring_reduce<DT, OP, true, true, U>>(grid, block, s, a);
+    return launch<k_ring_reduce<DT, OP, true, false, U>>(grid, block, s, a);
   }
-  return hipGetLastError();
+  if (d_final) return launch<k_ring_reduce<DT, OP, false, true, U>>(grid, block, s, a);
+  return launch<k_ring_reduce<DT, OP, false, false, U>>(grid, block, s, a);
 }
 
 template <int DT, int OP, int U>
 static hipError_t ring_go(bool a_part, bool d_final, const RingTabArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.tiles * (unsigned)a.p), block(kBlock);
   if (a_part) {
-    if (d_final) hipLaunchKernelGGL((k_ring_reduce_tab<DT, OP, true, true, U>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_ring_reduce_tab<DT, OP, true, false, U>), grid, block, 0, s, a);
-  } else {
-    if (d_final) hipLaunchKernelGGL((k_ring_reduce_tab<DT, OP, false, true, U>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_ring_reduce_tab<DT, OP, false, false, U>), grid, block, 0, s, a);
+    if (d_final) return launch<k_ring_reduce_tab<DT, OP, true, true, U>>(grid, block, s, a);
+    return launch<k_ring_reduce_tab<DT, OP, true, false, U>>(grid, block, s, a);
   }
-  return hipGetLastError();
+  if (d_final) return launch<k_ring_reduce_tab<DT, OP, false, true, U>>(grid, block, s, a);
+  return launch<k_ring_reduce_tab<DT, OP, false, false, U>>(grid, block, s, a);
 }
 
 template <int DT, int OP, class Args>
@@ -310,15 +307,14 @@ template <bool ONE>
 static hipError_t copy_go(int esize, const CopyArgs& a, int unroll, hipStream_t s) {
   const dim3 grid((unsigned)a.tiles * (unsigned)a.nx), block(kBlock);
   if (esize == 4) {
-    if (unroll == 2) hipLaunchKernelGGL((k_copy<4, 2, ONE>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_copy<4, 1, ONE>), grid, block, 0, s, a);
-  } else if (esize == 2) {
-    if (unroll == 2) hipLaunchKernelGGL((k_copy<2, 2, ONE>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_copy<2, 1, ONE>), grid, block, 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
+    if (unroll == 2) return launch<k_copy<4, 2, ONE>>(grid, block, s, a);
+    return launch<k_copy<4, 1, ONE>>(grid, block, s, a);
   }
-  return hipGetLastError();
+  if (esize == 2) {
+    if (unroll == 2) return launch<k_copy<2, 2, ONE>>(grid, block, s, a);
+    return launch<k_copy<2, 1, ONE>>(grid, block, s, a);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_ring_reduce_tab(int dtype, int op, bool a_partial, bool d_final, const RingTabArgs& a,
@@ -335,15 +331,14 @@ hipError_t launch_ring_reduce_tab(int dtype, int op, bool a_partial, bool d_fina
 hipError_t launch_ring_copy_tab(int esize, const RingTabArgs& a, int unroll, hipStream_t s) {
   const dim3 grid((unsigned)a.tiles * (unsigned)a.p), block(kBlock);
   if (esize == 4) {
-    if (unroll == 2) hipLaunchKernelGGL((k_ring_copy_tab<4, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_ring_copy_tab<4, 1>), grid, block, 0, s, a);
-  } else if (esize == 2) {
-    if (unroll == 2) hipLaunchKernelGGL((k_ring_copy_tab<2, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_ring_copy_tab<2, 1>), grid, block, 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
+    if (unroll == 2) return launch<k_ring_copy_tab<4, 2>>(grid, block, s, a);
+    return launch<k_ring_copy_tab<4, 1>>(grid, block, s, a);
   }
-  return hipGetLastError();
+  if (esize == 2) {
+    if (unroll == 2) return launch<k_ring_copy_tab<2, 2>>(grid, block, s, a);
+    return launch<k_ring_copy_tab<2, 1>>(grid, block, s, a);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s) {
@@ -355,23 +350,21 @@ hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s) 
 hipError_t launch_fanout_tab(int esize, const FanoutTabArgs& a, int unroll, hipStream_t s) {
   const dim3 grid((unsigned)a.tiles * (unsigned)a.p), block(kBlock);
   if (esize == 4) {
-    if (unroll == 2) hipLaunchKernelGGL((k_fanout_tab<4, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_fanout_tab<4, 1>), grid, block, 0, s, a);
-  } else if (esize == 2) {
-    if (unroll == 2) hipLaunchKernelGGL((k_fanout_tab<2, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_fanout_tab<2, 1>), grid, block, 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
+    if (unroll == 2) return launch<k_fanout_tab<4, 2>>(grid, block, s, a);
+    return launch<k_fanout_tab<4, 1>>(grid, block, s, a);
   }
-  return hipGetLastError();
+  if (esize == 2) {
+    if (unroll == 2) return launch<k_fanout_tab<2, 2>>(grid, block, s, a);
+    return launch<k_fanout_tab<2, 1>>(grid, block, s, a);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fill64(unsigned long long* p, unsigned long long v, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + kBlock - 1) / kBlock;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_fill64, dim3((unsigned)blocks), dim3(kBlock), 0, s, p, v, n);
-  return hipGetLastError();
+  return launch<k_fill64>(dim3((unsigned)blocks), dim3(kBlock), s, p, v, n);
 }
 
 }  // namespace simar

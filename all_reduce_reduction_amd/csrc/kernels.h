@@ -18,6 +18,11 @@ namespace simar {
 
 constexpr int kBlock = 256;  // threads per workgroup (4 wavefronts of 64)
 
+// The device the library launches on (the one sim_init chose).  Launches
+// keep their kernel handles per device index, up to kMaxDevices devices.
+constexpr int kMaxDevices = 64;
+extern int g_launch_device;
+
 // Gather-fold of whole chunks: the fused one-shot (every rank's output
 // written from the same registers) or all-pairs step 1 / direct
 // reduce-scatter (only the owner's output written).
