@@ -96,6 +96,11 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 
+try:  # the prepared-call object (csrc/pycall.c), built beside the library
+    from . import _pycall
+except ImportError:  # not built: prepare_allreduce falls back to a ctypes call of the same entry point
+    _pycall = None
+
 
 def _check(status: int, what: str) -> int:
     if status != SIM_OK:
@@ -142,13 +147,17 @@ def prepare_allreduce(in_ptrs, out_ptrs, p, n, dtype, op, algo, stream=0):
     returns a function of no arguments that calls the C entry point and
     returns its status (for loops that repeat one call, where Python-side
     marshalling would otherwise dominate a few-microsecond call)."""
-    # a bare function pointer (no argtypes) called with ready-made ctypes
-    # objects: no per-call argument conversion (~0.8 us less per call)
     f = lib["sim_allreduce"]
     f.restype = ctypes.c_int
+    dt, o, a = _code(DTYPES, dtype, "dtype"), _code(OPS, op, "op"), _code(ALGOS, algo, "algo")
+    if _pycall is not None:
+        # the arguments held as C values and the entry point called directly
+        return _pycall.PreparedCall(ctypes.cast(f, ctypes.c_void_p).value, [int(q) for q in in_ptrs],
+                                    [int(q) for q in out_ptrs], p, n, dt, o, a, int(stream or 0))
+    # a bare function pointer (no argtypes) called with ready-made ctypes
+    # objects: no per-call argument conversion
     args = (_ptr_array(in_ptrs), _ptr_array(out_ptrs), ctypes.c_int(p), ctypes.c_size_t(n),
-            ctypes.c_int(_code(DTYPES, dtype, "dtype")), ctypes.c_int(_code(OPS, op, "op")),
-            ctypes.c_int(_code(ALGOS, algo, "algo")), ctypes.c_void_p(stream or None))
+            ctypes.c_int(dt), ctypes.c_int(o), ctypes.c_int(a), ctypes.c_void_p(stream or None))
     return lambda: f(*args)
 
 

@@ -65,6 +65,23 @@ def build(jobs: int = 0, out: str = LIB, build_dir: str = BUILD) -> str:
     return out
 
 
+def build_pycall(out_dir: str = HERE) -> str:
+    """Compile the prepared-call extension (_pycall) with the host C compiler
+    against this interpreter's headers; always rebuilds."""
+    import sysconfig
+    cc = os.environ.get("CC", "gcc")
+    out = os.path.join(out_dir, "_pycall" + sysconfig.get_config_var("EXT_SUFFIX"))
+    tmp = out + ".tmp"
+    cmd = [cc, "-O2", "-shared", "-fPIC", "-std=c11", "-Wall", "-Werror",
+           "-I", sysconfig.get_paths()["include"], "-I", INCLUDE,
+           os.path.join(CSRC, "pycall.c"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("pycall build failed:\n" + r.stdout + r.stderr)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     import argparse
     ap = argparse.ArgumentParser()
@@ -72,3 +89,4 @@ if __name__ == "__main__":
     ap.add_argument("--build-dir", default=BUILD)
     a = ap.parse_args()
     print(build(out=a.out, build_dir=a.build_dir))
+    print(build_pycall())

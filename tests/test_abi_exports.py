@@ -48,3 +48,26 @@ def test_binding_has_same_names_as_header():
     import all_reduce_reduction_amd as sim
     for n in declared():
         assert callable(getattr(sim, n)), n
+
+
+def test_prepared_call_object():
+    """prepare_allreduce returns the C-level prepared call (csrc/pycall.c),
+    which hands its stored arguments to sim_allreduce unchanged and checks
+    only what it must to store them."""
+    import pytest
+
+    import all_reduce_reduction_amd as sim
+    assert sim._pycall is not None, "the prepared-call extension is not built"
+    call = sim.prepare_allreduce([16, 32, 48], [64, 80, 96], 3, 5, "fp16", "max", "ring")
+    assert isinstance(call, sim._pycall.PreparedCall)
+    assert call() == -9 and call() == -9  # the library's own answer before sim_init, every time
+    with pytest.raises(TypeError):
+        call(1)
+    with pytest.raises(ValueError):  # list length must match p
+        sim.prepare_allreduce([0, 0, 0], [0, 0], 2, 4, "int32", "sum", "oneshot")
+    with pytest.raises(ValueError):  # more ranks than the stored arrays hold
+        sim.prepare_allreduce([0] * 17, [0] * 17, 17, 4, "int32", "sum", "oneshot")
+    with pytest.raises(TypeError):
+        sim.prepare_allreduce([None, None], [0, 0], 2, 4, "int32", "sum", "oneshot")
+    # p < 2 is the library's to refuse (before sim_init: not initialised)
+    assert sim.prepare_allreduce([0], [0], 1, 4, "int32", "sum", "oneshot")() == -9

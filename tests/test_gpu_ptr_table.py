@@ -181,15 +181,17 @@ def test_captured_calls_do_not_use_the_table(orc, lib):
     del graph
 
 
-def test_prepared_call_matches_the_oracle(orc, lib):
-    """The binding's prepared call (arguments marshalled once) repeated
-    with new inputs behind the same pointers."""
+@pytest.mark.parametrize("algo", ["auto", "ring", "oneshot_ll", "allpairs_persistent"])
+def test_prepared_call_matches_the_oracle(orc, lib, algo):
+    """The binding's prepared call (arguments marshalled once, held by the
+    C-level call object) repeated with new inputs behind the same pointers."""
     from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
     sim = lib
     p, n, dtype = 8, 4096 + 3, "fp16"
     din = to_device(_inputs(dtype, p, n, 2), dtype)
     dout = empty_like_poisoned(n, dtype, p)
-    call = sim.prepare_allreduce(ptrs(din), ptrs(dout), p, n, dtype, "sum", "auto", stream())
+    call = sim.prepare_allreduce(ptrs(din), ptrs(dout), p, n, dtype, "sum", algo, stream())
+    assert isinstance(call, sim._pycall.PreparedCall)
     for rep in range(3):
         xs = _inputs(dtype, p, n, 200 + rep)
         for t, x in zip(din, to_device(xs, dtype)):
