@@ -53,6 +53,15 @@
  *     max_bytes_per_rank or make one uncaptured call of the same shape
  *     first.  Once a call has been captured, outgrown scratch is kept until
  *     sim_finalize, so recorded graphs stay valid until then (not after).
+ *   - Co-residency: SIM_ALGO_RING_FIFO and SIM_ALGO_ALLPAIRS_PERSISTENT run
+ *     persistent workgroups that wait on one another, so all of them must be
+ *     resident on the GPU at once.  The library sizes the grid from the
+ *     kernels' occupancy on an otherwise idle GPU; kernels running at the
+ *     same time on other streams may hold CUs those workgroups need.  Every
+ *     wait is bounded: such a call then ends with SIM_ERR_TIMEOUT (reported
+ *     by sim_check_error; that call's outputs are undefined), never a hang.
+ *     AUTO does not pick these two schedules on MI355X (the calibrated model
+ *     ranks the one-shot first at every size).
  *   - Shared library buffers: the partial scratch (16-bit ring, tree,
  *     recursive exchange and 2PH all-reduces; the ring reduce-scatter), the
  *     LL packet buffer, and the FIFOs and counters of the single-launch
