@@ -203,6 +203,35 @@ def check_minmax_library(orc):
                 assert (ys[0].view(np.float16) == want16).all(), (p, op, algo, "fp16")
 
 
+def check_minmax_nan_and_signed_zero(orc):
+    """Min/max keep the accumulator unless the new operand compares strictly
+    below (min) or above (max) it; the pages leave NaN and signed-zero ties
+    open, and this is the reading both the oracle and the kernels take.
+    Expected values worked by hand at p = 2, n = 2 (element c is chunk c):
+    the all-pairs family folds chunk c owner first (rank c, then the other),
+    the ring starts chunk c at rank c + 1."""
+    nan, pz, nz = np.float32("nan"), np.float32(0.0), np.float32(-0.0)
+    # x0 = [NaN, NaN], x1 = [1, 1]: a NaN accumulator stays, a NaN operand is passed over
+    x = [np.array([nan, nan], np.float32), np.array([1.0, 1.0], np.float32)]
+    # x0 = [+0, -0], x1 = [-0, +0]: a tie keeps whichever value came first
+    z = [np.array([pz, nz], np.float32), np.array([nz, pz], np.float32)]
+    for algo in ALGOS:
+        ring = algo in ("ring", "ring_fifo")
+        # all-pairs: chunk 0 starts at rank 0 (NaN), chunk 1 at rank 1 (1.0);
+        # ring: chunk 0 starts at rank 1 (1.0), chunk 1 at rank 0 (NaN)
+        want_nan = [False, True] if ring else [True, False]
+        # all-pairs: chunk 0 starts with +0, chunk 1 with +0; ring: -0 and -0
+        want_sign = [True, True] if ring else [False, False]
+        for op in ("min", "max"):
+            ys, _ = orc.allreduce(x, "fp32", op, algo)
+            for r in range(2):
+                assert list(np.isnan(ys[r])) == want_nan, (algo, op, r, ys[r])
+                assert (ys[r][~np.isnan(ys[r])] == 1.0).all(), (algo, op, r, ys[r])
+            ys, _ = orc.allreduce(z, "fp32", op, algo)
+            for r in range(2):
+                assert (ys[r] == 0).all() and list(np.signbit(ys[r])) == want_sign, (algo, op, r, ys[r])
+
+
 def check_p2_sum(orc):
     rng = np.random.default_rng(3)
     a, b = (rng.standard_normal(1001).astype(np.float32) for _ in range(2))
@@ -633,7 +662,7 @@ def check_topology_exact(orc):
 ALL_CHECKS = [
     check_worked_example, check_step_counts, check_exactly_once, check_int_brute_force,
     check_fold_order_probes, check_identical_ranks, check_order_independent_fp,
-    check_minmax_library, check_p2_sum, check_avg, check_16bit_single_rounding,
+    check_minmax_library, check_minmax_nan_and_signed_zero, check_p2_sum, check_avg, check_16bit_single_rounding,
     check_error_bound_16bit, check_rs_ag, check_sampled,
     check_tree_drawing, check_dtree_listing, check_tree_shapes, check_tree_chains, check_tree_rounds,
     check_tree_association, check_tree_chain_closed_form, check_rexch, check_hier, check_topology_exact,

@@ -126,6 +126,63 @@ def test_edge_values(orc):
                         assert_parity(got[r], want[r], dtype, f"finite {dtype} {op} {algo} p={p}")
 
 
+# fp32 NaNs: quiet (both signs, a payload) and signalling
+NAN32 = np.array([0x7FC00000, 0xFFC00000, 0x7FC12345, 0x7F800001, 0xFFA00000], dtype=np.uint32).view(np.float32)
+
+
+def test_nan_inputs(orc):
+    """NaN inputs among finite values.  min/max choose an input (the
+    accumulator is kept unless the comparison holds, so a NaN accumulator
+    stays and a NaN operand is passed over): for fp32 they must match the
+    oracle bit for bit, NaN payloads included.  Every op must be NaN exactly
+    where the oracle is and bit-exact elsewhere; the payload of a NaN that
+    arithmetic produced is left open, as IEEE 754 leaves it.  Outputs start
+    as a finite sentinel, so an unwritten element fails even where a NaN is
+    expected."""
+    import torch
+
+    import all_reduce_reduction_amd as sim
+    from tests.gpu_util import TORCH_STORAGE, bits, dev, ptrs, stream, to_device, to_host, widen16
+    rng = np.random.default_rng(11)
+    finite = np.array([0.5, -1.25, 2.0, -3.0, 1.0, 0.0, -0.0], dtype=np.float32)  # |prod| <= 3^8 at p = 8
+    sentinel = np.float32(-12345.0)
+    for p, n in ((2, 37), (3, 8 * 64 + 5), (8, 8 * 512 + 5)):
+        x32 = []
+        for _ in range(p):
+            v = finite[rng.integers(0, len(finite), n)]
+            m = rng.random(n) < 0.08
+            v[m] = NAN32[rng.integers(0, len(NAN32), int(m.sum()))]
+            x32.append(v)
+        for dtype in ("fp32", "fp16", "bf16"):
+            if dtype == "fp32":
+                xs, fill = x32, float(sentinel)
+            elif dtype == "fp16":
+                with np.errstate(invalid="ignore"):
+                    xs = [x.astype(np.float16).view(np.uint16) for x in x32]
+                fill = int(np.float16(sentinel).view(np.int16))
+            else:
+                xs = [orc.f32_to_bf16(x) for x in x32]
+                fill = int(orc.f32_to_bf16(np.array([sentinel], dtype=np.float32)).view(np.int16)[0])
+            din = to_device(xs, dtype)
+            for op in ("sum", "prod", "min", "max", "avg"):
+                for algo in ALGOS:
+                    want, _ = orc.allreduce(xs, dtype, op, algo)
+                    dout = [torch.full((n,), fill, dtype=TORCH_STORAGE[dtype], device=dev()) for _ in range(p)]
+                    st = sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, algo, stream())
+                    assert st == 0, (dtype, op, algo, p, n, st)
+                    assert sim.sim_check_error(stream()) == 0
+                    got = to_host(dout, dtype)
+                    what = f"NaN inputs {dtype} {op} {algo} p={p} n={n}"
+                    for r in range(p):
+                        g = got[r] if dtype == "fp32" else widen16(got[r], dtype)
+                        w = want[r] if dtype == "fp32" else widen16(want[r], dtype)
+                        assert (np.isnan(g) == np.isnan(w)).all(), f"{what} r{r}: NaN positions differ"
+                        ok = ~np.isnan(w)
+                        assert (bits(got[r])[ok] == bits(want[r])[ok]).all(), f"{what} r{r}: values differ"
+                        if dtype == "fp32" and op in ("min", "max"):
+                            assert (bits(got[r]) == bits(want[r])).all(), f"{what} r{r}: NaN payloads differ"
+
+
 def test_16bit_ties_round_to_even(orc):
     """Products of 16-bit values often land exactly half-way between two
     16-bit numbers in fp32; the result must be the fp32 value rounded once,

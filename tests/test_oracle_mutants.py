@@ -35,6 +35,10 @@ MUTANTS = {
                              "case OR_MIN: r.i = (b.i < a.i) ? a.i : b.i; break;"),
     "fp_max_is_min": ("default:     r.f = (b.f > a.f) ? b.f : a.f; break;",
                       "default:     r.f = (b.f < a.f) ? b.f : a.f; break;"),
+    "fp_min_ties_take_operand": ("case OR_MIN: r.f = (b.f < a.f) ? b.f : a.f; break;",
+                                 "case OR_MIN: r.f = (b.f <= a.f) ? b.f : a.f; break;"),
+    "fp_min_replaces_nan_accumulator": ("case OR_MIN: r.f = (b.f < a.f) ? b.f : a.f; break;",
+                                        "case OR_MIN: r.f = (b.f < a.f || a.f != a.f) ? b.f : a.f; break;"),
     "int_prod_is_sum": ("case OR_PROD: r.u = a.u * b.u; break;", "case OR_PROD: r.u = a.u + b.u; break;"),
     "int_avg_no_divide": ("(c->op == OR_AVG) ? (int32_t)(v.i / c->p) : v.i", "v.i"),
     "fp_avg_not_scaled": ("a.f = scaled;", "(void)scaled;"),
