@@ -86,11 +86,20 @@ def assert_parity(got: np.ndarray, want: np.ndarray, dtype: str, what: str = "")
     assert diff.size == 0, f"{what}: {diff.size} elements differ, first at {diff[:5]}: got {got[diff[:5]]} want {want[diff[:5]]}"
 
 
-def run_allreduce(xs: Sequence[np.ndarray], dtype: str, op: str, algo: str, inplace: bool = False):
+def run_allreduce(xs: Sequence[np.ndarray], dtype: str, op: str, algo: str, inplace: bool = False,
+                  fill=None):
+    """The library's all-reduce of xs (host arrays, storage format) on the
+    device; outputs start as the poison pattern, or as `fill` (a storage
+    value) when given."""
     n = xs[0].size
     p = len(xs)
     din = to_device(xs, dtype)
-    dout = din if inplace else empty_like_poisoned(n, dtype, p)
+    if inplace:
+        dout = din
+    elif fill is not None:
+        dout = [torch.full((max(n, 1),), fill, dtype=TORCH_STORAGE[dtype], device=dev())[:n] for _ in range(p)]
+    else:
+        dout = empty_like_poisoned(n, dtype, p)
     st = sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, algo, stream())
     if st != 0:
         raise sim.SimError(st, f"sim_allreduce({algo}, p={p}, n={n}, {dtype}, {op})")

@@ -139,10 +139,7 @@ def test_nan_inputs(orc):
     arithmetic produced is left open, as IEEE 754 leaves it.  Outputs start
     as a finite sentinel, so an unwritten element fails even where a NaN is
     expected."""
-    import torch
-
-    import all_reduce_reduction_amd as sim
-    from tests.gpu_util import TORCH_STORAGE, bits, dev, ptrs, stream, to_device, to_host, widen16
+    from tests.gpu_util import bits, run_allreduce, widen16
     rng = np.random.default_rng(11)
     finite = np.array([0.5, -1.25, 2.0, -3.0, 1.0, 0.0, -0.0], dtype=np.float32)  # |prod| <= 3^8 at p = 8
     sentinel = np.float32(-12345.0)
@@ -163,15 +160,10 @@ def test_nan_inputs(orc):
             else:
                 xs = [orc.f32_to_bf16(x) for x in x32]
                 fill = int(orc.f32_to_bf16(np.array([sentinel], dtype=np.float32)).view(np.int16)[0])
-            din = to_device(xs, dtype)
             for op in ("sum", "prod", "min", "max", "avg"):
                 for algo in ALGOS:
                     want, _ = orc.allreduce(xs, dtype, op, algo)
-                    dout = [torch.full((n,), fill, dtype=TORCH_STORAGE[dtype], device=dev()) for _ in range(p)]
-                    st = sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, algo, stream())
-                    assert st == 0, (dtype, op, algo, p, n, st)
-                    assert sim.sim_check_error(stream()) == 0
-                    got = to_host(dout, dtype)
+                    got = run_allreduce(xs, dtype, op, algo, fill=fill)
                     what = f"NaN inputs {dtype} {op} {algo} p={p} n={n}"
                     for r in range(p):
                         g = got[r] if dtype == "fp32" else widen16(got[r], dtype)

@@ -89,6 +89,43 @@ def test_topology_edge_values(orc, lib):
                 assert (got[r].view(np.uint32) == want[r].view(np.uint32)).all(), (algo, op, r)
 
 
+def test_topology_nan_inputs(orc, lib):
+    """NaN inputs through the step executor: fp32 min/max select inputs, so
+    they match the oracle bit for bit (payloads included); sum, prod and avg
+    are NaN exactly where the oracle is, bit-exact elsewhere, in fp32 and in
+    the fp32 partials of the 16-bit schedules.  Outputs start as a finite
+    sentinel, so an unwritten element fails where a NaN is expected too."""
+    from tests.gpu_util import bits, run_allreduce, widen16
+    p, n = 8, 4096 + 3
+    rng = np.random.default_rng(78)
+    vals = np.array([0.5, -1.25, 2.0, -3.0, 1.0, 0.0, -0.0], dtype=np.float32)
+    nans = np.array([0x7FC00000, 0xFFC00000, 0x7FC12345, 0x7F800001], dtype=np.uint32).view(np.float32)
+    x32 = []
+    for _ in range(p):
+        v = vals[rng.integers(0, vals.size, n)]
+        m = rng.random(n) < 0.08
+        v[m] = nans[rng.integers(0, nans.size, int(m.sum()))]
+        x32.append(v)
+    for algo, G, k in (("tree", 2, 2), ("rexch", 1, 2), ("hier", 4, 2), ("hier_large", 2, 2)):
+        _topo(lib, G, k)
+        for dtype in ("fp32", "bf16"):
+            xs = x32 if dtype == "fp32" else [orc.f32_to_bf16(x) for x in x32]
+            fill = -12345.0 if dtype == "fp32" else int(
+                orc.f32_to_bf16(np.array([-12345.0], dtype=np.float32)).view(np.int16)[0])
+            for op in OPS:
+                want, _ = orc.allreduce(xs, dtype, op, algo, ranks_per_node=G, radix=k)
+                got = run_allreduce(xs, dtype, op, algo, fill=fill)
+                for r in range(p):
+                    g = got[r] if dtype == "fp32" else widen16(got[r], dtype)
+                    w = want[r] if dtype == "fp32" else widen16(want[r], dtype)
+                    what = (algo, dtype, op, r)
+                    assert (np.isnan(g) == np.isnan(w)).all(), what
+                    ok = ~np.isnan(w)
+                    assert (bits(got[r])[ok] == bits(want[r])[ok]).all(), what
+                    if dtype == "fp32" and op in ("min", "max"):
+                        assert (bits(got[r]) == bits(want[r])).all(), what
+
+
 def test_topology_repeated_calls_reuse_scratch(orc, lib):
     """fp16 partials live in library scratch: back-to-back calls of different
     schedules and sizes on one stream stay independent."""
