@@ -3,7 +3,7 @@
 //
 // One-shot ("MSCCL++ ...", section "The Collective Algorithm Library":
 // in 1PA every rank reads every rank's data and reduces it in one phase;
-// "concurrent multi-peer reduction" reads all peers at once instead of one
+// its multi-peer reduction reads all peers at the same time instead of one
 // by one): each lane issues the 16-byte loads of all p ranks for its
 // vector back to back, folds them in VGPRs in the all-pairs order (owner of
 // the chunk first, then the other ranks ascending -- the order of the

@@ -203,7 +203,7 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p,
 /* The schedule SIM_ALGO_AUTO would run for this call, with its predicted
  * time in microseconds: argmin over legal algos of
  *   T_a = alpha_a * launches_a(p) + traffic_a(p, n, dtype) / B_a
- * ("time = latency + bytes / bandwidth"), traffic_a being the schedule's
+ * (a launch cost plus bytes over bandwidth), traffic_a being the schedule's
  * algorithmic HBM bytes over all simulated ranks. */
 int sim_select(int p, size_t n, int dtype, int op, int* algo_out, double* predicted_us);
 

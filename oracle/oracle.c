@@ -52,8 +52,8 @@
  *    ascending child order; the root's total is post-processed and is every
  *    rank's result.  Tree two = tree one's mirror (node x plays n-1-x) for
  *    an even node count, tree one shifted by +1 node for an odd one (the
- *    pages say "shifted by one rank" without a direction: the +1 is a
- *    reading, and parity is unpinned for that direction alone).  With
+ *    pages move tree one over by a single rank but give no direction: the
+ *    +1 is a reading, and parity is unpinned for that direction alone).  With
  *    G ranks per node, node k is rank kG and ranks kG+1..kG+G-1 hang below
  *    it as a chain.
  *  - recursive exchange: p must be k^m; round j (j = 0 first) folds the k
