@@ -159,6 +159,32 @@ struct RingFifoArgs {
   int withhold;                // test hook: rank 0 leaves at once, its partners' waits expire
 };
 
+// The single-launch ring with LL packets (small messages): p * C persistent
+// workgroups, rank-major grid.  Every value that crosses from rank r to
+// rank r+1 -- a partial of the reduce-scatter half (fp32 / int32 bits) or a
+// finished element of the all-gather half (storage bits) -- travels as one
+// 8-byte packet {low 32 bits payload, high 32 bits epoch} in the receiver's
+// region of the LL buffer: send k (0 <= k < 2p-2) of chunk offset o at
+// ll[(r+1) * ll_stride + k * maxchunk + o].  No counters: the receiver
+// polls the packets themselves.
+struct RingLLArgs {
+  const void* x[SIM_MAX_RANKS];
+  void* y[SIM_MAX_RANKS];
+  int64_t lo[SIM_MAX_RANKS + 1];
+  unsigned long long* ll;
+  int64_t ll_stride;           // packets per rank region
+  int64_t maxchunk;            // longest chunk (packets per send)
+  unsigned long long spin_limit;
+  int* err;
+  int p;
+  int C;                       // channels per rank
+  int Cg;                      // channels in the grid (rank-major, C rounded up to a multiple of 8 when it fits)
+  unsigned int epoch;          // flag the senders write
+  unsigned int wait_epoch;     // flag the receivers accept (== epoch unless a test skews it)
+  float inv_p;
+  int withhold;                // test hook: rank 0 leaves at once, its partners' waits expire
+};
+
 // The all-pairs schedule in ONE launch: p * C persistent workgroups.
 // Workgroup (rank r, channel c) folds its slice of chunk r from every
 // rank's input into Y[r] (owner first, then ascending) and signals; then,
@@ -211,6 +237,7 @@ static_assert(sizeof(FanoutTabArgs) <= 64, "must fit the small-argument launch p
 static_assert(sizeof(RingTabArgs) <= 64, "must fit the small-argument launch path");
 static_assert(sizeof(SchedArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingFifoArgs) <= 4096, "kernel argument segment too large");
+static_assert(sizeof(RingLLArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(AllPairsPArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(RingArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(CopyArgs) <= 4096, "kernel argument segment too large");
@@ -235,6 +262,8 @@ int ll_blocks_per_cu(int dtype, int op);
 hipError_t launch_ring_fifo(int dtype, int op, const RingFifoArgs& a, hipStream_t s);
 hipError_t launch_sched_fold(int dtype, int op, const SchedArgs& a, hipStream_t s);
 int ring_fifo_blocks_per_cu(int dtype, int op);
+hipError_t launch_ring_ll(int dtype, int op, const RingLLArgs& a, hipStream_t s);
+int ring_ll_blocks_per_cu(int dtype, int op);
 hipError_t launch_allpairs_persistent(int dtype, int op, const AllPairsPArgs& a, hipStream_t s);
 int allpairs_persistent_blocks_per_cu(int dtype, int op, int p);
 

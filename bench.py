@@ -312,6 +312,14 @@ def main():
             lat[a] = round(time_calls(call, 2000, 200) * 1e6, 2)
             if a == "auto":
                 lat["auto_pick"] = sim.sim_last_algo()
+        # the single-launch ring runs its LL protocol at this size; its FIFO
+        # protocol for comparison
+        sim.sim_debug_set("ring_ll_max", 0)
+        call = sim.prepare_allreduce(lip, lop, P, LAT_N, "fp16", "sum", "ring_fifo", stream)
+        if call() != 0:
+            raise sim.SimError(call(), "sim_allreduce(ring_fifo, FIFO protocol)")
+        lat["ring_fifo_fifo_protocol"] = round(time_calls(call, 2000, 200) * 1e6, 2)
+        sim.sim_debug_set("ring_ll_max", 256 << 10)
         for name, a, G, k in TOPOLOGY_RUNS:
             sim.sim_config_set("ranks_per_node", G)
             sim.sim_config_set("radix", k)

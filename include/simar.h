@@ -64,8 +64,9 @@
  *     ranks the one-shot first at every size).
  *   - Shared library buffers: the partial scratch (16-bit ring, tree,
  *     recursive exchange and 2PH all-reduces; the ring reduce-scatter), the
- *     LL packet buffer, and the FIFOs and counters of the single-launch
- *     ring and all-pairs belong to the library, one set per process.  Calls
+ *     LL packet buffer (the LL one-shot and the single-launch ring's LL
+ *     protocol), and the FIFOs and counters of the single-launch ring and
+ *     all-pairs belong to the library, one set per process.  Calls
  *     that use one of them must not run at the same time on different
  *     streams (calls on one stream are ordered); one-shot, all-pairs, the
  *     32-bit ring all-reduce, the ring all-gather and the all-pairs
@@ -133,7 +134,9 @@ enum {
   SIM_ALGO_ONESHOT = 3,     /* the 2 all-pairs steps fused in one launch */
   SIM_ALGO_ONESHOT_LL = 4,  /* one-shot through 8-byte data+flag packets */
   SIM_ALGO_RING_FIFO = 5,   /* the ring in ONE launch: persistent workgroups, bounded
-                               FIFOs between neighbours, in-kernel signal/wait */
+                               FIFOs between neighbours, in-kernel signal/wait; up to
+                               SIM_DEBUG_RING_LL_MAX bytes per rank (256 KiB) every hop
+                               is instead one polled LL packet (NCCL's LL protocol) */
   SIM_ALGO_TREE = 6,        /* double binary tree: each half of the buffer reduced up
                                and broadcast down one of two complementary trees */
   SIM_ALGO_REXCH = 7,       /* k-ary recursive exchange: log_k(p) rounds */
@@ -333,7 +336,9 @@ enum {
   SIM_DEBUG_FIFO_WITHHOLD = 9, /* 1: rank 0's ring workgroups leave at once (forces a bounded-wait expiry) */
   SIM_DEBUG_FIFO_VECS = 10,    /* single-launch ring: 16-byte vectors per lane per slot, 1, 2 or 4 (default 4) */
   SIM_DEBUG_PTR_TABLE = 11,    /* 0: all-reduce calls never use the pointer table (default 1) */
-  SIM_DEBUG_PTR_SETS = 12      /* get only: pointer sets the table holds */
+  SIM_DEBUG_PTR_SETS = 12,     /* get only: pointer sets the table holds */
+  SIM_DEBUG_RING_LL_MAX = 13   /* single-launch ring: largest message (bytes per rank) sent as
+                                  LL packets (default 256 KiB; 0 = never) */
 };
 int sim_debug_set(int key, uint64_t value);
 int sim_debug_get(int key, uint64_t* value);

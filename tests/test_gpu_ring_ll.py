@@ -1,0 +1,123 @@
+"""The single-launch ring's LL protocol (small messages): every hop is one
+8-byte {payload, epoch} packet polled by the receiver.  Its fold order is
+the ring's, so both protocols must give the ring oracle's bits at the same
+sizes; channel counts; stale packets and unrelated flags in the buffer; the
+epoch count it shares with the LL one-shot across a wraparound; and a
+missing partner or an unsatisfiable flag ending in SIM_ERR_TIMEOUT."""
+import pytest
+
+from tests.test_gpu_parity import inputs, prod_inputs
+
+pytestmark = pytest.mark.gpu
+
+OK, TIMEOUT = 0, -7
+DTYPES = ["int32", "fp32", "fp16", "bf16"]
+OPS = ["sum", "prod", "min", "max", "avg"]
+SHAPES = [(2, 1), (3, 7), (8, 3), (8, 4096), (5, 999), (16, 257), (8, 8191), (7, 12345)]
+FORCE_LL, NEVER_LL = 1 << 30, 0
+
+
+@pytest.fixture(autouse=True)
+def lib():
+    import all_reduce_reduction_amd as sim
+    sim.sim_init(0, 16, 0)
+    yield sim
+    sim.sim_debug_set("ring_ll_max", 256 << 10)
+    sim.sim_debug_set("fifo_channels", 0)
+    sim.sim_debug_set("ll_wait_skew", 0)
+    sim.sim_debug_set("fifo_withhold", 0)
+    sim.sim_debug_set("spin_limit", 1 << 20)
+
+
+def test_default_limit(lib):
+    assert lib.sim_debug_get("ring_ll_max") == 256 << 10
+
+
+@pytest.mark.parametrize("op", OPS)
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_both_protocols_give_the_ring_bits(orc, lib, dtype, op):
+    from tests.gpu_util import assert_parity, run_allreduce
+    sim = lib
+    for p, n in SHAPES:
+        xs = (prod_inputs if op == "prod" else inputs)(p, n, dtype, 9, orc)
+        want, _ = orc.allreduce(xs, dtype, op, "ring_fifo")
+        for limit in (FORCE_LL, NEVER_LL):
+            sim.sim_debug_set("ring_ll_max", limit)
+            for inplace in (False, True):
+                print(f"ring_fifo limit={limit} p={p} n={n} {dtype} {op} inplace={inplace}", flush=True)
+                got = run_allreduce([x.copy() for x in xs], dtype, op, "ring_fifo", inplace=inplace)
+                for r in range(p):
+                    assert_parity(got[r], want[r], dtype, f"limit {limit} p={p} n={n} ip={inplace} r{r}")
+
+
+def test_channel_counts(orc, lib):
+    import synthdata
+    from tests.gpu_util import assert_parity, run_allreduce
+    sim = lib
+    xs = synthdata.normal(61, 8, 8 * 2048 + 5, "fp32")
+    want, _ = orc.allreduce(xs, "fp32", "sum", "ring_fifo")
+    sim.sim_debug_set("ring_ll_max", FORCE_LL)
+    for ch in (1, 2, 5, 16):
+        sim.sim_debug_set("fifo_channels", ch)
+        print(f"ring LL channels {ch}", flush=True)
+        got = run_allreduce(xs, "fp32", "sum", "ring_fifo")
+        for r in range(8):
+            assert_parity(got[r], want[r], "fp32", f"channels {ch} r{r}")
+
+
+def test_stale_and_foreign_packets_are_ignored(orc, lib):
+    import synthdata
+    from tests.gpu_util import run_allreduce
+    sim = lib
+    xs = synthdata.normal(62, 8, 4096, "bf16")
+    want, _ = orc.allreduce(xs, "bf16", "sum", "ring_fifo")
+    run_allreduce(xs, "bf16", "sum", "ring_fifo")
+    cur = sim.sim_debug_get("epoch")
+    for fill in ((cur << 32) | 0xDEADBEEF, (0x13572468 << 32) | 0x0BADF00D):
+        sim.sim_debug_set("fill_ll", fill)
+        got = run_allreduce(xs, "bf16", "sum", "ring_fifo")
+        for r in range(8):
+            assert (got[r] == want[r]).all()
+
+
+def test_epoch_wraparound_shared_with_the_ll_oneshot(orc, lib):
+    import synthdata
+    from tests.gpu_util import run_allreduce
+    sim = lib
+    xs = synthdata.normal(63, 8, 4096 + 3, "fp16")
+    want_ring, _ = orc.allreduce(xs, "fp16", "sum", "ring_fifo")
+    want_ll, _ = orc.allreduce(xs, "fp16", "sum", "oneshot_ll")
+    sim.sim_debug_set("epoch", 0xFFFFFFFD)
+    seen = []
+    for k in range(6):
+        algo = "ring_fifo" if k % 2 == 0 else "oneshot_ll"
+        got = run_allreduce(xs, "fp16", "sum", algo)
+        seen.append(sim.sim_debug_get("epoch"))
+        want = want_ring if algo == "ring_fifo" else want_ll
+        for r in range(8):
+            assert (got[r] == want[r]).all(), (k, algo, r)
+    assert seen == [0xFFFFFFFE, 0xFFFFFFFF, 1, 2, 3, 4]
+
+
+def test_missing_partner_and_unsatisfiable_flag_time_out(orc, lib):
+    """Rank 0's workgroups leave at once, or every receiver waits for a flag
+    no sender writes (both host-set test flags): the bounded polls expire,
+    the kernel ends, the error word says SIM_ERR_TIMEOUT; the next call is
+    correct."""
+    import synthdata
+    from tests.gpu_util import empty_like_poisoned, ptrs, run_allreduce, stream, to_device
+    sim = lib
+    xs = synthdata.normal(64, 8, 4096, "bf16")
+    want, _ = orc.allreduce(xs, "bf16", "sum", "ring_fifo")
+    din = to_device(xs, "bf16")
+    for hook in ("fifo_withhold", "ll_wait_skew"):
+        sim.sim_debug_set("spin_limit", 64)
+        sim.sim_debug_set(hook, 1)
+        dout = empty_like_poisoned(4096, "bf16", 8)
+        assert sim.sim_allreduce(ptrs(din), ptrs(dout), 8, 4096, "bf16", "sum", "ring_fifo", stream()) == OK
+        assert sim.sim_check_error(stream()) == TIMEOUT, hook
+        sim.sim_debug_set(hook, 0)
+        sim.sim_debug_set("spin_limit", 1 << 20)
+        got = run_allreduce(xs, "bf16", "sum", "ring_fifo")
+        for r in range(8):
+            assert (got[r] == want[r]).all(), (hook, r)
