@@ -33,16 +33,16 @@ namespace simar {
 Model default_model() {
   Model m;
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING] = {2.9, 5800.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ALLPAIRS] = {3.2, 5700.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT] = {3.5, 5700.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT_LL] = {7.9, 6900.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING_FIFO] = {28.2, 6450.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING] = {2.7, 5800.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ALLPAIRS] = {2.8, 5700.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT] = {3.0, 5750.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT_LL] = {7.9, 6700.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING_FIFO] = {14.1, 6400.0, -1.0, -1.0};
   m.a[SIM_ALGO_TREE] = {4.1, 6000.0, -1.0, -1.0};
   m.a[SIM_ALGO_REXCH] = {3.9, 5250.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER] = {3.1, 5900.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER_LARGE] = {3.1, 5800.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {6.7, 6600.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER] = {4.0, 5950.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER_LARGE] = {4.4, 5900.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {6.6, 6600.0, -1.0, -1.0};
   return m;
 }
 
