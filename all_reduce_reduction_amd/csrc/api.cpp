@@ -865,14 +865,21 @@ int run_allreduce(const Call& c) {
       a.ll_stride = g.ll_stride;
       a.n = (int64_t)c.n;
       a.nwords = ((int64_t)c.n * e + 3) / 4;
-      a.tile_words = kBlock;
+      // At least 16 tiles while a tile keeps 16 words, and consumers take
+      // the tile 8 ahead: under the round-robin dispatch of workgroups to
+      // the 8 XCDs the packets of a tile are then read on the XCD that wrote
+      // them (with one tile per workgroup, or a workgroup count that is a
+      // multiple of 8)
+      int64_t tw = kBlock;
+      while (tw > 16 && (a.nwords + tw - 1) / tw < 16) tw /= 2;
+      a.tile_words = tw;
       a.ntiles = (a.nwords + a.tile_words - 1) / a.tile_words;
       a.spin_limit = g.spin_limit;
       a.err = g.err;
       a.p = p;
       a.epoch = epoch;
       a.wait_epoch = epoch + g.wait_skew;
-      a.shift = a.ntiles > 1 ? 1 : 0;
+      a.shift = a.ntiles >= 16 ? 8 : (a.ntiles > 1 ? 1 : 0);
       a.inv_p = inv_p_of(p);
       int& occ = g.ll_occ[c.dtype][c.op];
       if (occ == 0) occ = ll_blocks_per_cu(c.dtype, c.op);

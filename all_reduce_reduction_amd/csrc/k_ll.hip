@@ -12,7 +12,8 @@
 //   produce: rank q's data word k is stored as the packet
 //            {low 32 bits = data, high 32 bits = epoch} to ll[q][k] with a
 //            64-bit agent-scope atomic store (one instruction; agent scope
-//            makes it visible to the other XCDs' L2s);
+//            makes it visible to the other XCDs' L2s); the p words of an
+//            index are loaded together before their packets are stored;
 //   consume: each workgroup then takes a tile produced by ANOTHER
 //            workgroup (tile t + shift), polls the p packets of every word
 //            with 64-bit agent-scope atomic loads until each carries the
@@ -41,16 +42,20 @@ __global__ void __launch_bounds__(kBlock) k_ll(LLArgs a) {
   const int64_t nwords = a.nwords;
 
   // ---- produce ----------------------------------------------------------------
+  // The p words of one index are loaded together, then packed and stored:
+  // one load round trip per word index, not one per rank.
   for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
     const int64_t kend = min(nwords, (t + 1) * a.tile_words);
     for (int64_t k = t * a.tile_words + threadIdx.x; k < kend; k += kBlock) {
-      for (int q = 0; q < p; q++) {
-        uint32_t w;
-        if (EPW == 1 || (k + 1) * EPW <= a.n) w = ((const uint32_t*)a.x[q])[k];
-        else w = ((const uint16_t*)a.x[q])[k * EPW];  // odd 16-bit tail: lone element
-        __hip_atomic_store(a.ll + q * a.ll_stride + k, flag | w, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
+      const bool whole = (EPW == 1 || (k + 1) * EPW <= a.n);  // else the odd 16-bit tail: a lone element
+      uint32_t w[SIM_MAX_RANKS];
+#pragma unroll
+      for (int q = 0; q < SIM_MAX_RANKS; q++)
+        if (q < p) w[q] = whole ? ((const uint32_t*)a.x[q])[k] : ((const uint16_t*)a.x[q])[k * EPW];
+#pragma unroll
+      for (int q = 0; q < SIM_MAX_RANKS; q++)
+        if (q < p)
+          __hip_atomic_store(a.ll + q * a.ll_stride + k, flag | w[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
