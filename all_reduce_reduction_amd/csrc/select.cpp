@@ -34,14 +34,14 @@ Model default_model() {
   Model m;
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0};
   m.a[SIM_ALGO_RING] = {2.7, 5800.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ALLPAIRS] = {2.8, 5700.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT] = {3.0, 5750.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT_LL] = {7.9, 6700.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING_FIFO] = {14.1, 6400.0, -1.0, -1.0};
-  m.a[SIM_ALGO_TREE] = {4.1, 6000.0, -1.0, -1.0};
-  m.a[SIM_ALGO_REXCH] = {3.9, 5250.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER] = {4.0, 5950.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER_LARGE] = {4.4, 5900.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ALLPAIRS] = {2.9, 5700.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT] = {3.0, 5700.0, -1.0, -1.0};
+  m.a[SIM_ALGO_ONESHOT_LL] = {8.6, 13500.0, -1.0, -1.0};
+  m.a[SIM_ALGO_RING_FIFO] = {14.2, 6350.0, -1.0, -1.0};
+  m.a[SIM_ALGO_TREE] = {4.4, 6050.0, -1.0, -1.0};
+  m.a[SIM_ALGO_REXCH] = {4.2, 5250.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER] = {4.2, 5950.0, -1.0, -1.0};
+  m.a[SIM_ALGO_HIER_LARGE] = {4.5, 5900.0, -1.0, -1.0};
   m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {6.6, 6600.0, -1.0, -1.0};
   return m;
 }
