@@ -73,7 +73,9 @@ def _load() -> ctypes.CDLL:
         "sim_model_predict": ([i, i, i, d, ctypes.POINTER(d)], i),
         "sim_model_set": ([i, d, d, d, d], i),
         "sim_model_reset": ([], i),
+        "sim_model_set_workgroup_rate": ([i, d], i),
         "sim_check_error": ([vp], i),
+        "sim_copy_streams": ([pp, pp, i, sz, i, vp], i),
         "sim_config_set": ([i, i], i),
         "sim_config_get": ([i, ctypes.POINTER(i)], i),
         "sim_tree_info": ([i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)], i),
@@ -84,6 +86,7 @@ def _load() -> ctypes.CDLL:
         "sim_verify_custom": ([i, i, i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.c_char_p, sz], i),
         "sim_debug_set": ([i, ctypes.c_uint64], i),
         "sim_debug_get": ([i, ctypes.POINTER(ctypes.c_uint64)], i),
+        "sim_debug_set_epoch": ([ctypes.c_uint32], i),
         "sim_status_string": ([i], ctypes.c_char_p),
         "sim_version": ([], i),
     }
@@ -198,6 +201,11 @@ def sim_model_set(algo, alpha_us: float, steps: float, bytes_factor: float, gbps
     _check(lib.sim_model_set(_code(ALGOS, algo, "algo"), alpha_us, steps, bytes_factor, gbps), "sim_model_set")
 
 
+def sim_model_set_workgroup_rate(algo, gbps_per_workgroup: float) -> None:
+    _check(lib.sim_model_set_workgroup_rate(_code(ALGOS, algo, "algo"), float(gbps_per_workgroup)),
+           "sim_model_set_workgroup_rate")
+
+
 def sim_model_reset() -> None:
     _check(lib.sim_model_reset(), "sim_model_reset")
 
@@ -205,6 +213,11 @@ def sim_model_reset() -> None:
 def sim_check_error(stream=0) -> int:
     """Returns the status (SIM_OK or SIM_ERR_TIMEOUT) without raising."""
     return lib.sim_check_error(stream or None)
+
+
+def sim_copy_streams(src_ptrs, dst_ptrs, k: int, nbytes: int, workgroups: int = 0, stream=0) -> int:
+    return lib.sim_copy_streams(_ptr_array(src_ptrs), _ptr_array(dst_ptrs), k, nbytes, workgroups,
+                                stream or None)
 
 
 def sim_config_set(key, value: int) -> None:
@@ -281,6 +294,10 @@ def sim_debug_get(key) -> int:
     v = ctypes.c_uint64(0)
     _check(lib.sim_debug_get(_code(DEBUG, key, "debug key"), ctypes.byref(v)), "sim_debug_get")
     return v.value
+
+
+def sim_debug_set_epoch(epoch: int) -> None:
+    _check(lib.sim_debug_set_epoch(int(epoch) & 0xFFFFFFFF), "sim_debug_set_epoch")
 
 
 def sim_status_string(status: int) -> str:

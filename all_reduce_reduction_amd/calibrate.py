@@ -17,6 +17,24 @@ per lane) per size for the bulk schedules.  --check then times every legal sched
 selector's pick with the measured fastest: a strict match, and a tolerant
 match when the pick is within max(3%, the measured spread) of the best.
 
+Workgroup budgets (T-CCL's restricted mode, "T-CCL ...", sections III-C3
+and IV-B): sweep_budget() times each schedule at a bandwidth-bound size
+under budgets of 16 .. 128 workgroups and fits the rate one workgroup
+sustains (wg_gbps), which the model uses under a budget (see sim_select in
+include/simar.h).  The check runs at budgets none, 128 and 32.  Besides the
+argmin it reports, per case, every schedule's predicted and measured time,
+the relative error of each prediction, and how many pairs of schedules the
+model ranks in the measured order (pairs measured within the tolerance of
+each other count as ties): on one HBM the one-shot is expected to be the
+fastest at every size, so the argmin alone could not tell a working model
+from a constant pick, while the ranking and the errors can.
+
+Buffers: every measurement rotates over up to 8 sets of rank buffers, as
+many as keep the working set of consecutive calls at 512 MiB or more
+(above the 256 MB Infinity Cache) while the sets fit, so sizes from 4 MiB
+per rank up are timed from HBM as calls that touch fresh data would be;
+below that the whole rotation still fits the cache.
+
 Run on the GPU:  python -m all_reduce_reduction_amd.calibrate [--check]
 """
 from __future__ import annotations
@@ -64,33 +82,58 @@ def _timer():
 
 
 class Bench:
-    """Device buffers for p ranks, reused across sizes (largest first)."""
+    """Device buffers for p ranks: set 0 holds the largest size, sets 1..7
+    up to ROT_SET_BYTES per rank; calls rotate over the sets (see the module
+    docstring)."""
 
-    def __init__(self, max_bytes: int):
+    ROT_BYTES = 512 << 20      # working set the rotation aims for
+    ROT_SET_BYTES = 32 << 20   # bytes per rank of the extra sets
+    MAX_SETS = 8
+
+    def __init__(self, max_bytes: int, steps_scale: float = 1.0):
         import torch
         import all_reduce_reduction_amd as sim
         self.sim = sim
         dev = torch.device("cuda:0")
-        self.ins = [torch.randint(-3000, 3000, (max_bytes // 2,), dtype=torch.int16, device=dev) for _ in range(P)]
-        self.outs = [torch.empty_like(self.ins[0]) for _ in range(P)]
-        self.ip = [t.data_ptr() for t in self.ins]
-        self.op = [t.data_ptr() for t in self.outs]
+        self.sets = []
+        for k in range(self.MAX_SETS):
+            cap = max_bytes if k == 0 else min(max_bytes, self.ROT_SET_BYTES)
+            ins = [torch.randint(-3000, 3000, (cap // 2,), dtype=torch.int16, device=dev) for _ in range(P)]
+            outs = [torch.empty_like(ins[0]) for _ in range(P)]
+            self.sets.append((cap, ins, outs))
         self.stream = int(torch.cuda.current_stream().cuda_stream)
         self.time = _timer()
+        self.steps_scale = steps_scale
 
     def legal(self, algo, nbytes):
         return algo != "oneshot_ll" or nbytes <= self.sim.LL_MAX_BYTES_PER_RANK
 
-    def measure(self, algo, dtype, n):
+    def nsets(self, nbytes: int) -> int:
+        want = -(-self.ROT_BYTES // (2 * P * max(nbytes, 1)))
+        fit = sum(1 for cap, _, _ in self.sets if cap >= nbytes)
+        return max(1, min(self.MAX_SETS, want, fit))
+
+    def measure(self, algo, dtype, n, reps=5):
         sim = self.sim
         nbytes = n * sim.ESIZE[dtype]
-        steps = max(5, min(2000, int(2e5 / max(1.0, nbytes / 4e3))))
+        steps = max(5, min(2000, int(2e5 / max(1.0, nbytes / 4e3) * self.steps_scale)))
+        calls = []
+        for cap, ins, outs in self.sets[:self.nsets(nbytes)]:
+            c = sim.prepare_allreduce([t.data_ptr() for t in ins], [t.data_ptr() for t in outs], P, n, dtype,
+                                      "sum", algo, self.stream)
+            st = c()
+            if st:
+                raise sim.SimError(st, f"sim_allreduce({algo})")
+            calls.append(c)
+        if len(calls) == 1:
+            fn = calls[0]
+        else:
+            it = [0]
 
-        call = sim.prepare_allreduce(self.ip, self.op, P, n, dtype, "sum", algo, self.stream)
-        st = call()
-        if st:
-            raise sim.SimError(st, f"sim_allreduce({algo})")
-        us, spread = self.time(call, steps, max(2, steps // 10))
+            def fn():
+                calls[it[0]]()
+                it[0] = (it[0] + 1) % len(calls)
+        us, spread = self.time(fn, steps, max(2, steps // 10), reps)
         if sim.sim_check_error(self.stream) != 0:
             raise RuntimeError("device error during calibration")
         return us, spread
@@ -166,6 +209,53 @@ def sweep_workgroups(sim, b, sizes):
     return table, raw
 
 
+# Workgroup budgets of the sweep and the size it runs at (bandwidth-bound:
+# the bytes term is > 90% of every schedule's time there); LL only up to its
+# buffer, at its largest grid size.
+BUDGETS = (16, 32, 64, 128)
+BUDGET_BYTES = 48 << 20
+BUDGET_BYTES_LL = 768 << 10
+
+
+def fit_wg_rate(points, gbps):
+    """Per-workgroup rate b from [(W, B_obs)]: each point where the budget
+    binds (B_obs < 0.97 B) gives W b = (B_obs^-3 - B^-3)^(-1/3), the
+    inverse of the model's smooth minimum; b is their median over W.  0
+    when no budget bound (the algo then keeps B under every budget)."""
+    est = []
+    for w, bo in points:
+        if 0 < bo < 0.97 * gbps:
+            est.append((bo ** -3 - gbps ** -3) ** (-1.0 / 3.0) / w)
+    return float(statistics.median(est)) if est else 0.0
+
+
+def sweep_budget(sim, b, fits):
+    rates, raw = {}, {}
+    for algo in ALGOS:
+        nbytes = BUDGET_BYTES_LL if algo == "oneshot_ll" else BUDGET_BYTES
+        n = nbytes // 2
+        alpha, gbps = fits[algo]["alpha_us"], fits[algo]["gbps"]
+        sim.sim_model_set(algo, 1.0, -1, -1, 1e300)
+        launches = sim.sim_model_predict(algo, P, "bf16", nbytes)
+        sim.sim_model_set(algo, 0.0, -1, -1, 1.0)
+        traffic = sim.sim_model_predict(algo, P, "bf16", nbytes) * 1e3  # bytes
+        sim.sim_model_reset()
+        pts = []
+        for w in BUDGETS:
+            sim.sim_config_set("max_workgroups", w)
+            us = b.measure(algo, "bf16", n)[0]
+            # persistent schedules keep at least one workgroup per rank
+            weff = max(w, P) if algo in ("ring_fifo", "allpairs_persistent") else w
+            left = max(us - alpha * launches, 1e-3)
+            pts.append((weff, traffic / left / 1e3))
+            raw.setdefault(algo, []).append({"budget": w, "bytes_per_rank": nbytes, "us": round(us, 3),
+                                             "gbps_observed": round(traffic / left / 1e3, 1)})
+            print(f"budget {algo:20s} {w:4d} workgroups {us:10.2f} us", flush=True)
+        sim.sim_config_set("max_workgroups", 0)
+        rates[algo] = fit_wg_rate(pts, gbps)
+    return rates, raw
+
+
 def calibrate(out_path: str):
     import all_reduce_reduction_amd as sim
     sim.sim_init(0, P, 0)
@@ -202,12 +292,18 @@ def calibrate(out_path: str):
         raw.setdefault("fit", {})[algo] = {"alpha_us": alpha, "gbps": gbps}
     set_topology(sim, "ring")
     sim.sim_model_reset()
+    rates, budget_raw = sweep_budget(sim, b, raw["fit"])
+    for algo, r in rates.items():
+        raw["fit"][algo]["wg_gbps"] = r
     wg_table, wg_raw = sweep_workgroups(sim, b, sizes)
     model = {"device": "MI355X (gfx950)", "p": P, "dtype": "bf16",
              "grid": "1.5 x 2^k bytes per rank, k = 10..27",
              "topology": {a: {"ranks_per_node": g, "radix": k} for a, (g, k) in TOPOLOGY.items()},
              "algos": raw["fit"], "workgroups": wg_table,
              "measurements": {a: raw[a] for a in ALGOS + tuple(TOPOLOGY) if a in raw},
+             "budget_measurements": budget_raw,
+             "rotation": f"up to {Bench.MAX_SETS} buffer sets, >= {Bench.ROT_BYTES >> 20} MiB per rotation "
+                         f"where they fit",
              "workgroup_measurements": wg_raw}
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
@@ -216,37 +312,80 @@ def calibrate(out_path: str):
     return out_path
 
 
-def check(model_path: str):
+CHECK_BUDGETS = (0, 128, 32)
+
+
+def _pairs_agree(pred, meas, tol):
+    """(agreeing pairs, pairs): a pair of schedules agrees when the model
+    orders it as measured, or when the two measured times are within `tol`
+    of each other (a tie either way)."""
+    names = sorted(meas)
+    agree = total = 0
+    for i, a in enumerate(names):
+        for c in names[i + 1:]:
+            total += 1
+            if abs(meas[a] - meas[c]) <= tol * min(meas[a], meas[c]):
+                agree += 1
+            elif (pred[a] < pred[c]) == (meas[a] < meas[c]):
+                agree += 1
+    return agree, total
+
+
+def check(model_path: str, steps_scale: float = 1.0, budgets=CHECK_BUDGETS, reps: int = 5):
+    """The selector against measurement at the evaluation sizes, under each
+    workgroup budget; returns the report (see the module docstring)."""
     import all_reduce_reduction_amd as sim
     sim.sim_init(0, P, 0)
     sim.sim_model_load(model_path)
     cases = [("bf16", 8192 * t) for t in (1, 16, 256, 4096)] + [("fp16", (1 << k) // 2) for k in range(10, 21)]
-    b = Bench(64 << 20)
-    rows = []
-    strict = tolerant = 0
-    for dtype, n in cases:
-        nbytes = n * sim.ESIZE[dtype]
-        meas = {}
-        spreads = {}
-        for algo in ALGOS:
-            if b.legal(algo, nbytes):
-                meas[algo], spreads[algo] = b.measure(algo, dtype, n)
-        pick, pred = sim.sim_select(P, n, dtype)
-        best = min(meas, key=meas.get)
-        tol = max(0.03, spreads[best], spreads[pick])
-        s_ok = pick == best
-        t_ok = meas[pick] <= meas[best] * (1 + tol)
-        strict += s_ok
-        tolerant += t_ok
-        rows.append({"dtype": dtype, "bytes_per_rank": nbytes, "pick": pick, "predicted_us": round(pred, 2),
-                     "measured_best": best, "measured_us": {a: round(v, 2) for a, v in meas.items()},
-                     "strict": s_ok, "tolerant": t_ok})
-        print(f"check {dtype} {nbytes:>9d} B/rank pick {pick:10s} best {best:10s} "
-              + " ".join(f"{a}={v:.1f}" for a, v in meas.items()), flush=True)
-    report = {"model": os.path.basename(model_path), "cases": len(cases), "strict_matches": strict, "tolerant_matches": tolerant,
-              "rows": rows}
-    print(json.dumps({"selector_check": {k: report[k] for k in ("cases", "strict_matches", "tolerant_matches")}}),
-          flush=True)
+    b = Bench(64 << 20, steps_scale)
+    by_budget = {}
+    for budget in budgets:
+        sim.sim_config_set("max_workgroups", budget)
+        rows = []
+        strict = tolerant = agree = pairs = 0
+        errs = []
+        for dtype, n in cases:
+            nbytes = n * sim.ESIZE[dtype]
+            meas, spreads, pred = {}, {}, {}
+            for algo in ALGOS:
+                if b.legal(algo, nbytes):
+                    meas[algo], spreads[algo] = b.measure(algo, dtype, n, reps)
+                    pred[algo] = sim.sim_model_predict(algo, P, dtype, nbytes)
+            pick, pick_us = sim.sim_select(P, n, dtype)
+            best = min(meas, key=meas.get)
+            tol = max(0.03, spreads[best], spreads[pick])
+            s_ok = pick == best
+            t_ok = meas[pick] <= meas[best] * (1 + tol)
+            ag, pt = _pairs_agree(pred, meas, max(0.03, max(spreads.values())))
+            strict += s_ok
+            tolerant += t_ok
+            agree += ag
+            pairs += pt
+            err = {a: round((pred[a] - meas[a]) / meas[a], 4) for a in meas}
+            errs.append(abs(err[pick]))
+            rows.append({"dtype": dtype, "bytes_per_rank": nbytes, "pick": pick, "predicted_us": round(pick_us, 2),
+                         "measured_best": best, "measured_us": {a: round(v, 2) for a, v in meas.items()},
+                         "predicted_us_all": {a: round(v, 2) for a, v in pred.items()},
+                         "rel_error": err, "strict": s_ok, "tolerant": t_ok,
+                         "pairs_agree": ag, "pairs": pt})
+            print(f"check budget {budget or 'none':>4} {dtype} {nbytes:>9d} B/rank pick {pick:10s} "
+                  f"best {best:10s} err(pick) {err[pick]:+.3f} pairs {ag}/{pt} "
+                  + " ".join(f"{a}={v:.1f}" for a, v in meas.items()), flush=True)
+        by_budget["none" if budget == 0 else str(budget)] = {
+            "cases": len(cases), "strict_matches": strict, "tolerant_matches": tolerant,
+            "pairs_agree": agree, "pairs": pairs,
+            "pick_rel_error_median": round(float(statistics.median(errs)), 4),
+            "pick_rel_error_max": round(max(errs), 4), "rows": rows}
+    sim.sim_config_set("max_workgroups", 0)
+    report = {"model": os.path.basename(model_path), "cases": len(cases),
+              "strict_matches": by_budget["none"]["strict_matches"] if "none" in by_budget else None,
+              "tolerant_matches": by_budget["none"]["tolerant_matches"] if "none" in by_budget else None,
+              "budgets": by_budget}
+    print(json.dumps({"selector_check": {k: {kk: v[kk] for kk in ("cases", "strict_matches", "tolerant_matches",
+                                                                    "pairs_agree", "pairs", "pick_rel_error_median",
+                                                                    "pick_rel_error_max")}
+                                         for k, v in by_budget.items()}}), flush=True)
     return report
 
 

@@ -356,13 +356,13 @@ int run_fold(const Call& c, bool all_out, const int64_t* lo, const int64_t* out_
   return hip_err(launch_fold(c.dtype, c.op, c.p, all_out, a, unroll, c.s));
 }
 
-int run_copy_step(const Call& c, const std::vector<CopyXfer>& xs) {
+int run_copy_step(const Call& c, const CopyXfer* xs, int count) {
   CopyArgs a;
   std::memset(&a, 0, sizeof a);
   const int e = esize_of(c.dtype), V = 16 / e;
   int64_t maxlen = 0;
-  a.nx = (int)xs.size();
-  for (size_t k = 0; k < xs.size(); k++) {
+  a.nx = count;
+  for (int k = 0; k < count; k++) {
     a.x[k] = xs[k];
     a.x[k].vec_ok = (xs[k].src_shift % V == 0) && (xs[k].dst_shift % V == 0);
     maxlen = std::max(maxlen, xs[k].hi - xs[k].lo);
@@ -774,9 +774,8 @@ int run_sched(const Call& c, const Schedule& sch) {
       if (rc) return rc;
     }
     for (size_t b = 0; b < copies.size(); b += SIM_MAX_RANKS) {
-      std::vector<CopyXfer> part_of(copies.begin() + b,
-                                    copies.begin() + std::min(copies.size(), b + SIM_MAX_RANKS));
-      int rc = run_copy_step(c, part_of);
+      const int count = (int)std::min<size_t>(copies.size() - b, SIM_MAX_RANKS);
+      int rc = run_copy_step(c, copies.data() + b, count);
       if (rc) return rc;
     }
     for (auto& m : moves) loc[(size_t)m.first] = m.second;
@@ -812,35 +811,35 @@ int run_allreduce(const Call& c) {
         f.tiles = tiles_for(c, (maxchunk + V - 1) / V, p, unroll);
         return hip_err(launch_fanout_tab(esize_of(c.dtype), f, unroll, c.s));
       }
-      std::vector<CopyXfer> xs;                  // step 2: FANOUT from each owner
+      CopyXfer xs[SIM_MAX_RANKS];                // step 2: FANOUT from each owner (p transfers)
+      int nx = 0;
       for (const Xfer& xf : sch->steps[1]) {
-        CopyXfer x;
+        CopyXfer& x = xs[nx++];
         std::memset(&x, 0, sizeof x);
         x.src = c.y[xf.src];
         for (int r = 0; r < p; r++)
           if (r != xf.src) x.dst[x.ndst++] = c.y[r];
         x.lo = lo[xf.chunk];
         x.hi = lo[xf.chunk + 1];
-        xs.push_back(x);
       }
-      return run_copy_step(c, xs);
+      return run_copy_step(c, xs, nx);
     }
     case SIM_ALGO_RING: {
       if (const PtrSet* set = ptr_set_for(c)) return run_ring_tab(c, set, lo);
       int rc = run_ring_rs(c, *sch, p - 1, false, lo);
       if (rc) return rc;
       for (int st = p - 1; st < 2 * (p - 1); st++) {
-        std::vector<CopyXfer> xs;
+        CopyXfer xs[SIM_MAX_RANKS];  // p transfers per step
+        int nx = 0;
         for (const Xfer& xf : sch->steps[st]) {
-          CopyXfer x;
+          CopyXfer& x = xs[nx++];
           std::memset(&x, 0, sizeof x);
           x.src = c.y[xf.src];
           x.dst[x.ndst++] = c.y[xf.dst];
           x.lo = lo[xf.chunk];
           x.hi = lo[xf.chunk + 1];
-          xs.push_back(x);
         }
-        rc = run_copy_step(c, xs);
+        rc = run_copy_step(c, xs, nx);
         if (rc) return rc;
       }
       return SIM_OK;
@@ -955,7 +954,7 @@ int run_all_gather(const Call& c) {
       }
     }
     xs.erase(std::remove_if(xs.begin(), xs.end(), [](const CopyXfer& x) { return x.ndst == 0; }), xs.end());
-    int rc = run_copy_step(c, xs);
+    int rc = run_copy_step(c, xs.data(), (int)xs.size());
     if (rc) return rc;
   }
   return SIM_OK;
@@ -986,7 +985,7 @@ int pick(int coll, int p, size_t n, int dtype, int* algo, double* us) {
                                     SIM_ALGO_ONESHOT_LL, SIM_ALGO_RING_FIFO, SIM_ALGO_ALLPAIRS_PERSISTENT};
   for (int a : kCandidates) {
     if (!legal(coll, a, p, n, dtype)) continue;
-    const double t = model_predict(g.model, coll, a, p, (double)n, esize_of(dtype), g_topo);
+    const double t = model_predict(g.model, coll, a, p, (double)n, esize_of(dtype), g_topo, g_max_wg);
     if (best < 0 || t < bt) {
       best = a;
       bt = t;
@@ -1003,7 +1002,7 @@ int resolve_algo(int coll, int p, size_t n, int dtype, int* algo, double* us) {
   if (*algo == SIM_ALGO_AUTO && coll == COLL_ALLREDUCE && g.env_algo > 0) *algo = g.env_algo;
   if (*algo == SIM_ALGO_AUTO) return pick(coll, p, n, dtype, algo, us);
   if (!legal(coll, *algo, p, n, dtype)) return SIM_ERR_UNSUPPORTED;
-  if (us) *us = model_predict(g.model, coll, *algo, p, (double)n, esize_of(dtype), g_topo);
+  if (us) *us = model_predict(g.model, coll, *algo, p, (double)n, esize_of(dtype), g_topo, g_max_wg);
   return SIM_OK;
 }
 
@@ -1222,7 +1221,7 @@ int sim_reduce_scatter(const void* const* in_ptrs, void* const* out_ptrs, int p,
   rc = run_reduce_scatter(c);
   if (rc) return rc;
   g.last_algo = algo;
-  log_call("ReduceScatter", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e, g_topo));
+  log_call("ReduceScatter", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e, g_topo, g_max_wg));
   return SIM_OK;
 }
 
@@ -1271,7 +1270,7 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p, siz
   rc = run_all_gather(c);
   if (rc) return rc;
   g.last_algo = algo;
-  log_call("AllGather", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e, g_topo));
+  log_call("AllGather", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e, g_topo, g_max_wg));
   return SIM_OK;
 }
 
@@ -1308,7 +1307,7 @@ int sim_model_predict(int algo, int p, int dtype, double bytes_per_rank, double*
   if (is_topology_algo(algo) && !cached_schedule(COLL_ALLREDUCE, algo, p, g_topo, nullptr))
     return SIM_ERR_UNSUPPORTED;
   const int e = esize_of(dtype);
-  *us_out = model_predict(g.model, COLL_ALLREDUCE, algo, p, bytes_per_rank / e, e, g_topo);
+  *us_out = model_predict(g.model, COLL_ALLREDUCE, algo, p, bytes_per_rank / e, e, g_topo, g_max_wg);
   return SIM_OK;
 }
 
@@ -1321,6 +1320,13 @@ int sim_model_set(int algo, double alpha_us, double steps, double bytes_factor, 
   m.steps = steps;
   m.bytes_factor = bytes_factor;
   g.model.source = "sim_model_set";
+  return SIM_OK;
+}
+
+int sim_model_set_workgroup_rate(int algo, double gbps_per_workgroup) {
+  if (algo < SIM_ALGO_RING || algo > kLastAlgo || !(gbps_per_workgroup >= 0)) return SIM_ERR_INVALID_ARG;
+  g.model.a[algo].wg_gbps = gbps_per_workgroup;
+  g.model.source = "sim_model_set_workgroup_rate";
   return SIM_OK;
 }
 
@@ -1340,6 +1346,37 @@ int sim_check_error(void* stream) {
     return word;
   }
   return SIM_OK;
+}
+
+int sim_copy_streams(const void* const* src_ptrs, void* const* dst_ptrs, int k, size_t bytes, int workgroups,
+                     void* stream) {
+  if (!g.init) return SIM_ERR_NOT_INIT;
+  if (k < 1 || k > SIM_MAX_RANKS || workgroups < 0 || (bytes & 15u)) return SIM_ERR_INVALID_ARG;
+  if (!src_ptrs || !dst_ptrs) return SIM_ERR_INVALID_ARG;
+  if (bytes > ((size_t)1 << 46)) return SIM_ERR_INVALID_ARG;
+  Range srcs[SIM_MAX_RANKS], dsts[SIM_MAX_RANKS];
+  for (int q = 0; q < k; q++) {
+    if (!src_ptrs[q] || !dst_ptrs[q]) return SIM_ERR_INVALID_ARG;
+    if (((uintptr_t)src_ptrs[q] | (uintptr_t)dst_ptrs[q]) & 15u) return SIM_ERR_ALIGN;
+    srcs[q] = {(uintptr_t)src_ptrs[q], (uintptr_t)src_ptrs[q] + bytes};
+    dsts[q] = {(uintptr_t)dst_ptrs[q], (uintptr_t)dst_ptrs[q] + bytes};
+  }
+  for (int q = 0; q < k; q++)
+    for (int r = 0; r < k; r++)
+      if (overlap(dsts[q], srcs[r]) || (r != q && overlap(dsts[q], dsts[r]))) return SIM_ERR_ALIAS;
+  if (bytes == 0) return SIM_OK;
+  if (use_device() != SIM_OK) return SIM_ERR_HIP;
+  CopyStreamsArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int q = 0; q < k; q++) {
+    a.src[q] = src_ptrs[q];
+    a.dst[q] = dst_ptrs[q];
+  }
+  a.k = k;
+  a.nvec = (int64_t)(bytes / 16);
+  int64_t wg = workgroups > 0 ? workgroups : (a.nvec + kBlock - 1) / kBlock;
+  wg = std::max<int64_t>(1, std::min<int64_t>(wg, kMaxTiles));
+  return hip_err(launch_copy_streams(a, (int)wg, (hipStream_t)stream));
 }
 
 int sim_config_set(int key, int value) {
@@ -1518,6 +1555,8 @@ int sim_debug_set(int key, uint64_t value) {
   }
   return SIM_ERR_INVALID_ARG;
 }
+
+int sim_debug_set_epoch(uint32_t epoch) { return sim_debug_set(SIM_DEBUG_EPOCH, epoch); }
 
 int sim_debug_get(int key, uint64_t* value) {
   if (!value) return SIM_ERR_INVALID_ARG;

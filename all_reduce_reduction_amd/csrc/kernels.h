@@ -231,7 +231,18 @@ struct SchedArgs {
   float inv_p;
 };
 
+// k independent streaming copies (the ceiling of the one-shot's access
+// pattern): dst[q][0 .. 16 nvec) = src[q][0 .. 16 nvec) for q < k.
+struct CopyStreamsArgs {
+  const void* src[SIM_MAX_RANKS];
+  void* dst[SIM_MAX_RANKS];
+  int64_t nvec;  // 16-byte vectors per stream
+  int k;
+  int pad_;
+};
+
 static_assert(sizeof(FoldArgs) <= 4096, "kernel argument segment too large");
+static_assert(sizeof(CopyStreamsArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(FoldTabArgs) <= 64, "must fit the small-argument launch path");
 static_assert(sizeof(FanoutTabArgs) <= 64, "must fit the small-argument launch path");
 static_assert(sizeof(RingTabArgs) <= 64, "must fit the small-argument launch path");
@@ -256,6 +267,7 @@ hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, c
                               int unroll, hipStream_t s);
 hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s);
 hipError_t launch_ll(int dtype, int op, const LLArgs& a, int grid, hipStream_t s);
+hipError_t launch_copy_streams(const CopyStreamsArgs& a, int workgroups, hipStream_t s);
 hipError_t launch_fill64(unsigned long long* p, unsigned long long v, int64_t n, hipStream_t s);
 // Workgroups of the LL kernel (dtype, op) that fit on one CU at once.
 int ll_blocks_per_cu(int dtype, int op);

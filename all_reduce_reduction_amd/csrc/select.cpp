@@ -27,22 +27,24 @@
 namespace simar {
 
 // Built-in defaults: the fit of the calibration sweep on MI355X (p = 8,
-// bf16, 1.5 KiB .. 192 MiB per rank; the topology schedules at the
-// topologies the calibration file states), rounded.  A calibration file
-// loaded with sim_model_load() or SIM_CALIB replaces them.
+// bf16, 1.5 KiB .. 192 MiB per rank, rotating buffer sets; per-workgroup
+// rates from budgets of 16 .. 128 workgroups at 48 MiB per rank, LL at
+// 768 KiB; the topology schedules at the topologies the calibration file
+// states), rounded.  A calibration file loaded with sim_model_load() or
+// SIM_CALIB replaces them.
 Model default_model() {
   Model m;
-  m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING] = {2.7, 5800.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ALLPAIRS] = {2.9, 5700.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT] = {3.0, 5700.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ONESHOT_LL] = {8.6, 13500.0, -1.0, -1.0};
-  m.a[SIM_ALGO_RING_FIFO] = {14.2, 6350.0, -1.0, -1.0};
-  m.a[SIM_ALGO_TREE] = {4.4, 6050.0, -1.0, -1.0};
-  m.a[SIM_ALGO_REXCH] = {4.2, 5250.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER] = {4.2, 5950.0, -1.0, -1.0};
-  m.a[SIM_ALGO_HIER_LARGE] = {4.5, 5900.0, -1.0, -1.0};
-  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {6.6, 6600.0, -1.0, -1.0};
+  m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0, 0.0};
+  m.a[SIM_ALGO_RING] = {2.7, 5800.0, -1.0, -1.0, 24.0};
+  m.a[SIM_ALGO_ALLPAIRS] = {2.9, 5700.0, -1.0, -1.0, 43.5};
+  m.a[SIM_ALGO_ONESHOT] = {3.1, 5700.0, -1.0, -1.0, 49.0};
+  m.a[SIM_ALGO_ONESHOT_LL] = {8.6, 13800.0, -1.0, -1.0, 8.7};
+  m.a[SIM_ALGO_RING_FIFO] = {14.1, 6350.0, -1.0, -1.0, 15.8};
+  m.a[SIM_ALGO_TREE] = {4.0, 6000.0, -1.0, -1.0, 0.0};
+  m.a[SIM_ALGO_REXCH] = {3.9, 5250.0, -1.0, -1.0, 0.0};
+  m.a[SIM_ALGO_HIER] = {4.1, 5950.0, -1.0, -1.0, 0.0};
+  m.a[SIM_ALGO_HIER_LARGE] = {4.4, 5900.0, -1.0, -1.0, 0.0};
+  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {7.1, 6600.0, -1.0, -1.0, 31.4};
   return m;
 }
 
@@ -168,7 +170,27 @@ int model_workgroups(const Model& m, int algo, double bytes_per_rank) {
   return model_launch(m, algo, bytes_per_rank).total;
 }
 
-double model_predict(const Model& m, int coll, int algo, int p, double n, int esize, const Topology& t) {
+// A workgroup budget (T-CCL's restricted mode, "T-CCL ...", sections III-C3
+// and IV-B: communication confined to a fixed number of thread blocks) caps
+// how many workgroups each launch of a schedule runs.  Few workgroups
+// cannot keep enough memory requests in flight, so the bandwidth term
+// falls: each workgroup sustains about b GB/s, and W of them about W b,
+// until they saturate HBM at B.  A hard min(B, W b) over-predicts at
+// budgets near the knee, where the workgroups already contend; the cube
+// smooth minimum follows the knee (one-shot, p = 8, bf16, 64 MiB per rank
+// on MI355X: 32 workgroups 1.55 TB/s, 128 workgroups 4.5 TB/s, no budget
+// 5.6 TB/s).
+double model_bandwidth(const Model& m, int algo, int p, int budget) {
+  const AlgoModel& am = m.a[algo];
+  if (budget <= 0 || !(am.wg_gbps > 0)) return am.gbps;
+  const bool persistent = algo == SIM_ALGO_RING_FIFO || algo == SIM_ALGO_ALLPAIRS_PERSISTENT;
+  const double w = persistent ? std::max(budget, p) : budget;
+  const double bw = w * am.wg_gbps;
+  return std::pow(std::pow(am.gbps, -3.0) + std::pow(bw, -3.0), -1.0 / 3.0);
+}
+
+double model_predict(const Model& m, int coll, int algo, int p, double n, int esize, const Topology& t,
+                     int budget) {
   if (algo <= 0 || algo >= kNumAlgos) return 1e30;
   const AlgoModel& am = m.a[algo];
   const int launches = model_launches(coll, algo, p, t);
@@ -176,7 +198,7 @@ double model_predict(const Model& m, int coll, int algo, int p, double n, int es
   const double steps = am.steps >= 0 ? am.steps : (double)launches;
   const double bytes = am.bytes_factor >= 0 ? am.bytes_factor * n * esize
                                             : model_traffic(coll, algo, p, n, esize, t);
-  return am.alpha_us * steps + bytes / (am.gbps * 1e3);  // GB/s -> bytes per us
+  return am.alpha_us * steps + bytes / (model_bandwidth(m, algo, p, budget) * 1e3);  // GB/s -> bytes per us
 }
 
 // ---------------------------------------------------------------------------
@@ -365,6 +387,15 @@ bool model_load_json(const char* path, Model* m, std::string* err) {
     out.a[a].gbps = bw->second.num;
     out.a[a].steps = -1;
     out.a[a].bytes_factor = -1;
+    out.a[a].wg_gbps = 0;
+    auto wr = o.obj.find("wg_gbps");  // optional: rate of one workgroup under a budget
+    if (wr != o.obj.end()) {
+      if (wr->second.kind != JVal::NUM || !(wr->second.num >= 0)) {
+        if (err) *err = "wg_gbps must be a number >= 0";
+        return false;
+      }
+      out.a[a].wg_gbps = wr->second.num;
+    }
   }
   // optional launch-configuration table: "workgroups": {algo: [[bytes, total], ...]}
   auto wt = root.obj.find("workgroups");

@@ -17,6 +17,7 @@ struct AlgoModel {
   double gbps = 4000.0;        // effective rate for the schedule's bytes
   double steps = -1.0;         // override of the launch count law when >= 0
   double bytes_factor = -1.0;  // override of the traffic law (bytes per message byte) when >= 0
+  double wg_gbps = 0.0;        // rate one workgroup sustains, for calls under a workgroup budget (0: no term)
 };
 
 // One measured launch configuration.
@@ -64,9 +65,18 @@ double model_traffic(int coll, int algo, int p, double n, int esize, const Topol
 // reads once and writes each receiver.
 double schedule_traffic(const Schedule& s, double n, int esize);
 
-// T = alpha * launches + traffic / B, in microseconds.
+// The bandwidth a call of `algo` can use under a workgroup budget of
+// `budget` workgroups per launch (0: none): B itself without a budget or
+// without a per-workgroup rate, else the smooth minimum
+//   (B^-3 + (W b)^-3)^(-1/3)
+// of B and the budget's aggregate rate W b, W being the budget (at least one
+// workgroup per rank for the single-launch schedules, which keep that many).
+double model_bandwidth(const Model& m, int algo, int p, int budget);
+
+// T = alpha * launches + traffic / B_eff, in microseconds, B_eff being
+// model_bandwidth() at `budget`.
 double model_predict(const Model& m, int coll, int algo, int p, double n, int esize,
-                     const Topology& t = Topology());
+                     const Topology& t = Topology(), int budget = 0);
 
 // Parse a calibration file; returns false (and leaves *m alone) on error.
 bool model_load_json(const char* path, Model* m, std::string* err);

@@ -207,7 +207,14 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p,
  * time in microseconds: argmin over legal algos of
  *   T_a = alpha_a * launches_a(p) + traffic_a(p, n, dtype) / B_a
  * (a launch cost plus bytes over bandwidth), traffic_a being the schedule's
- * algorithmic HBM bytes over all simulated ranks. */
+ * algorithmic HBM bytes over all simulated ranks.  Under a workgroup budget
+ * W (SIM_CONFIG_MAX_WORKGROUPS > 0) an algo with a per-workgroup rate b_a
+ * (sim_model_set_workgroup_rate, or "wg_gbps" in the calibration file) is
+ * priced with B_a replaced by (B_a^-3 + (W_a b_a)^-3)^(-1/3), the smooth
+ * minimum of B_a and what W_a workgroups sustain; W_a = W, or max(W, p) for
+ * SIM_ALGO_RING_FIFO and SIM_ALGO_ALLPAIRS_PERSISTENT, which keep one
+ * workgroup per rank ("T-CCL ...", sections III-C3 and IV-B: restricted
+ * mode).  The budget in effect is the current SIM_CONFIG_MAX_WORKGROUPS. */
 int sim_select(int p, size_t n, int dtype, int op, int* algo_out, double* predicted_us);
 
 /* The algo the most recent successful collective actually ran. */
@@ -219,12 +226,21 @@ int sim_last_algo(void);
  * lane)], ...]}, after T-CCL's ranked launch-configuration table, section
  * III-C3): bulk kernels of that algo then launch the measured best total of
  * the nearest size (log scale), never more than covers the transfer, with
- * the entry's 16-byte vectors per lane (1 or 2; 1 when absent).  Errors:
- * SIM_ERR_INVALID_ARG (the current model is kept). */
+ * the entry's 16-byte vectors per lane (1 or 2; 1 when absent).  An algo
+ * entry may carry "wg_gbps", its per-workgroup rate under a budget (see
+ * sim_select; 0 when absent).  Errors: SIM_ERR_INVALID_ARG (the current
+ * model is kept). */
 int sim_model_load(const char* json_path);
 
-/* Predicted time of `algo` for `bytes_per_rank` bytes per rank. */
+/* Predicted time of `algo` for `bytes_per_rank` bytes per rank of `dtype`
+ * (the element size fixes the element count the traffic laws take), under
+ * the current workgroup budget as sim_select prices it. */
 int sim_model_predict(int algo, int p, int dtype, double bytes_per_rank, double* us_out);
+
+/* Set one algo's per-workgroup rate b (GB/s one workgroup sustains; 0
+ * removes the budget term, so a budget leaves that algo's B unchanged).
+ * Errors: SIM_ERR_INVALID_ARG (unknown algo, negative or NaN rate). */
+int sim_model_set_workgroup_rate(int algo, double gbps_per_workgroup);
 
 /* Override one algo's model: alpha_us and gbps always; `steps` (latency
  * units) and `bytes_factor` (bytes moved per byte of message) replace the
@@ -241,6 +257,25 @@ int sim_model_reset(void);
  * SIM_OK, or SIM_ERR_TIMEOUT if a bounded wait expired since the last
  * check (that call's outputs are undefined). */
 int sim_check_error(void* stream);
+
+/* ---- measurement --------------------------------------------------------- */
+
+/* k independent copies in one launch: dst_ptrs[q][0 .. bytes) =
+ * src_ptrs[q][0 .. bytes) for q < k, asynchronously on `stream`.  Each lane
+ * moves 16-byte vectors with the same streaming loads and stores, address
+ * split and grid-stride walk as the one-shot's fold, so k = p measures what
+ * the one-shot's access pattern (p input and p output streams, "MSCCL++
+ * ...", section "The Collective Algorithm Library", 1PA) can reach on this
+ * GPU without its arithmetic, and k = 1 a plain copy: the same-GPU ceiling
+ * the one-shot's HBM bandwidth is read against.  `workgroups` is the grid
+ * size (0: one workgroup per 256 vectors of a stream, at most 2^20).
+ * Pointers are caller-owned device memory, 16-byte aligned; no destination
+ * may overlap a source or another destination.  Errors: SIM_ERR_NOT_INIT,
+ * SIM_ERR_INVALID_ARG (k outside 1..SIM_MAX_RANKS, a NULL pointer, bytes
+ * not a multiple of 16, workgroups < 0), SIM_ERR_ALIGN, SIM_ERR_ALIAS,
+ * SIM_ERR_HIP; nothing is enqueued on an error.  bytes == 0 is a no-op. */
+int sim_copy_streams(const void* const* src_ptrs, void* const* dst_ptrs, int k, size_t bytes, int workgroups,
+                     void* stream);
 
 /* ---- topology (host only; no device needed) ------------------------- */
 
@@ -342,6 +377,10 @@ enum {
 };
 int sim_debug_set(int key, uint64_t value);
 int sim_debug_get(int key, uint64_t* value);
+/* The LL epoch hook under its own name: sim_debug_set(SIM_DEBUG_EPOCH,
+ * epoch) -- the next LL call uses epoch + 1, so a value near 2^32 forces the
+ * wrap (the packet buffer is cleared and the epoch restarts at 1). */
+int sim_debug_set_epoch(uint32_t epoch);
 
 const char* sim_status_string(int status);
 int sim_version(void);

@@ -1,9 +1,10 @@
 """Alpha-beta cost model, written out -- TEST INFRASTRUCTURE ONLY.
 
 "MSCCL, in depth ...", section "Why generic collectives leave time on the
-table": each synchronised step costs a fixed latency alpha and each byte
-costs 1/B; a ring all-reduce over p ranks takes 2(p-1) steps, the all-pairs
-schedule 2, and both send 2(p-1)/p of the buffer:
+table", prices a schedule as a per-step latency alpha times its number of
+synchronised steps, plus the bytes it moves over the bandwidth B.  Over p
+ranks the ring all-reduce has 2(p-1) steps and the all-pairs schedule 2,
+and each moves 2(p-1)/p of the buffer:
 
     T_ring(n)     = 2(p-1) alpha + 2(p-1)/p * n / B
     T_allpairs(n) = 2      alpha + 2(p-1)/p * n / B

@@ -42,6 +42,7 @@ def test_status_strings_and_not_initialised():
     assert st == -9
     assert sim.prepare_allreduce([0, 0], [0, 0], 2, 4, "int32", "sum", "oneshot")() == -9
     assert sim.sim_check_error() == -9
+    assert sim.sim_copy_streams([0], [0], 1, 16) == -9
 
 
 def test_binding_has_same_names_as_header():
@@ -89,3 +90,15 @@ def test_binding_enums_match_the_header():
     debug_in_header = {k for k in enum if k.startswith("SIM_DEBUG_")}
     assert debug_in_header == {"SIM_DEBUG_" + k.upper() for k in sim.DEBUG}
     assert sim.MAX_RANKS == int(re.search(r"#define SIM_MAX_RANKS (\d+)", text).group(1))
+
+
+def test_epoch_hook_under_its_own_name():
+    import all_reduce_reduction_amd as sim
+    old = sim.sim_debug_get("epoch")
+    try:
+        sim.sim_debug_set_epoch(0xFFFFFFFD)
+        assert sim.sim_debug_get("epoch") == 0xFFFFFFFD
+        sim.sim_debug_set_epoch(7)
+        assert sim.sim_debug_get("epoch") == 7
+    finally:
+        sim.sim_debug_set("epoch", old)

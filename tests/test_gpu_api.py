@@ -124,7 +124,7 @@ def test_ll_epoch_wraparound(lib, orc):
     from tests.gpu_util import run_allreduce
     sim = lib
     xs, want = _ll_case(orc, seed=1)
-    sim.sim_debug_set("epoch", 0xFFFFFFFD)
+    sim.sim_debug_set_epoch(0xFFFFFFFD)  # the named hook (same as sim_debug_set("epoch", ...))
     seen = []
     for _ in range(4):
         got = run_allreduce(xs, "fp16", "sum", "oneshot_ll")

@@ -291,18 +291,27 @@ def test_verifier_agrees_with_independent_model(case):
 
 
 # ---------------------------------------------------------------------------
-@settings(max_examples=100, deadline=None)
-@given(st.integers(2, 16), st.integers(1, 1 << 28), st.sampled_from(["int32", "fp32", "fp16", "bf16"]))
-def test_selector_picks_its_own_argmin(p, nbytes, dtype):
+@settings(max_examples=150, deadline=None)
+@given(st.integers(2, 16), st.integers(1, 1 << 28), st.sampled_from(["int32", "fp32", "fp16", "bf16"]),
+       st.sampled_from([0, 1, 8, 32, 128, 1024]))
+def test_selector_picks_its_own_argmin(p, nbytes, dtype, budget):
+    """The pick is the argmin of the per-algo predictions, under any budget
+    (with the packaged calibration's per-workgroup rates)."""
     esize = sim.ESIZE[dtype]
     n = max(1, nbytes // esize)
-    pick, pred = sim.sim_select(p, n, dtype)
-    best = None
-    for a in SINGLE:
-        if a == "oneshot_ll" and n * esize > sim.LL_MAX_BYTES_PER_RANK:
-            continue
-        t = sim.sim_model_predict(a, p, dtype, n * esize)
-        if best is None or t < best[1]:
-            best = (a, t)
-    assert pred == pytest.approx(best[1])
-    assert sim.sim_model_predict(pick, p, dtype, n * esize) == pytest.approx(best[1])
+    sim.sim_model_load(sim.CALIBRATION)
+    sim.sim_config_set("max_workgroups", budget)
+    try:
+        pick, pred = sim.sim_select(p, n, dtype)
+        best = None
+        for a in SINGLE:
+            if a == "oneshot_ll" and n * esize > sim.LL_MAX_BYTES_PER_RANK:
+                continue
+            t = sim.sim_model_predict(a, p, dtype, n * esize)
+            if best is None or t < best[1]:
+                best = (a, t)
+        assert pred == pytest.approx(best[1])
+        assert sim.sim_model_predict(pick, p, dtype, n * esize) == pytest.approx(best[1])
+    finally:
+        sim.sim_config_set("max_workgroups", 0)
+        sim.sim_model_reset()

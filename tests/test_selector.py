@@ -120,6 +120,21 @@ def test_packaged_calibration_loads_and_picks_oneshot():
             assert sim.sim_select(8, n, dtype)[0] == "oneshot"
         rep = json.load(open(os.path.join(os.path.dirname(sim.CALIBRATION), "selector_check_mi355x.json")))
         assert rep["strict_matches"] == rep["cases"]
+        # the committed check, under every workgroup budget it ran: the pick
+        # is the measured fastest, and the model orders at least 90% of the
+        # pairs of schedules as measured
+        assert set(rep["budgets"]) == {"none", "128", "32"}
+        for b in rep["budgets"].values():
+            assert b["strict_matches"] == b["cases"] == len(b["rows"])
+            assert b["pairs_agree"] >= 0.9 * b["pairs"]
+        # the fitted per-workgroup rates are there, and a budget slows the one-shot's prediction
+        model = json.load(open(sim.CALIBRATION))
+        assert model["algos"]["oneshot"]["wg_gbps"] > 0
+        t0 = sim.sim_model_predict("oneshot", 8, "bf16", 64 << 20)
+        sim.sim_config_set("max_workgroups", 32)
+        t32 = sim.sim_model_predict("oneshot", 8, "bf16", 64 << 20)
+        sim.sim_config_set("max_workgroups", 0)
+        assert t32 > 2 * t0
     finally:
         sim.sim_model_reset()
 
@@ -169,3 +184,75 @@ def test_workgroup_budget_config():
         assert sim.sim_config_get("max_workgroups") == 64
     finally:
         sim.sim_config_set("max_workgroups", 0)
+
+
+def _smooth_min(b, w, rate):
+    # written out independently of the library: 1 / B_eff^3 = 1 / B^3 + 1 / (W b)^3
+    return 1.0 / ((1.0 / b ** 3 + 1.0 / (w * rate) ** 3) ** (1.0 / 3.0))
+
+
+def test_budget_term_prices_and_flips_the_argmin():
+    """Under a workgroup budget an algo with a per-workgroup rate is priced
+    with the smooth minimum of B and W b; without one (or with rate 0) the
+    budget changes nothing.  A schedule that needs fewer bytes but sustains
+    little per workgroup loses to one that streams faster per workgroup once
+    the budget is tight."""
+    sim.sim_model_reset()
+    S = 64 << 20
+    try:
+        for other in ("ring", "oneshot_ll", "ring_fifo", "allpairs_persistent"):
+            sim.sim_model_set(other, 1e9, -1, -1, 1.0)
+        sim.sim_model_set("oneshot", 3.0, -1, -1, 6000.0)
+        sim.sim_model_set("allpairs", 3.0, -1, -1, 5000.0)
+        sim.sim_model_set_workgroup_rate("oneshot", 40.0)
+        sim.sim_model_set_workgroup_rate("allpairs", 120.0)
+        assert sim.sim_select(8, S // 2, "bf16")[0] == "oneshot"
+        assert sim.sim_model_predict("oneshot", 8, "bf16", S) == pytest.approx(3.0 + 16 * S / 6000e3)
+        sim.sim_config_set("max_workgroups", 32)
+        t1 = sim.sim_model_predict("oneshot", 8, "bf16", S)
+        t2 = sim.sim_model_predict("allpairs", 8, "bf16", S)
+        assert t1 == pytest.approx(3.0 + 16 * S / (_smooth_min(6000.0, 32, 40.0) * 1e3), rel=1e-12)
+        assert t2 == pytest.approx(2 * 3.0 + 17 * S / (_smooth_min(5000.0, 32, 120.0) * 1e3), rel=1e-12)
+        algo, us = sim.sim_select(8, S // 2, "bf16")
+        assert algo == "allpairs" and us == pytest.approx(t2)
+        # a generous budget hardly matters: 4096 workgroups sustain far more than B
+        sim.sim_config_set("max_workgroups", 4096)
+        assert sim.sim_select(8, S // 2, "bf16")[0] == "oneshot"
+        # rate 0 removes the term
+        sim.sim_config_set("max_workgroups", 32)
+        sim.sim_model_set_workgroup_rate("oneshot", 0.0)
+        assert sim.sim_model_predict("oneshot", 8, "bf16", S) == pytest.approx(3.0 + 16 * S / 6000e3)
+        # the single-launch schedules keep one workgroup per rank: W = max(budget, p)
+        sim.sim_model_set("allpairs_persistent", 6.0, -1, -1, 6500.0)
+        sim.sim_model_set_workgroup_rate("allpairs_persistent", 50.0)
+        sim.sim_config_set("max_workgroups", 2)
+        assert sim.sim_model_predict("allpairs_persistent", 8, "bf16", S) == pytest.approx(
+            6.0 + 23 * S / (_smooth_min(6500.0, 8, 50.0) * 1e3), rel=1e-12)
+        with pytest.raises(sim.SimError):
+            sim.sim_model_set_workgroup_rate("oneshot", -1.0)
+        with pytest.raises(sim.SimError):
+            sim.sim_model_set_workgroup_rate("auto", 1.0)
+    finally:
+        sim.sim_config_set("max_workgroups", 0)
+        sim.sim_model_reset()
+
+
+def test_budget_rate_json(tmp_path):
+    f = tmp_path / "m.json"
+    f.write_text(json.dumps({"algos": {"oneshot": {"alpha_us": 3.0, "gbps": 6000.0, "wg_gbps": 40.0}}}))
+    try:
+        sim.sim_model_load(str(f))
+        S = 1 << 26
+        sim.sim_config_set("max_workgroups", 64)
+        assert sim.sim_model_predict("oneshot", 8, "bf16", S) == pytest.approx(
+            3.0 + 16 * S / (_smooth_min(6000.0, 64, 40.0) * 1e3), rel=1e-12)
+        for bad in ('"x"', "-1", "null"):
+            f.write_text('{"algos": {"oneshot": {"alpha_us": 1.0, "gbps": 1.0, "wg_gbps": %s}}}' % bad)
+            with pytest.raises(sim.SimError):
+                sim.sim_model_load(str(f))
+        # the refused files changed nothing
+        assert sim.sim_model_predict("oneshot", 8, "bf16", S) == pytest.approx(
+            3.0 + 16 * S / (_smooth_min(6000.0, 64, 40.0) * 1e3), rel=1e-12)
+    finally:
+        sim.sim_config_set("max_workgroups", 0)
+        sim.sim_model_reset()
