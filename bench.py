@@ -20,6 +20,22 @@ Printed JSON line:
                  plain one-shot vs the LL packet path vs the selector's pick
                  (and, as latency_8KiB_graph_us, calls replayed from a
                  captured HIP graph)
+  ceiling        what the one-shot's access pattern can reach on this GPU in the
+                 same run: the library's k-stream copy (sim_copy_streams) with
+                 8 inputs and 8 outputs of 64 MiB (the one-shot's streams and
+                 bytes, no arithmetic) and with 1 input and 1 output of 1 GiB,
+                 and hipMemcpyAsync device-to-device of 1 GiB (torch's copy_)
+  workload2_fp32_32MiB, workload5_256MiB
+                 the parity workloads' timed figures next to the CPU oracle's
+                 time for the same call (all host threads, and one thread on a
+                 stated sample): busBW, algorithmic HBM GB/s per schedule; the
+                 standalone reduce-scatter and all-gather with their own laws
+  workload4_latency_us
+                 per-call microseconds of the LL packet path vs the plain
+                 one-shot (and the selector's pick) from 1 KiB to 1 MiB per rank
+  selector_check the selector's pick vs the measured fastest schedule at the
+                 evaluation sizes, under workgroup budgets none / 128 / 32, with
+                 per-case model error and pairwise ranking agreement
   cpu_baseline   the CPU oracle on the same host arrays (all host threads)
 """
 from __future__ import annotations
@@ -179,6 +195,258 @@ def large_workload(sim, synthdata, torch, np, dev, stream, steps, warmup) -> flo
     del d5, o5
     torch.cuda.empty_cache()
     return t5 * 1e6
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_cpu(fn, runs: int, warm: int = 0) -> float:
+    """Median seconds of `runs` calls of fn after `warm` untimed ones."""
+    import numpy as np
+    for _ in range(warm):
+        fn()
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def ceiling(sim, torch, dev, stream, steps: int, head_ip, head_op) -> dict:
+    """The same-run bandwidth ceiling of the one-shot's access pattern:
+    k independent streaming copies through the library (best over a few grid
+    sizes) and the runtime's device-to-device copy, all moving random bits as
+    the all-reduce does (and the copies once more with constant data)."""
+    out = {}
+    total = 1 << 30
+
+    def best_copy(k, per, const=False):
+        # random bits, like the all-reduce's inputs (the bus toggles as it does
+        # for real data); `const`: every word the same, for comparison
+        g = torch.Generator(device=dev)
+        g.manual_seed(k)
+        ins = [torch.randint(-2 ** 31, 2 ** 31 - 1, (per // 4,), dtype=torch.int32, device=dev, generator=g)
+               for _ in range(k)]
+        if const:
+            for q, t in enumerate(ins):
+                t.fill_(q + 1)
+        outs = [torch.empty_like(ins[0]) for _ in range(k)]
+        ip, op_ = [t.data_ptr() for t in ins], [t.data_ptr() for t in outs]
+        res = {}
+        for wg in (1024, 2048, 4096, 0):
+            def call(wg=wg):
+                if sim.sim_copy_streams(ip, op_, k, per, wg, stream):
+                    raise sim.SimError(-1, "sim_copy_streams")
+            res[wg] = time_calls(call, steps, 3)
+        torch.cuda.synchronize()
+        assert all(torch.equal(o, i) for i, o in zip(ins, outs)), "copy check failed"
+        wg = min(res, key=res.get)
+        gbs = 2 * k * per / res[wg] / 1e9
+        del ins, outs
+        torch.cuda.empty_cache()
+        return {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBPS, 4),
+                "us": round(res[wg] * 1e6, 2), "workgroups": wg or "cover",
+                "GBps_by_workgroups": {str(w or "cover"): round(2 * k * per / t / 1e9, 1) for w, t in res.items()}}
+    # the headline's own buffers and data: input q copied to output q
+    res = {}
+    for wg in (1024, 2048, 4096, 0):
+        def call(wg=wg):
+            if sim.sim_copy_streams(head_ip, head_op, P, S, wg, stream):
+                raise sim.SimError(-1, "sim_copy_streams")
+        res[wg] = time_calls(call, steps, 3)
+    wg = min(res, key=res.get)
+    gbs = 2 * P * S / res[wg] / 1e9
+    out["copy_headline_buffers"] = {
+        "GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBPS, 4), "us": round(res[wg] * 1e6, 2),
+        "workgroups": wg or "cover", "what": "the 8 headline inputs copied to the 8 headline outputs (64 MiB each)",
+        "GBps_by_workgroups": {str(w or "cover"): round(2 * P * S / t / 1e9, 1) for w, t in res.items()}}
+    out["copy_8in_8out_64MiB_each"] = best_copy(8, S)
+    out["copy_1in_1out_1GiB"] = best_copy(1, total)
+    out["constant_data"] = {"copy_8in_8out_64MiB_each": best_copy(8, S, True),
+                            "copy_1in_1out_1GiB": best_copy(1, total, True)}
+    src = torch.randint(-2 ** 31, 2 ** 31 - 1, (total // 4,), dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    t = time_calls(lambda: dst.copy_(src), steps, 3)
+    gbs = 2 * total / t / 1e9
+    out["hipMemcpyDtoD_1GiB"] = {"GBps": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBPS, 4),
+                                 "us": round(t * 1e6, 2), "via": "torch copy_ (hipMemcpyAsync device to device)"}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+def workload2(sim, synthdata, oracle, torch, np, dev, stream, steps: int, cpu: bool) -> dict:
+    """p = 8, fp32 N(0,1), 32 MiB per rank: ring (14 steps), all-pairs (2),
+    one-shot, and the single-launch forms; the CPU oracle of the same calls."""
+    n2 = 8_388_608
+    s2 = n2 * 4
+    xs = synthdata.workload_inputs(2, P, n2, "fp32")
+    din = [torch.from_numpy(x).to(dev) for x in xs]
+    dout = [torch.empty(n2, dtype=torch.float32, device=dev) for _ in range(P)]
+    ip, op_ = [t.data_ptr() for t in din], [t.data_ptr() for t in dout]
+    laws = {"oneshot": 2 * P * s2, "allpairs": (2 * P + 1) * s2, "ring": 5 * (P - 1) * s2,
+            "ring_fifo": 2 * P * s2 + (P - 1) * n2 * 12, "allpairs_persistent": (3 * P - 1) * s2}
+    res = {}
+    for a in ("ring", "allpairs", "oneshot", "ring_fifo", "allpairs_persistent"):
+        def call(a=a):
+            if sim.sim_allreduce(ip, op_, P, n2, "fp32", "sum", a, stream):
+                raise sim.SimError(-1, f"sim_allreduce({a})")
+        t = time_calls(call, steps, 3)
+        res[a] = {"us": round(t * 1e6, 2), "busbw_GBps": round(2 * (P - 1) / P * s2 / t / 1e9, 1),
+                  "hbm_algorithmic_GBps": round(laws[a] / t / 1e9, 1),
+                  "algorithmic_bytes": laws[a]}
+    assert sim.sim_check_error(stream) == 0
+    del din, dout
+    torch.cuda.empty_cache()
+    if cpu:
+        orc = oracle.get()
+        threads = orc.num_threads()
+        for a in ("ring", "allpairs", "oneshot"):
+            tc = time_cpu(lambda a=a: orc.allreduce(xs, "fp32", "sum", a), 3, 1)
+            res[a]["cpu_oracle"] = {"seconds": round(tc, 4), "busbw_GBps": round(2 * (P - 1) / P * s2 / tc / 1e9, 3),
+                                    "cores": threads}
+        orc.set_num_threads(1)
+        sub = [x[: n2 // 8].copy() for x in xs]
+        for a in ("ring", "oneshot"):
+            t1 = time_cpu(lambda a=a: orc.allreduce(sub, "fp32", "sum", a), 3, 1) * 8
+            res[a]["cpu_oracle"]["single_thread"] = {
+                "seconds": round(t1, 3), "busbw_GBps": round(2 * (P - 1) / P * s2 / t1 / 1e9, 4), "cores": 1,
+                "sample": "first 1/8 of each rank's buffer, median of 3, scaled to the full buffer"}
+        orc.set_num_threads(threads)
+    return res
+
+
+def workload5(sim, synthdata, oracle, torch, np, dev, stream, steps: int, cpu: bool) -> dict:
+    """p = 8, 256 MiB per rank: the all-reduce of every op of the workload
+    (selector's pick), the standalone reduce-scatter (32 MiB out per rank)
+    and all-gather (32 MiB in per rank), direct and ring; the CPU oracle of
+    the same calls (median of 2)."""
+    res = {"allreduce": {}, "reduce_scatter": {}, "all_gather": {}}
+    n_out = N5 // P
+    s_full = N5 * 4
+    orc = oracle.get() if cpu else None
+    for dtype, ops in (("fp32", ("prod", "min", "max", "avg")), ("int32", ("sum", "min", "max"))):
+        xs = synthdata.workload_inputs(5, P, N5, dtype)
+        tdt = torch.float32 if dtype == "fp32" else torch.int32
+        din = [torch.from_numpy(x).to(dev) for x in xs]
+        dout = [torch.empty(N5, dtype=tdt, device=dev) for _ in range(P)]
+        ip, op_ = [t.data_ptr() for t in din], [t.data_ptr() for t in dout]
+        for op in ops:
+            def call(op=op):
+                if sim.sim_allreduce(ip, op_, P, N5, dtype, op, "auto", stream):
+                    raise sim.SimError(-1, "sim_allreduce (workload 5)")
+            t = time_calls(call, steps, 2)
+            ran = sim.sim_last_algo()
+            law = algorithmic_bytes_at(ran, N5, 4)
+            ent = {"algo": ran, "us": round(t * 1e6, 2), "busbw_GBps": round(2 * (P - 1) / P * s_full / t / 1e9, 1),
+                   "hbm_algorithmic_GBps": round(law / t / 1e9, 1),
+                   "frac_of_peak": round(law / t / 1e9 / HBM_PEAK_GBPS, 4)}
+            if orc is not None:
+                tc = time_cpu(lambda op=op: orc.allreduce(xs, dtype, op, ran), 2)
+                ent["cpu_oracle"] = {"seconds": round(tc, 3), "cores": orc.num_threads(),
+                                     "busbw_GBps": round(2 * (P - 1) / P * s_full / tc / 1e9, 3)}
+            res["allreduce"][f"{dtype} {op}"] = ent
+        # standalone reduce-scatter and all-gather: direct (p+1) S_full; the ring
+        # reduce-scatter 3 (p-1) S_full (32-bit partials through scratch), the
+        # ring all-gather (2p-1) S_full
+        rs_out = [torch.empty(n_out, dtype=tdt, device=dev) for _ in range(P)]
+        rp = [t.data_ptr() for t in rs_out]
+        op_rs = "sum" if dtype == "int32" else "avg"
+        for a, law in (("allpairs", (P + 1) * s_full), ("ring", 3 * (P - 1) * s_full)):
+            def rs(a=a):
+                if sim.sim_reduce_scatter(ip, rp, P, n_out, dtype, op_rs, a, stream):
+                    raise sim.SimError(-1, "sim_reduce_scatter")
+            t = time_calls(rs, steps, 2)
+            ent = {"op": op_rs, "us": round(t * 1e6, 2),
+                   "busbw_GBps": round((P - 1) / P * s_full / t / 1e9, 1),
+                   "hbm_algorithmic_GBps": round(law / t / 1e9, 1), "algorithmic_bytes": law,
+                   "frac_of_peak": round(law / t / 1e9 / HBM_PEAK_GBPS, 4)}
+            if orc is not None:
+                tc = time_cpu(lambda a=a: orc.reduce_scatter(xs, dtype, op_rs, a), 2)
+                ent["cpu_oracle"] = {"seconds": round(tc, 3), "cores": orc.num_threads(),
+                                     "busbw_GBps": round((P - 1) / P * s_full / tc / 1e9, 3)}
+            res["reduce_scatter"][f"{dtype} {'direct' if a == 'allpairs' else 'ring'}"] = ent
+        small = [x[:n_out].copy() for x in xs] if orc is not None else None
+        for a, law in (("allpairs", (P + 1) * s_full), ("ring", (2 * P - 1) * s_full)):
+            def ag(a=a):
+                if sim.sim_all_gather(rp, op_, P, n_out, dtype, a, stream):
+                    raise sim.SimError(-1, "sim_all_gather")
+            t = time_calls(ag, steps, 2)
+            ent = {"us": round(t * 1e6, 2), "busbw_GBps": round((P - 1) / P * s_full / t / 1e9, 1),
+                   "hbm_algorithmic_GBps": round(law / t / 1e9, 1), "algorithmic_bytes": law,
+                   "frac_of_peak": round(law / t / 1e9 / HBM_PEAK_GBPS, 4)}
+            if orc is not None:
+                tc = time_cpu(lambda a=a: orc.all_gather(small, dtype, a), 2)
+                ent["cpu_oracle"] = {"seconds": round(tc, 3), "cores": orc.num_threads(),
+                                     "busbw_GBps": round((P - 1) / P * s_full / tc / 1e9, 3)}
+            res["all_gather"][f"{dtype} {'direct' if a == 'allpairs' else 'ring'}"] = ent
+        assert sim.sim_check_error(stream) == 0
+        if orc is not None:  # one thread, on 1/16 of every buffer (cost per element does not depend on n)
+            threads = orc.num_threads()
+            orc.set_num_threads(1)
+            sub = [x[: N5 // 16].copy() for x in xs]
+            op1 = "avg" if dtype == "fp32" else "sum"
+            t1 = time_cpu(lambda: orc.allreduce(sub, dtype, op1, "oneshot"), 2) * 16
+            orc.set_num_threads(threads)
+            res["allreduce"][f"{dtype} {op1}"]["cpu_oracle"]["single_thread"] = {
+                "seconds": round(t1, 3), "busbw_GBps": round(2 * (P - 1) / P * s_full / t1 / 1e9, 4), "cores": 1,
+                "sample": "first 1/16 of each rank's buffer, median of 2, scaled to the full buffer"}
+            del sub, small
+        del din, dout, rs_out, xs
+        torch.cuda.empty_cache()
+    return res
+
+
+def workload4(sim, synthdata, torch, np, dev, stream) -> dict:
+    """Per-call microseconds, p = 8, fp16 N(0,1), 1 KiB .. 1 MiB per rank:
+    the LL packet path vs the plain one-shot, and the selector's pick.  The
+    buffers are re-used (at these sizes the working set sits in the cache
+    either way)."""
+    out = {}
+    for k in range(10, 21):
+        n = (1 << k) // 2
+        xs = synthdata.workload_inputs(4, P, n, "fp16")
+        din = [torch.from_numpy(x.view(np.int16)).to(dev) for x in xs]
+        dout = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(P)]
+        ip, op_ = [t.data_ptr() for t in din], [t.data_ptr() for t in dout]
+        row = {}
+        for a in ("oneshot", "oneshot_ll", "auto"):
+            call = sim.prepare_allreduce(ip, op_, P, n, "fp16", "sum", a, stream)
+            if call() != 0:
+                raise sim.SimError(call(), f"sim_allreduce({a})")
+            row[a] = round(time_calls(call, 1000, 100) * 1e6, 2)
+            if a == "auto":
+                row["auto_pick"] = sim.sim_last_algo()
+        out[f"{1 << k >> 10}KiB"] = row
+    assert sim.sim_check_error(stream) == 0
+    return out
+
+
+def algorithmic_bytes_at(algo: str, n: int, esize: int) -> float:
+    """All-reduce traffic laws at n elements per rank of `esize` bytes."""
+    s_ = n * esize
+    if algo == "oneshot":
+        return 2.0 * P * s_
+    if algo == "allpairs":
+        return (2.0 * P + 1.0) * s_
+    if algo == "allpairs_persistent":
+        return (3.0 * P - 1.0) * s_
+    if algo == "ring":
+        if esize == 4:
+            return 5.0 * (P - 1) * s_
+        return n * (esize + esize + 4) + (P - 3) * n * (4 + esize + 4) + n * (4 + esize + esize) \
+            + (P - 1) * n * (esize + esize)
+    if algo == "ring_fifo":
+        return 2.0 * P * s_ + (P - 1) * n * 8.0 + (P - 1) * n * esize
+    raise ValueError(algo)
 
 
 def main():
@@ -349,6 +617,17 @@ def main():
             glat[a] = round(time_calls(graph.replay, 100, 10) * 1e6 / 20, 2)
             del graph
         extras["latency_8KiB_graph_us"] = glat
+        extras["workload4_latency_us"] = workload4(sim, synthdata, torch, np, dev, stream)
+        import oracle
+        ext_steps = max(10, args.steps // 4)
+        extras["workload2_fp32_32MiB"] = workload2(sim, synthdata, oracle, torch, np, dev, stream, ext_steps,
+                                                   not args.no_cpu_baseline)
+        extras["workload5_256MiB"] = workload5(sim, synthdata, oracle, torch, np, dev, stream,
+                                               max(5, args.steps // 10), not args.no_cpu_baseline)
+        extras["ceiling"] = ceiling(sim, torch, dev, stream, max(10, args.steps // 2), ip, op_)
+        cf = max(extras["ceiling"]["copy_8in_8out_64MiB_each"]["GBps"],
+                 extras["ceiling"]["copy_headline_buffers"]["GBps"])
+        extras["ceiling"]["oneshot_over_8x8_copy"] = round(achieved / cf, 4) if ran == "oneshot" else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -362,7 +641,7 @@ def main():
             runs.append(time.perf_counter() - t0)
         tc = float(np.median(runs))
         cpu = {"value": round(2 * (P - 1) / P * S / tc / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(),
                "sample": f"the full workload (8 ranks x 64 MiB bf16, schedule '{ran}'), median of {len(runs)} runs",
                "seconds_per_call": round(tc, 3)}
         # one thread, on the first 1/16 of every rank's buffer (the oracle's cost per element does not
@@ -394,6 +673,18 @@ def main():
                               "median": round(float(np.median(reps)) * 1e6, 2)},
         **extras,
     }
+    if not args.no_extras:
+        # the selector against measurement (this re-initialises the library
+        # and loads the packaged calibration)
+        from all_reduce_reduction_amd import calibrate
+        del din, dout
+        torch.cuda.empty_cache()
+        rep = calibrate.check(sim.CALIBRATION, steps_scale=0.1, reps=3)
+        out["selector_check"] = {
+            b: {k: v[k] for k in ("cases", "strict_matches", "tolerant_matches", "pairs_agree", "pairs",
+                                  "pick_rel_error_median", "pick_rel_error_max")}
+            | {"picks": sorted({r["pick"] for r in v["rows"]}), "fastest": sorted({r["measured_best"] for r in v["rows"]})}
+            for b, v in rep["budgets"].items()}
     print(json.dumps(out), flush=True)
     sim.sim_finalize()
 
