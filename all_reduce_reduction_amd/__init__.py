@@ -65,6 +65,7 @@ def _load() -> ctypes.CDLL:
         "sim_init": ([i, i, sz], i),
         "sim_finalize": ([], i),
         "sim_allreduce": ([pp, pp, i, sz, i, i, i, vp], i),
+        "sim_allreduce_noalloc": ([pp, pp, i, sz, i, i, i, vp], i),
         "sim_reduce_scatter": ([pp, pp, i, sz, i, i, i, vp], i),
         "sim_all_gather": ([pp, pp, i, sz, i, i, vp], i),
         "sim_select": ([i, sz, i, i, ctypes.POINTER(i), ctypes.POINTER(d)], i),
@@ -143,6 +144,15 @@ def sim_finalize() -> None:
 def sim_allreduce(in_ptrs, out_ptrs, p, n, dtype, op, algo, stream=0) -> int:
     return lib.sim_allreduce(_ptr_array(in_ptrs), _ptr_array(out_ptrs), p, n, _code(DTYPES, dtype, "dtype"),
                              _code(OPS, op, "op"), _code(ALGOS, algo, "algo"), stream or None)
+
+
+def sim_allreduce_noalloc(in_ptrs, out_ptrs, p, n, dtype, op, algo, stream=0) -> int:
+    return lib.sim_allreduce_noalloc(_ptr_array(in_ptrs), _ptr_array(out_ptrs), p, n,
+                                     _code(DTYPES, dtype, "dtype"), _code(OPS, op, "op"),
+                                     _code(ALGOS, algo, "algo"), stream or None)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def prepare_allreduce(in_ptrs, out_ptrs, p, n, dtype, op, algo, stream=0):

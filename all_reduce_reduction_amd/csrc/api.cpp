@@ -239,6 +239,10 @@ struct Call {
   void* const* y;
   bool inplace;
   hipStream_t s;
+  // allocation-free calls: partial slots in this fixed array (checked to be
+  // large enough before anything is enqueued), no pointer-table entry
+  void* fixed_scratch = nullptr;
+  bool noalloc = false;
 };
 
 // Workgroups per transfer (gridDim.x) of a bulk kernel; every bulk kernel
@@ -280,7 +284,7 @@ int tiles_for(const Call& c, int64_t vecs_per_unit, int units, int unroll) {
 // only once the copy's event has completed (a later call may come on
 // another stream, or on a new stream that reuses the handle).
 const PtrSet* ptr_set_for(const Call& c) {
-  if (!g.ptab_on || !g.ptab || g.capturing || c.p > SIM_MAX_RANKS) return nullptr;
+  if (c.noalloc || !g.ptab_on || !g.ptab || g.capturing || c.p > SIM_MAX_RANKS) return nullptr;
   PtrKey k;
   k.p = c.p;
   for (int q = 0; q < c.p; q++) {
@@ -381,13 +385,12 @@ int run_ring_rs(const Call& c, const Schedule& sch, int nsteps, bool final_out_c
   // it does not own yet); otherwise partials live in fp32/int32 scratch slots.
   const bool part_in_y = (e == 4) && !final_out_chunk;
   const size_t se = slot_elems(c.n, p);
-  if (!part_in_y && p > 2) {
+  if (!part_in_y && p > 2 && !c.fixed_scratch) {
     int rc = ensure_scratch(scratch_need(c.n, p));
     if (rc) return rc;
   }
-  auto slot = [&](int parity, int rank) -> void* {
-    return (char*)g.scratch + ((size_t)parity * p + rank) * se * 4;
-  };
+  char* const base = (char*)(c.fixed_scratch ? c.fixed_scratch : g.scratch);
+  auto slot = [&](int parity, int rank) -> void* { return base + ((size_t)parity * p + rank) * se * 4; };
   int64_t maxchunk = 0;
   for (int q = 0; q < p; q++) maxchunk = std::max(maxchunk, lo[q + 1] - lo[q]);
   for (int st = 0; st < nsteps; st++) {
@@ -976,14 +979,19 @@ bool legal(int coll, int algo, int p, size_t n, int dtype) {
   return algo == SIM_ALGO_RING || algo == SIM_ALGO_ALLPAIRS;
 }
 
-int pick(int coll, int p, size_t n, int dtype, int* algo, double* us) {
+// AUTO weighs the single-node schedules; the tree, recursive-exchange and
+// 2PH schedules model multi-node topologies and run when asked for by name
+const int kAutoCandidates[] = {SIM_ALGO_RING,       SIM_ALGO_ALLPAIRS,  SIM_ALGO_ONESHOT,
+                               SIM_ALGO_ONESHOT_LL, SIM_ALGO_RING_FIFO, SIM_ALGO_ALLPAIRS_PERSISTENT};
+// the schedules the allocation-free entry point runs (no library buffers)
+const int kNoAllocCandidates[] = {SIM_ALGO_RING, SIM_ALGO_ALLPAIRS, SIM_ALGO_ONESHOT};
+
+int pick(int coll, int p, size_t n, int dtype, int* algo, double* us, const int* cands = kAutoCandidates,
+         int ncands = (int)(sizeof kAutoCandidates / sizeof kAutoCandidates[0])) {
   int best = -1;
   double bt = 0;
-  // AUTO weighs the single-node schedules; the tree, recursive-exchange and
-  // 2PH schedules model multi-node topologies and run when asked for by name
-  static const int kCandidates[] = {SIM_ALGO_RING,   SIM_ALGO_ALLPAIRS,  SIM_ALGO_ONESHOT,
-                                    SIM_ALGO_ONESHOT_LL, SIM_ALGO_RING_FIFO, SIM_ALGO_ALLPAIRS_PERSISTENT};
-  for (int a : kCandidates) {
+  for (int k = 0; k < ncands; k++) {
+    const int a = cands[k];
     if (!legal(coll, a, p, n, dtype)) continue;
     const double t = model_predict(g.model, coll, a, p, (double)n, esize_of(dtype), g_topo, g_max_wg);
     if (best < 0 || t < bt) {
@@ -1126,6 +1134,15 @@ int sim_init(int device, int p_max, size_t max_bytes_per_rank) {
     g.ptab_host = nullptr;
   }
   g.ptab_slots.assign(kPtrSets, PtrSlot());
+  // the allocation-free entry point: its scratch array's address on this
+  // device, and its schedules lowered and verified now, so that its calls
+  // find them cached
+  if (noalloc_setup(device) != SIM_OK) {
+    sim_finalize();
+    return SIM_ERR_HIP;
+  }
+  for (int p = 2; p <= p_max; p++)
+    for (int a : kNoAllocCandidates) (void)cached_schedule(COLL_ALLREDUCE, a, p, g_topo, nullptr);
   g.init = true;
   if (max_bytes_per_rank > 0) {
     const size_t n = max_bytes_per_rank / 2;  // 16-bit elements need the most slots
@@ -1171,6 +1188,45 @@ int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size
   if (rc) return rc;
   g.last_algo = algo;
   log_call("AllReduce", c, us);
+  return SIM_OK;
+}
+
+int sim_allreduce_noalloc(const void* const* in_ptrs, void* const* out_ptrs, int p, size_t n, int dtype,
+                          int op, int algo, void* stream) {
+  int rc = check_scalars(p, dtype, op, true);
+  if (rc) return rc;
+  if (algo < SIM_ALGO_AUTO || algo > kLastAlgo) return SIM_ERR_INVALID_ARG;
+  if (algo != SIM_ALGO_AUTO && algo != SIM_ALGO_RING && algo != SIM_ALGO_ALLPAIRS && algo != SIM_ALGO_ONESHOT)
+    return SIM_ERR_UNSUPPORTED;
+  if (n == 0) return SIM_OK;
+  const size_t e = (size_t)esize_of(dtype);
+  if (n > ((size_t)1 << 46) / e) return SIM_ERR_INVALID_ARG;
+  bool inplace = false;
+  rc = check_buffers(in_ptrs, out_ptrs, p, n * e, n * e, nullptr, &inplace);
+  if (rc) return rc;
+  void* const fixed = noalloc_scratch(g.device);
+  if (!fixed) return SIM_ERR_NOT_INIT;
+  if (use_device() != SIM_OK) return SIM_ERR_HIP;
+  rc = begin_call(stream);
+  if (rc) return rc;
+  double us = 0;
+  if (algo == SIM_ALGO_AUTO) {
+    rc = pick(COLL_ALLREDUCE, p, n, dtype, &algo, &us, kNoAllocCandidates,
+              (int)(sizeof kNoAllocCandidates / sizeof kNoAllocCandidates[0]));
+    if (rc) return rc;
+  } else {
+    us = model_predict(g.model, COLL_ALLREDUCE, algo, p, (double)n, (int)e, g_topo, g_max_wg);
+  }
+  // only the 16-bit ring (p > 2) keeps partials: they must fit the array
+  if (algo == SIM_ALGO_RING && e == 2 && p > 2 && scratch_need(n, p) > SIM_NOALLOC_SCRATCH_BYTES)
+    return SIM_ERR_NOMEM;
+  Call c{COLL_ALLREDUCE, p, dtype, op, algo, n, in_ptrs, out_ptrs, inplace, (hipStream_t)stream};
+  c.fixed_scratch = fixed;
+  c.noalloc = true;
+  rc = run_allreduce(c);
+  if (rc) return rc;
+  g.last_algo = algo;
+  log_call("AllReduce (allocation-free)", c, us);
   return SIM_OK;
 }
 

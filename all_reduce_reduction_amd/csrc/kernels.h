@@ -268,6 +268,11 @@ hipError_t launch_ring_reduce(int dtype, int op, bool a_partial, bool d_final, c
 hipError_t launch_copy(int esize, const CopyArgs& a, int unroll, hipStream_t s);
 hipError_t launch_ll(int dtype, int op, const LLArgs& a, int grid, hipStream_t s);
 hipError_t launch_copy_streams(const CopyStreamsArgs& a, int workgroups, hipStream_t s);
+// The fixed scratch array of sim_allreduce_noalloc (noalloc.hip): look up its
+// device address once per device, with that device current (SIM_OK or
+// SIM_ERR_HIP), and read it back (nullptr before the lookup).
+int noalloc_setup(int device);
+void* noalloc_scratch(int device);
 hipError_t launch_fill64(unsigned long long* p, unsigned long long v, int64_t n, hipStream_t s);
 // Workgroups of the LL kernel (dtype, op) that fit on one CU at once.
 int ll_blocks_per_cu(int dtype, int op);

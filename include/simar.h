@@ -183,6 +183,31 @@ int sim_finalize(void);
 int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size_t n,
                   int dtype, int op, int algo, void* stream);
 
+/* Allocation-free all-reduce, for callers that cannot allocate device
+ * memory while they run: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The same call as sim_allreduce, with
+ * the same arguments, checks, fold orders and bit-identical results, for
+ * algo SIM_ALGO_ONESHOT, SIM_ALGO_ALLPAIRS, SIM_ALGO_RING or SIM_ALGO_AUTO
+ * (the selector's argmin over these three; sim_last_algo reports the
+ * pick); any other schedule is SIM_ERR_UNSUPPORTED.  It allocates nothing:
+ * no hipMalloc or hipFree, no scratch growth, no pointer-table entry (the
+ * pointers travel in the kernel arguments).  The only scratch, the fp32
+ * partial slots of the fp16/bf16 ring (p > 2), lives in a fixed device
+ * array of SIM_NOALLOC_SCRATCH_BYTES that the library's code object holds
+ * on every device it is loaded on until the process ends: the call needs
+ * 8 p ceil64(ceil(n/p) + 8) bytes of it (ceil64: rounded up to a multiple
+ * of 64): at p = 8 up to 8,388,544 elements per rank (16 MiB - 128 B of
+ * bf16).  A larger message is SIM_ERR_NOMEM with nothing enqueued.  Nothing in
+ * the array has to start at zero (every partial is written before it is
+ * read).  The array is shared by every call of this entry point on one
+ * device and keeps the last call's contents: calls that overlap in time on
+ * one device (on different streams, or from different host threads) race
+ * on it; calls on one stream are ordered.  Errors: as sim_allreduce, plus
+ * SIM_ERR_NOMEM as above. */
+#define SIM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int sim_allreduce_noalloc(const void* const* in_ptrs, void* const* out_ptrs, int p, size_t n, int dtype,
+                          int op, int algo, void* stream);
+
 /* Reduce-scatter ("Inside NCCL all-reduce", "What all-reduce promises":
  * every rank ends owning the finished reduction of one slice): inputs hold
  * p * n_out_per_rank elements; out_ptrs[r] (n_out_per_rank elements)
