@@ -75,6 +75,7 @@ def _load() -> ctypes.CDLL:
         "sim_model_set": ([i, d, d, d, d], i),
         "sim_model_reset": ([], i),
         "sim_model_set_workgroup_rate": ([i, d], i),
+        "sim_model_set_host_overlap": ([i, d], i),
         "sim_check_error": ([vp], i),
         "sim_copy_streams": ([pp, pp, i, sz, i, vp], i),
         "sim_config_set": ([i, i], i),
@@ -214,6 +215,11 @@ def sim_model_set(algo, alpha_us: float, steps: float, bytes_factor: float, gbps
 def sim_model_set_workgroup_rate(algo, gbps_per_workgroup: float) -> None:
     _check(lib.sim_model_set_workgroup_rate(_code(ALGOS, algo, "algo"), float(gbps_per_workgroup)),
            "sim_model_set_workgroup_rate")
+
+
+def sim_model_set_host_overlap(algo, host_us_per_launch: float) -> None:
+    _check(lib.sim_model_set_host_overlap(_code(ALGOS, algo, "algo"), float(host_us_per_launch)),
+           "sim_model_set_host_overlap")
 
 
 def sim_model_reset() -> None:

@@ -192,10 +192,12 @@ int check_buffers(const void* const* in, void* const* out, int p, size_t in_byte
 
 // ---- scratch ------------------------------------------------------------------
 // Ring partial slots: [parity 0/1][rank] x (max chunk + 8) fp32/int32 values,
-// each slot rounded to 64 values so every slot starts 256-byte aligned.
+// each slot rounded to whole blocks of 512 values (the layout of 16-bit
+// types' partials, see part_pos in device_common.h), so every slot also
+// starts 2 KiB aligned.
 size_t slot_elems(size_t n, int p) {
   const size_t e = (n + (size_t)p - 1) / (size_t)p + 8;
-  return (e + 63) / 64 * 64;
+  return (e + 511) / 512 * 512;
 }
 size_t scratch_need(size_t n, int p) { return 2 * (size_t)p * slot_elems(n, p) * 4; }
 
@@ -688,7 +690,7 @@ int run_sched(const Call& c, const Schedule& sch) {
   if (e == 4) {
     for (int r = 0; r < p; r++) part[r] = c.y[r];
   } else {
-    const size_t stride = (c.n + 63) / 64 * 64;  // fp32 elements per rank, 256-byte aligned slots
+    const size_t stride = (c.n + 511) / 512 * 512;  // fp32 elements per rank, whole 512-element blocks
     int rc = ensure_scratch((size_t)p * stride * 4);
     if (rc) return rc;
     for (int r = 0; r < p; r++) part[r] = (char*)g.scratch + (size_t)r * stride * 4;
@@ -1375,7 +1377,15 @@ int sim_model_set(int algo, double alpha_us, double steps, double bytes_factor, 
   m.gbps = gbps;
   m.steps = steps;
   m.bytes_factor = bytes_factor;
+  m.host_us = 0.0;  // the additive form as given; sim_model_set_host_overlap adds the host term
   g.model.source = "sim_model_set";
+  return SIM_OK;
+}
+
+int sim_model_set_host_overlap(int algo, double host_us_per_launch) {
+  if (algo < SIM_ALGO_RING || algo > kLastAlgo || !(host_us_per_launch >= 0)) return SIM_ERR_INVALID_ARG;
+  g.model.a[algo].host_us = host_us_per_launch;
+  g.model.source = "sim_model_set_host_overlap";
   return SIM_OK;
 }
 

@@ -179,13 +179,34 @@ __device__ __forceinline__ u32x4 pack(const typename Ty<DT>::A* in) {
   return v;
 }
 
-// accumulator-typed partials: V values at element index i0 (vector aligned)
+// Where partial j sits in an accumulator-typed partial buffer.  A lane
+// handles V elements per vector; for 16-bit types that is 8 partials of
+// 4 bytes, 32 bytes, stored as two 16-byte halves.  Kept in element order,
+// each 16-byte store instruction of a wave would write every other 16 bytes
+// of a 2 KiB run, and the half-filled lines reach memory as separate
+// partial writes.  So the partials of 16-bit types are laid out in blocks
+// of 512 elements (one wave's 64 vectors) as [half][lane][4]: every store
+// or load instruction of a wave covers one contiguous 1 KiB run.  32-bit
+// types (one 16-byte vector per lane, partials sometimes kept in the
+// outputs) stay in element order.  Buffers of 16-bit partials are sized in
+// whole blocks of 512 elements.
+template <int DT>
+__device__ __forceinline__ int64_t part_pos(int64_t j) {
+  if constexpr (Ty<DT>::E == 4) {
+    return j;
+  } else {
+    const int w = (int)(j & 511);  // w = lane * 8 + k within the block
+    return (j - w) + ((w & 4) << 6) + ((w >> 3) << 2) + (w & 3);
+  }
+}
+
+// accumulator-typed partials: V values at element index idx (vector aligned)
 template <int DT>
 __device__ __forceinline__ void load_part(const void* base, int64_t idx, typename Ty<DT>::A* out) {
   constexpr int V = epv<DT>();
 #pragma unroll
   for (int h = 0; h < V / 4; h++) {
-    const u32x4 w = ld16(base, (idx + 4 * h) * 4);
+    const u32x4 w = ld16(base, part_pos<DT>(idx + 4 * h) * 4);
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       // copy the lane out first: a bit cast applied directly to a vector
@@ -203,7 +224,7 @@ __device__ __forceinline__ void store_part(void* base, int64_t idx, const typena
     u32x4 w;
 #pragma unroll
     for (int k = 0; k < 4; k++) w[k] = __builtin_bit_cast(uint32_t, in[4 * h + k]);
-    st16(base, (idx + 4 * h) * 4, w);
+    st16(base, part_pos<DT>(idx + 4 * h) * 4, w);
   }
 }
 

@@ -101,14 +101,14 @@ __global__ void __launch_bounds__(kBlock) k_sched_fold(SchedArgs a) {
     A acc = A(0);
     for (int k = 0; k < nsrc; k++) {
       const int q = (int)((x.order >> (4 * k)) & 15u);
-      const A v = ((x.from_part >> k) & 1u) ? ((const A*)a.part[q])[i] : O::pre(load_elem<DT>(a.x[q], i), a.inv_p);
+      const A v = ((x.from_part >> k) & 1u) ? ((const A*)a.part[q])[part_pos<DT>(i)] : O::pre(load_elem<DT>(a.x[q], i), a.inv_p);
       acc = (k == 0) ? v : O::comb(acc, v);
     }
     if (x.final_) {
       acc = O::post(acc, p);
       for (uint32_t m = x.dmask; m; m &= m - 1) store_elem<DT>(a.y[__builtin_ctz(m)], i, acc);
     } else {
-      for (uint32_t m = x.dmask; m; m &= m - 1) ((A*)a.part[__builtin_ctz(m)])[i] = acc;
+      for (uint32_t m = x.dmask; m; m &= m - 1) ((A*)a.part[__builtin_ctz(m)])[part_pos<DT>(i)] = acc;
     }
   }
 }

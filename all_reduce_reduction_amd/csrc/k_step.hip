@@ -80,11 +80,11 @@ __device__ __forceinline__ void ring_reduce_xfer(const RingXfer& x, const int64_
   for (int64_t s = tile * kBlock + tid; s < nscalar; s += (int64_t)tiles * kBlock) {
     const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
     A in;
-    if constexpr (A_PART) in = ((const A*)x.a)[i - x.a_shift];
+    if constexpr (A_PART) in = ((const A*)x.a)[part_pos<DT>(i - x.a_shift)];
     else in = O::pre(load_elem<DT>(x.a, i), inv_p);
     A v = O::comb(in, O::pre(load_elem<DT>(x.b, i), inv_p));
     if constexpr (D_FINAL) store_elem<DT>(x.d, i - x.d_shift, O::post(v, p));
-    else ((A*)x.d)[i - x.d_shift] = v;
+    else ((A*)x.d)[part_pos<DT>(i - x.d_shift)] = v;
   }
 }
 

@@ -27,24 +27,26 @@
 namespace simar {
 
 // Built-in defaults: the fit of the calibration sweep on MI355X (p = 8,
-// bf16, 1.5 KiB .. 192 MiB per rank, rotating buffer sets; per-workgroup
-// rates from budgets of 16 .. 128 workgroups at 48 MiB per rank, LL at
-// 768 KiB; the topology schedules at the topologies the calibration file
-// states), rounded.  A calibration file loaded with sim_model_load() or
+// bf16, 1.5 KiB .. 192 MiB per rank, rotating buffer sets; host enqueue
+// costs where the pipelined form fits better; per-workgroup rates from
+// budgets of 16 .. 128 workgroups at 48 MiB per rank, LL at 768 KiB; the
+// topology schedules at the topologies the calibration file states),
+// rounded.  A calibration file loaded with sim_model_load() or
 // SIM_CALIB replaces them.
 Model default_model() {
   Model m;
-  m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0, 0.0};
-  m.a[SIM_ALGO_RING] = {2.7, 5800.0, -1.0, -1.0, 24.0};
-  m.a[SIM_ALGO_ALLPAIRS] = {2.9, 5700.0, -1.0, -1.0, 43.5};
-  m.a[SIM_ALGO_ONESHOT] = {3.1, 5700.0, -1.0, -1.0, 49.0};
-  m.a[SIM_ALGO_ONESHOT_LL] = {8.6, 13800.0, -1.0, -1.0, 8.7};
-  m.a[SIM_ALGO_RING_FIFO] = {14.1, 6350.0, -1.0, -1.0, 15.8};
-  m.a[SIM_ALGO_TREE] = {4.0, 6000.0, -1.0, -1.0, 0.0};
-  m.a[SIM_ALGO_REXCH] = {3.9, 5250.0, -1.0, -1.0, 0.0};
-  m.a[SIM_ALGO_HIER] = {4.1, 5950.0, -1.0, -1.0, 0.0};
-  m.a[SIM_ALGO_HIER_LARGE] = {4.4, 5900.0, -1.0, -1.0, 0.0};
-  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {7.1, 6600.0, -1.0, -1.0, 31.4};
+  // {alpha_us, gbps, steps, bytes_factor, wg_gbps, host_us}
+  m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0, 0.0, 0.0};
+  m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.5, 2.8};
+  m.a[SIM_ALGO_ALLPAIRS] = {1.9, 5650.0, -1.0, -1.0, 43.5, 3.0};
+  m.a[SIM_ALGO_ONESHOT] = {1.25, 5650.0, -1.0, -1.0, 49.0, 3.2};
+  m.a[SIM_ALGO_ONESHOT_LL] = {8.65, 12500.0, -1.0, -1.0, 8.6, 0.0};
+  m.a[SIM_ALGO_RING_FIFO] = {14.2, 6350.0, -1.0, -1.0, 16.0, 0.0};
+  m.a[SIM_ALGO_TREE] = {3.1, 6200.0, -1.0, -1.0, 0.0, 4.1};
+  m.a[SIM_ALGO_REXCH] = {2.1, 6050.0, -1.0, -1.0, 0.0, 4.05};
+  m.a[SIM_ALGO_HIER] = {3.35, 6250.0, -1.0, -1.0, 0.0, 4.25};
+  m.a[SIM_ALGO_HIER_LARGE] = {3.15, 6050.0, -1.0, -1.0, 0.0, 4.45};
+  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {7.4, 6650.0, -1.0, -1.0, 31.5, 0.0};
   return m;
 }
 
@@ -198,7 +200,8 @@ double model_predict(const Model& m, int coll, int algo, int p, double n, int es
   const double steps = am.steps >= 0 ? am.steps : (double)launches;
   const double bytes = am.bytes_factor >= 0 ? am.bytes_factor * n * esize
                                             : model_traffic(coll, algo, p, n, esize, t);
-  return am.alpha_us * steps + bytes / (model_bandwidth(m, algo, p, budget) * 1e3);  // GB/s -> bytes per us
+  const double gpu = am.alpha_us * steps + bytes / (model_bandwidth(m, algo, p, budget) * 1e3);  // GB/s -> B/us
+  return std::max(am.host_us * launches, gpu);
 }
 
 // ---------------------------------------------------------------------------
@@ -388,6 +391,15 @@ bool model_load_json(const char* path, Model* m, std::string* err) {
     out.a[a].steps = -1;
     out.a[a].bytes_factor = -1;
     out.a[a].wg_gbps = 0;
+    out.a[a].host_us = 0;
+    auto hu = o.obj.find("host_us");  // optional: host enqueue cost per launch
+    if (hu != o.obj.end()) {
+      if (hu->second.kind != JVal::NUM || !(hu->second.num >= 0)) {
+        if (err) *err = "host_us must be a number >= 0";
+        return false;
+      }
+      out.a[a].host_us = hu->second.num;
+    }
     auto wr = o.obj.find("wg_gbps");  // optional: rate of one workgroup under a budget
     if (wr != o.obj.end()) {
       if (wr->second.kind != JVal::NUM || !(wr->second.num >= 0)) {

@@ -18,6 +18,7 @@ struct AlgoModel {
   double steps = -1.0;         // override of the launch count law when >= 0
   double bytes_factor = -1.0;  // override of the traffic law (bytes per message byte) when >= 0
   double wg_gbps = 0.0;        // rate one workgroup sustains, for calls under a workgroup budget (0: no term)
+  double host_us = 0.0;        // host enqueue cost per launch, overlapping the GPU's work (0: no term)
 };
 
 // One measured launch configuration.
@@ -74,7 +75,10 @@ double schedule_traffic(const Schedule& s, double n, int esize);
 double model_bandwidth(const Model& m, int algo, int p, int budget);
 
 // T = alpha * launches + traffic / B_eff, in microseconds, B_eff being
-// model_bandwidth() at `budget`.
+// model_bandwidth() at `budget`; with a host enqueue cost H per launch,
+// T = max(H * launches, that): calls issued back to back overlap the host's
+// enqueue of one call with the GPU's execution of the previous one, so a
+// call costs whichever side is slower.
 double model_predict(const Model& m, int coll, int algo, int p, double n, int esize,
                      const Topology& t = Topology(), int budget = 0);
 

@@ -72,7 +72,15 @@ def parse():
     ap.add_argument("--profile-large", action="store_true",
                     help="only the 256 MiB-per-rank fp32 avg one-shot (workload 5's 4 GiB working set)")
     ap.add_argument("--profile-copy", action="store_true",
-                    help="only a plain 512 MiB -> 512 MiB device copy (the counter scale reference)")
+                    help="only the k-stream copy kernel at k = 1 (512 MiB) and k = 8 (64 MiB each), the counter "
+                         "scale references")
+    ap.add_argument("--profile-size", type=int, default=0,
+                    help="only the schedules of --profile-algos at this many bytes per rank (p = 8, fp16, "
+                         "workload 4's inputs), --steps calls each (for rocprofv3 kernel traces and counters)")
+    ap.add_argument("--profile-algos", default="oneshot,oneshot_ll,allpairs,allpairs_persistent,ring_fifo,ring")
+    ap.add_argument("--profile-rsag", action="store_true",
+                    help="only workload 5's standalone reduce-scatter (fp32 avg) and all-gather, direct then ring, "
+                         "256 MiB per rank, --steps calls each")
     return ap.parse_args()
 
 
@@ -148,6 +156,7 @@ def time_calls(fn, steps: int, warmup: int) -> float:
 
 
 KERNEL_SOURCES = ["all_reduce_reduction_amd/csrc/k_fold.hip", "all_reduce_reduction_amd/csrc/k_step.hip",
+                  "all_reduce_reduction_amd/csrc/k_streams.hip",
                   "all_reduce_reduction_amd/csrc/device_common.h", "all_reduce_reduction_amd/csrc/kernels.h"]
 
 
@@ -466,27 +475,66 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     if args.profile_copy:
-        # Counter scale references of known size: (1) the library's own copy
-        # kernel (the ring all-gather step, same 16-byte streaming loads/stores
-        # as k_fold) in a p = 2 fp32 ring all-reduce of 256 MiB per rank: each
-        # such launch reads 256 MiB and writes 256 MiB; (2) torch's
-        # device-to-device copy of 512 MiB.
+        # Counter scale references of known size: the library's k-stream copy
+        # (sim_copy_streams) with k = 1, 512 MiB read and 512 MiB written per
+        # launch, and with k = 8, 64 MiB per stream (the one-shot's 16
+        # streams: 512 MiB read, 512 MiB written); torch's device-to-device
+        # copy of 512 MiB for comparison.
         sim.sim_init(0, 2, 0)
-        n2 = (256 << 20) // 4
-        bufs = [torch.empty(n2, dtype=torch.float32, device=dev).fill_(1.0) for _ in range(4)]
-        ptr = [b.data_ptr() for b in bufs]
         s2 = int(torch.cuda.current_stream().cuda_stream)
-        t1 = time_calls(lambda: sim.sim_allreduce(ptr[:2], ptr[2:], 2, n2, "fp32", "sum", "ring", s2),
-                        args.steps, args.warmup)
-        src = torch.empty(S * P // 2 // 4, dtype=torch.int32, device=dev).fill_(7)
+        res = {}
+        for k, per in ((1, 512 << 20), (8, 64 << 20)):
+            src = [torch.randint(-2 ** 31, 2 ** 31 - 1, (per // 4,), dtype=torch.int32, device=dev) for _ in range(k)]
+            dst = [torch.empty_like(src[0]) for _ in range(k)]
+            sp, dp = [t.data_ptr() for t in src], [t.data_ptr() for t in dst]
+            res[f"k_copy_streams<{k}> us"] = round(time_calls(
+                lambda: sim.sim_copy_streams(sp, dp, k, per, 0, s2), args.steps, args.warmup) * 1e6, 2)
+            res[f"k_copy_streams<{k}> bytes read / written per launch"] = k * per
+            del src, dst
+        src = torch.randint(-2 ** 31, 2 ** 31 - 1, ((512 << 20) // 4,), dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
-        t2 = time_calls(lambda: dst.copy_(src), args.steps, args.warmup)
-        print(json.dumps({"k_copy_bytes_read": 2 * n2 * 4 // 2 * 1, "k_copy_bytes_written": n2 * 4,
-                          "us_per_ring_call": t1 * 1e6, "torch_copy_bytes": src.numel() * 4,
-                          "us_per_torch_copy": t2 * 1e6}), flush=True)
+        res["torch copy of 512 MiB us"] = round(time_calls(lambda: dst.copy_(src), args.steps, args.warmup) * 1e6, 2)
+        print(json.dumps(res), flush=True)
         return
     sim.sim_init(0, P, S)
     stream = int(torch.cuda.current_stream().cuda_stream)
+    if args.profile_size:
+        n = args.profile_size // 2
+        xs = synthdata.workload_inputs(4, P, n, "fp16")
+        din = [torch.from_numpy(x.view(np.int16)).to(dev) for x in xs]
+        dout = [torch.empty(n, dtype=torch.int16, device=dev) for _ in range(P)]
+        ip, op_ = [t.data_ptr() for t in din], [t.data_ptr() for t in dout]
+        res = {}
+        for a in args.profile_algos.split(","):
+            call = sim.prepare_allreduce(ip, op_, P, n, "fp16", "sum", a, stream)
+            if call() != 0:
+                raise sim.SimError(call(), f"sim_allreduce({a})")
+            res[a] = round(time_calls(call, args.steps, args.warmup) * 1e6, 3)
+        assert sim.sim_check_error(stream) == 0
+        print(json.dumps({"bytes_per_rank": args.profile_size, "us_per_call": res}), flush=True)
+        return
+    if args.profile_rsag:
+        n_out = N5 // P
+        xs5 = synthdata.workload_inputs(5, P, N5, "fp32")
+        d5 = [torch.from_numpy(x).to(dev) for x in xs5]
+        del xs5
+        o5 = [torch.empty(N5, dtype=torch.float32, device=dev) for _ in range(P)]
+        r5 = [torch.empty(n_out, dtype=torch.float32, device=dev) for _ in range(P)]
+        i5, p5, q5 = [t.data_ptr() for t in d5], [t.data_ptr() for t in o5], [t.data_ptr() for t in r5]
+        res = {}
+        for a in ("allpairs", "ring"):
+            def rs(a=a):
+                if sim.sim_reduce_scatter(i5, q5, P, n_out, "fp32", "avg", a, stream):
+                    raise sim.SimError(-1, "sim_reduce_scatter")
+            res[f"reduce_scatter {a}"] = round(time_calls(rs, args.steps, args.warmup) * 1e6, 2)
+        for a in ("allpairs", "ring"):
+            def ag(a=a):
+                if sim.sim_all_gather(q5, p5, P, n_out, "fp32", a, stream):
+                    raise sim.SimError(-1, "sim_all_gather")
+            res[f"all_gather {a}"] = round(time_calls(ag, args.steps, args.warmup) * 1e6, 2)
+        assert sim.sim_check_error(stream) == 0
+        print(json.dumps({"workload": "fp32, p=8, 256 MiB per rank", "us_per_call": res}), flush=True)
+        return
     if args.profile_large:
         us5 = large_workload(sim, synthdata, torch, np, dev, stream, args.steps, args.warmup)
         print(json.dumps({"workload": "fp32 avg, p=8, 256 MiB per rank", "us_per_step": us5}), flush=True)

@@ -53,15 +53,19 @@
  *     max_bytes_per_rank or make one uncaptured call of the same shape
  *     first.  Once a call has been captured, outgrown scratch is kept until
  *     sim_finalize, so recorded graphs stay valid until then (not after).
- *   - Co-residency: SIM_ALGO_RING_FIFO and SIM_ALGO_ALLPAIRS_PERSISTENT run
- *     persistent workgroups that wait on one another, so all of them must be
- *     resident on the GPU at once.  The library sizes the grid from the
+ *   - Co-residency: SIM_ALGO_RING_FIFO, SIM_ALGO_ALLPAIRS_PERSISTENT and
+ *     SIM_ALGO_ONESHOT_LL run workgroups that wait on one another (the LL
+ *     consumers poll packets other workgroups of the same launch write), so
+ *     all of them must be resident on the GPU at once.  The library sizes the grid from the
  *     kernels' occupancy on an otherwise idle GPU; kernels running at the
  *     same time on other streams may hold CUs those workgroups need.  Every
  *     wait is bounded: such a call then ends with SIM_ERR_TIMEOUT (reported
- *     by sim_check_error; that call's outputs are undefined), never a hang.
- *     AUTO does not pick these two schedules on MI355X (the calibrated model
- *     ranks the one-shot first at every size).
+ *     by sim_check_error; that call's outputs are undefined), never a hang;
+ *     a workgroup whose wait expired gives up its remaining waits at once.
+ *     AUTO does not pick these three schedules on MI355X (the calibrated
+ *     model ranks the one-shot first at every size and under every budget
+ *     the calibration checks), but it may with another calibration file:
+ *     callers that run other kernels concurrently should name a schedule.
  *   - Shared library buffers: the partial scratch (16-bit ring, tree,
  *     recursive exchange and 2PH all-reduces; the ring reduce-scatter), the
  *     LL packet buffer (the LL one-shot and the single-launch ring's LL
@@ -177,7 +181,7 @@ int sim_finalize(void);
  * r, each buffer holding n elements of `dtype`, combined with `op` in the
  * fold order of `algo` (see the header comment).  algo SIM_ALGO_AUTO picks
  * the schedule with sim_select().  Ring on fp16/bf16 keeps fp32 partials in
- * library scratch (8 * (ceil(n/p) + 8) * p bytes).  Errors: every code
+ * library scratch (8 * ceil512(ceil(n/p) + 8) * p bytes).  Errors: every code
  * above except SIM_ERR_TIMEOUT/SIM_ERR_VERIFY (asynchronous device errors
  * come back through sim_check_error). */
 int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size_t n,
@@ -195,8 +199,8 @@ int sim_allreduce(const void* const* in_ptrs, void* const* out_ptrs, int p, size
  * partial slots of the fp16/bf16 ring (p > 2), lives in a fixed device
  * array of SIM_NOALLOC_SCRATCH_BYTES that the library's code object holds
  * on every device it is loaded on until the process ends: the call needs
- * 8 p ceil64(ceil(n/p) + 8) bytes of it (ceil64: rounded up to a multiple
- * of 64): at p = 8 up to 8,388,544 elements per rank (16 MiB - 128 B of
+ * 8 p ceil512(ceil(n/p) + 8) bytes of it (ceil512: rounded up to a
+ * multiple of 512): at p = 8 up to 8,388,544 elements per rank (16 MiB - 128 B of
  * bf16).  A larger message is SIM_ERR_NOMEM with nothing enqueued.  Nothing in
  * the array has to start at zero (every partial is written before it is
  * read).  The array is shared by every call of this entry point on one
@@ -239,7 +243,12 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p,
  * minimum of B_a and what W_a workgroups sustain; W_a = W, or max(W, p) for
  * SIM_ALGO_RING_FIFO and SIM_ALGO_ALLPAIRS_PERSISTENT, which keep one
  * workgroup per rank ("T-CCL ...", sections III-C3 and IV-B: restricted
- * mode).  The budget in effect is the current SIM_CONFIG_MAX_WORKGROUPS. */
+ * mode).  The budget in effect is the current SIM_CONFIG_MAX_WORKGROUPS.
+ * An algo with a host enqueue cost H_a per launch (sim_model_set_host_overlap,
+ * or "host_us" in the calibration file) is priced max(H_a * launches_a, T_a):
+ * calls issued back to back overlap the host's enqueue of one call with the
+ * GPU's execution of the previous one, so a call costs whichever side is
+ * slower; H_a = 0 leaves T_a as it is. */
 int sim_select(int p, size_t n, int dtype, int op, int* algo_out, double* predicted_us);
 
 /* The algo the most recent successful collective actually ran. */
@@ -252,8 +261,9 @@ int sim_last_algo(void);
  * III-C3): bulk kernels of that algo then launch the measured best total of
  * the nearest size (log scale), never more than covers the transfer, with
  * the entry's 16-byte vectors per lane (1 or 2; 1 when absent).  An algo
- * entry may carry "wg_gbps", its per-workgroup rate under a budget (see
- * sim_select; 0 when absent).  Errors: SIM_ERR_INVALID_ARG (the current
+ * entry may carry "wg_gbps", its per-workgroup rate under a budget, and
+ * "host_us", its host enqueue cost per launch (see sim_select; 0 when
+ * absent).  Errors: SIM_ERR_INVALID_ARG (the current
  * model is kept). */
 int sim_model_load(const char* json_path);
 
@@ -261,6 +271,10 @@ int sim_model_load(const char* json_path);
  * (the element size fixes the element count the traffic laws take), under
  * the current workgroup budget as sim_select prices it. */
 int sim_model_predict(int algo, int p, int dtype, double bytes_per_rank, double* us_out);
+
+/* Set one algo's host enqueue cost per launch (microseconds; 0 removes the
+ * term).  Errors: SIM_ERR_INVALID_ARG (unknown algo, negative or NaN). */
+int sim_model_set_host_overlap(int algo, double host_us_per_launch);
 
 /* Set one algo's per-workgroup rate b (GB/s one workgroup sustains; 0
  * removes the budget term, so a budget leaves that algo's B unchanged).
@@ -270,7 +284,9 @@ int sim_model_set_workgroup_rate(int algo, double gbps_per_workgroup);
 /* Override one algo's model: alpha_us and gbps always; `steps` (latency
  * units) and `bytes_factor` (bytes moved per byte of message) replace the
  * built-in laws when >= 0 -- e.g. the multi-GPU form 2(p-1) alpha +
- * 2(p-1)/p n / B.  Pass negative values to keep the built-in laws. */
+ * 2(p-1)/p n / B.  Pass negative values to keep the built-in laws.  The
+ * algo's host enqueue term is cleared (the additive form exactly as given);
+ * its per-workgroup rate is kept. */
 int sim_model_set(int algo, double alpha_us, double steps, double bytes_factor, double gbps);
 
 /* Restore the built-in default model. */

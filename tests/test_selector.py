@@ -256,3 +256,40 @@ def test_budget_rate_json(tmp_path):
     finally:
         sim.sim_config_set("max_workgroups", 0)
         sim.sim_model_reset()
+
+
+def test_host_overlap_term():
+    """With a host enqueue cost H per launch a call costs max(H L, alpha L +
+    bytes / B); sim_model_set restores the additive form; the file's
+    host_us loads and is validated."""
+    sim.sim_model_reset()
+    try:
+        sim.sim_model_set("oneshot", 1.0, -1, -1, 5000.0)
+        sim.sim_model_set_host_overlap("oneshot", 3.0)
+        small, large = 4096, 64 << 20
+        assert sim.sim_model_predict("oneshot", 8, "bf16", small) == pytest.approx(3.0)
+        assert sim.sim_model_predict("oneshot", 8, "bf16", large) == pytest.approx(1.0 + 16 * large / 5000e3)
+        sim.sim_model_set("ring", 1.0, -1, -1, 5000.0)
+        sim.sim_model_set_host_overlap("ring", 2.5)   # 14 launches at p = 8
+        assert sim.sim_model_predict("ring", 8, "bf16", small) == pytest.approx(14 * 2.5)
+        sim.sim_model_set("oneshot", 1.0, -1, -1, 5000.0)   # clears the host term
+        assert sim.sim_model_predict("oneshot", 8, "bf16", small) == pytest.approx(1.0 + 16 * small / 5000e3)
+        with pytest.raises(sim.SimError):
+            sim.sim_model_set_host_overlap("oneshot", -1.0)
+    finally:
+        sim.sim_model_reset()
+
+
+def test_host_overlap_json(tmp_path):
+    f = tmp_path / "m.json"
+    f.write_text(json.dumps({"algos": {"oneshot": {"alpha_us": 1.0, "gbps": 5000.0, "host_us": 3.0}}}))
+    try:
+        sim.sim_model_load(str(f))
+        assert sim.sim_model_predict("oneshot", 8, "bf16", 4096) == pytest.approx(3.0)
+        for bad in ('"x"', "-2", "null"):
+            f.write_text('{"algos": {"oneshot": {"alpha_us": 1.0, "gbps": 1.0, "host_us": %s}}}' % bad)
+            with pytest.raises(sim.SimError):
+                sim.sim_model_load(str(f))
+        assert sim.sim_model_predict("oneshot", 8, "bf16", 4096) == pytest.approx(3.0)
+    finally:
+        sim.sim_model_reset()

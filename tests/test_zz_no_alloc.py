@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 
 P = 8
 # the largest n whose fp32 ring partials fit the fixed array at p = 8:
-# 2 p ceil64(ceil(n/p) + 8) * 4 bytes <= SIM_NOALLOC_SCRATCH_BYTES
+# 2 p ceil512(ceil(n/p) + 8) * 4 bytes <= SIM_NOALLOC_SCRATCH_BYTES
 N_MAX_RING16 = 8_388_544
 
 
