@@ -15,10 +15,10 @@
 //          signals ready(r, c).
 //   step 2 (FANOUT, as each rank pulling from the owner): the workgroup
 //          waits for ready(j, c) of every other owner j at once (one lane
-//          per owner), then, starting at r + 1, copies each owner's slice
-//          of Y[j] into Y[r], reading it with
-//          device-scope loads -- each rank reading a peer's finished chunk
-//          from the peer's buffer, as a GPU reads over its links.
+//          per owner), then copies every owner's slice of Y[j] into Y[r],
+//          reading it with device-scope loads -- each rank reading a peer's
+//          finished chunk from the peer's buffer, as a GPU reads over its
+//          links.  Each pass loads from all p - 1 owners before it stores.
 // On one HBM this moves (3p - 1) S bytes (the 2-launch all-pairs fans out
 // with one load and p - 1 stores: (2p + 1) S; the fused one-shot 2p S): it
 // is the all-pairs schedule with its synchronisation inside the kernel,
@@ -144,29 +144,51 @@ __global__ void __launch_bounds__(kBlock) k_allpairs_persistent(AllPairsPArgs a)
           p - 1, [&](int k) { return a.sem + ((int64_t)((r + 1 + k) % p) * C + ch) * 2; }, tag(epoch, 1),
           a.spin_limit, &ok_flag))
     goto timeout;
-  for (int jj = 1; jj < p; jj++) {
-    const int j = (r + jj) % p;
-    {
-      int64_t s_lo, s_hi;
-      slice(j, &s_lo, &s_hi);
-      const bool vec = (s_lo % V) == 0;
-      for (int64_t base = s_lo; base < s_hi; base += kSpan) {
-        const int64_t len = min(s_hi - base, kSpan);
-        const __amdgpu_buffer_rsrc_t src = out_rsrc(a.y[j], base * E, len * E);
-        u32x4 w[U];
-        bool full[U];
+  // Pass b covers offsets [b, b + kPull) of every owner's slice, one
+  // vector per lane per owner: the loads of all p - 1 owners for the pass
+  // are issued together, then stored, so a pass costs one device-scope
+  // round trip instead of one per owner (at 8 KiB per rank a slice is a
+  // single pass).
+  {
+    constexpr int64_t kPull = (int64_t)kBlock * V;
+    int64_t o_lo[MAXP], o_len[MAXP];
+    int64_t longest = 0;
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-          const int64_t off = ((int64_t)u * kBlock + tid) * V;
-          full[u] = vec && off + V <= len;
-          if (full[u]) w[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (int)(off * E), 0, kLd);
-        }
+    for (int jj = 1; jj < MAXP; jj++) {
+      o_lo[jj] = 0;
+      o_len[jj] = 0;
+      if (jj < p) {
+        int64_t s_lo, s_hi;
+        slice((r + jj) % p, &s_lo, &s_hi);
+        o_lo[jj] = s_lo;
+        o_len[jj] = s_hi - s_lo;
+        longest = max(longest, s_hi - s_lo);
+      }
+    }
+    for (int64_t b = 0; b < longest; b += kPull) {
+      u32x4 w[MAXP];
+      bool full[MAXP];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-          const int64_t off = ((int64_t)u * kBlock + tid) * V;
-          if (full[u]) {
-            st16(yr, (base + off) * E, w[u]);
-          } else if (off < len) {
+      for (int jj = 1; jj < MAXP; jj++) {
+        const int64_t len = (jj < p) ? min(max(o_len[jj] - b, (int64_t)0), kPull) : 0;
+        const bool vec = (o_lo[jj] % V) == 0;
+        const __amdgpu_buffer_rsrc_t src =
+            out_rsrc(a.y[jj < p ? (r + jj) % p : r], (o_lo[jj] + b) * E, len * E);
+        const int64_t off = (int64_t)tid * V;
+        full[jj] = jj < p && vec && off + V <= len;
+        if (full[jj]) w[jj] = __builtin_amdgcn_raw_buffer_load_b128(src, (int)(off * E), 0, kLd);
+      }
+#pragma unroll
+      for (int jj = 1; jj < MAXP; jj++) {
+        if (jj >= p) continue;
+        const int64_t len = min(max(o_len[jj] - b, (int64_t)0), kPull);
+        const int64_t base = o_lo[jj] + b;
+        const __amdgpu_buffer_rsrc_t src = out_rsrc(a.y[(r + jj) % p], base * E, len * E);
+        {
+          const int64_t off = (int64_t)tid * V;
+          if (full[jj]) {
+            st16(yr, (base + off) * E, w[jj]);
+          } else if (off < len) {  // ragged: element by element
             const int cnt = (int)min((int64_t)V, len - off);
             for (int e = 0; e < cnt; e++) {
               const int yoff = (int)((off + e) * E);

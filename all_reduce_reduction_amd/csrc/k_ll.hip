@@ -23,8 +23,12 @@
 // co-resident (the host caps the grid at the occupancy limit), so every
 // poll is answered.  A lane issues its p polls together and re-polls only
 // the packets still missing, at most spin_limit rounds; on expiry it
-// records SIM_ERR_TIMEOUT in the device error word, skips its writes and
-// the kernel exits normally.
+// records SIM_ERR_TIMEOUT in the device error word and raises its
+// workgroup's give-up flag, and from then on every lane of the workgroup
+// skips its remaining waits and writes (the outputs are undefined after a
+// timeout anyway): a workgroup that holds many words -- a small grid under a
+// workgroup budget -- gives up after one spin limit, not one per word.  The
+// kernel exits normally.
 #include "device_common.h"
 #include "kernels.h"
 #include "launch.h"
@@ -60,10 +64,17 @@ __global__ void __launch_bounds__(kBlock) k_ll(LLArgs a) {
   }
 
   // ---- consume ----------------------------------------------------------------
+  // give-up flag of the workgroup: set (to 1 only) by any lane whose wait
+  // expired, read by every lane before each word; a lane that reads it late
+  // spends at most one more wait
+  __shared__ int give_up;
+  if (threadIdx.x == 0) give_up = 0;
+  __syncthreads();
   for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
     const int64_t tile = (t + a.shift) % a.ntiles;
     const int64_t kend = min(nwords, (tile + 1) * a.tile_words);
     for (int64_t k = tile * a.tile_words + threadIdx.x; k < kend; k += kBlock) {
+      if (__hip_atomic_load(&give_up, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) break;
       // issue the p polls back to back (one memory round trip when every
       // packet is already there), then re-poll only the packets still missing
       unsigned long long pk[SIM_MAX_RANKS];
@@ -90,7 +101,8 @@ __global__ void __launch_bounds__(kBlock) k_ll(LLArgs a) {
       }
       if (!ok) {
         __hip_atomic_store(a.err, (int)SIM_ERR_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        continue;
+        __hip_atomic_store(&give_up, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        break;
       }
       uint32_t d[SIM_MAX_RANKS];
 #pragma unroll

@@ -172,6 +172,47 @@ def test_forced_timeout_reports_and_recovers(lib, orc):
         assert (got[r] == want[r]).all()
 
 
+def test_ll_timeout_gives_up_once_per_workgroup(lib, orc):
+    """Under a 4-workgroup budget each lane of the LL one-shot holds 64 words
+    at 1 MiB per rank.  With every wait made to expire, a workgroup stops at
+    its first expired wait: the call ends after about one spin limit, not
+    one per word (64 of them), reports SIM_ERR_TIMEOUT, and the next call is
+    correct."""
+    import time
+    import torch
+    from tests.gpu_util import empty_like_poisoned, ptrs, run_allreduce, stream, to_device
+    sim = lib
+    xs, want = _ll_case(orc, n=(1 << 20) // 2, seed=4)
+    din = to_device(xs, "fp16")
+    dout = empty_like_poisoned(xs[0].size, "fp16", 8)
+    spin = 4000
+    try:
+        sim.sim_config_set("max_workgroups", 4)
+        sim.sim_debug_set("spin_limit", spin)
+        # one expiring call with a single word per lane, to time one spin limit
+        one = [x[: 4 * 256 * 2].copy() for x in xs]
+        d1, o1 = to_device(one, "fp16"), empty_like_poisoned(one[0].size, "fp16", 8)
+        sim.sim_debug_set("ll_wait_skew", 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        assert sim.sim_allreduce(ptrs(d1), ptrs(o1), 8, one[0].size, "fp16", "sum", "oneshot_ll", stream()) == OK
+        assert sim.sim_check_error(stream()) == TIMEOUT
+        t_one = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        assert sim.sim_allreduce(ptrs(din), ptrs(dout), 8, xs[0].size, "fp16", "sum", "oneshot_ll", stream()) == OK
+        assert sim.sim_check_error(stream()) == TIMEOUT
+        t_many = time.perf_counter() - t0
+        print(f"one word per lane {t_one * 1e3:.2f} ms, 64 words per lane {t_many * 1e3:.2f} ms", flush=True)
+        assert t_many < 8 * t_one + 0.02, (t_one, t_many)
+    finally:
+        sim.sim_debug_set("ll_wait_skew", 0)
+        sim.sim_debug_set("spin_limit", 1 << 20)
+        sim.sim_config_set("max_workgroups", 0)
+    got = run_allreduce(xs, "fp16", "sum", "oneshot_ll")
+    for r in range(8):
+        assert (got[r] == want[r]).all()
+
+
 def test_auto_reports_what_ran_and_logs(lib, capfd):
     from tests.gpu_util import ptrs, stream
     sim = lib
