@@ -284,6 +284,7 @@ def ceiling(sim, torch, dev, stream, steps: int, head_sets) -> dict:
         "workgroups": wg or "cover", "what": "the 8 headline inputs copied to the 8 headline outputs (64 MiB each)",
         "GBps_by_workgroups": {str(w or "cover"): round(2 * P * S / t / 1e9, 1) for w, t in res.items()}}
     out["copy_8in_8out_64MiB_each"] = best_copy(8, S)
+    out["copy_8in_8out_256MiB_each"] = best_copy(8, 256 << 20)  # workload 5's streams (4 GiB working set)
     out["copy_1in_1out_1GiB"] = best_copy(1, total)
     out["constant_data"] = {"copy_8in_8out_64MiB_each": best_copy(8, S, True),
                             "copy_1in_1out_1GiB": best_copy(1, total, True)}
@@ -691,6 +692,9 @@ def main():
         cf = max(extras["ceiling"]["copy_8in_8out_64MiB_each"]["GBps"],
                  extras["ceiling"]["copy_headline_buffers"]["GBps"])
         extras["ceiling"]["oneshot_over_8x8_copy"] = round(achieved / cf, 4) if ran == "oneshot" else None
+        w5 = extras["workload5_256MiB"]["allreduce"]["fp32 avg"]
+        extras["ceiling"]["workload5_oneshot_over_its_8x8_copy"] = round(
+            w5["hbm_algorithmic_GBps"] / extras["ceiling"]["copy_8in_8out_256MiB_each"]["GBps"], 4)
 
     cpu = None
     if not args.no_cpu_baseline:
