@@ -213,6 +213,39 @@ def test_ll_timeout_gives_up_once_per_workgroup(lib, orc):
         assert (got[r] == want[r]).all()
 
 
+def test_environment_overrides(lib, tmp_path):
+    """SIM_ALGO names the schedule AUTO runs (an A/B switch; explicit algos
+    are untouched) and SIM_CALIB names the model file sim_init loads; both are
+    read at sim_init."""
+    import json
+    import os
+    import torch
+    from tests.gpu_util import ptrs, stream
+    sim = lib
+    model = tmp_path / "model.json"
+    model.write_text(json.dumps({"algos": {"oneshot": {"alpha_us": 7.5, "gbps": 1000.0}}}))
+    saved = {k: os.environ.get(k) for k in ("SIM_ALGO", "SIM_CALIB")}
+    try:
+        os.environ["SIM_ALGO"] = "allpairs"
+        os.environ["SIM_CALIB"] = str(model)
+        sim.sim_init(0, 16, 0)
+        ins, outs = _bufs(8, 8192)
+        assert sim.sim_allreduce(ptrs(ins), ptrs(outs), 8, 8192, "fp32", "sum", "auto", stream()) == OK
+        assert sim.sim_last_algo() == "allpairs"
+        assert sim.sim_allreduce(ptrs(ins), ptrs(outs), 8, 8192, "fp32", "sum", "ring", stream()) == OK
+        assert sim.sim_last_algo() == "ring"
+        assert sim.sim_model_predict("oneshot", 8, "fp32", 1 << 20) == pytest.approx(7.5 + 16 * (1 << 20) / 1e6)
+        torch.cuda.synchronize()
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+        sim.sim_init(0, 16, 0)   # back to the packaged calibration, no override
+    assert sim.sim_model_predict("oneshot", 8, "fp32", 1 << 20) != pytest.approx(7.5 + 16 * (1 << 20) / 1e6)
+
+
 def test_auto_reports_what_ran_and_logs(lib, capfd):
     from tests.gpu_util import ptrs, stream
     sim = lib
