@@ -23,11 +23,15 @@ under budgets of 16 .. 128 workgroups and fits the rate one workgroup
 sustains (wg_gbps), which the model uses under a budget (see sim_select in
 include/simar.h).  The check runs at budgets none, 128 and 32.  Besides the
 argmin it reports, per case, every schedule's predicted and measured time,
-the relative error of each prediction, and how many pairs of schedules the
+the relative error of each prediction, how many pairs of schedules the
 model ranks in the measured order (pairs measured within the tolerance of
-each other count as ties): on one HBM the one-shot is expected to be the
-fastest at every size, so the argmin alone could not tell a working model
-from a constant pick, while the ranking and the errors can.
+each other count as ties), and the runner-up: the model's argmin over the
+schedules left once the measured fastest is removed, against the measured
+one.  On one HBM the one-shot is expected to be the fastest at every size,
+so the argmin alone could not tell a working model from a constant pick;
+the pairwise ranking and the errors can.  (On MI355X the measured runner-up
+is the two-launch all-pairs at every checked size and budget, so it adds one
+ordering, not a test of its own.)
 
 Buffers: every measurement rotates over up to 8 sets of rank buffers, as
 many as keep the working set of consecutive calls at 512 MiB or more
@@ -368,7 +372,7 @@ def check(model_path: str, steps_scale: float = 1.0, budgets=CHECK_BUDGETS, reps
     for budget in budgets:
         sim.sim_config_set("max_workgroups", budget)
         rows = []
-        strict = tolerant = agree = pairs = 0
+        strict = tolerant = agree = pairs = ru_strict = ru_tolerant = 0
         errs = []
         for dtype, n in cases:
             nbytes = n * sim.ESIZE[dtype]
@@ -383,6 +387,14 @@ def check(model_path: str, steps_scale: float = 1.0, budgets=CHECK_BUDGETS, reps
             s_ok = pick == best
             t_ok = meas[pick] <= meas[best] * (1 + tol)
             ag, pt = _pairs_agree(pred, meas, max(0.03, max(spreads.values())))
+            # the runner-up: the model's argmin over the schedules left once the
+            # measured fastest is taken out, against the measured one
+            rest = [a for a in meas if a != best]
+            ru_pick = min(rest, key=lambda a: pred[a])
+            ru_best = min(rest, key=lambda a: meas[a])
+            ru_tol = max(0.03, spreads[ru_best], spreads[ru_pick])
+            ru_strict += ru_pick == ru_best
+            ru_tolerant += meas[ru_pick] <= meas[ru_best] * (1 + ru_tol)
             strict += s_ok
             tolerant += t_ok
             agree += ag
@@ -393,12 +405,14 @@ def check(model_path: str, steps_scale: float = 1.0, budgets=CHECK_BUDGETS, reps
                          "measured_best": best, "measured_us": {a: round(v, 2) for a, v in meas.items()},
                          "predicted_us_all": {a: round(v, 2) for a, v in pred.items()},
                          "rel_error": err, "strict": s_ok, "tolerant": t_ok,
+                         "runner_up_pick": ru_pick, "runner_up_measured": ru_best,
                          "pairs_agree": ag, "pairs": pt})
             print(f"check budget {budget or 'none':>4} {dtype} {nbytes:>9d} B/rank pick {pick:10s} "
                   f"best {best:10s} err(pick) {err[pick]:+.3f} pairs {ag}/{pt} "
                   + " ".join(f"{a}={v:.1f}" for a, v in meas.items()), flush=True)
         by_budget["none" if budget == 0 else str(budget)] = {
             "cases": len(cases), "strict_matches": strict, "tolerant_matches": tolerant,
+            "runner_up_strict": ru_strict, "runner_up_tolerant": ru_tolerant,
             "pairs_agree": agree, "pairs": pairs,
             "pick_rel_error_median": round(float(statistics.median(errs)), 4),
             "pick_rel_error_max": round(max(errs), 4), "rows": rows}
@@ -408,6 +422,7 @@ def check(model_path: str, steps_scale: float = 1.0, budgets=CHECK_BUDGETS, reps
               "tolerant_matches": by_budget["none"]["tolerant_matches"] if "none" in by_budget else None,
               "budgets": by_budget}
     print(json.dumps({"selector_check": {k: {kk: v[kk] for kk in ("cases", "strict_matches", "tolerant_matches",
+                                                                    "runner_up_strict", "runner_up_tolerant",
                                                                     "pairs_agree", "pairs", "pick_rel_error_median",
                                                                     "pick_rel_error_max")}
                                          for k, v in by_budget.items()}}), flush=True)

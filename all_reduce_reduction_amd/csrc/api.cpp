@@ -40,6 +40,11 @@ constexpr int kPtrSets = 512;
 // 1 to 64 KiB per rank against 24-32 us for the FIFO protocol, 21.8 against
 // 44.7 us at 128 KiB and 37.4 against 45.3 us at 256 KiB.
 constexpr size_t kRingLLMaxBytes = 256 << 10;
+// The phased one-shot (k_phased.hip) from this many bytes per rank on.
+// Measured on MI355X, p = 8 bf16, against the fused one-shot: 16 MiB 52.4
+// against 44.9 us, 32 MiB 89.5 against 93.3, 64 MiB 174 against 196,
+// 128 MiB 353 against 386, 256 MiB 711 against 759.
+constexpr size_t kPhasedMinBytes = 32 << 20;
 
 // A call's rank pointers as a hash key (p, then x[0..p), y[0..p)).
 struct PtrKey {
@@ -113,6 +118,21 @@ struct Ctx {
   // the single-launch ring runs its LL protocol up to this many bytes per rank
   size_t ring_ll_max = kRingLLMaxBytes;
   int ap_occ[4][5][2] = {};  // persistent all-pairs: [dtype][op][p == 8]
+  // phased one-shot: barrier slots (per slot an arrival counter, then
+  // ph_gmax release flags kPhasedFlagStride words apart), the count of
+  // barrier waits that gave up, and per slot the counter and flag values
+  // the next call starts from
+  unsigned long long* ph_mem = nullptr;
+  int64_t ph_slot_words = 0;
+  int ph_gmax = 0;
+  unsigned int* ph_expired = nullptr;
+  unsigned long long ph_ctr[kPhasedSlots] = {};
+  unsigned long long ph_seq[kPhasedSlots] = {};
+  unsigned ph_next = 0;
+  int ph_occ[4][5][5] = {};  // [dtype][op][log2 p - 1]: resident workgroups per CU (-1: none)
+  int phased_mode = 0;       // 0: from phased_min bytes per rank on, 1: always, 2: never
+  size_t phased_min = kPhasedMinBytes;
+  bool last_phased = false;  // the last one-shot ran phased (for the call log)
   Model model = default_model();
 };
 
@@ -252,15 +272,17 @@ struct Call {
 // Measured on MI355X: streaming kernels run fastest with one short-lived
 // workgroup per kBlock * unroll vectors (many waves in flight), so the
 // default covers the transfer exactly.  The calibration's launch table, when
-// it has an entry for this algo, replaces that with the measured best total
-// for the nearest message size; SIM_CONFIG_MAX_WORKGROUPS caps the total
+// it has an entry for this algo and was measured at this call's rank count,
+// replaces that with the measured best total for the nearest message size
+// (at p = 8 the one-shot's 2p streams per workgroup keep enough bytes in
+// flight with far fewer workgroups than at p = 2); SIM_CONFIG_MAX_WORKGROUPS caps the total
 // (T-CCL's restricted mode: communication given a fixed slice of the GPU);
 // SIM_DEBUG_WORKGROUPS forces a total.
 // 16-byte vectors per lane per pass of a bulk kernel: forced by the debug
 // hook, else the calibration's launch table entry for this call, else 1.
 int unroll_for(const Call& c) {
   if (g.unroll > 0) return g.unroll;
-  const int u = model_launch(g.model, c.algo, (double)c.n * esize_of(c.dtype)).unroll;
+  const int u = model_launch(g.model, c.algo, c.p, (double)c.n * esize_of(c.dtype)).unroll;
   return u > 0 ? u : 1;
 }
 
@@ -270,7 +292,7 @@ int tiles_for(const Call& c, int64_t vecs_per_unit, int units, int unroll) {
     t = g.force_wg / units;
   } else {
     t = (vecs_per_unit + (int64_t)kBlock * unroll - 1) / ((int64_t)kBlock * unroll);
-    const int total = model_workgroups(g.model, c.algo, (double)c.n * esize_of(c.dtype));
+    const int total = model_workgroups(g.model, c.algo, c.p, (double)c.n * esize_of(c.dtype));
     if (total > 0) t = std::min<int64_t>(t, std::max(1, total / units));
   }
   if (g_max_wg > 0) t = std::min<int64_t>(t, g_max_wg / units);
@@ -347,7 +369,8 @@ int run_fold(const Call& c, bool all_out, const int64_t* lo, const int64_t* out_
   for (int q = 0; q <= c.p; q++) a.lo[q] = lo[q];
   a.p = c.p;
   a.inv_p = inv_p_of(c.p);
-  const int unroll = (c.p == 8) ? unroll_for(c) : 1;  // the p = 8 kernels have a 2-vector form
+  // the fold forms for p = 2, 4 and 8 have a 2-vector form
+  const int unroll = (c.p == 2 || c.p == 4 || c.p == 8) ? unroll_for(c) : 1;
   a.tiles = tiles_for(c, (maxchunk + V - 1) / V, c.p, unroll);
   if (set && out_shift == nullptr) {
     FoldTabArgs t;
@@ -360,6 +383,72 @@ int run_fold(const Call& c, bool all_out, const int64_t* lo, const int64_t* out_
     return hip_err(launch_fold_tab(c.dtype, c.op, c.p, all_out, t, unroll, c.s));
   }
   return hip_err(launch_fold(c.dtype, c.op, c.p, all_out, a, unroll, c.s));
+}
+
+// The phased one-shot, when this call may use it: p = 2, 4, 8 or 16, no
+// workgroup budget, not under graph capture (the barrier counts are fixed
+// at enqueue time) and not the allocation-free entry point; by default from
+// phased_min bytes per rank on.  Returns SIM_OK after enqueueing it, a
+// negative value when the call should take the fused one-shot instead, or
+// an error.
+int run_fold_phased(const Call& c, const int64_t* lo) {
+  g.last_phased = false;
+  const int p = c.p;
+  if (!g.ph_mem || c.noalloc || g.capturing || g_max_wg > 0 || g.phased_mode == 2) return -1;
+  if (p != 2 && p != 4 && p != 8 && p != 16) return -1;
+  const int E = esize_of(c.dtype);
+  if (g.phased_mode == 0 && c.n * (size_t)E < g.phased_min) return -1;
+  const int pi = p == 2 ? 0 : p == 4 ? 1 : p == 8 ? 2 : 3;
+  int& occ = g.ph_occ[c.dtype][c.op][pi];
+  if (occ == 0) {
+    occ = fold_phased_blocks_per_cu(c.dtype, c.op, p);
+    if (occ < 1) occ = -1;
+  }
+  if (occ < 1) return -1;
+  // every workgroup resident at once: at most two per CU (the VGPR budget
+  // of a phase's results), fewer if the kernel fits fewer
+  int64_t G = (int64_t)std::min(occ, 2) * g.cu_count;
+  if (g.force_wg > 0) G = std::min<int64_t>(G, g.force_wg);
+  G = std::min<int64_t>(G, g.ph_gmax);
+  const int64_t tiles = std::max<int64_t>(1, G / p);
+  G = tiles * p;
+  if (G > g.ph_gmax) return -1;
+  // whole spans of the largest chunk (a chunk's rest is done after the phases)
+  const int V = 16 / E;
+  const int64_t span = (int64_t)kBlock * fold_phased_vecs_per_lane(p);
+  int64_t nfull = 0;
+  for (int q = 0; q < p; q++) {
+    int64_t head = (V - lo[q] % V) % V;
+    head = std::min(head, lo[q + 1] - lo[q]);
+    const int64_t nvec = (lo[q + 1] - lo[q] - head) / V;
+    nfull = std::max(nfull, nvec / span);
+  }
+  const int64_t nphase = (nfull + tiles - 1) / tiles;
+  const int64_t nbar = nphase > 0 ? 2 * nphase - 1 : 0;
+  PhasedArgs a;
+  std::memset(&a, 0, sizeof a);
+  for (int q = 0; q < p; q++) {
+    a.x[q] = c.x[q];
+    a.y[q] = c.y[q];
+  }
+  for (int q = 0; q <= p; q++) a.lo[q] = lo[q];
+  const unsigned slot = g.ph_next++ % kPhasedSlots;
+  a.ctr = g.ph_mem + (int64_t)slot * g.ph_slot_words;
+  a.flags = a.ctr + kPhasedFlagStride;
+  a.base = g.ph_ctr[slot];
+  a.seq = g.ph_seq[slot];
+  a.spin_limit = g.spin_limit;
+  a.expired = g.ph_expired;
+  a.tiles = (int)tiles;
+  a.nphase = (int)nphase;
+  a.inv_p = inv_p_of(p);
+  const int rc = hip_err(launch_fold_phased(c.dtype, c.op, p, a, c.s));
+  if (rc) return rc;
+  // the counts this call's barriers add (every workgroup meets every barrier)
+  g.ph_ctr[slot] += (unsigned long long)nbar * (unsigned long long)G;
+  g.ph_seq[slot] += (unsigned long long)nbar;
+  g.last_phased = true;
+  return SIM_OK;
 }
 
 int run_copy_step(const Call& c, const CopyXfer* xs, int count) {
@@ -797,8 +886,11 @@ int run_allreduce(const Call& c) {
   int64_t lo[SIM_MAX_RANKS + 1];
   for (int q = 0; q <= p; q++) lo[q] = chunk_lo((int64_t)c.n, p, q);
   switch (c.algo) {
-    case SIM_ALGO_ONESHOT:
+    case SIM_ALGO_ONESHOT: {
+      const int rc = run_fold_phased(c, lo);
+      if (rc >= 0) return rc;
       return run_fold(c, true, lo, nullptr, ptr_set_for(c));
+    }
     case SIM_ALGO_ALLPAIRS: {
       const PtrSet* set = ptr_set_for(c);
       int rc = run_fold(c, false, lo, nullptr, set);  // step 1: GATHER_REDUCE into each owner
@@ -1030,8 +1122,9 @@ int begin_call(void* stream) {
 
 void log_call(const char* what, const Call& c, double us) {
   if (!g.log) return;
-  std::fprintf(stderr, "[simar] %s: %zu bytes/rank p %d -> algo %s steps %d predicted %.2f us\n", what,
+  std::fprintf(stderr, "[simar] %s: %zu bytes/rank p %d -> algo %s%s steps %d predicted %.2f us\n", what,
                c.n * (size_t)esize_of(c.dtype), c.p, algo_name(c.algo),
+               (c.algo == SIM_ALGO_ONESHOT && g.last_phased) ? " (phased)" : "",
                model_launches(c.coll, c.algo, c.p, g_topo), us);
 }
 
@@ -1069,7 +1162,8 @@ const char* sim_status_string(int status) {
 
 int sim_finalize(void) {
   // (also releases what a failed sim_init had allocated before it gave up)
-  if (!g.init && !g.err && !g.ll && !g.fifo_sem && !g.scratch && !g.ptab && !g.ptab_host) return SIM_OK;
+  if (!g.init && !g.err && !g.ll && !g.fifo_sem && !g.scratch && !g.ptab && !g.ptab_host && !g.ph_mem)
+    return SIM_OK;
   // teardown is best effort: every allocation is released even if one call fails
   (void)hipSetDevice(g.device);
   (void)hipDeviceSynchronize();
@@ -1078,6 +1172,7 @@ int sim_finalize(void) {
   if (g.ll) (void)hipFree(g.ll);
   if (g.fifo) (void)hipFree(g.fifo);
   if (g.fifo_sem) (void)hipFree(g.fifo_sem);
+  if (g.ph_mem) (void)hipFree(g.ph_mem);
   if (g.err) (void)hipFree(g.err);
   for (PtrSlot& sl : g.ptab_slots)
     if (sl.done) (void)hipEventDestroy(sl.done);
@@ -1126,6 +1221,19 @@ int sim_init(int device, int p_max, size_t max_bytes_per_rank) {
     sim_finalize();
     return SIM_ERR_HIP;
   }
+  // phased one-shot barrier slots, zeroed (the expired count sits after them)
+  g.ph_gmax = 2 * g.cu_count;
+  g.ph_slot_words = (int64_t)(g.ph_gmax + 1) * kPhasedFlagStride;
+  const int64_t ph_words = g.ph_slot_words * kPhasedSlots + kPhasedFlagStride;
+  if (hipMalloc(&g.ph_mem, (size_t)ph_words * 8) != hipSuccess) {
+    sim_finalize();
+    return SIM_ERR_NOMEM;
+  }
+  if (launch_fill64(g.ph_mem, 0ull, ph_words, nullptr) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    sim_finalize();
+    return SIM_ERR_HIP;
+  }
+  g.ph_expired = (unsigned int*)(g.ph_mem + g.ph_slot_words * kPhasedSlots);
   // the pointer table only makes launches cheaper: without it every call
   // carries its pointers in its kernel arguments
   if (hipMalloc(&g.ptab, sizeof(PtrSet) * kPtrSets) != hipSuccess ||
@@ -1600,6 +1708,19 @@ int sim_debug_set(int key, uint64_t value) {
     case SIM_DEBUG_FIFO_WITHHOLD: g.fifo_withhold = value ? 1 : 0; return SIM_OK;
     case SIM_DEBUG_PTR_TABLE: g.ptab_on = value ? 1 : 0; return SIM_OK;
     case SIM_DEBUG_RING_LL_MAX: g.ring_ll_max = (size_t)value; return SIM_OK;
+    case SIM_DEBUG_PHASED:
+      if (value > 2) return SIM_ERR_INVALID_ARG;
+      g.phased_mode = (int)value;
+      return SIM_OK;
+    case SIM_DEBUG_PHASED_MIN: g.phased_min = (size_t)value; return SIM_OK;
+    case SIM_DEBUG_PHASED_EXPIRED: {
+      if (value != 0) return SIM_ERR_INVALID_ARG;
+      if (!g.init) return SIM_ERR_NOT_INIT;
+      if (use_device() != SIM_OK || hipDeviceSynchronize() != hipSuccess ||
+          hipMemset(g.ph_expired, 0, sizeof(unsigned int)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        return SIM_ERR_HIP;
+      return SIM_OK;
+    }
     case SIM_DEBUG_FIFO_VECS:
       if (value != 1 && value != 2 && value != (uint64_t)kFifoVecsPerLane) return SIM_ERR_INVALID_ARG;
       g.fifo_vecs = (int)value;
@@ -1640,6 +1761,18 @@ int sim_debug_get(int key, uint64_t* value) {
     case SIM_DEBUG_PTR_TABLE: *value = (uint64_t)g.ptab_on; return SIM_OK;
     case SIM_DEBUG_PTR_SETS: *value = (uint64_t)g.ptab_index.size(); return SIM_OK;
     case SIM_DEBUG_RING_LL_MAX: *value = (uint64_t)g.ring_ll_max; return SIM_OK;
+    case SIM_DEBUG_PHASED: *value = (uint64_t)g.phased_mode; return SIM_OK;
+    case SIM_DEBUG_PHASED_MIN: *value = (uint64_t)g.phased_min; return SIM_OK;
+    case SIM_DEBUG_PHASED_LAST: *value = g.last_phased ? 1 : 0; return SIM_OK;
+    case SIM_DEBUG_PHASED_EXPIRED: {
+      if (!g.init) return SIM_ERR_NOT_INIT;
+      unsigned int v = 0;
+      if (use_device() != SIM_OK || hipDeviceSynchronize() != hipSuccess ||
+          hipMemcpy(&v, g.ph_expired, sizeof v, hipMemcpyDeviceToHost) != hipSuccess)
+        return SIM_ERR_HIP;
+      *value = v;
+      return SIM_OK;
+    }
   }
   return SIM_ERR_INVALID_ARG;
 }

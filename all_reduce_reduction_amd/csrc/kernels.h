@@ -233,6 +233,29 @@ struct SchedArgs {
 
 // k independent streaming copies (the ceiling of the one-shot's access
 // pattern): dst[q][0 .. 16 nvec) = src[q][0 .. 16 nvec) for q < k.
+// The phased one-shot (k_phased.hip): the grid folds a phase's spans into
+// VGPRs, meets at a grid barrier, writes them out, and meets again before
+// the next phase.  Barrier state lives in one of kPhasedSlots slots (the
+// host takes them in turn, call by call): an arrival counter and one release
+// flag per workgroup, kPhasedFlagStride 64-bit words (256 bytes) apart.
+constexpr int kPhasedSlots = 4;
+constexpr int kPhasedFlagStride = 32;
+struct PhasedArgs {
+  const void* x[SIM_MAX_RANKS];
+  void* y[SIM_MAX_RANKS];
+  int64_t lo[SIM_MAX_RANKS + 1];  // chunk bounds
+  unsigned long long* ctr;        // the slot's arrival counter
+  unsigned long long* flags;      // the slot's release flags
+  unsigned long long base;        // the counter's value when this call starts
+  unsigned long long seq;         // the flags' value when this call starts
+  unsigned long long spin_limit;  // polls before a barrier wait gives up
+  unsigned int* expired;          // barrier waits that gave up (timing only, not an error)
+  int tiles;                      // workgroups per chunk (grid = tiles * p)
+  int nphase;
+  float inv_p;
+  int pad_;
+};
+
 struct CopyStreamsArgs {
   const void* src[SIM_MAX_RANKS];
   void* dst[SIM_MAX_RANKS];
@@ -243,6 +266,7 @@ struct CopyStreamsArgs {
 
 static_assert(sizeof(FoldArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(CopyStreamsArgs) <= 4096, "kernel argument segment too large");
+static_assert(sizeof(PhasedArgs) <= 4096, "kernel argument segment too large");
 static_assert(sizeof(FoldTabArgs) <= 64, "must fit the small-argument launch path");
 static_assert(sizeof(FanoutTabArgs) <= 64, "must fit the small-argument launch path");
 static_assert(sizeof(RingTabArgs) <= 64, "must fit the small-argument launch path");
@@ -283,5 +307,10 @@ hipError_t launch_ring_ll(int dtype, int op, const RingLLArgs& a, hipStream_t s)
 int ring_ll_blocks_per_cu(int dtype, int op);
 hipError_t launch_allpairs_persistent(int dtype, int op, const AllPairsPArgs& a, hipStream_t s);
 int allpairs_persistent_blocks_per_cu(int dtype, int op, int p);
+// The phased one-shot for p = 2, 4, 8 or 16 (hipErrorInvalidValue otherwise),
+// its resident workgroups per CU, and its result vectors per lane per phase.
+hipError_t launch_fold_phased(int dtype, int op, int p, const PhasedArgs& a, hipStream_t s);
+int fold_phased_blocks_per_cu(int dtype, int op, int p);
+int fold_phased_vecs_per_lane(int p);
 
 }  // namespace simar

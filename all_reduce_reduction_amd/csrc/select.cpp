@@ -39,7 +39,7 @@ Model default_model() {
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0, 0.0, 0.0};
   m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.5, 2.8};
   m.a[SIM_ALGO_ALLPAIRS] = {1.9, 5650.0, -1.0, -1.0, 43.5, 3.0};
-  m.a[SIM_ALGO_ONESHOT] = {1.25, 5650.0, -1.0, -1.0, 49.0, 3.2};
+  m.a[SIM_ALGO_ONESHOT] = {1.5, 6000.0, -1.0, -1.0, 47.3, 3.2};
   m.a[SIM_ALGO_ONESHOT_LL] = {8.65, 12500.0, -1.0, -1.0, 8.6, 0.0};
   m.a[SIM_ALGO_RING_FIFO] = {14.2, 6350.0, -1.0, -1.0, 16.0, 0.0};
   m.a[SIM_ALGO_TREE] = {3.1, 6200.0, -1.0, -1.0, 0.0, 4.1};
@@ -151,9 +151,10 @@ double model_traffic(int coll, int algo, int p, double n, int esize, const Topol
   return 0.0;
 }
 
-LaunchEntry model_launch(const Model& m, int algo, double bytes_per_rank) {
+LaunchEntry model_launch(const Model& m, int algo, int p, double bytes_per_rank) {
   LaunchEntry best;
   if (algo <= 0 || algo >= kNumAlgos || m.wg[algo].empty() || !(bytes_per_rank > 0)) return best;
+  if (m.wg_p > 0 && p != m.wg_p) return best;
   const double lb = std::log2(bytes_per_rank);
   double bd = 0;
   bool found = false;
@@ -168,8 +169,8 @@ LaunchEntry model_launch(const Model& m, int algo, double bytes_per_rank) {
   return best;
 }
 
-int model_workgroups(const Model& m, int algo, double bytes_per_rank) {
-  return model_launch(m, algo, bytes_per_rank).total;
+int model_workgroups(const Model& m, int algo, int p, double bytes_per_rank) {
+  return model_launch(m, algo, p, bytes_per_rank).total;
 }
 
 // A workgroup budget (T-CCL's restricted mode, "T-CCL ...", sections III-C3
@@ -408,6 +409,17 @@ bool model_load_json(const char* path, Model* m, std::string* err) {
       }
       out.a[a].wg_gbps = wr->second.num;
     }
+  }
+  // optional: the rank count the launch table was measured at
+  out.wg_p = 0;
+  auto pt = root.obj.find("p");
+  if (pt != root.obj.end()) {
+    if (pt->second.kind != JVal::NUM || !(pt->second.num >= 2 && pt->second.num <= SIM_MAX_RANKS) ||
+        pt->second.num != std::floor(pt->second.num)) {
+      if (err) *err = "p must be an integer rank count in 2..16";
+      return false;
+    }
+    out.wg_p = (int)pt->second.num;
   }
   // optional launch-configuration table: "workgroups": {algo: [[bytes, total], ...]}
   auto wt = root.obj.find("workgroups");

@@ -36,15 +36,19 @@ struct Model {
   // per algo, entries from the calibration sweep, ascending in bytes; empty
   // = cover every transfer exactly with one vector per lane.
   std::vector<LaunchEntry> wg[kNumAlgos];
+  // the rank count the table was measured at: a call with another count
+  // ignores it (0: the table applies to every count)
+  int wg_p = 0;
   std::string source = "built-in defaults";
 };
 
-// The table's entry for (algo, bytes per rank): the one of the nearest size
-// on a log scale; a default entry (total 0, unroll 0) when the table has
-// none.
-LaunchEntry model_launch(const Model& m, int algo, double bytes_per_rank);
+// The table's entry for (algo, p ranks, bytes per rank): the one of the
+// nearest size on a log scale; a default entry (total 0, unroll 0) when the
+// table has none or was measured at another rank count (a total tuned for
+// p = 8 ranks' 2p streams per workgroup starves a launch at p = 2).
+LaunchEntry model_launch(const Model& m, int algo, int p, double bytes_per_rank);
 // Its total workgroups (0: cover the transfer).
-int model_workgroups(const Model& m, int algo, double bytes_per_rank);
+int model_workgroups(const Model& m, int algo, int p, double bytes_per_rank);
 
 Model default_model();
 

@@ -25,7 +25,8 @@ Printed JSON line:
                  same run: the library's k-stream copy (sim_copy_streams) with
                  8 inputs and 8 outputs of 64 MiB (the one-shot's streams and
                  bytes, no arithmetic) and with 1 input and 1 output of 1 GiB,
-                 and hipMemcpyAsync device-to-device of 1 GiB (torch's copy_)
+                 and hipMemcpyAsync device-to-device of 1 GiB (torch's copy_);
+                 and the one-shot next to that copy at p = 2, 4, 8, 16
   workload2_fp32_32MiB, workload5_256MiB
                  the parity workloads' timed figures next to the CPU oracle's
                  time for the same call (all host threads, and one thread on a
@@ -156,7 +157,9 @@ def time_calls(fn, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / 1e3 / steps
 
 
-KERNEL_SOURCES = ["all_reduce_reduction_amd/csrc/k_fold.hip", "all_reduce_reduction_amd/csrc/k_step.hip",
+KERNEL_SOURCES = ["all_reduce_reduction_amd/csrc/k_phased.hip", "all_reduce_reduction_amd/csrc/k_fold.hip",
+                  "all_reduce_reduction_amd/csrc/fold_impl.h",
+                  "all_reduce_reduction_amd/csrc/fold.h", "all_reduce_reduction_amd/csrc/k_step.hip",
                   "all_reduce_reduction_amd/csrc/k_streams.hip",
                   "all_reduce_reduction_amd/csrc/device_common.h", "all_reduce_reduction_amd/csrc/kernels.h"]
 
@@ -421,6 +424,37 @@ def workload5(sim, synthdata, oracle, torch, np, dev, stream, steps: int, cpu: b
     return res
 
 
+def oneshot_by_p(sim, torch, dev, stream, steps: int) -> dict:
+    """The one-shot at 64 MiB per rank, bf16, for p = 2, 4, 8, 16 (workload
+    3's values), each next to the k-stream copy of the same p input and p
+    output buffers (its access pattern without the fold)."""
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    for p in (2, 4, 8, 16):
+        ins = [(torch.randn(N, device=dev, generator=g) * 0.02).to(torch.bfloat16).view(torch.int16)
+               for _ in range(p)]
+        outs = [torch.empty_like(ins[0]) for _ in range(p)]
+        ip, op_ = [t.data_ptr() for t in ins], [t.data_ptr() for t in outs]
+
+        def ar():
+            if sim.sim_allreduce(ip, op_, p, N, "bf16", "sum", "oneshot", stream):
+                raise sim.SimError(-1, "sim_allreduce")
+
+        def cp():
+            if sim.sim_copy_streams(ip, op_, p, S, 0, stream):
+                raise sim.SimError(-1, "sim_copy_streams")
+        t_ar, t_cp = time_calls(ar, steps, 3), time_calls(cp, steps, 3)
+        law = 2.0 * p * S
+        out[str(p)] = {"oneshot_us": round(t_ar * 1e6, 2), "oneshot_frac": round(law / t_ar / 1e9 / HBM_PEAK_GBPS, 4),
+                       "copy_us": round(t_cp * 1e6, 2), "copy_frac": round(law / t_cp / 1e9 / HBM_PEAK_GBPS, 4),
+                       "oneshot_over_copy": round(t_cp / t_ar, 4)}
+        del ins, outs
+        torch.cuda.empty_cache()
+    assert sim.sim_check_error(stream) == 0
+    return out
+
+
 def workload4(sim, synthdata, torch, np, dev, stream) -> dict:
     """Per-call microseconds, p = 8, fp16 N(0,1), 1 KiB .. 1 MiB per rank:
     the LL packet path vs the plain one-shot, and the selector's pick.  The
@@ -503,7 +537,7 @@ def main():
         res["torch copy of 512 MiB us"] = round(time_calls(lambda: dst.copy_(src), args.steps, args.warmup) * 1e6, 2)
         print(json.dumps(res), flush=True)
         return
-    sim.sim_init(0, P, S)
+    sim.sim_init(0, 16, S)  # p up to 16 for the one-shot-by-p figures
     stream = int(torch.cuda.current_stream().cuda_stream)
     if args.profile_size:
         n = args.profile_size // 2
@@ -570,13 +604,15 @@ def main():
     t = time_calls(step, args.steps, args.warmup)
     assert sim.sim_check_error(stream) == 0
     ran = sim.sim_last_algo()
+    phased = ran == "oneshot" and sim.sim_debug_get("phased_last") == 1
     if args.profile_only:
         print(json.dumps({"algo": ran, "us_per_step": t * 1e6}), flush=True)
         return
     # the same step repeated in 5 further batches (spread of the timed figure)
     reps = [time_calls(step, max(10, args.steps // 5), 2) for _ in range(5)]
     busbw = 2 * (P - 1) / P * S / t / 1e9
-    kernel = {"oneshot": "k_fold (one-shot, all outputs)", "allpairs": "k_fold + k_copy",
+    kernel = {"oneshot": "k_fold_phased (one-shot, phased)" if phased else "k_fold (one-shot, all outputs)",
+              "allpairs": "k_fold + k_copy",
               "ring": "k_ring_reduce + k_copy", "ring_fifo": "k_ring_fifo",
               "allpairs_persistent": "k_allpairs_persistent"}[ran]
     achieved = algorithmic_bytes(ran) / t / 1e9
@@ -689,6 +725,7 @@ def main():
         extras["workload5_256MiB"] = workload5(sim, synthdata, oracle, torch, np, dev, stream,
                                                max(5, args.steps // 10), not args.no_cpu_baseline)
         extras["ceiling"] = ceiling(sim, torch, dev, stream, max(10, args.steps // 2), sets)
+        extras["ceiling"]["oneshot_vs_copy_by_p"] = oneshot_by_p(sim, torch, dev, stream, max(10, args.steps // 2))
         cf = max(extras["ceiling"]["copy_8in_8out_64MiB_each"]["GBps"],
                  extras["ceiling"]["copy_headline_buffers"]["GBps"])
         extras["ceiling"]["oneshot_over_8x8_copy"] = round(achieved / cf, 4) if ran == "oneshot" else None
@@ -748,7 +785,8 @@ def main():
         torch.cuda.empty_cache()
         rep = calibrate.check(sim.CALIBRATION, steps_scale=0.1, reps=3)
         out["selector_check"] = {
-            b: {k: v[k] for k in ("cases", "strict_matches", "tolerant_matches", "pairs_agree", "pairs",
+            b: {k: v[k] for k in ("cases", "strict_matches", "tolerant_matches", "runner_up_strict",
+                                  "runner_up_tolerant", "pairs_agree", "pairs",
                                   "pick_rel_error_median", "pick_rel_error_max")}
             | {"picks": sorted({r["pick"] for r in v["rows"]}), "fastest": sorted({r["measured_best"] for r in v["rows"]})}
             for b, v in rep["budgets"].items()}

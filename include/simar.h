@@ -260,7 +260,9 @@ int sim_last_algo(void);
  * lane)], ...]}, after T-CCL's ranked launch-configuration table, section
  * III-C3): bulk kernels of that algo then launch the measured best total of
  * the nearest size (log scale), never more than covers the transfer, with
- * the entry's 16-byte vectors per lane (1 or 2; 1 when absent).  An algo
+ * the entry's 16-byte vectors per lane (1 or 2; 1 when absent).  A
+ * top-level "p" (2..16) names the rank count the table was measured at;
+ * calls with another rank count then ignore the table.  An algo
  * entry may carry "wg_gbps", its per-workgroup rate under a budget, and
  * "host_us", its host enqueue cost per launch (see sim_select; 0 when
  * absent).  Errors: SIM_ERR_INVALID_ARG (the current
@@ -413,8 +415,14 @@ enum {
   SIM_DEBUG_FIFO_VECS = 10,    /* single-launch ring: 16-byte vectors per lane per slot, 1, 2 or 4 (default 4) */
   SIM_DEBUG_PTR_TABLE = 11,    /* 0: all-reduce calls never use the pointer table (default 1) */
   SIM_DEBUG_PTR_SETS = 12,     /* get only: pointer sets the table holds */
-  SIM_DEBUG_RING_LL_MAX = 13   /* single-launch ring: largest message (bytes per rank) sent as
+  SIM_DEBUG_RING_LL_MAX = 13,  /* single-launch ring: largest message (bytes per rank) sent as
                                   LL packets (default 256 KiB; 0 = never) */
+  SIM_DEBUG_PHASED = 14,       /* one-shot, phased form: 0 from SIM_DEBUG_PHASED_MIN bytes per rank
+                                  on (default), 1 whenever the call allows it, 2 never */
+  SIM_DEBUG_PHASED_MIN = 15,   /* bytes per rank from which the one-shot runs phased (default 32 MiB) */
+  SIM_DEBUG_PHASED_EXPIRED = 16, /* phased one-shot barrier waits that gave up at the spin limit
+                                  (synchronizes the device; set only to 0, which clears it) */
+  SIM_DEBUG_PHASED_LAST = 17   /* get only: 1 if the last one-shot ran phased */
 };
 int sim_debug_set(int key, uint64_t value);
 int sim_debug_get(int key, uint64_t* value);

@@ -1,0 +1,165 @@
+"""The phased one-shot (k_fold_phased): the grid folds each phase's spans
+into registers, meets at a grid barrier, writes them out, and meets again
+before the next phase.  It must give the fused one-shot's bits (same fold
+order, same arithmetic) for every rank count it serves (2, 4, 8, 16),
+dtype and op, in place or not, with ragged chunk edges, with several
+phases, with no whole span at all, and when its barriers give up early (the
+barrier orders the traffic; it guards no data)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    import all_reduce_reduction_amd as sim
+    sim.sim_init(0, 16, 0)
+    yield sim
+    for key, v in (("phased", 0), ("workgroups", 0), ("spin_limit", 1 << 20)):
+        sim.sim_debug_set(key, v)
+    sim.sim_init(0, 8, 0)
+
+
+def _inputs(dtype, op, p, n, seed):
+    import synthdata
+    if dtype == "int32":
+        lo, hi = (-3, 4) if op == "prod" else (-1000, 1000)
+        return synthdata.int_uniform(seed, p, n, lo, hi)
+    if op == "prod":
+        rng = np.random.default_rng([seed, p, n])
+        x32 = [rng.uniform(0.5, 2.0, n).astype(np.float32) for _ in range(p)]
+        if dtype == "fp32":
+            return x32
+        if dtype == "fp16":
+            return [x.astype(np.float16).view(np.uint16) for x in x32]
+        import oracle
+        return [oracle.get().f32_to_bf16(x) for x in x32]
+    return synthdata.normal(seed, p, n, dtype)
+
+
+def _run(sim, xs, dtype, op, p, n, inplace=False, mode=1, wg=0):
+    from tests.gpu_util import empty_like_poisoned, ptrs, stream, to_device, to_host
+    din = to_device(xs, dtype)
+    dout = din if inplace else empty_like_poisoned(n, dtype, p)
+    sim.sim_debug_set("phased", mode)
+    sim.sim_debug_set("workgroups", wg)
+    try:
+        assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, "oneshot", stream()) == 0
+        ran = sim.sim_debug_get("phased_last")
+        got = to_host(dout, dtype)
+    finally:
+        sim.sim_debug_set("phased", 0)
+        sim.sim_debug_set("workgroups", 0)
+    assert sim.sim_check_error(stream()) == 0
+    return got, ran
+
+
+# 2 workgroups per chunk: a span is 256 lanes x 32 vectors (p <= 8) or x 16
+# (p = 16), so these sizes give chunks of several whole spans plus a rest
+# and phases that not every workgroup has work in
+@pytest.mark.parametrize("p", [2, 4, 8, 16])
+@pytest.mark.parametrize("dtype,op", [("bf16", "sum"), ("fp16", "avg"), ("fp32", "prod"), ("fp32", "min"),
+                                      ("int32", "max"), ("int32", "avg"), ("int32", "sum")])
+def test_phased_matches_oracle(orc, lib, p, dtype, op):
+    from tests.gpu_util import assert_parity
+    sim = lib
+    V = 16 // (2 if dtype in ("fp16", "bf16") else 4)
+    vecs = 256 * (32 if p <= 8 else 16)
+    n = p * (5 * vecs * V + 3 * 256 * V) + 2 * p + 3  # 5 whole spans and a rest per chunk, ragged edges
+    xs = _inputs(dtype, op, p, n, 70 + p)
+    want, _ = orc.allreduce(xs, dtype, op, "oneshot")
+    for inplace in (False, True):
+        got, ran = _run(sim, [x.copy() for x in xs], dtype, op, p, n, inplace=inplace, wg=2 * p)
+        assert ran == 1
+        for r in range(p):
+            assert_parity(got[r], want[r], dtype, f"phased p={p} {dtype} {op} inplace={inplace} r{r}")
+    assert sim.sim_debug_get("phased_expired") == 0
+
+
+@pytest.mark.parametrize("p", [2, 8, 16])
+def test_phased_equals_fused_bits(orc, lib, p):
+    """Same fold order, same arithmetic: the phased and fused one-shot agree
+    bit for bit, at the full grid and with one workgroup per chunk."""
+    from tests.gpu_util import bits
+    sim = lib
+    n = p * 256 * 32 * 8 * 3 + 77
+    xs = _inputs("bf16", "sum", p, n, 9)
+    fused, ran_f = _run(sim, xs, "bf16", "sum", p, n, mode=2)
+    assert ran_f == 0
+    for wg in (0, p):
+        phased, ran_p = _run(sim, xs, "bf16", "sum", p, n, mode=1, wg=wg)
+        assert ran_p == 1
+        for r in range(p):
+            assert (bits(phased[r]) == bits(fused[r])).all(), (p, wg, r)
+
+
+def test_phased_small_and_degenerate(orc, lib):
+    """No whole span at all (every vector done after the phases, no
+    barrier), a chunk shorter than a vector, and n < p."""
+    from tests.gpu_util import assert_parity
+    sim = lib
+    for p, n in ((8, 1), (8, 7), (2, 3), (8, 8 * 8 + 5), (16, 16 * 1000 + 9), (4, 4 * 256 * 8 * 32 - 1)):
+        xs = _inputs("bf16", "sum", p, n, 5)
+        want, _ = orc.allreduce(xs, "bf16", "sum", "oneshot")
+        got, ran = _run(sim, xs, "bf16", "sum", p, n)
+        assert ran == 1
+        for r in range(p):
+            assert_parity(got[r], want[r], "bf16", f"phased p={p} n={n} r{r}")
+
+
+def test_phased_barrier_gives_up_without_changing_results(orc, lib):
+    """A spin limit of one poll: waiting workgroups give up at once (and
+    say so in the expired count), the grid runs unaligned, and the result
+    is the same: the barrier orders traffic, it guards no data."""
+    from tests.gpu_util import assert_parity
+    sim = lib
+    p = 8
+    n = p * 256 * 32 * 8 * 4 + 11
+    xs = _inputs("fp32", "sum", p, n, 21)
+    want, _ = orc.allreduce(xs, "fp32", "sum", "oneshot")
+    sim.sim_debug_set("phased_expired", 0)
+    sim.sim_debug_set("spin_limit", 1)
+    try:
+        got, ran = _run(sim, xs, "fp32", "sum", p, n, wg=2 * p)
+    finally:
+        sim.sim_debug_set("spin_limit", 1 << 20)
+    assert ran == 1
+    for r in range(p):
+        assert_parity(got[r], want[r], "fp32", f"phased, barrier giving up, r{r}")
+    sim.sim_debug_set("phased_expired", 0)
+    assert sim.sim_debug_get("phased_expired") == 0
+
+
+def test_phased_selection_rules(orc, lib):
+    """By default the one-shot runs phased from 32 MiB per rank on, never
+    for rank counts other than 2, 4, 8 and 16, under a workgroup budget or
+    when switched off; the threshold is settable."""
+    import torch
+    from tests.gpu_util import ptrs, stream
+    sim = lib
+    assert sim.sim_debug_get("phased_min") == 32 << 20
+
+    def ran(p, nbytes, **cfg):
+        n = nbytes // 2
+        xs = [torch.zeros(n, dtype=torch.int16, device="cuda:0") for _ in range(p)]
+        ys = [torch.empty_like(x) for x in xs]
+        try:
+            for k, v in cfg.items():
+                (sim.sim_config_set if k == "max_workgroups" else sim.sim_debug_set)(k, v)
+            assert sim.sim_allreduce(ptrs(xs), ptrs(ys), p, n, "bf16", "sum", "oneshot", stream()) == 0
+            return sim.sim_debug_get("phased_last")
+        finally:
+            sim.sim_config_set("max_workgroups", 0)
+            sim.sim_debug_set("phased", 0)
+            sim.sim_debug_set("phased_min", 32 << 20)
+
+    assert ran(8, 32 << 20) == 1
+    assert ran(8, (32 << 20) - 16) == 0
+    assert ran(4, 32 << 20) == 1
+    assert ran(6, 32 << 20) == 0
+    assert ran(8, 32 << 20, max_workgroups=64) == 0
+    assert ran(8, 32 << 20, phased=2) == 0
+    assert ran(8, 1 << 20, phased_min=1 << 20) == 1
+    torch.cuda.synchronize()
+    assert sim.sim_debug_get("phased_expired") == 0

@@ -223,3 +223,34 @@ def test_table_path_in_place(orc, lib, algo, dtype):
         for r in range(p):
             assert_parity(got[r], want[r], dtype, f"{algo} in place rep {rep} r{r}")
     assert _sets(sim) == 1
+
+
+@pytest.mark.parametrize("algo", ["oneshot", "allpairs"])
+@pytest.mark.parametrize("p", [2, 3, 4, 6, 8, 9, 12, 15, 16])
+def test_fold_rank_count_forms(orc, lib, algo, p):
+    """The fold kernel is compiled per rank count (p = 2, 4, 8, 16 as
+    constants, with 1 or 2 vectors per lane; other counts read p at run
+    time, bounded by 8 or 16): every form, through the kernel-argument
+    path and the pointer table, several spans per chunk plus ragged chunk
+    edges, against the oracle."""
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
+    sim = lib
+    for dtype, op in (("bf16", "sum"), ("int32", "max"), ("fp32", "avg")):
+        n = p * 4096 * 3 + 2 * p + 1
+        xs = _inputs(dtype, p, n, 500 + p)
+        want, _ = orc.allreduce(xs, dtype, op, algo)
+        din = to_device(xs, dtype)
+        for table in (0, 1):
+            for unroll in (1, 2):
+                sim.sim_debug_set("ptr_table", table)
+                sim.sim_debug_set("unroll", unroll)
+                try:
+                    dout = empty_like_poisoned(n, dtype, p)
+                    assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, algo, stream()) == 0
+                    got = to_host(dout, dtype)
+                finally:
+                    sim.sim_debug_set("unroll", 0)
+                    sim.sim_debug_set("ptr_table", 1)
+                for r in range(p):
+                    assert_parity(got[r], want[r], dtype, f"{algo} p={p} {dtype} {op} table={table} "
+                                                          f"unroll={unroll} r{r}")

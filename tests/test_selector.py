@@ -127,6 +127,12 @@ def test_packaged_calibration_loads_and_picks_oneshot():
         for b in rep["budgets"].values():
             assert b["strict_matches"] == b["cases"] == len(b["rows"])
             assert b["pairs_agree"] >= 0.9 * b["pairs"]
+            # the model's pick among the schedules left once the measured
+            # fastest is removed, against the measured one
+            assert b["runner_up_strict"] >= 0.9 * b["cases"]
+            assert all(r["runner_up_pick"] != r["measured_best"] for r in b["rows"])
+        # unbudgeted, the pick's predicted time is within 5% of measured in the median case
+        assert rep["budgets"]["none"]["pick_rel_error_median"] <= 0.05
         # the fitted per-workgroup rates are there, and a budget slows the one-shot's prediction
         model = json.load(open(sim.CALIBRATION))
         assert model["algos"]["oneshot"]["wg_gbps"] > 0
@@ -161,6 +167,18 @@ def test_launch_table_json(tmp_path):
             # the refused file changed nothing
             assert sim.sim_model_predict("oneshot", 8, "bf16", 1 << 20) == pytest.approx(
                 3.0 + 16 * (1 << 20) / 5000.0e3)
+        # the rank count the table was measured at: an integer in 2..16
+        for pv in ('1', '17', '2.5', '"8"', '[8]', '-8'):
+            bad = tmp_path / "bad.json"
+            bad.write_text('{"p": %s, "algos": {"oneshot": {"alpha_us": 9.0, "gbps": 1.0}}}' % pv)
+            with pytest.raises(sim.SimError):
+                sim.sim_model_load(str(bad))
+            assert sim.sim_model_predict("oneshot", 8, "bf16", 1 << 20) == pytest.approx(
+                3.0 + 16 * (1 << 20) / 5000.0e3)
+        ok = tmp_path / "ok.json"
+        ok.write_text('{"p": 8, "algos": {"oneshot": {"alpha_us": 9.0, "gbps": 1.0}}}')
+        sim.sim_model_load(str(ok))
+        assert sim.sim_model_predict("oneshot", 8, "bf16", 1 << 20) == pytest.approx(9.0 + 16 * (1 << 20) / 1e3)
     finally:
         sim.sim_model_reset()
 
