@@ -45,6 +45,11 @@ constexpr size_t kRingLLMaxBytes = 256 << 10;
 // against 44.9 us, 32 MiB 89.5 against 93.3, 64 MiB 174 against 196,
 // 128 MiB 353 against 386, 256 MiB 711 against 759.
 constexpr size_t kPhasedMinBytes = 32 << 20;
+// Polls before a phased one-shot barrier wait gives up.  A wait normally
+// ends within the read half's tail (tens of polls); the barrier only orders
+// traffic, so when something keeps the grid from being resident at once
+// (another process's kernels) it is better to stop waiting early.
+constexpr unsigned long long kPhasedSpinLimit = 1 << 13;
 
 // A call's rank pointers as a hash key (p, then x[0..p), y[0..p)).
 struct PtrKey {
@@ -133,6 +138,13 @@ struct Ctx {
   int phased_mode = 0;       // 0: from phased_min bytes per rank on, 1: always, 2: never
   size_t phased_min = kPhasedMinBytes;
   bool last_phased = false;  // the last one-shot ran phased (for the call log)
+  // the most recent phased launch: its stream and sequence number, and the
+  // pinned host word its last workgroup writes that number to on leaving
+  unsigned long long* ph_host_done = nullptr;
+  unsigned long long* ph_dev_done = nullptr;
+  unsigned long long ph_launched = 0;
+  hipStream_t ph_stream = nullptr;
+  bool ph_any = false;
   Model model = default_model();
 };
 
@@ -394,10 +406,18 @@ int run_fold(const Call& c, bool all_out, const int64_t* lo, const int64_t* out_
 int run_fold_phased(const Call& c, const int64_t* lo) {
   g.last_phased = false;
   const int p = c.p;
-  if (!g.ph_mem || c.noalloc || g.capturing || g_max_wg > 0 || g.phased_mode == 2) return -1;
+  if (!g.ph_mem || !g.ph_dev_done || c.noalloc || g.capturing || g_max_wg > 0 || g.phased_mode == 2) return -1;
   if (p != 2 && p != 4 && p != 8 && p != 16) return -1;
   const int E = esize_of(c.dtype);
   if (g.phased_mode == 0 && c.n * (size_t)E < g.phased_min) return -1;
+  // Two phased kernels in flight at once could each hold part of the CUs
+  // while waiting at a barrier for workgroups the other keeps from being
+  // resident (until their waits give up).  Calls on one stream are ordered;
+  // a call on another stream takes the fused kernel while the last phased
+  // launch may still run.
+  if (g.ph_any && c.s != g.ph_stream &&
+      __atomic_load_n(g.ph_host_done, __ATOMIC_ACQUIRE) != g.ph_launched)
+    return -1;
   const int pi = p == 2 ? 0 : p == 4 ? 1 : p == 8 ? 2 : 3;
   int& occ = g.ph_occ[c.dtype][c.op][pi];
   if (occ == 0) {
@@ -424,7 +444,7 @@ int run_fold_phased(const Call& c, const int64_t* lo) {
     nfull = std::max(nfull, nvec / span);
   }
   const int64_t nphase = (nfull + tiles - 1) / tiles;
-  const int64_t nbar = nphase > 0 ? 2 * nphase - 1 : 0;
+  const int64_t nbar = nphase > 0 ? 2 * nphase - 1 : 0;  // plus one arrival per workgroup on leaving
   PhasedArgs a;
   std::memset(&a, 0, sizeof a);
   for (int q = 0; q < p; q++) {
@@ -437,16 +457,23 @@ int run_fold_phased(const Call& c, const int64_t* lo) {
   a.flags = a.ctr + kPhasedFlagStride;
   a.base = g.ph_ctr[slot];
   a.seq = g.ph_seq[slot];
-  a.spin_limit = g.spin_limit;
+  a.spin_limit = std::min(g.spin_limit, kPhasedSpinLimit);
   a.expired = g.ph_expired;
+  a.done = g.ph_dev_done;
+  a.done_seq = g.ph_launched + 1;
   a.tiles = (int)tiles;
   a.nphase = (int)nphase;
   a.inv_p = inv_p_of(p);
   const int rc = hip_err(launch_fold_phased(c.dtype, c.op, p, a, c.s));
   if (rc) return rc;
-  // the counts this call's barriers add (every workgroup meets every barrier)
-  g.ph_ctr[slot] += (unsigned long long)nbar * (unsigned long long)G;
+
+  // the counts this call adds: every workgroup meets every barrier and
+  // arrives once more on leaving
+  g.ph_ctr[slot] += (unsigned long long)(nbar + 1) * (unsigned long long)G;
   g.ph_seq[slot] += (unsigned long long)nbar;
+  g.ph_launched = a.done_seq;
+  g.ph_stream = c.s;
+  g.ph_any = true;
   g.last_phased = true;
   return SIM_OK;
 }
@@ -1162,7 +1189,8 @@ const char* sim_status_string(int status) {
 
 int sim_finalize(void) {
   // (also releases what a failed sim_init had allocated before it gave up)
-  if (!g.init && !g.err && !g.ll && !g.fifo_sem && !g.scratch && !g.ptab && !g.ptab_host && !g.ph_mem)
+  if (!g.init && !g.err && !g.ll && !g.fifo_sem && !g.scratch && !g.ptab && !g.ptab_host && !g.ph_mem &&
+      !g.ph_host_done)
     return SIM_OK;
   // teardown is best effort: every allocation is released even if one call fails
   (void)hipSetDevice(g.device);
@@ -1173,6 +1201,7 @@ int sim_finalize(void) {
   if (g.fifo) (void)hipFree(g.fifo);
   if (g.fifo_sem) (void)hipFree(g.fifo_sem);
   if (g.ph_mem) (void)hipFree(g.ph_mem);
+  if (g.ph_host_done) (void)hipHostFree(g.ph_host_done);
   if (g.err) (void)hipFree(g.err);
   for (PtrSlot& sl : g.ptab_slots)
     if (sl.done) (void)hipEventDestroy(sl.done);
@@ -1234,6 +1263,16 @@ int sim_init(int device, int p_max, size_t max_bytes_per_rank) {
     return SIM_ERR_HIP;
   }
   g.ph_expired = (unsigned int*)(g.ph_mem + g.ph_slot_words * kPhasedSlots);
+  // (no phased calls without the host word)
+  if (hipHostMalloc((void**)&g.ph_host_done, 64, hipHostMallocMapped | hipHostMallocCoherent) != hipSuccess ||
+      hipHostGetDevicePointer((void**)&g.ph_dev_done, g.ph_host_done, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    if (g.ph_host_done) (void)hipHostFree(g.ph_host_done);
+    g.ph_host_done = nullptr;
+    g.ph_dev_done = nullptr;
+  } else {
+    *g.ph_host_done = 0;
+  }
   // the pointer table only makes launches cheaper: without it every call
   // carries its pointers in its kernel arguments
   if (hipMalloc(&g.ptab, sizeof(PtrSet) * kPtrSets) != hipSuccess ||

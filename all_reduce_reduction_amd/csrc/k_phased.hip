@@ -32,7 +32,7 @@
 // in *expired; never an error).  The barrier: each workgroup adds 1 to the
 // slot's arrival counter; the one whose addition completes the count raises
 // every workgroup's own flag word (256 bytes apart) to the release value,
-// and each workgroup's lane 0 polls only its own flag.  Polling one shared
+// and each workgroup's lane 0 polls only its own flag (phased_arrive).  Polling one shared
 // counter instead (every waiting workgroup on one address) measured ~29 us
 // per barrier against ~4 us: the polls of hundreds of workgroups on one
 // memory location slow the reads still in flight.
@@ -53,22 +53,27 @@ template <int P> struct PhasedShape {
   static constexpr int D = P <= 8 ? 2 : 1;
 };
 
-// wait until every workgroup of the grid has arrived here (or the spin
-// limit).  The workgroup whose arrival makes the call's count a multiple of
-// the grid size releases that many barriers: it raises every workgroup's
-// flag to the release value with an atomic max (flags only grow, even if a
-// later barrier's release overtakes this one).  When every wait completes,
-// that is exactly barrier nb; after a give-up, workgroups ahead of the rest
-// may complete a count early, which opens a barrier early -- harmless, as
-// the barrier guards no data -- and never leaves one closed.
-__device__ __forceinline__ void phased_barrier(const PhasedArgs& a, unsigned long long nb,
-                                               unsigned long long* s_rel) {
+// One arrival at the slot's counter: at each barrier and once more when a
+// workgroup leaves, so a call adds (nbar + 1) * G, G = grid size and nbar =
+// its barrier count.  The arrival that makes the call's count a multiple k G
+// opens barrier k (k capped at nbar): it raises every workgroup's flag to
+// seq + k with an atomic max, so flags only grow even if a later release
+// overtakes this one.  When every wait completes, the k-th multiple is
+// reached exactly when barrier k is full; after a give-up, workgroups
+// running ahead may complete a count early and open a barrier early --
+// harmless, as the barrier guards no data -- and none is left closed.  The
+// arrival that completes the whole call's count is the grid's last action:
+// it writes done_seq to the host-visible word.
+__device__ __forceinline__ void phased_arrive(const PhasedArgs& a, unsigned long long nbar,
+                                              unsigned long long* s_rel) {
   __syncthreads();
   const unsigned long long G = gridDim.x;
   if (threadIdx.x == 0) {
     const unsigned long long old = __hip_atomic_fetch_add(a.ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long done = old + 1 - a.base;  // arrivals of this call so far, this one included
-    *s_rel = (done % G == 0) ? a.seq + done / G : 0ull;
+    const unsigned long long k = done / G;
+    *s_rel = (done % G == 0 && k > 0) ? a.seq + (k < nbar ? k : nbar) : 0ull;
+    if (done == (nbar + 1) * G) __hip_atomic_store(a.done, a.done_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   __syncthreads();
   const unsigned long long rel = *s_rel;
@@ -77,6 +82,13 @@ __device__ __forceinline__ void phased_barrier(const PhasedArgs& a, unsigned lon
       __hip_atomic_fetch_max(a.flags + (int64_t)i * kPhasedFlagStride, rel, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// barrier nb of the call: arrive, then wait (lane 0) until this
+// workgroup's own flag reaches seq + nb, or the spin limit
+__device__ __forceinline__ void phased_barrier(const PhasedArgs& a, unsigned long long nbar, unsigned long long nb,
+                                               unsigned long long* s_rel) {
+  phased_arrive(a, nbar, s_rel);
   if (threadIdx.x == 0) {
     const unsigned long long want = a.seq + nb;
     unsigned long long spins = 0;
@@ -144,6 +156,7 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
     return pack<DT>(acc);
   };
 
+  const unsigned long long nbar = a.nphase > 0 ? 2ull * a.nphase - 1 : 0ull;  // barriers of this call
   unsigned long long nb = 0;
   for (int ph = 0; ph < a.nphase; ph++) {
     const int64_t s0 = ((int64_t)ph * a.tiles + t) * span;  // this workgroup's first vector of the phase
@@ -166,7 +179,7 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
         }
       }
     }
-    phased_barrier(a, ++nb, &s_rel);
+    phased_barrier(a, nbar, ++nb, &s_rel);
     // ---- write half: output by output; the workgroups of chunk j start at
     // output j, so at any moment each output takes one chunk's stores ----
     if (whole) {
@@ -181,7 +194,7 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
         for (int k = 0; k < K; k++) st16u(yr, sbyte + (int64_t)k * kBlock * 16, lane, R[k]);
       }
     }
-    if (ph + 1 < a.nphase) phased_barrier(a, ++nb, &s_rel);
+    if (ph + 1 < a.nphase) phased_barrier(a, nbar, ++nb, &s_rel);
   }
 
   // the chunk's vectors past its last whole span, read, folded and written
@@ -206,6 +219,11 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
 #pragma unroll
     for (int r = 0; r < P; r++) store_elem<DT>(yp[r], i, acc);
   }
+
+  // leaving: one more arrival (the call's last one tells the host, which
+  // keeps a second phased grid from starting on another stream before this
+  // one has left)
+  phased_arrive(a, nbar, &s_rel);
 }
 
 namespace {

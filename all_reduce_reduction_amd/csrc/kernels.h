@@ -250,6 +250,8 @@ struct PhasedArgs {
   unsigned long long seq;         // the flags' value when this call starts
   unsigned long long spin_limit;  // polls before a barrier wait gives up
   unsigned int* expired;          // barrier waits that gave up (timing only, not an error)
+  unsigned long long* done;       // host-visible word: the last workgroup to leave writes done_seq
+  unsigned long long done_seq;
   int tiles;                      // workgroups per chunk (grid = tiles * p)
   int nphase;
   float inv_p;

@@ -163,3 +163,42 @@ def test_phased_selection_rules(orc, lib):
     assert ran(8, 1 << 20, phased_min=1 << 20) == 1
     torch.cuda.synchronize()
     assert sim.sim_debug_get("phased_expired") == 0
+
+
+def test_phased_across_streams(orc, lib):
+    """A phased call on another stream while a phased launch may still run
+    takes the fused kernel (two persistent grids would hold each other's
+    CUs at their barriers); on the same stream, or once the earlier launch
+    is done, it runs phased.  Every result matches the oracle."""
+    import torch
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, to_device, to_host
+    sim = lib
+    p = 8
+    n = p * 256 * 32 * 8 * 2 + 5
+    xs = _inputs("bf16", "sum", p, n, 31)
+    want, _ = orc.allreduce(xs, "bf16", "sum", "oneshot")
+    din = to_device(xs, "bf16")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = [empty_like_poisoned(n, "bf16", p) for _ in range(4)]
+    torch.cuda.synchronize()
+    sim.sim_debug_set("phased", 1)
+    try:
+        ran = []
+        for k, st in enumerate((sa, sa, sb, sa)):
+            assert sim.sim_allreduce(ptrs(din), ptrs(outs[k]), p, n, "bf16", "sum", "oneshot", st.cuda_stream) == 0
+            ran.append(sim.sim_debug_get("phased_last"))
+        torch.cuda.synchronize()
+        assert sim.sim_allreduce(ptrs(din), ptrs(outs[3]), p, n, "bf16", "sum", "oneshot", sb.cuda_stream) == 0
+        ran.append(sim.sim_debug_get("phased_last"))
+    finally:
+        sim.sim_debug_set("phased", 0)
+    torch.cuda.synchronize()
+    # the first two on one stream run phased; the first call on the other
+    # stream finds the phased launch before it unfinished, or already done
+    assert ran[0] == 1 and ran[1] == 1 and ran[4] == 1
+    assert ran[2] in (0, 1)
+    for k in range(4):
+        got = to_host(outs[k], "bf16")
+        for r in range(p):
+            assert_parity(got[r], want[r], "bf16", f"stream call {k} r{r}")
+    assert sim.sim_debug_get("phased_expired") == 0
