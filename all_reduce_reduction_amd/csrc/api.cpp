@@ -134,10 +134,10 @@ struct Ctx {
   unsigned long long ph_ctr[kPhasedSlots] = {};
   unsigned long long ph_seq[kPhasedSlots] = {};
   unsigned ph_next = 0;
-  int ph_occ[4][5][5] = {};  // [dtype][op][log2 p - 1]: resident workgroups per CU (-1: none)
+  int ph_occ[4][5][4][2] = {};  // [dtype][op][log2 p - 1][all outputs]: resident workgroups per CU (-1: none)
   int phased_mode = 0;       // 0: from phased_min bytes per rank on, 1: always, 2: never
   size_t phased_min = kPhasedMinBytes;
-  bool last_phased = false;  // the last one-shot ran phased (for the call log)
+  bool last_phased = false;  // the current (or last) call ran a phased fold
   // the most recent phased launch: its stream and sequence number, and the
   // pinned host word its last workgroup writes that number to on leaving
   unsigned long long* ph_host_done = nullptr;
@@ -397,19 +397,30 @@ int run_fold(const Call& c, bool all_out, const int64_t* lo, const int64_t* out_
   return hip_err(launch_fold(c.dtype, c.op, c.p, all_out, a, unroll, c.s));
 }
 
-// The phased one-shot, when this call may use it: p = 2, 4, 8 or 16, no
-// workgroup budget, not under graph capture (the barrier counts are fixed
-// at enqueue time) and not the allocation-free entry point; by default from
-// phased_min bytes per rank on.  Returns SIM_OK after enqueueing it, a
-// negative value when the call should take the fused one-shot instead, or
-// an error.
-int run_fold_phased(const Call& c, const int64_t* lo) {
-  g.last_phased = false;
+// The phased fold, when this call may use it: every output (the one-shot)
+// or the owner's (all-pairs step 1; the direct reduce-scatter, whose owner
+// writes element i at i - out_shift[j]); p = 2, 4, 8 or 16, no workgroup
+// budget, not under graph capture (the barrier counts are fixed at enqueue
+// time) and not the allocation-free entry point; by default from phased_min
+// bytes per rank (of the input) on.  Returns SIM_OK after enqueueing it, a
+// negative value when the call should take the fused fold instead, or an
+// error.
+int run_fold_phased(const Call& c, const int64_t* lo, bool all_out, const int64_t* out_shift) {
   const int p = c.p;
   if (!g.ph_mem || !g.ph_dev_done || c.noalloc || g.capturing || g_max_wg > 0 || g.phased_mode == 2) return -1;
   if (p != 2 && p != 4 && p != 8 && p != 16) return -1;
   const int E = esize_of(c.dtype);
-  if (g.phased_mode == 0 && c.n * (size_t)E < g.phased_min) return -1;
+  // the owner-only forms write S bytes, not p S: their phase separation
+  // gains less, and a phase only partly filled (its 64 MiB of results
+  // holds a 32 MiB message twice) costs more than it gains -- measured on
+  // MI355X, p = 8, direct reduce-scatter: 32 MiB input per rank 50 against
+  // 48 us, 64 MiB 94-98 against 104-107, 256 MiB 378-394 against 407-413
+  const size_t min_bytes = all_out ? g.phased_min : 2 * g.phased_min;
+  if (g.phased_mode == 0 && c.n * (size_t)E < min_bytes) return -1;
+  // owner-only with shifted outputs: whole 16-byte vectors need 16-byte aligned output offsets
+  if (out_shift)
+    for (int q = 0; q < p; q++)
+      if (out_shift[q] % (16 / E) != 0) return -1;
   // Two phased kernels in flight at once could each hold part of the CUs
   // while waiting at a barrier for workgroups the other keeps from being
   // resident (until their waits give up).  Calls on one stream are ordered;
@@ -419,9 +430,9 @@ int run_fold_phased(const Call& c, const int64_t* lo) {
       __atomic_load_n(g.ph_host_done, __ATOMIC_ACQUIRE) != g.ph_launched)
     return -1;
   const int pi = p == 2 ? 0 : p == 4 ? 1 : p == 8 ? 2 : 3;
-  int& occ = g.ph_occ[c.dtype][c.op][pi];
+  int& occ = g.ph_occ[c.dtype][c.op][pi][all_out ? 1 : 0];
   if (occ == 0) {
-    occ = fold_phased_blocks_per_cu(c.dtype, c.op, p);
+    occ = fold_phased_blocks_per_cu(c.dtype, c.op, p, all_out);
     if (occ < 1) occ = -1;
   }
   if (occ < 1) return -1;
@@ -452,6 +463,8 @@ int run_fold_phased(const Call& c, const int64_t* lo) {
     a.y[q] = c.y[q];
   }
   for (int q = 0; q <= p; q++) a.lo[q] = lo[q];
+  if (out_shift)
+    for (int q = 0; q < p; q++) a.out_shift[q] = out_shift[q];
   const unsigned slot = g.ph_next++ % kPhasedSlots;
   a.ctr = g.ph_mem + (int64_t)slot * g.ph_slot_words;
   a.flags = a.ctr + kPhasedFlagStride;
@@ -464,7 +477,7 @@ int run_fold_phased(const Call& c, const int64_t* lo) {
   a.tiles = (int)tiles;
   a.nphase = (int)nphase;
   a.inv_p = inv_p_of(p);
-  const int rc = hip_err(launch_fold_phased(c.dtype, c.op, p, a, c.s));
+  const int rc = hip_err(launch_fold_phased(c.dtype, c.op, p, all_out, a, c.s));
   if (rc) return rc;
 
   // the counts this call adds: every workgroup meets every barrier and
@@ -914,13 +927,14 @@ int run_allreduce(const Call& c) {
   for (int q = 0; q <= p; q++) lo[q] = chunk_lo((int64_t)c.n, p, q);
   switch (c.algo) {
     case SIM_ALGO_ONESHOT: {
-      const int rc = run_fold_phased(c, lo);
+      const int rc = run_fold_phased(c, lo, true, nullptr);
       if (rc >= 0) return rc;
       return run_fold(c, true, lo, nullptr, ptr_set_for(c));
     }
     case SIM_ALGO_ALLPAIRS: {
       const PtrSet* set = ptr_set_for(c);
-      int rc = run_fold(c, false, lo, nullptr, set);  // step 1: GATHER_REDUCE into each owner
+      int rc = run_fold_phased(c, lo, false, nullptr);  // step 1: GATHER_REDUCE into each owner
+      if (rc < 0) rc = run_fold(c, false, lo, nullptr, set);
       if (rc) return rc;
       if (set) {  // step 2 (FANOUT) from the same table entry
         const int V = 16 / esize_of(c.dtype);
@@ -1026,6 +1040,8 @@ int run_reduce_scatter(const Call& c) {
   if (c.algo == SIM_ALGO_ALLPAIRS) {
     std::vector<int64_t> shift(p);
     for (int q = 0; q < p; q++) shift[q] = lo[q];
+    const int rc = run_fold_phased(c, lo.data(), false, shift.data());
+    if (rc >= 0) return rc;
     return run_fold(c, false, lo.data(), shift.data(), nullptr);
   }
   return run_ring_rs(c, *sch, p - 1, true, lo.data());
@@ -1144,6 +1160,7 @@ int begin_call(void* stream) {
   }
   g.capturing = (st != hipStreamCaptureStatusNone);
   if (g.capturing) g.captured = true;
+  g.last_phased = false;
   return SIM_OK;
 }
 
@@ -1151,7 +1168,7 @@ void log_call(const char* what, const Call& c, double us) {
   if (!g.log) return;
   std::fprintf(stderr, "[simar] %s: %zu bytes/rank p %d -> algo %s%s steps %d predicted %.2f us\n", what,
                c.n * (size_t)esize_of(c.dtype), c.p, algo_name(c.algo),
-               (c.algo == SIM_ALGO_ONESHOT && g.last_phased) ? " (phased)" : "",
+               g.last_phased ? " (phased fold)" : "",
                model_launches(c.coll, c.algo, c.p, g_topo), us);
 }
 

@@ -244,6 +244,7 @@ struct PhasedArgs {
   const void* x[SIM_MAX_RANKS];
   void* y[SIM_MAX_RANKS];
   int64_t lo[SIM_MAX_RANKS + 1];  // chunk bounds
+  int64_t out_shift[SIM_MAX_RANKS];  // owner-only mode: y[j] index = i - out_shift[j] (a multiple of 16 bytes)
   unsigned long long* ctr;        // the slot's arrival counter
   unsigned long long* flags;      // the slot's release flags
   unsigned long long base;        // the counter's value when this call starts
@@ -309,10 +310,16 @@ hipError_t launch_ring_ll(int dtype, int op, const RingLLArgs& a, hipStream_t s)
 int ring_ll_blocks_per_cu(int dtype, int op);
 hipError_t launch_allpairs_persistent(int dtype, int op, const AllPairsPArgs& a, hipStream_t s);
 int allpairs_persistent_blocks_per_cu(int dtype, int op, int p);
-// The phased one-shot for p = 2, 4, 8 or 16 (hipErrorInvalidValue otherwise),
-// its resident workgroups per CU, and its result vectors per lane per phase.
-hipError_t launch_fold_phased(int dtype, int op, int p, const PhasedArgs& a, hipStream_t s);
-int fold_phased_blocks_per_cu(int dtype, int op, int p);
+// The phased fold for p = 2, 4, 8 or 16 (hipErrorInvalidValue otherwise):
+// every output (the one-shot) or the owner's (all-pairs step 1, the direct
+// reduce-scatter); its resident workgroups per CU, and its result vectors
+// per lane per phase.
+hipError_t launch_fold_phased(int dtype, int op, int p, bool all_out, const PhasedArgs& a, hipStream_t s);
+int fold_phased_blocks_per_cu(int dtype, int op, int p, bool all_out);
 int fold_phased_vecs_per_lane(int p);
+template <bool ALL_OUT>
+hipError_t phased_launch(int dtype, int op, int p, const PhasedArgs& a, hipStream_t s);
+template <bool ALL_OUT>
+int phased_occupancy(int dtype, int op, int p);
 
 }  // namespace simar

@@ -1,0 +1,350 @@
+// phased_impl.h -- the phased fold for large messages (gfx950): the one-shot
+// all-reduce (every output) and all-pairs step 1 / the direct reduce-scatter
+// (the owner's output only), included by k_phased.hip and
+// k_phased_owner.hip, which instantiate one output mode each.
+//
+// It computes exactly what the fused one-shot computes ("MSCCL++ ...",
+// section "The Collective Algorithm Library", 1PA: every rank reads every
+// rank's data and reduces it in one phase; the fold in the all-pairs order of
+// "MSCCL, in depth ...", section "Writing an algorithm in MSCCLang": owner of
+// the chunk first, then the other ranks ascending), with the same 2 p S bytes
+// -- only the order in which the whole GPU issues them differs.  The fused
+// kernel keeps every workgroup reading and writing at once: the p input
+// streams and p output streams of all workgroups share HBM the whole time.
+// On MI355X that mix moves ~0.71 of the 8 TB/s peak, while the same
+// workgroups reading alone reach ~0.87 and writing alone ~0.70 (measured,
+// 64 MiB per rank, p = 8).  Here the grid takes turns instead:
+//
+//   read half:  every workgroup loads its span of all p inputs (16-byte
+//               loads, the next span's loads in flight while this one
+//               folds) and keeps the folded result in VGPRs: K vectors per
+//               lane, K * 16 * kBlock bytes per workgroup;
+//   grid barrier;
+//   write half: every workgroup stores its results to the p outputs, output
+//               by output, the workgroups of chunk j starting at output j;
+//   grid barrier (before the next phase's reads), and so on.
+//
+// The grid is persistent (two workgroups per CU, all resident), and a phase
+// covers K * kBlock vectors of every workgroup: 64 MiB of results per phase
+// on 256 CUs, one phase for the 64 MiB-per-rank headline.
+//
+// The barrier is for timing only: every element is read, folded and written
+// by one lane, so no workgroup ever reads what another writes, and the
+// result does not depend on when (or whether) a barrier opens.  A waiting
+// workgroup therefore gives up after the spin limit and carries on (counted
+// in *expired; never an error).  The barrier: each workgroup adds 1 to the
+// slot's arrival counter; the one whose addition completes the count raises
+// every workgroup's own flag word (256 bytes apart) to the release value,
+// and each workgroup's lane 0 polls only its own flag (phased_arrive).  Polling one shared
+// counter instead (every waiting workgroup on one address) measured ~29 us
+// per barrier against ~4 us: the polls of hundreds of workgroups on one
+// memory location slow the reads still in flight.
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "kernels.h"
+#include "launch.h"
+
+namespace simar {
+
+namespace {
+
+// result vectors per lane per phase, and load sets in flight while folding
+// (with p = 16, 16 vectors per lane: the 16 operands of a fold take 64 VGPRs)
+template <int P> struct PhasedShape {
+  static constexpr int K = P <= 8 ? 32 : 16;
+  static constexpr int D = P <= 8 ? 2 : 1;
+};
+
+// One arrival at the slot's counter: at each barrier and once more when a
+// workgroup leaves, so a call adds (nbar + 1) * G, G = grid size and nbar =
+// its barrier count.  Barrier k opens once R = G - G / 10 of its G
+// arrivals are in: the arrival that makes the call's count (k - 1) G + R
+// raises every workgroup's flag to seq + k (k capped at nbar) with an
+// atomic max, so flags only grow even if a later release overtakes this
+// one, and the last tenth pass straight through when they arrive.  Waiting
+// for the very last workgroup measured ~1.5% slower at 64 MiB per rank
+// (the slowest readers' tail overlaps the first writes instead of idling
+// the grid).  When every wait completes, barrier k opens exactly at its
+// R-th arrival; after a give-up, workgroups running ahead may complete a
+// count early and open a barrier early -- harmless, as the barrier guards
+// no data -- and none is left closed, as the count passes every (k - 1) G
+// + R on its way to (nbar + 1) G.  The arrival that completes the whole
+// call's count is the grid's last action: it writes done_seq to the
+// host-visible word.
+__device__ __forceinline__ void phased_arrive(const PhasedArgs& a, unsigned long long nbar,
+                                              unsigned long long* s_rel) {
+  __syncthreads();
+  const unsigned long long G = gridDim.x;
+  if (threadIdx.x == 0) {
+    const unsigned long long old = __hip_atomic_fetch_add(a.ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long done = old + 1 - a.base;  // arrivals of this call so far, this one included
+    const unsigned long long R = G - G / 10;
+    const unsigned long long k = done >= R ? (done - R) / G + 1 : 0;  // the barrier this arrival may open
+    *s_rel = (done >= R && (done - R) % G == 0) ? a.seq + (k < nbar ? k : nbar) : 0ull;
+    if (done == (nbar + 1) * G) __hip_atomic_store(a.done, a.done_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  __syncthreads();
+  const unsigned long long rel = *s_rel;
+  if (rel) {
+    for (unsigned i = threadIdx.x; i < G; i += kBlock)
+      __hip_atomic_fetch_max(a.flags + (int64_t)i * kPhasedFlagStride, rel, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// barrier nb of the call: arrive, then wait (lane 0) until this
+// workgroup's own flag reaches seq + nb, or the spin limit
+__device__ __forceinline__ void phased_barrier(const PhasedArgs& a, unsigned long long nbar, unsigned long long nb,
+                                               unsigned long long* s_rel) {
+  phased_arrive(a, nbar, s_rel);
+  if (threadIdx.x == 0) {
+    const unsigned long long want = a.seq + nb;
+    unsigned long long spins = 0;
+    while (__hip_atomic_load(a.flags + (int64_t)blockIdx.x * kPhasedFlagStride, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT) < want) {
+      if (++spins > a.spin_limit) {
+        __hip_atomic_fetch_add(a.expired, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+}
+
+}  // namespace
+
+template <int DT, int OP, int P, bool ALL_OUT>
+__global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
+  typedef typename Ty<DT>::A A;
+  typedef Op<DT, OP> O;
+  constexpr int V = epv<DT>();
+  constexpr int E = Ty<DT>::E;
+  constexpr int K = PhasedShape<P>::K;
+  constexpr int D = PhasedShape<P>::D;
+  const int j = (int)(blockIdx.x % (unsigned)P);
+  const int t = (int)(blockIdx.x / (unsigned)P);
+  const int64_t lo = a.lo[j], hi = a.lo[j + 1];
+  const float inv_p = a.inv_p;
+  __shared__ unsigned long long s_rel;
+
+  // operand k of the fold: rank j for k == 0, then the ranks != j ascending
+  const void* xp[P];
+#pragma unroll
+  for (int k = 0; k < P; k++) xp[k] = a.x[(k == 0) ? j : (k <= j ? k - 1 : k)];
+  // outputs: every rank's, or (owner-only) rank j's, element i at i - shift
+  void* yp[ALL_OUT ? P : 1];
+#pragma unroll
+  for (int r = 0; r < (ALL_OUT ? P : 1); r++) yp[r] = a.y[ALL_OUT ? r : j];
+  const int64_t oshift = ALL_OUT ? 0 : a.out_shift[j];
+
+  // chunk j: scalar head up to the first 16-byte boundary, whole vectors,
+  // scalar tail (every pointer is 16-byte aligned)
+  int64_t head = (V - lo % V) % V;
+  if (head > hi - lo) head = hi - lo;
+  const int64_t vbeg = lo + head;
+  const int64_t nvec = (hi - vbeg) / V;
+  const int64_t tail_beg = vbeg + nvec * V;
+  const int64_t nscalar = head + (hi - tail_beg);
+  const int tid = threadIdx.x;
+  const int64_t span = (int64_t)kBlock * K;
+  const uint32_t lane = lane_offset((uint32_t)tid * 16u);
+
+  auto fold = [&](const u32x4* L) {
+    A acc[V], tt[V];
+    unpack<DT>(L[0], acc);
+#pragma unroll
+    for (int e = 0; e < V; e++) acc[e] = O::pre(acc[e], inv_p);
+#pragma unroll
+    for (int k = 1; k < P; k++) {
+      unpack<DT>(L[k], tt);
+#pragma unroll
+      for (int e = 0; e < V; e++) acc[e] = O::comb(acc[e], O::pre(tt[e], inv_p));
+    }
+#pragma unroll
+    for (int e = 0; e < V; e++) acc[e] = O::post(acc[e], P);
+    return pack<DT>(acc);
+  };
+
+  const unsigned long long nbar = a.nphase > 0 ? 2ull * a.nphase - 1 : 0ull;  // barriers of this call
+  unsigned long long nb = 0;
+  for (int ph = 0; ph < a.nphase; ph++) {
+    const int64_t s0 = ((int64_t)ph * a.tiles + t) * span;  // this workgroup's first vector of the phase
+    const int64_t sbyte = vbeg * E + s0 * 16;
+    const bool whole = s0 + span <= nvec;  // uniform over the workgroup (partial spans come after the loop)
+    u32x4 R[K];
+    // ---- read half: a whole span's results stay in VGPRs ----
+    if (whole) {
+      // D sets of p loads in flight while one set folds.  The scheduling
+      // barriers keep each set's p loads issued together, ahead of the fold
+      // that follows: without them the compiler interleaved the 32-bit folds
+      // with their own loads, waiting on every load (1-3 in flight per wave
+      // instead of ~16; the fp32 phased reduce-scatter ran 1.5x slower than
+      // the bf16 one).
+      u32x4 L[D][P];
+#pragma unroll
+      for (int d = 0; d < D; d++)
+#pragma unroll
+        for (int q = 0; q < P; q++) L[d][q] = ld16u(xp[q], sbyte + (int64_t)d * kBlock * 16, lane);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < K; k++) {
+        R[k] = fold(L[k % D]);
+        if (k + D < K) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < P; q++) L[k % D][q] = ld16u(xp[q], sbyte + (int64_t)(k + D) * kBlock * 16, lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    phased_barrier(a, nbar, ++nb, &s_rel);
+    // ---- write half: output by output; the workgroups of chunk j start at
+    // output j, so at any moment each output takes one chunk's stores ----
+    if (whole) {
+      if constexpr (ALL_OUT) {
+#pragma unroll
+        for (int rr = 0; rr < P; rr++) {
+          const int r = (rr + j) & (P - 1);  // P is a power of two
+          void* yr = yp[0];
+#pragma unroll
+          for (int q = 1; q < P; q++)
+            if (q == r) yr = yp[q];
+#pragma unroll
+          for (int k = 0; k < K; k++) st16u(yr, sbyte + (int64_t)k * kBlock * 16, lane, R[k]);
+        }
+      } else {
+        const int64_t obyte = sbyte - oshift * E;  // 16-byte aligned: the host checks oshift % V == 0
+#pragma unroll
+        for (int k = 0; k < K; k++) st16u(yp[0], obyte + (int64_t)k * kBlock * 16, lane, R[k]);
+      }
+    }
+    if (ph + 1 < a.nphase) phased_barrier(a, nbar, ++nb, &s_rel);
+  }
+
+  // the chunk's vectors past its last whole span, read, folded and written
+  // vector by vector by all of the chunk's workgroups
+  for (int64_t v = nvec / span * span + (int64_t)t * kBlock + tid; v < nvec; v += (int64_t)a.tiles * kBlock) {
+    const int64_t vb = (vbeg + v * V) * E;
+    u32x4 L[P];
+#pragma unroll
+    for (int q = 0; q < P; q++) L[q] = ld16(xp[q], vb);
+    const u32x4 out = fold(L);
+    if constexpr (ALL_OUT) {
+#pragma unroll
+      for (int r = 0; r < P; r++) st16(yp[r], vb, out);
+    } else {
+      st16(yp[0], vb - oshift * E, out);
+    }
+  }
+
+  // ragged chunk edges, element by element, in the same fold order
+  for (int64_t s = (int64_t)t * kBlock + tid; s < nscalar; s += (int64_t)a.tiles * kBlock) {
+    const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
+    A acc = O::pre(load_elem<DT>(xp[0], i), inv_p);
+#pragma unroll
+    for (int k = 1; k < P; k++) acc = O::comb(acc, O::pre(load_elem<DT>(xp[k], i), inv_p));
+    acc = O::post(acc, P);
+    if constexpr (ALL_OUT) {
+#pragma unroll
+      for (int r = 0; r < P; r++) store_elem<DT>(yp[r], i, acc);
+    } else {
+      store_elem<DT>(yp[0], i - oshift, acc);
+    }
+  }
+
+  // leaving: one more arrival (the call's last one tells the host, which
+  // keeps a second phased grid from starting on another stream before this
+  // one has left)
+  phased_arrive(a, nbar, &s_rel);
+}
+
+namespace {
+
+template <int DT, int OP, bool ALL_OUT>
+hipError_t phased_by_p(int p, const PhasedArgs& a, hipStream_t s) {
+  const dim3 g((unsigned)a.tiles * (unsigned)p), b(kBlock);
+  switch (p) {
+    case 2: return launch<k_fold_phased<DT, OP, 2, ALL_OUT>>(g, b, s, a);
+    case 4: return launch<k_fold_phased<DT, OP, 4, ALL_OUT>>(g, b, s, a);
+    case 8: return launch<k_fold_phased<DT, OP, 8, ALL_OUT>>(g, b, s, a);
+    case 16: return launch<k_fold_phased<DT, OP, 16, ALL_OUT>>(g, b, s, a);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DT, bool ALL_OUT>
+hipError_t phased_by_op(int op, int p, const PhasedArgs& a, hipStream_t s) {
+  switch (op) {
+    case SIM_SUM: return phased_by_p<DT, SIM_SUM, ALL_OUT>(p, a, s);
+    case SIM_PROD: return phased_by_p<DT, SIM_PROD, ALL_OUT>(p, a, s);
+    case SIM_MIN: return phased_by_p<DT, SIM_MIN, ALL_OUT>(p, a, s);
+    case SIM_MAX: return phased_by_p<DT, SIM_MAX, ALL_OUT>(p, a, s);
+    case SIM_AVG: return phased_by_p<DT, SIM_AVG, ALL_OUT>(p, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int OP, int P, bool ALL_OUT>
+int occ_of() {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)k_fold_phased<DT, OP, P, ALL_OUT>, kBlock, 0) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return nb;
+}
+
+template <int DT, int OP, bool ALL_OUT>
+int occ_by_p(int p) {
+  switch (p) {
+    case 2: return occ_of<DT, OP, 2, ALL_OUT>();
+    case 4: return occ_of<DT, OP, 4, ALL_OUT>();
+    case 8: return occ_of<DT, OP, 8, ALL_OUT>();
+    case 16: return occ_of<DT, OP, 16, ALL_OUT>();
+  }
+  return 0;
+}
+
+template <int DT, bool ALL_OUT>
+int occ_by_op(int op, int p) {
+  switch (op) {
+    case SIM_SUM: return occ_by_p<DT, SIM_SUM, ALL_OUT>(p);
+    case SIM_PROD: return occ_by_p<DT, SIM_PROD, ALL_OUT>(p);
+    case SIM_MIN: return occ_by_p<DT, SIM_MIN, ALL_OUT>(p);
+    case SIM_MAX: return occ_by_p<DT, SIM_MAX, ALL_OUT>(p);
+    case SIM_AVG: return occ_by_p<DT, SIM_AVG, ALL_OUT>(p);
+  }
+  return 0;
+}
+
+}  // namespace
+
+// the launcher and occupancy query of one output mode (every dtype, op and p)
+template <bool ALL_OUT>
+hipError_t phased_launch(int dtype, int op, int p, const PhasedArgs& a, hipStream_t s) {
+  switch (dtype) {
+    case SIM_INT32: return phased_by_op<SIM_INT32, ALL_OUT>(op, p, a, s);
+    case SIM_FP32: return phased_by_op<SIM_FP32, ALL_OUT>(op, p, a, s);
+    case SIM_FP16: return phased_by_op<SIM_FP16, ALL_OUT>(op, p, a, s);
+    case SIM_BF16: return phased_by_op<SIM_BF16, ALL_OUT>(op, p, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool ALL_OUT>
+int phased_occupancy(int dtype, int op, int p) {
+  switch (dtype) {
+    case SIM_INT32: return occ_by_op<SIM_INT32, ALL_OUT>(op, p);
+    case SIM_FP32: return occ_by_op<SIM_FP32, ALL_OUT>(op, p);
+    case SIM_FP16: return occ_by_op<SIM_FP16, ALL_OUT>(op, p);
+    case SIM_BF16: return occ_by_op<SIM_BF16, ALL_OUT>(op, p);
+  }
+  return 0;
+}
+
+}  // namespace simar

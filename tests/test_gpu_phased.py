@@ -162,6 +162,16 @@ def test_phased_selection_rules(orc, lib):
     assert ran(8, 32 << 20, phased=2) == 0
     assert ran(8, 1 << 20, phased_min=1 << 20) == 1
     torch.cuda.synchronize()
+    # the owner-only forms from twice the threshold
+    def ran_rs(nbytes):
+        n = nbytes // 2
+        xs = [torch.zeros(n, dtype=torch.int16, device="cuda:0") for _ in range(8)]
+        ys = [torch.empty(n // 8, dtype=torch.int16, device="cuda:0") for _ in range(8)]
+        assert sim.sim_reduce_scatter(ptrs(xs), ptrs(ys), 8, n // 8, "bf16", "sum", "allpairs", stream()) == 0
+        return sim.sim_debug_get("phased_last")
+    assert ran_rs(32 << 20) == 0
+    assert ran_rs(64 << 20) == 1
+    torch.cuda.synchronize()
     assert sim.sim_debug_get("phased_expired") == 0
 
 
@@ -201,4 +211,55 @@ def test_phased_across_streams(orc, lib):
         got = to_host(outs[k], "bf16")
         for r in range(p):
             assert_parity(got[r], want[r], "bf16", f"stream call {k} r{r}")
+    assert sim.sim_debug_get("phased_expired") == 0
+
+
+@pytest.mark.parametrize("p", [2, 4, 8, 16])
+@pytest.mark.parametrize("dtype,op", [("bf16", "sum"), ("fp16", "max"), ("fp32", "avg"), ("int32", "prod")])
+def test_phased_owner_only_matches_oracle(orc, lib, p, dtype, op):
+    """The owner-only phased fold: all-pairs step 1 (outputs in place in
+    the all-reduce layout) and the direct reduce-scatter (each owner's
+    chunk written from offset 0 of its output, and in place), several
+    phases and a rest per chunk; a chunk that does not fill whole 16-byte
+    vectors keeps the reduce-scatter on the fused fold."""
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
+    sim = lib
+    V = 16 // (2 if dtype in ("fp16", "bf16") else 4)
+    vecs = 256 * (32 if p <= 8 else 16)
+    # all-pairs all-reduce
+    n = p * (5 * vecs * V + 3 * 256 * V) + 2 * p + 3
+    xs = _inputs(dtype, op, p, n, 80 + p)
+    want, _ = orc.allreduce(xs, dtype, op, "allpairs")
+    din = to_device(xs, dtype)
+    dout = empty_like_poisoned(n, dtype, p)
+    sim.sim_debug_set("phased", 1)
+    sim.sim_debug_set("workgroups", 2 * p)
+    try:
+        assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, dtype, op, "allpairs", stream()) == 0
+        assert sim.sim_debug_get("phased_last") == 1
+        got = to_host(dout, dtype)
+        for r in range(p):
+            assert_parity(got[r], want[r], dtype, f"all-pairs phased p={p} {dtype} {op} r{r}")
+        # direct reduce-scatter: whole vectors per chunk (phased), then a ragged chunk (fused)
+        for n_out, phased in ((V * (5 * vecs + 3 * 256 + 7), 1), (V * (2 * vecs) + 1, 0)):
+            xs = _inputs(dtype, op, p, p * n_out, 90 + p)
+            want, _ = orc.reduce_scatter(xs, dtype, op, "allpairs")
+            for inplace in (False, True):
+                din = to_device(xs, dtype)
+                outs = ([d[r * n_out:(r + 1) * n_out] for r, d in enumerate(din)] if inplace
+                        else empty_like_poisoned(n_out, dtype, p))
+                st = sim.sim_reduce_scatter(ptrs(din), ptrs(outs), p, n_out, dtype, op, "allpairs", stream())
+                if inplace and (n_out * (16 // V)) % 16:
+                    assert st == sim.STATUS_CODE["SIM_ERR_ALIGN"]
+                    continue
+                assert st == 0
+                assert sim.sim_debug_get("phased_last") == phased
+                got = to_host(outs, dtype)
+                for r in range(p):
+                    assert_parity(got[r], want[r], dtype,
+                                  f"RS phased={phased} p={p} {dtype} {op} n_out={n_out} inplace={inplace} r{r}")
+    finally:
+        sim.sim_debug_set("phased", 0)
+        sim.sim_debug_set("workgroups", 0)
+    assert sim.sim_check_error(stream()) == 0
     assert sim.sim_debug_get("phased_expired") == 0
