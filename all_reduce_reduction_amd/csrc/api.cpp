@@ -134,7 +134,7 @@ struct Ctx {
   unsigned long long ph_ctr[kPhasedSlots] = {};
   unsigned long long ph_seq[kPhasedSlots] = {};
   unsigned ph_next = 0;
-  int ph_occ[4][5][4][2] = {};  // [dtype][op][log2 p - 1][all outputs]: resident workgroups per CU (-1: none)
+  int ph_occ[4][5][4][3] = {};  // [dtype][op][log2 p - 1][form]: resident workgroups per CU (-1: none)
   int phased_mode = 0;       // 0: from phased_min bytes per rank on, 1: always, 2: never
   size_t phased_min = kPhasedMinBytes;
   bool last_phased = false;  // the current (or last) call ran a phased fold
@@ -397,30 +397,42 @@ int run_fold(const Call& c, bool all_out, const int64_t* lo, const int64_t* out_
   return hip_err(launch_fold(c.dtype, c.op, c.p, all_out, a, unroll, c.s));
 }
 
-// The phased fold, when this call may use it: every output (the one-shot)
-// or the owner's (all-pairs step 1; the direct reduce-scatter, whose owner
-// writes element i at i - out_shift[j]); p = 2, 4, 8 or 16, no workgroup
-// budget, not under graph capture (the barrier counts are fixed at enqueue
-// time) and not the allocation-free entry point; by default from phased_min
-// bytes per rank (of the input) on.  Returns SIM_OK after enqueueing it, a
-// negative value when the call should take the fused fold instead, or an
-// error.
-int run_fold_phased(const Call& c, const int64_t* lo, bool all_out, const int64_t* out_shift) {
+// The phased kernels, when this call may use one: the fold writing every
+// output (kPhasedAll: the one-shot) or the owner's (kPhasedOwner: all-pairs
+// step 1; the direct reduce-scatter, whose owner writes element i at i -
+// out_shift[j]), or the direct all-gather's copy (kPhasedGather: output
+// block j from rank j's input); p = 2, 4, 8 or 16, no workgroup budget, not
+// under graph capture (the barrier counts are fixed at enqueue time) and
+// not the allocation-free entry point; by default from phased_min bytes per
+// rank on (of the input for the fold, of the output for the gather).
+// Returns SIM_OK after enqueueing it, a negative value when the call should
+// take the fused kernel instead, or an error.
+enum PhasedForm { kPhasedAll = 0, kPhasedOwner = 1, kPhasedGather = 2 };
+int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t* out_shift) {
   const int p = c.p;
+  const bool all_out = form != kPhasedOwner;
   if (!g.ph_mem || !g.ph_dev_done || c.noalloc || g.capturing || g_max_wg > 0 || g.phased_mode == 2) return -1;
   if (p != 2 && p != 4 && p != 8 && p != 16) return -1;
   const int E = esize_of(c.dtype);
-  // the owner-only forms write S bytes, not p S: their phase separation
-  // gains less, and a phase only partly filled (its 64 MiB of results
-  // holds a 32 MiB message twice) costs more than it gains -- measured on
-  // MI355X, p = 8, direct reduce-scatter: 32 MiB input per rank 50 against
-  // 48 us, 64 MiB 94-98 against 104-107, 256 MiB 378-394 against 407-413
-  const size_t min_bytes = all_out ? g.phased_min : 2 * g.phased_min;
+  // The owner-only fold writes S bytes, not p S, and the gather reads only
+  // S / p: their phase separation gains less, and a phase only partly
+  // filled (its 64 MiB of results holds a 32 MiB message twice) costs more
+  // than it gains.  Measured on MI355X, p = 8, phased against fused: direct
+  // reduce-scatter 32 MiB input per rank 50 against 48 us, 64 MiB 94-105
+  // against 103-107, 256 MiB 378-413 against 407-417; direct all-gather
+  // 32 MiB output per rank 58-60 against 55-57, 64 MiB 109-110 against
+  // 115, 256 MiB 428-431 against 450-458.  Both start at twice the
+  // one-shot's threshold.
+  const size_t min_bytes = form == kPhasedAll ? g.phased_min : 2 * g.phased_min;
   if (g.phased_mode == 0 && c.n * (size_t)E < min_bytes) return -1;
-  // owner-only with shifted outputs: whole 16-byte vectors need 16-byte aligned output offsets
+  // owner-only with shifted outputs, and the gather's inputs: whole 16-byte
+  // vectors need 16-byte aligned offsets on both sides
   if (out_shift)
     for (int q = 0; q < p; q++)
       if (out_shift[q] % (16 / E) != 0) return -1;
+  if (form == kPhasedGather)
+    for (int q = 0; q < p; q++)
+      if (lo[q] % (16 / E) != 0) return -1;
   // Two phased kernels in flight at once could each hold part of the CUs
   // while waiting at a barrier for workgroups the other keeps from being
   // resident (until their waits give up).  Calls on one stream are ordered;
@@ -430,9 +442,9 @@ int run_fold_phased(const Call& c, const int64_t* lo, bool all_out, const int64_
       __atomic_load_n(g.ph_host_done, __ATOMIC_ACQUIRE) != g.ph_launched)
     return -1;
   const int pi = p == 2 ? 0 : p == 4 ? 1 : p == 8 ? 2 : 3;
-  int& occ = g.ph_occ[c.dtype][c.op][pi][all_out ? 1 : 0];
+  int& occ = g.ph_occ[c.dtype][form == kPhasedGather ? 0 : c.op][pi][form];
   if (occ == 0) {
-    occ = fold_phased_blocks_per_cu(c.dtype, c.op, p, all_out);
+    occ = form == kPhasedGather ? gather_phased_blocks_per_cu(E, p) : fold_phased_blocks_per_cu(c.dtype, c.op, p, all_out);
     if (occ < 1) occ = -1;
   }
   if (occ < 1) return -1;
@@ -477,7 +489,8 @@ int run_fold_phased(const Call& c, const int64_t* lo, bool all_out, const int64_
   a.tiles = (int)tiles;
   a.nphase = (int)nphase;
   a.inv_p = inv_p_of(p);
-  const int rc = hip_err(launch_fold_phased(c.dtype, c.op, p, all_out, a, c.s));
+  const int rc = hip_err(form == kPhasedGather ? launch_gather_phased(E, p, a, c.s)
+                                               : launch_fold_phased(c.dtype, c.op, p, all_out, a, c.s));
   if (rc) return rc;
 
   // the counts this call adds: every workgroup meets every barrier and
@@ -927,13 +940,13 @@ int run_allreduce(const Call& c) {
   for (int q = 0; q <= p; q++) lo[q] = chunk_lo((int64_t)c.n, p, q);
   switch (c.algo) {
     case SIM_ALGO_ONESHOT: {
-      const int rc = run_fold_phased(c, lo, true, nullptr);
+      const int rc = run_phased(c, lo, kPhasedAll, nullptr);
       if (rc >= 0) return rc;
       return run_fold(c, true, lo, nullptr, ptr_set_for(c));
     }
     case SIM_ALGO_ALLPAIRS: {
       const PtrSet* set = ptr_set_for(c);
-      int rc = run_fold_phased(c, lo, false, nullptr);  // step 1: GATHER_REDUCE into each owner
+      int rc = run_phased(c, lo, kPhasedOwner, nullptr);  // step 1: GATHER_REDUCE into each owner
       if (rc < 0) rc = run_fold(c, false, lo, nullptr, set);
       if (rc) return rc;
       if (set) {  // step 2 (FANOUT) from the same table entry
@@ -1040,7 +1053,7 @@ int run_reduce_scatter(const Call& c) {
   if (c.algo == SIM_ALGO_ALLPAIRS) {
     std::vector<int64_t> shift(p);
     for (int q = 0; q < p; q++) shift[q] = lo[q];
-    const int rc = run_fold_phased(c, lo.data(), false, shift.data());
+    const int rc = run_phased(c, lo.data(), kPhasedOwner, shift.data());
     if (rc >= 0) return rc;
     return run_fold(c, false, lo.data(), shift.data(), nullptr);
   }
@@ -1053,6 +1066,12 @@ int run_all_gather(const Call& c) {
   if (!sch) return SIM_ERR_VERIFY;
   const int p = c.p;
   const int64_t nin = (int64_t)c.n / p;
+  if (c.algo == SIM_ALGO_ALLPAIRS) {  // direct: output block q is rank q's input
+    int64_t lo[SIM_MAX_RANKS + 1];
+    for (int q = 0; q <= p; q++) lo[q] = q * nin;
+    const int rc = run_phased(c, lo, kPhasedGather, nullptr);
+    if (rc >= 0) return rc;
+  }
   for (size_t st = 0; st < sch->steps.size(); st++) {
     // merge the step's transfers that share (source rank, block) into one
     // multi-destination copy: one load, several stores

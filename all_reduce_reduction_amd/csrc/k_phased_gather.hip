@@ -1,0 +1,143 @@
+// k_phased_gather.hip -- the direct all-gather for large messages, phased
+// (gfx950).
+//
+// The all-gather of "Inside NCCL all-reduce" (section "What all-reduce
+// promises": reduce-scatter then all-gather; the all-gather alone gives every
+// rank every rank's block): out[r][q n_in + i] = in[q][i].  Done directly it
+// reads each block once and writes it p times, (p + 1) S bytes with S = the
+// output per rank, almost all of them writes.  The phased form (the grid
+// barrier and its slots are those of the phased fold, phased_impl.h): the
+// grid's workgroups load their spans of the source blocks into VGPRs -- 32
+// (16 at p = 16) 16-byte vectors per lane, all in flight at once, no
+// arithmetic -- meet at the grid barrier, then store them to the p outputs
+// output by output (the workgroups of block j starting at output j), and
+// meet again before the next phase.  Measured against the fused copy
+// (one load, p stores per vector, every workgroup reading and writing at
+// once) in the all-gather's own section of the design notes.
+#include "phased_impl.h"
+
+namespace simar {
+
+// E: element bytes (the copy moves 16-byte vectors; E matters for the chunk
+// bounds and the ragged edges only)
+template <int E, int P>
+__global__ void __launch_bounds__(kBlock) k_gather_phased(PhasedArgs a) {
+  typedef typename std::conditional<E == 4, uint32_t, uint16_t>::type U;
+  constexpr int V = 16 / E;
+  constexpr int K = PhasedShape<P>::K;
+  const int j = (int)(blockIdx.x % (unsigned)P);
+  const int t = (int)(blockIdx.x / (unsigned)P);
+  // output block j = [lo, hi) holds source rank j's input, element i of the
+  // block at index i - lo of that input (lo is a multiple of V: the host
+  // checks, so input and output offsets are both 16-byte aligned)
+  const int64_t lo = a.lo[j], hi = a.lo[j + 1];
+  const char* xj = (const char*)a.x[j] - lo * E;  // indexed by output element (only bytes >= lo*E are touched)
+  __shared__ unsigned long long s_rel;
+  void* yp[P];
+#pragma unroll
+  for (int r = 0; r < P; r++) yp[r] = a.y[r];
+
+  int64_t head = (V - lo % V) % V;
+  if (head > hi - lo) head = hi - lo;
+  const int64_t vbeg = lo + head;
+  const int64_t nvec = (hi - vbeg) / V;
+  const int64_t tail_beg = vbeg + nvec * V;
+  const int64_t nscalar = head + (hi - tail_beg);
+  const int tid = threadIdx.x;
+  const int64_t span = (int64_t)kBlock * K;
+  const uint32_t lane = lane_offset((uint32_t)tid * 16u);
+
+  const unsigned long long nbar = a.nphase > 0 ? 2ull * a.nphase - 1 : 0ull;
+  unsigned long long nb = 0;
+  for (int ph = 0; ph < a.nphase; ph++) {
+    const int64_t s0 = ((int64_t)ph * a.tiles + t) * span;
+    const int64_t sbyte = vbeg * E + s0 * 16;
+    const bool whole = s0 + span <= nvec;
+    u32x4 R[K];
+    if (whole) {
+#pragma unroll
+      for (int k = 0; k < K; k++) R[k] = ld16u(xj, sbyte + (int64_t)k * kBlock * 16, lane);
+    }
+    phased_barrier(a, nbar, ++nb, &s_rel);
+    if (whole) {
+#pragma unroll
+      for (int rr = 0; rr < P; rr++) {
+        const int r = (rr + j) & (P - 1);
+        void* yr = yp[0];
+#pragma unroll
+        for (int q = 1; q < P; q++)
+          if (q == r) yr = yp[q];
+#pragma unroll
+        for (int k = 0; k < K; k++) st16u(yr, sbyte + (int64_t)k * kBlock * 16, lane, R[k]);
+      }
+    }
+    if (ph + 1 < a.nphase) phased_barrier(a, nbar, ++nb, &s_rel);
+  }
+
+  // the block's vectors past its last whole span, then its ragged edges
+  for (int64_t v = nvec / span * span + (int64_t)t * kBlock + tid; v < nvec; v += (int64_t)a.tiles * kBlock) {
+    const int64_t vb = (vbeg + v * V) * E;
+    const u32x4 w = ld16(xj, vb);
+#pragma unroll
+    for (int r = 0; r < P; r++) st16(yp[r], vb, w);
+  }
+  for (int64_t s = (int64_t)t * kBlock + tid; s < nscalar; s += (int64_t)a.tiles * kBlock) {
+    const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
+    const U w = ((const U*)xj)[i];
+#pragma unroll
+    for (int r = 0; r < P; r++) ((U*)yp[r])[i] = w;
+  }
+  phased_arrive(a, nbar, &s_rel);
+}
+
+namespace {
+
+template <int E>
+hipError_t gather_by_p(int p, const PhasedArgs& a, hipStream_t s) {
+  const dim3 g((unsigned)a.tiles * (unsigned)p), b(kBlock);
+  switch (p) {
+    case 2: return launch<k_gather_phased<E, 2>>(g, b, s, a);
+    case 4: return launch<k_gather_phased<E, 4>>(g, b, s, a);
+    case 8: return launch<k_gather_phased<E, 8>>(g, b, s, a);
+    case 16: return launch<k_gather_phased<E, 16>>(g, b, s, a);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int E, int P>
+int gather_occ_of() {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)k_gather_phased<E, P>, kBlock, 0) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return nb;
+}
+
+template <int E>
+int gather_occ(int p) {
+  switch (p) {
+    case 2: return gather_occ_of<E, 2>();
+    case 4: return gather_occ_of<E, 4>();
+    case 8: return gather_occ_of<E, 8>();
+    case 16: return gather_occ_of<E, 16>();
+  }
+  return 0;
+}
+
+}  // namespace
+
+hipError_t launch_gather_phased(int esize, int p, const PhasedArgs& a, hipStream_t s) {
+  if (esize == 4) return gather_by_p<4>(p, a, s);
+  if (esize == 2) return gather_by_p<2>(p, a, s);
+  return hipErrorInvalidValue;
+}
+
+int gather_phased_blocks_per_cu(int esize, int p) {
+  if (esize == 4) return gather_occ<4>(p);
+  if (esize == 2) return gather_occ<2>(p);
+  return 0;
+}
+
+}  // namespace simar

@@ -171,6 +171,15 @@ def test_phased_selection_rules(orc, lib):
         return sim.sim_debug_get("phased_last")
     assert ran_rs(32 << 20) == 0
     assert ran_rs(64 << 20) == 1
+
+    def ran_ag(out_bytes):
+        n_in = out_bytes // 2 // 8
+        xs = [torch.zeros(n_in, dtype=torch.int16, device="cuda:0") for _ in range(8)]
+        ys = [torch.empty(8 * n_in, dtype=torch.int16, device="cuda:0") for _ in range(8)]
+        assert sim.sim_all_gather(ptrs(xs), ptrs(ys), 8, n_in, "bf16", "allpairs", stream()) == 0
+        return sim.sim_debug_get("phased_last")
+    assert ran_ag(32 << 20) == 0
+    assert ran_ag(64 << 20) == 1
     torch.cuda.synchronize()
     assert sim.sim_debug_get("phased_expired") == 0
 
@@ -258,6 +267,47 @@ def test_phased_owner_only_matches_oracle(orc, lib, p, dtype, op):
                 for r in range(p):
                     assert_parity(got[r], want[r], dtype,
                                   f"RS phased={phased} p={p} {dtype} {op} n_out={n_out} inplace={inplace} r{r}")
+    finally:
+        sim.sim_debug_set("phased", 0)
+        sim.sim_debug_set("workgroups", 0)
+    assert sim.sim_check_error(stream()) == 0
+    assert sim.sim_debug_get("phased_expired") == 0
+
+
+@pytest.mark.parametrize("p", [2, 4, 8, 16])
+@pytest.mark.parametrize("dtype", ["int32", "fp32", "fp16", "bf16"])
+def test_phased_all_gather_matches_oracle(orc, lib, p, dtype):
+    """The phased direct all-gather: several phases and a rest per block, out
+    of place and in place (each rank's input is its own block of its
+    output); a block that does not fill whole 16-byte vectors keeps the fused
+    copy.  Copies are exact: compared bit for bit."""
+    from tests.gpu_util import assert_parity, empty_like_poisoned, ptrs, stream, to_device, to_host
+    sim = lib
+    V = 16 // (2 if dtype in ("fp16", "bf16") else 4)
+    vecs = 256 * (32 if p <= 8 else 16)
+    sim.sim_debug_set("phased", 1)
+    sim.sim_debug_set("workgroups", 2 * p)
+    try:
+        for n_in, phased in ((V * (5 * vecs + 3 * 256 + 7), 1), (V * (2 * vecs) + 3, 0)):
+            xs = _inputs(dtype, "sum", p, n_in, 40 + p)
+            want, _ = orc.all_gather(xs, dtype, "allpairs")
+            din = to_device(xs, dtype)
+            dout = empty_like_poisoned(p * n_in, dtype, p)
+            assert sim.sim_all_gather(ptrs(din), ptrs(dout), p, n_in, dtype, "allpairs", stream()) == 0
+            assert sim.sim_debug_get("phased_last") == phased
+            got = to_host(dout, dtype)
+            for r in range(p):
+                assert_parity(got[r], want[r], dtype, f"AG phased={phased} p={p} {dtype} n_in={n_in} r{r}")
+            if phased:
+                outs = empty_like_poisoned(p * n_in, dtype, p)
+                for r in range(p):
+                    outs[r][r * n_in:(r + 1) * n_in].copy_(din[r])
+                ins = [o[r * n_in:(r + 1) * n_in] for r, o in enumerate(outs)]
+                assert sim.sim_all_gather(ptrs(ins), ptrs(outs), p, n_in, dtype, "allpairs", stream()) == 0
+                assert sim.sim_debug_get("phased_last") == 1
+                got = to_host(outs, dtype)
+                for r in range(p):
+                    assert_parity(got[r], want[r], dtype, f"AG phased in place p={p} {dtype} r{r}")
     finally:
         sim.sim_debug_set("phased", 0)
         sim.sim_debug_set("workgroups", 0)
