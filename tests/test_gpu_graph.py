@@ -134,3 +134,43 @@ def test_scratch_does_not_grow_under_capture_and_outgrown_scratch_is_kept(orc, l
         assert_parity(got[r], want[r], "bf16", f"replay after growth r{r}")
     del graph
     sim.sim_init(0, 8, 0)
+
+
+def test_phased_sizes_capture_the_fused_kernels(orc, lib):
+    """At a size where the one-shot runs phased, a captured call takes the
+    fused kernel (the phased grid's barrier counts are fixed when it is
+    enqueued, which a replay would repeat); every replay matches the
+    oracle, and the eager call after the replays runs phased again."""
+    import torch
+    from tests.gpu_util import assert_parity, ptrs, stream, to_device, to_host
+    sim = lib
+    p, n = 8, (64 << 20) // 2 + 8 * 3  # 64 MiB of bf16 per rank, chunks a little ragged
+    xs = _fresh(p, n, "bf16", 70, orc)
+    din = to_device(xs, "bf16")
+    dout = [torch.empty(n, dtype=torch.int16, device="cuda:0") for _ in range(p)]
+    assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, "bf16", "sum", "oneshot", stream()) == 0
+    assert sim.sim_debug_get("phased_last") == 1
+    torch.cuda.synchronize()
+    graph, st = _capture(sim, din, dout, p, n, "bf16", "oneshot")
+    assert st == 0 and sim.sim_debug_get("phased_last") == 0
+    # compare a sample of indices on every rank, and every element of rank 0
+    idx = np.unique(np.concatenate([np.arange(0, n, 9973), np.arange(n - 64, n)]))
+    for rep in range(2):
+        xr = _fresh(p, n, "bf16", 71 + rep, orc)
+        for t, x in zip(din, to_device(xr, "bf16")):
+            t.copy_(x)
+        for t in dout:
+            t.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = to_host(dout, "bf16")
+        want = orc.allreduce_at(xr, "bf16", "sum", "oneshot", idx)
+        for r in range(p):
+            assert_parity(got[r][idx], want, "bf16", f"captured one-shot replay {rep} r{r}")
+        want0, _ = orc.allreduce(xr, "bf16", "sum", "oneshot")
+        assert_parity(got[0], want0[0], "bf16", f"captured one-shot replay {rep} rank 0 in full")
+    del graph
+    assert sim.sim_allreduce(ptrs(din), ptrs(dout), p, n, "bf16", "sum", "oneshot", stream()) == 0
+    assert sim.sim_debug_get("phased_last") == 1
+    torch.cuda.synchronize()
