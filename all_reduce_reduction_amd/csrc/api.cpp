@@ -134,7 +134,7 @@ struct Ctx {
   unsigned long long ph_ctr[kPhasedSlots] = {};
   unsigned long long ph_seq[kPhasedSlots] = {};
   unsigned ph_next = 0;
-  int ph_occ[4][5][4][3] = {};  // [dtype][op][log2 p - 1][form]: resident workgroups per CU (-1: none)
+  int ph_occ[4][5][4][4] = {};  // [dtype][op][log2 p - 1][form]: resident workgroups per CU (-1: none)
   int phased_mode = 0;       // 0: from phased_min bytes per rank on, 1: always, 2: never
   size_t phased_min = kPhasedMinBytes;
   bool last_phased = false;  // the current (or last) call ran a phased fold
@@ -407,10 +407,13 @@ int run_fold(const Call& c, bool all_out, const int64_t* lo, const int64_t* out_
 // rank on (of the input for the fold, of the output for the gather).
 // Returns SIM_OK after enqueueing it, a negative value when the call should
 // take the fused kernel instead, or an error.
-enum PhasedForm { kPhasedAll = 0, kPhasedOwner = 1, kPhasedGather = 2 };
+// kPhasedFanout: all-pairs step 2, owner j's finished chunk from output j to
+// the other outputs, with the gather's kernel.
+enum PhasedForm { kPhasedAll = 0, kPhasedOwner = 1, kPhasedGather = 2, kPhasedFanout = 3 };
 int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t* out_shift) {
   const int p = c.p;
   const bool all_out = form != kPhasedOwner;
+  const bool copy = form == kPhasedGather || form == kPhasedFanout;
   if (!g.ph_mem || !g.ph_dev_done || c.noalloc || g.capturing || g_max_wg > 0 || g.phased_mode == 2) return -1;
   if (p != 2 && p != 4 && p != 8 && p != 16) return -1;
   const int E = esize_of(c.dtype);
@@ -442,9 +445,10 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
       __atomic_load_n(g.ph_host_done, __ATOMIC_ACQUIRE) != g.ph_launched)
     return -1;
   const int pi = p == 2 ? 0 : p == 4 ? 1 : p == 8 ? 2 : 3;
-  int& occ = g.ph_occ[c.dtype][form == kPhasedGather ? 0 : c.op][pi][form];
+  int& occ = g.ph_occ[c.dtype][copy ? 0 : c.op][pi][form];
   if (occ == 0) {
-    occ = form == kPhasedGather ? gather_phased_blocks_per_cu(E, p) : fold_phased_blocks_per_cu(c.dtype, c.op, p, all_out);
+    occ = copy ? gather_phased_blocks_per_cu(E, p, form == kPhasedFanout)
+               : fold_phased_blocks_per_cu(c.dtype, c.op, p, all_out);
     if (occ < 1) occ = -1;
   }
   if (occ < 1) return -1;
@@ -471,7 +475,9 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
   PhasedArgs a;
   std::memset(&a, 0, sizeof a);
   for (int q = 0; q < p; q++) {
-    a.x[q] = c.x[q];
+    // the fan-out's block q comes from output q itself (the kernel indexes
+    // its source as x[q] - lo[q] by output element)
+    a.x[q] = form == kPhasedFanout ? (const void*)((const char*)c.y[q] + lo[q] * E) : c.x[q];
     a.y[q] = c.y[q];
   }
   for (int q = 0; q <= p; q++) a.lo[q] = lo[q];
@@ -489,8 +495,8 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
   a.tiles = (int)tiles;
   a.nphase = (int)nphase;
   a.inv_p = inv_p_of(p);
-  const int rc = hip_err(form == kPhasedGather ? launch_gather_phased(E, p, a, c.s)
-                                               : launch_fold_phased(c.dtype, c.op, p, all_out, a, c.s));
+  const int rc = hip_err(copy ? launch_gather_phased(E, p, form == kPhasedFanout, a, c.s)
+                              : launch_fold_phased(c.dtype, c.op, p, all_out, a, c.s));
   if (rc) return rc;
 
   // the counts this call adds: every workgroup meets every barrier and
@@ -949,6 +955,12 @@ int run_allreduce(const Call& c) {
       int rc = run_phased(c, lo, kPhasedOwner, nullptr);  // step 1: GATHER_REDUCE into each owner
       if (rc < 0) rc = run_fold(c, false, lo, nullptr, set);
       if (rc) return rc;
+      const bool step1_phased = g.last_phased;
+      rc = run_phased(c, lo, kPhasedFanout, nullptr);  // step 2 (FANOUT), phased
+      if (rc >= 0) {
+        g.last_phased = g.last_phased || step1_phased;
+        return rc;
+      }
       if (set) {  // step 2 (FANOUT) from the same table entry
         const int V = 16 / esize_of(c.dtype);
         int64_t maxchunk = 0;

@@ -1,5 +1,5 @@
-// k_phased_gather.hip -- the direct all-gather for large messages, phased
-// (gfx950).
+// k_phased_gather.hip -- the direct all-gather and the all-pairs fan-out
+// for large messages, phased (gfx950).
 //
 // The all-gather of "Inside NCCL all-reduce" (section "What all-reduce
 // promises": reduce-scatter then all-gather; the all-gather alone gives every
@@ -20,7 +20,9 @@ namespace simar {
 
 // E: element bytes (the copy moves 16-byte vectors; E matters for the chunk
 // bounds and the ragged edges only)
-template <int E, int P>
+// SKIP_OWN: the all-pairs fan-out (step 2): block j is owner j's finished
+// chunk, already in output j, copied to the other p - 1 outputs only.
+template <int E, int P, bool SKIP_OWN>
 __global__ void __launch_bounds__(kBlock) k_gather_phased(PhasedArgs a) {
   typedef typename std::conditional<E == 4, uint32_t, uint16_t>::type U;
   constexpr int V = 16 / E;
@@ -61,7 +63,7 @@ __global__ void __launch_bounds__(kBlock) k_gather_phased(PhasedArgs a) {
     phased_barrier(a, nbar, ++nb, &s_rel);
     if (whole) {
 #pragma unroll
-      for (int rr = 0; rr < P; rr++) {
+      for (int rr = SKIP_OWN ? 1 : 0; rr < P; rr++) {
         const int r = (rr + j) & (P - 1);
         void* yr = yp[0];
 #pragma unroll
@@ -79,35 +81,37 @@ __global__ void __launch_bounds__(kBlock) k_gather_phased(PhasedArgs a) {
     const int64_t vb = (vbeg + v * V) * E;
     const u32x4 w = ld16(xj, vb);
 #pragma unroll
-    for (int r = 0; r < P; r++) st16(yp[r], vb, w);
+    for (int r = 0; r < P; r++)
+      if (!SKIP_OWN || r != j) st16(yp[r], vb, w);
   }
   for (int64_t s = (int64_t)t * kBlock + tid; s < nscalar; s += (int64_t)a.tiles * kBlock) {
     const int64_t i = (s < head) ? lo + s : tail_beg + (s - head);
     const U w = ((const U*)xj)[i];
 #pragma unroll
-    for (int r = 0; r < P; r++) ((U*)yp[r])[i] = w;
+    for (int r = 0; r < P; r++)
+      if (!SKIP_OWN || r != j) ((U*)yp[r])[i] = w;
   }
   phased_arrive(a, nbar, &s_rel);
 }
 
 namespace {
 
-template <int E>
+template <int E, bool SKIP_OWN>
 hipError_t gather_by_p(int p, const PhasedArgs& a, hipStream_t s) {
   const dim3 g((unsigned)a.tiles * (unsigned)p), b(kBlock);
   switch (p) {
-    case 2: return launch<k_gather_phased<E, 2>>(g, b, s, a);
-    case 4: return launch<k_gather_phased<E, 4>>(g, b, s, a);
-    case 8: return launch<k_gather_phased<E, 8>>(g, b, s, a);
-    case 16: return launch<k_gather_phased<E, 16>>(g, b, s, a);
+    case 2: return launch<k_gather_phased<E, 2, SKIP_OWN>>(g, b, s, a);
+    case 4: return launch<k_gather_phased<E, 4, SKIP_OWN>>(g, b, s, a);
+    case 8: return launch<k_gather_phased<E, 8, SKIP_OWN>>(g, b, s, a);
+    case 16: return launch<k_gather_phased<E, 16, SKIP_OWN>>(g, b, s, a);
   }
   return hipErrorInvalidValue;
 }
 
-template <int E, int P>
+template <int E, int P, bool SKIP_OWN>
 int gather_occ_of() {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)k_gather_phased<E, P>, kBlock, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)k_gather_phased<E, P, SKIP_OWN>, kBlock, 0) !=
       hipSuccess) {
     (void)hipGetLastError();
     return 0;
@@ -115,28 +119,28 @@ int gather_occ_of() {
   return nb;
 }
 
-template <int E>
+template <int E, bool SKIP_OWN>
 int gather_occ(int p) {
   switch (p) {
-    case 2: return gather_occ_of<E, 2>();
-    case 4: return gather_occ_of<E, 4>();
-    case 8: return gather_occ_of<E, 8>();
-    case 16: return gather_occ_of<E, 16>();
+    case 2: return gather_occ_of<E, 2, SKIP_OWN>();
+    case 4: return gather_occ_of<E, 4, SKIP_OWN>();
+    case 8: return gather_occ_of<E, 8, SKIP_OWN>();
+    case 16: return gather_occ_of<E, 16, SKIP_OWN>();
   }
   return 0;
 }
 
 }  // namespace
 
-hipError_t launch_gather_phased(int esize, int p, const PhasedArgs& a, hipStream_t s) {
-  if (esize == 4) return gather_by_p<4>(p, a, s);
-  if (esize == 2) return gather_by_p<2>(p, a, s);
+hipError_t launch_gather_phased(int esize, int p, bool skip_own, const PhasedArgs& a, hipStream_t s) {
+  if (esize == 4) return skip_own ? gather_by_p<4, true>(p, a, s) : gather_by_p<4, false>(p, a, s);
+  if (esize == 2) return skip_own ? gather_by_p<2, true>(p, a, s) : gather_by_p<2, false>(p, a, s);
   return hipErrorInvalidValue;
 }
 
-int gather_phased_blocks_per_cu(int esize, int p) {
-  if (esize == 4) return gather_occ<4>(p);
-  if (esize == 2) return gather_occ<2>(p);
+int gather_phased_blocks_per_cu(int esize, int p, bool skip_own) {
+  if (esize == 4) return skip_own ? gather_occ<4, true>(p) : gather_occ<4, false>(p);
+  if (esize == 2) return skip_own ? gather_occ<2, true>(p) : gather_occ<2, false>(p);
   return 0;
 }
 

@@ -317,10 +317,12 @@ int allpairs_persistent_blocks_per_cu(int dtype, int op, int p);
 hipError_t launch_fold_phased(int dtype, int op, int p, bool all_out, const PhasedArgs& a, hipStream_t s);
 int fold_phased_blocks_per_cu(int dtype, int op, int p, bool all_out);
 int fold_phased_vecs_per_lane(int p);
-// The phased direct all-gather (k_phased_gather.hip; out_shift unused, lo
-// the output blocks, each a multiple of 16 bytes from the buffer start).
-hipError_t launch_gather_phased(int esize, int p, const PhasedArgs& a, hipStream_t s);
-int gather_phased_blocks_per_cu(int esize, int p);
+// The phased copy (k_phased_gather.hip; out_shift unused, lo the output
+// blocks, x[j] - lo[j] the source of block j indexed by output element):
+// the direct all-gather (every output), or with skip_own the all-pairs
+// fan-out (every output but j).
+hipError_t launch_gather_phased(int esize, int p, bool skip_own, const PhasedArgs& a, hipStream_t s);
+int gather_phased_blocks_per_cu(int esize, int p, bool skip_own);
 template <bool ALL_OUT>
 hipError_t phased_launch(int dtype, int op, int p, const PhasedArgs& a, hipStream_t s);
 template <bool ALL_OUT>

@@ -67,7 +67,7 @@
  *     the calibration checks), but it may with another calibration file:
  *     callers that run other kernels concurrently should name a schedule.
  *   - Phased kernels: from 32 MiB per rank SIM_ALGO_ONESHOT, and from 64 MiB
- *     step 1 of SIM_ALGO_ALLPAIRS, the direct (SIM_ALGO_ALLPAIRS)
+ *     both steps of SIM_ALGO_ALLPAIRS, the direct (SIM_ALGO_ALLPAIRS)
  *     reduce-scatter (input bytes per rank; when n_out_per_rank fills whole
  *     16-byte vectors) and the direct all-gather (output bytes per rank;
  *     when n_in_per_rank fills whole 16-byte vectors), for p = 2, 4, 8, 16
@@ -432,12 +432,12 @@ enum {
   SIM_DEBUG_PTR_SETS = 12,     /* get only: pointer sets the table holds */
   SIM_DEBUG_RING_LL_MAX = 13,  /* single-launch ring: largest message (bytes per rank) sent as
                                   LL packets (default 256 KiB; 0 = never) */
-  SIM_DEBUG_PHASED = 14,       /* phased kernels (one-shot, all-pairs step 1, direct reduce-scatter
-                                  and all-gather):
+  SIM_DEBUG_PHASED = 14,       /* phased kernels (one-shot, all-pairs, direct reduce-scatter and
+                                  all-gather):
                                   0 from SIM_DEBUG_PHASED_MIN bytes per rank on (default),
                                   1 whenever the call allows it, 2 never */
   SIM_DEBUG_PHASED_MIN = 15,   /* bytes per rank from which the one-shot runs phased (default
-                                  32 MiB); all-pairs step 1, the direct reduce-scatter (input bytes)
+                                  32 MiB); the all-pairs, the direct reduce-scatter (input bytes)
                                   and the direct all-gather (output bytes) from twice that */
   SIM_DEBUG_PHASED_EXPIRED = 16, /* phased fold barrier waits that gave up at the spin limit
                                   (synchronizes the device; set only to 0, which clears it) */
