@@ -55,7 +55,7 @@ namespace {
 // (with p = 16, 16 vectors per lane: the 16 operands of a fold take 64 VGPRs)
 template <int P> struct PhasedShape {
   static constexpr int K = P <= 8 ? 32 : 16;
-  static constexpr int D = P <= 8 ? 2 : 1;
+  static constexpr int D = P >= 16 ? 1 : 16 / P;  // about 16 loads in flight per lane
 };
 
 // One arrival at the slot's counter: at each barrier and once more when a
