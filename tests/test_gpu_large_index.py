@@ -74,3 +74,47 @@ def test_past_4GiB_per_rank(orc, big, algo, G, op):
     x1 = orc.bf16_to_f32(xs[1][idx])
     exact = x0 + x1 if op == "sum" else np.maximum(x0, x1)
     assert (orc.bf16_to_f32(got) == exact).all()
+
+
+def test_phased_reduce_scatter_and_all_gather_past_4GiB(orc, big):
+    """The phased direct reduce-scatter (input past 2^31 elements and 2^32
+    bytes per rank) and the phased direct all-gather (output past both),
+    p = 2, bf16 integer values: sampled elements around every limit against
+    the exact results, and the all-gather's two outputs compared in full."""
+    import torch
+
+    from tests.gpu_util import ptrs, stream
+    sim, xs, din, dout, idx = big
+    n_out = (1 << 30) + (1 << 15)  # whole 16-byte vectors per chunk: the phased forms run
+    n_in = 2 * n_out
+    dev = din[0].device
+    rs = [torch.full((n_out,), 0x7E5A, dtype=torch.int16, device=dev) for _ in range(P)]
+    print(f"large-index phased reduce-scatter p={P} n_in={n_in}", flush=True)
+    assert sim.sim_reduce_scatter(ptrs(din), ptrs(rs), P, n_out, "bf16", "sum", "allpairs", stream()) == 0
+    assert sim.sim_debug_get("phased_last") == 1
+    assert sim.sim_check_error(stream()) == 0
+    sidx = np.unique(np.concatenate([
+        np.array([0, 1, 7, 8, (1 << 30) - 1, 1 << 30, n_out - 9, n_out - 1], dtype=np.int64),
+        np.random.default_rng(7).integers(0, n_out, 4096, dtype=np.int64)]))
+    ti = torch.from_numpy(sidx).to(dev)
+    for r in range(P):
+        got = orc.bf16_to_f32(rs[r][ti].cpu().numpy().view(np.uint16))
+        src = r * n_out + sidx  # element of the all-reduce the owner r holds
+        want = orc.bf16_to_f32(xs[0][src]) + orc.bf16_to_f32(xs[1][src])
+        assert (got == want).all(), f"reduce-scatter rank {r}"
+    del rs
+    # all-gather: rank q's first n_out elements into block q of every output
+    for t in dout:
+        t.fill_(0x7E5A)
+    ins = [d[:n_out] for d in din]
+    print(f"large-index phased all-gather p={P} n_out={P * n_out}", flush=True)
+    assert sim.sim_all_gather(ptrs(ins), ptrs(dout), P, n_out, "bf16", "allpairs", stream()) == 0
+    assert sim.sim_debug_get("phased_last") == 1
+    assert sim.sim_check_error(stream()) == 0
+    assert torch.equal(dout[0][:n_in], dout[1][:n_in]), "outputs differ"
+    gidx = np.unique(np.concatenate([sidx, n_out + sidx, np.array([(1 << 31) - 1, 1 << 31, n_in - 1])]))
+    got = dout[0][torch.from_numpy(gidx).to(dev)].cpu().numpy().view(np.uint16)
+    q = gidx // n_out
+    want = np.where(q == 0, xs[0][gidx % n_out], xs[1][gidx % n_out])
+    assert (got == want).all()
+    torch.cuda.synchronize()
