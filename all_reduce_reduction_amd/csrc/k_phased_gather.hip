@@ -7,7 +7,8 @@
 // reads each block once and writes it p times, (p + 1) S bytes with S = the
 // output per rank, almost all of them writes.  The phased form (the grid
 // barrier and its slots are those of the phased fold, phased_impl.h): the
-// grid's workgroups load their spans of the source blocks into VGPRs -- 32
+// grid's workgroups load their parts of the source blocks (laid out as the
+// phased fold's, phase_span) into VGPRs -- 32
 // (16 at p = 16) 16-byte vectors per lane, all in flight at once, no
 // arithmetic -- meet at the grid barrier, then store them to the p outputs
 // output by output (the workgroups of block j starting at output j), and
@@ -52,13 +53,14 @@ __global__ void __launch_bounds__(kBlock) k_gather_phased(PhasedArgs a) {
   const unsigned long long nbar = a.nphase > 0 ? 2ull * a.nphase - 1 : 0ull;
   unsigned long long nb = 0;
   for (int ph = 0; ph < a.nphase; ph++) {
-    const int64_t s0 = ((int64_t)ph * a.tiles + t) * span;
-    const int64_t sbyte = vbeg * E + s0 * 16;
-    const bool whole = s0 + span <= nvec;
+    const PhaseSpan sp = phase_span(ph, t, a.tiles, nvec, span);
+    const int64_t sbyte = vbeg * E + sp.v0 * 16;
+    const int64_t kst = sp.vstride * 16;
+    const bool whole = sp.whole;
     u32x4 R[K];
     if (whole) {
 #pragma unroll
-      for (int k = 0; k < K; k++) R[k] = ld16u(xj, sbyte + (int64_t)k * kBlock * 16, lane);
+      for (int k = 0; k < K; k++) R[k] = ld16u(xj, sbyte + (int64_t)k * kst, lane);
     }
     phased_barrier(a, nbar, ++nb, &s_rel);
     if (whole) {
@@ -70,7 +72,7 @@ __global__ void __launch_bounds__(kBlock) k_gather_phased(PhasedArgs a) {
         for (int q = 1; q < P; q++)
           if (q == r) yr = yp[q];
 #pragma unroll
-        for (int k = 0; k < K; k++) st16u(yr, sbyte + (int64_t)k * kBlock * 16, lane, R[k]);
+        for (int k = 0; k < K; k++) st16u(yr, sbyte + (int64_t)k * kst, lane, R[k]);
       }
     }
     if (ph + 1 < a.nphase) phased_barrier(a, nbar, ++nb, &s_rel);
