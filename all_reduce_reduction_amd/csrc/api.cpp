@@ -41,10 +41,11 @@ constexpr int kPtrSets = 512;
 // 44.7 us at 128 KiB and 37.4 against 45.3 us at 256 KiB.
 constexpr size_t kRingLLMaxBytes = 256 << 10;
 // The phased one-shot (k_phased.hip) from this many bytes per rank on.
-// Measured on MI355X, p = 8 bf16, against the fused one-shot: 16 MiB 52.4
-// against 44.9 us, 32 MiB 89.5 against 93.3, 64 MiB 174 against 196,
-// 128 MiB 353 against 386, 256 MiB 711 against 759.
-constexpr size_t kPhasedMinBytes = 32 << 20;
+// Measured on MI355X, p = 8, against the fused one-shot (bf16; fp32):
+// 12 MiB 36.2 against 35.3 us; 37.2 against 37.5, 16 MiB 44.5 against 46.3;
+// 44.6 against 48.5, 32 MiB 84.7 against 94.1; 89.2 against 93.1, 64 MiB
+// 174 against 201, 128 MiB 347 against 404.
+constexpr size_t kPhasedMinBytes = 16 << 20;
 // Polls before a phased one-shot barrier wait gives up.  A wait normally
 // ends within the read half's tail (tens of polls); the barrier only orders
 // traffic, so when something keeps the grid from being resident at once
@@ -417,16 +418,18 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
   if (!g.ph_mem || !g.ph_dev_done || c.noalloc || g.capturing || g_max_wg > 0 || g.phased_mode == 2) return -1;
   if (p != 2 && p != 4 && p != 8 && p != 16) return -1;
   const int E = esize_of(c.dtype);
-  // The owner-only fold writes S bytes, not p S, and the gather reads only
-  // S / p: their phase separation gains less, and a phase only partly
-  // filled (its 64 MiB of results holds a 32 MiB message twice) costs more
-  // than it gains.  Measured on MI355X, p = 8, phased against fused: direct
-  // reduce-scatter 32 MiB input per rank 50 against 48 us, 64 MiB 94-105
-  // against 103-107, 256 MiB 378-413 against 407-417; direct all-gather
-  // 32 MiB output per rank 58-60 against 55-57, 64 MiB 109-110 against
-  // 115, 256 MiB 428-431 against 450-458.  Both start at twice the
-  // one-shot's threshold.
-  const size_t min_bytes = form == kPhasedAll ? g.phased_min : 2 * g.phased_min;
+  // The owner-only fold writes S bytes, not p S, and the copy reads only
+  // S / p: their phase separation gains less than the one-shot's against
+  // the barriers' cost, and the copy's last phase, not dealt out evenly
+  // (k_phased_gather.hip), leaves workgroups idle.  Measured on MI355X,
+  // p = 8 (bf16; fp32), phased against fused: direct reduce-scatter, input
+  // bytes per rank, 24 MiB 38.6 against 37.0 us; 39.6 against 37.9, 32 MiB
+  // 48.9 against 51.1; 47.5 against 49.0, 64 MiB 93.6 against 104.0;
+  // direct all-gather, output bytes per rank, 48 MiB 84.9 against 85.3;
+  // 85.0 against 86.3, 56 MiB 98.7 against 109.8; 99.9 against 107.1,
+  // 64 MiB 103.1 against 117.6.  So: owner-only from twice the one-shot's
+  // threshold, the copy from four times.
+  const size_t min_bytes = form == kPhasedAll ? g.phased_min : form == kPhasedOwner ? 2 * g.phased_min : 4 * g.phased_min;
   if (g.phased_mode == 0 && c.n * (size_t)E < min_bytes) return -1;
   // owner-only with shifted outputs, and the gather's inputs: whole 16-byte
   // vectors need 16-byte aligned offsets on both sides
@@ -460,17 +463,21 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
   const int64_t tiles = std::max<int64_t>(1, G / p);
   G = tiles * p;
   if (G > g.ph_gmax) return -1;
-  // whole spans of the largest chunk (a chunk's rest is done after the phases)
+  // The fold takes every whole block (kBlock 16-byte vectors) of the
+  // largest chunk in phases of tiles * K blocks, the last one dealt out
+  // evenly; the copy takes every whole span (K blocks) in phases of tiles
+  // spans.  What is past them is done after the phases.
   const int V = 16 / E;
-  const int64_t span = (int64_t)kBlock * fold_phased_vecs_per_lane(p);
-  int64_t nfull = 0;
+  const int64_t K = fold_phased_vecs_per_lane(p);
+  int64_t nmax = 0;  // whole blocks (fold) or spans (copy) of the largest chunk
   for (int q = 0; q < p; q++) {
     int64_t head = (V - lo[q] % V) % V;
     head = std::min(head, lo[q + 1] - lo[q]);
     const int64_t nvec = (lo[q + 1] - lo[q] - head) / V;
-    nfull = std::max(nfull, nvec / span);
+    nmax = std::max(nmax, nvec / (copy ? kBlock * K : kBlock));
   }
-  const int64_t nphase = (nfull + tiles - 1) / tiles;
+  const int64_t per_phase = copy ? tiles : tiles * K;
+  const int64_t nphase = (nmax + per_phase - 1) / per_phase;
   const int64_t nbar = nphase > 0 ? 2 * nphase - 1 : 0;  // plus one arrival per workgroup on leaving
   PhasedArgs a;
   std::memset(&a, 0, sizeof a);

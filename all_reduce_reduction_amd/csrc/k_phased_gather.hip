@@ -19,6 +19,35 @@
 
 namespace simar {
 
+namespace {
+
+// Where a workgroup's K vectors per lane lie in phase ph of its block (nvec
+// whole vectors, tiles workgroups, span = kBlock * K vectors each).  While
+// the whole phase lies inside the block, the workgroups interleave as the
+// phased fold's do (phase_blocks): the workgroup's k-th group of kBlock
+// vectors is group k * tiles + t of the phase.  The phase that reaches the
+// block's end gives each workgroup one contiguous span, used only if whole,
+// and the vectors past the last whole span are copied one by one after the
+// phases: the phases' whole spans cover exactly the block's first
+// floor(nvec / span) * span vectors.  (Dealing that last phase out evenly,
+// as the fold does, needs loads the workgroup may skip; the compiler then
+// waited for every earlier access before each store -- one store in flight
+// per wave -- and the all-gather at 64 MiB per rank ran 7% slower.)
+struct PhaseSpan {
+  int64_t v0;       // the lane-0 vector of the workgroup's first group
+  int64_t vstride;  // vectors from one of its groups to the next
+  bool whole;       // all K groups inside the block (uniform over the workgroup)
+};
+__device__ __forceinline__ PhaseSpan phase_span(int ph, int t, int tiles, int64_t nvec, int64_t span) {
+  const int64_t ptile = (int64_t)tiles * span;  // a block's vectors per phase
+  if ((int64_t)(ph + 1) * ptile <= nvec)
+    return {(int64_t)ph * ptile + (int64_t)t * kBlock, (int64_t)tiles * kBlock, true};
+  const int64_t s0 = ((int64_t)ph * tiles + t) * span;
+  return {s0, (int64_t)kBlock, s0 + span <= nvec};
+}
+
+}  // namespace
+
 // E: element bytes (the copy moves 16-byte vectors; E matters for the chunk
 // bounds and the ragged edges only)
 // SKIP_OWN: the all-pairs fan-out (step 2): block j is owner j's finished

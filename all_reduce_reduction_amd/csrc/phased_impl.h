@@ -17,7 +17,8 @@
 //
 //   read half:  every workgroup loads its K blocks of all p inputs (16-byte
 //               loads, the next blocks' loads in flight while one folds;
-//               the chunk's workgroups take its blocks in turn, phase_span)
+//               the chunk's workgroups take its blocks in turn,
+//               phase_blocks)
 //               and keeps the folded result in VGPRs: K vectors per lane,
 //               K * 16 * kBlock bytes per workgroup;
 //   grid barrier;
@@ -116,33 +117,43 @@ __device__ __forceinline__ void phased_barrier(const PhasedArgs& a, unsigned lon
   __syncthreads();
 }
 
-// Where a workgroup's K vectors per lane lie in phase ph of its chunk (nvec
-// whole vectors, tiles workgroups, span = kBlock * K vectors each; a block
-// is kBlock vectors, one per lane).  While the whole phase lies inside the
-// chunk, the chunk's workgroups interleave block by block: block k of
-// workgroup t is block k * tiles + t of the phase, so at each step of the
-// write half the chunk's stores cover one contiguous range of the output
-// rather than tiles ranges a span apart (measured on MI355X, p = 8: one-shot
-// 168-171 against 176-177 us at 64 MiB per rank, 715-721 against 737-740 us
-// for fp32 at 256 MiB; direct reduce-scatter and all-gather 4-6% faster at
-// 64 MiB).  The phase that reaches the chunk's end gives each workgroup one
-// contiguous span instead, used only if whole, and the vectors past the
-// last whole span are done one by one after the phases; either way the
-// phases' whole spans cover exactly the chunk's first floor(nvec / span) *
-// span vectors.  (Dealing that last phase's blocks out evenly, with the
-// unused slots re-reading a loaded block to keep the code straight-line,
-// measured slower: 105 against 90 us at 32 MiB per rank.)
-struct PhaseSpan {
-  int64_t v0;       // the lane-0 vector of the workgroup's first block
-  int64_t vstride;  // vectors from one of its blocks to the next
-  bool whole;       // all K blocks inside the chunk (uniform over the workgroup)
+// Which of its chunk's blocks (kBlock whole vectors, one per lane) a
+// workgroup holds in phase ph.  A chunk has nblk whole blocks and a phase
+// takes up to tiles * K of them; the chunk's tiles workgroups interleave
+// block by block: the workgroup's block k is block k * tiles + t of the
+// phase, so at each step of the write half the chunk's stores cover one
+// contiguous range of the output rather than tiles ranges far apart
+// (measured on MI355X, p = 8: one-shot 168-171 against 176-177 us at 64 MiB
+// per rank, 715-721 against 737-740 us for fp32 at 256 MiB; direct
+// reduce-scatter and all-gather 4-6% faster at 64 MiB).  The phase that
+// reaches the chunk's end deals its blocks out evenly -- every workgroup
+// left / tiles of them, the first left % tiles one more -- so no workgroup
+// idles while others hold a full K.  The blocks of every workgroup of every
+// phase cover the chunk's first min(nblk, nphase * tiles * K) blocks once.
+struct PhaseBlocks {
+  int64_t v0;  // the lane-0 vector of the workgroup's first block
+  int kv;      // blocks held, 0 ... K (uniform over the workgroup)
 };
-__device__ __forceinline__ PhaseSpan phase_span(int ph, int t, int tiles, int64_t nvec, int64_t span) {
-  const int64_t ptile = (int64_t)tiles * span;  // a chunk's vectors per phase
-  if ((int64_t)(ph + 1) * ptile <= nvec)
-    return {(int64_t)ph * ptile + (int64_t)t * kBlock, (int64_t)tiles * kBlock, true};
-  const int64_t s0 = ((int64_t)ph * tiles + t) * span;
-  return {s0, (int64_t)kBlock, s0 + span <= nvec};
+template <int K>
+__device__ __forceinline__ PhaseBlocks phase_blocks(int ph, int t, int tiles, int64_t nblk) {
+  const int64_t pblk = (int64_t)tiles * K;  // a chunk's blocks per phase
+  const int64_t left = nblk - (int64_t)ph * pblk;
+  const int kv = left >= pblk ? K : left <= 0 ? 0 : (int)(left / tiles) + (t < left % tiles ? 1 : 0);
+  return {((int64_t)ph * pblk + t) * kBlock, kv};
+}
+
+// A workgroup holding kv < K blocks takes them as runs of B = K/2, K/4, ...,
+// 1 blocks, one per bit set in kv: the run of B covers blocks k0 ... k0 + B
+// - 1 (k0 = the sum of kv's higher bits) and keeps its results in the fixed
+// slots K - 2B ... K - B - 1 of the workgroup's K result registers, so every
+// register index is a constant and no slot is loaded for nothing.  f is
+// called with std::integral_constant<int, B> for B = TOP, TOP/2, ..., 1.
+template <int B, class F>
+__device__ __forceinline__ void for_each_run(F&& f) {
+  if constexpr (B >= 1) {
+    f(std::integral_constant<int, B>{});
+    for_each_run<B / 2>(f);
+  }
 }
 
 }  // namespace
@@ -180,7 +191,6 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
   const int64_t tail_beg = vbeg + nvec * V;
   const int64_t nscalar = head + (hi - tail_beg);
   const int tid = threadIdx.x;
-  const int64_t span = (int64_t)kBlock * K;
   const uint32_t lane = lane_offset((uint32_t)tid * 16u);
 
   auto fold = [&](const u32x4* L) {
@@ -199,66 +209,94 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
     return pack<DT>(acc);
   };
 
-  const unsigned long long nbar = a.nphase > 0 ? 2ull * a.nphase - 1 : 0ull;  // barriers of this call
-  unsigned long long nb = 0;
-  for (int ph = 0; ph < a.nphase; ph++) {
-    const PhaseSpan sp = phase_span(ph, t, a.tiles, nvec, span);
-    const int64_t sbyte = vbeg * E + sp.v0 * 16;  // this workgroup's first vector of the phase
-    const int64_t kst = sp.vstride * 16;           // bytes from one of its blocks to the next
-    const bool whole = sp.whole;                   // uniform over the workgroup
-    u32x4 R[K];
-    // ---- read half: the K blocks' results stay in VGPRs ----
-    if (whole) {
-      // D sets of p loads in flight while one set folds.  The scheduling
-      // barriers keep each set's p loads issued together, ahead of the fold
-      // that follows: without them the compiler interleaved the 32-bit folds
-      // with their own loads, waiting on every load (1-3 in flight per wave
-      // instead of ~16; the fp32 phased reduce-scatter ran 1.5x slower than
-      // the bf16 one).
-      u32x4 L[D][P];
+  // read B blocks, k0 ... k0 + B - 1, into R[S0 ... S0 + B - 1]: D sets of
+  // p loads in flight while one set folds.  The scheduling barriers keep
+  // each set's p loads issued together, ahead of the fold that follows:
+  // without them the compiler interleaved the 32-bit folds with their own
+  // loads, waiting on every load (1-3 in flight per wave instead of ~16; the
+  // fp32 phased reduce-scatter ran 1.5x slower than the bf16 one).
+  auto read_run = [&](auto b_tag, auto s_tag, u32x4* R, int64_t sbyte, int64_t kst, int k0)
+                      __attribute__((always_inline)) {
+    constexpr int B = decltype(b_tag)::value, S0 = decltype(s_tag)::value;
+    constexpr int DR = D < B ? D : B;
+    u32x4 L[DR][P];
 #pragma unroll
-      for (int d = 0; d < D; d++)
+    for (int d = 0; d < DR; d++)
 #pragma unroll
-        for (int q = 0; q < P; q++) L[d][q] = ld16u(xp[q], sbyte + (int64_t)d * kst, lane);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int q = 0; q < P; q++) L[d][q] = ld16u(xp[q], sbyte + (int64_t)(k0 + d) * kst, lane);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < K; k++) {
-        R[k] = fold(L[k % D]);
-        if (k + D < K) {
-          __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < B; i++) {
+      R[S0 + i] = fold(L[i % DR]);
+      if (i + DR < B) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int q = 0; q < P; q++) L[k % D][q] = ld16u(xp[q], sbyte + (int64_t)(k + D) * kst, lane);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int q = 0; q < P; q++) L[i % DR][q] = ld16u(xp[q], sbyte + (int64_t)(k0 + i + DR) * kst, lane);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  // store R[S0 ... S0 + B - 1] to blocks k0 ... k0 + B - 1 of one output
+  auto write_run = [&](auto b_tag, auto s_tag, const u32x4* R, void* y, int64_t obyte, int64_t kst, int k0)
+                       __attribute__((always_inline)) {
+    constexpr int B = decltype(b_tag)::value, S0 = decltype(s_tag)::value;
+#pragma unroll
+    for (int i = 0; i < B; i++) st16u(y, obyte + (int64_t)(k0 + i) * kst, lane, R[S0 + i]);
+  };
+  // every block the workgroup holds in the phase, as one run of K or as the
+  // runs of kv's bits (for_each_run)
+  auto runs = [&](int kv, auto&& run) __attribute__((always_inline)) {
+    if (kv == K) {
+      run(std::integral_constant<int, K>{}, std::integral_constant<int, 0>{}, 0);
+    } else if (kv > 0) {
+      for_each_run<K / 2>([&](auto b_tag) __attribute__((always_inline)) {
+        constexpr int B = decltype(b_tag)::value;
+        if (kv & B) run(b_tag, std::integral_constant<int, K - 2 * B>{}, kv & ~(2 * B - 1));
+      });
+    }
+  };
+
+  const unsigned long long nbar = a.nphase > 0 ? 2ull * a.nphase - 1 : 0ull;  // barriers of this call
+  unsigned long long nb = 0;
+  const int64_t nblk = nvec / kBlock;                   // the chunk's whole blocks
+  const int64_t kst = (int64_t)a.tiles * kBlock * 16;   // bytes from one of a workgroup's blocks to the next
+  for (int ph = 0; ph < a.nphase; ph++) {
+    const PhaseBlocks pb = phase_blocks<K>(ph, t, a.tiles, nblk);
+    const int64_t sbyte = vbeg * E + pb.v0 * 16;  // this workgroup's first block of the phase
+    u32x4 R[K];  // the phase's results, in VGPRs from the read half to the write half
+    runs(pb.kv, [&](auto b_tag, auto s_tag, int k0) __attribute__((always_inline)) {
+      read_run(b_tag, s_tag, R, sbyte, kst, k0);
+    });
     phased_barrier(a, nbar, ++nb, &s_rel);
-    // ---- write half: output by output; the workgroups of chunk j start at
-    // output j, so at any moment each output takes one chunk's stores ----
-    if (whole) {
-      if constexpr (ALL_OUT) {
+    // write half: output by output; the workgroups of chunk j start at
+    // output j, so at any moment each output takes one chunk's stores
+    if constexpr (ALL_OUT) {
 #pragma unroll
-        for (int rr = 0; rr < P; rr++) {
-          const int r = (rr + j) & (P - 1);  // P is a power of two
-          void* yr = yp[0];
+      for (int rr = 0; rr < P; rr++) {
+        const int r = (rr + j) & (P - 1);  // P is a power of two
+        void* yr = yp[0];
 #pragma unroll
-          for (int q = 1; q < P; q++)
-            if (q == r) yr = yp[q];
-#pragma unroll
-          for (int k = 0; k < K; k++) st16u(yr, sbyte + (int64_t)k * kst, lane, R[k]);
-        }
-      } else {
-        const int64_t obyte = sbyte - oshift * E;  // 16-byte aligned: the host checks oshift % V == 0
-#pragma unroll
-        for (int k = 0; k < K; k++) st16u(yp[0], obyte + (int64_t)k * kst, lane, R[k]);
+        for (int q = 1; q < P; q++)
+          if (q == r) yr = yp[q];
+        runs(pb.kv, [&](auto b_tag, auto s_tag, int k0) __attribute__((always_inline)) {
+          write_run(b_tag, s_tag, R, yr, sbyte, kst, k0);
+        });
       }
+    } else {
+      const int64_t obyte = sbyte - oshift * E;  // 16-byte aligned: the host checks oshift % V == 0
+      runs(pb.kv, [&](auto b_tag, auto s_tag, int k0) __attribute__((always_inline)) {
+        write_run(b_tag, s_tag, R, yp[0], obyte, kst, k0);
+      });
     }
     if (ph + 1 < a.nphase) phased_barrier(a, nbar, ++nb, &s_rel);
   }
 
-  // the chunk's vectors past its last whole span, read, folded and written
-  // vector by vector by all of the chunk's workgroups
-  for (int64_t v = nvec / span * span + (int64_t)t * kBlock + tid; v < nvec; v += (int64_t)a.tiles * kBlock) {
+  // the chunk's vectors past the blocks the phases hold (less than a block
+  // when the grid runs enough phases), read, folded and written vector by
+  // vector by all of the chunk's workgroups
+  const int64_t held = (int64_t)a.nphase * a.tiles * K;
+  for (int64_t v = (nblk < held ? nblk : held) * kBlock + (int64_t)t * kBlock + tid; v < nvec;
+       v += (int64_t)a.tiles * kBlock) {
     const int64_t vb = (vbeg + v * V) * E;
     u32x4 L[P];
 #pragma unroll

@@ -132,13 +132,16 @@ def test_phased_barrier_gives_up_without_changing_results(orc, lib):
 
 
 def test_phased_selection_rules(orc, lib):
-    """By default the one-shot runs phased from 32 MiB per rank on, never
-    for rank counts other than 2, 4, 8 and 16, under a workgroup budget or
-    when switched off; the threshold is settable."""
+    """By default the one-shot runs phased from 16 MiB per rank on, the
+    owner-only fold (direct reduce-scatter, all-pairs step 1) from 32 MiB and
+    the copy (direct all-gather, all-pairs step 2) from 64 MiB; never for
+    rank counts other than 2, 4, 8 and 16, under a workgroup budget or when
+    switched off; the threshold is settable (the others follow it)."""
     import torch
     from tests.gpu_util import ptrs, stream
     sim = lib
-    assert sim.sim_debug_get("phased_min") == 32 << 20
+    MIN = 16 << 20
+    assert sim.sim_debug_get("phased_min") == MIN
 
     def ran(p, nbytes, **cfg):
         n = nbytes // 2
@@ -152,25 +155,25 @@ def test_phased_selection_rules(orc, lib):
         finally:
             sim.sim_config_set("max_workgroups", 0)
             sim.sim_debug_set("phased", 0)
-            sim.sim_debug_set("phased_min", 32 << 20)
+            sim.sim_debug_set("phased_min", MIN)
 
-    assert ran(8, 32 << 20) == 1
-    assert ran(8, (32 << 20) - 16) == 0
-    assert ran(4, 32 << 20) == 1
-    assert ran(6, 32 << 20) == 0
-    assert ran(8, 32 << 20, max_workgroups=64) == 0
-    assert ran(8, 32 << 20, phased=2) == 0
+    assert ran(8, MIN) == 1
+    assert ran(8, MIN - 16) == 0
+    assert ran(4, MIN) == 1
+    assert ran(6, 2 * MIN) == 0
+    assert ran(8, 2 * MIN, max_workgroups=64) == 0
+    assert ran(8, 2 * MIN, phased=2) == 0
     assert ran(8, 1 << 20, phased_min=1 << 20) == 1
     torch.cuda.synchronize()
-    # the owner-only forms from twice the threshold
+
     def ran_rs(nbytes):
         n = nbytes // 2
         xs = [torch.zeros(n, dtype=torch.int16, device="cuda:0") for _ in range(8)]
         ys = [torch.empty(n // 8, dtype=torch.int16, device="cuda:0") for _ in range(8)]
         assert sim.sim_reduce_scatter(ptrs(xs), ptrs(ys), 8, n // 8, "bf16", "sum", "allpairs", stream()) == 0
         return sim.sim_debug_get("phased_last")
-    assert ran_rs(32 << 20) == 0
-    assert ran_rs(64 << 20) == 1
+    assert ran_rs(2 * MIN - 16 * 8) == 0
+    assert ran_rs(2 * MIN) == 1
 
     def ran_ag(out_bytes):
         n_in = out_bytes // 2 // 8
@@ -178,8 +181,8 @@ def test_phased_selection_rules(orc, lib):
         ys = [torch.empty(8 * n_in, dtype=torch.int16, device="cuda:0") for _ in range(8)]
         assert sim.sim_all_gather(ptrs(xs), ptrs(ys), 8, n_in, "bf16", "allpairs", stream()) == 0
         return sim.sim_debug_get("phased_last")
-    assert ran_ag(32 << 20) == 0
-    assert ran_ag(64 << 20) == 1
+    assert ran_ag(4 * MIN - 16 * 8) == 0
+    assert ran_ag(4 * MIN) == 1
     torch.cuda.synchronize()
     assert sim.sim_debug_get("phased_expired") == 0
 
