@@ -139,8 +139,9 @@ struct Ctx {
   int phased_mode = 0;       // 0: from phased_min bytes per rank on, 1: always, 2: never
   size_t phased_min = kPhasedMinBytes;
   bool last_phased = false;  // the current (or last) call ran a phased fold
-  // the most recent phased launch: its stream and sequence number, and the
-  // pinned host word its last workgroup writes that number to on leaving
+  // the most recent phased launch with a barrier: its stream and sequence
+  // number, and the pinned host word the workgroup that opens its last
+  // barrier writes that number to
   unsigned long long* ph_host_done = nullptr;
   unsigned long long* ph_dev_done = nullptr;
   unsigned long long ph_launched = 0;
@@ -442,8 +443,9 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
   // Two phased kernels in flight at once could each hold part of the CUs
   // while waiting at a barrier for workgroups the other keeps from being
   // resident (until their waits give up).  Calls on one stream are ordered;
-  // a call on another stream takes the fused kernel while the last phased
-  // launch may still run.
+  // a call on another stream takes the fused kernel until the last phased
+  // launch has opened its last barrier (after which none of its workgroups
+  // waits for anything, so its CUs drain on their own).
   if (g.ph_any && c.s != g.ph_stream &&
       __atomic_load_n(g.ph_host_done, __ATOMIC_ACQUIRE) != g.ph_launched)
     return -1;
@@ -478,7 +480,7 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
   }
   const int64_t per_phase = copy ? tiles : tiles * K;
   const int64_t nphase = (nmax + per_phase - 1) / per_phase;
-  const int64_t nbar = nphase > 0 ? 2 * nphase - 1 : 0;  // plus one arrival per workgroup on leaving
+  const int64_t nbar = nphase > 0 ? 2 * nphase - 1 : 0;
   PhasedArgs a;
   std::memset(&a, 0, sizeof a);
   for (int q = 0; q < p; q++) {
@@ -506,13 +508,16 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
                               : launch_fold_phased(c.dtype, c.op, p, all_out, a, c.s));
   if (rc) return rc;
 
-  // the counts this call adds: every workgroup meets every barrier and
-  // arrives once more on leaving
-  g.ph_ctr[slot] += (unsigned long long)(nbar + 1) * (unsigned long long)G;
+  // the counts this call adds: every workgroup meets every barrier.  A
+  // launch without barriers (no whole block to phase) never waits, so it
+  // does not hold up calls on other streams.
+  g.ph_ctr[slot] += (unsigned long long)nbar * (unsigned long long)G;
   g.ph_seq[slot] += (unsigned long long)nbar;
-  g.ph_launched = a.done_seq;
-  g.ph_stream = c.s;
-  g.ph_any = true;
+  if (nbar > 0) {
+    g.ph_launched = a.done_seq;
+    g.ph_stream = c.s;
+    g.ph_any = true;
+  }
   g.last_phased = true;
   return SIM_OK;
 }

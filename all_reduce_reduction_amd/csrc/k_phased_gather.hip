@@ -122,7 +122,6 @@ __global__ void __launch_bounds__(kBlock) k_gather_phased(PhasedArgs a) {
     for (int r = 0; r < P; r++)
       if (!SKIP_OWN || r != j) ((U*)yp[r])[i] = w;
   }
-  phased_arrive(a, nbar, &s_rel);
 }
 
 namespace {

@@ -233,9 +233,9 @@ struct SchedArgs {
 
 // k independent streaming copies (the ceiling of the one-shot's access
 // pattern): dst[q][0 .. 16 nvec) = src[q][0 .. 16 nvec) for q < k.
-// The phased one-shot (k_phased.hip): the grid folds a phase's spans into
-// VGPRs, meets at a grid barrier, writes them out, and meets again before
-// the next phase.  Barrier state lives in one of kPhasedSlots slots (the
+// The phased kernels (k_phased.hip, k_phased_owner.hip, k_phased_gather.hip):
+// the grid loads (and folds) a phase's blocks into VGPRs, meets at a grid
+// barrier, writes them out, and meets again before the next phase.  Barrier state lives in one of kPhasedSlots slots (the
 // host takes them in turn, call by call): an arrival counter and one release
 // flag per workgroup, kPhasedFlagStride 64-bit words (256 bytes) apart.
 constexpr int kPhasedSlots = 4;
@@ -251,7 +251,7 @@ struct PhasedArgs {
   unsigned long long seq;         // the flags' value when this call starts
   unsigned long long spin_limit;  // polls before a barrier wait gives up
   unsigned int* expired;          // barrier waits that gave up (timing only, not an error)
-  unsigned long long* done;       // host-visible word: the last workgroup to leave writes done_seq
+  unsigned long long* done;       // host-visible word: the opener of the last barrier writes done_seq
   unsigned long long done_seq;
   int tiles;                      // workgroups per chunk (grid = tiles * p)
   int nphase;

@@ -60,11 +60,10 @@ template <int P> struct PhasedShape {
   static constexpr int D = P >= 16 ? 1 : 16 / P;  // about 16 loads in flight per lane
 };
 
-// One arrival at the slot's counter: at each barrier and once more when a
-// workgroup leaves, so a call adds (nbar + 1) * G, G = grid size and nbar =
-// its barrier count.  Barrier k opens once R = G - G / 10 of its G
-// arrivals are in: the arrival that makes the call's count (k - 1) G + R
-// raises every workgroup's flag to seq + k (k capped at nbar) with an
+// One arrival at the slot's counter at each barrier, so a call adds nbar *
+// G, G = grid size and nbar = its barrier count.  Barrier k opens once R =
+// G - G / 10 of its G arrivals are in: the arrival that makes the call's
+// count (k - 1) G + R raises every workgroup's flag to seq + k with an
 // atomic max, so flags only grow even if a later release overtakes this
 // one, and the last tenth pass straight through when they arrive.  Waiting
 // for the very last workgroup measured ~1.5% slower at 64 MiB per rank
@@ -73,9 +72,12 @@ template <int P> struct PhasedShape {
 // R-th arrival; after a give-up, workgroups running ahead may complete a
 // count early and open a barrier early -- harmless, as the barrier guards
 // no data -- and none is left closed, as the count passes every (k - 1) G
-// + R on its way to (nbar + 1) G.  The arrival that completes the whole
-// call's count is the grid's last action: it writes done_seq to the
-// host-visible word.
+// + R on its way to nbar G.  The arrival that opens the last barrier also
+// writes done_seq to the host-visible word: from then on no workgroup of
+// the grid waits for anything, so another phased grid may start beside it.
+// (Workgroups do not arrive once more on leaving: the arrivals at one
+// counter serialize, ~10-20 ns each, and a second round at the grid's end
+// added to every call.)
 __device__ __forceinline__ void phased_arrive(const PhasedArgs& a, unsigned long long nbar,
                                               unsigned long long* s_rel) {
   __syncthreads();
@@ -84,9 +86,10 @@ __device__ __forceinline__ void phased_arrive(const PhasedArgs& a, unsigned long
     const unsigned long long old = __hip_atomic_fetch_add(a.ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned long long done = old + 1 - a.base;  // arrivals of this call so far, this one included
     const unsigned long long R = G - G / 10;
-    const unsigned long long k = done >= R ? (done - R) / G + 1 : 0;  // the barrier this arrival may open
-    *s_rel = (done >= R && (done - R) % G == 0) ? a.seq + (k < nbar ? k : nbar) : 0ull;
-    if (done == (nbar + 1) * G) __hip_atomic_store(a.done, a.done_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const bool opens = done >= R && (done - R) % G == 0;
+    const unsigned long long k = opens ? (done - R) / G + 1 : 0;  // the barrier this arrival opens
+    *s_rel = opens ? a.seq + (k < nbar ? k : nbar) : 0ull;
+    if (opens && k == nbar) __hip_atomic_store(a.done, a.done_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   }
   __syncthreads();
   const unsigned long long rel = *s_rel;
@@ -325,10 +328,6 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
     }
   }
 
-  // leaving: one more arrival (the call's last one tells the host, which
-  // keeps a second phased grid from starting on another stream before this
-  // one has left)
-  phased_arrive(a, nbar, &s_rel);
 }
 
 namespace {
