@@ -37,15 +37,15 @@ Model default_model() {
   Model m;
   // {alpha_us, gbps, steps, bytes_factor, wg_gbps, host_us}
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0, 0.0, 0.0};
-  m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.5, 2.8};
-  m.a[SIM_ALGO_ALLPAIRS] = {2.0, 5850.0, -1.0, -1.0, 43.5, 3.0};
-  m.a[SIM_ALGO_ONESHOT] = {1.5, 5950.0, -1.0, -1.0, 47.8, 3.2};
+  m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.5, 2.7};
+  m.a[SIM_ALGO_ALLPAIRS] = {2.1, 6100.0, -1.0, -1.0, 43.5, 3.0};
+  m.a[SIM_ALGO_ONESHOT] = {1.7, 6200.0, -1.0, -1.0, 47.4, 3.1};
   m.a[SIM_ALGO_ONESHOT_LL] = {8.95, 12700.0, -1.0, -1.0, 8.8, 0.0};
-  m.a[SIM_ALGO_RING_FIFO] = {14.2, 6350.0, -1.0, -1.0, 16.0, 0.0};
-  m.a[SIM_ALGO_TREE] = {3.1, 6200.0, -1.0, -1.0, 0.0, 4.1};
-  m.a[SIM_ALGO_REXCH] = {2.1, 6050.0, -1.0, -1.0, 0.0, 4.05};
-  m.a[SIM_ALGO_HIER] = {3.35, 6250.0, -1.0, -1.0, 0.0, 4.25};
-  m.a[SIM_ALGO_HIER_LARGE] = {3.15, 6050.0, -1.0, -1.0, 0.0, 4.45};
+  m.a[SIM_ALGO_RING_FIFO] = {14.3, 6350.0, -1.0, -1.0, 16.0, 0.0};
+  m.a[SIM_ALGO_TREE] = {3.0, 6200.0, -1.0, -1.0, 0.0, 4.5};
+  m.a[SIM_ALGO_REXCH] = {2.05, 6050.0, -1.0, -1.0, 0.0, 4.2};
+  m.a[SIM_ALGO_HIER] = {3.25, 6250.0, -1.0, -1.0, 0.0, 4.5};
+  m.a[SIM_ALGO_HIER_LARGE] = {3.15, 6050.0, -1.0, -1.0, 0.0, 4.75};
   m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {7.15, 8000.0, -1.0, -1.0, 32.0, 0.0};
   return m;
 }
