@@ -419,18 +419,36 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
   if (!g.ph_mem || !g.ph_dev_done || c.noalloc || g.capturing || g_max_wg > 0 || g.phased_mode == 2) return -1;
   if (p != 2 && p != 4 && p != 8 && p != 16) return -1;
   const int E = esize_of(c.dtype);
-  // The owner-only fold writes S bytes, not p S, and the copy reads only
-  // S / p: their phase separation gains less than the one-shot's against
-  // the barriers' cost, and the copy's last phase, not dealt out evenly
-  // (k_phased_gather.hip), leaves workgroups idle.  Measured on MI355X,
-  // p = 8 (bf16; fp32), phased against fused: direct reduce-scatter, input
-  // bytes per rank, 24 MiB 38.6 against 37.0 us; 39.6 against 37.9, 32 MiB
-  // 48.9 against 51.1; 47.5 against 49.0, 64 MiB 93.6 against 104.0;
-  // direct all-gather, output bytes per rank, 48 MiB 84.9 against 85.3;
-  // 85.0 against 86.3, 56 MiB 98.7 against 109.8; 99.9 against 107.1,
-  // 64 MiB 103.1 against 117.6.  So: owner-only from twice the one-shot's
-  // threshold, the copy from four times.
-  const size_t min_bytes = form == kPhasedAll ? g.phased_min : form == kPhasedOwner ? 2 * g.phased_min : 4 * g.phased_min;
+  // Where the phased form pays, in units of the settable threshold
+  // (g.phased_min, 16 MiB by default), by form (one-shot, owner-only fold,
+  // copy) and rank count; 0 = never by default.  The owner-only fold writes
+  // S bytes, not p S, and the copy reads only S / p, so their phase
+  // separation gains less against the barriers' cost, and the copy's last
+  // phase, not dealt out evenly (k_phased_gather.hip), leaves workgroups
+  // idle.  At p = 2 the fused forms already run at ~0.75 of peak.  Measured
+  // on MI355X, bf16, phased / fused (us):
+  //   p = 2: one-shot 48 MiB 34.7 / 34.5, 96 MiB 68.8 / 65.4; reduce-scatter
+  //          (input per rank) 32 MiB 20.2 / 18.0, 96 MiB 52.4 / 49.2;
+  //          all-gather (output per rank) 48 MiB 29.9 / 29.7, 64 MiB 34.3 / 38.1
+  //   p = 4: one-shot 24 MiB 36.1 / 35.9, 32 MiB 47.7 / 50.4; reduce-scatter
+  //          24 MiB 23.1 / 20.3, 32 MiB 28.9 / 31.7; all-gather 64 MiB
+  //          66.3 / 62.2, 96 MiB 92.1 / 88.7
+  //   p = 8: one-shot 12 MiB 36.7 / 35.1, 16 MiB 44.7 / 46.7; reduce-scatter
+  //          24 MiB 34.5 / 36.9, 32 MiB 44.0 / 48.8; all-gather 48 MiB
+  //          84.6 / 84.6, 64 MiB 103.6 / 119.4 (fp32 within 3% of these)
+  //   p = 16: one-shot 8 MiB 49.1 / 49.2, 16 MiB 92.0 / 96.6; reduce-scatter
+  //          16 MiB 43.9 / 46.8; all-gather 16 MiB 58.5 / 57.8, 24 MiB
+  //          85.4 / 90.1
+  static const double kFrom[3][4] = {
+      // p = 2, 4, 8, 16
+      {0.0, 2.0, 1.0, 1.0},  // one-shot
+      {0.0, 2.0, 2.0, 1.0},  // owner-only fold (direct reduce-scatter, all-pairs step 1)
+      {4.0, 0.0, 4.0, 1.5},  // copy (direct all-gather, all-pairs step 2)
+  };
+  const int pi = p == 2 ? 0 : p == 4 ? 1 : p == 8 ? 2 : 3;
+  const double from = kFrom[form == kPhasedAll ? 0 : form == kPhasedOwner ? 1 : 2][pi];
+  if (g.phased_mode == 0 && from == 0.0) return -1;
+  const size_t min_bytes = (size_t)(from * (double)g.phased_min);
   if (g.phased_mode == 0 && c.n * (size_t)E < min_bytes) return -1;
   // owner-only with shifted outputs, and the gather's inputs: whole 16-byte
   // vectors need 16-byte aligned offsets on both sides
@@ -449,7 +467,6 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
   if (g.ph_any && c.s != g.ph_stream &&
       __atomic_load_n(g.ph_host_done, __ATOMIC_ACQUIRE) != g.ph_launched)
     return -1;
-  const int pi = p == 2 ? 0 : p == 4 ? 1 : p == 8 ? 2 : 3;
   int& occ = g.ph_occ[c.dtype][copy ? 0 : c.op][pi][form];
   if (occ == 0) {
     occ = copy ? gather_phased_blocks_per_cu(E, p, form == kPhasedFanout)

@@ -11,8 +11,10 @@ pytestmark = pytest.mark.gpu
 
 P = 2
 N = (1 << 31) + (1 << 16) + 7
-ALGOS = [("oneshot", 1), ("allpairs", 1), ("ring", 1), ("ring_fifo", 1), ("allpairs_persistent", 1),
-         ("tree", 1), ("hier_large", 1)]
+# "oneshot_phased": the one-shot with its phased form forced (at p = 2 the
+# fused form is the default at every size)
+ALGOS = [("oneshot", 1), ("oneshot_phased", 1), ("allpairs", 1), ("ring", 1), ("ring_fifo", 1),
+         ("allpairs_persistent", 1), ("tree", 1), ("hier_large", 1)]
 
 
 @pytest.fixture(scope="module")
@@ -60,8 +62,16 @@ def test_past_4GiB_per_rank(orc, big, algo, G, op):
     for t in dout:
         t.fill_(0x7E5A)  # a NaN pattern in bf16: an unwritten element fails
     print(f"large-index {algo} {op} p={P} n={N}", flush=True)
-    st = sim.sim_allreduce(ptrs(din), ptrs(dout), P, N, "bf16", op, algo, stream())
+    phased = algo == "oneshot_phased"
+    algo = "oneshot" if phased else algo
+    sim.sim_debug_set("phased", 1 if phased else 0)
+    try:
+        st = sim.sim_allreduce(ptrs(din), ptrs(dout), P, N, "bf16", op, algo, stream())
+    finally:
+        sim.sim_debug_set("phased", 0)
     assert st == 0, st
+    if phased:
+        assert sim.sim_debug_get("phased_last") == 1
     assert sim.sim_check_error(stream()) == 0
     assert torch.equal(dout[0], dout[1]), "ranks differ"
     want = orc.allreduce_at(xs, "bf16", op, algo, idx)
@@ -90,7 +100,11 @@ def test_phased_reduce_scatter_and_all_gather_past_4GiB(orc, big):
     dev = din[0].device
     rs = [torch.full((n_out,), 0x7E5A, dtype=torch.int16, device=dev) for _ in range(P)]
     print(f"large-index phased reduce-scatter p={P} n_in={n_in}", flush=True)
-    assert sim.sim_reduce_scatter(ptrs(din), ptrs(rs), P, n_out, "bf16", "sum", "allpairs", stream()) == 0
+    sim.sim_debug_set("phased", 1)  # at p = 2 the reduce-scatter is not phased by default
+    try:
+        assert sim.sim_reduce_scatter(ptrs(din), ptrs(rs), P, n_out, "bf16", "sum", "allpairs", stream()) == 0
+    finally:
+        sim.sim_debug_set("phased", 0)
     assert sim.sim_debug_get("phased_last") == 1
     assert sim.sim_check_error(stream()) == 0
     sidx = np.unique(np.concatenate([

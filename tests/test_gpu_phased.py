@@ -132,11 +132,13 @@ def test_phased_barrier_gives_up_without_changing_results(orc, lib):
 
 
 def test_phased_selection_rules(orc, lib):
-    """By default the one-shot runs phased from 16 MiB per rank on, the
-    owner-only fold (direct reduce-scatter, all-pairs step 1) from 32 MiB and
-    the copy (direct all-gather, all-pairs step 2) from 64 MiB; never for
-    rank counts other than 2, 4, 8 and 16, under a workgroup budget or when
-    switched off; the threshold is settable (the others follow it)."""
+    """By default, at p = 8, the one-shot runs phased from 16 MiB per rank
+    on, the owner-only fold (direct reduce-scatter, all-pairs step 1) from
+    32 MiB and the copy (direct all-gather, all-pairs step 2) from 64 MiB;
+    other rank counts have their own thresholds (the one-shot from 32 MiB at
+    p = 4 and 16 MiB at p = 16, never at p = 2); never for rank counts other
+    than 2, 4, 8 and 16, under a workgroup budget or when switched off; the
+    threshold unit is settable (the others follow it)."""
     import torch
     from tests.gpu_util import ptrs, stream
     sim = lib
@@ -159,7 +161,11 @@ def test_phased_selection_rules(orc, lib):
 
     assert ran(8, MIN) == 1
     assert ran(8, MIN - 16) == 0
-    assert ran(4, MIN) == 1
+    assert ran(4, MIN) == 0
+    assert ran(4, 2 * MIN) == 1
+    assert ran(16, MIN) == 1
+    assert ran(2, 4 * MIN) == 0
+    assert ran(2, 4 * MIN, phased=1) == 1
     assert ran(6, 2 * MIN) == 0
     assert ran(8, 2 * MIN, max_workgroups=64) == 0
     assert ran(8, 2 * MIN, phased=2) == 0
