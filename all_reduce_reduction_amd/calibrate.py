@@ -10,7 +10,10 @@ message sizes that sits BETWEEN the evaluation sizes (powers of two times
 squares with relative weights (so microsecond and millisecond points count
 alike), and writes the JSON file sim_model_load() reads.
 
-The fit is a two-regime estimate (see fit()).  A launch-configuration sweep
+The fit is a two-regime estimate (see fit()).  The one-shot and the
+single-launch ring change kernels with the size (phased form, FIFO
+protocol); each of them gets a second entry ("algos_hi") fitted on the
+sizes of its second regime.  A launch-configuration sweep
 (sweep_workgroups) then stores the best (total workgroups, 16-byte vectors
 per lane) per size for the bulk schedules.  --check then times every legal schedule at the evaluation sizes (8192 x
 {1, 16, 256, 4096} tokens bf16, and 1 KiB .. 1 MiB fp16) and compares the
@@ -52,6 +55,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 DEFAULT_OUT = os.path.join(HERE, "calib", "mi355x.json")
 ALGOS = ("ring", "allpairs", "oneshot", "oneshot_ll", "ring_fifo", "allpairs_persistent")
+# Schedules whose kernels change with the size, fitted as two regimes
+# ("algos" below the switch, "algos_hi" from it): the one-shot's fused and
+# phased forms, the single-launch ring's LL and FIFO protocols.
+REGIMES = ("oneshot", "ring_fifo")
 # The topology schedules are fitted too (sim_model_predict prices them),
 # each at the topology stated here; AUTO does not weigh them.
 TOPOLOGY = {"tree": (1, 2), "rexch": (1, 2), "hier": (4, 2), "hier_large": (4, 2)}  # (ranks per node, radix)
@@ -140,6 +147,7 @@ class Bench:
         us, spread = self.time(fn, steps, max(2, steps // 10), reps)
         if sim.sim_check_error(self.stream) != 0:
             raise RuntimeError("device error during calibration")
+        self.last_phased = sim.sim_debug_get("phased_last")
         return us, spread
 
 
@@ -297,14 +305,19 @@ def calibrate(out_path: str):
         for nbytes in sizes[:6]:
             if b.legal(algo, nbytes):
                 b.measure(algo, "bf16", nbytes // 2)
+    ll_max = sim.sim_debug_get("ring_ll_max")
     for algo in ALGOS + tuple(TOPOLOGY):
         set_topology(sim, algo)
-        pts = []
+        pts, regime = [], []
         for nbytes in sizes:
             if not b.legal(algo, nbytes):
                 continue
             n = nbytes // 2
             us, spread = b.measure(algo, "bf16", n)
+            # the second regime (see REGIMES): the one-shot's phased calls,
+            # the single-launch ring's FIFO protocol
+            regime.append(b.last_phased == 1 if algo == "oneshot" else
+                          nbytes > ll_max if algo == "ring_fifo" else False)
             # the laws (launch count, traffic) of this algo, with unit alpha / B
             sim.sim_model_set(algo, 1.0, -1, -1, 1e300)
             launches = sim.sim_model_predict(algo, P, "bf16", nbytes)
@@ -315,20 +328,37 @@ def calibrate(out_path: str):
                                              "spread": round(spread, 4)})
             print(f"calibrate {algo:10s} {nbytes:>10d} B/rank {us:10.2f} us", flush=True)
         raw[algo + "_fit_points"] = len(pts)
-        host, alpha, gbps = fit_host(pts, algo)
-        raw.setdefault("fit", {})[algo] = {"alpha_us": alpha, "gbps": gbps, "host_us": host}
+        lo = [x for x, r in zip(pts, regime) if not r]
+        hi = [x for x, r in zip(pts, regime) if r]
+        if algo in REGIMES and len(lo) >= 3 and len(hi) >= 3:
+            for key, part in (("fit", lo), ("fit_hi", hi)):
+                host, alpha, gbps = fit_host(part, algo)
+                raw.setdefault(key, {})[algo] = {"alpha_us": alpha, "gbps": gbps, "host_us": host}
+        else:
+            host, alpha, gbps = fit_host(pts, algo)
+            raw.setdefault("fit", {})[algo] = {"alpha_us": alpha, "gbps": gbps, "host_us": host}
     set_topology(sim, "ring")
     sim.sim_model_reset()
-    rates, budget_raw = sweep_budget(sim, b, raw["fit"])
+    # the budget sweep's size runs the one-shot fused (no phased form under a
+    # budget) and the single-launch ring with FIFOs: each is fitted against
+    # the regime it runs in, and the rate goes into both entries
+    hi_fits = raw.get("fit_hi", {})
+    budget_fits = {a: (hi_fits[a] if a == "ring_fifo" and a in hi_fits else f) for a, f in raw["fit"].items()}
+    rates, budget_raw = sweep_budget(sim, b, budget_fits)
     for algo, r in rates.items():
         raw["fit"][algo]["wg_gbps"] = r
+        if algo in hi_fits:
+            hi_fits[algo]["wg_gbps"] = r
     wg_table, wg_raw = sweep_workgroups(sim, b, sizes)
     model = {"device": "MI355X (gfx950)", "p": P, "dtype": "bf16",
              "grid": "1.5 x 2^k bytes per rank, k = 10..27",
              "form": "T = max(host_us * launches, alpha_us * launches + traffic / B_eff); B_eff = gbps, or "
                      "(gbps^-3 + (W wg_gbps)^-3)^(-1/3) under a budget of W workgroups",
              "topology": {a: {"ranks_per_node": g, "radix": k} for a, (g, k) in TOPOLOGY.items()},
-             "algos": raw["fit"], "workgroups": wg_table,
+             "algos": raw["fit"], "algos_hi": raw.get("fit_hi", {}),
+             "regimes": {"oneshot": "algos_hi from the size where it runs phased (at this p)",
+                         "ring_fifo": f"algos_hi above {ll_max} bytes per rank (FIFO protocol)"},
+             "workgroups": wg_table,
              "measurements": {a: raw[a] for a in ALGOS + tuple(TOPOLOGY) if a in raw},
              "budget_measurements": budget_raw,
              "rotation": f"up to {Bench.MAX_SETS} buffer sets, >= {Bench.ROT_BYTES >> 20} MiB per rotation "
@@ -337,7 +367,7 @@ def calibrate(out_path: str):
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
         json.dump(model, f, indent=1)
-    print(json.dumps({"calibration": out_path, "algos": raw["fit"]}), flush=True)
+    print(json.dumps({"calibration": out_path, "algos": raw["fit"], "algos_hi": raw.get("fit_hi", {})}), flush=True)
     return out_path
 
 

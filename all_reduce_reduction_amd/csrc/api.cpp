@@ -412,13 +412,10 @@ int run_fold(const Call& c, bool all_out, const int64_t* lo, const int64_t* out_
 // kPhasedFanout: all-pairs step 2, owner j's finished chunk from output j to
 // the other outputs, with the gather's kernel.
 enum PhasedForm { kPhasedAll = 0, kPhasedOwner = 1, kPhasedGather = 2, kPhasedFanout = 3 };
-int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t* out_shift) {
-  const int p = c.p;
-  const bool all_out = form != kPhasedOwner;
-  const bool copy = form == kPhasedGather || form == kPhasedFanout;
-  if (!g.ph_mem || !g.ph_dev_done || c.noalloc || g.capturing || g_max_wg > 0 || g.phased_mode == 2) return -1;
-  if (p != 2 && p != 4 && p != 8 && p != 16) return -1;
-  const int E = esize_of(c.dtype);
+// Bytes per rank from which a call of a phased form runs phased (0: never),
+// given the rank count, the switch (SIM_DEBUG_PHASED) and the workgroup
+// budget (the persistent grid needs every CU).
+size_t phased_threshold(int form, int p) {
   // Where the phased form pays, in units of the settable threshold
   // (g.phased_min, 16 MiB by default), by form (one-shot, owner-only fold,
   // copy) and rank count; 0 = never by default.  The owner-only fold writes
@@ -445,11 +442,23 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
       {0.0, 2.0, 2.0, 1.0},  // owner-only fold (direct reduce-scatter, all-pairs step 1)
       {4.0, 0.0, 4.0, 1.5},  // copy (direct all-gather, all-pairs step 2)
   };
+  if (g.phased_mode == 2 || g_max_wg > 0 || (p != 2 && p != 4 && p != 8 && p != 16)) return 0;
+  if (g.phased_mode == 1) return 1;
   const int pi = p == 2 ? 0 : p == 4 ? 1 : p == 8 ? 2 : 3;
   const double from = kFrom[form == kPhasedAll ? 0 : form == kPhasedOwner ? 1 : 2][pi];
-  if (g.phased_mode == 0 && from == 0.0) return -1;
-  const size_t min_bytes = (size_t)(from * (double)g.phased_min);
-  if (g.phased_mode == 0 && c.n * (size_t)E < min_bytes) return -1;
+  return from == 0.0 ? 0 : std::max<size_t>(1, (size_t)(from * (double)g.phased_min));
+}
+
+int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t* out_shift) {
+  const int p = c.p;
+  const bool all_out = form != kPhasedOwner;
+  const bool copy = form == kPhasedGather || form == kPhasedFanout;
+  if (!g.ph_mem || !g.ph_dev_done || c.noalloc || g.capturing || g_max_wg > 0 || g.phased_mode == 2) return -1;
+  if (p != 2 && p != 4 && p != 8 && p != 16) return -1;
+  const int E = esize_of(c.dtype);
+  const size_t min_bytes = phased_threshold(form, p);
+  if (min_bytes == 0) return -1;
+  if (c.n * (size_t)E < min_bytes) return -1;
   // owner-only with shifted outputs, and the gather's inputs: whole 16-byte
   // vectors need 16-byte aligned offsets on both sides
   if (out_shift)
@@ -467,6 +476,7 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
   if (g.ph_any && c.s != g.ph_stream &&
       __atomic_load_n(g.ph_host_done, __ATOMIC_ACQUIRE) != g.ph_launched)
     return -1;
+  const int pi = p == 2 ? 0 : p == 4 ? 1 : p == 8 ? 2 : 3;
   int& occ = g.ph_occ[c.dtype][copy ? 0 : c.op][pi][form];
   if (occ == 0) {
     occ = copy ? gather_phased_blocks_per_cu(E, p, form == kPhasedFanout)
@@ -1183,6 +1193,20 @@ const int kAutoCandidates[] = {SIM_ALGO_RING,       SIM_ALGO_ALLPAIRS,  SIM_ALGO
 // the schedules the allocation-free entry point runs (no library buffers)
 const int kNoAllocCandidates[] = {SIM_ALGO_RING, SIM_ALGO_ALLPAIRS, SIM_ALGO_ONESHOT};
 
+// Bytes per rank from which the model prices an algo with its second regime
+// (Model::hi; 0: one regime): the single-launch ring's FIFO protocol above
+// the LL limit, and the one-shot from the size where it runs phased.
+double model_hi_from(int coll, int algo, int p) {
+  if (coll != COLL_ALLREDUCE) return 0.0;
+  if (algo == SIM_ALGO_RING_FIFO) return (double)g.ring_ll_max + 1.0;
+  if (algo == SIM_ALGO_ONESHOT) return (double)phased_threshold(kPhasedAll, p);
+  return 0.0;
+}
+
+double predict(int coll, int algo, int p, double n, int esize) {
+  return model_predict(g.model, coll, algo, p, n, esize, g_topo, g_max_wg, model_hi_from(coll, algo, p));
+}
+
 int pick(int coll, int p, size_t n, int dtype, int* algo, double* us, const int* cands = kAutoCandidates,
          int ncands = (int)(sizeof kAutoCandidates / sizeof kAutoCandidates[0])) {
   int best = -1;
@@ -1190,7 +1214,7 @@ int pick(int coll, int p, size_t n, int dtype, int* algo, double* us, const int*
   for (int k = 0; k < ncands; k++) {
     const int a = cands[k];
     if (!legal(coll, a, p, n, dtype)) continue;
-    const double t = model_predict(g.model, coll, a, p, (double)n, esize_of(dtype), g_topo, g_max_wg);
+    const double t = predict(coll, a, p, (double)n, esize_of(dtype));
     if (best < 0 || t < bt) {
       best = a;
       bt = t;
@@ -1207,7 +1231,7 @@ int resolve_algo(int coll, int p, size_t n, int dtype, int* algo, double* us) {
   if (*algo == SIM_ALGO_AUTO && coll == COLL_ALLREDUCE && g.env_algo > 0) *algo = g.env_algo;
   if (*algo == SIM_ALGO_AUTO) return pick(coll, p, n, dtype, algo, us);
   if (!legal(coll, *algo, p, n, dtype)) return SIM_ERR_UNSUPPORTED;
-  if (us) *us = model_predict(g.model, coll, *algo, p, (double)n, esize_of(dtype), g_topo, g_max_wg);
+  if (us) *us = predict(coll, *algo, p, (double)n, esize_of(dtype));
   return SIM_OK;
 }
 
@@ -1441,7 +1465,7 @@ int sim_allreduce_noalloc(const void* const* in_ptrs, void* const* out_ptrs, int
               (int)(sizeof kNoAllocCandidates / sizeof kNoAllocCandidates[0]));
     if (rc) return rc;
   } else {
-    us = model_predict(g.model, COLL_ALLREDUCE, algo, p, (double)n, (int)e, g_topo, g_max_wg);
+    us = predict(COLL_ALLREDUCE, algo, p, (double)n, (int)e);
   }
   // only the 16-bit ring (p > 2) keeps partials: they must fit the array
   if (algo == SIM_ALGO_RING && e == 2 && p > 2 && scratch_need(n, p) > SIM_NOALLOC_SCRATCH_BYTES)
@@ -1503,7 +1527,7 @@ int sim_reduce_scatter(const void* const* in_ptrs, void* const* out_ptrs, int p,
   rc = run_reduce_scatter(c);
   if (rc) return rc;
   g.last_algo = algo;
-  log_call("ReduceScatter", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e, g_topo, g_max_wg));
+  log_call("ReduceScatter", c, predict(c.coll, algo, p, (double)c.n, (int)e));
   return SIM_OK;
 }
 
@@ -1552,7 +1576,7 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p, siz
   rc = run_all_gather(c);
   if (rc) return rc;
   g.last_algo = algo;
-  log_call("AllGather", c, model_predict(g.model, c.coll, algo, p, (double)c.n, (int)e, g_topo, g_max_wg));
+  log_call("AllGather", c, predict(c.coll, algo, p, (double)c.n, (int)e));
   return SIM_OK;
 }
 
@@ -1589,7 +1613,7 @@ int sim_model_predict(int algo, int p, int dtype, double bytes_per_rank, double*
   if (is_topology_algo(algo) && !cached_schedule(COLL_ALLREDUCE, algo, p, g_topo, nullptr))
     return SIM_ERR_UNSUPPORTED;
   const int e = esize_of(dtype);
-  *us_out = model_predict(g.model, COLL_ALLREDUCE, algo, p, bytes_per_rank / e, e, g_topo, g_max_wg);
+  *us_out = predict(COLL_ALLREDUCE, algo, p, bytes_per_rank / e, e);
   return SIM_OK;
 }
 
@@ -1602,6 +1626,7 @@ int sim_model_set(int algo, double alpha_us, double steps, double bytes_factor, 
   m.steps = steps;
   m.bytes_factor = bytes_factor;
   m.host_us = 0.0;  // the additive form as given; sim_model_set_host_overlap adds the host term
+  g.model.has_hi[algo] = false;  // one line for every size
   g.model.source = "sim_model_set";
   return SIM_OK;
 }
@@ -1609,6 +1634,7 @@ int sim_model_set(int algo, double alpha_us, double steps, double bytes_factor, 
 int sim_model_set_host_overlap(int algo, double host_us_per_launch) {
   if (algo < SIM_ALGO_RING || algo > kLastAlgo || !(host_us_per_launch >= 0)) return SIM_ERR_INVALID_ARG;
   g.model.a[algo].host_us = host_us_per_launch;
+  g.model.hi[algo].host_us = host_us_per_launch;
   g.model.source = "sim_model_set_host_overlap";
   return SIM_OK;
 }
@@ -1616,6 +1642,7 @@ int sim_model_set_host_overlap(int algo, double host_us_per_launch) {
 int sim_model_set_workgroup_rate(int algo, double gbps_per_workgroup) {
   if (algo < SIM_ALGO_RING || algo > kLastAlgo || !(gbps_per_workgroup >= 0)) return SIM_ERR_INVALID_ARG;
   g.model.a[algo].wg_gbps = gbps_per_workgroup;
+  g.model.hi[algo].wg_gbps = gbps_per_workgroup;
   g.model.source = "sim_model_set_workgroup_rate";
   return SIM_OK;
 }

@@ -35,18 +35,24 @@ namespace simar {
 // SIM_CALIB replaces them.
 Model default_model() {
   Model m;
-  // {alpha_us, gbps, steps, bytes_factor, wg_gbps, host_us}
+  // {alpha_us, gbps, steps, bytes_factor, wg_gbps, host_us}, from the MI355X
+  // calibration (p = 8, bf16)
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0, 0.0, 0.0};
-  m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.5, 2.7};
+  m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.5, 2.8};
   m.a[SIM_ALGO_ALLPAIRS] = {2.1, 6100.0, -1.0, -1.0, 43.5, 3.0};
-  m.a[SIM_ALGO_ONESHOT] = {1.7, 6200.0, -1.0, -1.0, 47.4, 3.1};
-  m.a[SIM_ALGO_ONESHOT_LL] = {8.95, 12700.0, -1.0, -1.0, 8.8, 0.0};
-  m.a[SIM_ALGO_RING_FIFO] = {14.3, 6350.0, -1.0, -1.0, 16.0, 0.0};
-  m.a[SIM_ALGO_TREE] = {3.0, 6200.0, -1.0, -1.0, 0.0, 4.5};
-  m.a[SIM_ALGO_REXCH] = {2.05, 6050.0, -1.0, -1.0, 0.0, 4.2};
-  m.a[SIM_ALGO_HIER] = {3.25, 6250.0, -1.0, -1.0, 0.0, 4.5};
-  m.a[SIM_ALGO_HIER_LARGE] = {3.15, 6050.0, -1.0, -1.0, 0.0, 4.75};
-  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {7.15, 8000.0, -1.0, -1.0, 32.0, 0.0};
+  m.a[SIM_ALGO_ONESHOT] = {1.4, 5850.0, -1.0, -1.0, 48.1, 3.25};
+  m.a[SIM_ALGO_ONESHOT_LL] = {8.9, 13150.0, -1.0, -1.0, 8.9, 0.0};
+  m.a[SIM_ALGO_RING_FIFO] = {13.6, 665.0, -1.0, -1.0, 16.2, 0.0};
+  m.a[SIM_ALGO_TREE] = {3.2, 6200.0, -1.0, -1.0, 0.0, 4.4};
+  m.a[SIM_ALGO_REXCH] = {2.25, 6050.0, -1.0, -1.0, 0.0, 4.25};
+  m.a[SIM_ALGO_HIER] = {3.35, 6250.0, -1.0, -1.0, 0.0, 4.4};
+  m.a[SIM_ALGO_HIER_LARGE] = {3.25, 6050.0, -1.0, -1.0, 0.0, 4.6};
+  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {7.0, 8050.0, -1.0, -1.0, 32.0, 0.0};
+  // second regimes: the phased one-shot, the single-launch ring's FIFO protocol
+  m.hi[SIM_ALGO_ONESHOT] = {3.35, 6300.0, -1.0, -1.0, 48.1, 0.0};
+  m.has_hi[SIM_ALGO_ONESHOT] = true;
+  m.hi[SIM_ALGO_RING_FIFO] = {24.0, 6450.0, -1.0, -1.0, 16.2, 50.5};
+  m.has_hi[SIM_ALGO_RING_FIFO] = true;
   return m;
 }
 
@@ -183,8 +189,7 @@ int model_workgroups(const Model& m, int algo, int p, double bytes_per_rank) {
 // smooth minimum follows the knee (one-shot, p = 8, bf16, 64 MiB per rank
 // on MI355X: 32 workgroups 1.55 TB/s, 128 workgroups 4.5 TB/s, no budget
 // 5.6 TB/s).
-double model_bandwidth(const Model& m, int algo, int p, int budget) {
-  const AlgoModel& am = m.a[algo];
+double model_bandwidth(const AlgoModel& am, int algo, int p, int budget) {
   if (budget <= 0 || !(am.wg_gbps > 0)) return am.gbps;
   const bool persistent = algo == SIM_ALGO_RING_FIFO || algo == SIM_ALGO_ALLPAIRS_PERSISTENT;
   const double w = persistent ? std::max(budget, p) : budget;
@@ -193,15 +198,16 @@ double model_bandwidth(const Model& m, int algo, int p, int budget) {
 }
 
 double model_predict(const Model& m, int coll, int algo, int p, double n, int esize, const Topology& t,
-                     int budget) {
+                     int budget, double hi_from) {
   if (algo <= 0 || algo >= kNumAlgos) return 1e30;
-  const AlgoModel& am = m.a[algo];
+  const bool hi = hi_from > 0 && m.has_hi[algo] && n * esize >= hi_from;
+  const AlgoModel& am = hi ? m.hi[algo] : m.a[algo];
   const int launches = model_launches(coll, algo, p, t);
   if (launches < 0) return 1e30;  // no schedule for this topology
   const double steps = am.steps >= 0 ? am.steps : (double)launches;
   const double bytes = am.bytes_factor >= 0 ? am.bytes_factor * n * esize
                                             : model_traffic(coll, algo, p, n, esize, t);
-  const double gpu = am.alpha_us * steps + bytes / (model_bandwidth(m, algo, p, budget) * 1e3);  // GB/s -> B/us
+  const double gpu = am.alpha_us * steps + bytes / (model_bandwidth(am, algo, p, budget) * 1e3);  // GB/s -> B/us
   return std::max(am.host_us * launches, gpu);
 }
 
@@ -372,10 +378,8 @@ bool model_load_json(const char* path, Model* m, std::string* err) {
     return false;
   }
   Model out = *m;
-  for (int a = 1; a < kNumAlgos; a++) {
-    auto ai = it->second.obj.find(kAlgoNames[a]);
-    if (ai == it->second.obj.end()) continue;
-    const JVal& o = ai->second;
+  // one algo entry: alpha_us and gbps, optional host_us and wg_gbps
+  auto entry = [&](const JVal& o, AlgoModel* am) {
     if (o.kind != JVal::OBJ) {
       if (err) *err = "algo entry is not an object";
       return false;
@@ -387,19 +391,19 @@ bool model_load_json(const char* path, Model* m, std::string* err) {
       if (err) *err = "algo entry needs numeric alpha_us >= 0 and gbps > 0";
       return false;
     }
-    out.a[a].alpha_us = al->second.num;
-    out.a[a].gbps = bw->second.num;
-    out.a[a].steps = -1;
-    out.a[a].bytes_factor = -1;
-    out.a[a].wg_gbps = 0;
-    out.a[a].host_us = 0;
+    am->alpha_us = al->second.num;
+    am->gbps = bw->second.num;
+    am->steps = -1;
+    am->bytes_factor = -1;
+    am->wg_gbps = 0;
+    am->host_us = 0;
     auto hu = o.obj.find("host_us");  // optional: host enqueue cost per launch
     if (hu != o.obj.end()) {
       if (hu->second.kind != JVal::NUM || !(hu->second.num >= 0)) {
         if (err) *err = "host_us must be a number >= 0";
         return false;
       }
-      out.a[a].host_us = hu->second.num;
+      am->host_us = hu->second.num;
     }
     auto wr = o.obj.find("wg_gbps");  // optional: rate of one workgroup under a budget
     if (wr != o.obj.end()) {
@@ -407,7 +411,28 @@ bool model_load_json(const char* path, Model* m, std::string* err) {
         if (err) *err = "wg_gbps must be a number >= 0";
         return false;
       }
-      out.a[a].wg_gbps = wr->second.num;
+      am->wg_gbps = wr->second.num;
+    }
+    return true;
+  };
+  for (int a = 1; a < kNumAlgos; a++) {
+    auto ai = it->second.obj.find(kAlgoNames[a]);
+    if (ai == it->second.obj.end()) continue;
+    if (!entry(ai->second, &out.a[a])) return false;
+    out.has_hi[a] = false;  // a file's algo entry replaces both regimes; "algos_hi" adds the second
+  }
+  // optional: second regimes, "algos_hi": {algo: entry} (Model::hi)
+  auto hit = root.obj.find("algos_hi");
+  if (hit != root.obj.end()) {
+    if (hit->second.kind != JVal::OBJ) {
+      if (err) *err = "'algos_hi' is not an object";
+      return false;
+    }
+    for (int a = 1; a < kNumAlgos; a++) {
+      auto ai = hit->second.obj.find(kAlgoNames[a]);
+      if (ai == hit->second.obj.end()) continue;
+      if (!entry(ai->second, &out.hi[a])) return false;
+      out.has_hi[a] = true;
     }
   }
   // optional: the rank count the launch table was measured at

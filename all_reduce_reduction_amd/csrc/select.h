@@ -32,6 +32,12 @@ struct LaunchEntry {
 
 struct Model {
   AlgoModel a[kNumAlgos];
+  // A second regime of an algo whose kernels change with the size: the
+  // single-launch ring's FIFO protocol above its LL limit, the phased
+  // one-shot from its threshold.  Used from the size the caller names
+  // (model_predict's hi_from); absent unless has_hi.
+  AlgoModel hi[kNumAlgos];
+  bool has_hi[kNumAlgos] = {};
   // Measured launch configurations (after T-CCL's ranked CTA-config table):
   // per algo, entries from the calibration sweep, ascending in bytes; empty
   // = cover every transfer exactly with one vector per lane.
@@ -76,15 +82,17 @@ double schedule_traffic(const Schedule& s, double n, int esize);
 //   (B^-3 + (W b)^-3)^(-1/3)
 // of B and the budget's aggregate rate W b, W being the budget (at least one
 // workgroup per rank for the single-launch schedules, which keep that many).
-double model_bandwidth(const Model& m, int algo, int p, int budget);
+double model_bandwidth(const AlgoModel& am, int algo, int p, int budget);
 
 // T = alpha * launches + traffic / B_eff, in microseconds, B_eff being
 // model_bandwidth() at `budget`; with a host enqueue cost H per launch,
 // T = max(H * launches, that): calls issued back to back overlap the host's
 // enqueue of one call with the GPU's execution of the previous one, so a
-// call costs whichever side is slower.
+// call costs whichever side is slower.  From hi_from bytes per rank on
+// (when > 0) the algo's second regime prices the call, when the model has
+// one (Model::hi).
 double model_predict(const Model& m, int coll, int algo, int p, double n, int esize,
-                     const Topology& t = Topology(), int budget = 0);
+                     const Topology& t = Topology(), int budget = 0, double hi_from = 0.0);
 
 // Parse a calibration file; returns false (and leaves *m alone) on error.
 bool model_load_json(const char* path, Model* m, std::string* err);

@@ -266,7 +266,12 @@ int sim_all_gather(const void* const* in_ptrs, void* const* out_ptrs, int p,
  * or "host_us" in the calibration file) is priced max(H_a * launches_a, T_a):
  * calls issued back to back overlap the host's enqueue of one call with the
  * GPU's execution of the previous one, so a call costs whichever side is
- * slower; H_a = 0 leaves T_a as it is. */
+ * slower; H_a = 0 leaves T_a as it is.  Two algos change kernels with the
+ * size, and the model may hold a second (alpha, B, ...) entry for each,
+ * used from that size on: SIM_ALGO_RING_FIFO above SIM_DEBUG_RING_LL_MAX
+ * bytes per rank (the FIFO protocol instead of LL packets), and
+ * SIM_ALGO_ONESHOT from the size where it runs phased (see "Phased
+ * kernels"; never under a workgroup budget). */
 int sim_select(int p, size_t n, int dtype, int op, int* algo_out, double* predicted_us);
 
 /* The algo the most recent successful collective actually ran. */
@@ -283,8 +288,10 @@ int sim_last_algo(void);
  * calls with another rank count then ignore the table.  An algo
  * entry may carry "wg_gbps", its per-workgroup rate under a budget, and
  * "host_us", its host enqueue cost per launch (see sim_select; 0 when
- * absent).  Errors: SIM_ERR_INVALID_ARG (the current
- * model is kept). */
+ * absent).  An optional "algos_hi" object holds second entries of the same
+ * form for the algos whose kernels change with the size (see sim_select);
+ * an algo listed in "algos" but not in "algos_hi" gets one entry for every
+ * size.  Errors: SIM_ERR_INVALID_ARG (the current model is kept). */
 int sim_model_load(const char* json_path);
 
 /* Predicted time of `algo` for `bytes_per_rank` bytes per rank of `dtype`
@@ -306,7 +313,8 @@ int sim_model_set_workgroup_rate(int algo, double gbps_per_workgroup);
  * built-in laws when >= 0 -- e.g. the multi-GPU form 2(p-1) alpha +
  * 2(p-1)/p n / B.  Pass negative values to keep the built-in laws.  The
  * algo's host enqueue term is cleared (the additive form exactly as given);
- * its per-workgroup rate is kept. */
+ * its per-workgroup rate is kept; a second entry it had for large sizes is
+ * dropped (this one then prices every size). */
 int sim_model_set(int algo, double alpha_us, double steps, double bytes_factor, double gbps);
 
 /* Restore the built-in default model. */

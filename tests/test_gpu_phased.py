@@ -94,6 +94,29 @@ def test_phased_equals_fused_bits(orc, lib, p):
             assert (bits(phased[r]) == bits(fused[r])).all(), (p, wg, r)
 
 
+@pytest.mark.parametrize("p", [4, 8, 16])
+def test_phased_last_phase_runs(orc, lib, p):
+    """A last phase holding fewer than K blocks per workgroup is dealt out
+    evenly and taken as runs of K/2, K/4, ..., 1 blocks (one per bit of the
+    count, fixed result registers): counts that set every bit, uneven
+    dealing over 3 and 5 workgroups per chunk, a lone trailing block and a
+    ragged tail, bit-identical to the fused one-shot."""
+    from tests.gpu_util import bits
+    sim = lib
+    K = 32 if p <= 8 else 16
+    blk = 256 * 8  # bf16 elements per block (256 lanes x 8)
+    for tiles, left in ((1, K - 1), (3, 3 * K - 1), (3, K + 13), (5, 2 * K + 3), (3, 1)):
+        chunk = (tiles * K + left) * blk + 3 * 8 + 5  # one full phase, the last one, a rest and a ragged tail
+        n = p * chunk
+        xs = _inputs("bf16", "sum", p, n, 31 + tiles + left)
+        fused, ran_f = _run(sim, xs, "bf16", "sum", p, n, mode=2)
+        phased, ran_p = _run(sim, xs, "bf16", "sum", p, n, mode=1, wg=tiles * p)
+        assert ran_f == 0 and ran_p == 1
+        for r in range(p):
+            assert (bits(phased[r]) == bits(fused[r])).all(), (p, tiles, left, r)
+    assert sim.sim_debug_get("phased_expired") == 0
+
+
 def test_phased_small_and_degenerate(orc, lib):
     """No whole span at all (every vector done after the phases, no
     barrier), a chunk shorter than a vector, and n < p."""

@@ -317,3 +317,59 @@ def test_host_overlap_json(tmp_path):
         assert sim.sim_model_predict("oneshot", 8, "bf16", 4096) == pytest.approx(3.0)
     finally:
         sim.sim_model_reset()
+
+
+def test_second_regime_prices_from_the_switch(tmp_path):
+    """An "algos_hi" entry prices the one-shot from the size where it runs
+    phased (per rank count; never under a budget or when switched off) and
+    the single-launch ring above its LL limit; sim_model_set and a file
+    entry without "algos_hi" go back to one entry for every size."""
+    f = tmp_path / "m.json"
+    lo_os, hi_os = {"alpha_us": 2.0, "gbps": 5000.0}, {"alpha_us": 4.0, "gbps": 6400.0}
+    lo_rf, hi_rf = {"alpha_us": 10.0, "gbps": 3000.0}, {"alpha_us": 20.0, "gbps": 6000.0}
+    f.write_text(json.dumps({"algos": {"oneshot": lo_os, "ring_fifo": lo_rf},
+                             "algos_hi": {"oneshot": hi_os, "ring_fifo": hi_rf}}))
+
+    def t(e, p, S, law):  # one launch, law bytes per message byte
+        return e["alpha_us"] + law * S / (e["gbps"] * 1e3)
+
+    try:
+        sim.sim_model_load(str(f))
+        MIN = sim.sim_debug_get("phased_min")
+        pr = lambda algo, p, S: sim.sim_model_predict(algo, p, "bf16", S)
+        assert pr("oneshot", 8, MIN - 2) == pytest.approx(t(lo_os, 8, MIN - 2, 16))
+        assert pr("oneshot", 8, MIN) == pytest.approx(t(hi_os, 8, MIN, 16))
+        assert pr("oneshot", 4, MIN) == pytest.approx(t(lo_os, 4, MIN, 8))
+        assert pr("oneshot", 4, 2 * MIN) == pytest.approx(t(hi_os, 4, 2 * MIN, 8))
+        assert pr("oneshot", 2, 8 * MIN) == pytest.approx(t(lo_os, 2, 8 * MIN, 4))
+        assert pr("oneshot", 16, MIN) == pytest.approx(t(hi_os, 16, MIN, 32))
+        try:
+            sim.sim_config_set("max_workgroups", 64)  # no per-workgroup rate: B as it is
+            assert pr("oneshot", 8, 4 * MIN) == pytest.approx(t(lo_os, 8, 4 * MIN, 16))
+        finally:
+            sim.sim_config_set("max_workgroups", 0)
+        for mode, S, e in ((2, 4 * MIN, lo_os), (1, 4096, hi_os)):
+            try:
+                sim.sim_debug_set("phased", mode)
+                assert pr("oneshot", 8, S) == pytest.approx(t(e, 8, S, 16))
+            finally:
+                sim.sim_debug_set("phased", 0)
+        # the single-launch ring moves 51 S at p = 8 in bf16 (2pS + (p-1) 8 n + (p-1) 2 n, n = S / 2)
+        LL = sim.sim_debug_get("ring_ll_max")
+        assert pr("ring_fifo", 8, LL) == pytest.approx(t(lo_rf, 8, LL, 51))
+        assert pr("ring_fifo", 8, LL + 16) == pytest.approx(t(hi_rf, 8, LL + 16, 51))
+        # one entry for every size again
+        sim.sim_model_set("oneshot", 2.0, -1, -1, 5000.0)
+        assert pr("oneshot", 8, 4 * MIN) == pytest.approx(t(lo_os, 8, 4 * MIN, 16))
+        assert pr("ring_fifo", 8, LL + 16) == pytest.approx(t(hi_rf, 8, LL + 16, 51))
+        f.write_text(json.dumps({"algos": {"ring_fifo": lo_rf}}))
+        sim.sim_model_load(str(f))
+        assert pr("ring_fifo", 8, LL + 16) == pytest.approx(t(lo_rf, 8, LL + 16, 51))
+        # a bad second entry is refused and changes nothing
+        for bad in ('[]', '{"oneshot": {"alpha_us": 1.0}}', '{"oneshot": {"alpha_us": -1.0, "gbps": 1.0}}'):
+            f.write_text('{"algos": {"oneshot": {"alpha_us": 9.0, "gbps": 9.0}}, "algos_hi": %s}' % bad)
+            with pytest.raises(sim.SimError):
+                sim.sim_model_load(str(f))
+        assert pr("ring_fifo", 8, LL + 16) == pytest.approx(t(lo_rf, 8, LL + 16, 51))
+    finally:
+        sim.sim_model_reset()
