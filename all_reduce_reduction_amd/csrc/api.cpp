@@ -124,15 +124,16 @@ struct Ctx {
   // the single-launch ring runs its LL protocol up to this many bytes per rank
   size_t ring_ll_max = kRingLLMaxBytes;
   int ap_occ[4][5][2] = {};  // persistent all-pairs: [dtype][op][p == 8]
-  // phased one-shot: barrier slots (per slot an arrival counter, then
-  // ph_gmax release flags kPhasedFlagStride words apart), the count of
-  // barrier waits that gave up, and per slot the counter and flag values
-  // the next call starts from
+  // phased kernels: barrier slots (per slot a counter, ph_gmax release
+  // flags, then kPhasedGroups group counters, all kPhasedFlagStride words
+  // apart), the count of barrier waits that gave up, and per slot the
+  // counter, group counter and flag values the next call starts from
   unsigned long long* ph_mem = nullptr;
   int64_t ph_slot_words = 0;
   int ph_gmax = 0;
   unsigned int* ph_expired = nullptr;
   unsigned long long ph_ctr[kPhasedSlots] = {};
+  unsigned long long ph_gctr[kPhasedSlots][kPhasedGroups] = {};
   unsigned long long ph_seq[kPhasedSlots] = {};
   unsigned ph_next = 0;
   int ph_occ[4][5][4][4] = {};  // [dtype][op][log2 p - 1][form]: resident workgroups per CU (-1: none)
@@ -522,6 +523,8 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
   const unsigned slot = g.ph_next++ % kPhasedSlots;
   a.ctr = g.ph_mem + (int64_t)slot * g.ph_slot_words;
   a.flags = a.ctr + kPhasedFlagStride;
+  a.gctr = a.flags + (int64_t)g.ph_gmax * kPhasedFlagStride;
+  for (int q = 0; q < kPhasedGroups; q++) a.gbase[q] = g.ph_gctr[slot][q];
   a.base = g.ph_ctr[slot];
   a.seq = g.ph_seq[slot];
   a.spin_limit = std::min(g.spin_limit, kPhasedSpinLimit);
@@ -535,10 +538,15 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
                               : launch_fold_phased(c.dtype, c.op, p, all_out, a, c.s));
   if (rc) return rc;
 
-  // the counts this call adds: every workgroup meets every barrier.  A
-  // launch without barriers (no whole block to phase) never waits, so it
-  // does not hold up calls on other streams.
-  g.ph_ctr[slot] += (unsigned long long)nbar * (unsigned long long)G;
+  // the counts this call adds: every workgroup meets every barrier at its
+  // group's counter (workgroup b in group b mod NG), every group completes
+  // its share of every barrier once at the slot's counter.  A launch
+  // without barriers (no whole block to phase) never waits, so it does not
+  // hold up calls on other streams.
+  const int64_t NG = std::min<int64_t>(G, kPhasedGroups);
+  for (int64_t q = 0; q < NG; q++)
+    g.ph_gctr[slot][q] += (unsigned long long)nbar * (unsigned long long)(G / NG + (q < G % NG ? 1 : 0));
+  g.ph_ctr[slot] += (unsigned long long)nbar * (unsigned long long)NG;
   g.ph_seq[slot] += (unsigned long long)nbar;
   if (nbar > 0) {
     g.ph_launched = a.done_seq;
@@ -1353,7 +1361,7 @@ int sim_init(int device, int p_max, size_t max_bytes_per_rank) {
   }
   // phased one-shot barrier slots, zeroed (the expired count sits after them)
   g.ph_gmax = 2 * g.cu_count;
-  g.ph_slot_words = (int64_t)(g.ph_gmax + 1) * kPhasedFlagStride;
+  g.ph_slot_words = (int64_t)(1 + g.ph_gmax + kPhasedGroups) * kPhasedFlagStride;
   const int64_t ph_words = g.ph_slot_words * kPhasedSlots + kPhasedFlagStride;
   if (hipMalloc(&g.ph_mem, (size_t)ph_words * 8) != hipSuccess) {
     sim_finalize();

@@ -236,18 +236,27 @@ struct SchedArgs {
 // The phased kernels (k_phased.hip, k_phased_owner.hip, k_phased_gather.hip):
 // the grid loads (and folds) a phase's blocks into VGPRs, meets at a grid
 // barrier, writes them out, and meets again before the next phase.  Barrier state lives in one of kPhasedSlots slots (the
-// host takes them in turn, call by call): an arrival counter and one release
-// flag per workgroup, kPhasedFlagStride 64-bit words (256 bytes) apart.
+// host takes them in turn, call by call): a counter, one release flag per
+// workgroup and kPhasedGroups group counters, kPhasedFlagStride 64-bit
+// words (256 bytes) apart.
 constexpr int kPhasedSlots = 4;
 constexpr int kPhasedFlagStride = 32;
+// Arrivals count first per group of workgroups (workgroup b in group b mod
+// kPhasedGroups), each group on its own counter; the arrival that completes
+// a group's share of a barrier then counts once at the slot's counter.
+// Arrivals at one counter serialize (~12 ns each on MI355X), so 512
+// workgroups on one counter took ~6 us per barrier.
+constexpr int kPhasedGroups = 8;
 struct PhasedArgs {
   const void* x[SIM_MAX_RANKS];
   void* y[SIM_MAX_RANKS];
   int64_t lo[SIM_MAX_RANKS + 1];  // chunk bounds
   int64_t out_shift[SIM_MAX_RANKS];  // owner-only mode: y[j] index = i - out_shift[j] (a multiple of 16 bytes)
-  unsigned long long* ctr;        // the slot's arrival counter
+  unsigned long long* ctr;        // the slot's counter: groups' completed shares
   unsigned long long* flags;      // the slot's release flags
-  unsigned long long base;        // the counter's value when this call starts
+  unsigned long long* gctr;       // the slot's group counters, kPhasedFlagStride words apart
+  unsigned long long gbase[kPhasedGroups];  // the group counters' values when this call starts
+  unsigned long long base;        // the slot counter's value when this call starts
   unsigned long long seq;         // the flags' value when this call starts
   unsigned long long spin_limit;  // polls before a barrier wait gives up
   unsigned int* expired;          // barrier waits that gave up (timing only, not an error)

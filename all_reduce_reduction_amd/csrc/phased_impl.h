@@ -34,10 +34,11 @@
 // by one lane, so no workgroup ever reads what another writes, and the
 // result does not depend on when (or whether) a barrier opens.  A waiting
 // workgroup therefore gives up after the spin limit and carries on (counted
-// in *expired; never an error).  The barrier: each workgroup adds 1 to the
-// slot's arrival counter; the one whose addition completes the count raises
-// every workgroup's own flag word (256 bytes apart) to the release value,
-// and each workgroup's lane 0 polls only its own flag (phased_arrive).  Polling one shared
+// in *expired; never an error).  The barrier: each workgroup adds 1 to its
+// group's arrival counter, the arrival that completes a group's share adds
+// 1 to the slot's counter, and the one that completes that count raises
+// every workgroup's own flag word (256 bytes apart) to the release value;
+// each workgroup's lane 0 polls only its own flag (phased_arrive).  Polling one shared
 // counter instead (every waiting workgroup on one address) measured ~29 us
 // per barrier against ~4 us: the polls of hundreds of workgroups on one
 // memory location slow the reads still in flight.
@@ -60,36 +61,53 @@ template <int P> struct PhasedShape {
   static constexpr int D = P >= 16 ? 1 : 16 / P;  // about 16 loads in flight per lane
 };
 
-// One arrival at the slot's counter at each barrier, so a call adds nbar *
-// G, G = grid size and nbar = its barrier count.  Barrier k opens once R =
-// G - G / 10 of its G arrivals are in: the arrival that makes the call's
-// count (k - 1) G + R raises every workgroup's flag to seq + k with an
+// One arrival per workgroup at each barrier, counted in two levels: at the
+// counter of the workgroup's group (workgroup b in group b mod NG, NG =
+// min(kPhasedGroups, G), n_g workgroups each), and, by the arrival that
+// completes the group's share of a barrier, once at the slot's counter.  A
+// group's share of barrier k is complete at its R_g-th arrival, R_g = n_g -
+// n_g / 10 (the group's count reaching (k - 1) n_g + R_g); barrier k opens
+// when all NG groups have completed theirs (the slot's count reaching k
+// NG): that arrival raises every workgroup's flag to seq + k with an
 // atomic max, so flags only grow even if a later release overtakes this
-// one, and the last tenth pass straight through when they arrive.  Waiting
-// for the very last workgroup measured ~1.5% slower at 64 MiB per rank
-// (the slowest readers' tail overlaps the first writes instead of idling
-// the grid).  When every wait completes, barrier k opens exactly at its
-// R-th arrival; after a give-up, workgroups running ahead may complete a
-// count early and open a barrier early -- harmless, as the barrier guards
-// no data -- and none is left closed, as the count passes every (k - 1) G
-// + R on its way to nbar G.  The arrival that opens the last barrier also
-// writes done_seq to the host-visible word: from then on no workgroup of
-// the grid waits for anything, so another phased grid may start beside it.
-// (Workgroups do not arrive once more on leaving: the arrivals at one
-// counter serialize, ~10-20 ns each, and a second round at the grid's end
-// added to every call.)
+// one, and each group's last tenth passes straight through.  Waiting for
+// the very last workgroup measured ~1.5% slower at 64 MiB per rank (the
+// slowest readers' tail overlaps the first writes instead of idling the
+// grid).  A call adds nbar n_g to each group's counter and nbar NG to the
+// slot's.  When every wait completes, barrier k opens exactly when every
+// group has its R_g-th arrival; after a give-up, workgroups running ahead
+// may complete a count early and open a barrier early -- harmless, as the
+// barrier guards no data -- and none is left closed, as every count passes
+// all its thresholds on its way to its total.  The arrival that opens the
+// last barrier also writes done_seq to the host-visible word: from then on
+// no workgroup of the grid waits for anything, so another phased grid may
+// start beside it.  (One counter for all G arrivals serialized them at
+// ~12 ns each -- 512 workgroups, ~6 us per barrier; and workgroups do not
+// arrive once more on leaving, which added a second such round to every
+// call.)
 __device__ __forceinline__ void phased_arrive(const PhasedArgs& a, unsigned long long nbar,
                                               unsigned long long* s_rel) {
   __syncthreads();
-  const unsigned long long G = gridDim.x;
+  const unsigned G = gridDim.x;
   if (threadIdx.x == 0) {
-    const unsigned long long old = __hip_atomic_fetch_add(a.ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long done = old + 1 - a.base;  // arrivals of this call so far, this one included
-    const unsigned long long R = G - G / 10;
-    const bool opens = done >= R && (done - R) % G == 0;
-    const unsigned long long k = opens ? (done - R) / G + 1 : 0;  // the barrier this arrival opens
-    *s_rel = opens ? a.seq + (k < nbar ? k : nbar) : 0ull;
-    if (opens && k == nbar) __hip_atomic_store(a.done, a.done_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    const unsigned NG = G < (unsigned)kPhasedGroups ? G : (unsigned)kPhasedGroups;
+    const unsigned gi = blockIdx.x % NG;
+    const unsigned long long n = G / NG + (gi < G % NG ? 1u : 0u);  // workgroups in this group
+    const unsigned long long R = n - n / 10;
+    const unsigned long long old = __hip_atomic_fetch_add(a.gctr + (int64_t)gi * kPhasedFlagStride, 1ull,
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned long long done = old + 1 - a.gbase[gi];  // this group's arrivals of this call, this one included
+    unsigned long long rel = 0;
+    if (done >= R && (done - R) % n == 0) {  // the group's share of a barrier is complete
+      const unsigned long long told = __hip_atomic_fetch_add(a.ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned long long shares = told + 1 - a.base;
+      if (shares % NG == 0) {  // every group's: the barrier opens
+        const unsigned long long k = shares / NG;
+        rel = a.seq + (k < nbar ? k : nbar);
+        if (k == nbar) __hip_atomic_store(a.done, a.done_seq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+    *s_rel = rel;
   }
   __syncthreads();
   const unsigned long long rel = *s_rel;
