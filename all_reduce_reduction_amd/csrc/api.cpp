@@ -423,25 +423,26 @@ size_t phased_threshold(int form, int p) {
   // S bytes, not p S, and the copy reads only S / p, so their phase
   // separation gains less against the barriers' cost, and the copy's last
   // phase, not dealt out evenly (k_phased_gather.hip), leaves workgroups
-  // idle.  At p = 2 the fused forms already run at ~0.75 of peak.  Measured
-  // on MI355X, bf16, phased / fused (us):
-  //   p = 2: one-shot 48 MiB 34.7 / 34.5, 96 MiB 68.8 / 65.4; reduce-scatter
-  //          (input per rank) 32 MiB 20.2 / 18.0, 96 MiB 52.4 / 49.2;
-  //          all-gather (output per rank) 48 MiB 29.9 / 29.7, 64 MiB 34.3 / 38.1
-  //   p = 4: one-shot 24 MiB 36.1 / 35.9, 32 MiB 47.7 / 50.4; reduce-scatter
-  //          24 MiB 23.1 / 20.3, 32 MiB 28.9 / 31.7; all-gather 64 MiB
-  //          66.3 / 62.2, 96 MiB 92.1 / 88.7
-  //   p = 8: one-shot 12 MiB 36.7 / 35.1, 16 MiB 44.7 / 46.7; reduce-scatter
-  //          24 MiB 34.5 / 36.9, 32 MiB 44.0 / 48.8; all-gather 48 MiB
-  //          84.6 / 84.6, 64 MiB 103.6 / 119.4 (fp32 within 3% of these)
-  //   p = 16: one-shot 8 MiB 49.1 / 49.2, 16 MiB 92.0 / 96.6; reduce-scatter
-  //          16 MiB 43.9 / 46.8; all-gather 16 MiB 58.5 / 57.8, 24 MiB
-  //          85.4 / 90.1
+  // idle.  At p = 2 the fused one-shot already runs at ~0.75 of peak.
+  // Measured on MI355X, bf16, phased / fused (us):
+  //   p = 2: one-shot 32 MiB 22.7 / 24.8, 64 MiB 42.7 / 43.4, 96 MiB
+  //          68.5 / 65.7; reduce-scatter (input per rank) 24 MiB 13.1 / 12.5,
+  //          32 MiB 17.0 / 18.1; all-gather (output per rank) 12 MiB
+  //          10.5 / 9.7, 16 MiB 11.9 / 12.5
+  //   p = 4: one-shot 12 MiB 18.7 / 17.8, 16 MiB 24.0 / 28.0; reduce-scatter
+  //          24 MiB 21.4 / 19.8, 32 MiB 28.9 / 32.3; all-gather 16 MiB
+  //          17.4 / 17.3, 48 MiB 46.1 / 44.5, 64 MiB 66.0 / 65.1
+  //   p = 8: one-shot 8 MiB 24.9 / 23.1, 12 MiB 35.2 / 37.7; reduce-scatter
+  //          16 MiB 23.8 / 22.5, 24 MiB 35.4 / 36.4; all-gather 16 MiB
+  //          29.2 / 28.4, 24 MiB 42.4 / 45.0 (fp32 within 3% of bf16)
+  //   p = 16: one-shot 8 MiB 48.4 / 49.5; reduce-scatter 8 MiB 24.4 / 24.3,
+  //          12 MiB 34.5 / 35.7; all-gather 8 MiB 29.3 / 29.6, 12 MiB
+  //          42.3 / 45.4
   static const double kFrom[3][4] = {
       // p = 2, 4, 8, 16
-      {0.0, 2.0, 1.0, 1.0},  // one-shot
-      {0.0, 2.0, 2.0, 1.0},  // owner-only fold (direct reduce-scatter, all-pairs step 1)
-      {4.0, 0.0, 4.0, 1.5},  // copy (direct all-gather, all-pairs step 2)
+      {0.0, 1.0, 0.75, 0.5},   // one-shot
+      {2.0, 2.0, 1.5, 0.75},   // owner-only fold (direct reduce-scatter, all-pairs step 1)
+      {1.0, 0.0, 1.5, 0.75},   // copy (direct all-gather, all-pairs step 2)
   };
   if (g.phased_mode == 2 || g_max_wg > 0 || (p != 2 && p != 4 && p != 8 && p != 16)) return 0;
   if (g.phased_mode == 1) return 1;

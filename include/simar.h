@@ -72,8 +72,8 @@
  *     SIM_ALGO_ALLPAIRS and the direct all-gather (output bytes per rank;
  *     when n_in_per_rank fills whole 16-byte vectors), each from a size per
  *     rank that depends on the form and on p (SIM_DEBUG_PHASED_MIN; at
- *     p = 8: one-shot 16 MiB, reduce-scatter and step 1 32 MiB, all-gather
- *     and step 2 64 MiB), for p = 2, 4, 8, 16
+ *     p = 8: one-shot 12 MiB, reduce-scatter and step 1 24 MiB, all-gather
+ *     and step 2 24 MiB), for p = 2, 4, 8, 16
  *     and not under capture, under a workgroup budget or through
  *     sim_allreduce_noalloc, run as one persistent grid that meets at grid
  *     barriers between reading and writing.  The barriers order the traffic
@@ -448,12 +448,11 @@ enum {
                                   0 from SIM_DEBUG_PHASED_MIN bytes per rank on (default),
                                   1 whenever the call allows it, 2 never */
   SIM_DEBUG_PHASED_MIN = 15,   /* the unit of the phased kernels' thresholds (default 16 MiB):
-                                  at p = 8 the one-shot runs phased from 1 unit per rank,
+                                  at p = 8 the one-shot runs phased from 3/4 unit per rank,
                                   all-pairs step 1 and the direct reduce-scatter (input bytes)
-                                  from 2, all-pairs step 2 and the direct all-gather (output
-                                  bytes) from 4; other rank counts have their own multiples
-                                  (none at p = 2 for the one-shot and reduce-scatter, none at
-                                  p = 4 for the all-gather) */
+                                  and all-pairs step 2 and the direct all-gather (output bytes)
+                                  from 1.5; other rank counts have their own multiples (never at
+                                  p = 2 for the one-shot, never at p = 4 for the all-gather) */
   SIM_DEBUG_PHASED_EXPIRED = 16, /* phased fold barrier waits that gave up at the spin limit
                                   (synchronizes the device; set only to 0, which clears it) */
   SIM_DEBUG_PHASED_LAST = 17   /* get only: 1 if the last collective call ran a phased kernel */

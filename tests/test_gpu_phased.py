@@ -155,13 +155,13 @@ def test_phased_barrier_gives_up_without_changing_results(orc, lib):
 
 
 def test_phased_selection_rules(orc, lib):
-    """By default, at p = 8, the one-shot runs phased from 16 MiB per rank
-    on, the owner-only fold (direct reduce-scatter, all-pairs step 1) from
-    32 MiB and the copy (direct all-gather, all-pairs step 2) from 64 MiB;
-    other rank counts have their own thresholds (the one-shot from 32 MiB at
-    p = 4 and 16 MiB at p = 16, never at p = 2); never for rank counts other
-    than 2, 4, 8 and 16, under a workgroup budget or when switched off; the
-    threshold unit is settable (the others follow it)."""
+    """By default, at p = 8, the one-shot runs phased from 12 MiB per rank
+    on (3/4 of the 16 MiB unit), the owner-only fold (direct reduce-scatter,
+    all-pairs step 1) and the copy (direct all-gather, all-pairs step 2) from
+    24 MiB; other rank counts have their own thresholds (the one-shot from
+    16 MiB at p = 4 and 8 MiB at p = 16, never at p = 2); never for rank
+    counts other than 2, 4, 8 and 16, under a workgroup budget or when
+    switched off; the unit is settable (the thresholds follow it)."""
     import torch
     from tests.gpu_util import ptrs, stream
     sim = lib
@@ -182,11 +182,12 @@ def test_phased_selection_rules(orc, lib):
             sim.sim_debug_set("phased", 0)
             sim.sim_debug_set("phased_min", MIN)
 
-    assert ran(8, MIN) == 1
-    assert ran(8, MIN - 16) == 0
-    assert ran(4, MIN) == 0
-    assert ran(4, 2 * MIN) == 1
-    assert ran(16, MIN) == 1
+    assert ran(8, MIN * 3 // 4) == 1
+    assert ran(8, MIN * 3 // 4 - 16) == 0
+    assert ran(4, MIN - 16) == 0
+    assert ran(4, MIN) == 1
+    assert ran(16, MIN // 2) == 1
+    assert ran(16, MIN // 2 - 32) == 0
     assert ran(2, 4 * MIN) == 0
     assert ran(2, 4 * MIN, phased=1) == 1
     assert ran(6, 2 * MIN) == 0
@@ -201,8 +202,8 @@ def test_phased_selection_rules(orc, lib):
         ys = [torch.empty(n // 8, dtype=torch.int16, device="cuda:0") for _ in range(8)]
         assert sim.sim_reduce_scatter(ptrs(xs), ptrs(ys), 8, n // 8, "bf16", "sum", "allpairs", stream()) == 0
         return sim.sim_debug_get("phased_last")
-    assert ran_rs(2 * MIN - 16 * 8) == 0
-    assert ran_rs(2 * MIN) == 1
+    assert ran_rs(MIN * 3 // 2 - 16 * 8) == 0
+    assert ran_rs(MIN * 3 // 2) == 1
 
     def ran_ag(out_bytes):
         n_in = out_bytes // 2 // 8
@@ -210,8 +211,8 @@ def test_phased_selection_rules(orc, lib):
         ys = [torch.empty(8 * n_in, dtype=torch.int16, device="cuda:0") for _ in range(8)]
         assert sim.sim_all_gather(ptrs(xs), ptrs(ys), 8, n_in, "bf16", "allpairs", stream()) == 0
         return sim.sim_debug_get("phased_last")
-    assert ran_ag(4 * MIN - 16 * 8) == 0
-    assert ran_ag(4 * MIN) == 1
+    assert ran_ag(MIN * 3 // 2 - 16 * 8) == 0
+    assert ran_ag(MIN * 3 // 2) == 1
     torch.cuda.synchronize()
     assert sim.sim_debug_get("phased_expired") == 0
 

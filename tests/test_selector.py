@@ -337,12 +337,14 @@ def test_second_regime_prices_from_the_switch(tmp_path):
         sim.sim_model_load(str(f))
         MIN = sim.sim_debug_get("phased_min")
         pr = lambda algo, p, S: sim.sim_model_predict(algo, p, "bf16", S)
-        assert pr("oneshot", 8, MIN - 2) == pytest.approx(t(lo_os, 8, MIN - 2, 16))
-        assert pr("oneshot", 8, MIN) == pytest.approx(t(hi_os, 8, MIN, 16))
-        assert pr("oneshot", 4, MIN) == pytest.approx(t(lo_os, 4, MIN, 8))
-        assert pr("oneshot", 4, 2 * MIN) == pytest.approx(t(hi_os, 4, 2 * MIN, 8))
+        # phased from 3/4 of the unit at p = 8, 1 at p = 4, 1/2 at p = 16, never at p = 2
+        T8 = MIN * 3 // 4
+        assert pr("oneshot", 8, T8 - 2) == pytest.approx(t(lo_os, 8, T8 - 2, 16))
+        assert pr("oneshot", 8, T8) == pytest.approx(t(hi_os, 8, T8, 16))
+        assert pr("oneshot", 4, MIN - 2) == pytest.approx(t(lo_os, 4, MIN - 2, 8))
+        assert pr("oneshot", 4, MIN) == pytest.approx(t(hi_os, 4, MIN, 8))
         assert pr("oneshot", 2, 8 * MIN) == pytest.approx(t(lo_os, 2, 8 * MIN, 4))
-        assert pr("oneshot", 16, MIN) == pytest.approx(t(hi_os, 16, MIN, 32))
+        assert pr("oneshot", 16, MIN // 2) == pytest.approx(t(hi_os, 16, MIN // 2, 32))
         try:
             sim.sim_config_set("max_workgroups", 64)  # no per-workgroup rate: B as it is
             assert pr("oneshot", 8, 4 * MIN) == pytest.approx(t(lo_os, 8, 4 * MIN, 16))
