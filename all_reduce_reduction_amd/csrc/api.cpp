@@ -295,10 +295,12 @@ struct Call {
 // SIM_DEBUG_WORKGROUPS forces a total.
 // 16-byte vectors per lane per pass of a bulk kernel: forced by the debug
 // hook, else the calibration's launch table entry for this call, else 1.
-int unroll_for(const Call& c) {
-  if (g.unroll > 0) return g.unroll;
-  const int u = model_launch(g.model, c.algo, c.p, (double)c.n * esize_of(c.dtype)).unroll;
-  return u > 0 ? u : 1;
+// 16-byte vectors per lane per pass of a bulk kernel: SIM_DEBUG_UNROLL, else
+// the launch table's entry, else 1; at most max_u (the kernel's largest form)
+int unroll_for(const Call& c, int max_u = 2) {
+  int u = g.unroll > 0 ? g.unroll : model_launch(g.model, c.algo, c.p, (double)c.n * esize_of(c.dtype)).unroll;
+  if (u < 1) u = 1;
+  return u < max_u ? u : max_u;
 }
 
 int tiles_for(const Call& c, int64_t vecs_per_unit, int units, int unroll) {
@@ -384,8 +386,23 @@ int run_fold(const Call& c, bool all_out, const int64_t* lo, const int64_t* out_
   for (int q = 0; q <= c.p; q++) a.lo[q] = lo[q];
   a.p = c.p;
   a.inv_p = inv_p_of(c.p);
-  // the fold forms for p = 2, 4 and 8 have a 2-vector form
-  const int unroll = (c.p == 2 || c.p == 4 || c.p == 8) ? unroll_for(c) : 1;
+  // The fold forms for p = 2, 4 and 8 have 2- and 4-vector forms.  Under a
+  // workgroup budget below the CU count every workgroup has a CU to itself
+  // and the fold runs at the bytes each one keeps in flight, so it takes 4
+  // vectors per lane when the budget binds even at 4 (every budgeted
+  // workgroup still gets a whole span); on smaller messages, which a budget
+  // does not cap, the table's choice keeps the workgroup count up.  MI355X,
+  // p = 8 bf16 one-shot, 1 / 2 / 4 vectors: 64 MiB per rank under 32
+  // workgroups 691 / 810 / 608 us, under 128 234 / 270 / 213 us; 4 MiB under
+  // 128 16.9 / 19.3 / 14.8 us; at a budget of 256 the three are within 6%.
+  int unroll = 1;
+  if (c.p == 2 || c.p == 4 || c.p == 8) {
+    unroll = unroll_for(c, 4);
+    const int64_t span4 = (int64_t)kBlock * 4, vecs = (maxchunk + V - 1) / V;
+    if (g.unroll == 0 && g_max_wg > 0 && g_max_wg < g.cu_count &&
+        (vecs + span4 - 1) / span4 >= std::max<int64_t>(1, g_max_wg / c.p))
+      unroll = 4;
+  }
   a.tiles = tiles_for(c, (maxchunk + V - 1) / V, c.p, unroll);
   if (set && out_shift == nullptr) {
     FoldTabArgs t;
@@ -1850,7 +1867,7 @@ int sim_debug_set(int key, uint64_t value) {
     case SIM_DEBUG_LOG: g.log = value ? 1 : 0; return SIM_OK;
     case SIM_DEBUG_WORKGROUPS: g.force_wg = (int)value; return SIM_OK;
     case SIM_DEBUG_UNROLL:
-      if (value > 2) return SIM_ERR_INVALID_ARG;
+      if (value > 4 || value == 3) return SIM_ERR_INVALID_ARG;
       g.unroll = (int)value;
       return SIM_OK;
     case SIM_DEBUG_FIFO_CHANNELS:

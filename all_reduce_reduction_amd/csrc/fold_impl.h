@@ -174,9 +174,12 @@ __global__ void __launch_bounds__(kBlock) k_fold(Args a) {
 }
 
 // The launchers of one (P, PMAX) pair, for every dtype, op and output mode;
-// U = 2 only where the rank count is a compile-time constant of 8 or less
-// (with p up to 16 unknown, a second vector per lane would hold 2 * 16 * 4
-// more VGPRs).
+// U = 2 and U = 4 only where the rank count is a compile-time constant of 8
+// or less (with p up to 16 unknown, a second vector per lane would hold
+// 2 * 16 * 4 more VGPRs).  U = 4 keeps 4 p loads in flight per lane (128
+// VGPRs at p = 8): it is for launches with fewer workgroups than CUs (a
+// workgroup budget), where each workgroup has a CU to itself and the fold
+// runs at what one workgroup keeps in flight.
 template <int DT, int OP, int P, int PMAX, bool ALL_OUT, int U, class Args>
 static hipError_t go(const Args& a, hipStream_t s) {
   return launch<k_fold<DT, OP, P, PMAX, ALL_OUT, U, Args>>(dim3((unsigned)a.tiles * (unsigned)a.p), dim3(kBlock), s,
@@ -188,6 +191,8 @@ static hipError_t by_shape(bool all_out, int unroll, const Args& a, hipStream_t 
   if constexpr (P > 0 && P <= 8) {
     if (unroll == 2)
       return all_out ? go<DT, OP, P, PMAX, true, 2>(a, s) : go<DT, OP, P, PMAX, false, 2>(a, s);
+    if (unroll == 4)
+      return all_out ? go<DT, OP, P, PMAX, true, 4>(a, s) : go<DT, OP, P, PMAX, false, 4>(a, s);
   }
   return all_out ? go<DT, OP, P, PMAX, true, 1>(a, s) : go<DT, OP, P, PMAX, false, 1>(a, s);
 }

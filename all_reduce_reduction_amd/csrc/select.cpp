@@ -38,20 +38,20 @@ Model default_model() {
   // {alpha_us, gbps, steps, bytes_factor, wg_gbps, host_us}, from the MI355X
   // calibration (p = 8, bf16)
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0, 0.0, 0.0};
-  m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.5, 2.8};
-  m.a[SIM_ALGO_ALLPAIRS] = {2.1, 6100.0, -1.0, -1.0, 43.5, 3.0};
-  m.a[SIM_ALGO_ONESHOT] = {1.4, 5850.0, -1.0, -1.0, 48.1, 3.25};
-  m.a[SIM_ALGO_ONESHOT_LL] = {8.9, 13150.0, -1.0, -1.0, 8.9, 0.0};
-  m.a[SIM_ALGO_RING_FIFO] = {13.6, 665.0, -1.0, -1.0, 16.2, 0.0};
-  m.a[SIM_ALGO_TREE] = {3.2, 6200.0, -1.0, -1.0, 0.0, 4.4};
-  m.a[SIM_ALGO_REXCH] = {2.25, 6050.0, -1.0, -1.0, 0.0, 4.25};
-  m.a[SIM_ALGO_HIER] = {3.35, 6250.0, -1.0, -1.0, 0.0, 4.4};
-  m.a[SIM_ALGO_HIER_LARGE] = {3.25, 6050.0, -1.0, -1.0, 0.0, 4.6};
-  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {7.0, 8050.0, -1.0, -1.0, 32.0, 0.0};
+  m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.4, 2.8};
+  m.a[SIM_ALGO_ALLPAIRS] = {2.1, 6100.0, -1.0, -1.0, 47.2, 3.0};
+  m.a[SIM_ALGO_ONESHOT] = {1.7, 6200.0, -1.0, -1.0, 53.5, 3.3};
+  m.a[SIM_ALGO_ONESHOT_LL] = {8.9, 12600.0, -1.0, -1.0, 8.8, 0.0};
+  m.a[SIM_ALGO_RING_FIFO] = {14.0, 675.0, -1.0, -1.0, 16.2, 0.0};
+  m.a[SIM_ALGO_TREE] = {3.1, 6200.0, -1.0, -1.0, 0.0, 4.2};
+  m.a[SIM_ALGO_REXCH] = {2.3, 6050.0, -1.0, -1.0, 0.0, 4.1};
+  m.a[SIM_ALGO_HIER] = {3.3, 6200.0, -1.0, -1.0, 0.0, 4.3};
+  m.a[SIM_ALGO_HIER_LARGE] = {3.2, 6050.0, -1.0, -1.0, 0.0, 4.5};
+  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {6.9, 8000.0, -1.0, -1.0, 32.0, 0.0};
   // second regimes: the phased one-shot, the single-launch ring's FIFO protocol
-  m.hi[SIM_ALGO_ONESHOT] = {3.35, 6300.0, -1.0, -1.0, 48.1, 0.0};
+  m.hi[SIM_ALGO_ONESHOT] = {6.7, 6300.0, -1.0, -1.0, 53.5, 0.0};
   m.has_hi[SIM_ALGO_ONESHOT] = true;
-  m.hi[SIM_ALGO_RING_FIFO] = {24.0, 6450.0, -1.0, -1.0, 16.2, 50.5};
+  m.hi[SIM_ALGO_RING_FIFO] = {24.0, 6450.0, -1.0, -1.0, 16.2, 51.0};
   m.has_hi[SIM_ALGO_RING_FIFO] = true;
   return m;
 }

@@ -367,7 +367,12 @@ int sim_copy_streams(const void* const* src_ptrs, void* const* dst_ptrs, int k, 
  *                              number of thread blocks so the rest of the GPU
  *                              stays free for compute).  0 (default) = no cap;
  *                              the single-launch ring still uses at least one
- *                              workgroup per rank.  Results do not depend on it.
+ *                              workgroup per rank.  Below the CU count, where
+ *                              it caps the launch, the fused fold (one-shot,
+ *                              all-pairs step 1, direct reduce-scatter) keeps
+ *                              4 vectors per lane in flight instead of the
+ *                              launch table's 1 or 2.
+ *                              Results do not depend on it.
  * Out-of-range values are SIM_ERR_INVALID_ARG and change nothing. */
 enum { SIM_CONFIG_RANKS_PER_NODE = 0, SIM_CONFIG_RADIX = 1, SIM_CONFIG_MAX_WORKGROUPS = 2 };
 int sim_config_set(int key, int value);
@@ -433,8 +438,10 @@ enum {
   SIM_DEBUG_FILL_LL = 3,       /* fill the LL buffer with this 64-bit packet (synchronous) */
   SIM_DEBUG_LOG = 4,           /* 1: log one line per call to stderr (also SIM_DEBUG=1) */
   SIM_DEBUG_WORKGROUPS = 5,    /* force the workgroup count of bulk kernels (0 = heuristic) */
-  SIM_DEBUG_UNROLL = 6,        /* 16-byte vectors per lane per pass in bulk kernels: 1 or 2
-                                  (0, the default: the launch table's entry, else 1) */
+  SIM_DEBUG_UNROLL = 6,        /* 16-byte vectors per lane per pass in bulk kernels: 1, 2 or 4
+                                  (4: the fused fold at p = 2, 4, 8; other kernels take 2);
+                                  0, the default: the launch table's entry, else 1, and the
+                                  fused fold takes 4 where a budget below the CU count caps it */
   SIM_DEBUG_FIFO_CHANNELS = 7, /* single-launch ring: channels per rank, <= 128 (0 = heuristic) */
   SIM_DEBUG_FIFO_SLOTS = 8,    /* single-launch ring: slots per FIFO, 2..8 (default 4) */
   SIM_DEBUG_FIFO_WITHHOLD = 9, /* 1: rank 0's ring workgroups leave at once (forces a bounded-wait expiry) */

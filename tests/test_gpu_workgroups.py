@@ -104,3 +104,50 @@ def test_launch_table(orc, lib, tmp_path, unroll):
         _check_all(orc, lib, f"table unroll {unroll}")
     finally:
         lib.sim_model_load(lib.CALIBRATION)
+
+
+@pytest.mark.parametrize("how", ["budget 7", "budget 64", "forced 4"])
+@pytest.mark.parametrize("p", [2, 4, 8])
+def test_fold_four_vectors_per_lane(orc, lib, how, p):
+    """The fused fold's 4-vector form (taken where a workgroup budget below
+    the CU count caps the launch -- budget 7 here; under budget 64 these
+    sizes keep the table's form -- or forced with SIM_DEBUG_UNROLL = 4)
+    against the oracle:
+    one-shot and all-pairs for every dtype and op, in place and not, and the
+    direct reduce-scatter, on a ragged size with several 4-vector spans per
+    chunk and a partial last span."""
+    from tests.gpu_util import (assert_parity, empty_like_poisoned, ptrs, run_allreduce, stream, to_device,
+                                to_host)
+    kind, val = how.split()
+    if kind == "budget":
+        lib.sim_config_set("max_workgroups", int(val))
+    else:
+        lib.sim_debug_set("unroll", int(val))
+    try:
+        n = p * 8192 * 3 + 77  # a 4-vector span is 256 lanes x 4 x 16 bytes = 8192 bf16 elements
+        for dtype in ("int32", "fp32", "fp16", "bf16"):
+            for op in ("sum", "prod", "min", "max", "avg"):
+                xs = _inputs(p, n, dtype, 90 + p, orc)
+                if op == "prod":
+                    import synthdata
+                    xs = (synthdata.int_uniform(91, p, n, -3, 3) if dtype == "int32"
+                          else synthdata.uniform(91, p, n, 0.5, 2.0, dtype))
+                for algo in ("oneshot", "allpairs"):
+                    want, _ = orc.allreduce(xs, dtype, op, algo)
+                    for inplace in (False, True):
+                        print(f"{how} p={p} {algo} {dtype} {op} inplace={inplace} n={n}", flush=True)
+                        got = run_allreduce(xs, dtype, op, algo, inplace=inplace)
+                        for r in range(p):
+                            assert_parity(got[r], want[r], dtype, f"{how} {algo} {dtype} {op} r{r}")
+        n_out = 8192 * 2 + 5
+        xs = _inputs(p, p * n_out, "bf16", 92, orc)
+        din = to_device(xs, "bf16")
+        dout = empty_like_poisoned(n_out, "bf16", p)
+        assert lib.sim_reduce_scatter(ptrs(din), ptrs(dout), p, n_out, "bf16", "sum", "allpairs", stream()) == 0
+        got = to_host(dout, "bf16")
+        want, _ = orc.reduce_scatter(xs, "bf16", "sum", "allpairs")
+        for r in range(p):
+            assert_parity(got[r], want[r], "bf16", f"{how} RS r{r}")
+    finally:
+        lib.sim_config_set("max_workgroups", 0)
+        lib.sim_debug_set("unroll", 0)
