@@ -206,13 +206,14 @@ def fit_host(points, algo):
 # Launch-configuration sweep (after T-CCL's offline ranking of CTA
 # configurations per collective and size, section III-C3): the bulk
 # schedules at each grid size with a range of total workgroups and one or
-# two 16-byte vectors per lane; (0, 1) is the library's default (one vector
+# two 16-byte vectors per lane (also four for the one-shot, whose fused fold
+# has that form); (0, 1) is the library's default (one vector
 # per lane, one workgroup per kBlock vectors, covering the transfer).  The
 # best pair per size goes into the calibration file; a pair within 1% of the
 # default's time keeps the default.
 WG_ALGOS = ("oneshot", "allpairs", "ring")
 WG_TOTALS = (0, 256, 512, 1024, 2048, 4096, 8192, 16384)
-WG_UNROLLS = (1, 2)  # 16-byte vectors per lane per pass
+WG_UNROLLS = {"oneshot": (1, 2, 4), "allpairs": (1, 2), "ring": (1, 2)}  # 16-byte vectors per lane per pass
 
 
 def sweep_workgroups(sim, b, sizes):
@@ -225,7 +226,7 @@ def sweep_workgroups(sim, b, sizes):
                 continue
             n = nbytes // 2
             times = {}
-            for unroll in WG_UNROLLS:
+            for unroll in WG_UNROLLS[algo]:
                 sim.sim_debug_set("unroll", unroll)
                 for total in WG_TOTALS:
                     sim.sim_debug_set("workgroups", total)

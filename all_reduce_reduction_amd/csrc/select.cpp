@@ -39,19 +39,19 @@ Model default_model() {
   // calibration (p = 8, bf16)
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0, 0.0, 0.0};
   m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.4, 2.8};
-  m.a[SIM_ALGO_ALLPAIRS] = {2.1, 6100.0, -1.0, -1.0, 47.2, 3.0};
-  m.a[SIM_ALGO_ONESHOT] = {1.7, 6200.0, -1.0, -1.0, 53.5, 3.3};
-  m.a[SIM_ALGO_ONESHOT_LL] = {8.9, 12600.0, -1.0, -1.0, 8.8, 0.0};
-  m.a[SIM_ALGO_RING_FIFO] = {14.0, 675.0, -1.0, -1.0, 16.2, 0.0};
-  m.a[SIM_ALGO_TREE] = {3.1, 6200.0, -1.0, -1.0, 0.0, 4.2};
-  m.a[SIM_ALGO_REXCH] = {2.3, 6050.0, -1.0, -1.0, 0.0, 4.1};
-  m.a[SIM_ALGO_HIER] = {3.3, 6200.0, -1.0, -1.0, 0.0, 4.3};
-  m.a[SIM_ALGO_HIER_LARGE] = {3.2, 6050.0, -1.0, -1.0, 0.0, 4.5};
+  m.a[SIM_ALGO_ALLPAIRS] = {2.1, 6100.0, -1.0, -1.0, 47.3, 3.0};
+  m.a[SIM_ALGO_ONESHOT] = {1.75, 6300.0, -1.0, -1.0, 53.1, 3.25};
+  m.a[SIM_ALGO_ONESHOT_LL] = {8.9, 13250.0, -1.0, -1.0, 8.9, 0.0};
+  m.a[SIM_ALGO_RING_FIFO] = {13.9, 685.0, -1.0, -1.0, 16.3, 0.0};
+  m.a[SIM_ALGO_TREE] = {3.05, 6200.0, -1.0, -1.0, 0.0, 4.15};
+  m.a[SIM_ALGO_REXCH] = {2.25, 6050.0, -1.0, -1.0, 0.0, 4.0};
+  m.a[SIM_ALGO_HIER] = {3.2, 6200.0, -1.0, -1.0, 0.0, 4.3};
+  m.a[SIM_ALGO_HIER_LARGE] = {3.0, 6050.0, -1.0, -1.0, 0.0, 4.35};
   m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {6.9, 8000.0, -1.0, -1.0, 32.0, 0.0};
   // second regimes: the phased one-shot, the single-launch ring's FIFO protocol
-  m.hi[SIM_ALGO_ONESHOT] = {6.7, 6300.0, -1.0, -1.0, 53.5, 0.0};
+  m.hi[SIM_ALGO_ONESHOT] = {6.4, 6250.0, -1.0, -1.0, 53.1, 0.0};
   m.has_hi[SIM_ALGO_ONESHOT] = true;
-  m.hi[SIM_ALGO_RING_FIFO] = {24.0, 6450.0, -1.0, -1.0, 16.2, 51.0};
+  m.hi[SIM_ALGO_RING_FIFO] = {24.0, 6450.0, -1.0, -1.0, 16.3, 51.0};
   m.has_hi[SIM_ALGO_RING_FIFO] = true;
   return m;
 }
@@ -466,9 +466,9 @@ bool model_load_json(const char* path, Model* m, std::string* err) {
         bool ok = shape && e.arr[0].kind == JVal::NUM && e.arr[1].kind == JVal::NUM && e.arr[0].num > 0 &&
                   e.arr[1].num >= 0 && e.arr[1].num <= (double)(1 << 24);
         if (ok && e.arr.size() == 3)
-          ok = e.arr[2].kind == JVal::NUM && (e.arr[2].num == 1 || e.arr[2].num == 2);
+          ok = e.arr[2].kind == JVal::NUM && (e.arr[2].num == 1 || e.arr[2].num == 2 || e.arr[2].num == 4);
         if (!ok) {
-          if (err) *err = "workgroup entries are [bytes > 0, total in 0..2^24(, vectors per lane 1 or 2)]";
+          if (err) *err = "workgroup entries are [bytes > 0, total in 0..2^24(, vectors per lane 1, 2 or 4)]";
           return false;
         }
         LaunchEntry le;

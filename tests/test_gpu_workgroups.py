@@ -93,7 +93,7 @@ def test_forced_workgroups(orc, lib, total):
         lib.sim_debug_set("workgroups", 0)
 
 
-@pytest.mark.parametrize("unroll", [None, 1, 2])
+@pytest.mark.parametrize("unroll", [None, 1, 2, 4])
 def test_launch_table(orc, lib, tmp_path, unroll):
     f = tmp_path / "table.json"
     extra = [] if unroll is None else [unroll]

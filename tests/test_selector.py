@@ -191,11 +191,12 @@ def test_launch_table_json(tmp_path):
 
 def test_unroll_debug_hook_range():
     assert sim.sim_debug_get("unroll") == 0  # default: the launch table decides
-    for v in (1, 2, 0):
+    for v in (1, 2, 4, 0):
         sim.sim_debug_set("unroll", v)
         assert sim.sim_debug_get("unroll") == v
-    with pytest.raises(sim.SimError):
-        sim.sim_debug_set("unroll", 3)
+    for v in (3, 5):
+        with pytest.raises(sim.SimError):
+            sim.sim_debug_set("unroll", v)
 
 
 def test_workgroup_budget_config():
