@@ -44,7 +44,8 @@ CONFIG = {"ranks_per_node": 0, "radix": 1, "max_workgroups": 2}
 DEBUG = {"epoch": 0, "spin_limit": 1, "ll_wait_skew": 2, "fill_ll": 3, "log": 4, "workgroups": 5,
          "unroll": 6, "fifo_channels": 7, "fifo_slots": 8, "fifo_withhold": 9, "fifo_vecs": 10,
          "ptr_table": 11, "ptr_sets": 12, "ring_ll_max": 13,
-              "phased": 14, "phased_min": 15, "phased_expired": 16, "phased_last": 17}
+              "phased": 14, "phased_min": 15, "phased_expired": 16, "phased_last": 17,
+         "phased_layout": 18, "phased_whole_last": 19}
 MAX_RANKS = 16
 LL_MAX_BYTES_PER_RANK = 1 << 20
 

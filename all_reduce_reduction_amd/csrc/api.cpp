@@ -140,6 +140,9 @@ struct Ctx {
   int phased_mode = 0;       // 0: from phased_min bytes per rank on, 1: always, 2: never
   size_t phased_min = kPhasedMinBytes;
   bool last_phased = false;  // the current (or last) call ran a phased fold
+  bool last_whole = false;   // ... the phased one-shot in the whole-buffer layout
+  int ph_layout = 0;         // 0: the one-shot's whole-buffer layout where it applies; 1: per chunk
+  int ph_occ_whole[4][5][4] = {};  // that layout's kernel: workgroups per CU (0 = not asked yet, -1 = none)
   // the most recent phased launch with a barrier: its stream and sequence
   // number, and the pinned host word the workgroup that opens its last
   // barrier writes that number to
@@ -525,10 +528,32 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
     nmax = std::max(nmax, nvec / (copy ? kBlock * K : kBlock));
   }
   const int64_t per_phase = copy ? tiles : tiles * K;
-  const int64_t nphase = (nmax + per_phase - 1) / per_phase;
+  int64_t nphase = (nmax + per_phase - 1) / per_phase;
+  // The one-shot's whole-buffer layout (phased_impl.h): when every chunk is
+  // the same whole number of blocks, and no fewer blocks than the grid has
+  // workgroups, the grid's workgroups take the whole buffer's blocks in
+  // turn, G blocks per step, instead of each chunk's in turn.
+  const int64_t bel = (int64_t)kBlock * V;  // elements per block
+  const int64_t n = lo[p];
+  bool whole = form == kPhasedAll && g.ph_layout == 0 && lo[0] == 0 && n % (p * bel) == 0 &&
+               n / (p * bel) >= G;
+  for (int q = 1; whole && q < p; q++) whole = lo[q] == q * (n / p);
+  if (whole) {  // its kernel must fit the same grid, all resident
+    int& wocc = g.ph_occ_whole[c.dtype][c.op][pi];
+    if (wocc == 0) {
+      wocc = fold_phased_blocks_per_cu(c.dtype, c.op, p, true, true);
+      if (wocc < 1) wocc = -1;
+    }
+    whole = wocc >= std::min(occ, 2);
+  }
+  if (whole) nphase = (n / bel + G * K - 1) / (G * K);
   const int64_t nbar = nphase > 0 ? 2 * nphase - 1 : 0;
   PhasedArgs a;
   std::memset(&a, 0, sizeof a);
+  if (whole) {
+    a.gblk = n / bel;
+    a.gbpc = n / (p * bel);
+  }
   for (int q = 0; q < p; q++) {
     // the fan-out's block q comes from output q itself (the kernel indexes
     // its source as x[q] - lo[q] by output element)
@@ -572,6 +597,7 @@ int run_phased(const Call& c, const int64_t* lo, PhasedForm form, const int64_t*
     g.ph_any = true;
   }
   g.last_phased = true;
+  g.last_whole = whole;
   return SIM_OK;
 }
 
@@ -1271,6 +1297,7 @@ int begin_call(void* stream) {
   g.capturing = (st != hipStreamCaptureStatusNone);
   if (g.capturing) g.captured = true;
   g.last_phased = false;
+  g.last_whole = false;
   return SIM_OK;
 }
 
@@ -1882,6 +1909,10 @@ int sim_debug_set(int key, uint64_t value) {
       g.phased_mode = (int)value;
       return SIM_OK;
     case SIM_DEBUG_PHASED_MIN: g.phased_min = (size_t)value; return SIM_OK;
+    case SIM_DEBUG_PHASED_LAYOUT:
+      if (value > 1) return SIM_ERR_INVALID_ARG;
+      g.ph_layout = (int)value;
+      return SIM_OK;
     case SIM_DEBUG_PHASED_EXPIRED: {
       if (value != 0) return SIM_ERR_INVALID_ARG;
       if (!g.init) return SIM_ERR_NOT_INIT;
@@ -1933,6 +1964,8 @@ int sim_debug_get(int key, uint64_t* value) {
     case SIM_DEBUG_PHASED: *value = (uint64_t)g.phased_mode; return SIM_OK;
     case SIM_DEBUG_PHASED_MIN: *value = (uint64_t)g.phased_min; return SIM_OK;
     case SIM_DEBUG_PHASED_LAST: *value = g.last_phased ? 1 : 0; return SIM_OK;
+    case SIM_DEBUG_PHASED_LAYOUT: *value = (uint64_t)g.ph_layout; return SIM_OK;
+    case SIM_DEBUG_PHASED_WHOLE_LAST: *value = g.last_whole ? 1 : 0; return SIM_OK;
     case SIM_DEBUG_PHASED_EXPIRED: {
       if (!g.init) return SIM_ERR_NOT_INIT;
       unsigned int v = 0;

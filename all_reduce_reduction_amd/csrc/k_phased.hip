@@ -1,22 +1,28 @@
 // k_phased.hip -- the phased fold (phased_impl.h) with every rank's output
 // written: the one-shot all-reduce for large messages; and the launchers of
-// both output modes (the owner-only mode is instantiated in
-// k_phased_owner.hip).
+// both output modes and layouts (the owner-only mode is instantiated in
+// k_phased_owner.hip, the one-shot's whole-buffer layout in
+// k_phased_whole.hip).
 #include "phased_impl.h"
 
 namespace simar {
 
-template hipError_t phased_launch<true>(int, int, int, const PhasedArgs&, hipStream_t);
-template int phased_occupancy<true>(int, int, int);
-extern template hipError_t phased_launch<false>(int, int, int, const PhasedArgs&, hipStream_t);
-extern template int phased_occupancy<false>(int, int, int);
+template hipError_t phased_launch<true, false>(int, int, int, const PhasedArgs&, hipStream_t);
+template int phased_occupancy<true, false>(int, int, int);
+extern template hipError_t phased_launch<false, false>(int, int, int, const PhasedArgs&, hipStream_t);
+extern template int phased_occupancy<false, false>(int, int, int);
+extern template hipError_t phased_launch<true, true>(int, int, int, const PhasedArgs&, hipStream_t);
+extern template int phased_occupancy<true, true>(int, int, int);
 
+// all_out with a.gblk > 0: the one-shot in the whole-buffer layout
 hipError_t launch_fold_phased(int dtype, int op, int p, bool all_out, const PhasedArgs& a, hipStream_t s) {
-  return all_out ? phased_launch<true>(dtype, op, p, a, s) : phased_launch<false>(dtype, op, p, a, s);
+  if (!all_out) return phased_launch<false, false>(dtype, op, p, a, s);
+  return a.gblk > 0 ? phased_launch<true, true>(dtype, op, p, a, s) : phased_launch<true, false>(dtype, op, p, a, s);
 }
 
-int fold_phased_blocks_per_cu(int dtype, int op, int p, bool all_out) {
-  return all_out ? phased_occupancy<true>(dtype, op, p) : phased_occupancy<false>(dtype, op, p);
+int fold_phased_blocks_per_cu(int dtype, int op, int p, bool all_out, bool whole) {
+  if (!all_out) return phased_occupancy<false, false>(dtype, op, p);
+  return whole ? phased_occupancy<true, true>(dtype, op, p) : phased_occupancy<true, false>(dtype, op, p);
 }
 
 int fold_phased_vecs_per_lane(int p) {

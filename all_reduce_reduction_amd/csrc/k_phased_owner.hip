@@ -5,7 +5,7 @@
 
 namespace simar {
 
-template hipError_t phased_launch<false>(int, int, int, const PhasedArgs&, hipStream_t);
-template int phased_occupancy<false>(int, int, int);
+template hipError_t phased_launch<false, false>(int, int, int, const PhasedArgs&, hipStream_t);
+template int phased_occupancy<false, false>(int, int, int);
 
 }  // namespace simar

@@ -262,6 +262,8 @@ struct PhasedArgs {
   unsigned int* expired;          // barrier waits that gave up (timing only, not an error)
   unsigned long long* done;       // host-visible word: the opener of the last barrier writes done_seq
   unsigned long long done_seq;
+  int64_t gblk;                   // the one-shot's whole-buffer layout: the buffer's blocks (0: per chunk)
+  int64_t gbpc;                   // whole-buffer layout: blocks per chunk (every chunk the same, >= the grid)
   int tiles;                      // workgroups per chunk (grid = tiles * p)
   int nphase;
   float inv_p;
@@ -324,7 +326,8 @@ int allpairs_persistent_blocks_per_cu(int dtype, int op, int p);
 // reduce-scatter); its resident workgroups per CU, and its result vectors
 // per lane per phase.
 hipError_t launch_fold_phased(int dtype, int op, int p, bool all_out, const PhasedArgs& a, hipStream_t s);
-int fold_phased_blocks_per_cu(int dtype, int op, int p, bool all_out);
+// whole: the one-shot's whole-buffer layout (PhasedArgs::gblk > 0)
+int fold_phased_blocks_per_cu(int dtype, int op, int p, bool all_out, bool whole = false);
 int fold_phased_vecs_per_lane(int p);
 // The phased copy (k_phased_gather.hip; out_shift unused, lo the output
 // blocks, x[j] - lo[j] the source of block j indexed by output element):

@@ -179,8 +179,11 @@ __device__ __forceinline__ void for_each_run(F&& f) {
 
 }  // namespace
 
-template <int DT, int OP, int P, bool ALL_OUT>
+// WHOLE (the one-shot only; the host sets a.gblk): the whole-buffer layout
+// of a phase's blocks, see the phase loop below.
+template <int DT, int OP, int P, bool ALL_OUT, bool WHOLE>
 __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
+  static_assert(ALL_OUT || !WHOLE, "the whole-buffer layout writes every output");
   typedef typename Ty<DT>::A A;
   typedef Op<DT, OP> O;
   constexpr int V = epv<DT>();
@@ -193,10 +196,12 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
   const float inv_p = a.inv_p;
   __shared__ unsigned long long s_rel;
 
-  // operand k of the fold: rank j for k == 0, then the ranks != j ascending
+  // operand k of the fold: rank j for k == 0, then the ranks != j ascending.
+  // The whole-buffer layout loads the ranks in their own order and puts each
+  // block's operands in its chunk's order in registers (fold_in below).
   const void* xp[P];
 #pragma unroll
-  for (int k = 0; k < P; k++) xp[k] = a.x[(k == 0) ? j : (k <= j ? k - 1 : k)];
+  for (int k = 0; k < P; k++) xp[k] = WHOLE ? a.x[k] : a.x[(k == 0) ? j : (k <= j ? k - 1 : k)];
   // outputs: every rank's, or (owner-only) rank j's, element i at i - shift
   void* yp[ALL_OUT ? P : 1];
 #pragma unroll
@@ -229,6 +234,18 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
     for (int e = 0; e < V; e++) acc[e] = O::post(acc[e], P);
     return pack<DT>(acc);
   };
+  // the same fold of a block of chunk c whose operands L[q] are rank q's:
+  // rank c first, then the ranks != c ascending (c uniform: every select is
+  // one v_cndmask per dword on a scalar condition)
+  auto fold_in = [&](const u32x4* L, int c) {
+    u32x4 Lc[P];
+    Lc[0] = L[0];
+#pragma unroll
+    for (int q = 1; q < P; q++) Lc[0] = (q == c) ? L[q] : Lc[0];
+#pragma unroll
+    for (int k = 1; k < P; k++) Lc[k] = (k - 1 < c) ? L[k - 1] : L[k];
+    return fold(Lc);
+  };
 
   // read B blocks, k0 ... k0 + B - 1, into R[S0 ... S0 + B - 1]: D sets of
   // p loads in flight while one set folds.  The scheduling barriers keep
@@ -236,7 +253,8 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
   // without them the compiler interleaved the 32-bit folds with their own
   // loads, waiting on every load (1-3 in flight per wave instead of ~16; the
   // fp32 phased reduce-scatter ran 1.5x slower than the bf16 one).
-  auto read_run = [&](auto b_tag, auto s_tag, u32x4* R, int64_t sbyte, int64_t kst, int k0)
+  // chunk_of(k): the chunk of the workgroup's block k of the phase (WHOLE)
+  auto read_run = [&](auto b_tag, auto s_tag, u32x4* R, int64_t sbyte, int64_t kst, int k0, auto&& chunk_of)
                       __attribute__((always_inline)) {
     constexpr int B = decltype(b_tag)::value, S0 = decltype(s_tag)::value;
     constexpr int DR = D < B ? D : B;
@@ -248,7 +266,10 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < B; i++) {
-      R[S0 + i] = fold(L[i % DR]);
+      if constexpr (WHOLE)
+        R[S0 + i] = fold_in(L[i % DR], chunk_of(k0 + i));
+      else
+        R[S0 + i] = fold(L[i % DR]);
       if (i + DR < B) {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -277,16 +298,53 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
     }
   };
 
+  // The layout of a phase's blocks.  Per chunk: workgroup (j, t) holds
+  // blocks of chunk j, the chunk's workgroups taking its blocks in turn, so
+  // each step of the write half covers p ranges of tiles blocks, a chunk
+  // apart.  WHOLE (the one-shot, when every chunk is the same whole number
+  // of blocks, no fewer than the grid's G workgroups): the grid takes the
+  // whole buffer's blocks in turn, workgroup (j, t) at turn j tiles + t (so
+  // each XCD's workgroups hold neighbouring blocks), and each step of the
+  // write half covers one range of G blocks.  Each block keeps its own
+  // chunk's fold order.  Measured on MI355X (p = 8, bf16, 64 MiB per rank):
+  // 168 against 174-175 us, the p write ranges next to each other instead
+  // of a chunk apart.
+  const int G = a.tiles * P;
+  const int lt = WHOLE ? G : a.tiles;                   // workgroups taking turns
+  const int lpos = WHOLE ? j * a.tiles + t : t;         // this workgroup's turn
+  const int64_t lblk = WHOLE ? a.gblk : nvec / kBlock;  // whole blocks laid out
+  const int64_t lbyte = WHOLE ? 0 : vbeg * E;           // byte of the first
   const unsigned long long nbar = a.nphase > 0 ? 2ull * a.nphase - 1 : 0ull;  // barriers of this call
   unsigned long long nb = 0;
-  const int64_t nblk = nvec / kBlock;                   // the chunk's whole blocks
-  const int64_t kst = (int64_t)a.tiles * kBlock * 16;   // bytes from one of a workgroup's blocks to the next
+  const int64_t kst = (int64_t)lt * kBlock * 16;  // bytes from one of a workgroup's blocks to the next
   for (int ph = 0; ph < a.nphase; ph++) {
-    const PhaseBlocks pb = phase_blocks<K>(ph, t, a.tiles, nblk);
-    const int64_t sbyte = vbeg * E + pb.v0 * 16;  // this workgroup's first block of the phase
+    const PhaseBlocks pb = phase_blocks<K>(ph, lpos, lt, lblk);
+    const int64_t sbyte = lbyte + pb.v0 * 16;  // this workgroup's first block of the phase
+    // WHOLE: the chunk of the workgroup's block k is c0 plus the bits of inc
+    // up to k (its blocks are G apart and a chunk holds at least G blocks,
+    // so the chunk grows by at most one from a block to the next)
+    int c0 = 0;
+    uint32_t inc = 0;
+    if constexpr (WHOLE) {
+      if (pb.kv > 0) {
+        const int64_t g0 = pb.v0 / kBlock;
+        c0 = (int)(g0 / a.gbpc);
+        int64_t r = g0 - (int64_t)c0 * a.gbpc;
+        for (int k = 1; k < pb.kv; k++) {
+          r += G;
+          if (r >= a.gbpc) {
+            r -= a.gbpc;
+            inc |= 1u << k;
+          }
+        }
+      }
+    }
+    auto chunk_of = [&](int k) __attribute__((always_inline)) {
+      return c0 + __builtin_popcount(inc & (0xFFFFFFFFu >> (31 - k)));
+    };
     u32x4 R[K];  // the phase's results, in VGPRs from the read half to the write half
     runs(pb.kv, [&](auto b_tag, auto s_tag, int k0) __attribute__((always_inline)) {
-      read_run(b_tag, s_tag, R, sbyte, kst, k0);
+      read_run(b_tag, s_tag, R, sbyte, kst, k0, chunk_of);
     });
     phased_barrier(a, nbar, ++nb, &s_rel);
     // write half: output by output; the workgroups of chunk j start at
@@ -312,9 +370,12 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
     if (ph + 1 < a.nphase) phased_barrier(a, nbar, ++nb, &s_rel);
   }
 
+  if constexpr (WHOLE) return;  // every element sits in a whole block of the layout
+
   // the chunk's vectors past the blocks the phases hold (less than a block
   // when the grid runs enough phases), read, folded and written vector by
   // vector by all of the chunk's workgroups
+  const int64_t nblk = nvec / kBlock;
   const int64_t held = (int64_t)a.nphase * a.tiles * K;
   for (int64_t v = (nblk < held ? nblk : held) * kBlock + (int64_t)t * kBlock + tid; v < nvec;
        v += (int64_t)a.tiles * kBlock) {
@@ -350,85 +411,86 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
 
 namespace {
 
-template <int DT, int OP, bool ALL_OUT>
+template <int DT, int OP, bool ALL_OUT, bool WHOLE>
 hipError_t phased_by_p(int p, const PhasedArgs& a, hipStream_t s) {
   const dim3 g((unsigned)a.tiles * (unsigned)p), b(kBlock);
   switch (p) {
-    case 2: return launch<k_fold_phased<DT, OP, 2, ALL_OUT>>(g, b, s, a);
-    case 4: return launch<k_fold_phased<DT, OP, 4, ALL_OUT>>(g, b, s, a);
-    case 8: return launch<k_fold_phased<DT, OP, 8, ALL_OUT>>(g, b, s, a);
-    case 16: return launch<k_fold_phased<DT, OP, 16, ALL_OUT>>(g, b, s, a);
+    case 2: return launch<k_fold_phased<DT, OP, 2, ALL_OUT, WHOLE>>(g, b, s, a);
+    case 4: return launch<k_fold_phased<DT, OP, 4, ALL_OUT, WHOLE>>(g, b, s, a);
+    case 8: return launch<k_fold_phased<DT, OP, 8, ALL_OUT, WHOLE>>(g, b, s, a);
+    case 16: return launch<k_fold_phased<DT, OP, 16, ALL_OUT, WHOLE>>(g, b, s, a);
   }
   return hipErrorInvalidValue;
 }
 
-template <int DT, bool ALL_OUT>
+template <int DT, bool ALL_OUT, bool WHOLE>
 hipError_t phased_by_op(int op, int p, const PhasedArgs& a, hipStream_t s) {
   switch (op) {
-    case SIM_SUM: return phased_by_p<DT, SIM_SUM, ALL_OUT>(p, a, s);
-    case SIM_PROD: return phased_by_p<DT, SIM_PROD, ALL_OUT>(p, a, s);
-    case SIM_MIN: return phased_by_p<DT, SIM_MIN, ALL_OUT>(p, a, s);
-    case SIM_MAX: return phased_by_p<DT, SIM_MAX, ALL_OUT>(p, a, s);
-    case SIM_AVG: return phased_by_p<DT, SIM_AVG, ALL_OUT>(p, a, s);
+    case SIM_SUM: return phased_by_p<DT, SIM_SUM, ALL_OUT, WHOLE>(p, a, s);
+    case SIM_PROD: return phased_by_p<DT, SIM_PROD, ALL_OUT, WHOLE>(p, a, s);
+    case SIM_MIN: return phased_by_p<DT, SIM_MIN, ALL_OUT, WHOLE>(p, a, s);
+    case SIM_MAX: return phased_by_p<DT, SIM_MAX, ALL_OUT, WHOLE>(p, a, s);
+    case SIM_AVG: return phased_by_p<DT, SIM_AVG, ALL_OUT, WHOLE>(p, a, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int DT, int OP, int P, bool ALL_OUT>
+template <int DT, int OP, int P, bool ALL_OUT, bool WHOLE>
 int occ_of() {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)k_fold_phased<DT, OP, P, ALL_OUT>, kBlock, 0) !=
-      hipSuccess) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, (const void*)k_fold_phased<DT, OP, P, ALL_OUT, WHOLE>,
+                                                   kBlock, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
   return nb;
 }
 
-template <int DT, int OP, bool ALL_OUT>
+template <int DT, int OP, bool ALL_OUT, bool WHOLE>
 int occ_by_p(int p) {
   switch (p) {
-    case 2: return occ_of<DT, OP, 2, ALL_OUT>();
-    case 4: return occ_of<DT, OP, 4, ALL_OUT>();
-    case 8: return occ_of<DT, OP, 8, ALL_OUT>();
-    case 16: return occ_of<DT, OP, 16, ALL_OUT>();
+    case 2: return occ_of<DT, OP, 2, ALL_OUT, WHOLE>();
+    case 4: return occ_of<DT, OP, 4, ALL_OUT, WHOLE>();
+    case 8: return occ_of<DT, OP, 8, ALL_OUT, WHOLE>();
+    case 16: return occ_of<DT, OP, 16, ALL_OUT, WHOLE>();
   }
   return 0;
 }
 
-template <int DT, bool ALL_OUT>
+template <int DT, bool ALL_OUT, bool WHOLE>
 int occ_by_op(int op, int p) {
   switch (op) {
-    case SIM_SUM: return occ_by_p<DT, SIM_SUM, ALL_OUT>(p);
-    case SIM_PROD: return occ_by_p<DT, SIM_PROD, ALL_OUT>(p);
-    case SIM_MIN: return occ_by_p<DT, SIM_MIN, ALL_OUT>(p);
-    case SIM_MAX: return occ_by_p<DT, SIM_MAX, ALL_OUT>(p);
-    case SIM_AVG: return occ_by_p<DT, SIM_AVG, ALL_OUT>(p);
+    case SIM_SUM: return occ_by_p<DT, SIM_SUM, ALL_OUT, WHOLE>(p);
+    case SIM_PROD: return occ_by_p<DT, SIM_PROD, ALL_OUT, WHOLE>(p);
+    case SIM_MIN: return occ_by_p<DT, SIM_MIN, ALL_OUT, WHOLE>(p);
+    case SIM_MAX: return occ_by_p<DT, SIM_MAX, ALL_OUT, WHOLE>(p);
+    case SIM_AVG: return occ_by_p<DT, SIM_AVG, ALL_OUT, WHOLE>(p);
   }
   return 0;
 }
 
 }  // namespace
 
-// the launcher and occupancy query of one output mode (every dtype, op and p)
-template <bool ALL_OUT>
+// the launcher and occupancy query of one output mode and layout (every
+// dtype, op and p)
+template <bool ALL_OUT, bool WHOLE>
 hipError_t phased_launch(int dtype, int op, int p, const PhasedArgs& a, hipStream_t s) {
   switch (dtype) {
-    case SIM_INT32: return phased_by_op<SIM_INT32, ALL_OUT>(op, p, a, s);
-    case SIM_FP32: return phased_by_op<SIM_FP32, ALL_OUT>(op, p, a, s);
-    case SIM_FP16: return phased_by_op<SIM_FP16, ALL_OUT>(op, p, a, s);
-    case SIM_BF16: return phased_by_op<SIM_BF16, ALL_OUT>(op, p, a, s);
+    case SIM_INT32: return phased_by_op<SIM_INT32, ALL_OUT, WHOLE>(op, p, a, s);
+    case SIM_FP32: return phased_by_op<SIM_FP32, ALL_OUT, WHOLE>(op, p, a, s);
+    case SIM_FP16: return phased_by_op<SIM_FP16, ALL_OUT, WHOLE>(op, p, a, s);
+    case SIM_BF16: return phased_by_op<SIM_BF16, ALL_OUT, WHOLE>(op, p, a, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <bool ALL_OUT>
+template <bool ALL_OUT, bool WHOLE>
 int phased_occupancy(int dtype, int op, int p) {
   switch (dtype) {
-    case SIM_INT32: return occ_by_op<SIM_INT32, ALL_OUT>(op, p);
-    case SIM_FP32: return occ_by_op<SIM_FP32, ALL_OUT>(op, p);
-    case SIM_FP16: return occ_by_op<SIM_FP16, ALL_OUT>(op, p);
-    case SIM_BF16: return occ_by_op<SIM_BF16, ALL_OUT>(op, p);
+    case SIM_INT32: return occ_by_op<SIM_INT32, ALL_OUT, WHOLE>(op, p);
+    case SIM_FP32: return occ_by_op<SIM_FP32, ALL_OUT, WHOLE>(op, p);
+    case SIM_FP16: return occ_by_op<SIM_FP16, ALL_OUT, WHOLE>(op, p);
+    case SIM_BF16: return occ_by_op<SIM_BF16, ALL_OUT, WHOLE>(op, p);
   }
   return 0;
 }

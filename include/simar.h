@@ -462,7 +462,13 @@ enum {
                                   p = 2 for the one-shot, never at p = 4 for the all-gather) */
   SIM_DEBUG_PHASED_EXPIRED = 16, /* phased fold barrier waits that gave up at the spin limit
                                   (synchronizes the device; set only to 0, which clears it) */
-  SIM_DEBUG_PHASED_LAST = 17   /* get only: 1 if the last collective call ran a phased kernel */
+  SIM_DEBUG_PHASED_LAST = 17, /* get only: 1 if the last collective call ran a phased kernel */
+  SIM_DEBUG_PHASED_LAYOUT = 18, /* the phased one-shot's block layout: 0 (default) the whole
+                                  buffer's blocks in turn over the grid where every chunk is the
+                                  same whole number of blocks, no fewer than the grid's
+                                  workgroups; 1 each chunk's blocks over its own workgroups */
+  SIM_DEBUG_PHASED_WHOLE_LAST = 19 /* get only: 1 if the last collective call ran the phased
+                                  one-shot in the whole-buffer layout */
 };
 int sim_debug_set(int key, uint64_t value);
 int sim_debug_get(int key, uint64_t* value);

@@ -346,3 +346,89 @@ def test_phased_all_gather_matches_oracle(orc, lib, p, dtype):
         sim.sim_debug_set("workgroups", 0)
     assert sim.sim_check_error(stream()) == 0
     assert sim.sim_debug_get("phased_expired") == 0
+
+
+def _run_layout(sim, xs, dtype, op, p, n, layout, wg, inplace=False, mode=1):
+    """The one-shot with the phased kernel's block layout set (0: whole
+    buffer where it applies, 1: per chunk); returns the outputs and whether
+    the whole-buffer layout ran."""
+    sim.sim_debug_set("phased_layout", layout)
+    try:
+        got, ran = _run(sim, [x.copy() for x in xs], dtype, op, p, n, inplace=inplace, mode=mode, wg=wg)
+        whole = sim.sim_debug_get("phased_whole_last")
+    finally:
+        sim.sim_debug_set("phased_layout", 0)
+    return got, ran, whole
+
+
+@pytest.mark.parametrize("p", [2, 4, 8, 16])
+@pytest.mark.parametrize("dtype,op", [("bf16", "sum"), ("fp16", "avg"), ("fp32", "prod"), ("fp32", "min"),
+                                      ("int32", "max"), ("int32", "avg")])
+def test_phased_whole_layout_matches_oracle(orc, lib, p, dtype, op):
+    """The one-shot's whole-buffer layout: the grid takes the buffer's blocks
+    in turn and folds each block in its own chunk's order.  Chunks change
+    inside a workgroup's run of blocks at varying places; one phase dealt
+    out unevenly, three phases with a short last one, and one workgroup per
+    chunk over more than p phases.  Against the oracle, in place and not,
+    and bit-identical to the per-chunk layout and to the fused kernel."""
+    from tests.gpu_util import assert_parity, bits
+    sim = lib
+    V = 16 // (2 if dtype in ("fp16", "bf16") else 4)
+    blk = 256 * V  # elements per block
+    K = 32 if p <= 8 else 16
+    for tiles, bpc in ((2, 4 * p + 3), (3, 3 * p * K // 4 + 5), (1, p * K + 7)):
+        n = p * bpc * blk  # every chunk bpc whole blocks, bpc >= the grid's tiles * p workgroups
+        xs = _inputs(dtype, op, p, n, 300 + p + tiles)
+        want, _ = orc.allreduce(xs, dtype, op, "oneshot")
+        fused, ran_f, _ = _run_layout(sim, xs, dtype, op, p, n, 0, 0, mode=2)
+        chunked, ran_c, whole_c = _run_layout(sim, xs, dtype, op, p, n, 1, tiles * p)
+        assert ran_f == 0 and ran_c == 1 and whole_c == 0
+        for inplace in (False, True):
+            print(f"whole layout p={p} {dtype} {op} tiles={tiles} blocks/chunk={bpc} inplace={inplace}", flush=True)
+            got, ran, whole = _run_layout(sim, xs, dtype, op, p, n, 0, tiles * p, inplace=inplace)
+            assert ran == 1 and whole == 1
+            for r in range(p):
+                assert_parity(got[r], want[r], dtype, f"whole p={p} {dtype} {op} tiles={tiles} r{r}")
+                assert (bits(got[r]) == bits(fused[r])).all(), (p, dtype, op, tiles, r)
+                assert (bits(got[r]) == bits(chunked[r])).all(), (p, dtype, op, tiles, r)
+    assert sim.sim_debug_get("phased_expired") == 0
+
+
+def test_phased_whole_layout_selection(orc, lib):
+    """Where the whole-buffer layout runs: the phased one-shot only, when
+    every chunk is the same whole number of blocks and no fewer blocks than
+    the grid has workgroups, and not when the layout is set to per chunk."""
+    from tests.gpu_util import assert_parity
+    sim = lib
+    p, blk = 8, 256 * 8
+    cases = [(p * 64 * blk, 16, 1),        # 64 blocks per chunk, 16 workgroups
+             (p * 64 * blk + 8, 16, 0),    # not whole blocks
+             (p * 64 * blk + p, 16, 0),    # whole elements per chunk, not whole blocks
+             (p * 15 * blk, 16, 0),        # fewer blocks per chunk than workgroups
+             (p * 16 * blk, 16, 1)]        # exactly as many
+    for n, wg, expect in cases:
+        xs = _inputs("bf16", "sum", p, n, 41)
+        want, _ = orc.allreduce(xs, "bf16", "sum", "oneshot")
+        got, ran, whole = _run_layout(sim, xs, "bf16", "sum", p, n, 0, wg)
+        assert ran == 1 and whole == expect, (n, wg, whole)
+        for r in range(p):
+            assert_parity(got[r], want[r], "bf16", f"selection n={n} r{r}")
+    n = p * 64 * blk
+    xs = _inputs("bf16", "sum", p, n, 42)
+    _, ran, whole = _run_layout(sim, xs, "bf16", "sum", p, n, 1, 16)
+    assert ran == 1 and whole == 0
+    # all-pairs step 1 (the owner-only phased fold) keeps the per-chunk layout
+    from tests.gpu_util import run_allreduce
+    sim.sim_debug_set("phased", 1)
+    sim.sim_debug_set("workgroups", 16)
+    try:
+        got = run_allreduce(xs, "bf16", "sum", "allpairs")
+        assert sim.sim_debug_get("phased_last") == 1 and sim.sim_debug_get("phased_whole_last") == 0
+    finally:
+        sim.sim_debug_set("phased", 0)
+        sim.sim_debug_set("workgroups", 0)
+    want, _ = orc.allreduce(xs, "bf16", "sum", "allpairs")
+    for r in range(p):
+        assert_parity(got[r], want[r], "bf16", f"allpairs r{r}")
+    with pytest.raises(sim.SimError):
+        sim.sim_debug_set("phased_layout", 2)
