@@ -335,9 +335,10 @@ int fold_phased_vecs_per_lane(int p);
 // fan-out (every output but j).
 hipError_t launch_gather_phased(int esize, int p, bool skip_own, const PhasedArgs& a, hipStream_t s);
 int gather_phased_blocks_per_cu(int esize, int p, bool skip_own);
-template <bool ALL_OUT>
+// WHOLE: the one-shot's whole-buffer layout (only with ALL_OUT)
+template <bool ALL_OUT, bool WHOLE>
 hipError_t phased_launch(int dtype, int op, int p, const PhasedArgs& a, hipStream_t s);
-template <bool ALL_OUT>
+template <bool ALL_OUT, bool WHOLE>
 int phased_occupancy(int dtype, int op, int p);
 
 }  // namespace simar

@@ -158,6 +158,7 @@ def time_calls(fn, steps: int, warmup: int) -> float:
 
 
 KERNEL_SOURCES = ["all_reduce_reduction_amd/csrc/k_phased.hip", "all_reduce_reduction_amd/csrc/phased_impl.h",
+                  "all_reduce_reduction_amd/csrc/k_phased_whole.hip",
                   "all_reduce_reduction_amd/csrc/k_phased_owner.hip", "all_reduce_reduction_amd/csrc/k_phased_gather.hip",
                   "all_reduce_reduction_amd/csrc/k_fold.hip",
                   "all_reduce_reduction_amd/csrc/fold_impl.h",
