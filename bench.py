@@ -32,6 +32,9 @@ Printed JSON line:
                  time for the same call (all host threads, and one thread on a
                  stated sample): busBW, algorithmic HBM GB/s per schedule; the
                  standalone reduce-scatter and all-gather with their own laws
+  phased_layout_ab_us
+                 the headline's phased one-shot in its per-chunk block layout
+                 and in the whole-buffer layout, alternating batches
   workload4_latency_us
                  per-call microseconds of the LL packet path vs the plain
                  one-shot (and the selector's pick) from 1 KiB to 1 MiB per rank
@@ -665,6 +668,19 @@ def main():
             budget[str(b) if b else "none"] = round(2 * (P - 1) / P * S / tb / 1e9, 1)
         sim.sim_config_set("max_workgroups", 0)
         extras["oneshot_busbw_by_workgroup_budget"] = budget
+        # the phased one-shot's block layouts side by side on the headline:
+        # per chunk against the whole-buffer layout the library picks here
+        # (SIM_DEBUG_PHASED_LAYOUT), alternating, three batches each
+        lay = {"per_chunk_us": [], "whole_buffer_us": []}
+        for _ in range(3):
+            for key, v in (("per_chunk_us", 1), ("whole_buffer_us", 0)):
+                sim.sim_debug_set("phased_layout", v)
+                lay[key].append(round(time_calls(lambda: step("oneshot"), max(10, args.steps // 4), 5) * 1e6, 2))
+                if v == 0:
+                    lay["whole_buffer_ran"] = sim.sim_debug_get("phased_whole_last")
+        sim.sim_debug_set("phased_layout", 0)
+        lay["ratio_of_medians"] = round(float(np.median(lay["whole_buffer_us"]) / np.median(lay["per_chunk_us"])), 4)
+        extras["phased_layout_ab_us"] = lay
         us5 = large_workload(sim, synthdata, torch, np, dev, stream, max(10, args.steps // 10), 3)
         extras["workload5_fp32_avg_256MiB_oneshot"] = {
             "us": round(us5, 2), "busbw_GBps": round(2 * (P - 1) / P * N5 * 4 / us5 / 1e3, 1),
