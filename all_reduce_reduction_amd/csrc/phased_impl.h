@@ -28,7 +28,10 @@
 //
 // The grid is persistent (two workgroups per CU, all resident), and a phase
 // covers K * kBlock vectors of every workgroup: 64 MiB of results per phase
-// on 256 CUs, one phase for the 64 MiB-per-rank headline.
+// on 256 CUs, one phase at 64 MiB per rank with p = 8.  Where every chunk is
+// the same whole number of blocks (no fewer than the grid's workgroups), the
+// one-shot lays the phases out over the whole buffer instead of chunk by
+// chunk (the WHOLE form, see the phase loop).
 //
 // The barrier is for timing only: every element is read, folded and written
 // by one lane, so no workgroup ever reads what another writes, and the
@@ -306,9 +309,8 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
   // whole buffer's blocks in turn, workgroup (j, t) at turn j tiles + t (so
   // each XCD's workgroups hold neighbouring blocks), and each step of the
   // write half covers one range of G blocks.  Each block keeps its own
-  // chunk's fold order.  Measured on MI355X (p = 8, bf16, 64 MiB per rank):
-  // 168 against 174-175 us, the p write ranges next to each other instead
-  // of a chunk apart.
+  // chunk's fold order.  Measured on MI355X (p = 8, bf16, 64 MiB per rank,
+  // same run): 170.0-170.5 against 174.3-174.8 us per call.
   const int G = a.tiles * P;
   const int lt = WHOLE ? G : a.tiles;                   // workgroups taking turns
   const int lpos = WHOLE ? j * a.tiles + t : t;         // this workgroup's turn
