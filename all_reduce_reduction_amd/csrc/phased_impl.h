@@ -192,7 +192,12 @@ __global__ void __launch_bounds__(kBlock) k_fold_phased(PhasedArgs a) {
   constexpr int V = epv<DT>();
   constexpr int E = Ty<DT>::E;
   constexpr int K = PhasedShape<P>::K;
-  constexpr int D = PhasedShape<P>::D;
+  // load sets in flight while one folds: about 16 loads per lane, or about 8
+  // in the whole-buffer layout, whose register selects per block ran better
+  // with fewer sets ahead (p = 8 on MI355X, one set against two: 169.5
+  // against 171.8-172.4 us at 64 MiB per rank, 337 against 343 us at 128 MiB,
+  // fp32 at 32 MiB 89.5-90.3 against 93.4-93.6 us)
+  constexpr int D = WHOLE ? (P >= 8 ? 1 : 8 / P) : PhasedShape<P>::D;
   const int j = (int)(blockIdx.x % (unsigned)P);
   const int t = (int)(blockIdx.x / (unsigned)P);
   const int64_t lo = a.lo[j], hi = a.lo[j + 1];
