@@ -38,20 +38,20 @@ Model default_model() {
   // {alpha_us, gbps, steps, bytes_factor, wg_gbps, host_us}, from the MI355X
   // calibration (p = 8, bf16)
   m.a[SIM_ALGO_AUTO] = {0.0, 1.0, -1.0, -1.0, 0.0, 0.0};
-  m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.4, 2.75};
-  m.a[SIM_ALGO_ALLPAIRS] = {2.15, 6100.0, -1.0, -1.0, 47.3, 3.05};
-  m.a[SIM_ALGO_ONESHOT] = {1.8, 6300.0, -1.0, -1.0, 53.6, 3.2};
-  m.a[SIM_ALGO_ONESHOT_LL] = {8.95, 12800.0, -1.0, -1.0, 8.8, 0.0};
-  m.a[SIM_ALGO_RING_FIFO] = {13.9, 685.0, -1.0, -1.0, 16.1, 0.0};
-  m.a[SIM_ALGO_TREE] = {3.05, 6200.0, -1.0, -1.0, 0.0, 4.25};
-  m.a[SIM_ALGO_REXCH] = {2.05, 6000.0, -1.0, -1.0, 0.0, 4.0};
-  m.a[SIM_ALGO_HIER] = {3.35, 6200.0, -1.0, -1.0, 0.0, 4.5};
-  m.a[SIM_ALGO_HIER_LARGE] = {3.3, 6050.0, -1.0, -1.0, 0.0, 4.45};
-  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {7.2, 8000.0, -1.0, -1.0, 32.0, 0.0};
+  m.a[SIM_ALGO_RING] = {2.5, 6350.0, -1.0, -1.0, 24.4, 2.8};
+  m.a[SIM_ALGO_ALLPAIRS] = {2.15, 6100.0, -1.0, -1.0, 47.2, 3.0};
+  m.a[SIM_ALGO_ONESHOT] = {1.8, 6250.0, -1.0, -1.0, 53.3, 3.2};
+  m.a[SIM_ALGO_ONESHOT_LL] = {8.9, 13500.0, -1.0, -1.0, 8.9, 0.0};
+  m.a[SIM_ALGO_RING_FIFO] = {13.5, 660.0, -1.0, -1.0, 16.25, 0.0};
+  m.a[SIM_ALGO_TREE] = {3.15, 6200.0, -1.0, -1.0, 0.0, 4.15};
+  m.a[SIM_ALGO_REXCH] = {2.25, 6000.0, -1.0, -1.0, 0.0, 4.1};
+  m.a[SIM_ALGO_HIER] = {3.35, 6200.0, -1.0, -1.0, 0.0, 4.25};
+  m.a[SIM_ALGO_HIER_LARGE] = {3.2, 6000.0, -1.0, -1.0, 0.0, 4.45};
+  m.a[SIM_ALGO_ALLPAIRS_PERSISTENT] = {6.95, 8000.0, -1.0, -1.0, 32.0, 0.0};
   // second regimes: the phased one-shot, the single-launch ring's FIFO protocol
-  m.hi[SIM_ALGO_ONESHOT] = {8.5, 6550.0, -1.0, -1.0, 53.6, 0.0};
+  m.hi[SIM_ALGO_ONESHOT] = {8.8, 6600.0, -1.0, -1.0, 53.3, 0.0};
   m.has_hi[SIM_ALGO_ONESHOT] = true;
-  m.hi[SIM_ALGO_RING_FIFO] = {24.35, 6450.0, -1.0, -1.0, 16.1, 52.6};
+  m.hi[SIM_ALGO_RING_FIFO] = {24.2, 6450.0, -1.0, -1.0, 16.25, 50.6};
   m.has_hi[SIM_ALGO_RING_FIFO] = true;
   return m;
 }
